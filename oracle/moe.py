@@ -1,0 +1,263 @@
+"""CPU oracle of the Hy3-style MoE FFN layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links this module: only the tests, the smoke check and the benchmark's CPU
+baseline leg do.  It shares no code with the HIP library.
+
+It is a plain, slow, float64 statement of what the layer computes.  Inputs
+arrive as exact float64 values (bfloat16 and float32 widen to float64 without
+error), and nothing is rounded on the way.
+
+Sources (the pages this follows):
+
+* hy3 README ("hy3 — tencent/Hy3 GGUF Converter and Inference Engine"),
+  "Model facts" table: 192 routed experts, top-8, plus one shared expert that
+  is always active.  MoE routing row: sigmoid of the router logits; the top-8
+  are chosen on sigmoid + expert_bias; the combine weights are the unbiased
+  sigmoid scores, renormalised to sum 1 and then scaled by 2.826.
+* CANN deployment article on Hy3, section 一: HYV3Config defaults
+  router_scaling_factor=2.826, num_experts_per_tok=8, route_norm=True,
+  moe_router_use_sigmoid=True.
+* HunyuanImage 3.0 MoE reading, "HunyuanTopKGate easy_topk" path: router
+  Linear H->E without bias, float32 weight with activations cast to float32;
+  softmax over the expert axis, top-K, sum of the K picked probabilities
+  clamped at 1e-8, division.  "Routed Experts" eager path: tokens repeated K
+  times, one mask per expert, each expert run on its selected rows, outputs
+  written back, reshaped to [T, K, H], multiplied by the routing weights and
+  summed over K.  "Shared MLP": one expert that every token goes through,
+  added to the routed output.  The experts use SiLU/SwiGLU
+  (down(silu(gate(a)) * up(a))).
+
+Readings where the pages are silent (each is listed with the other readings
+in the design notes):
+
+* ties in the selection score go to the lower expert index, and the K picked
+  indices are returned in descending selection score;
+* the bias is added to the sigmoid score, not to the logit;
+* the shared expert has weight 1 (the 2.826 factor is for routed experts);
+* sigmoid mode has no renormalisation epsilon (a sum of sigmoids is > 0);
+* selection is flat over all E experts (no expert groups).
+
+Parity pins: every public function is pinned by a test in
+``tests/test_oracle_pins.py`` (hand-derived golden values, brute force over
+all K-subsets, a loop-only dense evaluation, closed forms and invariants).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Optional, Sequence, Tuple
+
+import numpy as np
+
+ROUTE_SIGMOID_BIAS = 0
+ROUTE_SOFTMAX = 1
+
+ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
+
+
+# --------------------------------------------------------------------------
+# Router
+# --------------------------------------------------------------------------
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """logits[t, e] = sum_h x[t, h] * w_router[e, h]   (bias-free linear H->E).
+
+    HunyuanImage 3.0 MoE reading, HunyuanTopKGate: ``wg`` is a bias-free
+    float32 Linear of weight shape [E, H]; the hy3 README keeps the router
+    gate in F32.  Evaluated in float64, where every product of a bf16 or fp32
+    activation with an fp32 weight is exact.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_router, dtype=np.float64)
+    return x @ w.T
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """Logistic function 1 / (1 + exp(-z)), evaluated without overflow."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def softmax_rows(z: np.ndarray) -> np.ndarray:
+    """Softmax over the expert axis (dim=1), with the row maximum subtracted."""
+    z = np.asarray(z, dtype=np.float64)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def topk_desc(score: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest entries of each row, in descending score.
+
+    Equal scores are ordered by ascending expert index (a stable sort of the
+    negated scores), so the lower index wins a tie at the k-th place.
+    """
+    order = np.argsort(-np.asarray(score, dtype=np.float64), axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+@dataclasses.dataclass
+class Route:
+    idx: np.ndarray        # [T, K] int64, descending selection score
+    weight: np.ndarray     # [T, K] float64 combine weights
+    margin: np.ndarray     # [T] selection score of the K-th minus the (K+1)-th pick
+    select_score: np.ndarray  # [T, E] the score the selection is taken on
+    prob: np.ndarray       # [T, E] sigmoid scores / softmax probabilities
+
+
+def route_from_logits(logits: np.ndarray, K: int, mode: int = ROUTE_SIGMOID_BIAS,
+                      bias: Optional[np.ndarray] = None, scale: float = 2.826,
+                      renorm_eps: float = 1e-8) -> Route:
+    """Scores, top-K selection and combine weights from router logits.
+
+    Sigmoid mode (hy3 README, Model facts / MoE routing; HYV3Config
+    moe_router_use_sigmoid, route_norm, router_scaling_factor):
+        s = sigmoid(L);  pick top-K of s + bias;
+        w_j = scale * s[pick_j] / sum_j' s[pick_j'].
+    The bias only steers the choice; the weights use the unbiased s.
+
+    Softmax mode (HunyuanImage 3.0 MoE reading, easy_topk):
+        p = softmax(L);  pick top-K of p;
+        w_j = p[pick_j] / max(sum_j' p[pick_j'], renorm_eps).
+    No bias, no scale.
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    if not (1 <= K <= E):
+        raise ValueError("need 1 <= K <= E")
+    if mode == ROUTE_SIGMOID_BIAS:
+        prob = sigmoid(L)
+        b = np.zeros(E) if bias is None else np.asarray(bias, dtype=np.float64)
+        sel = prob + b[None, :]
+    elif mode == ROUTE_SOFTMAX:
+        prob = softmax_rows(L)
+        sel = prob
+    else:
+        raise ValueError("unknown route mode")
+    idx = topk_desc(sel, K)
+    rows = np.arange(T)[:, None]
+    picked = prob[rows, idx]
+    tot = picked.sum(axis=1, keepdims=True)
+    if mode == ROUTE_SIGMOID_BIAS:
+        weight = scale * (picked / tot)
+    else:
+        weight = picked / np.maximum(tot, renorm_eps)
+    if K < E:
+        ssorted = -np.sort(-sel, axis=1)
+        margin = ssorted[:, K - 1] - ssorted[:, K]
+    else:
+        margin = np.full(T, np.inf)
+    return Route(idx=idx, weight=weight, margin=margin, select_score=sel, prob=prob)
+
+
+def route(x, w_router, K: int, mode: int = ROUTE_SIGMOID_BIAS, bias=None,
+          scale: float = 2.826, renorm_eps: float = 1e-8) -> Route:
+    """The gate of the layer: router logits, then scores/selection/weights."""
+    return route_from_logits(router_logits(x, w_router), K, mode, bias, scale, renorm_eps)
+
+
+# --------------------------------------------------------------------------
+# Experts
+# --------------------------------------------------------------------------
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z)."""
+    return np.asarray(z, dtype=np.float64) * sigmoid(z)
+
+
+def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+                  w_down: np.ndarray) -> np.ndarray:
+    """One SwiGLU expert on rows ``a`` [n, H]:  down( silu(a W_gate^T) * (a W_up^T) ).
+
+    Weights are in nn.Linear layout [out, in]: gate/up [I, H], down [H, I]
+    (HunyuanImage 3.0 MoE reading, stacked gate/up and down weights).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    g = a @ np.asarray(w_gate, dtype=np.float64).T
+    u = a @ np.asarray(w_up, dtype=np.float64).T
+    h = silu(g) * u
+    return h @ np.asarray(w_down, dtype=np.float64).T
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
+                        experts: ExpertFn, E: int,
+                        shared: Optional[Sequence[np.ndarray]] = None) -> np.ndarray:
+    """Routed experts + shared expert for a given route (the eager path).
+
+    Follows the eager path of the HunyuanImage 3.0 MoE reading: every token
+    row is repeated K times so that copy j of token t pairs with expert
+    idx[t, j]; for each expert, the copies routed to it are selected by a mask
+    and run through that expert; the outputs are written back in copy order,
+    viewed as [T, K, H], multiplied by the routing weights and summed over K.
+    The shared expert (a parallel branch every token passes through) is
+    computed first and added, as that reading's "Shared MLP" section states.
+
+    ``experts(e)`` returns (gate, up, down) of routed expert e in float64;
+    experts no copy is routed to are never requested.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(idx)
+    weight = np.asarray(weight, dtype=np.float64)
+    T, H = x.shape
+    K = idx.shape[1] if idx.ndim == 2 else 0
+    out_shared = np.zeros((T, H))
+    if shared is not None:
+        out_shared = swiglu_expert(x, *shared)
+    if T == 0 or K == 0:
+        return out_shared
+    flat_idx = idx.reshape(-1)
+    x_rep = np.repeat(x, K, axis=0)                 # [T*K, H], copy j of token t at t*K+j
+    expert_out = np.zeros_like(x_rep)
+    for e in range(E):
+        mask = flat_idx == e
+        if not mask.any():
+            continue
+        wg, wu, wd = experts(e)
+        expert_out[mask] = swiglu_expert(x_rep[mask], wg, wu, wd)
+    routed = (expert_out.reshape(T, K, H) * weight[:, :, None]).sum(axis=1)
+    return out_shared + routed
+
+
+def forward(x, w_router, experts: ExpertFn, E: int, K: int,
+            shared: Optional[Sequence[np.ndarray]] = None,
+            mode: int = ROUTE_SIGMOID_BIAS, bias=None, scale: float = 2.826,
+            renorm_eps: float = 1e-8) -> Tuple[np.ndarray, Route]:
+    """The full MoE FFN layer: gate, then routed + shared experts."""
+    r = route(x, w_router, K, mode, bias, scale, renorm_eps)
+    return forward_given_route(x, r.idx, r.weight, experts, E, shared), r
+
+
+def dense_masked(x, idx, weight, experts: ExpertFn, E: int,
+                 shared: Optional[Sequence[np.ndarray]] = None) -> np.ndarray:
+    """Brute force: evaluate every expert on every token and mask.
+
+    out[t] = shared(x_t) + sum_e M[t, e] * f_e(x_t), where M is zero except
+    M[t, idx[t, j]] = weight[t, j].  Used on tiny inputs only, as a check of
+    the sparse dispatch above.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    M = np.zeros((T, E))
+    idx = np.asarray(idx)
+    for t in range(T):
+        for j in range(idx.shape[1]):
+            M[t, idx[t, j]] += weight[t, j]
+    out = np.zeros((T, H)) if shared is None else swiglu_expert(x, *shared)
+    for e in range(E):
+        out = out + M[:, e:e + 1] * swiglu_expert(x, *experts(e))
+    return out
+
+
+def layer_flops(T: int, H: int, E: int, K: int, I: int, I_shared: int) -> dict:
+    """Algorithmic FLOP counts of the layer (real rows only, no padding)."""
+    routed = 6.0 * H * I * T * K
+    shared = 6.0 * H * I_shared * T
+    router = 2.0 * T * H * E
+    return {"routed": routed, "shared": shared, "router": router,
+            "experts": routed + shared, "total": routed + shared + router}

@@ -1,0 +1,275 @@
+"""Seeded synthetic inputs for the Hy3-style MoE FFN layer.
+
+This module is shared by the tests, the benchmark and the CPU oracle's
+callers.  It holds no arithmetic of the method itself: it only draws random
+tensors with the shapes and distributions of the layer's workloads, rounds
+them to bfloat16 where the workload stores bfloat16, and decodes bfloat16 bit
+patterns back to exact float64 values.
+
+Shapes follow the Hy3 model facts (hy3 README, "Model facts" table: hidden
+4096, 192 routed experts with top-8 plus one shared expert, expert
+intermediate 1536) and the HunyuanImage-3.0 MoE reading (64 routed experts,
+softmax routing).
+
+Random streams
+--------------
+Every tensor has its own numpy PCG64 stream,
+``default_rng(SeedSequence([seed, key, tensor_id, expert_id]))``, so that any
+tensor (and any single expert of a stacked weight) can be regenerated on its
+own, in any order, on any number of threads.
+
+* ``key`` is a *model key* for weights (so that the decode and the prefill
+  workloads of the same model share one set of weights) and ``1000 + cfg_id``
+  for per-workload data (activations and the expert bias).
+* tensor ids: 0 x, 1 router weight, 2 expert bias, 3 gate, 4 up, 5 down,
+  6/7/8 shared gate/up/down.
+
+Distributions: x ~ N(0, 1); router weight ~ N(0, 0.02); bias ~ U(-0.1, 0.1)
+(or 0.3 * N(0, 1) for the skewed prefill chunk, and none for softmax
+routing); gate/up ~ N(0, 1/sqrt(H)); down ~ N(0, 1/sqrt(I)).  The second
+parameter of N is the standard deviation.
+
+bfloat16 values are produced from float32 draws by round-to-nearest-even on
+the bit pattern and are stored as ``uint16`` arrays of the raw bits.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+T_X, T_WR, T_BIAS, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN = range(9)
+
+ROUTE_SIGMOID_BIAS = 0
+ROUTE_SOFTMAX = 1
+
+
+# --------------------------------------------------------------------------
+# bfloat16 bit handling (input plumbing, not part of the method)
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Works on the IEEE-754 bit pattern: add 0x7FFF plus the lowest kept bit,
+    then drop the 16 low bits.  Inputs are finite by construction.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact decode of bfloat16 bits to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact decode of bfloat16 bits to float64."""
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Workload descriptions
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    cfg_id: int
+    model_key: int
+    T: int
+    H: int
+    E: int
+    K: int
+    I: int
+    I_shared: int
+    dtype: str                 # "f32" or "bf16": activations and expert weights
+    route_mode: int            # ROUTE_SIGMOID_BIAS or ROUTE_SOFTMAX
+    scale: float               # router scaling factor applied to routed weights
+    renorm_eps: float          # clamp of the renormalisation denominator
+    bias_kind: str             # "uniform", "skew" or "none"
+
+    def with_T(self, T: int) -> "MoEConfig":
+        return dataclasses.replace(self, T=int(T))
+
+    def with_(self, **kw) -> "MoEConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# Hy3 router scaling factor (hy3 README "Model facts", MoE routing row; the
+# CANN deployment article section 一 lists router_scaling_factor=2.826).
+HY3_SCALE = 2.826
+
+CONFIGS: Dict[int, MoEConfig] = {
+    0: MoEConfig("tiny_fp32", 0, 0, T=8, H=256, E=16, K=4, I=128, I_shared=128,
+                 dtype="f32", route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE,
+                 renorm_eps=0.0, bias_kind="uniform"),
+    1: MoEConfig("hy3_decode_T16", 1, 1, T=16, H=4096, E=192, K=8, I=1536,
+                 I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                 scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform"),
+    2: MoEConfig("hy3_prefill_T8192_skew", 2, 1, T=8192, H=4096, E=192, K=8,
+                 I=1536, I_shared=1536, dtype="bf16",
+                 route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
+                 bias_kind="skew"),
+    # Router-only sweep: M in {2, 64, 512, 4096}; the expert weights are not used.
+    3: MoEConfig("hy3_router_only", 3, 1, T=4096, H=4096, E=192, K=8, I=1536,
+                 I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                 scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform"),
+    4: MoEConfig("hunyuanimage_softmax_T32768", 4, 4, T=32768, H=4096, E=64,
+                 K=8, I=1536, I_shared=1536, dtype="bf16",
+                 route_mode=ROUTE_SOFTMAX, scale=1.0, renorm_eps=1e-8,
+                 bias_kind="none"),
+}
+
+ROUTER_SWEEP_M = (2, 64, 512, 4096)
+
+
+def _rng(seed: int, key: int, tensor_id: int, expert_id: int = 0):
+    return np.random.default_rng(
+        np.random.SeedSequence([int(seed), int(key), int(tensor_id), int(expert_id)]))
+
+
+def _normal_f32(rng, shape, std: float) -> np.ndarray:
+    a = rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
+    a *= np.float32(std)
+    return a.reshape(shape)
+
+
+def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(a32) if dtype == "bf16" else np.ascontiguousarray(a32)
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of a stored tensor (bf16 bits or float32)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(a)
+    return np.asarray(a, dtype=np.float64)
+
+
+def _default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class MoEInputs:
+    """Lazily generated, seeded inputs of one workload.
+
+    Storage dtypes: x and expert weights are float32 or bf16 bits (uint16)
+    per ``cfg.dtype``; the router weight and the bias are always float32.
+    """
+
+    def __init__(self, cfg: MoEConfig, seed: int = 0):
+        self.cfg = cfg
+        self.seed = int(seed)
+        self._cache: Dict[Tuple, np.ndarray] = {}
+
+    # ---- data streams (per workload) ----
+    def _data_key(self) -> int:
+        return 1000 + self.cfg.cfg_id
+
+    def x(self) -> np.ndarray:
+        k = ("x",)
+        if k not in self._cache:
+            c = self.cfg
+            a = _normal_f32(_rng(self.seed, self._data_key(), T_X), (c.T, c.H), 1.0)
+            self._cache[k] = _store(a, c.dtype)
+        return self._cache[k]
+
+    def bias(self) -> Optional[np.ndarray]:
+        c = self.cfg
+        if c.bias_kind == "none":
+            return None
+        k = ("bias",)
+        if k not in self._cache:
+            rng = _rng(self.seed, self._data_key(), T_BIAS)
+            if c.bias_kind == "uniform":
+                b = rng.uniform(-0.1, 0.1, size=c.E).astype(np.float32)
+            elif c.bias_kind == "skew":
+                b = (np.float32(0.3) * rng.standard_normal(c.E, dtype=np.float32))
+            else:
+                raise ValueError(c.bias_kind)
+            self._cache[k] = np.ascontiguousarray(b, dtype=np.float32)
+        return self._cache[k]
+
+    # ---- model streams (shared between workloads of one model) ----
+    def w_router(self) -> np.ndarray:
+        k = ("wr",)
+        if k not in self._cache:
+            c = self.cfg
+            self._cache[k] = _normal_f32(_rng(self.seed, c.model_key, T_WR), (c.E, c.H), 0.02)
+        return self._cache[k]
+
+    def expert(self, e: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """(gate [I,H], up [I,H], down [H,I]) of routed expert ``e``, stored dtype."""
+        c = self.cfg
+        mk = c.model_key
+        g = _normal_f32(_rng(self.seed, mk, T_GATE, e), (c.I, c.H), 1.0 / np.sqrt(c.H))
+        u = _normal_f32(_rng(self.seed, mk, T_UP, e), (c.I, c.H), 1.0 / np.sqrt(c.H))
+        d = _normal_f32(_rng(self.seed, mk, T_DOWN, e), (c.H, c.I), 1.0 / np.sqrt(c.I))
+        return _store(g, c.dtype), _store(u, c.dtype), _store(d, c.dtype)
+
+    def shared(self) -> Optional[Tuple[np.ndarray, np.ndarray, np.ndarray]]:
+        c = self.cfg
+        if c.I_shared == 0:
+            return None
+        k = ("shared",)
+        if k not in self._cache:
+            mk, Is = c.model_key, c.I_shared
+            g = _normal_f32(_rng(self.seed, mk, T_SGATE), (Is, c.H), 1.0 / np.sqrt(c.H))
+            u = _normal_f32(_rng(self.seed, mk, T_SUP), (Is, c.H), 1.0 / np.sqrt(c.H))
+            d = _normal_f32(_rng(self.seed, mk, T_SDOWN), (c.H, Is), 1.0 / np.sqrt(Is))
+            self._cache[k] = (_store(g, c.dtype), _store(u, c.dtype), _store(d, c.dtype))
+        return self._cache[k]
+
+    def stacked_experts(self, threads: Optional[int] = None):
+        """All routed experts stacked: gate/up [E,I,H], down [E,H,I] (stored dtype)."""
+        c = self.cfg
+        st = np.uint16 if c.dtype == "bf16" else np.float32
+        wg = np.empty((c.E, c.I, c.H), dtype=st)
+        wu = np.empty((c.E, c.I, c.H), dtype=st)
+        wd = np.empty((c.E, c.H, c.I), dtype=st)
+
+        def job(e):
+            g, u, d = self.expert(e)
+            wg[e], wu[e], wd[e] = g, u, d
+
+        with ThreadPoolExecutor(threads or _default_threads()) as ex:
+            list(ex.map(job, range(c.E)))
+        return wg, wu, wd
+
+    # ---- float64 views for the oracle ----
+    def x_f64(self) -> np.ndarray:
+        return to_f64(self.x(), self.cfg.dtype)
+
+    def expert_f64(self, e: int):
+        return tuple(to_f64(a, self.cfg.dtype) for a in self.expert(e))
+
+    def shared_f64(self):
+        s = self.shared()
+        return None if s is None else tuple(to_f64(a, self.cfg.dtype) for a in s)
+
+
+def make_inputs(cfg_id: int, seed: int = 0, T: Optional[int] = None) -> MoEInputs:
+    cfg = CONFIGS[cfg_id]
+    if T is not None:
+        cfg = cfg.with_T(T)
+    return MoEInputs(cfg, seed)
+
+
+def random_small(seed: int, T: int, H: int, E: int, K: int, I: int, I_shared: int,
+                 dtype: str = "f32", route_mode: int = ROUTE_SIGMOID_BIAS,
+                 scale: float = HY3_SCALE, renorm_eps: float = 0.0,
+                 bias_kind: str = "uniform") -> MoEInputs:
+    """A small ad-hoc workload with the same distributions (for property tests)."""
+    cfg = MoEConfig(f"small_{seed}", 900 + (seed % 97), 900 + seed, T=T, H=H, E=E, K=K,
+                    I=I, I_shared=I_shared, dtype=dtype, route_mode=route_mode,
+                    scale=scale, renorm_eps=renorm_eps, bias_kind=bias_kind)
+    return MoEInputs(cfg, seed)

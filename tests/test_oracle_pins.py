@@ -1,0 +1,330 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each pin is chosen so that a plausible mistake in the oracle fails it:
+
+* hand-worked fixtures in tests/golden (closed forms; the pages print no
+  numeric worked example of the layer);
+* brute force over every K-subset for the selection;
+* a loop-only, scalar re-derivation of the whole layer on tiny inputs;
+* the eager masked dispatch against dense evaluation of every expert;
+* invariants the pages' definitions imply (weight sums, bias-only-selects,
+  relabelling/permutation symmetry, special cases).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import CONFIGS, MoEInputs, random_small
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def expert_fn_from_list(lst):
+    return lambda e: (np.array(lst[e][0]), np.array(lst[e][1]), np.array(lst[e][2]))
+
+
+# ---------------------------------------------------------------- golden ----
+def test_golden_sigmoid_bias_route():
+    c = load("route_sigmoid_bias_hand.json")
+    r = oracle.route_from_logits(np.array(c["logits"]), c["K"], oracle.ROUTE_SIGMOID_BIAS,
+                                 np.array(c["bias"]), c["scale"])
+    assert r.idx.tolist() == c["idx"]
+    np.testing.assert_allclose(r.weight, c["weight"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r.margin, c["margin"], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("K", ["2", "3"])
+def test_golden_sigmoid_ties(K):
+    c = load("route_sigmoid_ties_hand.json")
+    e = c["by_K"][K]
+    r = oracle.route_from_logits(np.array(c["logits"]), int(K), oracle.ROUTE_SIGMOID_BIAS,
+                                 np.array(c["bias"]), c["scale"])
+    assert r.idx.tolist() == e["idx"]
+    np.testing.assert_allclose(r.weight, e["weight"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r.margin, e["margin"], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("K", ["2", "3"])
+def test_golden_softmax_route(K):
+    c = load("route_softmax_hand.json")
+    e = c["by_K"][K]
+    r = oracle.route_from_logits(np.array(c["logits"]), int(K), oracle.ROUTE_SOFTMAX,
+                                 None, 1.0, 1e-8)
+    assert r.idx.tolist() == e["idx"]
+    np.testing.assert_allclose(r.weight, e["weight"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r.margin, e["margin"], rtol=0, atol=1e-14)
+
+
+def test_golden_router_identity_weight_gives_logits():
+    c = load("route_sigmoid_bias_hand.json")
+    L = np.array(c["logits"])
+    np.testing.assert_array_equal(oracle.router_logits(L, np.eye(L.shape[1])), L)
+
+
+def test_golden_swiglu():
+    c = load("swiglu_hand.json")
+    out = oracle.swiglu_expert(np.array(c["a"]), np.array(c["w_gate"]),
+                               np.array(c["w_up"]), np.array(c["w_down"]))
+    np.testing.assert_allclose(out, c["out"], rtol=0, atol=1e-13)
+
+
+def test_golden_layer():
+    c = load("layer_hand.json")
+    ex = [(d["gate"], d["up"], d["down"]) for d in c["experts"]]
+    sh = tuple(np.array(c["shared"][k]) for k in ("gate", "up", "down"))
+    out, r = oracle.forward(np.array(c["x"]), np.array(c["w_router"]),
+                            expert_fn_from_list(ex), E=3, K=c["K"], shared=sh,
+                            mode=oracle.ROUTE_SIGMOID_BIAS, bias=np.array(c["bias"]),
+                            scale=c["scale"])
+    assert r.idx.tolist() == c["idx"]
+    np.testing.assert_allclose(r.weight, c["weight"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out, c["out"], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------ selection ----
+@pytest.mark.parametrize("seed", range(6))
+def test_selection_brute_force_all_subsets(seed):
+    """The picked set maximises the sum of selection scores over all K-subsets."""
+    rng = np.random.default_rng(seed)
+    T, E, K = 5, 7, 3
+    L = rng.normal(0, 1.5, (T, E))
+    bias = rng.uniform(-0.3, 0.3, E)
+    r = oracle.route_from_logits(L, K, oracle.ROUTE_SIGMOID_BIAS, bias, 2.826)
+    for t in range(T):
+        b = [1.0 / (1.0 + math.exp(-L[t, e])) + bias[e] for e in range(E)]
+        best = max(itertools.combinations(range(E), K), key=lambda S: sum(b[e] for e in S))
+        assert sorted(r.idx[t].tolist()) == sorted(best)
+        picked = [b[e] for e in r.idx[t]]
+        assert all(picked[i] >= picked[i + 1] for i in range(K - 1))
+        rest = sorted((b[e] for e in range(E) if e not in best), reverse=True)
+        assert abs(r.margin[t] - (min(picked) - rest[0])) < 1e-15
+
+
+def test_zero_bias_selects_top_logits():
+    """sigmoid is increasing, so with zero bias the picks are the top-K logits."""
+    rng = np.random.default_rng(1)
+    L = rng.normal(size=(50, 33))
+    r = oracle.route_from_logits(L, 6, oracle.ROUTE_SIGMOID_BIAS, np.zeros(33), 2.826)
+    expect = np.argsort(-L, axis=1)[:, :6]
+    np.testing.assert_array_equal(r.idx, expect)
+
+
+def test_large_bias_forces_selection():
+    rng = np.random.default_rng(2)
+    E, K = 24, 5
+    forced = [3, 7, 11, 19, 20]
+    bias = np.zeros(E)
+    bias[forced] = 10.0
+    r = oracle.route_from_logits(rng.normal(size=(40, E)), K, oracle.ROUTE_SIGMOID_BIAS,
+                                 bias, 2.826)
+    for t in range(40):
+        assert sorted(r.idx[t].tolist()) == forced
+
+
+def test_bias_selects_but_weights_are_unbiased():
+    rng = np.random.default_rng(3)
+    L = rng.normal(size=(64, 16))
+    bias = rng.uniform(-0.3, 0.3, 16)
+    r = oracle.route_from_logits(L, 4, oracle.ROUTE_SIGMOID_BIAS, bias, 2.826)
+    s = np.array([[1.0 / (1.0 + math.exp(-v)) for v in row] for row in L])
+    r0 = oracle.route_from_logits(L, 4, oracle.ROUTE_SIGMOID_BIAS, None, 2.826)
+    assert (np.sort(r.idx, 1) != np.sort(r0.idx, 1)).any(), "bias must change some picks"
+    for t in range(64):
+        sel = s[t, r.idx[t]]
+        np.testing.assert_allclose(r.weight[t], 2.826 * sel / sel.sum(), rtol=1e-14)
+    np.testing.assert_allclose(r.weight.sum(1), 2.826, rtol=0, atol=1e-12)
+
+
+def test_softmax_weights_sum_to_one_and_shift_invariant():
+    rng = np.random.default_rng(4)
+    L = rng.normal(size=(32, 64))
+    r = oracle.route_from_logits(L, 8, oracle.ROUTE_SOFTMAX, None, 1.0, 1e-8)
+    np.testing.assert_allclose(r.weight.sum(1), 1.0, rtol=0, atol=1e-14)
+    r2 = oracle.route_from_logits(L + rng.normal(size=(32, 1)) * 5, 8, oracle.ROUTE_SOFTMAX,
+                                  None, 1.0, 1e-8)
+    np.testing.assert_array_equal(r.idx, r2.idx)
+    np.testing.assert_allclose(r.weight, r2.weight, rtol=1e-12)
+    np.testing.assert_allclose(r.prob.sum(1), 1.0, atol=1e-14)
+
+
+def test_softmax_and_sigmoid_against_math():
+    z = np.array([-800.0, -30.0, -1.0, 0.0, 0.5, 30.0, 800.0])
+    expect = [0.0 if v < -700 else 1.0 / (1.0 + math.exp(-v)) for v in z]
+    np.testing.assert_allclose(oracle.sigmoid(z), expect, rtol=1e-15, atol=1e-300)
+    row = np.array([[1.0, 2.0, 3.0]])
+    den = math.exp(1) + math.exp(2) + math.exp(3)
+    np.testing.assert_allclose(oracle.softmax_rows(row),
+                               [[math.exp(1) / den, math.exp(2) / den, math.exp(3) / den]],
+                               rtol=1e-15)
+
+
+def test_logits_against_fsum():
+    inp = MoEInputs(CONFIGS[0])
+    x, w = inp.x_f64(), inp.w_router().astype(np.float64)
+    L = oracle.router_logits(x, w)
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        t, e = int(rng.integers(x.shape[0])), int(rng.integers(w.shape[0]))
+        ref = math.fsum(float(x[t, h]) * float(w[e, h]) for h in range(x.shape[1]))
+        assert abs(L[t, e] - ref) <= 1e-14 * max(1.0, abs(ref))
+
+
+# ---------------------------------------------------------- whole layer ----
+def _scalar_layer(x, wr, bias, experts, shared, K, scale):
+    """Loop-only statement of the layer, token by token, no numpy arithmetic."""
+    T, H = len(x), len(x[0])
+    E = len(wr)
+    outs = []
+    for t in range(T):
+        logit = [sum(x[t][h] * wr[e][h] for h in range(H)) for e in range(E)]
+        s = [1.0 / (1.0 + math.exp(-v)) for v in logit]
+        b = [s[e] + bias[e] for e in range(E)]
+        picks = sorted(range(E), key=lambda e: (-b[e], e))[:K]
+        tot = sum(s[e] for e in picks)
+        out = [0.0] * H
+        terms = [(e, scale * s[e] / tot) for e in picks] + [(None, 1.0)]
+        for e, w in terms:
+            wg, wu, wd = shared if e is None else experts[e]
+            I = len(wg)
+            g = [sum(wg[i][h] * x[t][h] for h in range(H)) for i in range(I)]
+            u = [sum(wu[i][h] * x[t][h] for h in range(H)) for i in range(I)]
+            hh = [g[i] / (1.0 + math.exp(-g[i])) * u[i] for i in range(I)]
+            for o in range(H):
+                out[o] += w * sum(wd[o][i] * hh[i] for i in range(I))
+        outs.append(out)
+    return outs
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_layer_matches_scalar_loops(seed):
+    inp = random_small(seed, T=4, H=6, E=5, K=2, I=3, I_shared=2)
+    c = inp.cfg
+    x = inp.x_f64()
+    wr = inp.w_router().astype(np.float64)
+    bias = inp.bias().astype(np.float64)
+    ex = [inp.expert_f64(e) for e in range(c.E)]
+    sh = inp.shared_f64()
+    out, _ = oracle.forward(x, wr, lambda e: ex[e], c.E, c.K, sh,
+                            oracle.ROUTE_SIGMOID_BIAS, bias, c.scale)
+    ref = _scalar_layer(x.tolist(), wr.tolist(), bias.tolist(),
+                        [tuple(a.tolist() for a in t) for t in ex],
+                        tuple(a.tolist() for a in sh), c.K, c.scale)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def _cfg0():
+    inp = MoEInputs(CONFIGS[0])
+    c = inp.cfg
+    ex = [inp.expert_f64(e) for e in range(c.E)]
+    return inp, c, inp.x_f64(), inp.w_router().astype(np.float64), \
+        inp.bias().astype(np.float64), ex, inp.shared_f64()
+
+
+def test_eager_equals_dense_masked_cfg0():
+    inp, c, x, wr, bias, ex, sh = _cfg0()
+    out, r = oracle.forward(x, wr, lambda e: ex[e], c.E, c.K, sh,
+                            oracle.ROUTE_SIGMOID_BIAS, bias, c.scale)
+    dense = oracle.dense_masked(x, r.idx, r.weight, lambda e: ex[e], c.E, sh)
+    np.testing.assert_allclose(out, dense, rtol=0, atol=1e-12)
+    assert np.abs(out).max() > 0.1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_eager_equals_dense_masked_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.integers(2, 9))
+    K = int(rng.integers(1, E + 1))
+    inp = random_small(seed, T=int(rng.integers(1, 12)), H=8, E=E, K=K, I=5, I_shared=4)
+    c = inp.cfg
+    ex = [inp.expert_f64(e) for e in range(E)]
+    x = inp.x_f64()
+    out, r = oracle.forward(x, inp.w_router().astype(np.float64), lambda e: ex[e], E, K,
+                            inp.shared_f64(), oracle.ROUTE_SIGMOID_BIAS,
+                            inp.bias().astype(np.float64), c.scale)
+    dense = oracle.dense_masked(x, r.idx, r.weight, lambda e: ex[e], E, inp.shared_f64())
+    np.testing.assert_allclose(out, dense, rtol=0, atol=1e-12)
+
+
+def test_softmax_layer_eager_equals_dense():
+    inp = random_small(7, T=9, H=8, E=6, K=3, I=5, I_shared=4, route_mode=1, scale=1.0,
+                       renorm_eps=1e-8, bias_kind="none")
+    c = inp.cfg
+    ex = [inp.expert_f64(e) for e in range(c.E)]
+    x = inp.x_f64()
+    out, r = oracle.forward(x, inp.w_router().astype(np.float64), lambda e: ex[e], c.E, c.K,
+                            inp.shared_f64(), oracle.ROUTE_SOFTMAX, None, 1.0, 1e-8)
+    dense = oracle.dense_masked(x, r.idx, r.weight, lambda e: ex[e], c.E, inp.shared_f64())
+    np.testing.assert_allclose(out, dense, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r.weight.sum(1), 1.0, atol=1e-14)
+
+
+def test_token_permutation_equivariance_and_duplicates():
+    inp, c, x, wr, bias, ex, sh = _cfg0()
+    perm = np.random.default_rng(6).permutation(c.T)
+    f = lambda e: ex[e]
+    out, _ = oracle.forward(x, wr, f, c.E, c.K, sh, 0, bias, c.scale)
+    out_p, _ = oracle.forward(x[perm], wr, f, c.E, c.K, sh, 0, bias, c.scale)
+    np.testing.assert_allclose(out_p, out[perm], rtol=0, atol=1e-13)
+    xd = np.concatenate([x, x[:3]])
+    out_d, _ = oracle.forward(xd, wr, f, c.E, c.K, sh, 0, bias, c.scale)
+    np.testing.assert_allclose(out_d[c.T:], out[:3], rtol=0, atol=1e-13)
+
+
+def test_expert_relabelling_invariance():
+    inp, c, x, wr, bias, ex, sh = _cfg0()
+    perm = np.random.default_rng(7).permutation(c.E)       # new expert i is old perm[i]
+    f = lambda e: ex[e]
+    out, r = oracle.forward(x, wr, f, c.E, c.K, sh, 0, bias, c.scale)
+    out2, r2 = oracle.forward(x, wr[perm], lambda e: ex[perm[e]], c.E, c.K, sh, 0,
+                              bias[perm], c.scale)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(np.sort(perm[r2.idx], 1), np.sort(r.idx, 1))
+
+
+def test_k_equals_E_makes_bias_irrelevant():
+    inp = random_small(11, T=6, H=8, E=5, K=5, I=4, I_shared=3)
+    c = inp.cfg
+    ex = [inp.expert_f64(e) for e in range(c.E)]
+    x, wr = inp.x_f64(), inp.w_router().astype(np.float64)
+    o1, r1 = oracle.forward(x, wr, lambda e: ex[e], c.E, c.K, inp.shared_f64(), 0,
+                            inp.bias().astype(np.float64), c.scale)
+    o2, _ = oracle.forward(x, wr, lambda e: ex[e], c.E, c.K, inp.shared_f64(), 0,
+                           np.linspace(-1, 1, c.E), c.scale)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    assert np.isinf(r1.margin).all()
+
+
+def test_zero_down_weights_leave_only_shared():
+    inp, c, x, wr, bias, ex, sh = _cfg0()
+    zero = [(g, u, np.zeros_like(d)) for g, u, d in ex]
+    out, _ = oracle.forward(x, wr, lambda e: zero[e], c.E, c.K, sh, 0, bias, c.scale)
+    np.testing.assert_allclose(out, oracle.swiglu_expert(x, *sh), rtol=0, atol=0)
+
+
+def test_no_shared_expert():
+    inp, c, x, wr, bias, ex, sh = _cfg0()
+    f = lambda e: ex[e]
+    with_sh, r = oracle.forward(x, wr, f, c.E, c.K, sh, 0, bias, c.scale)
+    without, _ = oracle.forward(x, wr, f, c.E, c.K, None, 0, bias, c.scale)
+    np.testing.assert_allclose(with_sh - without, oracle.swiglu_expert(x, *sh), atol=1e-13)
+
+
+def test_empty_token_batch():
+    inp, c, x, wr, bias, ex, sh = _cfg0()
+    out, r = oracle.forward(x[:0], wr, lambda e: ex[e], c.E, c.K, sh, 0, bias, c.scale)
+    assert out.shape == (0, c.H) and r.idx.shape == (0, c.K)
+
+
+def test_flop_count():
+    f = oracle.layer_flops(T=8192, H=4096, E=192, K=8, I=1536, I_shared=1536)
+    assert abs(f["experts"] - 2.783e12) / 2.783e12 < 1e-3

@@ -1,0 +1,81 @@
+"""The seeded input generator: determinism, distributions, bf16 rounding."""
+import numpy as np
+import pytest
+import torch
+
+from synth import (CONFIGS, MoEInputs, bf16_bits_to_f32, f32_to_bf16_bits,
+                   make_inputs, random_small)
+
+
+def test_bf16_rne_matches_torch():
+    """torch's float32 -> bfloat16 cast is an independent round-to-nearest-even."""
+    rng = np.random.default_rng(0)
+    a = np.concatenate([rng.normal(size=100000).astype(np.float32),
+                        np.array([1.0, -2.5, 3.0039062, 1.00390625, 1.01171875,
+                                  65504.0, 1e-30, -0.0], dtype=np.float32)])
+    mine = f32_to_bf16_bits(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(mine, ref)
+    back = bf16_bits_to_f32(mine)
+    np.testing.assert_array_equal(back, torch.from_numpy(a).to(torch.bfloat16).float().numpy())
+
+
+def test_ties_round_to_even():
+    # 1 + 2^-8 is exactly halfway between bf16 neighbours 1 and 1 + 2^-7.
+    a = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8], dtype=np.float32)
+    np.testing.assert_array_equal(bf16_bits_to_f32(f32_to_bf16_bits(a)),
+                                  np.array([1.0, 1.0 + 2.0 ** -6], dtype=np.float32))
+
+
+def test_determinism_and_independence():
+    a, b = make_inputs(0), make_inputs(0)
+    np.testing.assert_array_equal(a.x(), b.x())
+    np.testing.assert_array_equal(a.expert(3)[0], b.expert(3)[0])
+    assert not np.array_equal(a.expert(3)[0], a.expert(4)[0])
+    assert not np.array_equal(make_inputs(0, seed=1).x(), a.x())
+
+
+def test_decode_and_prefill_share_weights_not_data():
+    d = MoEInputs(CONFIGS[1].with_(T=4, H=64, I=32, I_shared=32))
+    p = MoEInputs(CONFIGS[2].with_(T=4, H=64, I=32, I_shared=32))
+    np.testing.assert_array_equal(d.w_router(), p.w_router())
+    np.testing.assert_array_equal(d.expert(5)[2], p.expert(5)[2])
+    assert not np.array_equal(d.x(), p.x())
+
+
+def test_distributions_cfg0():
+    inp = make_inputs(0)
+    c = inp.cfg
+    x = inp.x()
+    assert x.dtype == np.float32 and x.shape == (c.T, c.H)
+    assert abs(x.std() - 1.0) < 0.05
+    wr = inp.w_router()
+    assert wr.shape == (c.E, c.H) and abs(wr.std() - 0.02) < 0.002
+    b = inp.bias()
+    assert b.shape == (c.E,) and b.min() >= -0.1 and b.max() <= 0.1
+    g, u, d = inp.expert(0)
+    assert g.shape == (c.I, c.H) and d.shape == (c.H, c.I)
+    assert abs(g.std() - 1 / np.sqrt(c.H)) < 0.1 / np.sqrt(c.H)
+    assert abs(d.std() - 1 / np.sqrt(c.I)) < 0.1 / np.sqrt(c.I)
+
+
+def test_skew_bias_and_softmax_have_expected_kinds():
+    p = MoEInputs(CONFIGS[2].with_(T=2, H=64, I=32, I_shared=32))
+    b = p.bias()
+    assert abs(b.std() - 0.3) < 0.1
+    s = MoEInputs(CONFIGS[4].with_(T=2, H=64, I=32, I_shared=32))
+    assert s.bias() is None and s.cfg.route_mode == 1
+
+
+def test_bf16_storage_and_stack():
+    inp = random_small(1, T=3, H=16, E=3, K=2, I=8, I_shared=8, dtype="bf16")
+    assert inp.x().dtype == np.uint16
+    wg, wu, wd = inp.stacked_experts(threads=2)
+    assert wg.shape == (3, 8, 16) and wd.shape == (3, 16, 8)
+    np.testing.assert_array_equal(wg[2], inp.expert(2)[0])
+
+
+@pytest.mark.parametrize("cfg_id", sorted(CONFIGS))
+def test_config_shapes(cfg_id):
+    c = CONFIGS[cfg_id]
+    assert 1 <= c.K <= c.E and c.H % 8 == 0 and c.I % 8 == 0
