@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the Hy3-style MoE FFN layer on one MI355X.
+
+One step = one hy3moe_forward (router GEMM, score + top-K select,
+permutation, grouped gate-up + SwiGLU, grouped down, weighted combine) over
+one batch of seeded synthetic input already resident in HBM.
+
+Default workload: Hy3 decode, T=16 tokens, H=4096, 192 routed experts
+(top-8) + 1 shared expert, I=1536, bf16 weights/activations, fp32 router.
+`--workload prefill` (T=8192, skewed bias) and `--workload softmax`
+(HunyuanImage-3.0 softmax routing, T=32768, E=64) run the other layer shapes.
+
+Printed: one JSON line with tokens/s, the dominant kernel's roofline fraction
+(its per-launch duration measured live with HIP events on the library's
+stream, via hy3moe_forward_timed), the whole-layer fractions, and the CPU
+oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4}
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
+METRIC = "Hy3 MoE layer tokens/s; % bf16 MFMA peak (prefill) / % HBM BW (decode)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when the
+    kernel sources changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_sources_sha") != kernel_sources_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens in the CPU oracle sample (default: 16 decode, 48 otherwise)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the run, copy this many MiB device-to-device (PMC calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
+              "(sharding is described in DESIGN.md).  Run with --gpus 1.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_moe_amd as sm
+    from synth import CONFIGS, MoEInputs
+    from synth.device import to_torch, upload_weights
+
+    dev = torch.device("cuda:0")
+    sm.load()
+    inp = MoEInputs(CONFIGS[WORKLOADS[args.workload]])
+    c = inp.cfg
+    t0 = time.time()
+    weights = upload_weights(inp, dev)
+    x = to_torch(inp.x(), c.dtype, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {c.name}: inputs uploaded in {time.time() - t0:.1f}s")
+    cfg = sm.make_config(c.T, c.H, c.E, c.K, c.I, c.I_shared, c.dtype, c.route_mode,
+                         scale=c.scale, renorm_eps=c.renorm_eps)
+    ws = sm.alloc_workspace(cfg, True, dev)
+    out = torch.empty_like(x)
+    idx = torch.empty((c.T, c.K), dtype=torch.int32, device=dev)
+    wgt = torch.empty((c.T, c.K), dtype=torch.float32, device=dev)
+
+    # Route of this batch (outside the timed region) for the byte/FLOP counts.
+    sm.hy3moe_forward(cfg, x, weights, out, ws, idx, wgt)
+    torch.cuda.synchronize()
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=c.E)
+    U = int((counts > 0).sum())
+
+    for _ in range(args.warmup):
+        sm.hy3moe_forward(cfg, x, weights, out, ws)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, synchronised on both sides ----
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        sm.hy3moe_forward(cfg, x, weights, out, ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    # ---- per-stage durations: HIP events recorded between the kernels ----
+    n_ev = sm.HY3MOE_N_STAGES + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for row in evs:
+        sm.hy3moe_forward_timed(cfg, x, weights, out, ws, row)
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs]))
+                for i, name in enumerate(sm.STAGE_NAMES)}
+    log("[bench] stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+
+    # ---- algorithmic work ----
+    eb = 2 if c.dtype == "bf16" else 4
+    T, H, E, K, I, Is = c.T, c.H, c.E, c.K, c.I, c.I_shared
+    R = T * K + (T if Is else 0)
+    groups = U + (1 if Is else 0)
+    gu_weight_bytes = U * 2 * I * H * eb + (2 * Is * H * eb if Is else 0)
+    dn_weight_bytes = U * H * I * eb + (H * Is * eb if Is else 0)
+    gu_bytes = gu_weight_bytes + T * H * eb + R * I * eb
+    dn_bytes = dn_weight_bytes + R * I * eb + R * H * eb
+    layer_bytes = gu_weight_bytes + dn_weight_bytes + E * H * 4 + 2 * T * H * eb
+    gu_flops = 4.0 * H * (T * K * I + (T * Is if Is else 0))
+    dn_flops = 2.0 * H * (T * K * I + (T * Is if Is else 0))
+    layer_flops = 1.5 * gu_flops + 2.0 * T * H * E
+    layer_s = ms_per_step / 1e3
+    gu_s = stage_ms["gate_up"] / 1e3
+    decode = args.workload == "decode"
+    if decode:
+        roof = {"kernel": "gate_up (weight-streaming grouped GEMM + SwiGLU)", "bound": "hbm",
+                "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "per_unit": f"{2 * I * H * eb} B of gate+up weights per touched expert "
+                            f"x {groups} experts + x and h rows"}
+    else:
+        roof = {"kernel": "gate_up (tiled grouped GEMM + SwiGLU)", "bound": "mfma",
+                "achieved": gu_flops / gu_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "per_unit": f"{4 * H * I} FLOP per routed row x {T * K} rows + "
+                            f"{4 * H * Is} per shared row x {T}"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    tr = measured_traffic(args.workload, "gate_up")
+    roof["traffic"] = tr
+    roof["avg_launch_ms"] = stage_ms["gate_up"]
+
+    layer = {
+        "unique_experts": U, "max_load": int(counts.max()),
+        "stage_ms": stage_ms,
+        "bytes": layer_bytes, "GB_s": layer_bytes / layer_s / 1e9,
+        "hbm_frac": layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS,
+        "flops": layer_flops, "TFLOP_s": layer_flops / layer_s / 1e12,
+        "mfma_frac": layer_flops / layer_s / 1e12 / PEAK_BF16_TFLOPS,
+        "down_achieved": (dn_bytes / (stage_ms["down"] / 1e3) / 1e9 if decode
+                          else dn_flops / (stage_ms["down"] / 1e3) / 1e12),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args, idx.cpu().numpy())
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC, "value": T / layer_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c.dtype,
+        "data": "synthetic (seeded, random-init weights of the layer's shapes)",
+        "config": {"workload": c.name, "T": T, "H": H, "E": E, "K": K, "I": I, "I_shared": Is,
+                   "route": "sigmoid+bias" if c.route_mode == 0 else "softmax"},
+        "roofline": roof, "cpu_baseline": cpu, "layer": layer,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(inp, args, gpu_idx):
+    """The float64 oracle, as it stands, on a bounded sample of the same batch."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [d.get("num_threads") for d in threadpool_info() if d.get("user_api") == "blas"]
+        cores = int(blas[0]) if blas else os.cpu_count()
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    c = inp.cfg
+    n = args.cpu_sample_tokens or (16 if args.workload == "decode" else 48)
+    n = min(n, c.T)
+    tokens = np.arange(n)
+    x64 = inp.x_f64()[tokens]
+    wr = inp.w_router().astype(np.float64)
+    b = inp.bias()
+    b64 = None if b is None else b.astype(np.float64)
+    need = sorted(set(gpu_idx[tokens].reshape(-1).tolist()))
+    t0 = time.time()
+    with ThreadPoolExecutor(8) as ex:
+        ws = dict(zip(need, ex.map(inp.expert_f64, need)))
+    sh = inp.shared_f64()
+    log(f"[bench] oracle sample: {n} tokens, {len(need)} experts in float64 "
+        f"(generated in {time.time() - t0:.1f}s)")
+    t1 = time.perf_counter()
+    r = oracle.route(x64, wr, c.K, c.route_mode, b64, c.scale, c.renorm_eps)
+    dt = time.perf_counter() - t1
+    # Experts the oracle picks that the GPU did not (near-ties): input preparation,
+    # kept out of the oracle's time.
+    for e in sorted(set(r.idx.reshape(-1).tolist()) - set(ws)):
+        ws[e] = inp.expert_f64(e)
+    t2 = time.perf_counter()
+    oracle.forward_given_route(x64, r.idx, r.weight, ws.__getitem__, c.E, sh)
+    dt += time.perf_counter() - t2
+    del ws
+    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of the {c.T} tokens of the same batch (route over them, "
+                      f"{len(need)} experts + shared, float64 numpy), {dt:.2f}s"}
+
+
+if __name__ == "__main__":
+    main()

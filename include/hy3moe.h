@@ -1,0 +1,190 @@
+/*
+ * hy3moe.h -- C ABI of the MI355X (gfx950) Hy3-style sparse MoE FFN layer.
+ *
+ * The layer (hy3 README "Model facts": 192 routed experts, top-8, one shared
+ * expert that is always active, expert intermediate 1536, hidden 4096):
+ *
+ *   logits = x W_r^T                      bias-free router linear, fp32-accurate
+ *   s      = sigmoid(logits)              (HYV3Config moe_router_use_sigmoid)
+ *   pick   = top-K of s + expert_bias     bias steers the choice only
+ *   w      = scale * s[pick] / sum s[pick]   unbiased, renormalised, x2.826
+ *   out    = shared(x) + sum_j w_j * expert_{pick_j}(x)
+ *   expert(a) = W_down ( silu(W_gate a) * (W_up a) )     SwiGLU
+ *
+ * and the HunyuanImage-3.0 softmax variant (HunyuanImage 3.0 MoE reading,
+ * easy_topk): p = softmax(logits); pick = top-K of p;
+ * w = p[pick] / max(sum p[pick], renorm_eps); no bias, no scale.
+ *
+ * Everything runs as hand-written HIP kernels on the caller's stream.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - All tensor pointers are DEVICE memory owned by the caller, row-major,
+ *    dense, and 16-byte aligned.  The library allocates nothing and keeps no
+ *    state between calls.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; the call returns after enqueueing.  Calls on different
+ *    streams are safe when each has its own workspace; calls sharing one
+ *    workspace must be ordered by the caller.
+ *  - Validation happens before anything is enqueued: on a non-zero return
+ *    nothing has been launched.  Faults during kernel execution surface at
+ *    the caller's next synchronisation on the stream.
+ *  - T == 0 is a successful no-op.  Non-finite inputs are undefined.
+ *  - Element types: HY3MOE_BF16 means bfloat16 (1-8-7 bits) for x, out and
+ *    all expert weights; HY3MOE_F32 means float32 for them.  The router
+ *    weight, the expert bias and the combine weights are always float32.
+ */
+#ifndef HY3MOE_H
+#define HY3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---- */
+#define HY3MOE_OK               0
+#define HY3MOE_ERR_INVALID     -1  /* null pointer, T<0, K<1, K>E, E>256, K>64, bad enum */
+#define HY3MOE_ERR_UNSUPPORTED -2  /* H, I or I_shared not a multiple of 64; T > 2^24;
+                                      H, I or I_shared > 65536; split router with fp32 x */
+#define HY3MOE_ERR_WORKSPACE   -3  /* workspace smaller than hy3moe_workspace_bytes()   */
+#define HY3MOE_ERR_ALIGN       -4  /* a pointer is not 16-byte aligned                  */
+#define HY3MOE_ERR_HIP         -5  /* a kernel launch failed (hipGetLastError)          */
+
+/* ---- enums ---- */
+#define HY3MOE_F32  0
+#define HY3MOE_BF16 1
+
+#define HY3MOE_ROUTE_SIGMOID_BIAS 0  /* Hy3: sigmoid, biased top-K, unbiased renorm x scale */
+#define HY3MOE_ROUTE_SOFTMAX      1  /* HunyuanImage-3.0 easy_topk: softmax, top-K, clamp  */
+
+/* Router arithmetic.  FP32: logits exact to fp32 accumulation (the fp32 weight
+ * is split on the fly into three bf16 terms whose sum is the weight exactly,
+ * each term runs on bf16 MFMA with fp32 accumulation; fp32 activations use
+ * fp32 MFMA).  SPLIT2_BF16: the two-term approximation W ~ W_hi + W_lo/256
+ * with two accumulators and one fused multiply-add in the epilogue (Hy3
+ * Preview inference case, section 2 "Router GEMM"); bf16 activations only. */
+#define HY3MOE_ROUTER_FP32        0
+#define HY3MOE_ROUTER_SPLIT2_BF16 1
+
+/* Shape and mode of one layer call. */
+typedef struct hy3moe_config {
+  int64_t T;          /* tokens (rows of x)                                   */
+  int32_t H;          /* hidden size                                          */
+  int32_t E;          /* routed experts, 1..256                               */
+  int32_t K;          /* experts per token, 1..min(E,64)                      */
+  int32_t I;          /* routed expert intermediate size                      */
+  int32_t I_shared;   /* shared expert intermediate size; 0 = no shared expert */
+  int32_t dtype;      /* HY3MOE_BF16 or HY3MOE_F32 (x, out, expert weights)   */
+  int32_t route_mode; /* HY3MOE_ROUTE_*                                       */
+  int32_t router_prec;/* HY3MOE_ROUTER_*                                      */
+  float   scale;      /* routed-weight scale: 2.826 for Hy3, 1 for softmax    */
+  float   renorm_eps; /* softmax mode: clamp of the top-K sum (1e-8); sigmoid mode: unused */
+} hy3moe_config;
+
+/* Weights.  Layouts follow nn.Linear [out, in] (K-contiguous rows), stacked
+ * over experts (HunyuanImage 3.0 MoE reading, stacked moe_weight/moe_weight_2):
+ *   w_router  [E, H]     fp32
+ *   expert_bias [E]      fp32, sigmoid mode only; NULL means all zero
+ *   w_gate, w_up [E, I, H]      dtype
+ *   w_down       [E, H, I]      dtype
+ *   ws_gate, ws_up [I_shared, H], ws_down [H, I_shared]  dtype (NULL if I_shared==0) */
+typedef struct hy3moe_weights {
+  const float *w_router;
+  const float *expert_bias;
+  const void  *w_gate;
+  const void  *w_up;
+  const void  *w_down;
+  const void  *ws_gate;
+  const void  *ws_up;
+  const void  *ws_down;
+} hy3moe_weights;
+
+/* Byte offsets of the intermediate buffers inside a forward workspace (for
+ * inspection by tests; all offsets are from the workspace base and 256-byte
+ * aligned).  Groups 0..E-1 are the routed experts, group E the shared expert.
+ * Rows are "expert-major": group g owns rows [offsets[g], offsets[g+1]).      */
+typedef struct hy3moe_ws_layout {
+  size_t total;          /* == hy3moe_workspace_bytes(cfg, 1)                  */
+  size_t logits_part;    /* double [S][T][E] router K-slice partial sums (S = n_ksplit) */
+  int32_t n_ksplit;
+  size_t idx;            /* int32 [T][K]  (used when the caller passes no idx_out)    */
+  size_t weight;         /* float [T][K]  (used when the caller passes no weight_out) */
+  size_t counts;         /* int32 [E+1]   rows per group (counts[E] = T or 0)   */
+  size_t offsets;        /* int32 [E+2]   exclusive prefix of counts            */
+  size_t sorted_token;   /* int32 [R]     token of each expert-major row, R = T*K + T_shared */
+  size_t pos_of;         /* int32 [T][K]  expert-major row of (token, pick)     */
+  size_t hist;           /* int32 [n_chunks][E] per-chunk expert counts / prefixes */
+  int32_t n_chunks;      /* (token, pick) chunks of the permutation             */
+  size_t tiles;          /* int32 [2*max_tiles] (group, first row) per row tile, then n_tiles */
+  int32_t max_tiles;
+  int32_t tile_rows;     /* rows per tile of the expert GEMMs for this T       */
+  size_t h;              /* dtype [R][I_max]  SwiGLU activations, I_max = max(I, I_shared) */
+  size_t y;              /* dtype [R][H]      expert outputs before the combine */
+} hy3moe_ws_layout;
+
+/* Workspace size in bytes for hy3moe_forward (for_forward != 0) or for
+ * hy3moe_route (for_forward == 0).  Returns 0 if cfg is invalid. */
+size_t hy3moe_workspace_bytes(const hy3moe_config *cfg, int for_forward);
+
+/* Fill *out with the forward workspace layout.  Returns HY3MOE_OK or an error. */
+int hy3moe_workspace_layout(const hy3moe_config *cfg, hy3moe_ws_layout *out);
+
+/* The gate: router GEMM, scoring and top-K selection.
+ *   x        [T, H] dtype
+ *   w_router [E, H] fp32;  expert_bias [E] fp32 (sigmoid mode; NULL = zero)
+ *   idx      [T, K] int32 out: picked experts in descending selection score,
+ *            equal scores ordered by ascending expert index
+ *   weight   [T, K] fp32 out: combine weights (sum to `scale` per token in
+ *            sigmoid mode, to 1 in softmax mode)
+ *   workspace: hy3moe_workspace_bytes(cfg, 0) bytes.
+ * Follows the hy3 README "Model facts" MoE routing row and the HunyuanImage
+ * 3.0 MoE reading's HunyuanTopKGate (easy_topk). */
+int hy3moe_route(const hy3moe_config *cfg, const void *x, const float *w_router,
+                 const float *expert_bias, int32_t *idx, float *weight,
+                 void *workspace, size_t ws_bytes, void *stream);
+
+/* The whole layer: gate, token->expert permutation, grouped SwiGLU experts
+ * (routed + shared), and the weighted top-K combine back to token order.
+ *   x   [T, H] dtype;   out [T, H] dtype (may not alias x)
+ *   idx_out [T, K] int32, weight_out [T, K] fp32: optional (NULL allowed)
+ *       copies of the route this call used
+ *   workspace: hy3moe_workspace_bytes(cfg, 1) bytes.
+ * The steps follow the FusedMoE chain of the Hy3 Preview inference case
+ * (section 3: routing/index preprocessing with a contiguous row range per
+ * expert, gate-up GEMM reading x through the route index, down GEMM written
+ * compactly per expert, top-K weighted aggregation at the end) and the
+ * shared/routed sum of the HunyuanImage 3.0 MoE reading ("Shared MLP"). */
+int hy3moe_forward(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
+                   void *out, int32_t *idx_out, float *weight_out,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/* Stages of hy3moe_forward, in launch order: router GEMM, score+select,
+ * permutation (histogram, scan + tile list, scatter), gate-up + SwiGLU,
+ * down, combine. */
+#define HY3MOE_N_STAGES 6
+
+/* hy3moe_forward that also records HY3MOE_N_STAGES + 1 caller-created HIP
+ * events (hipEvent_t handles, passed as void*) on `stream`: stage_events[0]
+ * before the first kernel and stage_events[i + 1] after stage i, so that
+ * hipEventElapsedTime between consecutive events gives each stage's duration
+ * on the stream the kernels run on.  Used for per-kernel timing; results are
+ * identical to hy3moe_forward.  Returns HY3MOE_ERR_INVALID if any event is
+ * NULL; otherwise as hy3moe_forward. */
+int hy3moe_forward_timed(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
+                         void *out, int32_t *idx_out, float *weight_out,
+                         void *workspace, size_t ws_bytes, void *stream,
+                         void *const *stage_events);
+
+/* Human-readable text of a return code (static storage). */
+const char *hy3moe_strerror(int code);
+
+/* Library ABI version (increments on any change of the structs above). */
+int hy3moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HY3MOE_H */

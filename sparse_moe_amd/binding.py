@@ -1,0 +1,238 @@
+"""Thin ctypes binding of libhy3moe.so (argument marshalling only).
+
+Every step of the layer runs in the library's HIP kernels.  PyTorch supplies
+device memory (``tensor.data_ptr()``) and the current HIP stream; nothing
+here computes any part of the layer, and there is no fallback: if the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch  # noqa: F401  (loads the HIP runtime the library then shares)
+
+from .build import LIB_PATH
+
+HY3MOE_OK = 0
+HY3MOE_F32 = 0
+HY3MOE_BF16 = 1
+HY3MOE_ROUTE_SIGMOID_BIAS = 0
+HY3MOE_ROUTE_SOFTMAX = 1
+HY3MOE_ROUTER_FP32 = 0
+HY3MOE_ROUTER_SPLIT2_BF16 = 1
+
+HY3MOE_N_STAGES = 6
+STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
+
+EXPORTED_SYMBOLS = (
+    "hy3moe_abi_version", "hy3moe_strerror", "hy3moe_workspace_bytes",
+    "hy3moe_workspace_layout", "hy3moe_route", "hy3moe_forward", "hy3moe_forward_timed",
+)
+
+
+class hy3moe_config(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+        ("K", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("route_mode", ctypes.c_int32),
+        ("router_prec", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("renorm_eps", ctypes.c_float),
+    ]
+
+
+class hy3moe_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
+
+
+class hy3moe_ws_layout(ctypes.Structure):
+    _fields_ = [
+        ("total", ctypes.c_size_t), ("logits_part", ctypes.c_size_t),
+        ("n_ksplit", ctypes.c_int32), ("idx", ctypes.c_size_t), ("weight", ctypes.c_size_t),
+        ("counts", ctypes.c_size_t), ("offsets", ctypes.c_size_t),
+        ("sorted_token", ctypes.c_size_t), ("pos_of", ctypes.c_size_t),
+        ("hist", ctypes.c_size_t), ("n_chunks", ctypes.c_int32),
+        ("tiles", ctypes.c_size_t), ("max_tiles", ctypes.c_int32),
+        ("tile_rows", ctypes.c_int32), ("h", ctypes.c_size_t), ("y", ctypes.c_size_t),
+    ]
+
+
+class Hy3MoEError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what} failed: {code} ({strerror(code)})")
+        self.code = code
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib_path() -> str:
+    return os.environ.get("HY3MOE_LIB", LIB_PATH)
+
+
+def load() -> ctypes.CDLL:
+    """Load libhy3moe.so (built in-tree); raises if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    p = lib_path()
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"HIP MoE library not found at {p}; build it with `python -m sparse_moe_amd.build` "
+            "(or __graft_entry__.build()).  There is no fallback path.")
+    L = ctypes.CDLL(p)
+    L.hy3moe_abi_version.restype = ctypes.c_int
+    L.hy3moe_strerror.restype = ctypes.c_char_p
+    L.hy3moe_strerror.argtypes = [ctypes.c_int]
+    L.hy3moe_workspace_bytes.restype = ctypes.c_size_t
+    L.hy3moe_workspace_bytes.argtypes = [ctypes.POINTER(hy3moe_config), ctypes.c_int]
+    L.hy3moe_workspace_layout.restype = ctypes.c_int
+    L.hy3moe_workspace_layout.argtypes = [ctypes.POINTER(hy3moe_config),
+                                          ctypes.POINTER(hy3moe_ws_layout)]
+    L.hy3moe_route.restype = ctypes.c_int
+    L.hy3moe_route.argtypes = [ctypes.POINTER(hy3moe_config), ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.hy3moe_forward.restype = ctypes.c_int
+    L.hy3moe_forward.argtypes = [ctypes.POINTER(hy3moe_config), ctypes.c_void_p,
+                                 ctypes.POINTER(hy3moe_weights), ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_size_t, ctypes.c_void_p]
+    L.hy3moe_forward_timed.restype = ctypes.c_int
+    L.hy3moe_forward_timed.argtypes = [ctypes.POINTER(hy3moe_config), ctypes.c_void_p,
+                                       ctypes.POINTER(hy3moe_weights), ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_void_p)]
+    if L.hy3moe_abi_version() != 1:
+        raise RuntimeError("libhy3moe ABI version mismatch")
+    _LIB = L
+    return L
+
+
+def strerror(code: int) -> str:
+    return load().hy3moe_strerror(int(code)).decode()
+
+
+def make_config(T: int, H: int, E: int, K: int, I: int, I_shared: int, dtype: str = "bf16",
+                route_mode: int = HY3MOE_ROUTE_SIGMOID_BIAS,
+                router_prec: int = HY3MOE_ROUTER_FP32, scale: float = 2.826,
+                renorm_eps: float = 1e-8) -> hy3moe_config:
+    return hy3moe_config(T=int(T), H=int(H), E=int(E), K=int(K), I=int(I),
+                         I_shared=int(I_shared),
+                         dtype=HY3MOE_BF16 if dtype == "bf16" else HY3MOE_F32,
+                         route_mode=int(route_mode), router_prec=int(router_prec),
+                         scale=float(scale), renorm_eps=float(renorm_eps))
+
+
+def hy3moe_workspace_bytes(cfg: hy3moe_config, for_forward: bool = True) -> int:
+    return int(load().hy3moe_workspace_bytes(ctypes.byref(cfg), 1 if for_forward else 0))
+
+
+def hy3moe_workspace_layout(cfg: hy3moe_config) -> hy3moe_ws_layout:
+    out = hy3moe_ws_layout()
+    rc = load().hy3moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(out))
+    if rc != HY3MOE_OK:
+        raise Hy3MoEError(rc, "hy3moe_workspace_layout")
+    return out
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+
+
+def alloc_workspace(cfg: hy3moe_config, for_forward: bool, device) -> torch.Tensor:
+    n = hy3moe_workspace_bytes(cfg, for_forward)
+    if n == 0:
+        raise Hy3MoEError(-1, "hy3moe_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def hy3moe_route(cfg: hy3moe_config, x: torch.Tensor, w_router: torch.Tensor,
+                 expert_bias: Optional[torch.Tensor], idx: torch.Tensor, weight: torch.Tensor,
+                 workspace: torch.Tensor, stream=None) -> None:
+    """C ABI hy3moe_route on torch device tensors (results in idx/weight)."""
+    _check_dev(x, w_router, expert_bias, idx, weight, workspace)
+    rc = load().hy3moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(expert_bias),
+                             _ptr(idx), _ptr(weight), _ptr(workspace), workspace.numel(),
+                             _stream(stream))
+    if rc != HY3MOE_OK:
+        raise Hy3MoEError(rc, "hy3moe_route")
+
+
+def hy3moe_forward(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str, torch.Tensor],
+                   out: torch.Tensor, workspace: torch.Tensor,
+                   idx_out: Optional[torch.Tensor] = None,
+                   weight_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """C ABI hy3moe_forward on torch device tensors (result in out)."""
+    names = ("w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+    ts = [weights.get(n) for n in names]
+    _check_dev(x, out, workspace, idx_out, weight_out, *ts)
+    w = hy3moe_weights(*[_ptr(t) for t in ts])
+    rc = load().hy3moe_forward(ctypes.byref(cfg), _ptr(x), ctypes.byref(w), _ptr(out),
+                               _ptr(idx_out), _ptr(weight_out), _ptr(workspace),
+                               workspace.numel(), _stream(stream))
+    if rc != HY3MOE_OK:
+        raise Hy3MoEError(rc, "hy3moe_forward")
+
+
+def hy3moe_forward_timed(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str, torch.Tensor],
+                         out: torch.Tensor, workspace: torch.Tensor, events,
+                         idx_out: Optional[torch.Tensor] = None,
+                         weight_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """C ABI hy3moe_forward_timed; ``events`` are HY3MOE_N_STAGES + 1 torch.cuda.Event
+    objects created with enable_timing=True (already recorded once, so that their
+    HIP handles exist)."""
+    names = ("w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+    ts = [weights.get(n) for n in names]
+    _check_dev(x, out, workspace, idx_out, weight_out, *ts)
+    if len(events) != HY3MOE_N_STAGES + 1:
+        raise ValueError("need HY3MOE_N_STAGES + 1 events")
+    w = hy3moe_weights(*[_ptr(t) for t in ts])
+    evs = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    rc = load().hy3moe_forward_timed(ctypes.byref(cfg), _ptr(x), ctypes.byref(w), _ptr(out),
+                                     _ptr(idx_out), _ptr(weight_out), _ptr(workspace),
+                                     workspace.numel(), _stream(stream), evs)
+    if rc != HY3MOE_OK:
+        raise Hy3MoEError(rc, "hy3moe_forward_timed")
+
+
+# Convenience wrappers that allocate outputs (tests and benchmark).
+def route(cfg: hy3moe_config, x, w_router, expert_bias=None, workspace=None,
+          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    T, K = int(cfg.T), int(cfg.K)
+    idx = torch.empty((T, K), dtype=torch.int32, device=x.device)
+    weight = torch.empty((T, K), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, False, x.device)
+    hy3moe_route(cfg, x, w_router, expert_bias, idx, weight, workspace, stream)
+    return idx, weight
+
+
+def forward(cfg: hy3moe_config, x, weights, workspace=None, return_route=False, stream=None):
+    out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, True, x.device)
+    idx = weight = None
+    if return_route:
+        idx = torch.empty((int(cfg.T), int(cfg.K)), dtype=torch.int32, device=x.device)
+        weight = torch.empty((int(cfg.T), int(cfg.K)), dtype=torch.float32, device=x.device)
+    hy3moe_forward(cfg, x, weights, out, workspace, idx, weight, stream)
+    return (out, idx, weight) if return_route else out

@@ -1,0 +1,101 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+//
+// MFMA operand convention used by every kernel here
+// -------------------------------------------------
+// Each lane of a 64-wide wavefront supplies one 16-byte "chunk" of an A row
+// and one of a B row.  Lane l = 16*g + r supplies chunk g (bytes 16g..16g+15
+// of a 64-byte K segment) of row r.  One call of Mma<T>::step() adds
+//     D[m][n] += sum_{g, i} A_chunk(row m, chunk g)[i] * B_chunk(row n, chunk g)[i]
+// i.e. the dot product of row m of A with row n of B over a 64-byte K slab
+// (32 bf16 or 16 fp32 values).  bf16 uses one v_mfma_f32_16x16x32_bf16;
+// fp32 uses four v_mfma_f32_16x16x4_f32, element i of every lane's chunk
+// feeding the i-th one.  The result tile is the standard 16x16 C layout:
+// lane l holds D[4*(l/16) + q][l % 16] in acc[q], q = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hy3moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// bfloat16 stored as its raw 16 bits.
+struct bf16_t { uint16_t bits; };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static constexpr int kPerChunk = 8;   // elements in 16 bytes
+  static constexpr int kBytes = 2;
+};
+template <> struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+  static constexpr int kBytes = 4;
+};
+
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16_t> {
+  __device__ __forceinline__ static void step(f32x4_t &acc, const uint4 &a, const uint4 &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  __device__ __forceinline__ static void step(f32x4_t &acc, const uint4 &a, const uint4 &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+};
+
+// Store four consecutive output values (one lane's column of a 16x16 tile).
+__device__ __forceinline__ void store4(bf16_t *p, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+  *reinterpret_cast<uint2 *>(p) = v;
+}
+__device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+}
+
+// SiLU(g) * u in fp32: g / (1 + e^-g) * u.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Mask of the active lanes (among `live`) whose key equals this lane's key.
+// Keys are < 512 (9 bits).
+__device__ __forceinline__ uint64_t match_key(int key, uint64_t live) {
+  uint64_t m = live;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+__device__ __forceinline__ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace hy3moe

@@ -1,0 +1,248 @@
+// C ABI of the MoE layer: validation, workspace layout and the launch chain.
+//
+// The chain, all on the caller's stream with no host synchronisation and no
+// device-to-host copy (routing counts stay on the device; the expert GEMM
+// grids are sized by an upper bound and surplus workgroups exit at once):
+//   router GEMM -> score/select -> permutation (hist, scan+tiles, scatter)
+//   -> grouped gate-up + SwiGLU -> grouped down -> weighted combine.
+#include <string.h>
+
+#include "../../include/hy3moe.h"
+#include "internal.h"
+
+namespace hy3moe {
+int skinny_tile_rows(int T);
+}
+
+using namespace hy3moe;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t al(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+int elt_bytes(int dtype) { return dtype == HY3MOE_F32 ? 4 : 2; }
+
+int validate_cfg(const hy3moe_config *c) {
+  if (!c) return HY3MOE_ERR_INVALID;
+  if (c->T < 0 || c->E < 1 || c->E > 256 || c->K < 1 || c->K > c->E || c->K > 64)
+    return HY3MOE_ERR_INVALID;
+  if (c->H < 1 || c->I < 1 || c->I_shared < 0) return HY3MOE_ERR_INVALID;
+  if (c->dtype != HY3MOE_F32 && c->dtype != HY3MOE_BF16) return HY3MOE_ERR_INVALID;
+  if (c->route_mode != HY3MOE_ROUTE_SIGMOID_BIAS && c->route_mode != HY3MOE_ROUTE_SOFTMAX)
+    return HY3MOE_ERR_INVALID;
+  if (c->router_prec != HY3MOE_ROUTER_FP32 && c->router_prec != HY3MOE_ROUTER_SPLIT2_BF16)
+    return HY3MOE_ERR_INVALID;
+  if (c->H % 64 || c->I % 64 || c->I_shared % 64) return HY3MOE_ERR_UNSUPPORTED;
+  if (c->H > 65536 || c->I > 65536 || c->I_shared > 65536) return HY3MOE_ERR_UNSUPPORTED;
+  if (c->T > (int64_t(1) << 24)) return HY3MOE_ERR_UNSUPPORTED;
+  if (c->router_prec == HY3MOE_ROUTER_SPLIT2_BF16 && c->dtype != HY3MOE_BF16)
+    return HY3MOE_ERR_UNSUPPORTED;
+  return HY3MOE_OK;
+}
+
+void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L) {
+  memset(L, 0, sizeof(*L));
+  const int64_t T = c->T;
+  const int E = c->E, K = c->K, H = c->H;
+  const int64_t N = T * K;
+  size_t off = 0;
+  L->n_ksplit = router_ksplit(T, H, E);
+  L->logits_part = off; off += al((size_t)L->n_ksplit * T * E * 8);
+  L->idx = off;         off += al((size_t)N * 4);
+  L->weight = off;      off += al((size_t)N * 4);
+  if (!for_forward) { L->total = off; return; }
+  L->n_chunks = (int32_t)((N + PERM_CHUNK - 1) / PERM_CHUNK);
+  L->hist = off;        off += al((size_t)L->n_chunks * E * 4);
+  L->counts = off;      off += al((size_t)(E + 1) * 4);
+  L->offsets = off;     off += al((size_t)(E + 2) * 4);
+  const int64_t T_sh = c->I_shared > 0 ? T : 0;
+  const int64_t R = N + T_sh;
+  L->sorted_token = off; off += al((size_t)R * 4);
+  L->pos_of = off;      off += al((size_t)N * 4);
+  if (T <= SKINNY_MAX_T) {
+    L->tile_rows = skinny_tile_rows((int)T);
+    L->max_tiles = E + 1;
+  } else {
+    L->tile_rows = TILED_ROWS;
+    L->max_tiles = (int32_t)((R + TILED_ROWS - 1) / TILED_ROWS + E + 1);
+  }
+  L->tiles = off;       off += al((size_t)(2 * L->max_tiles + 1) * 4);
+  const int Imax = c->I > c->I_shared ? c->I : c->I_shared;
+  const int eb = elt_bytes(c->dtype);
+  L->h = off;           off += al((size_t)R * Imax * eb);
+  L->y = off;           off += al((size_t)R * H * eb);
+  L->total = off;
+}
+
+bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+bool al4(const void *p) { return ((uintptr_t)p & 3) == 0; }
+
+int check_launch(hipError_t e) { return e == hipSuccess ? HY3MOE_OK : HY3MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int hy3moe_abi_version(void) { return 1; }
+
+const char *hy3moe_strerror(int code) {
+  switch (code) {
+    case HY3MOE_OK: return "ok";
+    case HY3MOE_ERR_INVALID: return "invalid argument";
+    case HY3MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+    case HY3MOE_ERR_WORKSPACE: return "workspace too small";
+    case HY3MOE_ERR_ALIGN: return "pointer not aligned (16 bytes for tensors, 4 for idx/weight/bias)";
+    case HY3MOE_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+size_t hy3moe_workspace_bytes(const hy3moe_config *cfg, int for_forward) {
+  if (validate_cfg(cfg) != HY3MOE_OK) return 0;
+  hy3moe_ws_layout L;
+  compute_layout(cfg, for_forward, &L);
+  return L.total;
+}
+
+int hy3moe_workspace_layout(const hy3moe_config *cfg, hy3moe_ws_layout *out) {
+  const int rc = validate_cfg(cfg);
+  if (rc != HY3MOE_OK) return rc;
+  if (!out) return HY3MOE_ERR_INVALID;
+  compute_layout(cfg, 1, out);
+  return HY3MOE_OK;
+}
+
+int hy3moe_route(const hy3moe_config *cfg, const void *x, const float *w_router,
+                 const float *expert_bias, int32_t *idx, float *weight, void *workspace,
+                 size_t ws_bytes, void *stream) {
+  int rc = validate_cfg(cfg);
+  if (rc != HY3MOE_OK) return rc;
+  if (cfg->T == 0) return HY3MOE_OK;
+  if (!x || !w_router || !idx || !weight || !workspace) return HY3MOE_ERR_INVALID;
+  if (!al16(x) || !al16(w_router) || !al16(workspace) || !al4(idx) || !al4(weight) ||
+      (expert_bias && !al4(expert_bias)))
+    return HY3MOE_ERR_ALIGN;
+  hy3moe_ws_layout L;
+  compute_layout(cfg, 0, &L);
+  if (ws_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  const int T = (int)cfg->T;
+  double *part = reinterpret_cast<double *>(ws + L.logits_part);
+  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w_router, part, T, cfg->H,
+                                  cfg->E, L.n_ksplit, s));
+  if (rc) return rc;
+  const float *bias = cfg->route_mode == HY3MOE_ROUTE_SIGMOID_BIAS ? expert_bias : nullptr;
+  return check_launch(launch_select(part, L.n_ksplit, T, cfg->E, cfg->K, bias, cfg->route_mode,
+                                    cfg->scale, cfg->renorm_eps, idx, weight, s));
+}
+
+static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
+                        void *out, int32_t *idx_out, float *weight_out, void *workspace,
+                        size_t ws_bytes, void *stream, void *const *events) {
+  int rc = validate_cfg(cfg);
+  if (rc != HY3MOE_OK) return rc;
+  if (cfg->T == 0) return HY3MOE_OK;
+  if (!x || !w || !out || !workspace || !w->w_router || !w->w_gate || !w->w_up || !w->w_down)
+    return HY3MOE_ERR_INVALID;
+  const bool has_shared = cfg->I_shared > 0;
+  if (has_shared && (!w->ws_gate || !w->ws_up || !w->ws_down)) return HY3MOE_ERR_INVALID;
+  if (x == out) return HY3MOE_ERR_INVALID;
+  if (!al16(x) || !al16(out) || !al16(workspace) || !al16(w->w_router) || !al16(w->w_gate) ||
+      !al16(w->w_up) || !al16(w->w_down) || (w->expert_bias && !al4(w->expert_bias)) ||
+      (idx_out && !al4(idx_out)) || (weight_out && !al4(weight_out)))
+    return HY3MOE_ERR_ALIGN;
+  if (has_shared && (!al16(w->ws_gate) || !al16(w->ws_up) || !al16(w->ws_down)))
+    return HY3MOE_ERR_ALIGN;
+  hy3moe_ws_layout L;
+  compute_layout(cfg, 1, &L);
+  if (ws_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  const int T = (int)cfg->T, H = cfg->H, E = cfg->E, K = cfg->K;
+  double *part = reinterpret_cast<double *>(ws + L.logits_part);
+  int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(ws + L.idx);
+  float *weight = weight_out ? weight_out : reinterpret_cast<float *>(ws + L.weight);
+
+  int stage = 0;
+  auto mark = [&]() {
+    if (events) hipEventRecord(static_cast<hipEvent_t>(events[stage]), s);
+    ++stage;
+  };
+  mark();
+  // 1-2. gate
+  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w->w_router, part, T, H, E,
+                                  L.n_ksplit, s));
+  if (rc) return rc;
+  mark();
+  const float *bias = cfg->route_mode == HY3MOE_ROUTE_SIGMOID_BIAS ? w->expert_bias : nullptr;
+  rc = check_launch(launch_select(part, L.n_ksplit, T, E, K, bias, cfg->route_mode, cfg->scale,
+                                  cfg->renorm_eps, idx, weight, s));
+  if (rc) return rc;
+  mark();
+
+  // 3. permutation
+  PermArgs pa;
+  pa.idx = idx;
+  pa.hist = reinterpret_cast<int32_t *>(ws + L.hist);
+  pa.counts = reinterpret_cast<int32_t *>(ws + L.counts);
+  pa.offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+  pa.sorted_token = reinterpret_cast<int32_t *>(ws + L.sorted_token);
+  pa.pos_of = reinterpret_cast<int32_t *>(ws + L.pos_of);
+  pa.tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
+  pa.T = T; pa.K = K; pa.E = E;
+  pa.T_shared = has_shared ? T : 0;
+  pa.nchunks = L.n_chunks;
+  pa.tile_rows = L.tile_rows;
+  pa.max_tiles = L.max_tiles;
+  rc = check_launch(launch_permute(pa, s));
+  if (rc) return rc;
+  mark();
+
+  // 4-5. grouped experts
+  const int Imax = cfg->I > cfg->I_shared ? cfg->I : cfg->I_shared;
+  ExpertArgs ea;
+  ea.sorted_token = pa.sorted_token;
+  ea.offsets = pa.offsets;
+  ea.tiles = pa.tiles;
+  ea.E = E; ea.H = H; ea.I = cfg->I; ea.I_shared = cfg->I_shared; ea.ldh = Imax;
+  ea.max_tiles = L.max_tiles;
+  ea.act = x; ea.w0 = w->w_gate; ea.w1 = w->w_up; ea.ws0 = w->ws_gate; ea.ws1 = w->ws_up;
+  ea.out = ws + L.h;
+  rc = check_launch(launch_gate_up(ea, cfg->dtype, T, s));
+  if (rc) return rc;
+  mark();
+  ea.act = ws + L.h; ea.w0 = w->w_down; ea.w1 = nullptr; ea.ws0 = w->ws_down; ea.ws1 = nullptr;
+  ea.out = ws + L.y;
+  rc = check_launch(launch_down(ea, cfg->dtype, T, s));
+  if (rc) return rc;
+  mark();
+
+  // 6. combine
+  rc = check_launch(launch_combine(ws + L.y, pa.pos_of, weight, pa.offsets, T, K, H, E,
+                                   has_shared ? 1 : 0, out, cfg->dtype, s));
+  if (rc) return rc;
+  mark();
+  return HY3MOE_OK;
+}
+
+int hy3moe_forward(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w, void *out,
+                   int32_t *idx_out, float *weight_out, void *workspace, size_t ws_bytes,
+                   void *stream) {
+  return forward_impl(cfg, x, w, out, idx_out, weight_out, workspace, ws_bytes, stream, nullptr);
+}
+
+int hy3moe_forward_timed(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
+                         void *out, int32_t *idx_out, float *weight_out, void *workspace,
+                         size_t ws_bytes, void *stream, void *const *stage_events) {
+  if (!stage_events) return HY3MOE_ERR_INVALID;
+  for (int i = 0; i <= HY3MOE_N_STAGES; ++i)
+    if (!stage_events[i]) return HY3MOE_ERR_INVALID;
+  return forward_impl(cfg, x, w, out, idx_out, weight_out, workspace, ws_bytes, stream,
+                      stage_events);
+}
+
+}  // extern "C"

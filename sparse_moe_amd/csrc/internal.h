@@ -1,0 +1,65 @@
+// Host-side launchers of the MoE kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hy3moe {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// Row-tile shapes of the expert GEMMs.
+constexpr int TILED_ROWS = 128;     // rows (token copies) per tile, large-T path
+constexpr int TILED_GU_COLS = 64;   // h columns per gate-up tile (64 gate + 64 up rows)
+constexpr int TILED_DN_COLS = 128;  // y columns per down tile
+constexpr int SKINNY_MAX_T = 64;    // at or below this T the weight-streaming path runs
+constexpr int SKINNY_GU_COLS = 64;  // h columns per skinny gate-up workgroup
+constexpr int SKINNY_DN_COLS = 128; // y columns per skinny down workgroup
+constexpr int PERM_CHUNK = 1024;    // (token, pick) entries per wavefront in the permutation
+
+// Router -------------------------------------------------------------------
+int router_ksplit(int64_t T, int H, int E);
+hipError_t launch_router(const void *x, int dtype, int router_prec, const float *w_router,
+                         double *part, int T, int H, int E, int S, hipStream_t stream);
+
+// Score + top-K select ------------------------------------------------------
+hipError_t launch_select(const double *part, int S, int T, int E, int K, const float *bias,
+                         int route_mode, float scale, float renorm_eps, int32_t *idx,
+                         float *weight, hipStream_t stream);
+
+// Permutation ---------------------------------------------------------------
+struct PermArgs {
+  const int32_t *idx;     // [T*K]
+  int32_t *hist;          // [nchunks][E]
+  int32_t *counts;        // [E+1]
+  int32_t *offsets;       // [E+2]
+  int32_t *sorted_token;  // [R]
+  int32_t *pos_of;        // [T*K]
+  int32_t *tiles;         // [2*max_tiles + 1]
+  int T, K, E, T_shared, nchunks, tile_rows, max_tiles;
+};
+hipError_t launch_permute(const PermArgs &a, hipStream_t stream);
+
+// Expert GEMMs ----------------------------------------------------------------
+struct ExpertArgs {
+  const void *act;        // gate-up: x [T][H]; down: h [R][ldh]
+  const void *w0;         // gate-up: w_gate [E][I][H]; down: w_down [E][H][I]
+  const void *w1;         // gate-up: w_up [E][I][H]; down: unused
+  const void *ws0;        // shared: gate [Is][H] / down [H][Is]
+  const void *ws1;        // shared: up [Is][H]
+  void *out;              // gate-up: h [R][ldh]; down: y [R][H]
+  const int32_t *sorted_token;
+  const int32_t *offsets;
+  const int32_t *tiles;   // (group, first row) pairs, then the tile count
+  int E, H, I, I_shared, ldh, max_tiles;
+};
+hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, hipStream_t stream);
+hipError_t launch_down(const ExpertArgs &a, int dtype, int T, hipStream_t stream);
+
+// Combine ---------------------------------------------------------------------
+hipError_t launch_combine(const void *y, const int32_t *pos_of, const float *weight,
+                          const int32_t *offsets, int T, int K, int H, int E, int has_shared,
+                          void *out, int dtype, hipStream_t stream);
+
+}  // namespace hy3moe

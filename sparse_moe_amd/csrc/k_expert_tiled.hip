@@ -1,0 +1,202 @@
+// Grouped expert GEMMs for many rows per expert (prefill): bf16/fp32 MFMA,
+// LDS double buffering, one workgroup per (row tile, column tile).
+//
+// Gate-up (FusedMoE chain, Hy3 Preview inference case section 3: the gate-up
+// GEMM reads the original input rows through the route index, with no
+// explicit gather pass):  for group g and expert-major rows r,
+//     a = x[sorted_token[r]]   (gathered while the tile is loaded)
+//     h[r][c] = silu(a . W_gate[g][c]) * (a . W_up[g][c])
+// The B tile holds 64 gate rows and the same 64 up rows, interleaved by 32,
+// so each wavefront ends up with the gate and up accumulators of the same
+// columns in the same lanes and applies SwiGLU in registers.
+//
+// Down ("written compactly per expert so that accesses stay sequential"):
+//     y[r][n] = h[r] . W_down[g][n]
+// h rows of one group are contiguous, so the row operand is a plain stripe.
+//
+// Tile: 128 weight rows x 128 token rows x 128 bytes of K per stage, 4
+// wavefronts in 2 x 2, each owning a 64 x 64 block (4 x 4 MFMA tiles of
+// 16 x 16).  The weight rows are the MFMA A operand and the token rows the B
+// operand, so each lane ends with 4 consecutive output columns of one row.
+// Group E is the shared expert (its own weight pointers and width I_shared).
+#include "common.cuh"
+#include "internal.h"
+
+namespace hy3moe {
+
+namespace {
+
+constexpr int BR = 128;          // weight rows per tile
+constexpr int BT = 128;          // token rows per tile (== TILED_ROWS)
+constexpr int KB = 128;          // bytes of K per stage (8 chunks of 16 B)
+constexpr int CHUNKS = KB / 16;  // 8
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * CHUNKS + (chunk ^ (row & 7)); }
+
+template <typename T, bool GATE_UP>
+__global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int n_col_tiles) {
+  __shared__ uint4 lds[2][(BR + BT) * CHUNKS];   // 2 x 32 KB
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_tiles = a.tiles[2 * a.max_tiles];
+  const int tile = blockIdx.x / n_col_tiles;
+  const int ct = blockIdx.x % n_col_tiles;
+  if (tile >= n_tiles) return;
+
+  const int g = a.tiles[2 * tile];
+  const int row0 = a.tiles[2 * tile + 1];           // first expert-major row of the tile
+  const int grp_end = a.offsets[g + 1];
+  const bool shared = (g == a.E);
+  const int Ig = shared ? a.I_shared : a.I;
+  const int Kdim = GATE_UP ? a.H : Ig;               // reduction length (elements)
+  constexpr int EB = Elem<T>::kBytes;
+  constexpr int EPC = Elem<T>::kPerChunk;
+
+  // Columns of this tile.
+  const int col0 = ct * (GATE_UP ? TILED_GU_COLS : TILED_DN_COLS);
+  if (GATE_UP && col0 >= Ig) return;
+
+  // ---- per-thread load descriptors: 4 weight rows + 4 token rows, 1 chunk each ----
+  const int lrow = tid >> 3, lch = tid & 7;     // row 0..31 within a pass, chunk 0..7
+  const char *wptr[4];
+  const char *xptr[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = p * 32 + lrow;   // LDS weight row 0..127
+    const T *base;
+    size_t wrow;
+    if (GATE_UP) {
+      const int half = r >> 6, rr = r & 63;
+      const bool up = rr >= 32;
+      const int c = col0 + half * 32 + (rr & 31);
+      const T *mat = shared ? static_cast<const T *>(up ? a.ws1 : a.ws0)
+                            : static_cast<const T *>(up ? a.w1 : a.w0) + (size_t)g * a.I * a.H;
+      base = mat;
+      wrow = (size_t)c * a.H;
+    } else {
+      const T *mat = shared ? static_cast<const T *>(a.ws0)
+                            : static_cast<const T *>(a.w0) + (size_t)g * a.H * a.I;
+      base = mat;
+      const int n = (col0 + r < a.H) ? col0 + r : col0;   // column tail: reload a valid row
+      wrow = (size_t)n * Ig;
+    }
+    wptr[p] = reinterpret_cast<const char *>(base + wrow) + lch * 16;
+
+    int trow = row0 + r;                       // expert-major row of this token slot
+    if (trow >= grp_end) trow = row0;          // ragged tail: reload a valid row
+    const T *act = static_cast<const T *>(a.act);
+    size_t arow;
+    if (GATE_UP) arow = (size_t)a.sorted_token[trow] * a.H;
+    else arow = (size_t)trow * a.ldh;
+    xptr[p] = reinterpret_cast<const char *>(act + arow) + lch * 16;
+  }
+
+  uint4 wreg[4], xreg[4];
+#define HY3_GLOAD(kbyte)                                                   \
+  _Pragma("unroll") for (int p = 0; p < 4; ++p) {                          \
+    wreg[p] = *reinterpret_cast<const uint4 *>(wptr[p] + (kbyte));         \
+    xreg[p] = *reinterpret_cast<const uint4 *>(xptr[p] + (kbyte));         \
+  }
+#define HY3_LSTORE(buf)                                                    \
+  _Pragma("unroll") for (int p = 0; p < 4; ++p) {                          \
+    const int r = p * 32 + lrow;                                           \
+    lds[buf][swz(r, lch)] = wreg[p];                                       \
+    lds[buf][BR * CHUNKS + swz(r, lch)] = xreg[p];                         \
+  }
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int wr_ = wave >> 1;      // weight-row block of this wavefront (0/1)
+  const int wt_ = wave & 1;       // token-row block (0/1)
+  const int r16 = lane & 15, cg = lane >> 4;
+  const int nk = Kdim * EB / KB;
+
+  HY3_GLOAD(0);
+  HY3_LSTORE(0);
+  __syncthreads();
+  int cur = 0;
+  for (int ks = 0; ks < nk; ++ks) {
+    // Prefetch the next stage; the last iteration re-reads stage 0 (in bounds)
+    // into the buffer nobody reads again, which keeps the loop branch-free.
+    const int knext = (ks + 1 < nk) ? (ks + 1) * KB : 0;
+    HY3_GLOAD(knext);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int ch = sub * 4 + cg;
+      uint4 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = lds[cur][swz(wr_ * 64 + i * 16 + r16, ch)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = lds[cur][BR * CHUNKS + swz(wt_ * 64 + j * 16 + r16, ch)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Mma<T>::step(acc[i][j], af[i], bfr[j]);
+    }
+    HY3_LSTORE(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+  }
+#undef HY3_GLOAD
+#undef HY3_LSTORE
+  (void)EPC;
+
+  // ---- epilogue: lane holds D[weight row 16i + 4cg + q][token row 16j + r16] ----
+  T *out = static_cast<T *>(a.out);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int trow = row0 + wt_ * 64 + j * 16 + r16;
+    if (trow >= grp_end) continue;
+    if (GATE_UP) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // weight rows wr_*64 + 16i + .. are gate cols col0 + 32*wr_ + 16i + ..;
+        // rows +32 are the matching up cols.
+        const int c = col0 + wr_ * 32 + i * 16 + 4 * cg;
+        const f32x4_t gv = acc[i][j], uv = acc[i + 2][j];
+        store4(out + (size_t)trow * a.ldh + c, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
+               swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = col0 + wr_ * 64 + i * 16 + 4 * cg;
+        if (n >= a.H) continue;
+        const f32x4_t v = acc[i][j];
+        store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+template <typename T>
+static hipError_t launch_tiled(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+  if (gate_up) {
+    const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
+    const int nct = Imax / TILED_GU_COLS;
+    hipLaunchKernelGGL((expert_tiled_kernel<T, true>), dim3(a.max_tiles * nct), dim3(256), 0,
+                       stream, a, nct);
+  } else {
+    const int nct = (a.H + TILED_DN_COLS - 1) / TILED_DN_COLS;
+    hipLaunchKernelGGL((expert_tiled_kernel<T, false>), dim3(a.max_tiles * nct), dim3(256), 0,
+                       stream, a, nct);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tiled_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream) {
+  return dtype == DT_F32 ? launch_tiled<float>(a, true, stream)
+                         : launch_tiled<bf16_t>(a, true, stream);
+}
+hipError_t launch_tiled_down(const ExpertArgs &a, int dtype, hipStream_t stream) {
+  return dtype == DT_F32 ? launch_tiled<float>(a, false, stream)
+                         : launch_tiled<bf16_t>(a, false, stream);
+}
+
+}  // namespace hy3moe

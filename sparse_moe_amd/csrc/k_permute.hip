@@ -1,0 +1,197 @@
+// Token -> expert permutation with a contiguous row range per expert.
+//
+// Follows the "routing and index preprocessing" stage of the FusedMoE chain
+// (Hy3 Preview inference case, section 3 table): blocked counting in on-chip
+// shared memory that reserves one contiguous output range per expert.  Here:
+//
+//  1. hist:    each wavefront counts the experts of one chunk of PERM_CHUNK
+//              (token, pick) entries into its own LDS histogram.  Entries with
+//              equal expert in a 64-wide step are grouped with a 9-ballot key
+//              match, so the lowest lane of each group adds the group size
+//              and no LDS atomics are needed.
+//  2. scan:    one workgroup sums the chunk histograms per expert (turning them
+//              into exclusive per-chunk prefixes), scans the group counts into
+//              row offsets (group E = the shared expert, T rows), and writes
+//              the row-tile list of the expert GEMMs, largest groups first.
+//  3. scatter: each wavefront revisits its chunk in entry order and places
+//              entry f = t*K + j at row offsets[e] + prefix + rank, where rank
+//              counts earlier entries of the same expert.  The order within an
+//              expert is therefore ascending (t, j): the permutation is stable
+//              and deterministic.  Shared-expert rows are t = 0..T-1.
+#include "common.cuh"
+#include "internal.h"
+
+namespace hy3moe {
+
+namespace {
+
+constexpr int MAXG = 257;   // routed experts (<= 256) + the shared expert
+
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t *__restrict__ idx, int N,
+                                                        int E, int nchunks,
+                                                        int32_t *__restrict__ hist) {
+  __shared__ int cnt[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x * 4 + wave;
+  for (int e = lane; e < 256; e += 64) cnt[wave][e] = 0;
+  __syncthreads();
+  if (chunk < nchunks) {
+    const int beg = chunk * PERM_CHUNK;
+    const int end = min(N, beg + PERM_CHUNK);
+    for (int base = beg; base < end; base += 64) {
+      const int f = base + lane;
+      const bool valid = f < end;
+      const int e = valid ? idx[f] : 0;
+      const uint64_t m = match_key(e, __ballot(valid));
+      const bool leader = valid && ((m & lanemask_lt(lane)) == 0);
+      if (leader) cnt[wave][e] += __popcll(m);
+    }
+  }
+  __syncthreads();
+  if (chunk < nchunks)
+    for (int e = lane; e < E; e += 64) hist[(size_t)chunk * E + e] = cnt[wave][e];
+}
+
+// Exclusive scan of v[0..n) (n <= 1024) in LDS by 256 threads, 4 per thread.
+__device__ void block_exclusive_scan(int *v, int n, int *total) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int loc[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = tid * 4 + i;
+    loc[i] = (k < n) ? v[k] : 0;
+    s += loc[i];
+  }
+  // inclusive scan of s across the wavefront
+  int inc = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += wsum[w];
+  int run = wbase + inc - s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = tid * 4 + i;
+    if (k < n) v[k] = run;
+    run += loc[i];
+  }
+  if (tid == 255) *total = run;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void perm_scan_kernel(int32_t *__restrict__ hist, int nchunks,
+                                                        int E, int T_shared, int tile_rows,
+                                                        int max_tiles,
+                                                        int32_t *__restrict__ counts,
+                                                        int32_t *__restrict__ offsets,
+                                                        int32_t *__restrict__ tiles) {
+  __shared__ int cnt[MAXG], off[MAXG + 1], ntile[MAXG], order[MAXG], tstart[MAXG + 1];
+  __shared__ int total_rows, total_tiles;
+  const int tid = threadIdx.x;
+  const int G = E + 1;
+  // 1. per-expert totals; chunk histograms become exclusive prefixes.
+  for (int e = tid; e < E; e += 256) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      int32_t *p = hist + (size_t)c * E + e;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    cnt[e] = run;
+  }
+  if (tid == 0) cnt[E] = T_shared;
+  __syncthreads();
+  for (int g = tid; g < G; g += 256) off[g] = cnt[g];
+  __syncthreads();
+  block_exclusive_scan(off, G, &total_rows);
+  if (tid == 0) off[G] = total_rows;
+  // 2. tiles per group, groups ranked by tile count (descending, ties by index).
+  for (int g = tid; g < G; g += 256) ntile[g] = (cnt[g] + tile_rows - 1) / tile_rows;
+  __syncthreads();
+  for (int g = tid; g < G; g += 256) {
+    const int mine = ntile[g];
+    int r = 0;
+    for (int h = 0; h < G; ++h) {
+      const int o = ntile[h];
+      r += (o > mine) || (o == mine && h < g);
+    }
+    order[r] = g;
+  }
+  __syncthreads();
+  for (int r = tid; r < G; r += 256) tstart[r] = ntile[order[r]];
+  __syncthreads();
+  block_exclusive_scan(tstart, G, &total_tiles);
+  // 3. outputs.
+  for (int g = tid; g < G; g += 256) {
+    counts[g] = cnt[g];
+    offsets[g] = off[g];
+  }
+  if (tid == 0) offsets[G] = off[G];
+  for (int r = tid; r < G; r += 256) {
+    const int g = order[r];
+    const int n = ntile[g];
+    int ts = tstart[r];
+    for (int i = 0; i < n && ts < max_tiles; ++i, ++ts) {
+      tiles[2 * ts] = g;
+      tiles[2 * ts + 1] = off[g] + i * tile_rows;
+    }
+  }
+  if (tid == 0) tiles[2 * max_tiles] = min(total_tiles, max_tiles);
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(
+    const int32_t *__restrict__ idx, int N, int K, int E, int nchunks,
+    const int32_t *__restrict__ hist, const int32_t *__restrict__ offsets, int T_shared,
+    int32_t *__restrict__ sorted_token, int32_t *__restrict__ pos_of) {
+  __shared__ int run[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x * 4 + wave;
+  if (chunk < nchunks)
+    for (int e = lane; e < E; e += 64) run[wave][e] = offsets[e] + hist[(size_t)chunk * E + e];
+  __syncthreads();
+  if (chunk < nchunks) {
+    const int beg = chunk * PERM_CHUNK;
+    const int end = min(N, beg + PERM_CHUNK);
+    for (int base = beg; base < end; base += 64) {
+      const int f = base + lane;
+      const bool valid = f < end;
+      const int e = valid ? idx[f] : 0;
+      const uint64_t m = match_key(e, __ballot(valid));
+      const uint64_t below = m & lanemask_lt(lane);
+      const int r0 = valid ? run[wave][e] : 0;
+      if (valid) {
+        const int pos = r0 + __popcll(below);
+        sorted_token[pos] = f / K;
+        pos_of[f] = pos;
+        if (below == 0) run[wave][e] = r0 + __popcll(m);
+      }
+    }
+  }
+  // Shared-expert rows: identity.
+  const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int base_sh = offsets[E];
+  for (int t = gtid; t < T_shared; t += gridDim.x * blockDim.x) sorted_token[base_sh + t] = t;
+}
+
+}  // namespace
+
+hipError_t launch_permute(const PermArgs &a, hipStream_t stream) {
+  const int N = a.T * a.K;
+  const int blocks = (a.nchunks + 3) / 4;
+  hipLaunchKernelGGL(perm_hist_kernel, dim3(blocks), dim3(256), 0, stream, a.idx, N, a.E,
+                     a.nchunks, a.hist);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, stream, a.hist, a.nchunks, a.E,
+                     a.T_shared, a.tile_rows, a.max_tiles, a.counts, a.offsets, a.tiles);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(blocks), dim3(256), 0, stream, a.idx, N, a.K,
+                     a.E, a.nchunks, a.hist, a.offsets, a.T_shared, a.sorted_token, a.pos_of);
+  return hipGetLastError();
+}
+
+}  // namespace hy3moe

@@ -1,0 +1,48 @@
+"""Upload of seeded synthetic inputs to GPU memory (plumbing only).
+
+bf16 tensors travel as their raw 16-bit patterns and are reinterpreted as
+torch.bfloat16 on the device; float32 tensors are copied as they are.
+"""
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+
+from .inputs import MoEInputs
+
+
+def to_torch(a: np.ndarray, dtype: str, device):
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+def upload_weights(inp: MoEInputs, device) -> Dict[str, object]:
+    """Router weight, expert bias (if any), stacked routed experts and the shared expert."""
+    import torch
+    c = inp.cfg
+    wg, wu, wd = inp.stacked_experts()
+    d = {"w_router": torch.from_numpy(inp.w_router()).to(device),
+         "w_gate": to_torch(wg, c.dtype, device), "w_up": to_torch(wu, c.dtype, device),
+         "w_down": to_torch(wd, c.dtype, device)}
+    del wg, wu, wd
+    b = inp.bias()
+    if b is not None:
+        d["expert_bias"] = torch.from_numpy(b).to(device)
+    sh = inp.shared()
+    if sh is not None:
+        d["ws_gate"], d["ws_up"], d["ws_down"] = (to_torch(a, c.dtype, device) for a in sh)
+    return d
+
+
+def with_bias_of(inp: MoEInputs, weights: Dict[str, object], device) -> Dict[str, object]:
+    """The same model weights with this workload's own expert bias (a data stream)."""
+    import torch
+    w = dict(weights)
+    b = inp.bias()
+    w["expert_bias"] = None if b is None else torch.from_numpy(b).to(device)
+    return w

@@ -1,0 +1,138 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_amd as sm
+from sparse_moe_amd import binding as b
+from synth import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hy3moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hy3moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(b.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return sm.load()
+
+
+def test_header_declares_the_documented_entry_points():
+    fns = declared_functions()
+    for need in ("hy3moe_route", "hy3moe_forward", "hy3moe_workspace_bytes",
+                 "hy3moe_workspace_layout", "hy3moe_strerror", "hy3moe_abi_version"):
+        assert need in fns
+    assert sorted(sm.EXPORTED_SYMBOLS) == fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version_and_strerror(lib):
+    assert lib.hy3moe_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
+    assert sm.strerror(7) == "unknown error code"
+
+
+def cfg_of(c, **kw):
+    d = dict(T=c.T, H=c.H, E=c.E, K=c.K, I=c.I, I_shared=c.I_shared, dtype=c.dtype,
+             route_mode=c.route_mode, scale=c.scale, renorm_eps=c.renorm_eps)
+    d.update(kw)
+    return sm.make_config(**d)
+
+
+@pytest.mark.parametrize("cfg_id", sorted(CONFIGS))
+def test_workspace_layout_is_consistent(lib, cfg_id):
+    cfg = cfg_of(CONFIGS[cfg_id])
+    L = sm.hy3moe_workspace_layout(cfg)
+    assert L.total == sm.hy3moe_workspace_bytes(cfg, True) > 0
+    assert 0 < sm.hy3moe_workspace_bytes(cfg, False) <= L.total
+    names = ["logits_part", "idx", "weight", "hist", "counts", "offsets", "sorted_token",
+             "pos_of", "tiles", "h", "y"]
+    offs = sorted(getattr(L, n) for n in names)
+    assert all(o % 256 == 0 for o in offs)
+    assert len(set(offs)) == len(offs)
+    c = CONFIGS[cfg_id]
+    R = c.T * c.K + (c.T if c.I_shared else 0)
+    eb = 2 if c.dtype == "bf16" else 4
+    assert L.total - L.y >= R * c.H * eb
+    assert L.y - L.h >= R * max(c.I, c.I_shared) * eb
+    assert L.max_tiles >= (R + L.tile_rows - 1) // L.tile_rows
+    assert L.tile_rows >= min(c.T, 16)
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(K=0), -1), (dict(K=17, E=16), -1), (dict(E=257, K=8), -1), (dict(T=-1), -1),
+    (dict(H=100), -2), (dict(I=96), -2), (dict(I_shared=32), -2), (dict(K=65, E=100), -1),
+    (dict(dtype="f32", router_prec=1), -2), (dict(route_mode=3), -1),
+])
+def test_invalid_configs_rejected(lib, bad, code):
+    c = CONFIGS[1]
+    kw = dict(T=16, H=c.H, E=c.E, K=c.K, I=c.I, I_shared=c.I_shared, dtype="bf16",
+              route_mode=0, scale=2.826)
+    kw.update(bad)
+    cfg = sm.make_config(**kw)
+    assert sm.hy3moe_workspace_bytes(cfg, True) == 0
+    L = b.hy3moe_ws_layout()
+    assert lib.hy3moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == code
+    w = b.hy3moe_weights(*([256] * 8))
+    rc = lib.hy3moe_forward(ctypes.byref(cfg), 256, ctypes.byref(w), 512, None, None, 1024,
+                            1 << 40, None)
+    assert rc == code
+
+
+def test_argument_errors_before_launch(lib):
+    cfg = cfg_of(CONFIGS[1])
+    need = sm.hy3moe_workspace_bytes(cfg, True)
+    good = b.hy3moe_weights(*([4096] * 8))
+    fw = lib.hy3moe_forward
+    # null pointers
+    assert fw(ctypes.byref(cfg), None, ctypes.byref(good), 8192, None, None, 4096, need, None) == -1
+    nul = b.hy3moe_weights(4096, 0, 4096, None, 4096, 4096, 4096, 4096)
+    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(nul), 8192, None, None, 4096, need, None) == -1
+    nsh = b.hy3moe_weights(4096, 0, 4096, 4096, 4096, None, 4096, 4096)
+    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(nsh), 8192, None, None, 4096, need, None) == -1
+    # aliasing out == x
+    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(good), 4096, None, None, 8192, need, None) == -1
+    # misaligned tensors
+    assert fw(ctypes.byref(cfg), 4104, ctypes.byref(good), 8192, None, None, 4096, need, None) == -4
+    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(good), 8192, 4097, None, 4096, need, None) == -4
+    # workspace too small
+    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(good), 8192, None, None, 4096, need - 1,
+              None) == -3
+    # route entry point
+    rw = lib.hy3moe_route
+    rneed = sm.hy3moe_workspace_bytes(cfg, False)
+    assert rw(ctypes.byref(cfg), 4096, None, None, 4096, 4096, 4096, rneed, None) == -1
+    assert rw(ctypes.byref(cfg), 4096, 4096, None, 4096, 4096, 4096, rneed - 1, None) == -3
+    assert rw(ctypes.byref(cfg), 4096, 4104 + 4, None, 4096, 4096, 4096, rneed, None) == -4
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    cfg = cfg_of(CONFIGS[1], T=0)
+    w = b.hy3moe_weights(*([4096] * 8))
+    assert lib.hy3moe_forward(ctypes.byref(cfg), 4096, ctypes.byref(w), 8192, None, None,
+                              4096, 0, None) == 0
+    assert lib.hy3moe_route(ctypes.byref(cfg), 4096, 4096, None, 4096, 4096, 4096, 0, None) == 0
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("HY3MOE_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(b, "_LIB", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        b.load()

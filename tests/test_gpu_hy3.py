@@ -1,0 +1,136 @@
+"""Full-size workloads on the GPU, in the launch configuration the benchmark
+times: Hy3 decode (T=16), Hy3 prefill with skewed bias (T=8192), the router
+sweep (M in {2, 64, 512, 4096}, fp32-accurate and two-term split), and the
+HunyuanImage-3.0 softmax long prefill (T=32768, E=64).
+
+Every route index is checked; outputs are checked on every token for decode
+and on a seeded sample of 256 tokens plus every near-tie token otherwise
+(each sampled row is computed by the oracle one by one from its route).
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_amd as sm
+from gpu_util import (MARGIN, check_output, check_route, config_of, log, oracle_route,
+                      out_to_np, to_torch, upload_weights, with_bias_of)
+from synth import CONFIGS, ROUTER_SWEEP_M, MoEInputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sm.load()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def hy3_weights(dev):
+    inp = MoEInputs(CONFIGS[1])
+    log("generating and uploading Hy3 expert weights (192 x 37.7 MB)")
+    w = upload_weights(inp, dev)
+    torch.cuda.synchronize()
+    yield w
+    del w
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def sampled_check(inp, dev, weights, n_sample=256, seed=0):
+    c = inp.cfg
+    weights = with_bias_of(inp, weights, dev)
+    cfg = config_of(inp)
+    x = to_torch(inp.x(), c.dtype, dev)
+    out, idx, w = sm.forward(cfg, x, weights, return_route=True)
+    torch.cuda.synchronize()
+    gidx, gw = idx.cpu().numpy(), w.cpu().numpy()
+    log(f"  oracle route over all {c.T} tokens")
+    r = oracle_route(inp)
+    info = check_route(gidx, gw, r)
+    tie = np.nonzero(r.margin <= MARGIN)[0]
+    rng = np.random.default_rng(seed)
+    tokens = np.union1d(rng.choice(c.T, size=min(n_sample, c.T), replace=False), tie)
+    log(f"  near-tie tokens: {tie.size}; oracle outputs on {tokens.size} tokens")
+    x64 = inp.x_f64()[tokens]
+    ridx, rw = r.idx[tokens].copy(), r.weight[tokens].copy()
+    t_is_tie = np.isin(tokens, tie)
+    ridx[t_is_tie] = gidx[tokens][t_is_tie]
+    rw[t_is_tie] = gw[tokens][t_is_tie]
+    ref = oracle.forward_given_route(x64, ridx, rw, inp.expert_f64, c.E, inp.shared_f64())
+    got = out_to_np(out)[tokens]
+    check_output(got, ref, c.dtype, c.name, workload_shape=True)
+    counts = np.bincount(gidx.reshape(-1), minlength=c.E)
+    log(f"  experts hit {int((counts > 0).sum())}/{c.E}, max load {counts.max()} "
+        f"(mean {counts.mean():.1f})")
+    return info
+
+
+def test_hy3_decode_T16_full(dev, hy3_weights):
+    inp = MoEInputs(CONFIGS[1])
+    c = inp.cfg
+    log(f"case {c.name}")
+    cfg = config_of(inp)
+    x = to_torch(inp.x(), c.dtype, dev)
+    out, idx, w = sm.forward(cfg, x, hy3_weights, return_route=True)
+    torch.cuda.synchronize()
+    gidx, gw = idx.cpu().numpy(), w.cpu().numpy()
+    r = oracle_route(inp)
+    check_route(gidx, gw, r)
+    np.testing.assert_allclose(gw.sum(1), 2.826, rtol=0, atol=4 * np.spacing(np.float32(2.826)))
+    ridx, rw = r.idx.copy(), r.weight.copy()
+    tie = r.margin <= MARGIN
+    ridx[tie], rw[tie] = gidx[tie], gw[tie]
+    ref = oracle.forward_given_route(inp.x_f64(), ridx, rw, inp.expert_f64, c.E,
+                                     inp.shared_f64())
+    check_output(out_to_np(out), ref, c.dtype, c.name, workload_shape=True)
+
+
+def test_hy3_prefill_T8192_skew_sampled(dev, hy3_weights):
+    inp = MoEInputs(CONFIGS[2])
+    log(f"case {inp.cfg.name}")
+    sampled_check(inp, dev, hy3_weights)
+
+
+@pytest.mark.parametrize("M", ROUTER_SWEEP_M)
+def test_router_sweep(dev, hy3_weights, M):
+    """Logits of both router arithmetics against the float64 oracle, per token row:
+    max|dL| / max|L| and ||dL|| / ||L||.  fp32-accurate: <= 1e-5 and the route
+    matches; two-term split: <= 1e-3 (the stated bound for the split)."""
+    inp = MoEInputs(CONFIGS[3].with_T(M))
+    c = inp.cfg
+    x = to_torch(inp.x(), c.dtype, dev)
+    L64 = oracle.router_logits(inp.x_f64(), inp.w_router().astype(np.float64))
+    for prec, tol in ((sm.HY3MOE_ROUTER_FP32, 1e-5), (sm.HY3MOE_ROUTER_SPLIT2_BF16, 1e-3)):
+        cfg = config_of(inp, router_prec=prec)
+        L = sm.hy3moe_workspace_layout(cfg)
+        ws = sm.alloc_workspace(cfg, False, dev)
+        idx, w = sm.route(cfg, x, hy3_weights["w_router"],
+                          torch.from_numpy(inp.bias()).to(dev), workspace=ws)
+        torch.cuda.synchronize()
+        part = ws.cpu().numpy()[L.logits_part:L.logits_part + 8 * L.n_ksplit * M * c.E]
+        Lg = part.view(np.float64).reshape(L.n_ksplit, M, c.E).sum(0)
+        d = np.abs(Lg - L64)
+        row_max = (d.max(1) / np.abs(L64).max(1)).max()
+        row_l2 = (np.linalg.norm(Lg - L64, axis=1) / np.linalg.norm(L64, axis=1)).max()
+        log(f"  M={M} prec={prec}: row max-rel {row_max:.3e} row l2-rel {row_l2:.3e}")
+        assert row_max <= tol and row_l2 <= tol
+        if prec == sm.HY3MOE_ROUTER_FP32:
+            check_route(idx.cpu().numpy(), w.cpu().numpy(), oracle_route(inp))
+
+
+def test_softmax_long_prefill_T32768_sampled(dev):
+    gc.collect()
+    torch.cuda.empty_cache()
+    inp = MoEInputs(CONFIGS[4])
+    log(f"case {inp.cfg.name}: uploading 64 experts")
+    w = upload_weights(inp, dev)
+    try:
+        sampled_check(inp, dev, w)
+    finally:
+        del w
+        torch.cuda.empty_cache()

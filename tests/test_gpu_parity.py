@@ -1,0 +1,186 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Small and medium cases run the oracle on every token; they span the
+weight-streaming path (T <= 64; 1, 2 and 4 row fragments) and the tiled path
+(several row tiles per expert with ragged tails), fp32 and bf16, both routing
+modes, with/without the shared expert, K = E, E = 256, forced routing and the
+empty batch.  The full-size workloads check every route index and a seeded
+sample of output rows (plus every near-tie token) in the launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_amd as sm
+from gpu_util import (MARGIN, check_output, check_route, config_of, log, oracle_route,
+                      out_to_np, to_torch, upload_weights)
+from synth import CONFIGS, MoEInputs, random_small
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sm.load()
+    return torch.device("cuda:0")
+
+
+def reference(inp, r, gidx, gw, tokens=None):
+    """Oracle output on the oracle's route, except near-tie tokens, which use the GPU's."""
+    c = inp.cfg
+    x64 = inp.x_f64()
+    idx, w = r.idx.copy(), r.weight.copy()
+    tie = r.margin <= MARGIN
+    idx[tie] = gidx[tie]
+    w[tie] = gw[tie].astype(np.float64)
+    if tokens is not None:
+        x64, idx, w = x64[tokens], idx[tokens], w[tokens]
+    return oracle.forward_given_route(x64, idx, w, inp.expert_f64, c.E, inp.shared_f64())
+
+
+def run_gpu(inp, dev, weights=None, workspace=None):
+    c = inp.cfg
+    if weights is None:
+        weights = upload_weights(inp, dev)
+    cfg = config_of(inp)
+    x = to_torch(inp.x(), c.dtype, dev)
+    out, idx, w = sm.forward(cfg, x, weights, workspace=workspace, return_route=True)
+    torch.cuda.synchronize()
+    return out, idx.cpu().numpy(), w.cpu().numpy()
+
+
+def full_check(inp, dev, **kw):
+    c = inp.cfg
+    log(f"case {c.name}: T={c.T} H={c.H} E={c.E} K={c.K} I={c.I} Is={c.I_shared} "
+        f"{c.dtype} mode={c.route_mode}")
+    out, gidx, gw = run_gpu(inp, dev, **kw)
+    r = oracle_route(inp)
+    info = check_route(gidx, gw, r)
+    ref = reference(inp, r, gidx, gw)
+    check_output(out_to_np(out), ref, c.dtype, c.name)
+    return out, gidx, gw, r, info
+
+
+SMALL = {
+    "skinny_T1": dict(seed=1, T=1, H=512, E=32, K=8, I=256, I_shared=256, dtype="bf16"),
+    "skinny_T16": dict(seed=2, T=16, H=512, E=32, K=8, I=256, I_shared=256, dtype="bf16"),
+    "skinny_T20": dict(seed=3, T=20, H=512, E=24, K=6, I=192, I_shared=128, dtype="bf16"),
+    "skinny_T40": dict(seed=4, T=40, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16"),
+    "skinny_T64_f32": dict(seed=5, T=64, H=256, E=16, K=4, I=128, I_shared=128, dtype="f32"),
+    "tiled_T65": dict(seed=6, T=65, H=512, E=16, K=4, I=256, I_shared=256, dtype="bf16"),
+    "tiled_T300_ragged": dict(seed=7, T=300, H=512, E=24, K=4, I=256, I_shared=128,
+                              dtype="bf16"),
+    "tiled_T200_f32": dict(seed=8, T=200, H=256, E=8, K=2, I=128, I_shared=192, dtype="f32"),
+    "tiled_T700_H320": dict(seed=9, T=700, H=320, E=12, K=3, I=320, I_shared=64,
+                            dtype="bf16"),
+    "softmax_T150": dict(seed=10, T=150, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16",
+                         route_mode=1, scale=1.0, renorm_eps=1e-8, bias_kind="none"),
+    "softmax_T12": dict(seed=11, T=12, H=256, E=64, K=8, I=128, I_shared=128, dtype="bf16",
+                        route_mode=1, scale=1.0, renorm_eps=1e-8, bias_kind="none"),
+    "no_shared_T100": dict(seed=12, T=100, H=256, E=16, K=4, I=128, I_shared=0, dtype="bf16"),
+    "no_shared_T8": dict(seed=13, T=8, H=256, E=16, K=4, I=128, I_shared=0, dtype="f32"),
+    "k_equals_E": dict(seed=14, T=90, H=256, E=8, K=8, I=128, I_shared=128, dtype="bf16"),
+    "E256_K16": dict(seed=15, T=80, H=256, E=256, K=16, I=64, I_shared=64, dtype="bf16"),
+    "E1_K1": dict(seed=16, T=33, H=128, E=1, K=1, I=64, I_shared=64, dtype="bf16"),
+}
+
+
+def test_cfg0_tiny_fp32(dev):
+    inp = MoEInputs(CONFIGS[0])
+    out, gidx, gw, r, info = full_check(inp, dev)
+    # the route itself: sums of weights are the scale
+    np.testing.assert_allclose(gw.sum(1), 2.826, rtol=0, atol=4 * np.spacing(np.float32(2.826)))
+    # brute-force dense evaluation of every expert agrees too
+    dense = oracle.dense_masked(inp.x_f64(), r.idx, r.weight, inp.expert_f64, inp.cfg.E,
+                                inp.shared_f64())
+    check_output(out_to_np(out), dense, "f32", "cfg0 vs dense")
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_cases(dev, name):
+    full_check(random_small(**SMALL[name]), dev)
+
+
+def test_forced_routing_single_expert_set(dev):
+    """A +10 bias forces every token onto the same K experts: each of those
+    groups holds all T rows (several row tiles)."""
+    inp = random_small(21, T=333, H=256, E=16, K=3, I=128, I_shared=128, dtype="bf16")
+    b = np.zeros(16, dtype=np.float32)
+    b[[2, 9, 13]] = 10.0
+    inp._cache[("bias",)] = b
+    out, gidx, gw, r, info = full_check(inp, dev)
+    assert (np.sort(gidx, 1) == np.array([2, 9, 13])).all()
+
+
+def test_permutation_is_exact_and_stable(dev):
+    inp = random_small(22, T=500, H=256, E=24, K=4, I=128, I_shared=128, dtype="bf16")
+    c = inp.cfg
+    cfg = config_of(inp)
+    L = sm.hy3moe_workspace_layout(cfg)
+    ws = sm.alloc_workspace(cfg, True, dev)
+    out, gidx, gw = run_gpu(inp, dev, workspace=ws)
+    wsh = ws.cpu().numpy()
+
+    def arr(off, n):
+        return wsh[off:off + 4 * n].view(np.int32)
+
+    counts = arr(L.counts, c.E + 1)
+    offsets = arr(L.offsets, c.E + 2)
+    N = c.T * c.K
+    sorted_token = arr(L.sorted_token, N + c.T)
+    pos_of = arr(L.pos_of, N)
+    flat = gidx.reshape(-1)
+    np.testing.assert_array_equal(counts[:c.E], np.bincount(flat, minlength=c.E))
+    assert counts[c.E] == c.T
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    # stable order: rows of expert e are its (t, j) entries in ascending flat index
+    order = np.argsort(flat, kind="stable")
+    np.testing.assert_array_equal(pos_of[order], np.arange(N))
+    np.testing.assert_array_equal(sorted_token[:N], order // c.K)
+    np.testing.assert_array_equal(sorted_token[N:], np.arange(c.T))
+    # tiles cover every row exactly once, largest groups first
+    tiles = arr(L.tiles, 2 * L.max_tiles + 1)
+    nt = tiles[-1]
+    pairs = tiles[:2 * nt].reshape(-1, 2)
+    covered = np.zeros(N + c.T, dtype=int)
+    for g, r0 in pairs:
+        covered[r0:min(r0 + L.tile_rows, offsets[g + 1])] += 1
+    assert (covered == 1).all()
+    per_group = np.array([np.sum(pairs[:, 0] == g) for g in range(c.E + 1)])
+    firsts = [np.argmax(pairs[:, 0] == g) for g in range(c.E + 1) if per_group[g]]
+    assert all(per_group[pairs[i, 0]] >= per_group[pairs[j, 0]]
+               for i, j in zip(sorted(firsts)[:-1], sorted(firsts)[1:]))
+
+
+def test_deterministic_bitwise(dev):
+    inp = random_small(23, T=257, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16")
+    w = upload_weights(inp, dev)
+    a, _, _ = run_gpu(inp, dev, weights=w)
+    b, _, _ = run_gpu(inp, dev, weights=w)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_empty_batch(dev):
+    inp = random_small(24, T=0, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16")
+    w = upload_weights(inp, dev)
+    cfg = config_of(inp)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(x)
+    sm.hy3moe_forward(cfg, x, w, out, torch.empty(0, dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+
+
+def test_route_entry_matches_forward_route(dev):
+    inp = random_small(25, T=77, H=512, E=32, K=8, I=128, I_shared=128, dtype="bf16")
+    w = upload_weights(inp, dev)
+    cfg = config_of(inp)
+    x = to_torch(inp.x(), "bf16", dev)
+    idx, wt = sm.route(cfg, x, w["w_router"], w["expert_bias"])
+    _, fidx, fw = run_gpu(inp, dev, weights=w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), fidx)
+    np.testing.assert_array_equal(wt.cpu().numpy(), fw)
+    check_route(fidx, fw, oracle_route(inp))
