@@ -69,6 +69,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens in the CPU oracle sample (default: 16 decode, 48 otherwise)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time spent timing the oracle sample")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device (PMC calibration)")
     args = ap.parse_args()
@@ -228,20 +230,24 @@ def cpu_baseline(inp, args, gpu_idx):
     sh = inp.shared_f64()
     log(f"[bench] oracle sample: {n} tokens, {len(need)} experts in float64 "
         f"(generated in {time.time() - t0:.1f}s)")
-    t1 = time.perf_counter()
+    # Experts the oracle picks that the GPU did not (near-ties) are input
+    # preparation and are generated before timing.
     r = oracle.route(x64, wr, c.K, c.route_mode, b64, c.scale, c.renorm_eps)
-    dt = time.perf_counter() - t1
-    # Experts the oracle picks that the GPU did not (near-ties): input preparation,
-    # kept out of the oracle's time.
     for e in sorted(set(r.idx.reshape(-1).tolist()) - set(ws)):
         ws[e] = inp.expert_f64(e)
-    t2 = time.perf_counter()
-    oracle.forward_given_route(x64, r.idx, r.weight, ws.__getitem__, c.E, sh)
-    dt += time.perf_counter() - t2
+    # Repeat the whole sample (route + experts + combine) until ~target seconds.
+    reps, dt = 0, 0.0
+    while reps < 3 or (dt < args.cpu_seconds and reps < 10000):
+        t1 = time.perf_counter()
+        r = oracle.route(x64, wr, c.K, c.route_mode, b64, c.scale, c.renorm_eps)
+        oracle.forward_given_route(x64, r.idx, r.weight, ws.__getitem__, c.E, sh)
+        dt += time.perf_counter() - t1
+        reps += 1
     del ws
-    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": n * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} of the {c.T} tokens of the same batch (route over them, "
-                      f"{len(need)} experts + shared, float64 numpy), {dt:.2f}s"}
+                      f"{len(need)} experts + shared, float64 numpy), repeated {reps}x "
+                      f"in {dt:.1f}s"}
 
 
 if __name__ == "__main__":
