@@ -26,6 +26,7 @@ SOURCES = [
     "k_permute.hip",
     "k_expert_skinny.hip",
     "k_expert_tiled.hip",
+    "k_expert_big.hip",
     "k_combine.hip",
 ]
 

@@ -7,7 +7,7 @@
 //   -> grouped gate-up + SwiGLU -> grouped down -> weighted combine.
 #include <string.h>
 
-#include "../../include/hy3moe.h"
+#include "hy3moe.h"
 #include "internal.h"
 
 namespace hy3moe {
@@ -61,12 +61,13 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
   const int64_t R = N + T_sh;
   L->sorted_token = off; off += al((size_t)R * 4);
   L->pos_of = off;      off += al((size_t)N * 4);
-  if (T <= SKINNY_MAX_T) {
+  const int path = expert_path(T, K, E);
+  if (path == PATH_SKINNY) {
     L->tile_rows = skinny_tile_rows((int)T);
     L->max_tiles = E + 1;
   } else {
-    L->tile_rows = TILED_ROWS;
-    L->max_tiles = (int32_t)((R + TILED_ROWS - 1) / TILED_ROWS + E + 1);
+    L->tile_rows = path == PATH_BIG ? BIG_ROWS : TILED_ROWS;
+    L->max_tiles = (int32_t)((R + L->tile_rows - 1) / L->tile_rows + E + 1);
   }
   L->tiles = off;       off += al((size_t)(2 * L->max_tiles + 1) * 4);
   const int Imax = c->I > c->I_shared ? c->I : c->I_shared;
@@ -212,12 +213,13 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.max_tiles = L.max_tiles;
   ea.act = x; ea.w0 = w->w_gate; ea.w1 = w->w_up; ea.ws0 = w->ws_gate; ea.ws1 = w->ws_up;
   ea.out = ws + L.h;
-  rc = check_launch(launch_gate_up(ea, cfg->dtype, T, s));
+  const int path = expert_path(T, K, E);
+  rc = check_launch(launch_gate_up(ea, cfg->dtype, T, path, s));
   if (rc) return rc;
   mark();
   ea.act = ws + L.h; ea.w0 = w->w_down; ea.w1 = nullptr; ea.ws0 = w->ws_down; ea.ws1 = nullptr;
   ea.out = ws + L.y;
-  rc = check_launch(launch_down(ea, cfg->dtype, T, s));
+  rc = check_launch(launch_down(ea, cfg->dtype, T, path, s));
   if (rc) return rc;
   mark();
 

@@ -17,6 +17,16 @@ constexpr int SKINNY_MAX_T = 64;    // at or below this T the weight-streaming p
 constexpr int SKINNY_GU_COLS = 64;  // h columns per skinny gate-up workgroup
 constexpr int SKINNY_DN_COLS = 128; // y columns per skinny down workgroup
 constexpr int PERM_CHUNK = 1024;    // (token, pick) entries per wavefront in the permutation
+constexpr int BIG_ROWS = 256;       // rows per tile of the large-tile path
+constexpr int BIG_MIN_AVG_ROWS = 192;  // mean routed rows per expert that selects it
+
+// Which expert-GEMM path runs for a batch (the tile list is built for it).
+enum { PATH_SKINNY = 0, PATH_TILED = 1, PATH_BIG = 2 };
+inline int expert_path(int64_t T, int K, int E) {
+  if (T <= SKINNY_MAX_T) return PATH_SKINNY;
+  if (T * K >= (int64_t)BIG_MIN_AVG_ROWS * E) return PATH_BIG;
+  return PATH_TILED;
+}
 
 // Router -------------------------------------------------------------------
 int router_ksplit(int64_t T, int H, int E);
@@ -54,8 +64,8 @@ struct ExpertArgs {
   const int32_t *tiles;   // (group, first row) pairs, then the tile count
   int E, H, I, I_shared, ldh, max_tiles;
 };
-hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, hipStream_t stream);
-hipError_t launch_down(const ExpertArgs &a, int dtype, int T, hipStream_t stream);
+hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);
+hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);
 
 // Combine ---------------------------------------------------------------------
 hipError_t launch_combine(const void *y, const int32_t *pos_of, const float *weight,

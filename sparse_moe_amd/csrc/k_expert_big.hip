@@ -1,0 +1,254 @@
+// Grouped expert GEMMs for many rows per expert (prefill), large tiles.
+//
+// Same operation as the 128x128 tiled path (gate-up with x rows gathered
+// through the route index at load time and SwiGLU in registers; down over the
+// contiguous h rows of each expert), laid out for gfx950:
+//
+//  * 256 weight rows x 256 token rows per workgroup, 8 wavefronts (two per
+//    SIMD) in 2 x 4, each owning 128 weight rows x 64 token rows (8 x 4 MFMA
+//    16x16x32 tiles, 128 fp32 accumulators per lane).
+//  * K is staged 128 bytes per row at a time (64 bf16): one stage is 4M MACs
+//    (~2000 MFMA cycles per CU at peak).  Global loads go to one of two
+//    register sets two stages ahead; each stage is written to the idle LDS
+//    buffer one stage ahead; one barrier per stage.
+//    LDS rows use the swizzle chunk ^ (row & 7), which makes the 16-byte
+//    operand reads of 8 consecutive rows and the wavefront's writes
+//    conflict-free, and every LDS access a base register plus an immediate.
+//  * Global addresses are a uniform base per matrix plus 32-bit per-thread
+//    offsets.
+//  * Workgroups are remapped so that consecutive logical tiles run on the
+//    same XCD (dispatch is round-robin over the 8 XCDs) with an equal share of
+//    the real tiles per XCD, and logical tiles
+//    are ordered in bands of 4 row tiles x all column tiles with the row tile
+//    fastest: an XCD's ~32 resident tiles share 4 token-row blocks and 8
+//    weight-row blocks in its L2.
+// Group E is the shared expert (its own weights and width I_shared).
+#include "common.cuh"
+#include "internal.h"
+
+namespace hy3moe {
+
+namespace {
+
+constexpr int BW = 256;          // weight rows per tile
+constexpr int BTK = 256;         // token rows per tile (== BIG_ROWS)
+constexpr int RB = 128;          // bytes of K per row per stage
+constexpr int CH = RB / 16;      // 16-byte chunks per row per stage (8)
+constexpr int ROWS = BW + BTK;   // LDS rows per stage
+constexpr int BAND = 4;          // row tiles per band of the tile order
+
+template <typename T, bool GATE_UP>
+__global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_col_tiles) {
+  __shared__ uint4 lds[2 * ROWS * CH];   // 2 x 64 KB
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // XCD-aware remap.  Dispatch is round-robin over the 8 XCDs (block b runs on
+  // XCD b % 8); each XCD takes a contiguous run of `per` logical tiles, where
+  // `per` comes from the device-side tile count so that every XCD gets an
+  // equal share of real tiles (the grid is sized for the upper bound).
+  const int n_tiles = a.tiles[2 * a.max_tiles];
+  const int band_sz = BAND * n_col_tiles;
+  const int per = ((n_tiles + BAND - 1) / BAND * band_sz + 7) >> 3;
+  const int b = blockIdx.x, rank = b >> 3;
+  if (rank >= per) return;
+  const int L = (b & 7) * per + rank;
+  const int band = L / band_sz, within = L - band * band_sz;
+  const int ct = within / BAND;
+  const int rt = band * BAND + (within - ct * BAND);
+  if (rt >= n_tiles) return;
+
+  const int g = a.tiles[2 * rt];
+  const int row0 = a.tiles[2 * rt + 1];
+  const int grp_end = a.offsets[g + 1];
+  const bool shared = (g == a.E);
+  const int Ig = shared ? a.I_shared : a.I;
+  const int Kdim = GATE_UP ? a.H : Ig;
+  constexpr int EB = Elem<T>::kBytes;
+  const int col0 = ct * (GATE_UP ? BW / 2 : BW);
+  if (GATE_UP && col0 >= Ig) return;
+
+  // ---- load descriptors: thread loads chunk lc of rows lr + 64 p, p = 0..3,
+  // of the weight block and of the token block.  Gate-up weight rows: each
+  // block of 64 rows [64q, 64q+64) holds gate cols col0 + 32q + [0, 32) and then
+  // the up cols of the same columns, so lr < 32 loads gate rows, lr >= 32 up rows.
+  // Global addresses: a base pointer plus 32-bit offsets (every matrix < 4 GiB).
+  const int lr = tid >> 3, lc = tid & 7;
+  const char *wb, *xb;
+  uint32_t woff[4], xoff[4];
+  {
+    const T *mat;
+    if (GATE_UP) {
+      const bool up = lr >= 32;
+      mat = shared ? static_cast<const T *>(up ? a.ws1 : a.ws0)
+                   : static_cast<const T *>(up ? a.w1 : a.w0) + (size_t)g * a.I * a.H;
+      xb = static_cast<const char *>(a.act);
+    } else {
+      mat = shared ? static_cast<const T *>(a.ws0)
+                   : static_cast<const T *>(a.w0) + (size_t)g * a.H * a.I;
+      xb = static_cast<const char *>(a.act) + (size_t)row0 * a.ldh * EB;
+    }
+    wb = reinterpret_cast<const char *>(mat);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = p * 64 + lr;
+    if (GATE_UP) {
+      int wrow = col0 + p * 32 + (lr & 31);
+      if (wrow >= Ig) wrow = col0;             // column tail (Ig % 128 == 64)
+      woff[p] = (uint32_t)wrow * (uint32_t)(a.H * EB) + lc * 16;
+    } else {
+      const int wrow = (col0 + r < a.H) ? col0 + r : col0;
+      woff[p] = (uint32_t)wrow * (uint32_t)(Ig * EB) + lc * 16;
+    }
+    int trow = row0 + r;
+    if (trow >= grp_end) trow = row0;          // ragged tail: reload a valid row
+    if (GATE_UP) xoff[p] = (uint32_t)a.sorted_token[trow] * (uint32_t)(a.H * EB) + lc * 16;
+    else xoff[p] = (uint32_t)(trow - row0) * (uint32_t)(a.ldh * EB) + lc * 16;
+  }
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int wr_ = wave >> 2, wt_ = wave & 3;
+  const int r16 = lane & 15, cg = lane >> 4;
+  const int nk = Kdim * EB / RB;
+  // LDS addresses (uint4 units).  Rows 16i + r16 and 64p + lr have the same
+  // swizzle term for every i and p, so each access is a base plus an immediate.
+  const int rd_a = (wr_ * 128 + r16) * CH;
+  const int rd_b = (BW + wt_ * 64 + r16) * CH;
+  const int sw0 = cg ^ (r16 & 7), sw1 = (4 + cg) ^ (r16 & 7);
+  const int wr_l = lr * CH + (lc ^ (lr & 7));
+
+  // Two register stage sets: stage s is loaded into set s % 2 at the start of
+  // iteration s - 2 and written to LDS at the end of iteration s - 1, so the
+  // global latency is covered by two iterations of MFMA work.
+  uint4 aw0, aw1, aw2, aw3, ax0, ax1, ax2, ax3;   // set 0
+  uint4 bw0, bw1, bw2, bw3, bx0, bx1, bx2, bx3;   // set 1
+#define HY3_GLOAD(S, kst)                                                              \
+  {                                                                                    \
+    const uint32_t kb_ = (uint32_t)(kst) * RB;                                         \
+    S##w0 = *reinterpret_cast<const uint4 *>(wb + (kb_ + woff[0]));                    \
+    S##w1 = *reinterpret_cast<const uint4 *>(wb + (kb_ + woff[1]));                    \
+    S##w2 = *reinterpret_cast<const uint4 *>(wb + (kb_ + woff[2]));                    \
+    S##w3 = *reinterpret_cast<const uint4 *>(wb + (kb_ + woff[3]));                    \
+    S##x0 = *reinterpret_cast<const uint4 *>(xb + (kb_ + xoff[0]));                    \
+    S##x1 = *reinterpret_cast<const uint4 *>(xb + (kb_ + xoff[1]));                    \
+    S##x2 = *reinterpret_cast<const uint4 *>(xb + (kb_ + xoff[2]));                    \
+    S##x3 = *reinterpret_cast<const uint4 *>(xb + (kb_ + xoff[3]));                    \
+  }
+#define HY3_LSTORE(S, buf)                                                             \
+  {                                                                                    \
+    uint4 *d_ = lds + (buf) * ROWS * CH + wr_l;                                        \
+    d_[0 * 64 * CH] = S##w0; d_[1 * 64 * CH] = S##w1;                                  \
+    d_[2 * 64 * CH] = S##w2; d_[3 * 64 * CH] = S##w3;                                  \
+    d_[(BW + 0 * 64) * CH] = S##x0; d_[(BW + 1 * 64) * CH] = S##x1;                    \
+    d_[(BW + 2 * 64) * CH] = S##x2; d_[(BW + 3 * 64) * CH] = S##x3;                    \
+  }
+#define HY3_COMPUTE(buf)                                                               \
+  {                                                                                    \
+    const uint4 *base_ = lds + (buf) * ROWS * CH;                                      \
+    _Pragma("unroll") for (int sub = 0; sub < 2; ++sub) {                              \
+      const int swz = sub ? sw1 : sw0;                                                 \
+      uint4 bf_[4];                                                                    \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                    \
+          bf_[j] = base_[rd_b + j * 16 * CH + swz];                                    \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                  \
+        const uint4 af_ = base_[rd_a + i * 16 * CH + swz];                             \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) Mma<T>::step(acc[i][j], af_, bf_[j]); \
+      }                                                                                \
+    }                                                                                  \
+  }
+// Iteration k: prefetch stage k+2 into set S (its stage k went to LDS at the
+// end of iteration k-1), compute buffer B, write set SN (stage k+1) to the
+// other buffer.  Past the end the prefetch re-reads stage 0 and the store
+// fills a buffer that is not read again: the body stays branch-free.
+#define HY3_ITER(k, S, B, SN)                                                          \
+  {                                                                                    \
+    HY3_GLOAD(S, ((k) + 2 < nk) ? (k) + 2 : 0);                                        \
+    HY3_COMPUTE(B);                                                                    \
+    HY3_LSTORE(SN, (B) ^ 1);                                                           \
+    __syncthreads();                                                                   \
+  }
+
+  HY3_GLOAD(a, 0);
+  HY3_GLOAD(b, (1 < nk) ? 1 : 0);
+  HY3_LSTORE(a, 0);
+  __syncthreads();
+  int k = 0;
+  for (; k + 2 <= nk; k += 2) {
+    HY3_ITER(k, a, 0, b);
+    HY3_ITER(k + 1, b, 1, a);
+  }
+  if (k < nk) HY3_ITER(k, a, 0, b);
+#undef HY3_ITER
+#undef HY3_COMPUTE
+#undef HY3_LSTORE
+#undef HY3_GLOAD
+
+  // ---- epilogue: lane holds D[weight row 16i + 4cg + q][token row 16j + r16] ----
+  T *out = static_cast<T *>(a.out);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int trow = row0 + wt_ * 64 + j * 16 + r16;
+    if (trow >= grp_end) continue;
+    if (GATE_UP) {
+      // wavefront wr_ holds weight rows 128 wr_ + [0, 128): frags i = 0,1 are
+      // gate cols col0 + 64 wr_ + [0, 32), i = 2,3 their up cols, i = 4,5 gate
+      // cols col0 + 64 wr_ + [32, 64), i = 6,7 their up cols.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gi = (i >> 1) * 4 + (i & 1);
+        const int c = col0 + wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
+        if (c >= Ig) continue;
+        const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
+        store4(out + (size_t)trow * a.ldh + c, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
+               swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = col0 + wr_ * 128 + i * 16 + 4 * cg;
+        if (n >= a.H) continue;
+        const f32x4_t v = acc[i][j];
+        store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+  int nct;
+  if (gate_up) {
+    const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
+    nct = (Imax + BW / 2 - 1) / (BW / 2);
+  } else {
+    nct = (a.H + BW - 1) / BW;
+  }
+  // Logical tiles: bands of BAND row tiles x nct columns; the grid covers the
+  // upper bound of row tiles, padded to a multiple of the 8 XCDs.
+  const int bands = (a.max_tiles + BAND - 1) / BAND;
+  const long logical = (long)bands * BAND * nct;
+  const dim3 grid((unsigned)((logical + 7) / 8 * 8));
+  if (gate_up)
+    hipLaunchKernelGGL((expert_big_kernel<T, true>), grid, dim3(512), 0, stream, a, nct);
+  else
+    hipLaunchKernelGGL((expert_big_kernel<T, false>), grid, dim3(512), 0, stream, a, nct);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_big_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream) {
+  return dtype == DT_F32 ? launch_big_t<float>(a, true, stream)
+                         : launch_big_t<bf16_t>(a, true, stream);
+}
+hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream) {
+  return dtype == DT_F32 ? launch_big_t<float>(a, false, stream)
+                         : launch_big_t<bf16_t>(a, false, stream);
+}
+
+}  // namespace hy3moe

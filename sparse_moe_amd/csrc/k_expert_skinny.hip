@@ -163,18 +163,22 @@ int skinny_tile_rows(int T) { return T <= 16 ? 16 : (T <= 32 ? 32 : 64); }
 
 hipError_t launch_tiled_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_tiled_down(const ExpertArgs &a, int dtype, hipStream_t stream);
+hipError_t launch_big_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream);
+hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream);
 
-hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, hipStream_t stream) {
-  if (T <= SKINNY_MAX_T)
+hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
+  if (path == PATH_SKINNY)
     return dtype == DT_F32 ? launch_skinny<float>(a, true, T, stream)
                            : launch_skinny<bf16_t>(a, true, T, stream);
+  if (path == PATH_BIG) return launch_big_gate_up(a, dtype, stream);
   return launch_tiled_gate_up(a, dtype, stream);
 }
 
-hipError_t launch_down(const ExpertArgs &a, int dtype, int T, hipStream_t stream) {
-  if (T <= SKINNY_MAX_T)
+hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
+  if (path == PATH_SKINNY)
     return dtype == DT_F32 ? launch_skinny<float>(a, false, T, stream)
                            : launch_skinny<bf16_t>(a, false, T, stream);
+  if (path == PATH_BIG) return launch_big_down(a, dtype, stream);
   return launch_tiled_down(a, dtype, stream);
 }
 

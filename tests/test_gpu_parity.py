@@ -85,6 +85,13 @@ SMALL = {
     "k_equals_E": dict(seed=14, T=90, H=256, E=8, K=8, I=128, I_shared=128, dtype="bf16"),
     "E256_K16": dict(seed=15, T=80, H=256, E=256, K=16, I=64, I_shared=64, dtype="bf16"),
     "E1_K1": dict(seed=16, T=33, H=128, E=1, K=1, I=64, I_shared=64, dtype="bf16"),
+    # large-tile path (mean routed rows per expert >= 192): ragged row tails,
+    # an I % 128 == 64 gate-up column tail and an H % 256 == 64 down column tail
+    "big_T400_E8": dict(seed=17, T=400, H=512, E=8, K=4, I=256, I_shared=128, dtype="bf16"),
+    "big_T513_tails": dict(seed=18, T=513, H=320, E=4, K=2, I=192, I_shared=64, dtype="bf16"),
+    "big_T300_f32": dict(seed=19, T=300, H=256, E=2, K=2, I=128, I_shared=192, dtype="f32"),
+    "big_softmax_T600": dict(seed=20, T=600, H=256, E=8, K=3, I=128, I_shared=128, dtype="bf16",
+                             route_mode=1, scale=1.0, renorm_eps=1e-8, bias_kind="none"),
 }
 
 
