@@ -71,6 +71,8 @@ def main():
                     help="tokens in the CPU oracle sample (default: 16 decode, 48 otherwise)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time spent timing the oracle sample")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure the achievable MFMA and copy ceilings instead of the layer")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device (PMC calibration)")
     args = ap.parse_args()
@@ -88,6 +90,9 @@ def main():
     from synth.device import to_torch, upload_weights
 
     dev = torch.device("cuda:0")
+    if args.ceilings:
+        print(json.dumps(ceilings(dev)), flush=True)
+        return
     sm.load()
     inp = MoEInputs(CONFIGS[WORKLOADS[args.workload]])
     c = inp.cfg
@@ -201,6 +206,54 @@ def main():
         "roofline": roof, "cpu_baseline": cpu, "layer": layer,
     }
     print(json.dumps(res), flush=True)
+
+
+def ceilings(dev):
+    """Achievable ceilings on this GPU: a dense bf16 MFMA microkernel (register
+    operands only, 16 independent chains per wavefront) and a 16-byte-per-lane
+    device copy of 4 GiB (read + write bytes counted)."""
+    import ctypes
+
+    import torch
+
+    from sparse_moe_amd.build import PROBE_PATH
+    L = ctypes.CDLL(PROBE_PATH)
+    L.hy3moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.hy3moe_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_int, ctypes.c_void_p]
+    s = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for blocks in (2048, 4096):
+        iters = 4000
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        assert L.hy3moe_probe_mfma(blocks, 100, out.data_ptr(), s) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        assert L.hy3moe_probe_mfma(blocks, iters, out.data_ptr(), s) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        flops = blocks * 4 * iters * 16 * 2.0 * 16 * 16 * 32
+        res[f"mfma_bf16_tflops_{blocks}blk"] = flops / ms / 1e9
+    n = 4 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    best = 0.0
+    for blocks in (1024, 2048, 4096, 8192):
+        assert L.hy3moe_probe_copy(src.data_ptr(), dst.data_ptr(), n, blocks, s) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            L.hy3moe_probe_copy(src.data_ptr(), dst.data_ptr(), n, blocks, s)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = 2 * n * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+        res[f"copy_GBs_{blocks}blk"] = gbs
+        best = max(best, gbs)
+    res["copy_GBs_best"] = best
+    res["mfma_bf16_tflops_best"] = max(v for k, v in res.items() if k.startswith("mfma"))
+    res["peak_published"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_GBs": PEAK_HBM_GBS}
+    return res
 
 
 def cpu_baseline(inp, args, gpu_idx):

@@ -18,6 +18,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_NAME = "libhy3moe.so"
 LIB_PATH = os.path.join(LIB_DIR, LIB_NAME)
+# Roofline ceiling probes (dense MFMA microkernel, device copy): a separate
+# measurement library, not part of the MoE layer's C ABI.
+PROBE_SOURCE = "ceiling_probe.hip"
+PROBE_PATH = os.path.join(LIB_DIR, "libhy3moe_probe.so")
 
 SOURCES = [
     "hy3moe_api.hip",
@@ -74,6 +78,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
+    ptmp = PROBE_PATH + ".tmp"
+    _run([hipcc, *CFLAGS, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", ptmp], verbose)
+    os.replace(ptmp, PROBE_PATH)
     return LIB_PATH
 
 

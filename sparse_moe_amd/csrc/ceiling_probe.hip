@@ -1,0 +1,64 @@
+// Achievable-ceiling probes for the roofline (measurement helpers, not part
+// of the MoE layer): a dense bf16 MFMA microkernel with register operands
+// only, and a 16-byte-per-lane device copy.  Built into libhy3moe_probe.so.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+namespace {
+
+// 16 independent accumulator chains per wavefront, so the MFMA pipe never
+// waits on a dependency; operands live in registers.
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float *out) {
+  const int lane = threadIdx.x & 63;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)((lane + i) & 7));
+    b[i] = (__bf16)(0.002f * (float)((lane * 3 + i) & 7));
+  }
+  f32x4_t acc[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src,
+                                                   uint4 *__restrict__ dst, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+// FLOPs done = n_blocks * 4 waves * iters * 16 MFMAs * 2*16*16*32.
+// `out` needs n_blocks * 256 floats.  Returns a hipError_t code.
+int hy3moe_probe_mfma(int n_blocks, int iters, float *out, void *stream) {
+  if (n_blocks <= 0 || iters <= 0 || !out) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(n_blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), iters, out);
+  return (int)hipGetLastError();
+}
+
+// Copies `bytes` (multiple of 16) from src to dst with n_blocks x 256 threads.
+int hy3moe_probe_copy(const void *src, void *dst, size_t bytes, int n_blocks, void *stream) {
+  if (!src || !dst || (bytes & 15) || n_blocks <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_kernel, dim3(n_blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -17,6 +17,7 @@ constexpr int SKINNY_MAX_T = 64;    // at or below this T the weight-streaming p
 constexpr int SKINNY_GU_COLS = 64;  // h columns per skinny gate-up workgroup
 constexpr int SKINNY_DN_COLS = 128; // y columns per skinny down workgroup
 constexpr int PERM_CHUNK = 1024;    // (token, pick) entries per wavefront in the permutation
+constexpr int MAX_KSPLIT = 16;      // router K-slices (partial logit sets)
 constexpr int BIG_ROWS = 256;       // rows per tile of the large-tile path
 constexpr int BIG_MIN_AVG_ROWS = 192;  // mean routed rows per expert that selects it
 

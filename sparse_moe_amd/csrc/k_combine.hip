@@ -63,13 +63,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y,
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  for (int j = 0; j < K; ++j) {
-    const int p = pos_of[(size_t)t * K + j];
-    const float w = weight[(size_t)t * K + j];
-    float v[V];
-    load_vec<T>(y + (size_t)p * H + n, v);
+  // Blocks of 8 picks: all row loads of a block are issued before its FMAs.
+  for (int j0 = 0; j0 < K; j0 += 8) {
+    float v[8][V], w[8];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = __builtin_fmaf(w, v[i], acc[i]);
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = j0 + jj < K ? j0 + jj : K - 1;
+      const int p = pos_of[(size_t)t * K + j];
+      w[jj] = weight[(size_t)t * K + j];
+      load_vec<T>(y + (size_t)p * H + n, v[jj]);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < K) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = __builtin_fmaf(w[jj], v[jj][i], acc[i]);
+      }
+    }
   }
   if (has_shared) {
     float v[V];

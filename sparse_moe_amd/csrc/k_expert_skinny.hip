@@ -5,15 +5,19 @@
 // of expert weights read from HBM (Hy3 Preview inference case, section on
 // decode parallelism: small-batch MoE grouped GEMM is memory-bound).  This
 // path reads every touched weight byte exactly once, straight from global
-// memory into MFMA operand registers (no LDS round trip), with many 16-byte
-// loads in flight per wavefront.
+// memory into MFMA operand registers (no LDS round trip).
 //
-// One workgroup = one group (routed expert or the shared expert) x one
-// column block; one tile holds all rows of the group (T <= 16*MT).
-// Each wavefront owns 16 gate + 16 up columns (gate-up) or 32 output columns
-// (down); the token rows (<= 16*MT, zero-padded by reloading a valid row)
-// are the MFMA B operand.  Same operand convention and fused SwiGLU epilogue
-// as the tiled path.
+// Work unit = one wavefront's share of one group (routed expert or the shared
+// expert, all of its <= 16*MT rows): 16 gate + 16 up weight rows (gate-up) or
+// 32 output rows of W_down (down), over the whole K.  The grid is persistent:
+// a fixed number of wavefronts strides over the units counted on the device,
+// so no partially filled round of waves is left at the end.  Inside a unit,
+// K is streamed in blocks of U 64-byte steps per row with two register sets,
+// so one block of loads is in flight while the previous one feeds the MFMAs
+// (8 steps = 24 loads per lane per block for one row fragment; fewer steps
+// with more row fragments to stay within two wavefronts' registers per SIMD).
+// The token rows (gathered through sorted_token for gate-up, contiguous h rows
+// for down; padded by reloading a valid row) are the other MFMA operand.
 #include "common.cuh"
 #include "internal.h"
 
@@ -21,15 +25,9 @@ namespace hy3moe {
 
 namespace {
 
-constexpr int U = 8;   // 64-byte K steps issued per loop iteration
-
 template <typename T, bool GATE_UP, int MT>
-__global__ __launch_bounds__(256) void expert_skinny_kernel(ExpertArgs a, int n_col_blocks) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_tiles = a.tiles[2 * a.max_tiles];
-  const int tile = blockIdx.x / n_col_blocks;
-  const int cb = blockIdx.x % n_col_blocks;
-  if (tile >= n_tiles) return;
+__device__ __forceinline__ void stream_unit(const ExpertArgs &a, int tile, int cb, int lane) {
+  constexpr int U = 8 / MT;   // 64-byte K steps per row per register set
   const int g = a.tiles[2 * tile];
   const int row0 = a.tiles[2 * tile + 1];
   const int grp_end = a.offsets[g + 1];
@@ -38,42 +36,33 @@ __global__ __launch_bounds__(256) void expert_skinny_kernel(ExpertArgs a, int n_
   const int Kdim = GATE_UP ? a.H : Ig;
   constexpr int EB = Elem<T>::kBytes;
   const int r16 = lane & 15, cg = lane >> 4;
+  const int col0 = cb * (GATE_UP ? 16 : 32);
+  if (col0 >= (GATE_UP ? Ig : a.H)) return;
 
-  int col0;
-  if (GATE_UP) {
-    col0 = cb * SKINNY_GU_COLS + wave * 16;
-    if (col0 >= Ig) return;
-  } else {
-    col0 = cb * SKINNY_DN_COLS + wave * 32;
-    if (col0 >= a.H) return;
-  }
-
-  const char *wptr[2];
+  const char *w0p, *w1p;
   if (GATE_UP) {
     const T *gate = shared ? static_cast<const T *>(a.ws0)
                            : static_cast<const T *>(a.w0) + (size_t)g * a.I * a.H;
     const T *up = shared ? static_cast<const T *>(a.ws1)
                          : static_cast<const T *>(a.w1) + (size_t)g * a.I * a.H;
-    wptr[0] = reinterpret_cast<const char *>(gate + (size_t)(col0 + r16) * a.H) + cg * 16;
-    wptr[1] = reinterpret_cast<const char *>(up + (size_t)(col0 + r16) * a.H) + cg * 16;
+    w0p = reinterpret_cast<const char *>(gate + (size_t)(col0 + r16) * a.H) + cg * 16;
+    w1p = reinterpret_cast<const char *>(up + (size_t)(col0 + r16) * a.H) + cg * 16;
   } else {
     const T *dn = shared ? static_cast<const T *>(a.ws0)
                          : static_cast<const T *>(a.w0) + (size_t)g * a.H * a.I;
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      int n = col0 + f * 16 + r16;
-      if (n >= a.H) n = col0;
-      wptr[f] = reinterpret_cast<const char *>(dn + (size_t)n * Ig) + cg * 16;
-    }
+    const int n0 = (col0 + r16 < a.H) ? col0 + r16 : col0;
+    const int n1 = (col0 + 16 + r16 < a.H) ? col0 + 16 + r16 : col0;
+    w0p = reinterpret_cast<const char *>(dn + (size_t)n0 * Ig) + cg * 16;
+    w1p = reinterpret_cast<const char *>(dn + (size_t)n1 * Ig) + cg * 16;
   }
-  const char *xptr[MT];
+  const char *xp[MT];
   const T *act = static_cast<const T *>(a.act);
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     int trow = row0 + m * 16 + r16;
     if (trow >= grp_end) trow = row0;
     const size_t arow = GATE_UP ? (size_t)a.sorted_token[trow] * a.H : (size_t)trow * a.ldh;
-    xptr[m] = reinterpret_cast<const char *>(act + arow) + cg * 16;
+    xp[m] = reinterpret_cast<const char *>(act + arow) + cg * 16;
   }
 
   f32x4_t acc[2][MT];
@@ -82,36 +71,38 @@ __global__ __launch_bounds__(256) void expert_skinny_kernel(ExpertArgs a, int n_
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nsub = Kdim * EB / 64;
-  int s = 0;
-  for (; s + U <= nsub; s += U) {
-    uint4 wv[U][2], xv[U][MT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int off = (s + u) * 64;
-      wv[u][0] = *reinterpret_cast<const uint4 *>(wptr[0] + off);
-      wv[u][1] = *reinterpret_cast<const uint4 *>(wptr[1] + off);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) xv[u][m] = *reinterpret_cast<const uint4 *>(xptr[m] + off);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) Mma<T>::step(acc[f][m], wv[u][f], xv[u][m]);
+  const int nsub = Kdim * EB / 64;   // 64-byte steps per row (a multiple of 2)
+  uint4 aw0[U], aw1[U], ax[U][MT];
+  uint4 bw0[U], bw1[U], bx[U][MT];
+#define HY3_LOAD(W0, W1, X, s0)                                                        \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                      \
+    const int o_ = ((s0) + u < nsub ? (s0) + u : nsub - 1) * 64;                       \
+    W0[u] = *reinterpret_cast<const uint4 *>(w0p + o_);                                \
+    W1[u] = *reinterpret_cast<const uint4 *>(w1p + o_);                                \
+    _Pragma("unroll") for (int m = 0; m < MT; ++m)                                     \
+        X[u][m] = *reinterpret_cast<const uint4 *>(xp[m] + o_);                        \
   }
-  for (; s < nsub; ++s) {
-    const int off = s * 64;
-    const uint4 w0 = *reinterpret_cast<const uint4 *>(wptr[0] + off);
-    const uint4 w1 = *reinterpret_cast<const uint4 *>(wptr[1] + off);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const uint4 xb = *reinterpret_cast<const uint4 *>(xptr[m] + off);
-      Mma<T>::step(acc[0][m], w0, xb);
-      Mma<T>::step(acc[1][m], w1, xb);
-    }
+#define HY3_MMA(W0, W1, X, s0)                                                         \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                      \
+    if ((s0) + u < nsub) {                                                             \
+      _Pragma("unroll") for (int m = 0; m < MT; ++m) {                                 \
+        Mma<T>::step(acc[0][m], W0[u], X[u][m]);                                       \
+        Mma<T>::step(acc[1][m], W1[u], X[u][m]);                                       \
+      }                                                                                \
+    }                                                                                  \
   }
+  // Steps past nsub re-read the last step (in bounds) and are not used.
+  HY3_LOAD(aw0, aw1, ax, 0);
+  for (int s = 0; s < nsub; s += 2 * U) {
+    HY3_LOAD(bw0, bw1, bx, s + U);
+    __builtin_amdgcn_sched_barrier(0);   // keep the next block's loads ahead
+    HY3_MMA(aw0, aw1, ax, s);
+    if (s + 2 * U < nsub) { HY3_LOAD(aw0, aw1, ax, s + 2 * U); }
+    __builtin_amdgcn_sched_barrier(0);
+    HY3_MMA(bw0, bw1, bx, s + U);
+  }
+#undef HY3_MMA
+#undef HY3_LOAD
 
   // Lane holds D[col 4cg + q][token row 16m + r16].
   T *out = static_cast<T *>(a.out);
@@ -135,17 +126,38 @@ __global__ __launch_bounds__(256) void expert_skinny_kernel(ExpertArgs a, int n_
   }
 }
 
+template <typename T, bool GATE_UP, int MT>
+__global__ __launch_bounds__(256, 2) void expert_stream_kernel(ExpertArgs a, int n_col_blocks) {
+  const int lane = threadIdx.x & 63;
+  // The wavefront index is uniform; readfirstlane makes that visible to the
+  // compiler, so every unit-dependent guard below is a scalar branch.  (An
+  // MFMA is a whole-wavefront operation: it must never sit under a per-lane
+  // EXEC mask that is expected to switch it off.)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_units = a.tiles[2 * a.max_tiles] * n_col_blocks;
+  const int total_waves = gridDim.x * 4;
+  // Wavefront ids interleave the XCDs (block b runs on XCD b % 8), so the
+  // units of one expert spread over all XCDs and HBM channels.
+  for (int u = blockIdx.x * 4 + wave; u < n_units; u += total_waves) {
+    const int tile = u / n_col_blocks;
+    stream_unit<T, GATE_UP, MT>(a, tile, u - tile * n_col_blocks, lane);
+  }
+}
+
+// Persistent grid: 8 wavefronts per CU (two per SIMD) on the 256 CUs.
+constexpr int STREAM_BLOCKS = 256 * 2;
+
 template <typename T, int MT>
 hipError_t launch_skinny_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
-    const int ncb = (Imax + SKINNY_GU_COLS - 1) / SKINNY_GU_COLS;
-    hipLaunchKernelGGL((expert_skinny_kernel<T, true, MT>), dim3(a.max_tiles * ncb), dim3(256),
-                       0, stream, a, ncb);
+    const int ncb = (Imax + 15) / 16;
+    hipLaunchKernelGGL((expert_stream_kernel<T, true, MT>), dim3(STREAM_BLOCKS), dim3(256), 0,
+                       stream, a, ncb);
   } else {
-    const int ncb = (a.H + SKINNY_DN_COLS - 1) / SKINNY_DN_COLS;
-    hipLaunchKernelGGL((expert_skinny_kernel<T, false, MT>), dim3(a.max_tiles * ncb), dim3(256),
-                       0, stream, a, ncb);
+    const int ncb = (a.H + 31) / 32;
+    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT>), dim3(STREAM_BLOCKS), dim3(256), 0,
+                       stream, a, ncb);
   }
   return hipGetLastError();
 }

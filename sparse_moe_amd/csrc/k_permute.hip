@@ -13,6 +13,7 @@
 //              into exclusive per-chunk prefixes), scans the group counts into
 //              row offsets (group E = the shared expert, T rows), and writes
 //              the row-tile list of the expert GEMMs, largest groups first.
+//     (Batches with at most four chunks run all three steps in one workgroup.)
 //  3. scatter: each wavefront revisits its chunk in entry order and places
 //              entry f = t*K + j at row offsets[e] + prefix + rank, where rank
 //              counts earlier entries of the same expert.  The order within an
@@ -27,6 +28,45 @@ namespace {
 
 constexpr int MAXG = 257;   // routed experts (<= 256) + the shared expert
 
+// One wavefront counts the experts of chunk `chunk` into its LDS histogram.
+__device__ __forceinline__ void hist_chunk(const int32_t *__restrict__ idx, int N, int chunk,
+                                           int lane, int *cnt_w) {
+  const int beg = chunk * PERM_CHUNK;
+  const int end = min(N, beg + PERM_CHUNK);
+  for (int base = beg; base < end; base += 64) {
+    const int f = base + lane;
+    const bool valid = f < end;
+    const int e = valid ? idx[f] : 0;
+    const uint64_t m = match_key(e, __ballot(valid));
+    const bool leader = valid && ((m & lanemask_lt(lane)) == 0);
+    if (leader) cnt_w[e] += __popcll(m);
+  }
+}
+
+// One wavefront places the entries of chunk `chunk` in entry order; run_w[e]
+// holds the next free row of expert e for this chunk.
+__device__ __forceinline__ void scatter_chunk(const int32_t *__restrict__ idx, int N, int K,
+                                              int chunk, int lane, int *run_w,
+                                              int32_t *__restrict__ sorted_token,
+                                              int32_t *__restrict__ pos_of) {
+  const int beg = chunk * PERM_CHUNK;
+  const int end = min(N, beg + PERM_CHUNK);
+  for (int base = beg; base < end; base += 64) {
+    const int f = base + lane;
+    const bool valid = f < end;
+    const int e = valid ? idx[f] : 0;
+    const uint64_t m = match_key(e, __ballot(valid));
+    const uint64_t below = m & lanemask_lt(lane);
+    const int r0 = valid ? run_w[e] : 0;
+    if (valid) {
+      const int pos = r0 + __popcll(below);
+      sorted_token[pos] = f / K;
+      pos_of[f] = pos;
+      if (below == 0) run_w[e] = r0 + __popcll(m);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t *__restrict__ idx, int N,
                                                         int E, int nchunks,
                                                         int32_t *__restrict__ hist) {
@@ -35,18 +75,7 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t *__restric
   const int chunk = blockIdx.x * 4 + wave;
   for (int e = lane; e < 256; e += 64) cnt[wave][e] = 0;
   __syncthreads();
-  if (chunk < nchunks) {
-    const int beg = chunk * PERM_CHUNK;
-    const int end = min(N, beg + PERM_CHUNK);
-    for (int base = beg; base < end; base += 64) {
-      const int f = base + lane;
-      const bool valid = f < end;
-      const int e = valid ? idx[f] : 0;
-      const uint64_t m = match_key(e, __ballot(valid));
-      const bool leader = valid && ((m & lanemask_lt(lane)) == 0);
-      if (leader) cnt[wave][e] += __popcll(m);
-    }
-  }
+  if (chunk < nchunks) hist_chunk(idx, N, chunk, lane, cnt[wave]);
   __syncthreads();
   if (chunk < nchunks)
     for (int e = lane; e < E; e += 64) hist[(size_t)chunk * E + e] = cnt[wave][e];
@@ -85,34 +114,20 @@ __device__ void block_exclusive_scan(int *v, int n, int *total) {
   __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void perm_scan_kernel(int32_t *__restrict__ hist, int nchunks,
-                                                        int E, int T_shared, int tile_rows,
-                                                        int max_tiles,
-                                                        int32_t *__restrict__ counts,
-                                                        int32_t *__restrict__ offsets,
-                                                        int32_t *__restrict__ tiles) {
-  __shared__ int cnt[MAXG], off[MAXG + 1], ntile[MAXG], order[MAXG], tstart[MAXG + 1];
+// From per-group row counts cnt[0..E] (LDS, group E = shared expert) write
+// counts, offsets and the row-tile list (largest groups first) and leave the
+// row offsets in off[0..E+1] (LDS).  Called by all 256 threads of one block.
+__device__ void scan_groups(int *cnt, int *off, int E, int tile_rows, int max_tiles,
+                            int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                            int32_t *__restrict__ tiles) {
+  __shared__ int ntile[MAXG], order[MAXG], tstart[MAXG + 1];
   __shared__ int total_rows, total_tiles;
   const int tid = threadIdx.x;
   const int G = E + 1;
-  // 1. per-expert totals; chunk histograms become exclusive prefixes.
-  for (int e = tid; e < E; e += 256) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      int32_t *p = hist + (size_t)c * E + e;
-      const int v = *p;
-      *p = run;
-      run += v;
-    }
-    cnt[e] = run;
-  }
-  if (tid == 0) cnt[E] = T_shared;
-  __syncthreads();
   for (int g = tid; g < G; g += 256) off[g] = cnt[g];
   __syncthreads();
   block_exclusive_scan(off, G, &total_rows);
   if (tid == 0) off[G] = total_rows;
-  // 2. tiles per group, groups ranked by tile count (descending, ties by index).
   for (int g = tid; g < G; g += 256) ntile[g] = (cnt[g] + tile_rows - 1) / tile_rows;
   __syncthreads();
   for (int g = tid; g < G; g += 256) {
@@ -128,7 +143,6 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t *__restrict__ hi
   for (int r = tid; r < G; r += 256) tstart[r] = ntile[order[r]];
   __syncthreads();
   block_exclusive_scan(tstart, G, &total_tiles);
-  // 3. outputs.
   for (int g = tid; g < G; g += 256) {
     counts[g] = cnt[g];
     offsets[g] = off[g];
@@ -144,6 +158,31 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t *__restrict__ hi
     }
   }
   if (tid == 0) tiles[2 * max_tiles] = min(total_tiles, max_tiles);
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void perm_scan_kernel(int32_t *__restrict__ hist, int nchunks,
+                                                        int E, int T_shared, int tile_rows,
+                                                        int max_tiles,
+                                                        int32_t *__restrict__ counts,
+                                                        int32_t *__restrict__ offsets,
+                                                        int32_t *__restrict__ tiles) {
+  __shared__ int cnt[MAXG], off[MAXG + 1];
+  const int tid = threadIdx.x;
+  // Per-expert totals; the chunk histograms become exclusive prefixes.
+  for (int e = tid; e < E; e += 256) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      int32_t *p = hist + (size_t)c * E + e;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    cnt[e] = run;
+  }
+  if (tid == 0) cnt[E] = T_shared;
+  __syncthreads();
+  scan_groups(cnt, off, E, tile_rows, max_tiles, counts, offsets, tiles);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
@@ -156,34 +195,58 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
   if (chunk < nchunks)
     for (int e = lane; e < E; e += 64) run[wave][e] = offsets[e] + hist[(size_t)chunk * E + e];
   __syncthreads();
-  if (chunk < nchunks) {
-    const int beg = chunk * PERM_CHUNK;
-    const int end = min(N, beg + PERM_CHUNK);
-    for (int base = beg; base < end; base += 64) {
-      const int f = base + lane;
-      const bool valid = f < end;
-      const int e = valid ? idx[f] : 0;
-      const uint64_t m = match_key(e, __ballot(valid));
-      const uint64_t below = m & lanemask_lt(lane);
-      const int r0 = valid ? run[wave][e] : 0;
-      if (valid) {
-        const int pos = r0 + __popcll(below);
-        sorted_token[pos] = f / K;
-        pos_of[f] = pos;
-        if (below == 0) run[wave][e] = r0 + __popcll(m);
-      }
-    }
-  }
+  if (chunk < nchunks) scatter_chunk(idx, N, K, chunk, lane, run[wave], sorted_token, pos_of);
   // Shared-expert rows: identity.
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int base_sh = offsets[E];
   for (int t = gtid; t < T_shared; t += gridDim.x * blockDim.x) sorted_token[base_sh + t] = t;
 }
 
+// Whole permutation in one workgroup when there are at most 4 chunks
+// (T*K <= 4 * PERM_CHUNK): one launch instead of three for small batches.
+__global__ __launch_bounds__(256) void perm_small_kernel(const int32_t *__restrict__ idx, int N,
+                                                         int K, int E, int nchunks, int T_shared,
+                                                         int tile_rows, int max_tiles,
+                                                         int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ offsets,
+                                                         int32_t *__restrict__ tiles,
+                                                         int32_t *__restrict__ sorted_token,
+                                                         int32_t *__restrict__ pos_of) {
+  __shared__ int cnt[4][256];
+  __shared__ int tot[MAXG], off[MAXG + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = lane; e < 256; e += 64) cnt[wave][e] = 0;
+  __syncthreads();
+  if (wave < nchunks) hist_chunk(idx, N, wave, lane, cnt[wave]);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int run = 0;
+    for (int w = 0; w < 4; ++w) {
+      const int v = cnt[w][e];
+      cnt[w][e] = run;
+      run += v;
+    }
+    tot[e] = run;
+  }
+  if (tid == 0) tot[E] = T_shared;
+  __syncthreads();
+  scan_groups(tot, off, E, tile_rows, max_tiles, counts, offsets, tiles);
+  for (int e = lane; e < E; e += 64) cnt[wave][e] += off[e];
+  __syncthreads();
+  if (wave < nchunks) scatter_chunk(idx, N, K, wave, lane, cnt[wave], sorted_token, pos_of);
+  for (int t = tid; t < T_shared; t += 256) sorted_token[off[E] + t] = t;
+}
+
 }  // namespace
 
 hipError_t launch_permute(const PermArgs &a, hipStream_t stream) {
   const int N = a.T * a.K;
+  if (a.nchunks <= 4) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(256), 0, stream, a.idx, N, a.K, a.E,
+                       a.nchunks, a.T_shared, a.tile_rows, a.max_tiles, a.counts, a.offsets,
+                       a.tiles, a.sorted_token, a.pos_of);
+    return hipGetLastError();
+  }
   const int blocks = (a.nchunks + 3) / 4;
   hipLaunchKernelGGL(perm_hist_kernel, dim3(blocks), dim3(256), 0, stream, a.idx, N, a.E,
                      a.nchunks, a.hist);

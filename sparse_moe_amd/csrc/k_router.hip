@@ -211,9 +211,12 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float *__restrict
 }  // namespace
 
 int router_ksplit(int64_t T, int H, int E) {
+  // Enough workgroups to spread the weight read over the chip; each K-slice
+  // stays a multiple of 64 and at least 128 long.
   const int64_t tiles = ((T + RT_TOK - 1) / RT_TOK) * ((E + RT_EXP - 1) / RT_EXP);
   int S = 1;
-  while (tiles * S < 512 && (H / (2 * S)) >= 256 && (H % (2 * S * 64)) == 0) S *= 2;
+  while (S < MAX_KSPLIT && tiles * S < 256 && (H / (2 * S)) >= 128 && (H % (2 * S * 64)) == 0)
+    S *= 2;
   return S;
 }
 

@@ -44,14 +44,25 @@ __global__ __launch_bounds__(256) void select_kernel(const double *__restrict__ 
 
   double sel[4], prob[4], logit[4];
   bool live[4];
+  // Partial loads go out in blocks of 8 (all loads of a block before its
+  // adds); the adds stay in slice order.
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
     live[q] = e < E;
-    double L = 0.0;
-    if (live[q])
-      for (int s = 0; s < S; ++s) L += part[((size_t)s * T + t) * E + e];
-    logit[q] = L;
+    logit[q] = 0.0;
+  }
+  for (int s0 = 0; s0 < S; s0 += 8) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      double v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = (live[q] && s0 + j < S) ? part[((size_t)(s0 + j) * T + t) * E + e] : 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) logit[q] += v[j];
+    }
   }
   if (mode == 0) {
 #pragma unroll

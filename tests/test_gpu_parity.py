@@ -122,8 +122,9 @@ def test_forced_routing_single_expert_set(dev):
     assert (np.sort(gidx, 1) == np.array([2, 9, 13])).all()
 
 
-def test_permutation_is_exact_and_stable(dev):
-    inp = random_small(22, T=500, H=256, E=24, K=4, I=128, I_shared=128, dtype="bf16")
+@pytest.mark.parametrize("T", [500, 3000])   # one-workgroup path and three-kernel path
+def test_permutation_is_exact_and_stable(dev, T):
+    inp = random_small(22, T=T, H=256, E=24, K=4, I=128, I_shared=128, dtype="bf16")
     c = inp.cfg
     cfg = config_of(inp)
     L = sm.hy3moe_workspace_layout(cfg)
