@@ -48,7 +48,8 @@ extern "C" {
 #define HY3MOE_OK               0
 #define HY3MOE_ERR_INVALID     -1  /* null pointer, T<0, K<1, K>E, E>256, K>64, bad enum */
 #define HY3MOE_ERR_UNSUPPORTED -2  /* H, I or I_shared not a multiple of 64; T > 2^24;
-                                      H, I or I_shared > 65536; split router with fp32 x */
+                                      H, I or I_shared > 65536; T*H or H*max(I, I_shared)
+                                      elements of 4 GiB or more; split router with fp32 x */
 #define HY3MOE_ERR_WORKSPACE   -3  /* workspace smaller than hy3moe_workspace_bytes()   */
 #define HY3MOE_ERR_ALIGN       -4  /* a pointer is not 16-byte aligned                  */
 #define HY3MOE_ERR_HIP         -5  /* a kernel launch failed (hipGetLastError)          */

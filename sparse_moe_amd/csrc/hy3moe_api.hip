@@ -39,6 +39,11 @@ int validate_cfg(const hy3moe_config *c) {
   if (c->T > (int64_t(1) << 24)) return HY3MOE_ERR_UNSUPPORTED;
   if (c->router_prec == HY3MOE_ROUTER_SPLIT2_BF16 && c->dtype != HY3MOE_BF16)
     return HY3MOE_ERR_UNSUPPORTED;
+  // The expert GEMMs address x and every expert matrix with 32-bit offsets.
+  const uint64_t eb = c->dtype == HY3MOE_F32 ? 4 : 2, lim = uint64_t(1) << 32;
+  const uint64_t Imax = c->I > c->I_shared ? c->I : c->I_shared;
+  if ((uint64_t)c->T * c->H * eb >= lim || (uint64_t)c->H * Imax * eb >= lim)
+    return HY3MOE_ERR_UNSUPPORTED;
   return HY3MOE_OK;
 }
 

@@ -80,6 +80,7 @@ def test_workspace_layout_is_consistent(lib, cfg_id):
     (dict(K=0), -1), (dict(K=17, E=16), -1), (dict(E=257, K=8), -1), (dict(T=-1), -1),
     (dict(H=100), -2), (dict(I=96), -2), (dict(I_shared=32), -2), (dict(K=65, E=100), -1),
     (dict(dtype="f32", router_prec=1), -2), (dict(route_mode=3), -1),
+    (dict(T=1 << 19), -2), (dict(H=65536, I=32768, I_shared=0), -2),
 ])
 def test_invalid_configs_rejected(lib, bad, code):
     c = CONFIGS[1]
