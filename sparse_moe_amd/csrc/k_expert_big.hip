@@ -14,6 +14,9 @@
 //    LDS rows use the swizzle chunk ^ (row & 7), which makes the 16-byte
 //    operand reads of 8 consecutive rows and the wavefront's writes
 //    conflict-free, and every LDS access a base register plus an immediate.
+//  * The instruction order of a stage is pinned (see stage_schedule): the
+//    global loads go out spread over the whole stage and the LDS writes over
+//    its second half, so a load has about a stage and a half to land.
 //  * Global addresses are a uniform base per matrix plus 32-bit per-thread
 //    offsets.
 //  * Workgroups are remapped so that consecutive logical tiles run on the
@@ -36,6 +39,34 @@ constexpr int RB = 128;          // bytes of K per row per stage
 constexpr int CH = RB / 16;      // 16-byte chunks per row per stage (8)
 constexpr int ROWS = BW + BTK;   // LDS rows per stage
 constexpr int BAND = 4;          // row tiles per band of the tile order
+
+// One group of the stage's instruction order: G global loads, 4 MFMAs, R LDS
+// operand reads, W LDS writes (scheduling-group masks: 0x020 global reads,
+// 0x008 MFMA, 0x100 LDS reads, 0x200 LDS writes).
+template <int G, int R, int W>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (G > 0) __builtin_amdgcn_sched_group_barrier(0x020, G, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  if constexpr (W > 0) __builtin_amdgcn_sched_group_barrier(0x200, W, 0);
+}
+
+// Order of one bf16 stage per wavefront: 64 MFMAs in two k-halves of 8 groups
+// of 4 (one A fragment against the 4 B fragments), the 24 operand reads two
+// groups ahead of their MFMAs (6 at the start of each half), one of the 8
+// global loads (stage k + 2) every 8 MFMAs, and the 8 LDS writes (stage k + 1)
+// one per group of the second half.  Left to itself the compiler sinks the
+// global loads to the end of the stage and hoists the LDS writes that wait
+// for the previous loads into the middle of the next stage, which leaves a
+// load about half a stage to land.
+__device__ __forceinline__ void stage_schedule() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  sched_group<1, 1, 0>(); sched_group<0, 1, 0>(); sched_group<1, 1, 0>(); sched_group<0, 1, 0>();
+  sched_group<1, 1, 0>(); sched_group<0, 1, 0>(); sched_group<1, 0, 0>(); sched_group<0, 0, 0>();
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  sched_group<1, 1, 1>(); sched_group<0, 1, 1>(); sched_group<1, 1, 1>(); sched_group<0, 1, 1>();
+  sched_group<1, 1, 1>(); sched_group<0, 1, 1>(); sched_group<1, 0, 1>(); sched_group<0, 0, 1>();
+}
 
 template <typename T, bool GATE_UP>
 __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_col_tiles) {
@@ -170,6 +201,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     HY3_GLOAD(S, ((k) + 2 < nk) ? (k) + 2 : 0);                                        \
     HY3_COMPUTE(B);                                                                    \
     HY3_LSTORE(SN, (B) ^ 1);                                                           \
+    if constexpr (sizeof(T) == 2) stage_schedule();                                    \
     __syncthreads();                                                                   \
   }
 

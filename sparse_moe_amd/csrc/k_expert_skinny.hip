@@ -25,9 +25,12 @@ namespace hy3moe {
 
 namespace {
 
+constexpr int UBASE = 8;          // 64-byte K steps per register set (one row fragment)
+constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
+
 template <typename T, bool GATE_UP, int MT>
 __device__ __forceinline__ void stream_unit(const ExpertArgs &a, int tile, int cb, int lane) {
-  constexpr int U = 8 / MT;   // 64-byte K steps per row per register set
+  constexpr int U = UBASE / MT;   // 64-byte K steps per row per register set
   const int g = a.tiles[2 * tile];
   const int row0 = a.tiles[2 * tile + 1];
   const int grp_end = a.offsets[g + 1];
@@ -127,7 +130,8 @@ __device__ __forceinline__ void stream_unit(const ExpertArgs &a, int tile, int c
 }
 
 template <typename T, bool GATE_UP, int MT>
-__global__ __launch_bounds__(256, 2) void expert_stream_kernel(ExpertArgs a, int n_col_blocks) {
+__global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(ExpertArgs a,
+                                                                          int n_col_blocks) {
   const int lane = threadIdx.x & 63;
   // The wavefront index is uniform; readfirstlane makes that visible to the
   // compiler, so every unit-dependent guard below is a scalar branch.  (An
@@ -144,8 +148,8 @@ __global__ __launch_bounds__(256, 2) void expert_stream_kernel(ExpertArgs a, int
   }
 }
 
-// Persistent grid: 8 wavefronts per CU (two per SIMD) on the 256 CUs.
-constexpr int STREAM_BLOCKS = 256 * 2;
+// Persistent grid: WAVES_PER_SIMD wavefronts per SIMD on the 256 CUs.
+constexpr int STREAM_BLOCKS = 256 * WAVES_PER_SIMD;
 
 template <typename T, int MT>
 hipError_t launch_skinny_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
