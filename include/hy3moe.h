@@ -124,6 +124,8 @@ typedef struct hy3moe_ws_layout {
   int32_t tile_rows;     /* rows per tile of the expert GEMMs for this T       */
   size_t h;              /* dtype [R][I_max]  SwiGLU activations, I_max = max(I, I_shared) */
   size_t y;              /* dtype [R][H]      expert outputs before the combine */
+  size_t w_planes;       /* bf16 [3][E][H] router weight split into bf16 terms, used
+                            for bf16 batches of T >= 1024 (0 = not used)           */
 } hy3moe_ws_layout;
 
 /* Workspace size in bytes for hy3moe_forward (for_forward != 0) or for

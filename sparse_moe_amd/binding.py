@@ -24,6 +24,7 @@ HY3MOE_ROUTER_FP32 = 0
 HY3MOE_ROUTER_SPLIT2_BF16 = 1
 
 HY3MOE_N_STAGES = 6
+ABI_VERSION = 2          # hy3moe_abi_version() of the library this binding matches
 STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 
 EXPORTED_SYMBOLS = (
@@ -56,6 +57,7 @@ class hy3moe_ws_layout(ctypes.Structure):
         ("hist", ctypes.c_size_t), ("n_chunks", ctypes.c_int32),
         ("tiles", ctypes.c_size_t), ("max_tiles", ctypes.c_int32),
         ("tile_rows", ctypes.c_int32), ("h", ctypes.c_size_t), ("y", ctypes.c_size_t),
+        ("w_planes", ctypes.c_size_t),
     ]
 
 
@@ -106,7 +108,7 @@ def load() -> ctypes.CDLL:
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p,
                                        ctypes.POINTER(ctypes.c_void_p)]
-    if L.hy3moe_abi_version() != 1:
+    if L.hy3moe_abi_version() != ABI_VERSION:
         raise RuntimeError("libhy3moe ABI version mismatch")
     _LIB = L
     return L

@@ -57,6 +57,9 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
   L->logits_part = off; off += al((size_t)L->n_ksplit * T * E * 8);
   L->idx = off;         off += al((size_t)N * 4);
   L->weight = off;      off += al((size_t)N * 4);
+  if (router_use_planes(T, c->dtype)) {
+    L->w_planes = off;  off += al((size_t)3 * E * H * 2);
+  }
   if (!for_forward) { L->total = off; return; }
   L->n_chunks = (int32_t)((N + PERM_CHUNK - 1) / PERM_CHUNK);
   L->hist = off;        off += al((size_t)L->n_chunks * E * 4);
@@ -91,7 +94,7 @@ int check_launch(hipError_t e) { return e == hipSuccess ? HY3MOE_OK : HY3MOE_ERR
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 1; }
+int hy3moe_abi_version(void) { return 2; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {
@@ -137,7 +140,8 @@ int hy3moe_route(const hy3moe_config *cfg, const void *x, const float *w_router,
   char *ws = static_cast<char *>(workspace);
   const int T = (int)cfg->T;
   double *part = reinterpret_cast<double *>(ws + L.logits_part);
-  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w_router, part, T, cfg->H,
+  uint16_t *planes = L.w_planes ? reinterpret_cast<uint16_t *>(ws + L.w_planes) : nullptr;
+  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w_router, planes, part, T, cfg->H,
                                   cfg->E, L.n_ksplit, s));
   if (rc) return rc;
   const float *bias = cfg->route_mode == HY3MOE_ROUTE_SIGMOID_BIAS ? expert_bias : nullptr;
@@ -170,6 +174,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   char *ws = static_cast<char *>(workspace);
   const int T = (int)cfg->T, H = cfg->H, E = cfg->E, K = cfg->K;
   double *part = reinterpret_cast<double *>(ws + L.logits_part);
+  uint16_t *planes = L.w_planes ? reinterpret_cast<uint16_t *>(ws + L.w_planes) : nullptr;
   int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(ws + L.idx);
   float *weight = weight_out ? weight_out : reinterpret_cast<float *>(ws + L.weight);
 
@@ -180,7 +185,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   };
   mark();
   // 1-2. gate
-  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w->w_router, part, T, H, E,
+  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w->w_router, planes, part, T, H, E,
                                   L.n_ksplit, s));
   if (rc) return rc;
   mark();

@@ -30,9 +30,13 @@ inline int expert_path(int64_t T, int K, int E) {
 }
 
 // Router -------------------------------------------------------------------
+constexpr int ROUTER_PLANES_MIN_T = 1024;  // bf16 batches this large pre-split the weight
+bool router_use_planes(int64_t T, int dtype);
 int router_ksplit(int64_t T, int H, int E);
+// planes: workspace for the bf16 weight planes [3][E][H], or null (split on the fly).
 hipError_t launch_router(const void *x, int dtype, int router_prec, const float *w_router,
-                         double *part, int T, int H, int E, int S, hipStream_t stream);
+                         uint16_t *planes, double *part, int T, int H, int E, int S,
+                         hipStream_t stream);
 
 // Score + top-K select ------------------------------------------------------
 hipError_t launch_select(const double *part, int S, int T, int E, int K, const float *bias,

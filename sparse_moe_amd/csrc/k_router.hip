@@ -18,6 +18,14 @@
 // The x tile is staged through LDS (shared by the 4 waves); each wave reads
 // its own 16 expert rows of W straight from global memory.
 //
+// Large batches (router_planes): every token tile would repeat the same split
+// of the same weight, so the split runs once per call into bf16 planes
+// [NP][E][H] in the workspace, and the GEMM streams the planes with the next
+// K step's weight fragments and the x tile after it already in flight (x
+// double-buffered in LDS).  The mid and lo products share one fp32
+// accumulator there (their sum is 2^-8 of the logit, so its rounding is far
+// below the hi accumulator's); the fp64 folding is the same.
+//
 // Accuracy: MFMA accumulates in fp32 over chunks of RT_CHUNK k values only;
 // each chunk sum is added into a float64 running total, and the K-slice
 // partials are written in float64 and summed by the select kernel in slice
@@ -208,22 +216,199 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float *__restrict
   }
 }
 
+// fp32 weight -> bf16 planes, 8 elements per thread.  PREC 0: hi, mid, lo
+// (exact three-term split); PREC 1: hi and bf16(256 (w - hi)).
+template <int PREC>
+__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ wr,
+                                                           uint16_t *__restrict__ planes,
+                                                           int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const float4 a = *reinterpret_cast<const float4 *>(wr + i);
+  const float4 b = *reinterpret_cast<const float4 *>(wr + i + 4);
+  const float wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint16_t th[8], tm[8], tl[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (PREC == 0) {
+      split3(wv[j], th[j], tm[j], tl[j]);
+    } else {
+      th[j] = f32_to_bf16(wv[j]);
+      tm[j] = f32_to_bf16((wv[j] - bf16_to_f32(th[j])) * 256.0f);
+    }
+  }
+  *reinterpret_cast<uint4 *>(planes + i) =
+      make_uint4(pack2(th[0], th[1]), pack2(th[2], th[3]), pack2(th[4], th[5]), pack2(th[6], th[7]));
+  *reinterpret_cast<uint4 *>(planes + n + i) =
+      make_uint4(pack2(tm[0], tm[1]), pack2(tm[2], tm[3]), pack2(tm[4], tm[5]), pack2(tm[6], tm[7]));
+  if (PREC == 0)
+    *reinterpret_cast<uint4 *>(planes + 2 * n + i) =
+        make_uint4(pack2(tl[0], tl[1]), pack2(tl[2], tl[3]), pack2(tl[4], tl[5]), pack2(tl[6], tl[7]));
+}
+
+// Router GEMM on pre-split bf16 planes.  K steps of 64: the weight fragments
+// of step st+1 are loaded while step st computes (two register sets), the x
+// tile of step st+2 goes to registers and is written to the idle LDS buffer
+// at the end of step st+1.  Loads past the last step re-read it (in bounds,
+// unused) so that no load is conditional, and a scheduling barrier keeps them
+// at the top of the step.  The loop body is one fp64 fold period (4 steps),
+// so the fold needs no branch.  Token rows past T re-read row T-1 and are
+// not stored.
+template <int PREC>
+__global__ __launch_bounds__(256, 2) void router_planes_kernel(const uint16_t *__restrict__ x,
+                                                               const uint16_t *__restrict__ wp,
+                                                               double *__restrict__ part, int T,
+                                                               int H, int E, int kslice) {
+  constexpr int NP = (PREC == 0) ? 3 : 2;
+  constexpr int XB = RT_TOK * 8;   // uint4 per LDS buffer
+  constexpr int FOLD = RT_CHUNK / 64;
+  __shared__ uint4 xs[2 * XB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RT_TOK, e0 = blockIdx.y * RT_EXP, s = blockIdx.z;
+  const int kbeg = s * kslice;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int e_row = min(e0 + wave * 16 + r16, E - 1);
+  const uint32_t pstride = (uint32_t)(E * H);   // elements per plane (< 2^24)
+  const uint16_t *wrow = wp + (size_t)e_row * H + kbeg + g * 8;
+  const int xrow = tid >> 3, xc = tid & 7;
+  const uint16_t *xp0 = x + (size_t)min(t0 + xrow, T - 1) * H + kbeg + xc * 8;
+  const uint16_t *xp1 = x + (size_t)min(t0 + xrow + 32, T - 1) * H + kbeg + xc * 8;
+  const int xw0 = swz(xrow, xc), xw1 = swz(xrow + 32, xc);
+  const int n = kslice / 64;
+
+  f32x4_t ahi[4], alo[4];
+  double tot[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ahi[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    alo[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tot[j][q] = 0.0;
+  }
+  // Register sets A and B: weight fragments w<set><sub><plane>, x chunks x<set><0|1>.
+  uint4 wA00, wA01, wA02, wA10, wA11, wA12, xA0, xA1;
+  uint4 wB00, wB01, wB02, wB10, wB11, wB12, xB0, xB1;
+
+#define HY3_W(st, sub, p) \
+  (*reinterpret_cast<const uint4 *>(wrow + (p) * pstride + (uint32_t)((st) * 64 + (sub) * 32)))
+#define HY3_LOADW(S, st)                                                               \
+  {                                                                                    \
+    const int st_ = (st);                                                              \
+    w##S##00 = HY3_W(st_, 0, 0); w##S##01 = HY3_W(st_, 0, 1);                          \
+    w##S##10 = HY3_W(st_, 1, 0); w##S##11 = HY3_W(st_, 1, 1);                          \
+    if (NP == 3) { w##S##02 = HY3_W(st_, 0, 2); w##S##12 = HY3_W(st_, 1, 2); }         \
+  }
+#define HY3_LOADX(S, st)                                                               \
+  {                                                                                    \
+    const int st_ = (st);                                                              \
+    x##S##0 = *reinterpret_cast<const uint4 *>(xp0 + st_ * 64);                        \
+    x##S##1 = *reinterpret_cast<const uint4 *>(xp1 + st_ * 64);                        \
+  }
+#define HY3_SUB(S, sub, buf)                                                           \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                      \
+    const uint4 xv = xs[(buf) * XB + swz(j * 16 + r16, (sub) * 4 + g)];                \
+    Mma<bf16_t>::step(ahi[j], w##S##sub##0, xv);                                       \
+    Mma<bf16_t>::step(alo[j], w##S##sub##1, xv);                                       \
+    if (NP == 3) Mma<bf16_t>::step(alo[j], w##S##sub##2, xv);                          \
+  }
+// Step st with its weights in set C and the x of step st+1 in set N.
+#define HY3_STEP(st, C, N, buf)                                                        \
+  {                                                                                    \
+    HY3_LOADW(N, min((st) + 1, n - 1));                                                \
+    HY3_LOADX(C, min((st) + 2, n - 1));                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    HY3_SUB(C, 0, buf);                                                                \
+    HY3_SUB(C, 1, buf);                                                                \
+    xs[((buf) ^ 1) * XB + xw0] = x##N##0;                                              \
+    xs[((buf) ^ 1) * XB + xw1] = x##N##1;                                              \
+    __syncthreads();                                                                   \
+  }
+#define HY3_FOLD()                                                                     \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                      \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                    \
+      if (PREC == 0)                                                                   \
+        tot[j][q] += (double)ahi[j][q] + (double)alo[j][q];                            \
+      else                                                                             \
+        tot[j][q] = __builtin_fma((double)alo[j][q], 1.0 / 256.0, tot[j][q] + (double)ahi[j][q]); \
+    }                                                                                  \
+    ahi[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};                                              \
+    alo[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};                                              \
+  }
+
+  HY3_LOADW(A, 0);
+  HY3_LOADX(A, 0);
+  HY3_LOADX(B, min(1, n - 1));
+  xs[xw0] = xA0;
+  xs[xw1] = xA1;
+  __syncthreads();
+  static_assert(FOLD == 4, "loop body is one fold period of 4 steps");
+  int st = 0;
+  for (; st + FOLD <= n; st += FOLD) {
+    HY3_STEP(st, A, B, 0);
+    HY3_STEP(st + 1, B, A, 1);
+    HY3_STEP(st + 2, A, B, 0);
+    HY3_STEP(st + 3, B, A, 1);
+    HY3_FOLD();
+  }
+  if (st < n) {   // 1..3 remaining steps (kslice not a multiple of 256)
+    HY3_STEP(st, A, B, 0);
+    if (st + 1 < n) HY3_STEP(st + 1, B, A, 1);
+    if (st + 2 < n) HY3_STEP(st + 2, A, B, 0);
+    HY3_FOLD();
+  }
+#undef HY3_FOLD
+#undef HY3_STEP
+#undef HY3_SUB
+#undef HY3_LOADX
+#undef HY3_LOADW
+#undef HY3_W
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + j * 16 + r16;
+    if (t >= T) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + wave * 16 + 4 * g + q;
+      if (e < E) part[((size_t)s * T + t) * E + e] = tot[j][q];
+    }
+  }
+}
+
 }  // namespace
+
+bool router_use_planes(int64_t T, int dtype) { return dtype == DT_BF16 && T >= ROUTER_PLANES_MIN_T; }
 
 int router_ksplit(int64_t T, int H, int E) {
   // Enough workgroups to spread the weight read over the chip; each K-slice
   // stays a multiple of 64 and at least 128 long.
   const int64_t tiles = ((T + RT_TOK - 1) / RT_TOK) * ((E + RT_EXP - 1) / RT_EXP);
   int S = 1;
-  while (S < MAX_KSPLIT && tiles * S < 256 && (H / (2 * S)) >= 128 && (H % (2 * S * 64)) == 0)
+  while (S < MAX_KSPLIT && tiles * S < 512 && (H / (2 * S)) >= 128 && (H % (2 * S * 64)) == 0)
     S *= 2;
   return S;
 }
 
-hipError_t launch_router(const void *x, int dtype, int router_prec, const float *wr, double *part,
-                         int T, int H, int E, int S, hipStream_t stream) {
+hipError_t launch_router(const void *x, int dtype, int router_prec, const float *wr,
+                         uint16_t *planes, double *part, int T, int H, int E, int S,
+                         hipStream_t stream) {
   const int kslice = H / S;
   dim3 grid((T + RT_TOK - 1) / RT_TOK, (E + RT_EXP - 1) / RT_EXP, S);
+  if (planes) {
+    const int64_t n = (int64_t)E * H;
+    const dim3 sgrid((unsigned)((n / 8 + 255) / 256));
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    if (router_prec == 0) {
+      hipLaunchKernelGGL(router_split_kernel<0>, sgrid, dim3(256), 0, stream, wr, planes, n);
+      hipLaunchKernelGGL(router_planes_kernel<0>, grid, dim3(256), 0, stream, xb, planes, part,
+                         T, H, E, kslice);
+    } else {
+      hipLaunchKernelGGL(router_split_kernel<1>, sgrid, dim3(256), 0, stream, wr, planes, n);
+      hipLaunchKernelGGL(router_planes_kernel<1>, grid, dim3(256), 0, stream, xb, planes, part,
+                         T, H, E, kslice);
+    }
+    return hipGetLastError();
+  }
   if (dtype == DT_F32) {
     hipLaunchKernelGGL(router_f32_kernel, grid, dim3(256), 0, stream,
                        static_cast<const float *>(x), wr, part, T, H, E, kslice);

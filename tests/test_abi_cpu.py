@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == 1
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 2
     for code in (0, -1, -2, -3, -4, -5):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -64,10 +64,14 @@ def test_workspace_layout_is_consistent(lib, cfg_id):
     assert 0 < sm.hy3moe_workspace_bytes(cfg, False) <= L.total
     names = ["logits_part", "idx", "weight", "hist", "counts", "offsets", "sorted_token",
              "pos_of", "tiles", "h", "y"]
+    c = CONFIGS[cfg_id]
+    planes = c.dtype == "bf16" and c.T >= 1024
+    assert (L.w_planes > 0) == planes
+    if planes:
+        names.append("w_planes")
     offs = sorted(getattr(L, n) for n in names)
     assert all(o % 256 == 0 for o in offs)
     assert len(set(offs)) == len(offs)
-    c = CONFIGS[cfg_id]
     R = c.T * c.K + (c.T if c.I_shared else 0)
     eb = 2 if c.dtype == "bf16" else 4
     assert L.total - L.y >= R * c.H * eb
