@@ -35,6 +35,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two floats -> packed bfloat16 pair (a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {
   static constexpr int kPerChunk = 8;   // elements in 16 bytes
@@ -66,8 +71,8 @@ template <> struct Mma<float> {
 // Store four consecutive output values (one lane's column of a 16x16 tile).
 __device__ __forceinline__ void store4(bf16_t *p, float a, float b, float c, float d) {
   uint2 v;
-  v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-  v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+  v.x = pack_bf16x2(a, b);
+  v.y = pack_bf16x2(c, d);
   *reinterpret_cast<uint2 *>(p) = v;
 }
 __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {

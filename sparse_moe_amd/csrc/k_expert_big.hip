@@ -222,30 +222,79 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
 
   // ---- epilogue: lane holds D[weight row 16i + 4cg + q][token row 16j + r16] ----
   T *out = static_cast<T *>(a.out);
+  if constexpr (sizeof(T) == 2) {
+    // Through LDS (free after the loop's last barrier): each lane writes its
+    // 4-column pieces into bf16 token rows (16-byte chunks swizzled by row),
+    // then each thread stores whole 16-byte chunks, so a wavefront writes two
+    // full output rows per instruction instead of 32-byte pieces of 16 rows.
+    constexpr int OC = GATE_UP ? BW / 2 / 8 : BW / 8;   // 16-byte chunks per tile row
+    char *stg = reinterpret_cast<char *>(lds);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int trow = row0 + wt_ * 64 + j * 16 + r16;
-    if (trow >= grp_end) continue;
-    if (GATE_UP) {
-      // wavefront wr_ holds weight rows 128 wr_ + [0, 128): frags i = 0,1 are
-      // gate cols col0 + 64 wr_ + [0, 32), i = 2,3 their up cols, i = 4,5 gate
-      // cols col0 + 64 wr_ + [32, 64), i = 6,7 their up cols.
+    for (int j = 0; j < 4; ++j) {
+      const int r = wt_ * 64 + j * 16 + r16;
+      char *row = stg + r * OC * 16;
+      if (GATE_UP) {
+        // wavefront wr_ holds weight rows 128 wr_ + [0, 128): frags i = 0,1 are
+        // gate cols 64 wr_ + [0, 32), i = 2,3 their up cols, i = 4,5 gate cols
+        // 64 wr_ + [32, 64), i = 6,7 their up cols.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gi = (i >> 1) * 4 + (i & 1);
-        const int c = col0 + wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
-        if (c >= Ig) continue;
-        const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
-        store4(out + (size_t)trow * a.ldh + c, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
-               swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
+        for (int i = 0; i < 4; ++i) {
+          const int gi = (i >> 1) * 4 + (i & 1);
+          const int c = wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
+          const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
+          uint2 v;
+          v.x = pack_bf16x2(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]));
+          v.y = pack_bf16x2(swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
+          *reinterpret_cast<uint2 *>(row + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = v;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = wr_ * 128 + i * 16 + 4 * cg;
+          const f32x4_t v4 = acc[i][j];
+          uint2 v;
+          v.x = pack_bf16x2(v4[0], v4[1]);
+          v.y = pack_bf16x2(v4[2], v4[3]);
+          *reinterpret_cast<uint2 *>(row + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = v;
+        }
       }
-    } else {
+    }
+    __syncthreads();
+    const int width = GATE_UP ? Ig : a.H;           // output columns of this matrix
+    const size_t ldo = GATE_UP ? (size_t)a.ldh : (size_t)a.H;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int n = col0 + wr_ * 128 + i * 16 + 4 * cg;
-        if (n >= a.H) continue;
-        const f32x4_t v = acc[i][j];
-        store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
+    for (int m = 0; m < 256 * OC / 512; ++m) {
+      const int q = tid + 512 * m;
+      const int r = q / OC, ch = q % OC;
+      const int c = col0 + ch * 8;
+      if (row0 + r < grp_end && c < width) {
+        const uint4 v = lds[r * OC + (ch ^ (r & 7))];
+        *reinterpret_cast<uint4 *>(out + (size_t)(row0 + r) * ldo + c) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int trow = row0 + wt_ * 64 + j * 16 + r16;
+      if (trow >= grp_end) continue;
+      if (GATE_UP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int gi = (i >> 1) * 4 + (i & 1);
+          const int c = col0 + wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
+          if (c >= Ig) continue;
+          const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
+          store4(out + (size_t)trow * a.ldh + c, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
+                 swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int n = col0 + wr_ * 128 + i * 16 + 4 * cg;
+          if (n >= a.H) continue;
+          const f32x4_t v = acc[i][j];
+          store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
+        }
       }
     }
   }
