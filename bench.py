@@ -164,7 +164,9 @@ def main():
                 "per_unit": f"{2 * I * H * eb} B of gate+up weights per touched expert "
                             f"x {groups} experts + x and h rows"}
     else:
-        roof = {"kernel": "gate_up (tiled grouped GEMM + SwiGLU)", "bound": "mfma",
+        tile_rows = sm.hy3moe_workspace_layout(cfg).tile_rows
+        path = "256x256-tile" if tile_rows == 256 else "128x128-tile"
+        roof = {"kernel": f"gate_up ({path} grouped GEMM + SwiGLU)", "bound": "mfma",
                 "achieved": gu_flops / gu_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "per_unit": f"{4 * H * I} FLOP per routed row x {T * K} rows + "
                             f"{4 * H * Is} per shared row x {T}"}
@@ -210,8 +212,9 @@ def main():
 
 def ceilings(dev):
     """Achievable ceilings on this GPU: a dense bf16 MFMA microkernel (register
-    operands only, 16 independent chains per wavefront) and a 16-byte-per-lane
-    device copy of 4 GiB (read + write bytes counted)."""
+    operands only, 16 independent chains per wavefront), a 16-byte-per-lane
+    device copy of 4 GiB (read + write bytes counted) and a streaming read of
+    the same 4 GiB."""
     import ctypes
 
     import torch
@@ -251,6 +254,22 @@ def ceilings(dev):
         res[f"copy_GBs_{blocks}blk"] = gbs
         best = max(best, gbs)
     res["copy_GBs_best"] = best
+    L.hy3moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    best = 0.0
+    for blocks in (1024, 2048, 4096, 8192):
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        assert L.hy3moe_probe_read(src.data_ptr(), n, blocks, out.data_ptr(), s) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            L.hy3moe_probe_read(src.data_ptr(), n, blocks, out.data_ptr(), s)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = n * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+        res[f"read_GBs_{blocks}blk"] = gbs
+        best = max(best, gbs)
+    res["read_GBs_best"] = best
     res["mfma_bf16_tflops_best"] = max(v for k, v in res.items() if k.startswith("mfma"))
     res["peak_published"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_GBs": PEAK_HBM_GBS}
     return res

@@ -1,6 +1,7 @@
 // Achievable-ceiling probes for the roofline (measurement helpers, not part
 // of the MoE layer): a dense bf16 MFMA microkernel with register operands
-// only, and a 16-byte-per-lane device copy.  Built into libhy3moe_probe.so.
+// only, a 16-byte-per-lane device copy, and a 16-byte-per-lane streaming read
+// (the bound of the weight-streaming GEMMs).  Built into libhy3moe_probe.so.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,6 +41,22 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src
   for (; i < n; i += stride) dst[i] = src[i];
 }
 
+// Reads n16 16-byte chunks, 4 per thread per step in flight, and writes one
+// word per thread (so the loads are not removed).
+__global__ __launch_bounds__(256) void read_kernel(const uint4 *__restrict__ src, size_t n16,
+                                                   uint32_t *__restrict__ out) {
+  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  size_t i = tid;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a.x ^ b.y ^ c.z ^ d.w;
+  }
+  for (; i < n16; i += stride) acc ^= src[i].x;
+  out[tid] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -58,6 +75,15 @@ int hy3moe_probe_copy(const void *src, void *dst, size_t bytes, int n_blocks, vo
   if (!src || !dst || (bytes & 15) || n_blocks <= 0) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(copy_kernel, dim3(n_blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
+  return (int)hipGetLastError();
+}
+
+// Reads `bytes` (multiple of 16) from src with n_blocks x 256 threads; out
+// holds n_blocks x 256 words.
+int hy3moe_probe_read(const void *src, size_t bytes, int n_blocks, void *out, void *stream) {
+  if (!src || !out || (bytes & 15) || n_blocks <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_kernel, dim3(n_blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4 *>(src), bytes / 16, static_cast<uint32_t *>(out));
   return (int)hipGetLastError();
 }
 

@@ -269,7 +269,12 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
       const int c = col0 + ch * 8;
       if (row0 + r < grp_end && c < width) {
         const uint4 v = lds[r * OC + (ch ^ (r & 7))];
-        *reinterpret_cast<uint4 *>(out + (size_t)(row0 + r) * ldo + c) = v;
+        uint4 *dst = reinterpret_cast<uint4 *>(out + (size_t)(row0 + r) * ldo + c);
+        // written once, read by the next kernel: non-temporal
+        __builtin_nontemporal_store(v.x, &dst->x);
+        __builtin_nontemporal_store(v.y, &dst->y);
+        __builtin_nontemporal_store(v.z, &dst->z);
+        __builtin_nontemporal_store(v.w, &dst->w);
       }
     }
   } else {

@@ -1,37 +1,14 @@
-// Scores, top-K selection and combine weights, one wavefront per token.
-//
-// Sigmoid mode (hy3 README "Model facts", MoE routing row; HYV3Config
-// moe_router_use_sigmoid / route_norm / router_scaling_factor):
-//   s = sigmoid(logit);  pick the K largest of s + expert_bias;
-//   w_j = scale * s[pick_j] / sum_j' s[pick_j'].
-// Softmax mode (HunyuanImage 3.0 MoE reading, easy_topk):
-//   p = softmax(logits);  pick the K largest p;
-//   w_j = p[pick_j] / max(sum_j' p[pick_j'], renorm_eps).
-//
-// The router's float64 K-slice partial sums are added in slice order and
-// the scores are evaluated in float64, so the selection is decided on
-// fp32-accurate logits with no further rounding.  Picks come out in
-// descending selection score; equal scores go to the lower expert index.
-// Each lane owns experts lane, lane+64, lane+128, lane+192 (E <= 256); the
-// arg-max of every round is a butterfly over the wavefront.
+// Scores, top-K selection and combine weights, one wavefront per token (the
+// per-token steps are in select_token.cuh).
 #include "common.cuh"
 #include "internal.h"
+#include "select_token.cuh"
 
 namespace hy3moe {
 
 namespace {
 
-__device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
-  return v;
-}
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
+template <int SB>
 __global__ __launch_bounds__(256) void select_kernel(const double *__restrict__ part, int S, int T,
                                                      int E, int K,
                                                      const float *__restrict__ bias, int mode,
@@ -41,91 +18,7 @@ __global__ __launch_bounds__(256) void select_kernel(const double *__restrict__ 
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;   // whole wavefront leaves together
-
-  double sel[4], prob[4], logit[4];
-  bool live[4];
-  // Partial loads go out in blocks of 8 (all loads of a block before its
-  // adds); the adds stay in slice order.
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    live[q] = e < E;
-    logit[q] = 0.0;
-  }
-  for (int s0 = 0; s0 < S; s0 += 8) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      double v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[j] = (live[q] && s0 + j < S) ? part[((size_t)(s0 + j) * T + t) * E + e] : 0.0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) logit[q] += v[j];
-    }
-  }
-  if (mode == 0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      prob[q] = 1.0 / (1.0 + exp(-logit[q]));
-      sel[q] = live[q] ? prob[q] + (bias ? (double)bias[e] : 0.0) : -INFINITY;
-    }
-  } else {
-    double m = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) if (live[q]) m = fmax(m, logit[q]);
-    m = wave_max(m);
-    double z = 0.0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      prob[q] = live[q] ? exp(logit[q] - m) : 0.0;
-      z += prob[q];
-    }
-    z = wave_sum(z);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      prob[q] = prob[q] / z;
-      sel[q] = live[q] ? prob[q] : -INFINITY;
-    }
-  }
-
-  bool taken[4] = {false, false, false, false};
-  int my_pick = -1;
-  double my_prob = 0.0, tot = 0.0;
-  for (int j = 0; j < K; ++j) {
-    double bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (live[q] && !taken[q] && sel[q] > bv) { bv = sel[q]; be = lane + 64 * q; }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
-    // Every lane now agrees on the winner be.
-    const int owner = be & 63, slot = be >> 6;
-    double p = 0.0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) if (q == slot) p = prob[q];
-    p = __shfl(p, owner, 64);
-    if (lane == owner) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) if (q == slot) taken[q] = true;
-    }
-    if (lane == j) { my_pick = be; my_prob = p; }
-    tot += p;
-  }
-  if (lane < K) {
-    double w;
-    if (mode == 0) w = (double)scale * (my_prob / tot);
-    else w = my_prob / fmax(tot, (double)renorm_eps);
-    idx_out[(size_t)t * K + lane] = my_pick;
-    w_out[(size_t)t * K + lane] = (float)w;
-  }
+  select_token<SB>(part, S, T, E, K, bias, mode, scale, renorm_eps, t, lane, idx_out, w_out);
 }
 
 }  // namespace
@@ -133,8 +26,16 @@ __global__ __launch_bounds__(256) void select_kernel(const double *__restrict__ 
 hipError_t launch_select(const double *part, int S, int T, int E, int K, const float *bias,
                          int route_mode, float scale, float renorm_eps, int32_t *idx,
                          float *weight, hipStream_t stream) {
-  hipLaunchKernelGGL(select_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, part, S, T, E, K,
-                     bias, route_mode, scale, renorm_eps, idx, weight);
+  // S is a power of two <= MAX_KSPLIT: load min(S, 8) slices per round.
+  const dim3 grid((T + 3) / 4);
+#define HY3_SEL(SB)                                                                    \
+  hipLaunchKernelGGL(select_kernel<SB>, grid, dim3(256), 0, stream, part, S, T, E, K, bias, \
+                     route_mode, scale, renorm_eps, idx, weight)
+  if (S >= 8) HY3_SEL(8);
+  else if (S == 4) HY3_SEL(4);
+  else if (S == 2) HY3_SEL(2);
+  else HY3_SEL(1);
+#undef HY3_SEL
   return hipGetLastError();
 }
 
