@@ -209,6 +209,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   pa.nchunks = L.n_chunks;
   pa.tile_rows = L.tile_rows;
   pa.max_tiles = L.max_tiles;
+  pa.sort_tiles = expert_path(T, K, E) != PATH_SKINNY;
   rc = check_launch(launch_permute(pa, s));
   if (rc) return rc;
   mark();

@@ -53,6 +53,7 @@ struct PermArgs {
   int32_t *pos_of;        // [T*K]
   int32_t *tiles;         // [2*max_tiles + 1]
   int T, K, E, T_shared, nchunks, tile_rows, max_tiles;
+  int sort_tiles;         // tile list largest groups first (else group order)
 };
 hipError_t launch_permute(const PermArgs &a, hipStream_t stream);
 

@@ -12,7 +12,9 @@
 //  2. scan:    one workgroup sums the chunk histograms per expert (turning them
 //              into exclusive per-chunk prefixes), scans the group counts into
 //              row offsets (group E = the shared expert, T rows), and writes
-//              the row-tile list of the expert GEMMs, largest groups first.
+//              the row-tile list of the expert GEMMs, largest groups first for
+//              the tile-grid paths (group order for the weight-streaming path,
+//              whose work units do not depend on the tile order).
 //     (Batches with at most four chunks run all three steps in one workgroup.)
 //  3. scatter: each wavefront revisits its chunk in entry order and places
 //              entry f = t*K + j at row offsets[e] + prefix + rank, where rank
@@ -115,12 +117,14 @@ __device__ void block_exclusive_scan(int *v, int n, int *total) {
 }
 
 // From per-group row counts cnt[0..E] (LDS, group E = shared expert) write
-// counts, offsets and the row-tile list (largest groups first) and leave the
-// row offsets in off[0..E+1] (LDS).  Called by all 256 threads of one block.
+// counts, offsets and the row-tile list (largest groups first when
+// sort_tiles, else in group order) and leave the row offsets in
+// off[0..E+1] (LDS).  Called by all 256 threads of one block.
 __device__ void scan_groups(int *cnt, int *off, int E, int tile_rows, int max_tiles,
-                            int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                            int32_t *__restrict__ tiles) {
-  __shared__ int ntile[MAXG], order[MAXG], tstart[MAXG + 1];
+                            int sort_tiles, int32_t *__restrict__ counts,
+                            int32_t *__restrict__ offsets, int32_t *__restrict__ tiles) {
+  __shared__ __attribute__((aligned(16))) int ntile[MAXG + 3];   // padded to whole int4s
+  __shared__ int order[MAXG], tstart[MAXG + 1];
   __shared__ int total_rows, total_tiles;
   const int tid = threadIdx.x;
   const int G = E + 1;
@@ -128,14 +132,25 @@ __device__ void scan_groups(int *cnt, int *off, int E, int tile_rows, int max_ti
   __syncthreads();
   block_exclusive_scan(off, G, &total_rows);
   if (tid == 0) off[G] = total_rows;
-  for (int g = tid; g < G; g += 256) ntile[g] = (cnt[g] + tile_rows - 1) / tile_rows;
+  for (int g = tid; g < (G + 3) / 4 * 4; g += 256)
+    ntile[g] = g < G ? (cnt[g] + tile_rows - 1) / tile_rows : -1;   // -1: never counted
   __syncthreads();
-  for (int g = tid; g < G; g += 256) {
+  // Rank of group g: groups with more tiles, or as many and a lower index.
+  // Four counts per LDS read, several reads in flight.
+  const int4 *nt4 = reinterpret_cast<const int4 *>(ntile);
+  if (!sort_tiles) {
+    for (int g = tid; g < G; g += 256) order[g] = g;
+  } else for (int g = tid; g < G; g += 256) {
     const int mine = ntile[g];
     int r = 0;
-    for (int h = 0; h < G; ++h) {
-      const int o = ntile[h];
-      r += (o > mine) || (o == mine && h < g);
+#pragma unroll 8
+    for (int h4 = 0; h4 < (G + 3) / 4; ++h4) {
+      const int4 o = nt4[h4];
+      const int h = 4 * h4;
+      r += (o.x > mine) || (o.x == mine && h < g);
+      r += (o.y > mine) || (o.y == mine && h + 1 < g);
+      r += (o.z > mine) || (o.z == mine && h + 2 < g);
+      r += (o.w > mine) || (o.w == mine && h + 3 < g);
     }
     order[r] = g;
   }
@@ -163,26 +178,33 @@ __device__ void scan_groups(int *cnt, int *off, int E, int tile_rows, int max_ti
 
 __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t *__restrict__ hist, int nchunks,
                                                         int E, int T_shared, int tile_rows,
-                                                        int max_tiles,
+                                                        int max_tiles, int sort_tiles,
                                                         int32_t *__restrict__ counts,
                                                         int32_t *__restrict__ offsets,
                                                         int32_t *__restrict__ tiles) {
   __shared__ int cnt[MAXG], off[MAXG + 1];
   const int tid = threadIdx.x;
-  // Per-expert totals; the chunk histograms become exclusive prefixes.
+  // Per-expert totals; the chunk histograms become exclusive prefixes.  The
+  // counts of 16 chunks are loaded before any of them is rewritten, so there
+  // is one memory round trip per 16 chunks rather than per chunk.
   for (int e = tid; e < E; e += 256) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      int32_t *p = hist + (size_t)c * E + e;
-      const int v = *p;
-      *p = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        v[j] = c0 + j < nchunks ? hist[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (c0 + j < nchunks) hist[(size_t)(c0 + j) * E + e] = run;
+        run += v[j];
+      }
     }
     cnt[e] = run;
   }
   if (tid == 0) cnt[E] = T_shared;
   __syncthreads();
-  scan_groups(cnt, off, E, tile_rows, max_tiles, counts, offsets, tiles);
+  scan_groups(cnt, off, E, tile_rows, max_tiles, sort_tiles, counts, offsets, tiles);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
@@ -207,6 +229,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
 __global__ __launch_bounds__(256) void perm_small_kernel(const int32_t *__restrict__ idx, int N,
                                                          int K, int E, int nchunks, int T_shared,
                                                          int tile_rows, int max_tiles,
+                                                         int sort_tiles,
                                                          int32_t *__restrict__ counts,
                                                          int32_t *__restrict__ offsets,
                                                          int32_t *__restrict__ tiles,
@@ -214,10 +237,12 @@ __global__ __launch_bounds__(256) void perm_small_kernel(const int32_t *__restri
                                                          int32_t *__restrict__ pos_of) {
   __shared__ int cnt[4][256];
   __shared__ int tot[MAXG], off[MAXG + 1];
+  __shared__ int32_t idx_s[4 * PERM_CHUNK];   // the picks, read twice below
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = lane; e < 256; e += 64) cnt[wave][e] = 0;
+  for (int f = tid; f < N; f += 256) idx_s[f] = idx[f];
   __syncthreads();
-  if (wave < nchunks) hist_chunk(idx, N, wave, lane, cnt[wave]);
+  if (wave < nchunks) hist_chunk(idx_s, N, wave, lane, cnt[wave]);
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
     int run = 0;
@@ -230,10 +255,10 @@ __global__ __launch_bounds__(256) void perm_small_kernel(const int32_t *__restri
   }
   if (tid == 0) tot[E] = T_shared;
   __syncthreads();
-  scan_groups(tot, off, E, tile_rows, max_tiles, counts, offsets, tiles);
+  scan_groups(tot, off, E, tile_rows, max_tiles, sort_tiles, counts, offsets, tiles);
   for (int e = lane; e < E; e += 64) cnt[wave][e] += off[e];
   __syncthreads();
-  if (wave < nchunks) scatter_chunk(idx, N, K, wave, lane, cnt[wave], sorted_token, pos_of);
+  if (wave < nchunks) scatter_chunk(idx_s, N, K, wave, lane, cnt[wave], sorted_token, pos_of);
   for (int t = tid; t < T_shared; t += 256) sorted_token[off[E] + t] = t;
 }
 
@@ -243,7 +268,8 @@ hipError_t launch_permute(const PermArgs &a, hipStream_t stream) {
   const int N = a.T * a.K;
   if (a.nchunks <= 4) {
     hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(256), 0, stream, a.idx, N, a.K, a.E,
-                       a.nchunks, a.T_shared, a.tile_rows, a.max_tiles, a.counts, a.offsets,
+                       a.nchunks, a.T_shared, a.tile_rows, a.max_tiles, a.sort_tiles, a.counts,
+                       a.offsets,
                        a.tiles, a.sorted_token, a.pos_of);
     return hipGetLastError();
   }
@@ -251,7 +277,8 @@ hipError_t launch_permute(const PermArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL(perm_hist_kernel, dim3(blocks), dim3(256), 0, stream, a.idx, N, a.E,
                      a.nchunks, a.hist);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, stream, a.hist, a.nchunks, a.E,
-                     a.T_shared, a.tile_rows, a.max_tiles, a.counts, a.offsets, a.tiles);
+                     a.T_shared, a.tile_rows, a.max_tiles, a.sort_tiles, a.counts, a.offsets,
+                     a.tiles);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(blocks), dim3(256), 0, stream, a.idx, N, a.K,
                      a.E, a.nchunks, a.hist, a.offsets, a.T_shared, a.sorted_token, a.pos_of);
   return hipGetLastError();

@@ -154,6 +154,117 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(const uint16_t *__rest
   }
 }
 
+// Small batches (T <= 64, one token tile): every workgroup has little work and
+// the per-step weight-load latency dominates, so each 256-long K chunk is
+// fetched at once: the x chunk (T rows x 512 B) into LDS and the lane's 8
+// weight slices of 8 floats into registers, then 8 x-steps of MFMA on the
+// split terms.  Token fragments past T are skipped (uniform branch).  Same
+// arithmetic as router_bf16_kernel: three (or two) fp32 accumulators per
+// 256-value chunk, folded into float64.
+template <int PREC>
+__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t *__restrict__ x,
+                                                           const float *__restrict__ wr,
+                                                           double *__restrict__ part, int T,
+                                                           int H, int E, int kslice) {
+  constexpr int KC = RT_CHUNK;             // k values per chunk (256)
+  __shared__ uint4 xs[RT_TOK * KC / 8];    // 64 rows x 512 B
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e0 = blockIdx.y * RT_EXP, s = blockIdx.z;
+  const int kbeg = s * kslice;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int e_row = e0 + wave * 16 + r16;
+  const float *wrow = wr + (size_t)(e_row < E ? e_row : 0) * H;
+  const int nfrag = (T + 15) >> 4;         // token fragments with real rows
+
+  constexpr int NT = (PREC == 0) ? 3 : 2;
+  double tot[4][4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tot[n][q] = 0.0;
+
+  for (int kc = kbeg; kc < kbeg + kslice; kc += KC) {
+    const int kn = min(KC, kbeg + kslice - kc);   // a multiple of 64
+    // Weight: sub-step u covers k = kc + 32u + 8g .. +7 (8 floats per lane).
+    float4 wv[16];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kk = kc + (32 * u < kn ? 32 * u : 0) + g * 8;
+      wv[2 * u] = *reinterpret_cast<const float4 *>(wrow + kk);
+      wv[2 * u + 1] = *reinterpret_cast<const float4 *>(wrow + kk + 4);
+    }
+    // x chunk: row r, 16-byte chunk c (kn / 8 chunks per row).
+    const int cpr = kn / 8;
+    for (int i = tid; i < RT_TOK * cpr; i += 256) {
+      const int r = i / cpr, c = i - r * cpr;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < T) v = *reinterpret_cast<const uint4 *>(x + (size_t)r * H + kc + c * 8);
+      xs[r * (KC / 8) + (c ^ (r & 7))] = v;
+    }
+    __syncthreads();
+    f32x4_t acc[NT][4];
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[a][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (32 * u < kn) {
+        const float w8[8] = {wv[2 * u].x, wv[2 * u].y, wv[2 * u].z, wv[2 * u].w,
+                             wv[2 * u + 1].x, wv[2 * u + 1].y, wv[2 * u + 1].z, wv[2 * u + 1].w};
+        uint16_t th[8], tm[8], tl[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (PREC == 0) {
+            split3(w8[i], th[i], tm[i], tl[i]);
+          } else {
+            th[i] = f32_to_bf16(w8[i]);
+            tm[i] = f32_to_bf16((w8[i] - bf16_to_f32(th[i])) * 256.0f);
+          }
+        }
+        uint4 fa[NT];
+        fa[0] = make_uint4(pack2(th[0], th[1]), pack2(th[2], th[3]), pack2(th[4], th[5]), pack2(th[6], th[7]));
+        fa[1] = make_uint4(pack2(tm[0], tm[1]), pack2(tm[2], tm[3]), pack2(tm[4], tm[5]), pack2(tm[6], tm[7]));
+        if (PREC == 0)
+          fa[NT - 1] = make_uint4(pack2(tl[0], tl[1]), pack2(tl[2], tl[3]), pack2(tl[4], tl[5]), pack2(tl[6], tl[7]));
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          if (n < nfrag) {
+            const int r = n * 16 + r16;
+            const uint4 xb = xs[r * (KC / 8) + ((u * 4 + g) ^ (r & 7))];
+#pragma unroll
+            for (int a = 0; a < NT; ++a) Mma<bf16_t>::step(acc[a][n], fa[a], xb);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (PREC == 0)
+          tot[n][q] += (double)acc[0][n][q] + ((double)acc[1][n][q] + (double)acc[2][n][q]);
+        else
+          tot[n][q] = __builtin_fma((double)acc[1][n][q], 1.0 / 256.0,
+                                    tot[n][q] + (double)acc[0][n][q]);
+      }
+    }
+    __syncthreads();   // xs is rewritten by the next chunk
+  }
+
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int t = n * 16 + r16;
+    if (t >= T) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + wave * 16 + 4 * g + q;
+      if (e < E) part[((size_t)s * T + t) * E + e] = tot[n][q];
+    }
+  }
+}
+
 // fp32 activations: fp32 MFMA on the fp32 weight.
 __global__ __launch_bounds__(256) void router_f32_kernel(const float *__restrict__ x,
                                                          const float *__restrict__ wr,
@@ -412,6 +523,14 @@ hipError_t launch_router(const void *x, int dtype, int router_prec, const float 
   if (dtype == DT_F32) {
     hipLaunchKernelGGL(router_f32_kernel, grid, dim3(256), 0, stream,
                        static_cast<const float *>(x), wr, part, T, H, E, kslice);
+  } else if (T <= RT_TOK) {
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    if (router_prec == 0)
+      hipLaunchKernelGGL(router_small_kernel<0>, grid, dim3(256), 0, stream, xb, wr, part, T, H,
+                         E, kslice);
+    else
+      hipLaunchKernelGGL(router_small_kernel<1>, grid, dim3(256), 0, stream, xb, wr, part, T, H,
+                         E, kslice);
   } else if (router_prec == 0) {
     hipLaunchKernelGGL(router_bf16_kernel<0>, grid, dim3(256), 0, stream,
                        static_cast<const uint16_t *>(x), wr, part, T, H, E, kslice);
