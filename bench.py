@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4}
+ROUTER_WORKLOAD = 3            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
 METRIC = "Hy3 MoE layer tokens/s; % bf16 MFMA peak (prefill) / % HBM BW (decode)"
@@ -75,6 +76,11 @@ def main():
                     help="measure the achievable MFMA and copy ceilings instead of the layer")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device (PMC calibration)")
+    ap.add_argument("--router-sweep", action="store_true",
+                    help="time the gate alone (hy3moe_route) at M = 2, 64, 512, 4096 tokens, "
+                         "fp32-accurate and two-term split router, instead of the layer")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the layer as a captured HIP graph replayed K times")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -94,6 +100,9 @@ def main():
         print(json.dumps(ceilings(dev)), flush=True)
         return
     sm.load()
+    if args.router_sweep:
+        print(json.dumps(router_sweep(args, dev)), flush=True)
+        return
     inp = MoEInputs(CONFIGS[WORKLOADS[args.workload]])
     c = inp.cfg
     t0 = time.time()
@@ -127,6 +136,27 @@ def main():
     wall = time.perf_counter() - w0
     ms_per_step = wall * 1e3 / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    # ---- optional: the same step captured once as a HIP graph, replayed ----
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            sm.hy3moe_forward(cfg, x, weights, out, ws)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sm.hy3moe_forward(cfg, x, weights, out, ws)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+        log(f"[bench] graph replay: {graph_ms:.4f} ms/step")
 
     # ---- per-stage durations: HIP events recorded between the kernels ----
     n_ev = sm.HY3MOE_N_STAGES + 1
@@ -206,8 +236,52 @@ def main():
         "config": {"workload": c.name, "T": T, "H": H, "E": E, "K": K, "I": I, "I_shared": Is,
                    "route": "sigmoid+bias" if c.route_mode == 0 else "softmax"},
         "roofline": roof, "cpu_baseline": cpu, "layer": layer,
+        "graph_ms_per_step": graph_ms,
     }
     print(json.dumps(res), flush=True)
+
+
+def router_sweep(args, dev):
+    """The gate alone on the router-only workload (H=4096, E=192, top-8):
+    hy3moe_route over the first M tokens, both router arithmetics.  Time per
+    call from HIP events over `steps` calls; GB/s counts the fp32 router
+    weight plus the M activation rows, TFLOP/s the 2*M*H*E of the product."""
+    import torch
+
+    import sparse_moe_amd as sm
+    from synth import CONFIGS, ROUTER_SWEEP_M, MoEInputs
+    from synth.device import to_torch
+
+    inp = MoEInputs(CONFIGS[ROUTER_WORKLOAD])
+    c = inp.cfg
+    x_all = to_torch(inp.x(), c.dtype, dev)
+    wr = torch.from_numpy(inp.w_router()).to(dev)
+    bias = torch.from_numpy(inp.bias()).to(dev)
+    rows = []
+    for M in ROUTER_SWEEP_M:
+        x = x_all[:M].contiguous()
+        for prec, name in ((sm.HY3MOE_ROUTER_FP32, "fp32-accurate (3-term bf16 split)"),
+                           (sm.HY3MOE_ROUTER_SPLIT2_BF16, "two-term bf16 split")):
+            cfg = sm.make_config(M, c.H, c.E, c.K, c.I, c.I_shared, c.dtype, c.route_mode,
+                                 router_prec=prec, scale=c.scale, renorm_eps=c.renorm_eps)
+            ws = sm.alloc_workspace(cfg, False, dev)
+            idx = torch.empty((M, c.K), dtype=torch.int32, device=dev)
+            wgt = torch.empty((M, c.K), dtype=torch.float32, device=dev)
+            for _ in range(args.warmup):
+                sm.hy3moe_route(cfg, x, wr, bias, idx, wgt, ws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                sm.hy3moe_route(cfg, x, wr, bias, idx, wgt, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.steps
+            nbytes = c.E * c.H * 4 + M * c.H * 2
+            rows.append({"M": M, "router": name, "us_per_call": us,
+                         "GB_s": nbytes / us / 1e3, "TFLOP_s": 2.0 * M * c.H * c.E / us / 1e6})
+            log(f"[router] M={M:5d} {name:34s} {us:8.2f} us")
+    return {"router_sweep": rows, "config": {"workload": c.name, "H": c.H, "E": c.E, "K": c.K},
+            "steps": args.steps, "note": "gate only: router GEMM + score/select"}
 
 
 def ceilings(dev):
