@@ -28,100 +28,110 @@ namespace {
 constexpr int UBASE = 8;          // 64-byte K steps per register set (one row fragment)
 constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
 
+// Where a unit's operands are (per lane) and what its epilogue needs.
+template <int MT>
+struct UnitSrc {
+  const char *w0p, *w1p;   // the two 16-row weight fragments (gate/up, or two down blocks)
+  const char *xp[MT];      // token rows (gathered x for gate-up, h rows for down)
+  int nsub;                // 64-byte K steps per row
+  int nf;                  // fragments streamed (2; 1 for half of a down unit)
+};
+struct UnitOut {
+  int row0, grp_end, col0, nsub, nf;
+};
+
+// Unit u (tile u / n_col_blocks, column block u % n_col_blocks) of this
+// kernel; returns false if the column block lies past the group's width.
+// half = 1 or 2: only the first or the second 16-row fragment of a down unit.
 template <typename T, bool GATE_UP, int MT>
-__device__ __forceinline__ void stream_unit(const ExpertArgs &a, int tile, int cb, int lane) {
-  constexpr int U = UBASE / MT;   // 64-byte K steps per row per register set
+__device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_blocks, int lane,
+                                        UnitSrc<MT> &src, UnitOut &o, int half = 0) {
+  constexpr int EB = Elem<T>::kBytes;
+  const int tile = u / n_col_blocks, cb = u - tile * n_col_blocks;
   const int g = a.tiles[2 * tile];
-  const int row0 = a.tiles[2 * tile + 1];
-  const int grp_end = a.offsets[g + 1];
+  o.row0 = a.tiles[2 * tile + 1];
+  o.grp_end = a.offsets[g + 1];
   const bool shared = (g == a.E);
   const int Ig = shared ? a.I_shared : a.I;
-  const int Kdim = GATE_UP ? a.H : Ig;
-  constexpr int EB = Elem<T>::kBytes;
+  o.col0 = cb * (GATE_UP ? 16 : 32) + (half == 2 ? 16 : 0);
+  o.nsub = (GATE_UP ? a.H : Ig) * EB / 64;
+  o.nf = half ? 1 : 2;
+  if (o.col0 >= (GATE_UP ? Ig : a.H)) return false;
+  src.nsub = o.nsub;
+  src.nf = o.nf;
   const int r16 = lane & 15, cg = lane >> 4;
-  const int col0 = cb * (GATE_UP ? 16 : 32);
-  if (col0 >= (GATE_UP ? Ig : a.H)) return;
-
-  const char *w0p, *w1p;
   if (GATE_UP) {
     const T *gate = shared ? static_cast<const T *>(a.ws0)
                            : static_cast<const T *>(a.w0) + (size_t)g * a.I * a.H;
     const T *up = shared ? static_cast<const T *>(a.ws1)
                          : static_cast<const T *>(a.w1) + (size_t)g * a.I * a.H;
-    w0p = reinterpret_cast<const char *>(gate + (size_t)(col0 + r16) * a.H) + cg * 16;
-    w1p = reinterpret_cast<const char *>(up + (size_t)(col0 + r16) * a.H) + cg * 16;
+    src.w0p = reinterpret_cast<const char *>(gate + (size_t)(o.col0 + r16) * a.H) + cg * 16;
+    src.w1p = reinterpret_cast<const char *>(up + (size_t)(o.col0 + r16) * a.H) + cg * 16;
   } else {
     const T *dn = shared ? static_cast<const T *>(a.ws0)
                          : static_cast<const T *>(a.w0) + (size_t)g * a.H * a.I;
-    const int n0 = (col0 + r16 < a.H) ? col0 + r16 : col0;
-    const int n1 = (col0 + 16 + r16 < a.H) ? col0 + 16 + r16 : col0;
-    w0p = reinterpret_cast<const char *>(dn + (size_t)n0 * Ig) + cg * 16;
-    w1p = reinterpret_cast<const char *>(dn + (size_t)n1 * Ig) + cg * 16;
+    const int n0 = (o.col0 + r16 < a.H) ? o.col0 + r16 : o.col0;
+    const int n1 = (o.col0 + 16 + r16 < a.H) ? o.col0 + 16 + r16 : o.col0;
+    src.w0p = reinterpret_cast<const char *>(dn + (size_t)n0 * Ig) + cg * 16;
+    src.w1p = reinterpret_cast<const char *>(dn + (size_t)n1 * Ig) + cg * 16;
   }
-  const char *xp[MT];
   const T *act = static_cast<const T *>(a.act);
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    int trow = row0 + m * 16 + r16;
-    if (trow >= grp_end) trow = row0;
+    int trow = o.row0 + m * 16 + r16;
+    if (trow >= o.grp_end) trow = o.row0;
     const size_t arow = GATE_UP ? (size_t)a.sorted_token[trow] * a.H : (size_t)trow * a.ldh;
-    xp[m] = reinterpret_cast<const char *>(act + arow) + cg * 16;
+    src.xp[m] = reinterpret_cast<const char *>(act + arow) + cg * 16;
   }
+  return true;
+}
 
-  f32x4_t acc[2][MT];
-#pragma unroll
-  for (int f = 0; f < 2; ++f)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+// Work item k >= k0 of wavefront w (of nw): item k is unit w + k * nw.  For
+// down, when the units left after the full rounds number at most nw / 2, each
+// of them is split into its two 16-row fragments for twice as many
+// wavefronts, so the last round costs half a unit.  Returns the item index
+// (kmax when there is none) and fills src / o.
+template <typename T, bool GATE_UP, int MT>
+__device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int nw, int n_units,
+                                         int n_col_blocks, int lane, UnitSrc<MT> &src,
+                                         UnitOut &o) {
+  const int full = n_units / nw, tail = n_units - full * nw;
+  const bool split = !GATE_UP && 2 * tail <= nw;
+  const int kmax = full + 1;
+  for (; k < kmax; ++k) {
+    if (k < full || !split) {
+      const int u = w + k * nw;
+      if (u >= n_units) return kmax;
+      if (unit_of<T, GATE_UP, MT>(a, u, n_col_blocks, lane, src, o)) return k;
+    } else {
+      if (w >= 2 * tail) return kmax;
+      if (unit_of<T, GATE_UP, MT>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
+                                  1 + (w & 1)))
+        return k;
+    }
+  }
+  return kmax;
+}
 
-  const int nsub = Kdim * EB / 64;   // 64-byte steps per row (a multiple of 2)
-  uint4 aw0[U], aw1[U], ax[U][MT];
-  uint4 bw0[U], bw1[U], bx[U][MT];
-#define HY3_LOAD(W0, W1, X, s0)                                                        \
-  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                      \
-    const int o_ = ((s0) + u < nsub ? (s0) + u : nsub - 1) * 64;                       \
-    W0[u] = *reinterpret_cast<const uint4 *>(w0p + o_);                                \
-    W1[u] = *reinterpret_cast<const uint4 *>(w1p + o_);                                \
-    _Pragma("unroll") for (int m = 0; m < MT; ++m)                                     \
-        X[u][m] = *reinterpret_cast<const uint4 *>(xp[m] + o_);                        \
-  }
-#define HY3_MMA(W0, W1, X, s0)                                                         \
-  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                      \
-    if ((s0) + u < nsub) {                                                             \
-      _Pragma("unroll") for (int m = 0; m < MT; ++m) {                                 \
-        Mma<T>::step(acc[0][m], W0[u], X[u][m]);                                       \
-        Mma<T>::step(acc[1][m], W1[u], X[u][m]);                                       \
-      }                                                                                \
-    }                                                                                  \
-  }
-  // Steps past nsub re-read the last step (in bounds) and are not used.
-  HY3_LOAD(aw0, aw1, ax, 0);
-  for (int s = 0; s < nsub; s += 2 * U) {
-    HY3_LOAD(bw0, bw1, bx, s + U);
-    __builtin_amdgcn_sched_barrier(0);   // keep the next block's loads ahead
-    HY3_MMA(aw0, aw1, ax, s);
-    if (s + 2 * U < nsub) { HY3_LOAD(aw0, aw1, ax, s + 2 * U); }
-    __builtin_amdgcn_sched_barrier(0);
-    HY3_MMA(bw0, bw1, bx, s + U);
-  }
-#undef HY3_MMA
-#undef HY3_LOAD
-
+template <typename T, bool GATE_UP, int MT>
+__device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut &o,
+                                              f32x4_t (&acc)[2][MT], int lane) {
+  const int r16 = lane & 15, cg = lane >> 4;
   // Lane holds D[col 4cg + q][token row 16m + r16].
   T *out = static_cast<T *>(a.out);
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int trow = row0 + m * 16 + r16;
-    if (trow >= grp_end) continue;
+    const int trow = o.row0 + m * 16 + r16;
+    if (trow >= o.grp_end) continue;
     if (GATE_UP) {
       const f32x4_t gv = acc[0][m], uv = acc[1][m];
-      store4(out + (size_t)trow * a.ldh + col0 + 4 * cg, swiglu(gv[0], uv[0]),
+      store4(out + (size_t)trow * a.ldh + o.col0 + 4 * cg, swiglu(gv[0], uv[0]),
              swiglu(gv[1], uv[1]), swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
     } else {
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        const int n = col0 + f * 16 + 4 * cg;
-        if (n >= a.H) continue;
+        const int n = o.col0 + f * 16 + 4 * cg;
+        if (f >= o.nf || n >= a.H) continue;
         const f32x4_t v = acc[f][m];
         store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
       }
@@ -132,6 +142,7 @@ __device__ __forceinline__ void stream_unit(const ExpertArgs &a, int tile, int c
 template <typename T, bool GATE_UP, int MT>
 __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(ExpertArgs a,
                                                                           int n_col_blocks) {
+  constexpr int U = UBASE / MT;   // 64-byte K steps per row per register set (one block)
   const int lane = threadIdx.x & 63;
   // The wavefront index is uniform; readfirstlane makes that visible to the
   // compiler, so every unit-dependent guard below is a scalar branch.  (An
@@ -139,13 +150,82 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   // EXEC mask that is expected to switch it off.)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = a.tiles[2 * a.max_tiles] * n_col_blocks;
-  const int total_waves = gridDim.x * 4;
+  const int nw = gridDim.x * 4, w = blockIdx.x * 4 + wave;
+  const int kmax = n_units / nw + 1;
   // Wavefront ids interleave the XCDs (block b runs on XCD b % 8), so the
   // units of one expert spread over all XCDs and HBM channels.
-  for (int u = blockIdx.x * 4 + wave; u < n_units; u += total_waves) {
-    const int tile = u / n_col_blocks;
-    stream_unit<T, GATE_UP, MT>(a, tile, u - tile * n_col_blocks, lane);
+  UnitSrc<MT> src;    // item whose blocks are being loaded
+  UnitOut om, ol;     // item being multiplied, item being loaded
+  int k_ld = next_item<T, GATE_UP, MT>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
+  if (k_ld >= kmax) return;
+  int k_mm = k_ld;
+  om = ol;
+  int s_ld = 0, s_mm = 0;   // next K step to load / to multiply, in their units
+
+  f32x4_t acc[2][MT];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 aw0[U], aw1[U], ax[U][MT];
+  uint4 bw0[U], bw1[U], bx[U][MT];
+  // Load the next block of the loading unit into set W0/W1/X, then move the
+  // loading position on (to the next unit at the end of this one).  Steps past
+  // nsub re-read the last step (in bounds) and are not used.
+#define HY3_LOAD(W0, W1, X)                                                            \
+  {                                                                                    \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
+      const int o_ = (s_ld + u < src.nsub ? s_ld + u : src.nsub - 1) * 64;             \
+      W0[u] = *reinterpret_cast<const uint4 *>(src.w0p + o_);                          \
+      if (src.nf == 2) W1[u] = *reinterpret_cast<const uint4 *>(src.w1p + o_);         \
+      _Pragma("unroll") for (int m = 0; m < MT; ++m)                                   \
+          X[u][m] = *reinterpret_cast<const uint4 *>(src.xp[m] + o_);                  \
+    }                                                                                  \
+    s_ld += U;                                                                         \
+    if (s_ld >= src.nsub) {                                                            \
+      k_ld = next_item<T, GATE_UP, MT>(a, k_ld + 1, w, nw, n_units, n_col_blocks, lane, \
+                                       src, ol);                                       \
+      s_ld = 0;                                                                        \
+    }                                                                                  \
   }
+  // Multiply one block of the multiplying unit; at its end, write the unit
+  // and move on.  `more` turns false after the last unit.
+#define HY3_MMA(W0, W1, X)                                                             \
+  {                                                                                    \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
+      if (s_mm + u < om.nsub) {                                                        \
+        _Pragma("unroll") for (int m = 0; m < MT; ++m) {                               \
+          Mma<T>::step(acc[0][m], W0[u], X[u][m]);                                     \
+          if (om.nf == 2) Mma<T>::step(acc[1][m], W1[u], X[u][m]);                     \
+        }                                                                              \
+      }                                                                                \
+    }                                                                                  \
+    s_mm += U;                                                                         \
+    if (s_mm >= om.nsub) {                                                             \
+      unit_epilogue<T, GATE_UP, MT>(a, om, acc, lane);                                 \
+      _Pragma("unroll") for (int f = 0; f < 2; ++f)                                    \
+        _Pragma("unroll") for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; \
+      k_mm = next_item<T, GATE_UP, MT>(a, k_mm + 1, w, nw, n_units, n_col_blocks, lane, \
+                                       src_dummy, om);                                 \
+      s_mm = 0;                                                                        \
+      more = k_mm < kmax;                                                              \
+    }                                                                                  \
+  }
+  UnitSrc<MT> src_dummy;   // next_unit also fills operand pointers; the multiply side ignores them
+  bool more = true;
+  HY3_LOAD(aw0, aw1, ax);
+  while (more) {
+    if (k_ld < kmax) HY3_LOAD(bw0, bw1, bx);
+    __builtin_amdgcn_sched_barrier(0);   // keep the next block's loads ahead
+    HY3_MMA(aw0, aw1, ax);
+    if (!more) break;
+    if (k_ld < kmax) HY3_LOAD(aw0, aw1, ax);
+    __builtin_amdgcn_sched_barrier(0);
+    HY3_MMA(bw0, bw1, bx);
+  }
+#undef HY3_MMA
+#undef HY3_LOAD
 }
 
 // Persistent grid: WAVES_PER_SIMD wavefronts per SIMD on the 256 CUs.
