@@ -19,12 +19,13 @@
 //    its second half, so a load has about a stage and a half to land.
 //  * Global addresses are a uniform base per matrix plus 32-bit per-thread
 //    offsets.
-//  * Workgroups are remapped so that consecutive logical tiles run on the
-//    same XCD (dispatch is round-robin over the 8 XCDs) with an equal share of
-//    the real tiles per XCD, and logical tiles
-//    are ordered in bands of 4 row tiles x all column tiles with the row tile
-//    fastest: an XCD's ~32 resident tiles share 4 token-row blocks and 8
-//    weight-row blocks in its L2.
+//  * One workgroup per CU, each looping over tiles.  Consecutive logical
+//    tiles run on the same XCD (dispatch is round-robin over the 8 XCDs) with
+//    an equal share of the real tiles per XCD, and logical tiles are ordered
+//    in bands of 4 row tiles x all column tiles with the row tile fastest: an
+//    XCD's 32 tiles in flight share 4 token-row blocks and 8 weight-row blocks
+//    in its L2.  The next tile's first two K stages are loaded while the
+//    finished tile's epilogue runs.
 // Group E is the shared expert (its own weights and width I_shared).
 #include "common.cuh"
 #include "internal.h"
@@ -68,84 +69,187 @@ __device__ __forceinline__ void stage_schedule() {
   sched_group<1, 1, 1>(); sched_group<0, 1, 1>(); sched_group<1, 0, 1>(); sched_group<0, 0, 1>();
 }
 
+// A tile of the list: its group, rows and output columns.
+struct BigTile {
+  int g, row0, grp_end, Ig, col0, nk;
+};
+
+// Logical tile r of this XCD's run (see the kernel); false if it is padding.
+template <typename T, bool GATE_UP>
+__device__ __forceinline__ bool big_tile_at(const ExpertArgs &a, int n_tiles, int n_col_tiles,
+                                            int per, int xcd, int r, BigTile &t) {
+  constexpr int EB = Elem<T>::kBytes;
+  const int band_sz = BAND * n_col_tiles;
+  const int L = xcd * per + r;
+  const int band = L / band_sz, within = L - band * band_sz;
+  const int ct = within / BAND;
+  const int rt = band * BAND + (within - ct * BAND);
+  if (rt >= n_tiles) return false;
+  t.g = a.tiles[2 * rt];
+  t.row0 = a.tiles[2 * rt + 1];
+  t.grp_end = a.offsets[t.g + 1];
+  t.Ig = (t.g == a.E) ? a.I_shared : a.I;
+  t.col0 = ct * (GATE_UP ? BW / 2 : BW);
+  t.nk = (GATE_UP ? a.H : t.Ig) * EB / RB;
+  return !(GATE_UP && t.col0 >= t.Ig);
+}
+
+// Load descriptors of tile t: thread loads chunk lc of rows lr + 64 p, p = 0..3,
+// of the weight block and of the token block.  Gate-up weight rows: each
+// block of 64 rows [64q, 64q+64) holds gate cols col0 + 32q + [0, 32) and then
+// the up cols of the same columns, so lr < 32 loads gate rows, lr >= 32 up rows.
+// Global addresses: a base pointer plus 32-bit offsets (every matrix < 4 GiB).
+template <typename T, bool GATE_UP>
+__device__ __forceinline__ void big_tile_loads(const ExpertArgs &a, const BigTile &t, int lr,
+                                               int lc, const char *&wb, const char *&xb,
+                                               uint32_t *woff, uint32_t *xoff) {
+  constexpr int EB = Elem<T>::kBytes;
+  const bool shared = (t.g == a.E);
+  const T *mat;
+  if (GATE_UP) {
+    const bool up = lr >= 32;
+    mat = shared ? static_cast<const T *>(up ? a.ws1 : a.ws0)
+                 : static_cast<const T *>(up ? a.w1 : a.w0) + (size_t)t.g * a.I * a.H;
+    xb = static_cast<const char *>(a.act);
+  } else {
+    mat = shared ? static_cast<const T *>(a.ws0)
+                 : static_cast<const T *>(a.w0) + (size_t)t.g * a.H * a.I;
+    xb = static_cast<const char *>(a.act) + (size_t)t.row0 * a.ldh * EB;
+  }
+  wb = reinterpret_cast<const char *>(mat);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = p * 64 + lr;
+    if (GATE_UP) {
+      int wrow = t.col0 + p * 32 + (lr & 31);
+      if (wrow >= t.Ig) wrow = t.col0;         // column tail (Ig % 128 == 64)
+      woff[p] = (uint32_t)wrow * (uint32_t)(a.H * EB) + lc * 16;
+    } else {
+      const int wrow = (t.col0 + r < a.H) ? t.col0 + r : t.col0;
+      woff[p] = (uint32_t)wrow * (uint32_t)(t.Ig * EB) + lc * 16;
+    }
+    int trow = t.row0 + r;
+    if (trow >= t.grp_end) trow = t.row0;      // ragged tail: reload a valid row
+    if (GATE_UP) xoff[p] = (uint32_t)a.sorted_token[trow] * (uint32_t)(a.H * EB) + lc * 16;
+    else xoff[p] = (uint32_t)(trow - t.row0) * (uint32_t)(a.ldh * EB) + lc * 16;
+  }
+}
+
+// Epilogue of a tile: lane holds D[weight row 16i + 4cg + q][token row 16j + r16]
+// of wavefront (wr_, wt_).  tid is the thread index.
+template <typename T, bool GATE_UP>
+__device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile &t,
+                                             const f32x4_t (&acc)[8][4], uint4 *lds, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr_ = wave >> 2, wt_ = wave & 3, r16 = lane & 15, cg = lane >> 4;
+  T *out = static_cast<T *>(a.out);
+  if constexpr (sizeof(T) == 2) {
+    // Through LDS (free after the loop's last barrier): each lane writes its
+    // 4-column pieces into bf16 token rows (16-byte chunks swizzled by row),
+    // then each thread stores whole 16-byte chunks, so a wavefront writes two
+    // full output rows per instruction instead of 32-byte pieces of 16 rows.
+    constexpr int OC = GATE_UP ? BW / 2 / 8 : BW / 8;   // 16-byte chunks per tile row
+    char *stg = reinterpret_cast<char *>(lds);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wt_ * 64 + j * 16 + r16;
+      char *row = stg + r * OC * 16;
+      if (GATE_UP) {
+        // wavefront wr_ holds weight rows 128 wr_ + [0, 128): frags i = 0,1 are
+        // gate cols 64 wr_ + [0, 32), i = 2,3 their up cols, i = 4,5 gate cols
+        // 64 wr_ + [32, 64), i = 6,7 their up cols.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int gi = (i >> 1) * 4 + (i & 1);
+          const int c = wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
+          const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
+          uint2 v;
+          v.x = pack_bf16x2(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]));
+          v.y = pack_bf16x2(swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
+          *reinterpret_cast<uint2 *>(row + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = v;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = wr_ * 128 + i * 16 + 4 * cg;
+          const f32x4_t v4 = acc[i][j];
+          uint2 v;
+          v.x = pack_bf16x2(v4[0], v4[1]);
+          v.y = pack_bf16x2(v4[2], v4[3]);
+          *reinterpret_cast<uint2 *>(row + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = v;
+        }
+      }
+    }
+    __syncthreads();
+    const int width = GATE_UP ? t.Ig : a.H;           // output columns of this matrix
+    const size_t ldo = GATE_UP ? (size_t)a.ldh : (size_t)a.H;
+#pragma unroll
+    for (int m = 0; m < 256 * OC / 512; ++m) {
+      const int q = tid + 512 * m;
+      const int r = q / OC, ch = q % OC;
+      const int c = t.col0 + ch * 8;
+      if (t.row0 + r < t.grp_end && c < width) {
+        const uint4 v = lds[r * OC + (ch ^ (r & 7))];
+        uint4 *dst = reinterpret_cast<uint4 *>(out + (size_t)(t.row0 + r) * ldo + c);
+        // written once, read by the next kernel: non-temporal
+        __builtin_nontemporal_store(v.x, &dst->x);
+        __builtin_nontemporal_store(v.y, &dst->y);
+        __builtin_nontemporal_store(v.z, &dst->z);
+        __builtin_nontemporal_store(v.w, &dst->w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int trow = t.row0 + wt_ * 64 + j * 16 + r16;
+      if (trow >= t.grp_end) continue;
+      if (GATE_UP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int gi = (i >> 1) * 4 + (i & 1);
+          const int c = t.col0 + wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
+          if (c >= t.Ig) continue;
+          const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
+          store4(out + (size_t)trow * a.ldh + c, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
+                 swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int n = t.col0 + wr_ * 128 + i * 16 + 4 * cg;
+          if (n >= a.H) continue;
+          const f32x4_t v = acc[i][j];
+          store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+  }
+}
+
 template <typename T, bool GATE_UP>
 __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_col_tiles) {
   __shared__ uint4 lds[2 * ROWS * CH];   // 2 x 64 KB
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // XCD-aware remap.  Dispatch is round-robin over the 8 XCDs (block b runs on
-  // XCD b % 8); each XCD takes a contiguous run of `per` logical tiles, where
-  // `per` comes from the device-side tile count so that every XCD gets an
-  // equal share of real tiles (the grid is sized for the upper bound).
+  // XCD-aware order.  Dispatch is round-robin over the 8 XCDs (workgroup b runs
+  // on XCD b % 8); each XCD takes a contiguous run of `per` logical tiles
+  // (`per` from the device-side tile count, so every XCD gets an equal share of
+  // real tiles), and its workgroups walk that run with a stride of their count.
   const int n_tiles = a.tiles[2 * a.max_tiles];
-  const int band_sz = BAND * n_col_tiles;
-  const int per = ((n_tiles + BAND - 1) / BAND * band_sz + 7) >> 3;
-  const int b = blockIdx.x, rank = b >> 3;
-  if (rank >= per) return;
-  const int L = (b & 7) * per + rank;
-  const int band = L / band_sz, within = L - band * band_sz;
-  const int ct = within / BAND;
-  const int rt = band * BAND + (within - ct * BAND);
-  if (rt >= n_tiles) return;
+  const int per = ((n_tiles + BAND - 1) / BAND * (BAND * n_col_tiles) + 7) >> 3;
+  const int xcd = blockIdx.x & 7, nb = gridDim.x >> 3;
+  int r = blockIdx.x >> 3;
+  BigTile cur;
+  while (r < per && !big_tile_at<T, GATE_UP>(a, n_tiles, n_col_tiles, per, xcd, r, cur)) r += nb;
+  if (r >= per) return;
 
-  const int g = a.tiles[2 * rt];
-  const int row0 = a.tiles[2 * rt + 1];
-  const int grp_end = a.offsets[g + 1];
-  const bool shared = (g == a.E);
-  const int Ig = shared ? a.I_shared : a.I;
-  const int Kdim = GATE_UP ? a.H : Ig;
-  constexpr int EB = Elem<T>::kBytes;
-  const int col0 = ct * (GATE_UP ? BW / 2 : BW);
-  if (GATE_UP && col0 >= Ig) return;
-
-  // ---- load descriptors: thread loads chunk lc of rows lr + 64 p, p = 0..3,
-  // of the weight block and of the token block.  Gate-up weight rows: each
-  // block of 64 rows [64q, 64q+64) holds gate cols col0 + 32q + [0, 32) and then
-  // the up cols of the same columns, so lr < 32 loads gate rows, lr >= 32 up rows.
-  // Global addresses: a base pointer plus 32-bit offsets (every matrix < 4 GiB).
   const int lr = tid >> 3, lc = tid & 7;
   const char *wb, *xb;
   uint32_t woff[4], xoff[4];
-  {
-    const T *mat;
-    if (GATE_UP) {
-      const bool up = lr >= 32;
-      mat = shared ? static_cast<const T *>(up ? a.ws1 : a.ws0)
-                   : static_cast<const T *>(up ? a.w1 : a.w0) + (size_t)g * a.I * a.H;
-      xb = static_cast<const char *>(a.act);
-    } else {
-      mat = shared ? static_cast<const T *>(a.ws0)
-                   : static_cast<const T *>(a.w0) + (size_t)g * a.H * a.I;
-      xb = static_cast<const char *>(a.act) + (size_t)row0 * a.ldh * EB;
-    }
-    wb = reinterpret_cast<const char *>(mat);
-  }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = p * 64 + lr;
-    if (GATE_UP) {
-      int wrow = col0 + p * 32 + (lr & 31);
-      if (wrow >= Ig) wrow = col0;             // column tail (Ig % 128 == 64)
-      woff[p] = (uint32_t)wrow * (uint32_t)(a.H * EB) + lc * 16;
-    } else {
-      const int wrow = (col0 + r < a.H) ? col0 + r : col0;
-      woff[p] = (uint32_t)wrow * (uint32_t)(Ig * EB) + lc * 16;
-    }
-    int trow = row0 + r;
-    if (trow >= grp_end) trow = row0;          // ragged tail: reload a valid row
-    if (GATE_UP) xoff[p] = (uint32_t)a.sorted_token[trow] * (uint32_t)(a.H * EB) + lc * 16;
-    else xoff[p] = (uint32_t)(trow - row0) * (uint32_t)(a.ldh * EB) + lc * 16;
-  }
-
-  f32x4_t acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  big_tile_loads<T, GATE_UP>(a, cur, lr, lc, wb, xb, woff, xoff);
 
   const int wr_ = wave >> 2, wt_ = wave & 3;
   const int r16 = lane & 15, cg = lane >> 4;
-  const int nk = Kdim * EB / RB;
   // LDS addresses (uint4 units).  Rows 16i + r16 and 64p + lr have the same
   // swizzle term for every i and p, so each access is a base plus an immediate.
   const int rd_a = (wr_ * 128 + r16) * CH;
@@ -198,7 +302,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
 // fills a buffer that is not read again: the body stays branch-free.
 #define HY3_ITER(k, S, B, SN)                                                          \
   {                                                                                    \
-    HY3_GLOAD(S, ((k) + 2 < nk) ? (k) + 2 : 0);                                        \
+    HY3_GLOAD(S, ((k) + 2 < cur.nk) ? (k) + 2 : 0);                                        \
     HY3_COMPUTE(B);                                                                    \
     HY3_LSTORE(SN, (B) ^ 1);                                                           \
     if constexpr (sizeof(T) == 2) stage_schedule();                                    \
@@ -206,103 +310,59 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
   }
 
   HY3_GLOAD(a, 0);
-  HY3_GLOAD(b, (1 < nk) ? 1 : 0);
+  HY3_GLOAD(b, (1 < cur.nk) ? 1 : 0);
   HY3_LSTORE(a, 0);
   __syncthreads();
-  int k = 0;
-  for (; k + 2 <= nk; k += 2) {
-    HY3_ITER(k, a, 0, b);
-    HY3_ITER(k + 1, b, 1, a);
+  f32x4_t acc[8][4];
+  // Persistent over this workgroup's tiles.  Between two tiles the next
+  // tile's first two K stages are issued before the finished tile's
+  // epilogue, so their latency overlaps the epilogue and its stores.
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_sched_barrier(0);
+    const int nk = cur.nk;
+    int k = 0;
+    for (; k + 2 <= nk; k += 2) {
+      HY3_ITER(k, a, 0, b);
+      HY3_ITER(k + 1, b, 1, a);
+    }
+    if (k < nk) HY3_ITER(k, a, 0, b);
+
+    BigTile nxt;
+    int rn = r + nb;
+    while (rn < per && !big_tile_at<T, GATE_UP>(a, n_tiles, n_col_tiles, per, xcd, rn, nxt))
+      rn += nb;
+    const bool has_next = rn < per;
+    // The address arithmetic below uses fresh copies of the thread index, so
+    // that the compiler recomputes it per tile instead of hoisting it out of
+    // the tile loop and holding it in registers through the main loop.
+    if (has_next) {   // the finished tile's load descriptors are free
+      int tid_n = tid;
+      asm volatile("" : "+v"(tid_n));
+      big_tile_loads<T, GATE_UP>(a, nxt, tid_n >> 3, tid_n & 7, wb, xb, woff, xoff);
+      HY3_GLOAD(a, 0);
+      HY3_GLOAD(b, (1 < nxt.nk) ? 1 : 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int tid_e = tid;
+    asm volatile("" : "+v"(tid_e));
+    big_epilogue<T, GATE_UP>(a, cur, acc, lds, tid_e);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!has_next) break;
+    __syncthreads();   // the epilogue's LDS reads are done
+    HY3_LSTORE(a, 0);
+    __syncthreads();
+    cur = nxt;
+    r = rn;
   }
-  if (k < nk) HY3_ITER(k, a, 0, b);
 #undef HY3_ITER
 #undef HY3_COMPUTE
 #undef HY3_LSTORE
 #undef HY3_GLOAD
 
-  // ---- epilogue: lane holds D[weight row 16i + 4cg + q][token row 16j + r16] ----
-  T *out = static_cast<T *>(a.out);
-  if constexpr (sizeof(T) == 2) {
-    // Through LDS (free after the loop's last barrier): each lane writes its
-    // 4-column pieces into bf16 token rows (16-byte chunks swizzled by row),
-    // then each thread stores whole 16-byte chunks, so a wavefront writes two
-    // full output rows per instruction instead of 32-byte pieces of 16 rows.
-    constexpr int OC = GATE_UP ? BW / 2 / 8 : BW / 8;   // 16-byte chunks per tile row
-    char *stg = reinterpret_cast<char *>(lds);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wt_ * 64 + j * 16 + r16;
-      char *row = stg + r * OC * 16;
-      if (GATE_UP) {
-        // wavefront wr_ holds weight rows 128 wr_ + [0, 128): frags i = 0,1 are
-        // gate cols 64 wr_ + [0, 32), i = 2,3 their up cols, i = 4,5 gate cols
-        // 64 wr_ + [32, 64), i = 6,7 their up cols.
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int gi = (i >> 1) * 4 + (i & 1);
-          const int c = wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
-          const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
-          uint2 v;
-          v.x = pack_bf16x2(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]));
-          v.y = pack_bf16x2(swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
-          *reinterpret_cast<uint2 *>(row + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = v;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int c = wr_ * 128 + i * 16 + 4 * cg;
-          const f32x4_t v4 = acc[i][j];
-          uint2 v;
-          v.x = pack_bf16x2(v4[0], v4[1]);
-          v.y = pack_bf16x2(v4[2], v4[3]);
-          *reinterpret_cast<uint2 *>(row + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = v;
-        }
-      }
-    }
-    __syncthreads();
-    const int width = GATE_UP ? Ig : a.H;           // output columns of this matrix
-    const size_t ldo = GATE_UP ? (size_t)a.ldh : (size_t)a.H;
-#pragma unroll
-    for (int m = 0; m < 256 * OC / 512; ++m) {
-      const int q = tid + 512 * m;
-      const int r = q / OC, ch = q % OC;
-      const int c = col0 + ch * 8;
-      if (row0 + r < grp_end && c < width) {
-        const uint4 v = lds[r * OC + (ch ^ (r & 7))];
-        uint4 *dst = reinterpret_cast<uint4 *>(out + (size_t)(row0 + r) * ldo + c);
-        // written once, read by the next kernel: non-temporal
-        __builtin_nontemporal_store(v.x, &dst->x);
-        __builtin_nontemporal_store(v.y, &dst->y);
-        __builtin_nontemporal_store(v.z, &dst->z);
-        __builtin_nontemporal_store(v.w, &dst->w);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int trow = row0 + wt_ * 64 + j * 16 + r16;
-      if (trow >= grp_end) continue;
-      if (GATE_UP) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int gi = (i >> 1) * 4 + (i & 1);
-          const int c = col0 + wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
-          if (c >= Ig) continue;
-          const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
-          store4(out + (size_t)trow * a.ldh + c, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
-                 swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int n = col0 + wr_ * 128 + i * 16 + 4 * cg;
-          if (n >= a.H) continue;
-          const f32x4_t v = acc[i][j];
-          store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
-        }
-      }
-    }
-  }
 }
 
 template <typename T>
@@ -318,7 +378,15 @@ hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   // upper bound of row tiles, padded to a multiple of the 8 XCDs.
   const int bands = (a.max_tiles + BAND - 1) / BAND;
   const long logical = (long)bands * BAND * nct;
-  const dim3 grid((unsigned)((logical + 7) / 8 * 8));
+  // One workgroup per CU (the LDS of a workgroup fills most of a CU); each
+  // walks its XCD's tiles.
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  const long cap = n_cu >= 8 ? n_cu / 8 * 8 : 8;
+  const long want = (logical + 7) / 8 * 8;
+  const dim3 grid((unsigned)(want < cap ? want : cap));
   if (gate_up)
     hipLaunchKernelGGL((expert_big_kernel<T, true>), grid, dim3(512), 0, stream, a, nct);
   else
