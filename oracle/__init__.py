@@ -2,12 +2,13 @@
 imported by tests, the smoke check and the benchmark's CPU-baseline leg,
 never by the product path."""
 from .moe import (ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, dense_masked,
-                  forward, forward_given_route, layer_flops, route,
+                  dequant_fp8, forward, forward_given_route, fp8_e4m3_value,
+                  layer_flops, route,
                   route_from_logits, router_logits, sigmoid, silu,
                   softmax_rows, swiglu_expert, topk_desc)
 
 __all__ = [
-    "ROUTE_SIGMOID_BIAS", "ROUTE_SOFTMAX", "Route", "dense_masked", "forward",
-    "forward_given_route", "layer_flops", "route", "route_from_logits",
+    "ROUTE_SIGMOID_BIAS", "ROUTE_SOFTMAX", "Route", "dense_masked", "dequant_fp8",
+    "forward", "forward_given_route", "fp8_e4m3_value", "layer_flops", "route", "route_from_logits",
     "router_logits", "sigmoid", "silu", "softmax_rows", "swiglu_expert", "topk_desc",
 ]

@@ -38,6 +38,18 @@ in the design notes):
 * sigmoid mode has no renormalisation epsilon (a sum of sigmoids is > 0);
 * selection is flat over all E experts (no expert groups).
 
+FP8 expert weights (the CANN deployment article, section 8.2 "量化策略":
+FP8 W8A8 weights with tensor-wise scales, routed experts quantised further
+to MXFP4 there; Hy3 Preview inference case, section 12: W8A8 among the
+deployed precisions).  A weight matrix is stored as one byte per element in
+the OCP FP8 E4M3 encoding (1 sign, 4 exponent bits with bias 7, 3 mantissa
+bits; subnormals at exponent field 0; no infinities; S.1111.111 is NaN) and
+one float32 scale per matrix; its value is scale * decode(code).  The pages
+fix neither the encoding variant nor the scale granularity beyond "tensor":
+E4M3 as above and one scale per expert matrix is the reading taken here.
+The oracle dequantises exactly (every E4M3 value times a float32 scale is
+exact in float64) and then runs the same float64 layer.
+
 Parity pins: every public function is pinned by a test in
 ``tests/test_oracle_pins.py`` (hand-derived golden values, brute force over
 all K-subsets, a loop-only dense evaluation, closed forms and invariants).
@@ -158,6 +170,32 @@ def route(x, w_router, K: int, mode: int = ROUTE_SIGMOID_BIAS, bias=None,
           scale: float = 2.826, renorm_eps: float = 1e-8) -> Route:
     """The gate of the layer: router logits, then scores/selection/weights."""
     return route_from_logits(router_logits(x, w_router), K, mode, bias, scale, renorm_eps)
+
+
+# --------------------------------------------------------------------------
+# FP8 expert weights
+# --------------------------------------------------------------------------
+def fp8_e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP FP8 E4M3 codes (uint8) in float64; NaN for S.1111.111.
+
+    Normal codes (exponent field e in 1..15): (-1)^s * (1 + m/8) * 2^(e-7).
+    Subnormal codes (e = 0): (-1)^s * (m/8) * 2^-6.  E4M3 has no infinities:
+    exponent field 15 is an ordinary binade except for mantissa 7 (NaN), so
+    the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6,
+                   (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, out)
+
+
+def dequant_fp8(codes: np.ndarray, scale) -> np.ndarray:
+    """scale * E4M3 value of every code, in float64 (one scale per matrix)."""
+    return np.float64(np.float32(scale)) * fp8_e4m3_value(codes)
 
 
 # --------------------------------------------------------------------------

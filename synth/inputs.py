@@ -31,6 +31,17 @@ parameter of N is the standard deviation.
 
 bfloat16 values are produced from float32 draws by round-to-nearest-even on
 the bit pattern and are stored as ``uint16`` arrays of the raw bits.
+
+FP8 expert weights (``w_format == "fp8_e4m3"``) are drawn directly as byte
+codes of the OCP FP8 E4M3 layout (sign, 4 exponent bits, 3 mantissa bits),
+not by quantising float draws: sign uniform, exponent field
+round(N(11.5, 1.3)) clipped to 0..15, mantissa field uniform, and the NaN
+pattern (exponent 15, mantissa 7) replaced by mantissa 6.  The encoded
+values then have a standard deviation of about 74, and 1 % of them lie in
+the top binade (up to 448).  Each matrix gets its own float32 scale
+(1 + U(0, 0.25)) / (74 sqrt(fan_in)), so that scale times value has about
+the spread of the bf16 weights.  Nothing here decodes the codes: that is
+the layer's own (de-quantisation) step.
 """
 from __future__ import annotations
 
@@ -42,6 +53,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 T_X, T_WR, T_BIAS, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN = range(9)
+T_CODES, T_SCALES = 100, 200     # offsets of the FP8 code and scale streams
 
 ROUTE_SIGMOID_BIAS = 0
 ROUTE_SOFTMAX = 1
@@ -93,6 +105,7 @@ class MoEConfig:
     scale: float               # router scaling factor applied to routed weights
     renorm_eps: float          # clamp of the renormalisation denominator
     bias_kind: str             # "uniform", "skew" or "none"
+    w_format: str = "dtype"    # expert weights: "dtype" (as `dtype`) or "fp8_e4m3"
 
     def with_T(self, T: int) -> "MoEConfig":
         return dataclasses.replace(self, T=int(T))
@@ -124,6 +137,11 @@ CONFIGS: Dict[int, MoEConfig] = {
                  K=8, I=1536, I_shared=1536, dtype="bf16",
                  route_mode=ROUTE_SOFTMAX, scale=1.0, renorm_eps=1e-8,
                  bias_kind="none"),
+    # Hy3 decode with FP8 E4M3 expert weights (one scale per matrix).
+    5: MoEConfig("hy3_decode_T16_fp8", 5, 5, T=16, H=4096, E=192, K=8, I=1536,
+                 I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                 scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform",
+                 w_format="fp8_e4m3"),
 }
 
 ROUTER_SWEEP_M = (2, 64, 512, 4096)
@@ -138,6 +156,20 @@ def _normal_f32(rng, shape, std: float) -> np.ndarray:
     a = rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
     a *= np.float32(std)
     return a.reshape(shape)
+
+
+def _fp8_codes(rng, shape) -> np.ndarray:
+    """E4M3 byte codes with the distribution described in the module notes."""
+    n = int(np.prod(shape))
+    sign = rng.integers(0, 2, n, dtype=np.int64)
+    ex = np.clip(np.rint(rng.normal(11.5, 1.3, n)), 0, 15).astype(np.int64)
+    man = rng.integers(0, 8, n, dtype=np.int64)
+    man = np.where((ex == 15) & (man == 7), 6, man)
+    return ((sign << 7) | (ex << 3) | man).astype(np.uint8).reshape(shape)
+
+
+def _fp8_scale(rng, fan_in: int) -> np.float32:
+    return np.float32((1.0 + 0.25 * rng.random()) / (74.0 * np.sqrt(fan_in)))
 
 
 def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
@@ -244,6 +276,50 @@ class MoEInputs:
         with ThreadPoolExecutor(threads or _default_threads()) as ex:
             list(ex.map(job, range(c.E)))
         return wg, wu, wd
+
+    # ---- FP8 expert weights (w_format == "fp8_e4m3") ----
+    def expert_fp8(self, e: int):
+        """((gate, up, down) uint8 E4M3 codes, (s_gate, s_up, s_down) float32) of expert e."""
+        c = self.cfg
+        mk = c.model_key
+        codes = (_fp8_codes(_rng(self.seed, mk, T_CODES + T_GATE, e), (c.I, c.H)),
+                 _fp8_codes(_rng(self.seed, mk, T_CODES + T_UP, e), (c.I, c.H)),
+                 _fp8_codes(_rng(self.seed, mk, T_CODES + T_DOWN, e), (c.H, c.I)))
+        rs = _rng(self.seed, mk, T_SCALES, e)
+        scales = (_fp8_scale(rs, c.H), _fp8_scale(rs, c.H), _fp8_scale(rs, c.I))
+        return codes, scales
+
+    def shared_fp8(self):
+        c = self.cfg
+        if c.I_shared == 0:
+            return None
+        k = ("shared_fp8",)
+        if k not in self._cache:
+            mk, Is = c.model_key, c.I_shared
+            codes = (_fp8_codes(_rng(self.seed, mk, T_CODES + T_SGATE), (Is, c.H)),
+                     _fp8_codes(_rng(self.seed, mk, T_CODES + T_SUP), (Is, c.H)),
+                     _fp8_codes(_rng(self.seed, mk, T_CODES + T_SDOWN), (c.H, Is)))
+            rs = _rng(self.seed, mk, T_SCALES + T_SGATE)
+            scales = (_fp8_scale(rs, c.H), _fp8_scale(rs, c.H), _fp8_scale(rs, Is))
+            self._cache[k] = (codes, scales)
+        return self._cache[k]
+
+    def stacked_experts_fp8(self, threads: Optional[int] = None):
+        """Codes gate/up [E,I,H], down [E,H,I] (uint8) and scales [3, E] (float32)."""
+        c = self.cfg
+        wg = np.empty((c.E, c.I, c.H), dtype=np.uint8)
+        wu = np.empty((c.E, c.I, c.H), dtype=np.uint8)
+        wd = np.empty((c.E, c.H, c.I), dtype=np.uint8)
+        sc = np.empty((3, c.E), dtype=np.float32)
+
+        def job(e):
+            (g, u, d), s = self.expert_fp8(e)
+            wg[e], wu[e], wd[e] = g, u, d
+            sc[:, e] = s
+
+        with ThreadPoolExecutor(threads or _default_threads()) as ex:
+            list(ex.map(job, range(c.E)))
+        return wg, wu, wd, sc
 
     # ---- float64 views for the oracle ----
     def x_f64(self) -> np.ndarray:

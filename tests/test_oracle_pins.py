@@ -328,3 +328,73 @@ def test_empty_token_batch():
 def test_flop_count():
     f = oracle.layer_flops(T=8192, H=4096, E=192, K=8, I=1536, I_shared=1536)
     assert abs(f["experts"] - 2.783e12) / 2.783e12 < 1e-3
+
+
+# ------------------------------------------------------ FP8 expert weights ----
+# OCP FP8 E4M3 (the encoding the FP8 weights are read in): code -> value,
+# worked by hand from the layout (sign, exponent bias 7, 3 mantissa bits,
+# subnormals at exponent field 0, S.1111.111 = NaN, no infinities).
+E4M3_HAND = {
+    0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+    0x0F: 1.875 * 2.0 ** -6, 0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0,
+    0x77: 240.0, 0x78: 256.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9),
+}
+
+
+def test_fp8_e4m3_hand_values():
+    codes = np.array(list(E4M3_HAND), dtype=np.uint8)
+    got = oracle.fp8_e4m3_value(codes)
+    np.testing.assert_array_equal(got, np.array(list(E4M3_HAND.values())))
+    v = oracle.fp8_e4m3_value(np.array([0x7F, 0xFF, 0x80], dtype=np.uint8))
+    assert np.isnan(v[0]) and np.isnan(v[1]) and v[2] == 0.0 and np.signbit(v[2])
+
+
+def test_fp8_e4m3_matches_torch_for_every_code():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.fp8_e4m3_value(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def test_fp8_e4m3_structure():
+    v = oracle.fp8_e4m3_value(np.arange(256, dtype=np.uint8))
+    pos = v[:0x7F]                       # codes 0x00..0x7E
+    assert (np.diff(pos) > 0).all()      # strictly increasing magnitudes
+    np.testing.assert_array_equal(v[0x80:0xFF], -pos)
+    assert np.isnan(v).sum() == 2
+    assert len(np.unique(v[~np.isnan(v)])) == 253        # +0 and -0 compare equal
+    # spacing: 2^-9 through the subnormals and the first binade, then doubling
+    np.testing.assert_array_equal(np.diff(pos[:16]), np.full(15, 2.0 ** -9))
+    assert pos[-1] - pos[-2] == 32.0
+
+
+def test_fp8_dequant_is_scale_times_value():
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, size=(7, 9)).astype(np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0x10
+    s = np.float32(0.0123)
+    d = oracle.dequant_fp8(codes, s)
+    np.testing.assert_array_equal(d, np.float64(s) * oracle.fp8_e4m3_value(codes))
+    # exact: the product of a 4-bit significand and a 24-bit one fits float64
+    assert (d / np.float64(s) == oracle.fp8_e4m3_value(codes)).all()
+
+
+def test_fp8_layer_equals_layer_on_dequantised_weights():
+    """The FP8 layer is the float64 layer on scale * value weights: a scale of
+    2^k on a down matrix scales that expert's routed output by exactly 2^k."""
+    inp = MoEInputs(CONFIGS[5].with_T(6).with_(H=64, E=4, K=2, I=32, I_shared=32))
+    c = inp.cfg
+    x = inp.x_f64()
+    wr = inp.w_router().astype(np.float64)
+    experts = {}
+    for e in range(c.E):
+        codes, sc = inp.expert_fp8(e)
+        experts[e] = tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))
+    out, r = oracle.forward(x, wr, lambda e: experts[e], c.E, c.K, None, 0,
+                            inp.bias().astype(np.float64), c.scale)
+    doubled = {e: (g, u, 2.0 * d) for e, (g, u, d) in experts.items()}
+    out2 = oracle.forward_given_route(x, r.idx, r.weight, lambda e: doubled[e], c.E)
+    np.testing.assert_allclose(out2, 2.0 * out, rtol=0, atol=0)

@@ -79,3 +79,21 @@ def test_bf16_storage_and_stack():
 def test_config_shapes(cfg_id):
     c = CONFIGS[cfg_id]
     assert 1 <= c.K <= c.E and c.H % 8 == 0 and c.I % 8 == 0
+
+
+def test_fp8_codes_and_scales():
+    from synth import CONFIGS, MoEInputs
+    inp = MoEInputs(CONFIGS[5].with_T(2).with_(H=256, E=3, I=128, I_shared=64))
+    (g, u, d), sc = inp.expert_fp8(1)
+    assert g.dtype == np.uint8 and g.shape == (128, 256) and d.shape == (256, 128)
+    for q in (g, u, d):
+        assert not ((q & 0x7F) == 0x7F).any()          # never the NaN pattern
+    assert all(isinstance(s, np.float32) and s > 0 for s in sc)
+    (g2, _, _), sc2 = inp.expert_fp8(1)
+    assert (g2 == g).all() and sc2 == sc                # reproducible
+    (g3, _, _), _ = inp.expert_fp8(2)
+    assert (g3 != g).mean() > 0.5                       # independent per expert
+    wg, wu, wd, s = inp.stacked_experts_fp8()
+    assert (wg[1] == g).all() and s.shape == (3, 3) and s[0, 1] == sc[0]
+    sh_codes, sh_sc = inp.shared_fp8()
+    assert sh_codes[2].shape == (256, 64) and len(sh_sc) == 3
