@@ -8,7 +8,8 @@ one batch of seeded synthetic input already resident in HBM.
 Default workload: Hy3 decode, T=16 tokens, H=4096, 192 routed experts
 (top-8) + 1 shared expert, I=1536, bf16 weights/activations, fp32 router.
 `--workload prefill` (T=8192, skewed bias) and `--workload softmax`
-(HunyuanImage-3.0 softmax routing, T=32768, E=64) run the other layer shapes.
+(HunyuanImage-3.0 softmax routing, T=32768, E=64) run the other layer shapes;
+`--workload decode_fp8` is the decode shape with FP8 E4M3 expert weights.
 
 Printed: one JSON line with tokens/s, the dominant kernel's roofline fraction
 (its per-launch duration measured live with HIP events on the library's
@@ -28,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4}
+WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4, "decode_fp8": 5}
 ROUTER_WORKLOAD = 3            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
@@ -111,7 +112,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {c.name}: inputs uploaded in {time.time() - t0:.1f}s")
     cfg = sm.make_config(c.T, c.H, c.E, c.K, c.I, c.I_shared, c.dtype, c.route_mode,
-                         scale=c.scale, renorm_eps=c.renorm_eps)
+                         scale=c.scale, renorm_eps=c.renorm_eps, w_format=c.w_format)
     ws = sm.alloc_workspace(cfg, True, dev)
     out = torch.empty_like(x)
     idx = torch.empty((c.T, c.K), dtype=torch.int32, device=dev)
@@ -174,11 +175,12 @@ def main():
 
     # ---- algorithmic work ----
     eb = 2 if c.dtype == "bf16" else 4
+    web = 1 if c.w_format == "fp8_e4m3" else eb      # bytes per expert weight element
     T, H, E, K, I, Is = c.T, c.H, c.E, c.K, c.I, c.I_shared
     R = T * K + (T if Is else 0)
     groups = U + (1 if Is else 0)
-    gu_weight_bytes = U * 2 * I * H * eb + (2 * Is * H * eb if Is else 0)
-    dn_weight_bytes = U * H * I * eb + (H * Is * eb if Is else 0)
+    gu_weight_bytes = U * 2 * I * H * web + (2 * Is * H * web if Is else 0)
+    dn_weight_bytes = U * H * I * web + (H * Is * web if Is else 0)
     gu_bytes = gu_weight_bytes + T * H * eb + R * I * eb
     dn_bytes = dn_weight_bytes + R * I * eb + R * H * eb
     layer_bytes = gu_weight_bytes + dn_weight_bytes + E * H * 4 + 2 * T * H * eb
@@ -187,12 +189,13 @@ def main():
     layer_flops = 1.5 * gu_flops + 2.0 * T * H * E
     layer_s = ms_per_step / 1e3
     gu_s = stage_ms["gate_up"] / 1e3
-    decode = args.workload == "decode"
+    decode = args.workload in ("decode", "decode_fp8")
     if decode:
+        kind = "FP8 E4M3" if web == 1 else c.dtype
         roof = {"kernel": "gate_up (weight-streaming grouped GEMM + SwiGLU)", "bound": "hbm",
                 "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "per_unit": f"{2 * I * H * eb} B of gate+up weights per touched expert "
-                            f"x {groups} experts + x and h rows"}
+                "per_unit": f"{2 * I * H * web} B of {kind} gate+up weights per touched "
+                            f"expert x {groups} experts + x and h rows"}
     else:
         tile_rows = sm.hy3moe_workspace_layout(cfg).tile_rows
         path = "256x256-tile" if tile_rows == 256 else "128x128-tile"
@@ -234,7 +237,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c.dtype,
         "data": "synthetic (seeded, random-init weights of the layer's shapes)",
         "config": {"workload": c.name, "T": T, "H": H, "E": E, "K": K, "I": I, "I_shared": Is,
-                   "route": "sigmoid+bias" if c.route_mode == 0 else "softmax"},
+                   "route": "sigmoid+bias" if c.route_mode == 0 else "softmax",
+                   "expert_weights": "fp8_e4m3" if web == 1 else c.dtype},
         "roofline": roof, "cpu_baseline": cpu, "layer": layer,
         "graph_ms_per_step": graph_ms,
     }
@@ -362,7 +366,7 @@ def cpu_baseline(inp, args, gpu_idx):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     c = inp.cfg
-    n = args.cpu_sample_tokens or (16 if args.workload == "decode" else 48)
+    n = args.cpu_sample_tokens or (16 if args.workload.startswith("decode") else 48)
     n = min(n, c.T)
     tokens = np.arange(n)
     x64 = inp.x_f64()[tokens]
@@ -371,16 +375,24 @@ def cpu_baseline(inp, args, gpu_idx):
     b64 = None if b is None else b.astype(np.float64)
     need = sorted(set(gpu_idx[tokens].reshape(-1).tolist()))
     t0 = time.time()
+    if c.w_format == "fp8_e4m3":      # the oracle's own dequantisation of the codes
+        def expert_f64(e):
+            codes, sc = inp.expert_fp8(e)
+            return tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))
+        shf = inp.shared_fp8()
+        sh = None if shf is None else tuple(oracle.dequant_fp8(q, s) for q, s in zip(*shf))
+    else:
+        expert_f64 = inp.expert_f64
+        sh = inp.shared_f64()
     with ThreadPoolExecutor(8) as ex:
-        ws = dict(zip(need, ex.map(inp.expert_f64, need)))
-    sh = inp.shared_f64()
+        ws = dict(zip(need, ex.map(expert_f64, need)))
     log(f"[bench] oracle sample: {n} tokens, {len(need)} experts in float64 "
         f"(generated in {time.time() - t0:.1f}s)")
     # Experts the oracle picks that the GPU did not (near-ties) are input
     # preparation and are generated before timing.
     r = oracle.route(x64, wr, c.K, c.route_mode, b64, c.scale, c.renorm_eps)
     for e in sorted(set(r.idx.reshape(-1).tolist()) - set(ws)):
-        ws[e] = inp.expert_f64(e)
+        ws[e] = expert_f64(e)
     # Repeat the whole sample (route + experts + combine) until ~target seconds.
     reps, dt = 0, 0.0
     while reps < 3 or (dt < args.cpu_seconds and reps < 10000):

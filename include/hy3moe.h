@@ -33,6 +33,8 @@
  *  - Element types: HY3MOE_BF16 means bfloat16 (1-8-7 bits) for x, out and
  *    all expert weights; HY3MOE_F32 means float32 for them.  The router
  *    weight, the expert bias and the combine weights are always float32.
+ *    With w_format HY3MOE_WFMT_FP8_E4M3 the expert weights are instead one
+ *    byte per element (see hy3moe_config.w_format).
  */
 #ifndef HY3MOE_H
 #define HY3MOE_H
@@ -49,7 +51,8 @@ extern "C" {
 #define HY3MOE_ERR_INVALID     -1  /* null pointer, T<0, K<1, K>E, E>256, K>64, bad enum */
 #define HY3MOE_ERR_UNSUPPORTED -2  /* H, I or I_shared not a multiple of 64; T > 2^24;
                                       H, I or I_shared > 65536; T*H or H*max(I, I_shared)
-                                      elements of 4 GiB or more; split router with fp32 x */
+                                      elements of 4 GiB or more; split router with fp32 x;
+                                      FP8 expert weights with fp32 x or with T > 64   */
 #define HY3MOE_ERR_WORKSPACE   -3  /* workspace smaller than hy3moe_workspace_bytes()   */
 #define HY3MOE_ERR_ALIGN       -4  /* a pointer is not 16-byte aligned                  */
 #define HY3MOE_ERR_HIP         -5  /* a kernel launch failed (hipGetLastError)          */
@@ -70,6 +73,19 @@ extern "C" {
 #define HY3MOE_ROUTER_FP32        0
 #define HY3MOE_ROUTER_SPLIT2_BF16 1
 
+/* Storage of the expert weights (w_gate, w_up, w_down and the shared
+ * expert's).  DTYPE: elements of cfg.dtype.  FP8_E4M3: one byte per element
+ * in the OCP FP8 E4M3 encoding (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; no infinities; S.1111.111 is NaN) with one float32 scale per expert
+ * matrix, the weight being scale * value (the FP8 W8A8 weights of the CANN
+ * deployment article, section 8.2, with tensor-wise scales).  Activations
+ * stay bfloat16 (x and out bf16, cfg.dtype must be HY3MOE_BF16); the expert
+ * GEMMs decode the codes exactly to bfloat16 and apply the scale to the
+ * float32 accumulators.  Supported for the weight-streaming batches
+ * (T <= 64), where the weight bytes set the time. */
+#define HY3MOE_WFMT_DTYPE    0
+#define HY3MOE_WFMT_FP8_E4M3 1
+
 /* Shape and mode of one layer call. */
 typedef struct hy3moe_config {
   int64_t T;          /* tokens (rows of x)                                   */
@@ -83,6 +99,7 @@ typedef struct hy3moe_config {
   int32_t router_prec;/* HY3MOE_ROUTER_*                                      */
   float   scale;      /* routed-weight scale: 2.826 for Hy3, 1 for softmax    */
   float   renorm_eps; /* softmax mode: clamp of the top-K sum (1e-8); sigmoid mode: unused */
+  int32_t w_format;   /* HY3MOE_WFMT_*: storage of the expert weights            */
 } hy3moe_config;
 
 /* Weights.  Layouts follow nn.Linear [out, in] (K-contiguous rows), stacked
@@ -91,7 +108,13 @@ typedef struct hy3moe_config {
  *   expert_bias [E]      fp32, sigmoid mode only; NULL means all zero
  *   w_gate, w_up [E, I, H]      dtype
  *   w_down       [E, H, I]      dtype
- *   ws_gate, ws_up [I_shared, H], ws_down [H, I_shared]  dtype (NULL if I_shared==0) */
+ *   ws_gate, ws_up [I_shared, H], ws_down [H, I_shared]  dtype (NULL if I_shared==0)
+ * With w_format FP8_E4M3 the six expert tensors hold E4M3 bytes and
+ *   w_gate_scale, w_up_scale, w_down_scale [E]   fp32, one per routed matrix
+ *   ws_scale [3]   fp32: shared gate, up, down (NULL if I_shared == 0)
+ * are required (4-byte aligned); with FP8 weights the six expert pointers
+ * need 16-byte alignment as always.  The scale pointers are ignored for
+ * w_format DTYPE. */
 typedef struct hy3moe_weights {
   const float *w_router;
   const float *expert_bias;
@@ -101,6 +124,10 @@ typedef struct hy3moe_weights {
   const void  *ws_gate;
   const void  *ws_up;
   const void  *ws_down;
+  const float *w_gate_scale;
+  const float *w_up_scale;
+  const float *w_down_scale;
+  const float *ws_scale;
 } hy3moe_weights;
 
 /* Byte offsets of the intermediate buffers inside a forward workspace (for

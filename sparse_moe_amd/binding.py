@@ -22,9 +22,11 @@ HY3MOE_ROUTE_SIGMOID_BIAS = 0
 HY3MOE_ROUTE_SOFTMAX = 1
 HY3MOE_ROUTER_FP32 = 0
 HY3MOE_ROUTER_SPLIT2_BF16 = 1
+HY3MOE_WFMT_DTYPE = 0
+HY3MOE_WFMT_FP8_E4M3 = 1
 
 HY3MOE_N_STAGES = 6
-ABI_VERSION = 2          # hy3moe_abi_version() of the library this binding matches
+ABI_VERSION = 3          # hy3moe_abi_version() of the library this binding matches
 STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 
 EXPORTED_SYMBOLS = (
@@ -39,13 +41,16 @@ class hy3moe_config(ctypes.Structure):
         ("K", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("route_mode", ctypes.c_int32),
         ("router_prec", ctypes.c_int32), ("scale", ctypes.c_float),
-        ("renorm_eps", ctypes.c_float),
+        ("renorm_eps", ctypes.c_float), ("w_format", ctypes.c_int32),
     ]
 
 
+WEIGHT_NAMES = ("w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up",
+                "ws_down", "w_gate_scale", "w_up_scale", "w_down_scale", "ws_scale")
+
+
 class hy3moe_weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in (
-        "w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
 
 
 class hy3moe_ws_layout(ctypes.Structure):
@@ -121,12 +126,14 @@ def strerror(code: int) -> str:
 def make_config(T: int, H: int, E: int, K: int, I: int, I_shared: int, dtype: str = "bf16",
                 route_mode: int = HY3MOE_ROUTE_SIGMOID_BIAS,
                 router_prec: int = HY3MOE_ROUTER_FP32, scale: float = 2.826,
-                renorm_eps: float = 1e-8) -> hy3moe_config:
+                renorm_eps: float = 1e-8, w_format: str = "dtype") -> hy3moe_config:
     return hy3moe_config(T=int(T), H=int(H), E=int(E), K=int(K), I=int(I),
                          I_shared=int(I_shared),
                          dtype=HY3MOE_BF16 if dtype == "bf16" else HY3MOE_F32,
                          route_mode=int(route_mode), router_prec=int(router_prec),
-                         scale=float(scale), renorm_eps=float(renorm_eps))
+                         scale=float(scale), renorm_eps=float(renorm_eps),
+                         w_format=(HY3MOE_WFMT_FP8_E4M3 if w_format == "fp8_e4m3"
+                                   else HY3MOE_WFMT_DTYPE))
 
 
 def hy3moe_workspace_bytes(cfg: hy3moe_config, for_forward: bool = True) -> int:
@@ -184,8 +191,7 @@ def hy3moe_forward(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str, torch
                    idx_out: Optional[torch.Tensor] = None,
                    weight_out: Optional[torch.Tensor] = None, stream=None) -> None:
     """C ABI hy3moe_forward on torch device tensors (result in out)."""
-    names = ("w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
-    ts = [weights.get(n) for n in names]
+    ts = [weights.get(n) for n in WEIGHT_NAMES]
     _check_dev(x, out, workspace, idx_out, weight_out, *ts)
     w = hy3moe_weights(*[_ptr(t) for t in ts])
     rc = load().hy3moe_forward(ctypes.byref(cfg), _ptr(x), ctypes.byref(w), _ptr(out),
@@ -202,8 +208,7 @@ def hy3moe_forward_timed(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str,
     """C ABI hy3moe_forward_timed; ``events`` are HY3MOE_N_STAGES + 1 torch.cuda.Event
     objects created with enable_timing=True (already recorded once, so that their
     HIP handles exist)."""
-    names = ("w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
-    ts = [weights.get(n) for n in names]
+    ts = [weights.get(n) for n in WEIGHT_NAMES]
     _check_dev(x, out, workspace, idx_out, weight_out, *ts)
     if len(events) != HY3MOE_N_STAGES + 1:
         raise ValueError("need HY3MOE_N_STAGES + 1 events")

@@ -39,6 +39,11 @@ int validate_cfg(const hy3moe_config *c) {
   if (c->T > (int64_t(1) << 24)) return HY3MOE_ERR_UNSUPPORTED;
   if (c->router_prec == HY3MOE_ROUTER_SPLIT2_BF16 && c->dtype != HY3MOE_BF16)
     return HY3MOE_ERR_UNSUPPORTED;
+  if (c->w_format != HY3MOE_WFMT_DTYPE && c->w_format != HY3MOE_WFMT_FP8_E4M3)
+    return HY3MOE_ERR_INVALID;
+  // FP8 expert weights: bf16 activations, weight-streaming batches only.
+  if (c->w_format == HY3MOE_WFMT_FP8_E4M3 && (c->dtype != HY3MOE_BF16 || c->T > SKINNY_MAX_T))
+    return HY3MOE_ERR_UNSUPPORTED;
   // The expert GEMMs address x and every expert matrix with 32-bit offsets.
   const uint64_t eb = c->dtype == HY3MOE_F32 ? 4 : 2, lim = uint64_t(1) << 32;
   const uint64_t Imax = c->I > c->I_shared ? c->I : c->I_shared;
@@ -94,7 +99,7 @@ int check_launch(hipError_t e) { return e == hipSuccess ? HY3MOE_OK : HY3MOE_ERR
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 2; }
+int hy3moe_abi_version(void) { return 3; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {
@@ -166,6 +171,14 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
     return HY3MOE_ERR_ALIGN;
   if (has_shared && (!al16(w->ws_gate) || !al16(w->ws_up) || !al16(w->ws_down)))
     return HY3MOE_ERR_ALIGN;
+  const bool fp8 = cfg->w_format == HY3MOE_WFMT_FP8_E4M3;
+  if (fp8) {
+    if (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale || (has_shared && !w->ws_scale))
+      return HY3MOE_ERR_INVALID;
+    if (!al4(w->w_gate_scale) || !al4(w->w_up_scale) || !al4(w->w_down_scale) ||
+        (has_shared && !al4(w->ws_scale)))
+      return HY3MOE_ERR_ALIGN;
+  }
   hy3moe_ws_layout L;
   compute_layout(cfg, 1, &L);
   if (ws_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
@@ -224,12 +237,21 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.max_tiles = L.max_tiles;
   ea.act = x; ea.w0 = w->w_gate; ea.w1 = w->w_up; ea.ws0 = w->ws_gate; ea.ws1 = w->ws_up;
   ea.out = ws + L.h;
+  ea.w_fp8 = fp8 ? 1 : 0;
+  ea.sc0 = fp8 ? w->w_gate_scale : nullptr;
+  ea.sc1 = fp8 ? w->w_up_scale : nullptr;
+  ea.ssc0 = fp8 && has_shared ? w->ws_scale : nullptr;
+  ea.ssc1 = fp8 && has_shared ? w->ws_scale + 1 : nullptr;
   const int path = expert_path(T, K, E);
   rc = check_launch(launch_gate_up(ea, cfg->dtype, T, path, s));
   if (rc) return rc;
   mark();
   ea.act = ws + L.h; ea.w0 = w->w_down; ea.w1 = nullptr; ea.ws0 = w->ws_down; ea.ws1 = nullptr;
   ea.out = ws + L.y;
+  ea.sc0 = fp8 ? w->w_down_scale : nullptr;
+  ea.sc1 = nullptr;
+  ea.ssc0 = fp8 && has_shared ? w->ws_scale + 2 : nullptr;
+  ea.ssc1 = nullptr;
   rc = check_launch(launch_down(ea, cfg->dtype, T, path, s));
   if (rc) return rc;
   mark();

@@ -69,6 +69,11 @@ struct ExpertArgs {
   const int32_t *offsets;
   const int32_t *tiles;   // (group, first row) pairs, then the tile count
   int E, H, I, I_shared, ldh, max_tiles;
+  // FP8 E4M3 expert weights (w_fp8 = 1): w0/w1/ws0/ws1 hold bytes and the
+  // weight is scale * value, with scales sc0[g] / sc1[g] for routed group g
+  // and *ssc0 / *ssc1 for the shared expert (gate-up: gate, up; down: down).
+  int w_fp8;
+  const float *sc0, *sc1, *ssc0, *ssc1;
 };
 hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);
 hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);

@@ -18,6 +18,14 @@
 // with more row fragments to stay within two wavefronts' registers per SIMD).
 // The token rows (gathered through sorted_token for gate-up, contiguous h rows
 // for down; padded by reloading a valid row) are the other MFMA operand.
+//
+// FP8 E4M3 weights (one byte per element, one float32 scale per matrix): a
+// 64-byte step then holds 64 K values per row.  Lane (r16, g) loads bytes
+// [16g, 16g + 16) of the step and decodes them exactly to two bf16 fragments
+// (K values 16g + [0, 8) and 16g + [8, 16)), and loads the matching 2 x 16
+// bytes of each token row; the two MFMAs of a step pair them up.  The scale
+// multiplies the float32 accumulators before SwiGLU / the store.  Half the
+// weight bytes per K value is the point: this path is bound by them.
 #include "common.cuh"
 #include "internal.h"
 
@@ -27,6 +35,22 @@ namespace {
 
 constexpr int UBASE = 8;          // 64-byte K steps per register set (one row fragment)
 constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
+
+// 64-byte steps per register set: bf16 weights UBASE / MT; FP8 weights 6 / 3
+// / 1 for 1 / 2 / 4 row fragments (each step also holds two token chunks).
+template <int MT, bool F8>
+constexpr int steps_per_set() {
+  return F8 ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1)) : UBASE / MT;
+}
+
+// 16 E4M3 bytes -> two fragments of 8 bf16 (bytes 0-7, bytes 8-15), exact.
+__device__ __forceinline__ void e4m3x16_to_bf16(const uint4 &q, uint4 &lo, uint4 &hi) {
+#define HY3_CV(w, h) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((w), 1.0f, (h)))
+  lo = make_uint4(HY3_CV(q.x, false), HY3_CV(q.x, true), HY3_CV(q.y, false), HY3_CV(q.y, true));
+  hi = make_uint4(HY3_CV(q.z, false), HY3_CV(q.z, true), HY3_CV(q.w, false), HY3_CV(q.w, true));
+#undef HY3_CV
+}
 
 // Where a unit's operands are (per lane) and what its epilogue needs.
 template <int MT>
@@ -38,15 +62,17 @@ struct UnitSrc {
 };
 struct UnitOut {
   int row0, grp_end, col0, nsub, nf;
+  float sc0, sc1;          // FP8 weights: scales of fragment 0 / 1's matrix
 };
 
 // Unit u (tile u / n_col_blocks, column block u % n_col_blocks) of this
 // kernel; returns false if the column block lies past the group's width.
 // half = 1 or 2: only the first or the second 16-row fragment of a down unit.
-template <typename T, bool GATE_UP, int MT>
+template <typename T, bool GATE_UP, int MT, bool F8>
 __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_blocks, int lane,
                                         UnitSrc<MT> &src, UnitOut &o, int half = 0) {
   constexpr int EB = Elem<T>::kBytes;
+  constexpr int WB = F8 ? 1 : EB;           // bytes per weight element
   const int tile = u / n_col_blocks, cb = u - tile * n_col_blocks;
   const int g = a.tiles[2 * tile];
   o.row0 = a.tiles[2 * tile + 1];
@@ -54,26 +80,30 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
   const bool shared = (g == a.E);
   const int Ig = shared ? a.I_shared : a.I;
   o.col0 = cb * (GATE_UP ? 16 : 32) + (half == 2 ? 16 : 0);
-  o.nsub = (GATE_UP ? a.H : Ig) * EB / 64;
+  o.nsub = (GATE_UP ? a.H : Ig) * WB / 64;
   o.nf = half ? 1 : 2;
   if (o.col0 >= (GATE_UP ? Ig : a.H)) return false;
   src.nsub = o.nsub;
   src.nf = o.nf;
   const int r16 = lane & 15, cg = lane >> 4;
   if (GATE_UP) {
-    const T *gate = shared ? static_cast<const T *>(a.ws0)
-                           : static_cast<const T *>(a.w0) + (size_t)g * a.I * a.H;
-    const T *up = shared ? static_cast<const T *>(a.ws1)
-                         : static_cast<const T *>(a.w1) + (size_t)g * a.I * a.H;
-    src.w0p = reinterpret_cast<const char *>(gate + (size_t)(o.col0 + r16) * a.H) + cg * 16;
-    src.w1p = reinterpret_cast<const char *>(up + (size_t)(o.col0 + r16) * a.H) + cg * 16;
+    const char *gate = shared ? static_cast<const char *>(a.ws0)
+                              : static_cast<const char *>(a.w0) + (size_t)g * a.I * a.H * WB;
+    const char *up = shared ? static_cast<const char *>(a.ws1)
+                            : static_cast<const char *>(a.w1) + (size_t)g * a.I * a.H * WB;
+    src.w0p = gate + (size_t)(o.col0 + r16) * a.H * WB + cg * 16;
+    src.w1p = up + (size_t)(o.col0 + r16) * a.H * WB + cg * 16;
   } else {
-    const T *dn = shared ? static_cast<const T *>(a.ws0)
-                         : static_cast<const T *>(a.w0) + (size_t)g * a.H * a.I;
+    const char *dn = shared ? static_cast<const char *>(a.ws0)
+                            : static_cast<const char *>(a.w0) + (size_t)g * a.H * a.I * WB;
     const int n0 = (o.col0 + r16 < a.H) ? o.col0 + r16 : o.col0;
     const int n1 = (o.col0 + 16 + r16 < a.H) ? o.col0 + 16 + r16 : o.col0;
-    src.w0p = reinterpret_cast<const char *>(dn + (size_t)n0 * Ig) + cg * 16;
-    src.w1p = reinterpret_cast<const char *>(dn + (size_t)n1 * Ig) + cg * 16;
+    src.w0p = dn + (size_t)n0 * Ig * WB + cg * 16;
+    src.w1p = dn + (size_t)n1 * Ig * WB + cg * 16;
+  }
+  if (F8) {
+    o.sc0 = shared ? *a.ssc0 : a.sc0[g];
+    o.sc1 = GATE_UP ? (shared ? *a.ssc1 : a.sc1[g]) : o.sc0;
   }
   const T *act = static_cast<const T *>(a.act);
 #pragma unroll
@@ -81,7 +111,9 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
     int trow = o.row0 + m * 16 + r16;
     if (trow >= o.grp_end) trow = o.row0;
     const size_t arow = GATE_UP ? (size_t)a.sorted_token[trow] * a.H : (size_t)trow * a.ldh;
-    src.xp[m] = reinterpret_cast<const char *>(act + arow) + cg * 16;
+    // bf16 weights: chunk g of each 64-byte step; FP8: bytes [32g, 32g+32) of
+    // each 128-byte step of the token row (the K values of the lane's codes)
+    src.xp[m] = reinterpret_cast<const char *>(act + arow) + cg * (F8 ? 32 : 16);
   }
   return true;
 }
@@ -91,7 +123,7 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
 // of them is split into its two 16-row fragments for twice as many
 // wavefronts, so the last round costs half a unit.  Returns the item index
 // (kmax when there is none) and fills src / o.
-template <typename T, bool GATE_UP, int MT>
+template <typename T, bool GATE_UP, int MT, bool F8>
 __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int nw, int n_units,
                                          int n_col_blocks, int lane, UnitSrc<MT> &src,
                                          UnitOut &o) {
@@ -102,20 +134,21 @@ __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int 
     if (k < full || !split) {
       const int u = w + k * nw;
       if (u >= n_units) return kmax;
-      if (unit_of<T, GATE_UP, MT>(a, u, n_col_blocks, lane, src, o)) return k;
+      if (unit_of<T, GATE_UP, MT, F8>(a, u, n_col_blocks, lane, src, o)) return k;
     } else {
       if (w >= 2 * tail) return kmax;
-      if (unit_of<T, GATE_UP, MT>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
-                                  1 + (w & 1)))
+      if (unit_of<T, GATE_UP, MT, F8>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
+                                      1 + (w & 1)))
         return k;
     }
   }
   return kmax;
 }
 
-template <typename T, bool GATE_UP, int MT>
+template <typename T, bool GATE_UP, int MT, bool F8>
 __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut &o,
                                               f32x4_t (&acc)[2][MT], int lane) {
+  const float s0 = F8 ? o.sc0 : 1.0f, s1 = F8 ? o.sc1 : 1.0f;
   const int r16 = lane & 15, cg = lane >> 4;
   // Lane holds D[col 4cg + q][token row 16m + r16].
   T *out = static_cast<T *>(a.out);
@@ -124,7 +157,7 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
     const int trow = o.row0 + m * 16 + r16;
     if (trow >= o.grp_end) continue;
     if (GATE_UP) {
-      const f32x4_t gv = acc[0][m], uv = acc[1][m];
+      const f32x4_t gv = acc[0][m] * s0, uv = acc[1][m] * s1;
       store4(out + (size_t)trow * a.ldh + o.col0 + 4 * cg, swiglu(gv[0], uv[0]),
              swiglu(gv[1], uv[1]), swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
     } else {
@@ -132,17 +165,18 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
       for (int f = 0; f < 2; ++f) {
         const int n = o.col0 + f * 16 + 4 * cg;
         if (f >= o.nf || n >= a.H) continue;
-        const f32x4_t v = acc[f][m];
+        const f32x4_t v = acc[f][m] * (f ? s1 : s0);
         store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
       }
     }
   }
 }
 
-template <typename T, bool GATE_UP, int MT>
+template <typename T, bool GATE_UP, int MT, bool F8>
 __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(ExpertArgs a,
                                                                           int n_col_blocks) {
-  constexpr int U = UBASE / MT;   // 64-byte K steps per row per register set (one block)
+  constexpr int U = steps_per_set<MT, F8>();   // 64-byte K steps per row per register set
+  constexpr int XN = F8 ? 2 : 1;               // 16-byte token chunks per step
   const int lane = threadIdx.x & 63;
   // The wavefront index is uniform; readfirstlane makes that visible to the
   // compiler, so every unit-dependent guard below is a scalar branch.  (An
@@ -156,7 +190,7 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   // units of one expert spread over all XCDs and HBM channels.
   UnitSrc<MT> src;    // item whose blocks are being loaded
   UnitOut om, ol;     // item being multiplied, item being loaded
-  int k_ld = next_item<T, GATE_UP, MT>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
+  int k_ld = next_item<T, GATE_UP, MT, F8>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
   if (k_ld >= kmax) return;
   int k_mm = k_ld;
   om = ol;
@@ -168,24 +202,26 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 aw0[U], aw1[U], ax[U][MT];
-  uint4 bw0[U], bw1[U], bx[U][MT];
+  uint4 aw0[U], aw1[U], ax[U][MT][XN];
+  uint4 bw0[U], bw1[U], bx[U][MT][XN];
   // Load the next block of the loading unit into set W0/W1/X, then move the
   // loading position on (to the next unit at the end of this one).  Steps past
   // nsub re-read the last step (in bounds) and are not used.
 #define HY3_LOAD(W0, W1, X)                                                            \
   {                                                                                    \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
-      const int o_ = (s_ld + u < src.nsub ? s_ld + u : src.nsub - 1) * 64;             \
+      const int st_ = s_ld + u < src.nsub ? s_ld + u : src.nsub - 1;                  \
+      const int o_ = st_ * 64;                                                         \
       W0[u] = *reinterpret_cast<const uint4 *>(src.w0p + o_);                          \
       if (src.nf == 2) W1[u] = *reinterpret_cast<const uint4 *>(src.w1p + o_);         \
       _Pragma("unroll") for (int m = 0; m < MT; ++m)                                   \
-          X[u][m] = *reinterpret_cast<const uint4 *>(src.xp[m] + o_);                  \
+        _Pragma("unroll") for (int h = 0; h < XN; ++h)                                 \
+          X[u][m][h] = *reinterpret_cast<const uint4 *>(src.xp[m] + st_ * 64 * XN + h * 16); \
     }                                                                                  \
     s_ld += U;                                                                         \
     if (s_ld >= src.nsub) {                                                            \
-      k_ld = next_item<T, GATE_UP, MT>(a, k_ld + 1, w, nw, n_units, n_col_blocks, lane, \
-                                       src, ol);                                       \
+      k_ld = next_item<T, GATE_UP, MT, F8>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
+                                           lane, src, ol);                             \
       s_ld = 0;                                                                        \
     }                                                                                  \
   }
@@ -195,19 +231,33 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   {                                                                                    \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       if (s_mm + u < om.nsub) {                                                        \
-        _Pragma("unroll") for (int m = 0; m < MT; ++m) {                               \
-          Mma<T>::step(acc[0][m], W0[u], X[u][m]);                                     \
-          if (om.nf == 2) Mma<T>::step(acc[1][m], W1[u], X[u][m]);                     \
+        if constexpr (F8) {                                                            \
+          uint4 l0_, h0_, l1_, h1_;                                                    \
+          e4m3x16_to_bf16(W0[u], l0_, h0_);                                            \
+          if (om.nf == 2) e4m3x16_to_bf16(W1[u], l1_, h1_);                            \
+          _Pragma("unroll") for (int m = 0; m < MT; ++m) {                             \
+            Mma<T>::step(acc[0][m], l0_, X[u][m][0]);                                  \
+            Mma<T>::step(acc[0][m], h0_, X[u][m][XN - 1]);                             \
+            if (om.nf == 2) {                                                          \
+              Mma<T>::step(acc[1][m], l1_, X[u][m][0]);                                \
+              Mma<T>::step(acc[1][m], h1_, X[u][m][XN - 1]);                           \
+            }                                                                          \
+          }                                                                            \
+        } else {                                                                       \
+          _Pragma("unroll") for (int m = 0; m < MT; ++m) {                             \
+            Mma<T>::step(acc[0][m], W0[u], X[u][m][0]);                                \
+            if (om.nf == 2) Mma<T>::step(acc[1][m], W1[u], X[u][m][0]);                \
+          }                                                                            \
         }                                                                              \
       }                                                                                \
     }                                                                                  \
     s_mm += U;                                                                         \
     if (s_mm >= om.nsub) {                                                             \
-      unit_epilogue<T, GATE_UP, MT>(a, om, acc, lane);                                 \
+      unit_epilogue<T, GATE_UP, MT, F8>(a, om, acc, lane);                             \
       _Pragma("unroll") for (int f = 0; f < 2; ++f)                                    \
         _Pragma("unroll") for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; \
-      k_mm = next_item<T, GATE_UP, MT>(a, k_mm + 1, w, nw, n_units, n_col_blocks, lane, \
-                                       src_dummy, om);                                 \
+      k_mm = next_item<T, GATE_UP, MT, F8>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
+                                           lane, src_dummy, om);                       \
       s_mm = 0;                                                                        \
       more = k_mm < kmax;                                                              \
     }                                                                                  \
@@ -231,26 +281,26 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
 // Persistent grid: WAVES_PER_SIMD wavefronts per SIMD on the 256 CUs.
 constexpr int STREAM_BLOCKS = 256 * WAVES_PER_SIMD;
 
-template <typename T, int MT>
+template <typename T, int MT, bool F8>
 hipError_t launch_skinny_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int ncb = (Imax + 15) / 16;
-    hipLaunchKernelGGL((expert_stream_kernel<T, true, MT>), dim3(STREAM_BLOCKS), dim3(256), 0,
-                       stream, a, ncb);
+    hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, F8>), dim3(STREAM_BLOCKS), dim3(256),
+                       0, stream, a, ncb);
   } else {
     const int ncb = (a.H + 31) / 32;
-    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT>), dim3(STREAM_BLOCKS), dim3(256), 0,
-                       stream, a, ncb);
+    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, F8>), dim3(STREAM_BLOCKS), dim3(256),
+                       0, stream, a, ncb);
   }
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool F8>
 hipError_t launch_skinny(const ExpertArgs &a, bool gate_up, int T_tokens, hipStream_t stream) {
-  if (T_tokens <= 16) return launch_skinny_t<T, 1>(a, gate_up, stream);
-  if (T_tokens <= 32) return launch_skinny_t<T, 2>(a, gate_up, stream);
-  return launch_skinny_t<T, 4>(a, gate_up, stream);
+  if (T_tokens <= 16) return launch_skinny_t<T, 1, F8>(a, gate_up, stream);
+  if (T_tokens <= 32) return launch_skinny_t<T, 2, F8>(a, gate_up, stream);
+  return launch_skinny_t<T, 4, F8>(a, gate_up, stream);
 }
 
 }  // namespace
@@ -264,16 +314,18 @@ hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream);
 
 hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
   if (path == PATH_SKINNY)
-    return dtype == DT_F32 ? launch_skinny<float>(a, true, T, stream)
-                           : launch_skinny<bf16_t>(a, true, T, stream);
+    return dtype == DT_F32 ? launch_skinny<float, false>(a, true, T, stream)
+           : a.w_fp8       ? launch_skinny<bf16_t, true>(a, true, T, stream)
+                           : launch_skinny<bf16_t, false>(a, true, T, stream);
   if (path == PATH_BIG) return launch_big_gate_up(a, dtype, stream);
   return launch_tiled_gate_up(a, dtype, stream);
 }
 
 hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
   if (path == PATH_SKINNY)
-    return dtype == DT_F32 ? launch_skinny<float>(a, false, T, stream)
-                           : launch_skinny<bf16_t>(a, false, T, stream);
+    return dtype == DT_F32 ? launch_skinny<float, false>(a, false, T, stream)
+           : a.w_fp8       ? launch_skinny<bf16_t, true>(a, false, T, stream)
+                           : launch_skinny<bf16_t, false>(a, false, T, stream);
   if (path == PATH_BIG) return launch_big_down(a, dtype, stream);
   return launch_tiled_down(a, dtype, stream);
 }

@@ -25,6 +25,8 @@ def upload_weights(inp: MoEInputs, device) -> Dict[str, object]:
     """Router weight, expert bias (if any), stacked routed experts and the shared expert."""
     import torch
     c = inp.cfg
+    if c.w_format == "fp8_e4m3":
+        return _upload_fp8(inp, device)
     wg, wu, wd = inp.stacked_experts()
     d = {"w_router": torch.from_numpy(inp.w_router()).to(device),
          "w_gate": to_torch(wg, c.dtype, device), "w_up": to_torch(wu, c.dtype, device),
@@ -46,3 +48,26 @@ def with_bias_of(inp: MoEInputs, weights: Dict[str, object], device) -> Dict[str
     b = inp.bias()
     w["expert_bias"] = None if b is None else torch.from_numpy(b).to(device)
     return w
+
+
+def _upload_fp8(inp: MoEInputs, device) -> Dict[str, object]:
+    """FP8 E4M3 expert codes (uint8) with their float32 scales."""
+    import torch
+    c = inp.cfg
+    wg, wu, wd, sc = inp.stacked_experts_fp8()
+    d = {"w_router": torch.from_numpy(inp.w_router()).to(device),
+         "w_gate": torch.from_numpy(wg).to(device), "w_up": torch.from_numpy(wu).to(device),
+         "w_down": torch.from_numpy(wd).to(device),
+         "w_gate_scale": torch.from_numpy(np.ascontiguousarray(sc[0])).to(device),
+         "w_up_scale": torch.from_numpy(np.ascontiguousarray(sc[1])).to(device),
+         "w_down_scale": torch.from_numpy(np.ascontiguousarray(sc[2])).to(device)}
+    del wg, wu, wd
+    b = inp.bias()
+    if b is not None:
+        d["expert_bias"] = torch.from_numpy(b).to(device)
+    sh = inp.shared_fp8()
+    if sh is not None:
+        codes, scales = sh
+        d["ws_gate"], d["ws_up"], d["ws_down"] = (torch.from_numpy(q).to(device) for q in codes)
+        d["ws_scale"] = torch.from_numpy(np.array(scales, dtype=np.float32)).to(device)
+    return d

@@ -242,6 +242,8 @@ class MoEInputs:
     def expert(self, e: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
         """(gate [I,H], up [I,H], down [H,I]) of routed expert ``e``, stored dtype."""
         c = self.cfg
+        if c.w_format != "dtype":
+            raise ValueError("FP8 expert weights: use expert_fp8()")
         mk = c.model_key
         g = _normal_f32(_rng(self.seed, mk, T_GATE, e), (c.I, c.H), 1.0 / np.sqrt(c.H))
         u = _normal_f32(_rng(self.seed, mk, T_UP, e), (c.I, c.H), 1.0 / np.sqrt(c.H))
@@ -252,6 +254,8 @@ class MoEInputs:
         c = self.cfg
         if c.I_shared == 0:
             return None
+        if c.w_format != "dtype":
+            raise ValueError("FP8 expert weights: use shared_fp8()")
         k = ("shared",)
         if k not in self._cache:
             mk, Is = c.model_key, c.I_shared
@@ -343,9 +347,10 @@ def make_inputs(cfg_id: int, seed: int = 0, T: Optional[int] = None) -> MoEInput
 def random_small(seed: int, T: int, H: int, E: int, K: int, I: int, I_shared: int,
                  dtype: str = "f32", route_mode: int = ROUTE_SIGMOID_BIAS,
                  scale: float = HY3_SCALE, renorm_eps: float = 0.0,
-                 bias_kind: str = "uniform") -> MoEInputs:
+                 bias_kind: str = "uniform", w_format: str = "dtype") -> MoEInputs:
     """A small ad-hoc workload with the same distributions (for property tests)."""
     cfg = MoEConfig(f"small_{seed}", 900 + (seed % 97), 900 + seed, T=T, H=H, E=E, K=K,
                     I=I, I_shared=I_shared, dtype=dtype, route_mode=route_mode,
-                    scale=scale, renorm_eps=renorm_eps, bias_kind=bias_kind)
+                    scale=scale, renorm_eps=renorm_eps, bias_kind=bias_kind,
+                    w_format=w_format)
     return MoEInputs(cfg, seed)

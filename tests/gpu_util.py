@@ -43,7 +43,8 @@ from synth.device import to_torch, upload_weights, with_bias_of  # noqa: E402,F4
 def config_of(inp: MoEInputs, **kw) -> sm.hy3moe_config:
     c = inp.cfg
     d = dict(T=c.T, H=c.H, E=c.E, K=c.K, I=c.I, I_shared=c.I_shared, dtype=c.dtype,
-             route_mode=c.route_mode, scale=c.scale, renorm_eps=c.renorm_eps)
+             route_mode=c.route_mode, scale=c.scale, renorm_eps=c.renorm_eps,
+             w_format=c.w_format)
     d.update(kw)
     return sm.make_config(**d)
 
@@ -90,19 +91,36 @@ def check_output(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "",
     tmax, trel = TOL[dtype]
     if dtype == "bf16" and not workload_shape and ref.size:
         tmax = max(tmax, 2.0 ** -6 * float(np.abs(ref).max()))
-    log(f"  {what} max_abs={mx:.3e} rel_l2={rel:.3e} (tol {tmax:g}/{trel:g})")
+    top = float(np.abs(ref).max()) if ref.size else 0.0
+    log(f"  {what} max_abs={mx:.3e} rel_l2={rel:.3e} (tol {tmax:g}/{trel:g}; max|ref| {top:.3g})")
     assert mx <= tmax and rel <= trel, f"{what}: max_abs {mx:.3e} rel_l2 {rel:.3e}"
     return mx, rel
 
 
 def expert_cache(inp: MoEInputs):
+    """expert(e) -> float64 (gate, up, down); FP8 weights dequantised by the oracle."""
     cache = {}
+    fp8 = inp.cfg.w_format == "fp8_e4m3"
 
     def f(e):
         if e not in cache:
-            cache[e] = inp.expert_f64(e)
+            if fp8:
+                codes, sc = inp.expert_fp8(e)
+                cache[e] = tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))
+            else:
+                cache[e] = inp.expert_f64(e)
         return cache[e]
     return f
+
+
+def shared_f64(inp: MoEInputs):
+    """float64 (gate, up, down) of the shared expert, or None."""
+    if inp.cfg.w_format != "fp8_e4m3":
+        return inp.shared_f64()
+    sh = inp.shared_fp8()
+    if sh is None:
+        return None
+    return tuple(oracle.dequant_fp8(q, s) for q, s in zip(*sh))
 
 
 def out_to_np(out: torch.Tensor) -> np.ndarray:

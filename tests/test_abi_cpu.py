@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 2
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 3
     for code in (0, -1, -2, -3, -4, -5):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -51,7 +51,8 @@ def test_abi_version_and_strerror(lib):
 
 def cfg_of(c, **kw):
     d = dict(T=c.T, H=c.H, E=c.E, K=c.K, I=c.I, I_shared=c.I_shared, dtype=c.dtype,
-             route_mode=c.route_mode, scale=c.scale, renorm_eps=c.renorm_eps)
+             route_mode=c.route_mode, scale=c.scale, renorm_eps=c.renorm_eps,
+             w_format=c.w_format)
     d.update(kw)
     return sm.make_config(**d)
 
@@ -85,6 +86,8 @@ def test_workspace_layout_is_consistent(lib, cfg_id):
     (dict(H=100), -2), (dict(I=96), -2), (dict(I_shared=32), -2), (dict(K=65, E=100), -1),
     (dict(dtype="f32", router_prec=1), -2), (dict(route_mode=3), -1),
     (dict(T=1 << 19), -2), (dict(H=65536, I=32768, I_shared=0), -2),
+    # FP8 expert weights: bf16 activations and weight-streaming batches only
+    (dict(w_format="fp8_e4m3", T=65), -2), (dict(w_format="fp8_e4m3", dtype="f32"), -2),
 ])
 def test_invalid_configs_rejected(lib, bad, code):
     c = CONFIGS[1]
@@ -141,3 +144,34 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(b, "_LIB", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         b.load()
+
+
+def test_weight_format_enum_is_checked(lib):
+    cfg = cfg_of(CONFIGS[5])
+    assert sm.hy3moe_workspace_bytes(cfg, True) > 0
+    cfg.w_format = 2
+    assert sm.hy3moe_workspace_bytes(cfg, True) == 0
+    L = b.hy3moe_ws_layout()
+    assert lib.hy3moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == -1
+
+
+def test_fp8_weights_need_their_scales(lib):
+    cfg = cfg_of(CONFIGS[5])
+    need = sm.hy3moe_workspace_bytes(cfg, True)
+    fw = lib.hy3moe_forward
+    ok = b.hy3moe_weights(*([4096] * 12))
+    missing = b.hy3moe_weights(*([4096] * 11 + [None]))        # no shared scales
+    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(missing), 8192, None, None, 4096, need,
+              None) == -1
+    nosc = b.hy3moe_weights(*([4096] * 8))                      # no scales at all
+    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(nosc), 8192, None, None, 4096, need,
+              None) == -1
+    mis = b.hy3moe_weights(*([4096] * 9 + [4098, 4096, 4096]))  # scale not 4-byte aligned
+    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(mis), 8192, None, None, 4096, need,
+              None) == -4
+    # the same weights without shared expert do not need the shared scales
+    cfg_ns = cfg_of(CONFIGS[5], I_shared=0)
+    need_ns = sm.hy3moe_workspace_bytes(cfg_ns, True)
+    assert fw(ctypes.byref(cfg_ns), 4096, ctypes.byref(missing), 8192, None, None, 4096,
+              need_ns - 1, None) == -3
+    del ok

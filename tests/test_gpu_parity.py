@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (MARGIN, check_output, check_route, config_of, log, oracle_route,
-                      out_to_np, to_torch, upload_weights)
+from gpu_util import (MARGIN, check_output, check_route, config_of, expert_cache, log,
+                      oracle_route, out_to_np, shared_f64, to_torch, upload_weights)
 from synth import CONFIGS, MoEInputs, random_small
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +38,7 @@ def reference(inp, r, gidx, gw, tokens=None):
     w[tie] = gw[tie].astype(np.float64)
     if tokens is not None:
         x64, idx, w = x64[tokens], idx[tokens], w[tokens]
-    return oracle.forward_given_route(x64, idx, w, inp.expert_f64, c.E, inp.shared_f64())
+    return oracle.forward_given_route(x64, idx, w, expert_cache(inp), c.E, shared_f64(inp))
 
 
 def run_gpu(inp, dev, weights=None, workspace=None):
@@ -92,6 +92,19 @@ SMALL = {
     "big_T300_f32": dict(seed=19, T=300, H=256, E=2, K=2, I=128, I_shared=192, dtype="f32"),
     "big_softmax_T600": dict(seed=20, T=600, H=256, E=8, K=3, I=128, I_shared=128, dtype="bf16",
                              route_mode=1, scale=1.0, renorm_eps=1e-8, bias_kind="none"),
+    # FP8 E4M3 expert weights (weight-streaming path; 1, 2 and 4 row fragments;
+    # ragged K blocks; no shared expert; softmax routing)
+    "fp8_T1": dict(seed=30, T=1, H=512, E=32, K=8, I=256, I_shared=256, dtype="bf16",
+                   w_format="fp8_e4m3"),
+    "fp8_T16": dict(seed=31, T=16, H=512, E=32, K=8, I=256, I_shared=256, dtype="bf16",
+                    w_format="fp8_e4m3"),
+    "fp8_T20_noshared": dict(seed=32, T=20, H=512, E=24, K=6, I=192, I_shared=0,
+                             dtype="bf16", w_format="fp8_e4m3"),
+    "fp8_T40_H320": dict(seed=33, T=40, H=320, E=12, K=3, I=320, I_shared=64, dtype="bf16",
+                         w_format="fp8_e4m3"),
+    "fp8_T64_softmax": dict(seed=34, T=64, H=256, E=16, K=4, I=128, I_shared=128,
+                            dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
+                            bias_kind="none", w_format="fp8_e4m3"),
 }
 
 
