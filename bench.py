@@ -9,7 +9,8 @@ Default workload: Hy3 decode, T=16 tokens, H=4096, 192 routed experts
 (top-8) + 1 shared expert, I=1536, bf16 weights/activations, fp32 router.
 `--workload prefill` (T=8192, skewed bias) and `--workload softmax`
 (HunyuanImage-3.0 softmax routing, T=32768, E=64) run the other layer shapes;
-`--workload decode_fp8` is the decode shape with FP8 E4M3 expert weights.
+`--workload decode_fp8` / `prefill_fp8` are the decode and prefill shapes with
+FP8 E4M3 expert weights.
 
 Printed: one JSON line with tokens/s, the dominant kernel's roofline fraction
 (its per-launch duration measured live with HIP events on the library's
@@ -29,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4, "decode_fp8": 5}
+WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4, "decode_fp8": 5, "prefill_fp8": 6}
 ROUTER_WORKLOAD = 3            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published

@@ -52,7 +52,7 @@ extern "C" {
 #define HY3MOE_ERR_UNSUPPORTED -2  /* H, I or I_shared not a multiple of 64; T > 2^24;
                                       H, I or I_shared > 65536; T*H or H*max(I, I_shared)
                                       elements of 4 GiB or more; split router with fp32 x;
-                                      FP8 expert weights with fp32 x or with T > 64   */
+                                      FP8 expert weights with fp32 x                  */
 #define HY3MOE_ERR_WORKSPACE   -3  /* workspace smaller than hy3moe_workspace_bytes()   */
 #define HY3MOE_ERR_ALIGN       -4  /* a pointer is not 16-byte aligned                  */
 #define HY3MOE_ERR_HIP         -5  /* a kernel launch failed (hipGetLastError)          */
@@ -81,8 +81,9 @@ extern "C" {
  * deployment article, section 8.2, with tensor-wise scales).  Activations
  * stay bfloat16 (x and out bf16, cfg.dtype must be HY3MOE_BF16); the expert
  * GEMMs decode the codes exactly to bfloat16 and apply the scale to the
- * float32 accumulators.  Supported for the weight-streaming batches
- * (T <= 64), where the weight bytes set the time. */
+ * float32 accumulators.  All three GEMM paths take FP8 weights: the
+ * weight-streaming one (T <= 64), where the weight bytes set the time, and
+ * the tile paths, which decode each chunk on its way into LDS. */
 #define HY3MOE_WFMT_DTYPE    0
 #define HY3MOE_WFMT_FP8_E4M3 1
 

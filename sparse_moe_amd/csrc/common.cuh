@@ -79,6 +79,23 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c, floa
   *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
 }
 
+// OCP FP8 E4M3 bytes -> bf16, exact (every E4M3 value is a bf16 value).  The
+// gfx950 scaled conversion with scale 1 decodes two bytes per instruction,
+// low bytes first.
+#define HY3_E4M3_PAIR(w, h) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((w), 1.0f, (h)))
+// 8 codes (bytes 0..7 of q) -> 8 bf16.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(const uint2 &q) {
+  return make_uint4(HY3_E4M3_PAIR(q.x, false), HY3_E4M3_PAIR(q.x, true),
+                    HY3_E4M3_PAIR(q.y, false), HY3_E4M3_PAIR(q.y, true));
+}
+// 16 codes -> two fragments of 8 bf16 (bytes 0-7, bytes 8-15).
+__device__ __forceinline__ void e4m3x16_to_bf16(const uint4 &q, uint4 &lo, uint4 &hi) {
+  lo = e4m3x8_to_bf16(make_uint2(q.x, q.y));
+  hi = e4m3x8_to_bf16(make_uint2(q.z, q.w));
+}
+#undef HY3_E4M3_PAIR
+
 // SiLU(g) * u in fp32: g / (1 + e^-g) * u.
 __device__ __forceinline__ float swiglu(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;

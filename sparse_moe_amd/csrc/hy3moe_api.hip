@@ -41,8 +41,8 @@ int validate_cfg(const hy3moe_config *c) {
     return HY3MOE_ERR_UNSUPPORTED;
   if (c->w_format != HY3MOE_WFMT_DTYPE && c->w_format != HY3MOE_WFMT_FP8_E4M3)
     return HY3MOE_ERR_INVALID;
-  // FP8 expert weights: bf16 activations, weight-streaming batches only.
-  if (c->w_format == HY3MOE_WFMT_FP8_E4M3 && (c->dtype != HY3MOE_BF16 || c->T > SKINNY_MAX_T))
+  // FP8 expert weights need bf16 activations.
+  if (c->w_format == HY3MOE_WFMT_FP8_E4M3 && c->dtype != HY3MOE_BF16)
     return HY3MOE_ERR_UNSUPPORTED;
   // The expert GEMMs address x and every expert matrix with 32-bit offsets.
   const uint64_t eb = c->dtype == HY3MOE_F32 ? 4 : 2, lim = uint64_t(1) << 32;

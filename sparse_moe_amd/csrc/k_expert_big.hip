@@ -27,6 +27,12 @@
 //    in its L2.  The next tile's first two K stages are loaded while the
 //    finished tile's epilogue runs.
 // Group E is the shared expert (its own weights and width I_shared).
+//
+// FP8 E4M3 weights (F8): a thread loads the 8 code bytes of its weight chunk,
+// decodes them exactly to 8 bf16 when it writes the chunk to LDS, and the
+// per-matrix scale multiplies the accumulators in the epilogue.
+#include <type_traits>
+
 #include "common.cuh"
 #include "internal.h"
 
@@ -99,34 +105,34 @@ __device__ __forceinline__ bool big_tile_at(const ExpertArgs &a, int n_tiles, in
 // block of 64 rows [64q, 64q+64) holds gate cols col0 + 32q + [0, 32) and then
 // the up cols of the same columns, so lr < 32 loads gate rows, lr >= 32 up rows.
 // Global addresses: a base pointer plus 32-bit offsets (every matrix < 4 GiB).
-template <typename T, bool GATE_UP>
+template <typename T, bool GATE_UP, bool F8>
 __device__ __forceinline__ void big_tile_loads(const ExpertArgs &a, const BigTile &t, int lr,
                                                int lc, const char *&wb, const char *&xb,
                                                uint32_t *woff, uint32_t *xoff) {
   constexpr int EB = Elem<T>::kBytes;
+  constexpr int WB = F8 ? 1 : EB;              // bytes per weight element
+  constexpr int WCH = F8 ? 8 : 16;             // weight bytes per 16-byte LDS chunk
   const bool shared = (t.g == a.E);
-  const T *mat;
   if (GATE_UP) {
     const bool up = lr >= 32;
-    mat = shared ? static_cast<const T *>(up ? a.ws1 : a.ws0)
-                 : static_cast<const T *>(up ? a.w1 : a.w0) + (size_t)t.g * a.I * a.H;
+    wb = shared ? static_cast<const char *>(up ? a.ws1 : a.ws0)
+                : static_cast<const char *>(up ? a.w1 : a.w0) + (size_t)t.g * a.I * a.H * WB;
     xb = static_cast<const char *>(a.act);
   } else {
-    mat = shared ? static_cast<const T *>(a.ws0)
-                 : static_cast<const T *>(a.w0) + (size_t)t.g * a.H * a.I;
+    wb = shared ? static_cast<const char *>(a.ws0)
+                : static_cast<const char *>(a.w0) + (size_t)t.g * a.H * a.I * WB;
     xb = static_cast<const char *>(a.act) + (size_t)t.row0 * a.ldh * EB;
   }
-  wb = reinterpret_cast<const char *>(mat);
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = p * 64 + lr;
     if (GATE_UP) {
       int wrow = t.col0 + p * 32 + (lr & 31);
       if (wrow >= t.Ig) wrow = t.col0;         // column tail (Ig % 128 == 64)
-      woff[p] = (uint32_t)wrow * (uint32_t)(a.H * EB) + lc * 16;
+      woff[p] = (uint32_t)wrow * (uint32_t)(a.H * WB) + lc * WCH;
     } else {
       const int wrow = (t.col0 + r < a.H) ? t.col0 + r : t.col0;
-      woff[p] = (uint32_t)wrow * (uint32_t)(t.Ig * EB) + lc * 16;
+      woff[p] = (uint32_t)wrow * (uint32_t)(t.Ig * WB) + lc * WCH;
     }
     int trow = t.row0 + r;
     if (trow >= t.grp_end) trow = t.row0;      // ragged tail: reload a valid row
@@ -137,9 +143,16 @@ __device__ __forceinline__ void big_tile_loads(const ExpertArgs &a, const BigTil
 
 // Epilogue of a tile: lane holds D[weight row 16i + 4cg + q][token row 16j + r16]
 // of wavefront (wr_, wt_).  tid is the thread index.
-template <typename T, bool GATE_UP>
+template <typename T, bool GATE_UP, bool F8>
 __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile &t,
                                              const f32x4_t (&acc)[8][4], uint4 *lds, int tid) {
+  // FP8: scale of the gate (or down) matrix and of the up matrix
+  float s0 = 1.0f, s1 = 1.0f;
+  if (F8) {
+    const bool shared = (t.g == a.E);
+    s0 = shared ? *a.ssc0 : a.sc0[t.g];
+    if (GATE_UP) s1 = shared ? *a.ssc1 : a.sc1[t.g];
+  }
   const int lane = tid & 63, wave = tid >> 6;
   const int wr_ = wave >> 2, wt_ = wave & 3, r16 = lane & 15, cg = lane >> 4;
   T *out = static_cast<T *>(a.out);
@@ -162,7 +175,7 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
         for (int i = 0; i < 4; ++i) {
           const int gi = (i >> 1) * 4 + (i & 1);
           const int c = wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
-          const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
+          const f32x4_t gv = acc[gi][j] * s0, uv = acc[gi + 2][j] * s1;
           uint2 v;
           v.x = pack_bf16x2(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]));
           v.y = pack_bf16x2(swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
@@ -172,7 +185,7 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int c = wr_ * 128 + i * 16 + 4 * cg;
-          const f32x4_t v4 = acc[i][j];
+          const f32x4_t v4 = acc[i][j] * s0;
           uint2 v;
           v.x = pack_bf16x2(v4[0], v4[1]);
           v.y = pack_bf16x2(v4[2], v4[3]);
@@ -209,7 +222,7 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
           const int gi = (i >> 1) * 4 + (i & 1);
           const int c = t.col0 + wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
           if (c >= t.Ig) continue;
-          const f32x4_t gv = acc[gi][j], uv = acc[gi + 2][j];
+          const f32x4_t gv = acc[gi][j] * s0, uv = acc[gi + 2][j] * s1;
           store4(out + (size_t)trow * a.ldh + c, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
                  swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
         }
@@ -218,7 +231,7 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
         for (int i = 0; i < 8; ++i) {
           const int n = t.col0 + wr_ * 128 + i * 16 + 4 * cg;
           if (n >= a.H) continue;
-          const f32x4_t v = acc[i][j];
+          const f32x4_t v = acc[i][j] * s0;
           store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
         }
       }
@@ -226,7 +239,11 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
   }
 }
 
-template <typename T, bool GATE_UP>
+// LDS form of a staged weight chunk: as loaded, or decoded from E4M3 codes.
+__device__ __forceinline__ uint4 weight_chunk(const uint4 &v) { return v; }
+__device__ __forceinline__ uint4 weight_chunk(const uint2 &q) { return e4m3x8_to_bf16(q); }
+
+template <typename T, bool GATE_UP, bool F8>
 __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_col_tiles) {
   __shared__ uint4 lds[2 * ROWS * CH];   // 2 x 64 KB
 
@@ -246,7 +263,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
   const int lr = tid >> 3, lc = tid & 7;
   const char *wb, *xb;
   uint32_t woff[4], xoff[4];
-  big_tile_loads<T, GATE_UP>(a, cur, lr, lc, wb, xb, woff, xoff);
+  big_tile_loads<T, GATE_UP, F8>(a, cur, lr, lc, wb, xb, woff, xoff);
 
   const int wr_ = wave >> 2, wt_ = wave & 3;
   const int r16 = lane & 15, cg = lane >> 4;
@@ -260,15 +277,19 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
   // Two register stage sets: stage s is loaded into set s % 2 at the start of
   // iteration s - 2 and written to LDS at the end of iteration s - 1, so the
   // global latency is covered by two iterations of MFMA work.
-  uint4 aw0, aw1, aw2, aw3, ax0, ax1, ax2, ax3;   // set 0
-  uint4 bw0, bw1, bw2, bw3, bx0, bx1, bx2, bx3;   // set 1
+  // Weight chunks: 16 bytes, or the 8 E4M3 code bytes of 8 weights (FP8).
+  typedef typename std::conditional<F8, uint2, uint4>::type wchunk_t;
+  wchunk_t aw0, aw1, aw2, aw3, bw0, bw1, bw2, bw3;
+  uint4 ax0, ax1, ax2, ax3;   // set 0
+  uint4 bx0, bx1, bx2, bx3;   // set 1
 #define HY3_GLOAD(S, kst)                                                              \
   {                                                                                    \
     const uint32_t kb_ = (uint32_t)(kst) * RB;                                         \
-    S##w0 = *reinterpret_cast<const uint4 *>(wb + (kb_ + woff[0]));                    \
-    S##w1 = *reinterpret_cast<const uint4 *>(wb + (kb_ + woff[1]));                    \
-    S##w2 = *reinterpret_cast<const uint4 *>(wb + (kb_ + woff[2]));                    \
-    S##w3 = *reinterpret_cast<const uint4 *>(wb + (kb_ + woff[3]));                    \
+    const uint32_t kw_ = F8 ? kb_ / 2 : kb_;   /* FP8 weight rows: half the bytes */   \
+    S##w0 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[0]));                 \
+    S##w1 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[1]));                 \
+    S##w2 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[2]));                 \
+    S##w3 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[3]));                 \
     S##x0 = *reinterpret_cast<const uint4 *>(xb + (kb_ + xoff[0]));                    \
     S##x1 = *reinterpret_cast<const uint4 *>(xb + (kb_ + xoff[1]));                    \
     S##x2 = *reinterpret_cast<const uint4 *>(xb + (kb_ + xoff[2]));                    \
@@ -277,8 +298,8 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
 #define HY3_LSTORE(S, buf)                                                             \
   {                                                                                    \
     uint4 *d_ = lds + (buf) * ROWS * CH + wr_l;                                        \
-    d_[0 * 64 * CH] = S##w0; d_[1 * 64 * CH] = S##w1;                                  \
-    d_[2 * 64 * CH] = S##w2; d_[3 * 64 * CH] = S##w3;                                  \
+    d_[0 * 64 * CH] = weight_chunk(S##w0); d_[1 * 64 * CH] = weight_chunk(S##w1);      \
+    d_[2 * 64 * CH] = weight_chunk(S##w2); d_[3 * 64 * CH] = weight_chunk(S##w3);      \
     d_[(BW + 0 * 64) * CH] = S##x0; d_[(BW + 1 * 64) * CH] = S##x1;                    \
     d_[(BW + 2 * 64) * CH] = S##x2; d_[(BW + 3 * 64) * CH] = S##x3;                    \
   }
@@ -342,14 +363,14 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     if (has_next) {   // the finished tile's load descriptors are free
       int tid_n = tid;
       asm volatile("" : "+v"(tid_n));
-      big_tile_loads<T, GATE_UP>(a, nxt, tid_n >> 3, tid_n & 7, wb, xb, woff, xoff);
+      big_tile_loads<T, GATE_UP, F8>(a, nxt, tid_n >> 3, tid_n & 7, wb, xb, woff, xoff);
       HY3_GLOAD(a, 0);
       HY3_GLOAD(b, (1 < nxt.nk) ? 1 : 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     int tid_e = tid;
     asm volatile("" : "+v"(tid_e));
-    big_epilogue<T, GATE_UP>(a, cur, acc, lds, tid_e);
+    big_epilogue<T, GATE_UP, F8>(a, cur, acc, lds, tid_e);
     __builtin_amdgcn_sched_barrier(0);
     if (!has_next) break;
     __syncthreads();   // the epilogue's LDS reads are done
@@ -365,7 +386,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
 
 }
 
-template <typename T>
+template <typename T, bool F8>
 hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   int nct;
   if (gate_up) {
@@ -388,21 +409,23 @@ hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   const long want = (logical + 7) / 8 * 8;
   const dim3 grid((unsigned)(want < cap ? want : cap));
   if (gate_up)
-    hipLaunchKernelGGL((expert_big_kernel<T, true>), grid, dim3(512), 0, stream, a, nct);
+    hipLaunchKernelGGL((expert_big_kernel<T, true, F8>), grid, dim3(512), 0, stream, a, nct);
   else
-    hipLaunchKernelGGL((expert_big_kernel<T, false>), grid, dim3(512), 0, stream, a, nct);
+    hipLaunchKernelGGL((expert_big_kernel<T, false, F8>), grid, dim3(512), 0, stream, a, nct);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_big_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_big_t<float>(a, true, stream)
-                         : launch_big_t<bf16_t>(a, true, stream);
+  return dtype == DT_F32 ? launch_big_t<float, false>(a, true, stream)
+         : a.w_fp8       ? launch_big_t<bf16_t, true>(a, true, stream)
+                         : launch_big_t<bf16_t, false>(a, true, stream);
 }
 hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_big_t<float>(a, false, stream)
-                         : launch_big_t<bf16_t>(a, false, stream);
+  return dtype == DT_F32 ? launch_big_t<float, false>(a, false, stream)
+         : a.w_fp8       ? launch_big_t<bf16_t, true>(a, false, stream)
+                         : launch_big_t<bf16_t, false>(a, false, stream);
 }
 
 }  // namespace hy3moe

@@ -43,15 +43,6 @@ constexpr int steps_per_set() {
   return F8 ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1)) : UBASE / MT;
 }
 
-// 16 E4M3 bytes -> two fragments of 8 bf16 (bytes 0-7, bytes 8-15), exact.
-__device__ __forceinline__ void e4m3x16_to_bf16(const uint4 &q, uint4 &lo, uint4 &hi) {
-#define HY3_CV(w, h) \
-  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((w), 1.0f, (h)))
-  lo = make_uint4(HY3_CV(q.x, false), HY3_CV(q.x, true), HY3_CV(q.y, false), HY3_CV(q.y, true));
-  hi = make_uint4(HY3_CV(q.z, false), HY3_CV(q.z, true), HY3_CV(q.w, false), HY3_CV(q.w, true));
-#undef HY3_CV
-}
-
 // Where a unit's operands are (per lane) and what its epilogue needs.
 template <int MT>
 struct UnitSrc {

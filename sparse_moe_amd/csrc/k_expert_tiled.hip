@@ -19,6 +19,10 @@
 // 16 x 16).  The weight rows are the MFMA A operand and the token rows the B
 // operand, so each lane ends with 4 consecutive output columns of one row.
 // Group E is the shared expert (its own weight pointers and width I_shared).
+//
+// FP8 E4M3 weights (F8): each thread loads the 8 code bytes of its chunk,
+// decodes them exactly to 8 bf16 before the LDS write, and the per-matrix
+// scale multiplies the accumulators in the epilogue; the rest is unchanged.
 #include "common.cuh"
 #include "internal.h"
 
@@ -33,7 +37,7 @@ constexpr int CHUNKS = KB / 16;  // 8
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * CHUNKS + (chunk ^ (row & 7)); }
 
-template <typename T, bool GATE_UP>
+template <typename T, bool GATE_UP, bool F8>
 __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int n_col_tiles) {
   __shared__ uint4 lds[2][(BR + BT) * CHUNKS];   // 2 x 32 KB
 
@@ -51,6 +55,8 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
   const int Kdim = GATE_UP ? a.H : Ig;               // reduction length (elements)
   constexpr int EB = Elem<T>::kBytes;
   constexpr int EPC = Elem<T>::kPerChunk;
+  constexpr int WB = F8 ? 1 : EB;                    // bytes per weight element
+  constexpr int WCH = F8 ? 8 : 16;                   // weight bytes per 16-byte LDS chunk
 
   // Columns of this tile.
   const int col0 = ct * (GATE_UP ? TILED_GU_COLS : TILED_DN_COLS);
@@ -63,24 +69,22 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = p * 32 + lrow;   // LDS weight row 0..127
-    const T *base;
-    size_t wrow;
+    const char *base;
+    size_t wrow;                   // element offset of the weight row
     if (GATE_UP) {
       const int half = r >> 6, rr = r & 63;
       const bool up = rr >= 32;
       const int c = col0 + half * 32 + (rr & 31);
-      const T *mat = shared ? static_cast<const T *>(up ? a.ws1 : a.ws0)
-                            : static_cast<const T *>(up ? a.w1 : a.w0) + (size_t)g * a.I * a.H;
-      base = mat;
+      base = shared ? static_cast<const char *>(up ? a.ws1 : a.ws0)
+                    : static_cast<const char *>(up ? a.w1 : a.w0) + (size_t)g * a.I * a.H * WB;
       wrow = (size_t)c * a.H;
     } else {
-      const T *mat = shared ? static_cast<const T *>(a.ws0)
-                            : static_cast<const T *>(a.w0) + (size_t)g * a.H * a.I;
-      base = mat;
+      base = shared ? static_cast<const char *>(a.ws0)
+                    : static_cast<const char *>(a.w0) + (size_t)g * a.H * a.I * WB;
       const int n = (col0 + r < a.H) ? col0 + r : col0;   // column tail: reload a valid row
       wrow = (size_t)n * Ig;
     }
-    wptr[p] = reinterpret_cast<const char *>(base + wrow) + lch * 16;
+    wptr[p] = base + wrow * WB + lch * WCH;
 
     int trow = row0 + r;                       // expert-major row of this token slot
     if (trow >= grp_end) trow = row0;          // ragged tail: reload a valid row
@@ -92,15 +96,20 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
   }
 
   uint4 wreg[4], xreg[4];
+  uint2 wq[4];                     // FP8: the chunk's 8 code bytes
+  // kbyte: byte offset of the stage in a bf16 (or fp32) row; FP8 weight rows
+  // advance by half of it.
 #define HY3_GLOAD(kbyte)                                                   \
   _Pragma("unroll") for (int p = 0; p < 4; ++p) {                          \
-    wreg[p] = *reinterpret_cast<const uint4 *>(wptr[p] + (kbyte));         \
+    if constexpr (F8) wq[p] = *reinterpret_cast<const uint2 *>(wptr[p] + (kbyte) / 2); \
+    else wreg[p] = *reinterpret_cast<const uint4 *>(wptr[p] + (kbyte));    \
     xreg[p] = *reinterpret_cast<const uint4 *>(xptr[p] + (kbyte));         \
   }
 #define HY3_LSTORE(buf)                                                    \
   _Pragma("unroll") for (int p = 0; p < 4; ++p) {                          \
     const int r = p * 32 + lrow;                                           \
-    lds[buf][swz(r, lch)] = wreg[p];                                       \
+    if constexpr (F8) lds[buf][swz(r, lch)] = e4m3x8_to_bf16(wq[p]);       \
+    else lds[buf][swz(r, lch)] = wreg[p];                                  \
     lds[buf][BR * CHUNKS + swz(r, lch)] = xreg[p];                         \
   }
 
@@ -147,6 +156,12 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
 
   // ---- epilogue: lane holds D[weight row 16i + 4cg + q][token row 16j + r16] ----
   T *out = static_cast<T *>(a.out);
+  // FP8: scale of the gate (or down) matrix and of the up matrix
+  float s0 = 1.0f, s1 = 1.0f;
+  if (F8) {
+    s0 = shared ? *a.ssc0 : a.sc0[g];
+    if (GATE_UP) s1 = shared ? *a.ssc1 : a.sc1[g];
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int trow = row0 + wt_ * 64 + j * 16 + r16;
@@ -157,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
         // weight rows wr_*64 + 16i + .. are gate cols col0 + 32*wr_ + 16i + ..;
         // rows +32 are the matching up cols.
         const int c = col0 + wr_ * 32 + i * 16 + 4 * cg;
-        const f32x4_t gv = acc[i][j], uv = acc[i + 2][j];
+        const f32x4_t gv = acc[i][j] * s0, uv = acc[i + 2][j] * s1;
         store4(out + (size_t)trow * a.ldh + c, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
                swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
       }
@@ -166,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
       for (int i = 0; i < 4; ++i) {
         const int n = col0 + wr_ * 64 + i * 16 + 4 * cg;
         if (n >= a.H) continue;
-        const f32x4_t v = acc[i][j];
+        const f32x4_t v = acc[i][j] * s0;
         store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
       }
     }
@@ -175,28 +190,30 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
 
 }  // namespace
 
-template <typename T>
+template <typename T, bool F8>
 static hipError_t launch_tiled(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int nct = Imax / TILED_GU_COLS;
-    hipLaunchKernelGGL((expert_tiled_kernel<T, true>), dim3(a.max_tiles * nct), dim3(256), 0,
-                       stream, a, nct);
+    hipLaunchKernelGGL((expert_tiled_kernel<T, true, F8>), dim3(a.max_tiles * nct), dim3(256),
+                       0, stream, a, nct);
   } else {
     const int nct = (a.H + TILED_DN_COLS - 1) / TILED_DN_COLS;
-    hipLaunchKernelGGL((expert_tiled_kernel<T, false>), dim3(a.max_tiles * nct), dim3(256), 0,
-                       stream, a, nct);
+    hipLaunchKernelGGL((expert_tiled_kernel<T, false, F8>), dim3(a.max_tiles * nct), dim3(256),
+                       0, stream, a, nct);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_tiled_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_tiled<float>(a, true, stream)
-                         : launch_tiled<bf16_t>(a, true, stream);
+  return dtype == DT_F32 ? launch_tiled<float, false>(a, true, stream)
+         : a.w_fp8       ? launch_tiled<bf16_t, true>(a, true, stream)
+                         : launch_tiled<bf16_t, false>(a, true, stream);
 }
 hipError_t launch_tiled_down(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_tiled<float>(a, false, stream)
-                         : launch_tiled<bf16_t>(a, false, stream);
+  return dtype == DT_F32 ? launch_tiled<float, false>(a, false, stream)
+         : a.w_fp8       ? launch_tiled<bf16_t, true>(a, false, stream)
+                         : launch_tiled<bf16_t, false>(a, false, stream);
 }
 
 }  // namespace hy3moe

@@ -142,6 +142,11 @@ CONFIGS: Dict[int, MoEConfig] = {
                  I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform",
                  w_format="fp8_e4m3"),
+    # Hy3 prefill chunk with the same FP8 experts and a skewed bias.
+    6: MoEConfig("hy3_prefill_T8192_skew_fp8", 6, 5, T=8192, H=4096, E=192, K=8,
+                 I=1536, I_shared=1536, dtype="bf16",
+                 route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
+                 bias_kind="skew", w_format="fp8_e4m3"),
 }
 
 ROUTER_SWEEP_M = (2, 64, 512, 4096)

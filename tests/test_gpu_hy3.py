@@ -42,7 +42,7 @@ def hy3_weights(dev):
     torch.cuda.empty_cache()
 
 
-def sampled_check(inp, dev, weights, n_sample=256, seed=0):
+def sampled_check(inp, dev, weights, n_sample=256, seed=0, workload_shape=True):
     c = inp.cfg
     weights = with_bias_of(inp, weights, dev)
     cfg = config_of(inp)
@@ -64,7 +64,7 @@ def sampled_check(inp, dev, weights, n_sample=256, seed=0):
     rw[t_is_tie] = gw[tokens][t_is_tie]
     ref = oracle.forward_given_route(x64, ridx, rw, expert_cache(inp), c.E, shared_f64(inp))
     got = out_to_np(out)[tokens]
-    check_output(got, ref, c.dtype, c.name, workload_shape=True)
+    check_output(got, ref, c.dtype, c.name, workload_shape=workload_shape)
     counts = np.bincount(gidx.reshape(-1), minlength=c.E)
     log(f"  experts hit {int((counts > 0).sum())}/{c.E}, max load {counts.max()} "
         f"(mean {counts.mean():.1f})")
@@ -140,17 +140,29 @@ def test_softmax_long_prefill_T32768_sampled(dev):
         torch.cuda.empty_cache()
 
 
-def test_hy3_decode_T16_fp8_full(dev):
+@pytest.fixture(scope="module")
+def hy3_fp8_weights(dev):
+    inp = MoEInputs(CONFIGS[5])
+    log("generating and uploading FP8 Hy3 expert weights (192 x 18.9 MB)")
+    w = upload_weights(inp, dev)
+    torch.cuda.synchronize()
+    yield w
+    del w
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_hy3_decode_T16_fp8_full(dev, hy3_fp8_weights):
     """Hy3 decode with FP8 E4M3 experts (one scale per matrix), every token.
 
     Not one of the bf16 workloads the 2e-2 bound is stated for: the output
     bound is the derived one (max(2e-2, 2^-6 max|ref|), a bf16 ulp or two at
     the largest output); rel-L2 stays 5e-3."""
-    inp = MoEInputs(CONFIGS[5])
-    log("generating and uploading FP8 Hy3 expert weights (192 x 18.9 MB)")
-    w = upload_weights(inp, dev)
-    torch.cuda.synchronize()
-    decode_full_check(inp, dev, w, workload_shape=False)
-    del w
-    gc.collect()
-    torch.cuda.empty_cache()
+    decode_full_check(MoEInputs(CONFIGS[5]), dev, hy3_fp8_weights, workload_shape=False)
+
+
+def test_hy3_prefill_T8192_skew_fp8_sampled(dev, hy3_fp8_weights):
+    """The prefill chunk on the same FP8 experts (large-tile path)."""
+    inp = MoEInputs(CONFIGS[6])
+    log(f"case {inp.cfg.name}")
+    sampled_check(inp, dev, hy3_fp8_weights, workload_shape=False)

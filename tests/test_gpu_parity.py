@@ -105,6 +105,17 @@ SMALL = {
     "fp8_T64_softmax": dict(seed=34, T=64, H=256, E=16, K=4, I=128, I_shared=128,
                             dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
                             bias_kind="none", w_format="fp8_e4m3"),
+    # ... and on the 128-row tiled path and the large-tile path (ragged row
+    # tails, I % 128 == 64 and H % 256 == 64 column tails)
+    "fp8_tiled_T300": dict(seed=35, T=300, H=512, E=24, K=4, I=256, I_shared=128,
+                           dtype="bf16", w_format="fp8_e4m3"),
+    "fp8_tiled_T700_H320": dict(seed=36, T=700, H=320, E=12, K=3, I=320, I_shared=64,
+                                dtype="bf16", w_format="fp8_e4m3"),
+    "fp8_big_T513_tails": dict(seed=37, T=513, H=320, E=4, K=2, I=192, I_shared=64,
+                               dtype="bf16", w_format="fp8_e4m3"),
+    "fp8_big_T400_softmax": dict(seed=38, T=400, H=512, E=8, K=4, I=256, I_shared=128,
+                                 dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
+                                 bias_kind="none", w_format="fp8_e4m3"),
 }
 
 

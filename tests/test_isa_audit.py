@@ -62,5 +62,5 @@ def test_large_tile_bf16_kernels_do_not_spill(tmp_path):
     asm = assemble("k_expert_big.hip", tmp_path)
     pairs = re.findall(r"\.name:\s+(\S+)\s+\.private_segment_fixed_size:\s+(\d+)", asm)
     bf16 = [(n, int(v)) for n, v in pairs if "expert_big_kernelINS_6bf16_t" in n]
-    assert len(bf16) == 2
+    assert len(bf16) == 4   # gate-up and down, bf16 and FP8 weights
     assert all(v == 0 for _, v in bf16), bf16
