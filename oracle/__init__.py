@@ -1,14 +1,15 @@
 """CPU oracle of the MoE FFN layer (float64).  TEST INFRASTRUCTURE ONLY:
 imported by tests, the smoke check and the benchmark's CPU-baseline leg,
 never by the product path."""
-from .moe import (ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, dense_masked,
+from .moe import (E4M3_MAX, ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, dense_masked,
                   dequant_fp8, forward, forward_given_route, fp8_e4m3_value,
-                  layer_flops, route,
+                  layer_flops, quant_dequant_e4m3, quant_e4m3, route,
                   route_from_logits, router_logits, sigmoid, silu,
                   softmax_rows, swiglu_expert, topk_desc)
 
 __all__ = [
-    "ROUTE_SIGMOID_BIAS", "ROUTE_SOFTMAX", "Route", "dense_masked", "dequant_fp8",
-    "forward", "forward_given_route", "fp8_e4m3_value", "layer_flops", "route", "route_from_logits",
+    "E4M3_MAX", "ROUTE_SIGMOID_BIAS", "ROUTE_SOFTMAX", "Route", "dense_masked", "dequant_fp8",
+    "forward", "forward_given_route", "fp8_e4m3_value", "layer_flops", "quant_dequant_e4m3",
+    "quant_e4m3", "route", "route_from_logits",
     "router_logits", "sigmoid", "silu", "softmax_rows", "swiglu_expert", "topk_desc",
 ]

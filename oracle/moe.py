@@ -50,6 +50,16 @@ E4M3 as above and one scale per expert matrix is the reading taken here.
 The oracle dequantises exactly (every E4M3 value times a float32 scale is
 exact in float64) and then runs the same float64 layer.
 
+Static FP8 activations (W8A8; the CANN article, section 8.2 and the FP8
+path of section 六, where an FP8 Linear quantises its input with a static
+per-tensor input scale).  The expert input x is quantised with one float32
+scale a1 of the layer, and each expert's h (the down projection's input)
+with that expert's float32 scale a2[e] (a2[E]: shared expert): code =
+E4M3(v / a), saturating, round to nearest even, decided in float32 (h is
+rounded from float64 to float32 first); the GEMMs then run on scale times
+value.  Granularity, saturation, rounding and the precision of the decision
+are readings: the pages name only "static per-tensor".
+
 Parity pins: every public function is pinned by a test in
 ``tests/test_oracle_pins.py`` (hand-derived golden values, brute force over
 all K-subsets, a loop-only dense evaluation, closed forms and invariants).
@@ -198,6 +208,44 @@ def dequant_fp8(codes: np.ndarray, scale) -> np.ndarray:
     return np.float64(np.float32(scale)) * fp8_e4m3_value(codes)
 
 
+E4M3_MAX = 448.0
+
+
+def quant_e4m3(v: np.ndarray, scale) -> np.ndarray:
+    """E4M3 codes of v / scale: static per-tensor activation quantisation.
+
+    The decision is taken in float32: v is rounded to float32, divided by the
+    float32 scale (one correctly rounded float32 division), clamped to
+    [-448, 448] (saturating: an overflow becomes the largest finite code) and
+    rounded to the nearest E4M3 value, ties to the even mantissa.  The E4M3
+    grid has spacing 2^(e-3) in the binade [2^e, 2^(e+1)) for e >= -6 and
+    spacing 2^-9 below 2^-6 (subnormals).  A value that rounds to zero keeps
+    its sign (0x80 for negative).  NaN inputs are not handled.
+    """
+    q = (np.asarray(v, dtype=np.float32) / np.float32(scale)).astype(np.float64)
+    neg = np.signbit(q)
+    a = np.minimum(np.abs(q), E4M3_MAX)
+    # exponent of the binade of a (a = f * 2^ex with f in [0.5, 1))
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(ex.astype(np.int64) - 1, -6)     # binade [2^e, 2^(e+1)), subnormals at -6
+    step = np.exp2((e - 3).astype(np.float64))      # grid spacing (2^-9 for subnormals)
+    r = np.rint(a / step) * step                    # exact: step is a power of two
+    # encode r
+    _, ex_r = np.frexp(np.where(r > 0, r, 1.0))
+    er = ex_r.astype(np.int64) - 1
+    normal = r >= 2.0 ** -6
+    field = np.where(normal, er + 7, 0)
+    man = np.where(normal, np.rint((r / np.exp2(er.astype(np.float64)) - 1.0) * 8.0),
+                   np.rint(r / 2.0 ** -9)).astype(np.int64)
+    code = np.where(r == 0, 0, (field << 3) | man)
+    return (code | (neg.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quant_dequant_e4m3(v: np.ndarray, scale) -> np.ndarray:
+    """scale * value(quant_e4m3(v, scale)) in float64."""
+    return dequant_fp8(quant_e4m3(v, scale), scale)
+
+
 # --------------------------------------------------------------------------
 # Experts
 # --------------------------------------------------------------------------
@@ -207,16 +255,22 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
-                  w_down: np.ndarray) -> np.ndarray:
+                  w_down: np.ndarray, a2: Optional[float] = None) -> np.ndarray:
     """One SwiGLU expert on rows ``a`` [n, H]:  down( silu(a W_gate^T) * (a W_up^T) ).
 
     Weights are in nn.Linear layout [out, in]: gate/up [I, H], down [H, I]
     (HunyuanImage 3.0 MoE reading, stacked gate/up and down weights).
+
+    With ``a2`` (static FP8 activations, W8A8), the down projection's input
+    h is first quantised to E4M3 with the static scale a2 and dequantised
+    (``quant_dequant_e4m3``), as an FP8 Linear quantises its input.
     """
     a = np.asarray(a, dtype=np.float64)
     g = a @ np.asarray(w_gate, dtype=np.float64).T
     u = a @ np.asarray(w_up, dtype=np.float64).T
     h = silu(g) * u
+    if a2 is not None:
+        h = quant_dequant_e4m3(h, a2)
     return h @ np.asarray(w_down, dtype=np.float64).T
 
 
@@ -225,7 +279,8 @@ def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
 # --------------------------------------------------------------------------
 def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
                         experts: ExpertFn, E: int,
-                        shared: Optional[Sequence[np.ndarray]] = None) -> np.ndarray:
+                        shared: Optional[Sequence[np.ndarray]] = None,
+                        a8: Optional[Tuple[float, Sequence[float]]] = None) -> np.ndarray:
     """Routed experts + shared expert for a given route (the eager path).
 
     Follows the eager path of the HunyuanImage 3.0 MoE reading: every token
@@ -238,15 +293,24 @@ def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
 
     ``experts(e)`` returns (gate, up, down) of routed expert e in float64;
     experts no copy is routed to are never requested.
+
+    ``a8 = (a1, a2)`` selects static FP8 activations (W8A8): the expert input
+    x is quantised once with the layer's scale a1 (``quant_dequant_e4m3``)
+    and every expert's h with its own scale a2[e] (a2[E] for the shared
+    expert).  The router is not affected: it reads the unquantised x.
     """
     x = np.asarray(x, dtype=np.float64)
     idx = np.asarray(idx)
     weight = np.asarray(weight, dtype=np.float64)
     T, H = x.shape
     K = idx.shape[1] if idx.ndim == 2 else 0
+    a2 = [None] * (E + 1)
+    if a8 is not None:
+        x = quant_dequant_e4m3(x, a8[0])
+        a2 = [float(v) for v in a8[1]]
     out_shared = np.zeros((T, H))
     if shared is not None:
-        out_shared = swiglu_expert(x, *shared)
+        out_shared = swiglu_expert(x, *shared, a2=a2[E])
     if T == 0 or K == 0:
         return out_shared
     flat_idx = idx.reshape(-1)
@@ -257,7 +321,7 @@ def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
         if not mask.any():
             continue
         wg, wu, wd = experts(e)
-        expert_out[mask] = swiglu_expert(x_rep[mask], wg, wu, wd)
+        expert_out[mask] = swiglu_expert(x_rep[mask], wg, wu, wd, a2=a2[e])
     routed = (expert_out.reshape(T, K, H) * weight[:, :, None]).sum(axis=1)
     return out_shared + routed
 
@@ -272,12 +336,13 @@ def forward(x, w_router, experts: ExpertFn, E: int, K: int,
 
 
 def dense_masked(x, idx, weight, experts: ExpertFn, E: int,
-                 shared: Optional[Sequence[np.ndarray]] = None) -> np.ndarray:
+                 shared: Optional[Sequence[np.ndarray]] = None,
+                 a8: Optional[Tuple[float, Sequence[float]]] = None) -> np.ndarray:
     """Brute force: evaluate every expert on every token and mask.
 
     out[t] = shared(x_t) + sum_e M[t, e] * f_e(x_t), where M is zero except
     M[t, idx[t, j]] = weight[t, j].  Used on tiny inputs only, as a check of
-    the sparse dispatch above.
+    the sparse dispatch above (``a8`` as there).
     """
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
@@ -286,9 +351,12 @@ def dense_masked(x, idx, weight, experts: ExpertFn, E: int,
     for t in range(T):
         for j in range(idx.shape[1]):
             M[t, idx[t, j]] += weight[t, j]
-    out = np.zeros((T, H)) if shared is None else swiglu_expert(x, *shared)
+    if a8 is not None:
+        x = quant_dequant_e4m3(x, a8[0])
+    sc = (lambda e: None) if a8 is None else (lambda e: float(a8[1][e]))
+    out = np.zeros((T, H)) if shared is None else swiglu_expert(x, *shared, a2=sc(E))
     for e in range(E):
-        out = out + M[:, e:e + 1] * swiglu_expert(x, *experts(e))
+        out = out + M[:, e:e + 1] * swiglu_expert(x, *experts(e), a2=sc(e))
     return out
 
 

@@ -42,6 +42,11 @@ the top binade (up to 448).  Each matrix gets its own float32 scale
 (1 + U(0, 0.25)) / (74 sqrt(fan_in)), so that scale times value has about
 the spread of the bf16 weights.  Nothing here decodes the codes: that is
 the layer's own (de-quantisation) step.
+
+Static FP8 activation scales (``act_format == "fp8_static"``, W8A8) stand
+in for calibrated ones: a1 = 4.5 / 448 for the layer input (x ~ N(0, 1):
+about 7 in a million values saturate) and a2[e] = (1 + U(0, 0.25)) * 12 / 448
+for each expert's h (a2[E] for the shared expert), float32.
 """
 from __future__ import annotations
 
@@ -54,6 +59,7 @@ import numpy as np
 
 T_X, T_WR, T_BIAS, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN = range(9)
 T_CODES, T_SCALES = 100, 200     # offsets of the FP8 code and scale streams
+T_ASCALES = 300                  # static FP8 activation scales
 
 ROUTE_SIGMOID_BIAS = 0
 ROUTE_SOFTMAX = 1
@@ -106,6 +112,7 @@ class MoEConfig:
     renorm_eps: float          # clamp of the renormalisation denominator
     bias_kind: str             # "uniform", "skew" or "none"
     w_format: str = "dtype"    # expert weights: "dtype" (as `dtype`) or "fp8_e4m3"
+    act_format: str = "dtype"  # expert activations: "dtype" or "fp8_static" (W8A8)
 
     def with_T(self, T: int) -> "MoEConfig":
         return dataclasses.replace(self, T=int(T))
@@ -147,6 +154,15 @@ CONFIGS: Dict[int, MoEConfig] = {
                  I=1536, I_shared=1536, dtype="bf16",
                  route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                  bias_kind="skew", w_format="fp8_e4m3"),
+    # The same two shapes and FP8 experts with static FP8 activations (W8A8).
+    7: MoEConfig("hy3_decode_T16_w8a8", 7, 5, T=16, H=4096, E=192, K=8, I=1536,
+                 I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                 scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform",
+                 w_format="fp8_e4m3", act_format="fp8_static"),
+    8: MoEConfig("hy3_prefill_T8192_skew_w8a8", 8, 5, T=8192, H=4096, E=192, K=8,
+                 I=1536, I_shared=1536, dtype="bf16",
+                 route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
+                 bias_kind="skew", w_format="fp8_e4m3", act_format="fp8_static"),
 }
 
 ROUTER_SWEEP_M = (2, 64, 512, 4096)
@@ -330,6 +346,13 @@ class MoEInputs:
             list(ex.map(job, range(c.E)))
         return wg, wu, wd, sc
 
+    def act_scales(self):
+        """Static FP8 activation scales: (a1 float32, a2 float32 [E + 1])."""
+        c = self.cfg
+        rs = _rng(self.seed, c.model_key, T_ASCALES)
+        a2 = ((1.0 + 0.25 * rs.random(c.E + 1)) * (12.0 / 448.0)).astype(np.float32)
+        return np.float32(4.5 / 448.0), a2
+
     # ---- float64 views for the oracle ----
     def x_f64(self) -> np.ndarray:
         return to_f64(self.x(), self.cfg.dtype)
@@ -352,10 +375,11 @@ def make_inputs(cfg_id: int, seed: int = 0, T: Optional[int] = None) -> MoEInput
 def random_small(seed: int, T: int, H: int, E: int, K: int, I: int, I_shared: int,
                  dtype: str = "f32", route_mode: int = ROUTE_SIGMOID_BIAS,
                  scale: float = HY3_SCALE, renorm_eps: float = 0.0,
-                 bias_kind: str = "uniform", w_format: str = "dtype") -> MoEInputs:
+                 bias_kind: str = "uniform", w_format: str = "dtype",
+                 act_format: str = "dtype") -> MoEInputs:
     """A small ad-hoc workload with the same distributions (for property tests)."""
     cfg = MoEConfig(f"small_{seed}", 900 + (seed % 97), 900 + seed, T=T, H=H, E=E, K=K,
                     I=I, I_shared=I_shared, dtype=dtype, route_mode=route_mode,
                     scale=scale, renorm_eps=renorm_eps, bias_kind=bias_kind,
-                    w_format=w_format)
+                    w_format=w_format, act_format=act_format)
     return MoEInputs(cfg, seed)

@@ -398,3 +398,146 @@ def test_fp8_layer_equals_layer_on_dequantised_weights():
     doubled = {e: (g, u, 2.0 * d) for e, (g, u, d) in experts.items()}
     out2 = oracle.forward_given_route(x, r.idx, r.weight, lambda e: doubled[e], c.E)
     np.testing.assert_allclose(out2, 2.0 * out, rtol=0, atol=0)
+
+
+# --------------------------------------------------------------------------
+# Static FP8 activations (W8A8): E4M3 quantiser and the layer that uses it
+# --------------------------------------------------------------------------
+_FINITE = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def test_e4m3_quant_round_trips_every_finite_code():
+    """Every finite E4M3 value quantises (scale 1) back to its own code."""
+    v = oracle.fp8_e4m3_value(_FINITE)
+    np.testing.assert_array_equal(oracle.quant_e4m3(v, 1.0), _FINITE)
+
+
+def test_e4m3_quant_ties_go_to_even_mantissa():
+    """Midpoints of neighbouring codes go to the even code; a float32 ulp
+    above or below decides for the upper or lower one."""
+    for sign in (0, 0x80):
+        lo = np.arange(0, 0x7E, dtype=np.int64) | sign
+        hi = lo + 1
+        vl = oracle.fp8_e4m3_value(lo.astype(np.uint8))
+        vh = oracle.fp8_e4m3_value(hi.astype(np.uint8))
+        mid = ((vl + vh) / 2).astype(np.float32)
+        assert (mid.astype(np.float64) == (vl + vh) / 2).all()   # exact in float32
+        even = np.where(lo % 2 == 0, lo, hi).astype(np.uint8)
+        np.testing.assert_array_equal(oracle.quant_e4m3(mid, 1.0), even)
+        away = np.nextafter(mid, np.float32(np.copysign(np.inf, mid[1])))
+        toward = np.nextafter(mid, np.float32(0))
+        np.testing.assert_array_equal(oracle.quant_e4m3(away, 1.0), hi.astype(np.uint8))
+        np.testing.assert_array_equal(oracle.quant_e4m3(toward, 1.0), lo.astype(np.uint8))
+
+
+def test_e4m3_quant_decides_in_float32():
+    """A float64 value just above a tie that rounds onto the tie in float32 is
+    a tie (the decision is taken on the float32 value)."""
+    tie = np.float64(1.0625)                       # between 1.0 (0x38) and 1.125 (0x39)
+    v = tie + 2.0 ** -40                           # above the tie in float64 only
+    assert np.float32(v) == np.float32(tie)
+    assert oracle.quant_e4m3(np.array([v]), 1.0)[0] == 0x38
+    assert oracle.quant_e4m3(np.array([tie + 2.0 ** -20]), 1.0)[0] == 0x39
+
+
+def test_e4m3_quant_matches_torch_cast_after_clamp():
+    """Against torch's float32 -> float8_e4m3fn cast (round to nearest even,
+    no saturation) of the clamped float32 quotient."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    n = 200_000
+    mag = np.exp2(rng.uniform(-16, 11, n))
+    v = (np.where(rng.random(n) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+    for s in (1.0, 0.0101, 4.5 / 448, 1.7):
+        got = oracle.quant_e4m3(v, s)
+        q = torch.from_numpy(v) / torch.tensor(s, dtype=torch.float32)
+        ref = q.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_quant_saturates_and_keeps_the_sign_of_zero():
+    v = np.array([448.0, 464.0, 465.0, 1e30, -1e30, 0.0, -0.0, 2.0 ** -11, -2.0 ** -11])
+    np.testing.assert_array_equal(oracle.quant_e4m3(v, 1.0),
+                                  [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x00, 0x80, 0x00, 0x80])
+
+
+def test_e4m3_quant_dequant_is_invariant_under_power_of_two_scales():
+    """In the normal range, scaling the static scale by 2^k shifts the grid by
+    whole binades: the dequantised values do not change."""
+    rng = np.random.default_rng(8)
+    s = 0.03
+    # |v / s| in [2^-3, 2^7.5]: normal at every scale 2^k s below (k = 3 .. -1)
+    v = s * np.exp2(rng.uniform(-3.0, 7.5, 10_000)) * np.where(rng.random(10_000) < 0.5, -1, 1)
+    a = oracle.quant_dequant_e4m3(v, s)
+    for k in (-1, 1, 3):
+        np.testing.assert_array_equal(oracle.quant_dequant_e4m3(v, s * 2.0 ** k), a)
+    # ... and the dequantised value is within half a grid step (2^-4 relative)
+    assert (np.abs(a - v) <= np.abs(v) * 2.0 ** -4 + 1e-300).all()
+
+
+def _w8a8_small(seed, T=12, H=64, E=5, K=2, I=32, I_shared=32, xmax=1.5, hmax=0.5):
+    """A small FP8 layer with static activation scales a1 = xmax / 448 and
+    a2[e] = hmax (1 + e / 4) / 448 (small maxima saturate many values)."""
+    inp = random_small(seed, T, H, E, K, I, I_shared, dtype="bf16", w_format="fp8_e4m3")
+    c = inp.cfg
+    experts = {}
+    for e in range(c.E):
+        codes, sc = inp.expert_fp8(e)
+        experts[e] = tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))
+    codes, sc = inp.shared_fp8()
+    shared = tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))
+    r = oracle.route(inp.x_f64(), inp.w_router().astype(np.float64), c.K, 0,
+                     inp.bias().astype(np.float64), c.scale)
+    a1 = xmax / 448
+    a2 = np.float32(hmax / 448) * (1.0 + np.arange(c.E + 1, dtype=np.float64) / 4)
+    return inp, experts, shared, r, (a1, a2)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_w8a8_layer_eager_equals_dense_masked(seed):
+    inp, experts, shared, r, a8 = _w8a8_small(seed)
+    c = inp.cfg
+    x = inp.x_f64()
+    got = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared, a8=a8)
+    ref = oracle.dense_masked(x, r.idx, r.weight, lambda e: experts[e], c.E, shared, a8=a8)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_w8a8_layer_scalar_loops():
+    """One token through a loop-only evaluation: quantise x with a1, run every
+    picked expert with element loops, quantise each h value with that
+    expert's a2, and sum with the route weights."""
+    inp, experts, shared, r, (a1, a2) = _w8a8_small(3, T=2, H=16, E=4, K=2, I=8, I_shared=8)
+    c = inp.cfg
+    x = inp.x_f64()
+    got = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared,
+                                     a8=(a1, a2))
+    for t in range(c.T):
+        xq = [float(oracle.quant_dequant_e4m3(np.array([x[t, k]]), a1)[0]) for k in range(c.H)]
+        ref = [0.0] * c.H
+        picks = [(int(r.idx[t, j]), float(r.weight[t, j])) for j in range(c.K)] + [(c.E, 1.0)]
+        for e, w in picks:
+            wg, wu, wd = experts[e] if e < c.E else shared
+            hq = []
+            for i in range(wg.shape[0]):
+                g = math.fsum(xq[k] * wg[i, k] for k in range(c.H))
+                u = math.fsum(xq[k] * wu[i, k] for k in range(c.H))
+                h = g / (1.0 + math.exp(-g)) * u
+                hq.append(float(oracle.quant_dequant_e4m3(np.array([h]), a2[e])[0]))
+            for n in range(c.H):
+                ref[n] += w * math.fsum(hq[i] * wd[n, i] for i in range(len(hq)))
+        np.testing.assert_allclose(got[t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_w8a8_layer_is_within_the_quantisation_error_of_w8a16():
+    """Quantising x and h (3 mantissa bits, round to nearest: at most 2^-4
+    relative each) moves the output by a few percent, never by a factor; the
+    difference is not zero (the activations really are quantised)."""
+    inp, experts, shared, r, a8 = _w8a8_small(4, T=64, H=128, E=6, K=2, I=64, I_shared=64,
+                                              xmax=5.0, hmax=12.0)
+    c = inp.cfg
+    x = inp.x_f64()
+    ref = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared)
+    got = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared, a8=a8)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 0.005 < rel < 0.08, rel

@@ -97,3 +97,15 @@ def test_fp8_codes_and_scales():
     assert (wg[1] == g).all() and s.shape == (3, 3) and s[0, 1] == sc[0]
     sh_codes, sh_sc = inp.shared_fp8()
     assert sh_codes[2].shape == (256, 64) and len(sh_sc) == 3
+
+
+def test_static_activation_scales():
+    inp = MoEInputs(CONFIGS[8])
+    a1, a2 = inp.act_scales()
+    assert a1.dtype == np.float32 and a2.dtype == np.float32
+    assert a2.shape == (inp.cfg.E + 1,)
+    assert a1 == np.float32(4.5 / 448)
+    assert (a2 >= np.float32(12 / 448)).all() and (a2 <= np.float32(1.25 * 12 / 448)).all()
+    # one model: the decode and prefill W8A8 workloads share the scales
+    np.testing.assert_array_equal(MoEInputs(CONFIGS[7]).act_scales()[1], a2)
+    assert CONFIGS[7].act_format == CONFIGS[8].act_format == "fp8_static"
