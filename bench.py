@@ -10,7 +10,9 @@ Default workload: Hy3 decode, T=16 tokens, H=4096, 192 routed experts
 `--workload prefill` (T=8192, skewed bias) and `--workload softmax`
 (HunyuanImage-3.0 softmax routing, T=32768, E=64) run the other layer shapes;
 `--workload decode_fp8` / `prefill_fp8` are the decode and prefill shapes with
-FP8 E4M3 expert weights.
+FP8 E4M3 expert weights, `decode_w8a8` / `prefill_w8a8` the same with static
+FP8 activations as well (FP8 MFMAs on the large-tile path, priced against the
+FP8 peak).
 
 Printed: one JSON line with tokens/s, the dominant kernel's roofline fraction
 (its per-launch duration measured live with HIP events on the library's
@@ -30,10 +32,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4, "decode_fp8": 5, "prefill_fp8": 6}
+WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4, "decode_fp8": 5, "prefill_fp8": 6,
+             "decode_w8a8": 7, "prefill_w8a8": 8}
 ROUTER_WORKLOAD = 3            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published
 METRIC = "Hy3 MoE layer tokens/s; % bf16 MFMA peak (prefill) / % HBM BW (decode)"
 
 
@@ -113,7 +117,8 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {c.name}: inputs uploaded in {time.time() - t0:.1f}s")
     cfg = sm.make_config(c.T, c.H, c.E, c.K, c.I, c.I_shared, c.dtype, c.route_mode,
-                         scale=c.scale, renorm_eps=c.renorm_eps, w_format=c.w_format)
+                         scale=c.scale, renorm_eps=c.renorm_eps, w_format=c.w_format,
+                         act_format=c.act_format)
     ws = sm.alloc_workspace(cfg, True, dev)
     out = torch.empty_like(x)
     idx = torch.empty((c.T, c.K), dtype=torch.int32, device=dev)
@@ -177,20 +182,26 @@ def main():
     # ---- algorithmic work ----
     eb = 2 if c.dtype == "bf16" else 4
     web = 1 if c.w_format == "fp8_e4m3" else eb      # bytes per expert weight element
+    tile_rows = sm.hy3moe_workspace_layout(cfg).tile_rows
+    # static FP8 activations: E4M3 bytes on the large-tile path (FP8 MFMAs),
+    # their bf16 values on the others
+    fp8_mma = c.act_format == "fp8_static" and tile_rows == 256
+    ab = 1 if fp8_mma else eb                         # bytes per x / h element
+    peak_mma = PEAK_FP8_TFLOPS if fp8_mma else PEAK_BF16_TFLOPS
     T, H, E, K, I, Is = c.T, c.H, c.E, c.K, c.I, c.I_shared
     R = T * K + (T if Is else 0)
     groups = U + (1 if Is else 0)
     gu_weight_bytes = U * 2 * I * H * web + (2 * Is * H * web if Is else 0)
     dn_weight_bytes = U * H * I * web + (H * Is * web if Is else 0)
-    gu_bytes = gu_weight_bytes + T * H * eb + R * I * eb
-    dn_bytes = dn_weight_bytes + R * I * eb + R * H * eb
+    gu_bytes = gu_weight_bytes + T * H * ab + R * I * ab
+    dn_bytes = dn_weight_bytes + R * I * ab + R * H * eb
     layer_bytes = gu_weight_bytes + dn_weight_bytes + E * H * 4 + 2 * T * H * eb
     gu_flops = 4.0 * H * (T * K * I + (T * Is if Is else 0))
     dn_flops = 2.0 * H * (T * K * I + (T * Is if Is else 0))
     layer_flops = 1.5 * gu_flops + 2.0 * T * H * E
     layer_s = ms_per_step / 1e3
     gu_s = stage_ms["gate_up"] / 1e3
-    decode = args.workload in ("decode", "decode_fp8")
+    decode = args.workload.startswith("decode")
     if decode:
         kind = "FP8 E4M3" if web == 1 else c.dtype
         roof = {"kernel": "gate_up (weight-streaming grouped GEMM + SwiGLU)", "bound": "hbm",
@@ -198,10 +209,11 @@ def main():
                 "per_unit": f"{2 * I * H * web} B of {kind} gate+up weights per touched "
                             f"expert x {groups} experts + x and h rows"}
     else:
-        tile_rows = sm.hy3moe_workspace_layout(cfg).tile_rows
         path = "256x256-tile" if tile_rows == 256 else "128x128-tile"
+        if fp8_mma:
+            path += " FP8 MFMA"
         roof = {"kernel": f"gate_up ({path} grouped GEMM + SwiGLU)", "bound": "mfma",
-                "achieved": gu_flops / gu_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "achieved": gu_flops / gu_s / 1e12, "peak": peak_mma, "unit": "TFLOP/s",
                 "per_unit": f"{4 * H * I} FLOP per routed row x {T * K} rows + "
                             f"{4 * H * Is} per shared row x {T}"}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -215,7 +227,7 @@ def main():
         "bytes": layer_bytes, "GB_s": layer_bytes / layer_s / 1e9,
         "hbm_frac": layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS,
         "flops": layer_flops, "TFLOP_s": layer_flops / layer_s / 1e12,
-        "mfma_frac": layer_flops / layer_s / 1e12 / PEAK_BF16_TFLOPS,
+        "mfma_frac": layer_flops / layer_s / 1e12 / peak_mma,
         "down_achieved": (dn_bytes / (stage_ms["down"] / 1e3) / 1e9 if decode
                           else dn_flops / (stage_ms["down"] / 1e3) / 1e12),
     }
@@ -235,11 +247,14 @@ def main():
     res = {
         "metric": METRIC, "value": T / layer_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c.dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8_mma else c.dtype,
         "data": "synthetic (seeded, random-init weights of the layer's shapes)",
         "config": {"workload": c.name, "T": T, "H": H, "E": E, "K": K, "I": I, "I_shared": Is,
                    "route": "sigmoid+bias" if c.route_mode == 0 else "softmax",
-                   "expert_weights": "fp8_e4m3" if web == 1 else c.dtype},
+                   "expert_weights": "fp8_e4m3" if web == 1 else c.dtype,
+                   "expert_activations": ("fp8_e4m3_static" if c.act_format == "fp8_static"
+                                          else c.dtype)},
         "roofline": roof, "cpu_baseline": cpu, "layer": layer,
         "graph_ms_per_step": graph_ms,
     }
@@ -385,6 +400,10 @@ def cpu_baseline(inp, args, gpu_idx):
     else:
         expert_f64 = inp.expert_f64
         sh = inp.shared_f64()
+    a8 = None
+    if c.act_format == "fp8_static":
+        a1, a2 = inp.act_scales()
+        a8 = (float(a1), a2.astype(np.float64))
     with ThreadPoolExecutor(8) as ex:
         ws = dict(zip(need, ex.map(expert_f64, need)))
     log(f"[bench] oracle sample: {n} tokens, {len(need)} experts in float64 "
@@ -399,7 +418,7 @@ def cpu_baseline(inp, args, gpu_idx):
     while reps < 3 or (dt < args.cpu_seconds and reps < 10000):
         t1 = time.perf_counter()
         r = oracle.route(x64, wr, c.K, c.route_mode, b64, c.scale, c.renorm_eps)
-        oracle.forward_given_route(x64, r.idx, r.weight, ws.__getitem__, c.E, sh)
+        oracle.forward_given_route(x64, r.idx, r.weight, ws.__getitem__, c.E, sh, a8=a8)
         dt += time.perf_counter() - t1
         reps += 1
     del ws

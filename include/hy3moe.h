@@ -87,6 +87,20 @@ extern "C" {
 #define HY3MOE_WFMT_DTYPE    0
 #define HY3MOE_WFMT_FP8_E4M3 1
 
+/* Activations of the expert GEMMs.  DTYPE: x and h as cfg.dtype.
+ * FP8_STATIC (W8A8; needs w_format FP8_E4M3): static per-tensor FP8
+ * activations, the FP8 path of the CANN deployment article (section 六: an
+ * FP8 Linear quantises its input with a static per-tensor input scale;
+ * section 8.2: W8A8).  The experts' input x is quantised once with the
+ * layer's scale x_scale and each group's h with its own scale h_scale[g]:
+ * code = E4M3(v / scale), the quotient a correctly rounded float32 division,
+ * clamped to +-448 (saturating), rounded to nearest even.  The GEMMs then
+ * run on scale * value of both operands (FP8 MFMAs on the large-tile path,
+ * the same values in bf16 on the other two).  The router reads the
+ * unquantised x. */
+#define HY3MOE_AFMT_DTYPE      0
+#define HY3MOE_AFMT_FP8_STATIC 1
+
 /* Shape and mode of one layer call. */
 typedef struct hy3moe_config {
   int64_t T;          /* tokens (rows of x)                                   */
@@ -101,6 +115,7 @@ typedef struct hy3moe_config {
   float   scale;      /* routed-weight scale: 2.826 for Hy3, 1 for softmax    */
   float   renorm_eps; /* softmax mode: clamp of the top-K sum (1e-8); sigmoid mode: unused */
   int32_t w_format;   /* HY3MOE_WFMT_*: storage of the expert weights            */
+  int32_t act_format; /* HY3MOE_AFMT_*: activations of the expert GEMMs          */
 } hy3moe_config;
 
 /* Weights.  Layouts follow nn.Linear [out, in] (K-contiguous rows), stacked
@@ -115,7 +130,11 @@ typedef struct hy3moe_config {
  *   ws_scale [3]   fp32: shared gate, up, down (NULL if I_shared == 0)
  * are required (4-byte aligned); with FP8 weights the six expert pointers
  * need 16-byte alignment as always.  The scale pointers are ignored for
- * w_format DTYPE. */
+ * w_format DTYPE.  With act_format FP8_STATIC
+ *   x_scale [1]      fp32: static scale of the experts' input x
+ *   h_scale [E + 1]  fp32: static scale of each routed expert's h, then the
+ *                    shared expert's (entry E read only if I_shared > 0)
+ * are required (4-byte aligned); ignored otherwise. */
 typedef struct hy3moe_weights {
   const float *w_router;
   const float *expert_bias;
@@ -129,6 +148,8 @@ typedef struct hy3moe_weights {
   const float *w_up_scale;
   const float *w_down_scale;
   const float *ws_scale;
+  const float *x_scale;
+  const float *h_scale;
 } hy3moe_weights;
 
 /* Byte offsets of the intermediate buffers inside a forward workspace (for
@@ -154,6 +175,9 @@ typedef struct hy3moe_ws_layout {
   size_t y;              /* dtype [R][H]      expert outputs before the combine */
   size_t w_planes;       /* bf16 [3][E][H] router weight split into bf16 terms, used
                             for bf16 batches of T >= 1024 (0 = not used)           */
+  size_t xq;             /* act_format FP8_STATIC: quantised x [T][H], E4M3 bytes on
+                            the large-tile path, else their bf16 values (0 = not
+                            used); h then holds h quantised the same way        */
 } hy3moe_ws_layout;
 
 /* Workspace size in bytes for hy3moe_forward (for_forward != 0) or for
@@ -208,6 +232,18 @@ int hy3moe_forward_timed(const hy3moe_config *cfg, const void *x, const hy3moe_w
                          void *out, int32_t *idx_out, float *weight_out,
                          void *workspace, size_t ws_bytes, void *stream,
                          void *const *stage_events);
+
+/* Static FP8 activation quantisation on its own: q[i] = E4M3(x[i] / *scale)
+ * for i < n, as act_format FP8_STATIC quantises the experts' input (the CANN
+ * deployment article, section 六, FP8 path: static per-tensor input scale).
+ *   x      [n] dtype (HY3MOE_BF16 or HY3MOE_F32), device, 16-byte aligned
+ *   scale  [1] fp32, device, 4-byte aligned (read on the device: no sync)
+ *   q      [n] uint8 out, device, 16-byte aligned: OCP E4M3 codes
+ * Quotient a correctly rounded float32 division, clamped to +-448, rounded to
+ * nearest even.  Errors: HY3MOE_ERR_INVALID (n < 0, bad dtype, null pointer
+ * with n > 0), HY3MOE_ERR_ALIGN.  n == 0 is a no-op. */
+int hy3moe_quantize_e4m3(const void *x, int32_t dtype, int64_t n, const float *scale, uint8_t *q,
+                         void *stream);
 
 /* Human-readable text of a return code (static storage). */
 const char *hy3moe_strerror(int code);

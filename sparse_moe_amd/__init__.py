@@ -5,7 +5,8 @@ from .binding import (EXPORTED_SYMBOLS, HY3MOE_BF16, HY3MOE_F32,
                       STAGE_NAMES, hy3moe_forward_timed,
                       HY3MOE_ROUTER_FP32, HY3MOE_ROUTER_SPLIT2_BF16, Hy3MoEError,
                       alloc_workspace, forward, hy3moe_config, hy3moe_forward,
-                      hy3moe_route, hy3moe_weights, hy3moe_workspace_bytes,
+                      hy3moe_quantize_e4m3, hy3moe_route, hy3moe_weights,
+                      hy3moe_workspace_bytes,
                       hy3moe_workspace_layout, hy3moe_ws_layout, load, make_config,
                       route, strerror)
 
@@ -14,6 +15,6 @@ __all__ = [
     "hy3moe_forward_timed", "HY3MOE_ROUTE_SIGMOID_BIAS",
     "HY3MOE_ROUTE_SOFTMAX", "HY3MOE_ROUTER_FP32", "HY3MOE_ROUTER_SPLIT2_BF16",
     "Hy3MoEError", "alloc_workspace", "forward", "hy3moe_config", "hy3moe_forward",
-    "hy3moe_route", "hy3moe_weights", "hy3moe_workspace_bytes", "hy3moe_workspace_layout",
+    "hy3moe_quantize_e4m3", "hy3moe_route", "hy3moe_weights", "hy3moe_workspace_bytes", "hy3moe_workspace_layout",
     "hy3moe_ws_layout", "load", "make_config", "route", "strerror",
 ]

@@ -24,14 +24,17 @@ HY3MOE_ROUTER_FP32 = 0
 HY3MOE_ROUTER_SPLIT2_BF16 = 1
 HY3MOE_WFMT_DTYPE = 0
 HY3MOE_WFMT_FP8_E4M3 = 1
+HY3MOE_AFMT_DTYPE = 0
+HY3MOE_AFMT_FP8_STATIC = 1
 
 HY3MOE_N_STAGES = 6
-ABI_VERSION = 3          # hy3moe_abi_version() of the library this binding matches
+ABI_VERSION = 4          # hy3moe_abi_version() of the library this binding matches
 STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 
 EXPORTED_SYMBOLS = (
     "hy3moe_abi_version", "hy3moe_strerror", "hy3moe_workspace_bytes",
     "hy3moe_workspace_layout", "hy3moe_route", "hy3moe_forward", "hy3moe_forward_timed",
+    "hy3moe_quantize_e4m3",
 )
 
 
@@ -42,11 +45,13 @@ class hy3moe_config(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("route_mode", ctypes.c_int32),
         ("router_prec", ctypes.c_int32), ("scale", ctypes.c_float),
         ("renorm_eps", ctypes.c_float), ("w_format", ctypes.c_int32),
+        ("act_format", ctypes.c_int32),
     ]
 
 
 WEIGHT_NAMES = ("w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up",
-                "ws_down", "w_gate_scale", "w_up_scale", "w_down_scale", "ws_scale")
+                "ws_down", "w_gate_scale", "w_up_scale", "w_down_scale", "ws_scale",
+                "x_scale", "h_scale")
 
 
 class hy3moe_weights(ctypes.Structure):
@@ -62,7 +67,7 @@ class hy3moe_ws_layout(ctypes.Structure):
         ("hist", ctypes.c_size_t), ("n_chunks", ctypes.c_int32),
         ("tiles", ctypes.c_size_t), ("max_tiles", ctypes.c_int32),
         ("tile_rows", ctypes.c_int32), ("h", ctypes.c_size_t), ("y", ctypes.c_size_t),
-        ("w_planes", ctypes.c_size_t),
+        ("w_planes", ctypes.c_size_t), ("xq", ctypes.c_size_t),
     ]
 
 
@@ -113,6 +118,9 @@ def load() -> ctypes.CDLL:
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p,
                                        ctypes.POINTER(ctypes.c_void_p)]
+    L.hy3moe_quantize_e4m3.restype = ctypes.c_int
+    L.hy3moe_quantize_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     if L.hy3moe_abi_version() != ABI_VERSION:
         raise RuntimeError("libhy3moe ABI version mismatch")
     _LIB = L
@@ -126,14 +134,17 @@ def strerror(code: int) -> str:
 def make_config(T: int, H: int, E: int, K: int, I: int, I_shared: int, dtype: str = "bf16",
                 route_mode: int = HY3MOE_ROUTE_SIGMOID_BIAS,
                 router_prec: int = HY3MOE_ROUTER_FP32, scale: float = 2.826,
-                renorm_eps: float = 1e-8, w_format: str = "dtype") -> hy3moe_config:
+                renorm_eps: float = 1e-8, w_format: str = "dtype",
+                act_format: str = "dtype") -> hy3moe_config:
     return hy3moe_config(T=int(T), H=int(H), E=int(E), K=int(K), I=int(I),
                          I_shared=int(I_shared),
                          dtype=HY3MOE_BF16 if dtype == "bf16" else HY3MOE_F32,
                          route_mode=int(route_mode), router_prec=int(router_prec),
                          scale=float(scale), renorm_eps=float(renorm_eps),
                          w_format=(HY3MOE_WFMT_FP8_E4M3 if w_format == "fp8_e4m3"
-                                   else HY3MOE_WFMT_DTYPE))
+                                   else HY3MOE_WFMT_DTYPE),
+                         act_format=(HY3MOE_AFMT_FP8_STATIC if act_format == "fp8_static"
+                                     else HY3MOE_AFMT_DTYPE))
 
 
 def hy3moe_workspace_bytes(cfg: hy3moe_config, for_forward: bool = True) -> int:
@@ -184,6 +195,21 @@ def hy3moe_route(cfg: hy3moe_config, x: torch.Tensor, w_router: torch.Tensor,
                              _stream(stream))
     if rc != HY3MOE_OK:
         raise Hy3MoEError(rc, "hy3moe_route")
+
+
+def hy3moe_quantize_e4m3(x: torch.Tensor, scale: torch.Tensor, q: torch.Tensor,
+                         stream=None) -> None:
+    """C ABI hy3moe_quantize_e4m3: q = E4M3 codes of x / scale (uint8, x.numel())."""
+    _check_dev(x, scale, q)
+    if x.dtype not in (torch.bfloat16, torch.float32) or q.dtype != torch.uint8:
+        raise ValueError("x must be bf16 or float32 and q uint8")
+    if q.numel() != x.numel() or scale.dtype != torch.float32 or scale.numel() < 1:
+        raise ValueError("q needs x.numel() bytes and scale one float32")
+    dt = HY3MOE_BF16 if x.dtype == torch.bfloat16 else HY3MOE_F32
+    rc = load().hy3moe_quantize_e4m3(_ptr(x), dt, x.numel(), _ptr(scale), _ptr(q),
+                                     _stream(stream))
+    if rc != HY3MOE_OK:
+        raise Hy3MoEError(rc, "hy3moe_quantize_e4m3")
 
 
 def hy3moe_forward(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str, torch.Tensor],

@@ -32,6 +32,7 @@ SOURCES = [
     "k_expert_tiled.hip",
     "k_expert_big.hip",
     "k_combine.hip",
+    "k_quant.hip",
 ]
 
 ARCH = "gfx950"

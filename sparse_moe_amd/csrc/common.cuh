@@ -94,6 +94,26 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const uint4 &q, uint4 &lo, uint4
   lo = e4m3x8_to_bf16(make_uint2(q.x, q.y));
   hi = e4m3x8_to_bf16(make_uint2(q.z, q.w));
 }
+
+// Static FP8 activation quantisation: E4M3 code of v / s, the quotient a
+// correctly rounded float32 division, clamped to +-448 (saturating) and
+// rounded to the nearest E4M3 value, ties to even (v_cvt_pk_fp8_f32).
+// Four values -> bytes 0..3 of the result.
+__device__ __forceinline__ uint32_t quant_e4m3x4(float a, float b, float c, float d, float s) {
+  const float lim = 448.0f;
+  a = fminf(fmaxf(a / s, -lim), lim);
+  b = fminf(fmaxf(b / s, -lim), lim);
+  c = fminf(fmaxf(c / s, -lim), lim);
+  d = fminf(fmaxf(d / s, -lim), lim);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+// Four codes -> their values as 4 bf16 (exact): the bf16 form in which the
+// bf16-MFMA paths carry quantised activations.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
+  return make_uint2(HY3_E4M3_PAIR(w, false), HY3_E4M3_PAIR(w, true));
+}
 #undef HY3_E4M3_PAIR
 
 // SiLU(g) * u in fp32: g / (1 + e^-g) * u.

@@ -44,12 +44,25 @@ int validate_cfg(const hy3moe_config *c) {
   // FP8 expert weights need bf16 activations.
   if (c->w_format == HY3MOE_WFMT_FP8_E4M3 && c->dtype != HY3MOE_BF16)
     return HY3MOE_ERR_UNSUPPORTED;
+  if (c->act_format != HY3MOE_AFMT_DTYPE && c->act_format != HY3MOE_AFMT_FP8_STATIC)
+    return HY3MOE_ERR_INVALID;
+  // Static FP8 activations go with FP8 weights.
+  if (c->act_format == HY3MOE_AFMT_FP8_STATIC && c->w_format != HY3MOE_WFMT_FP8_E4M3)
+    return HY3MOE_ERR_UNSUPPORTED;
   // The expert GEMMs address x and every expert matrix with 32-bit offsets.
   const uint64_t eb = c->dtype == HY3MOE_F32 ? 4 : 2, lim = uint64_t(1) << 32;
   const uint64_t Imax = c->I > c->I_shared ? c->I : c->I_shared;
   if ((uint64_t)c->T * c->H * eb >= lim || (uint64_t)c->H * Imax * eb >= lim)
     return HY3MOE_ERR_UNSUPPORTED;
   return HY3MOE_OK;
+}
+
+// GEMM path of a layer call: static FP8 activations run the large-tile
+// path's FP8 MFMAs, whose 128-value K stages need H, I, I_shared % 128 == 0.
+int path_of(const hy3moe_config *c) {
+  const bool big_ok = c->act_format != HY3MOE_AFMT_FP8_STATIC ||
+                      (c->H % 128 == 0 && c->I % 128 == 0 && c->I_shared % 128 == 0);
+  return expert_path(c->T, c->K, c->E, big_ok);
 }
 
 void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L) {
@@ -74,7 +87,7 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
   const int64_t R = N + T_sh;
   L->sorted_token = off; off += al((size_t)R * 4);
   L->pos_of = off;      off += al((size_t)N * 4);
-  const int path = expert_path(T, K, E);
+  const int path = path_of(c);
   if (path == PATH_SKINNY) {
     L->tile_rows = skinny_tile_rows((int)T);
     L->max_tiles = E + 1;
@@ -87,6 +100,9 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
   const int eb = elt_bytes(c->dtype);
   L->h = off;           off += al((size_t)R * Imax * eb);
   L->y = off;           off += al((size_t)R * H * eb);
+  if (c->act_format == HY3MOE_AFMT_FP8_STATIC) {
+    L->xq = off;        off += al((size_t)T * H * 2);
+  }
   L->total = off;
 }
 
@@ -99,7 +115,7 @@ int check_launch(hipError_t e) { return e == hipSuccess ? HY3MOE_OK : HY3MOE_ERR
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 3; }
+int hy3moe_abi_version(void) { return 4; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {
@@ -179,6 +195,11 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
         (has_shared && !al4(w->ws_scale)))
       return HY3MOE_ERR_ALIGN;
   }
+  const bool a8 = cfg->act_format == HY3MOE_AFMT_FP8_STATIC;
+  if (a8) {
+    if (!w->x_scale || !w->h_scale) return HY3MOE_ERR_INVALID;
+    if (!al4(w->x_scale) || !al4(w->h_scale)) return HY3MOE_ERR_ALIGN;
+  }
   hy3moe_ws_layout L;
   compute_layout(cfg, 1, &L);
   if (ws_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
@@ -222,12 +243,22 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   pa.nchunks = L.n_chunks;
   pa.tile_rows = L.tile_rows;
   pa.max_tiles = L.max_tiles;
-  pa.sort_tiles = expert_path(T, K, E) != PATH_SKINNY;
+  pa.sort_tiles = path_of(cfg) != PATH_SKINNY;
   rc = check_launch(launch_permute(pa, s));
   if (rc) return rc;
   mark();
 
   // 4-5. grouped experts
+  const int path = path_of(cfg);
+  // Static FP8 activations: x quantised once for every gate-up GEMM, as code
+  // bytes for the large-tile path's FP8 MFMAs, else as their bf16 values.
+  const void *act = x;
+  if (a8) {
+    rc = check_launch(launch_quant_e4m3(x, cfg->dtype, (int64_t)T * H, w->x_scale, ws + L.xq,
+                                        path == PATH_BIG ? 0 : 1, s));
+    if (rc) return rc;
+    act = ws + L.xq;
+  }
   const int Imax = cfg->I > cfg->I_shared ? cfg->I : cfg->I_shared;
   ExpertArgs ea;
   ea.sorted_token = pa.sorted_token;
@@ -235,14 +266,16 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.tiles = pa.tiles;
   ea.E = E; ea.H = H; ea.I = cfg->I; ea.I_shared = cfg->I_shared; ea.ldh = Imax;
   ea.max_tiles = L.max_tiles;
-  ea.act = x; ea.w0 = w->w_gate; ea.w1 = w->w_up; ea.ws0 = w->ws_gate; ea.ws1 = w->ws_up;
+  ea.act = act; ea.w0 = w->w_gate; ea.w1 = w->w_up; ea.ws0 = w->ws_gate; ea.ws1 = w->ws_up;
   ea.out = ws + L.h;
   ea.w_fp8 = fp8 ? 1 : 0;
   ea.sc0 = fp8 ? w->w_gate_scale : nullptr;
   ea.sc1 = fp8 ? w->w_up_scale : nullptr;
   ea.ssc0 = fp8 && has_shared ? w->ws_scale : nullptr;
   ea.ssc1 = fp8 && has_shared ? w->ws_scale + 1 : nullptr;
-  const int path = expert_path(T, K, E);
+  ea.a8 = a8 ? 1 : 0;
+  ea.xs = a8 ? w->x_scale : nullptr;
+  ea.hs = a8 ? w->h_scale : nullptr;
   rc = check_launch(launch_gate_up(ea, cfg->dtype, T, path, s));
   if (rc) return rc;
   mark();
@@ -262,6 +295,16 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   if (rc) return rc;
   mark();
   return HY3MOE_OK;
+}
+
+int hy3moe_quantize_e4m3(const void *x, int32_t dtype, int64_t n, const float *scale, uint8_t *q,
+                         void *stream) {
+  if (n < 0 || (dtype != HY3MOE_F32 && dtype != HY3MOE_BF16)) return HY3MOE_ERR_INVALID;
+  if (n == 0) return HY3MOE_OK;
+  if (!x || !scale || !q) return HY3MOE_ERR_INVALID;
+  if (!al16(x) || !al16(q) || !al4(scale)) return HY3MOE_ERR_ALIGN;
+  return check_launch(
+      launch_quant_e4m3(x, dtype, n, scale, q, 0, static_cast<hipStream_t>(stream)));
 }
 
 int hy3moe_forward(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w, void *out,

@@ -23,9 +23,11 @@ constexpr int BIG_MIN_AVG_ROWS = 192;  // mean routed rows per expert that selec
 
 // Which expert-GEMM path runs for a batch (the tile list is built for it).
 enum { PATH_SKINNY = 0, PATH_TILED = 1, PATH_BIG = 2 };
-inline int expert_path(int64_t T, int K, int E) {
+// big_ok = false keeps batches off the large-tile path (static FP8
+// activations there need H, I and I_shared to be multiples of 128).
+inline int expert_path(int64_t T, int K, int E, bool big_ok = true) {
   if (T <= SKINNY_MAX_T) return PATH_SKINNY;
-  if (T * K >= (int64_t)BIG_MIN_AVG_ROWS * E) return PATH_BIG;
+  if (big_ok && T * K >= (int64_t)BIG_MIN_AVG_ROWS * E) return PATH_BIG;
   return PATH_TILED;
 }
 
@@ -74,9 +76,22 @@ struct ExpertArgs {
   // and *ssc0 / *ssc1 for the shared expert (gate-up: gate, up; down: down).
   int w_fp8;
   const float *sc0, *sc1, *ssc0, *ssc1;
+  // Static FP8 activations (a8 = 1, with w_fp8): act holds E4M3 codes on the
+  // large-tile path and their exact bf16 values on the other two; *xs is the
+  // scale of x and hs[g] that of group g's h (hs[E]: shared).  The gate-up
+  // GEMMs store h quantised with hs[g] in the same form.
+  int a8;
+  const float *xs, *hs;
 };
 hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);
 hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);
+
+// Static FP8 activation quantisation: q[i] = E4M3(x[i] / *scale) for n
+// elements of x (dtype); carrier = 0 stores the code bytes, 1 their values as
+// bf16.  n % 8 == 0 and 16-byte aligned buffers for the vector path; any n
+// otherwise.
+hipError_t launch_quant_e4m3(const void *x, int dtype, int64_t n, const float *scale, void *q,
+                             int carrier, hipStream_t stream);
 
 // Combine ---------------------------------------------------------------------
 hipError_t launch_combine(const void *y, const int32_t *pos_of, const float *weight,

@@ -31,6 +31,14 @@
 // FP8 E4M3 weights (F8): a thread loads the 8 code bytes of its weight chunk,
 // decodes them exactly to 8 bf16 when it writes the chunk to LDS, and the
 // per-matrix scale multiplies the accumulators in the epilogue.
+//
+// Static FP8 activations (A8, W8A8): both operands are E4M3 bytes, so a
+// 128-byte stage row holds 128 K values and one 16x16x128 FP8 MFMA replaces
+// the two 16x16x32 bf16 ones of a fragment pair: the LDS layout, the reads
+// (chunks c and 4 + c of the lane's row, the same K positions for both
+// operands) and the 16-element output fragments stay as they are.  The
+// gate-up epilogue quantises h with the group's static scale and stores
+// bytes; the down epilogue scales by weight scale x activation scale.
 #include <type_traits>
 
 #include "common.cuh"
@@ -81,10 +89,10 @@ struct BigTile {
 };
 
 // Logical tile r of this XCD's run (see the kernel); false if it is padding.
-template <typename T, bool GATE_UP>
+template <typename T, bool GATE_UP, bool A8>
 __device__ __forceinline__ bool big_tile_at(const ExpertArgs &a, int n_tiles, int n_col_tiles,
                                             int per, int xcd, int r, BigTile &t) {
-  constexpr int EB = Elem<T>::kBytes;
+  constexpr int EB = A8 ? 1 : Elem<T>::kBytes;   // bytes per K element of a stage row
   const int band_sz = BAND * n_col_tiles;
   const int L = xcd * per + r;
   const int band = L / band_sz, within = L - band * band_sz;
@@ -105,13 +113,13 @@ __device__ __forceinline__ bool big_tile_at(const ExpertArgs &a, int n_tiles, in
 // block of 64 rows [64q, 64q+64) holds gate cols col0 + 32q + [0, 32) and then
 // the up cols of the same columns, so lr < 32 loads gate rows, lr >= 32 up rows.
 // Global addresses: a base pointer plus 32-bit offsets (every matrix < 4 GiB).
-template <typename T, bool GATE_UP, bool F8>
+template <typename T, bool GATE_UP, bool F8, bool A8>
 __device__ __forceinline__ void big_tile_loads(const ExpertArgs &a, const BigTile &t, int lr,
                                                int lc, const char *&wb, const char *&xb,
                                                uint32_t *woff, uint32_t *xoff) {
-  constexpr int EB = Elem<T>::kBytes;
-  constexpr int WB = F8 ? 1 : EB;              // bytes per weight element
-  constexpr int WCH = F8 ? 8 : 16;             // weight bytes per 16-byte LDS chunk
+  constexpr int EB = A8 ? 1 : Elem<T>::kBytes; // bytes per token-row element
+  constexpr int WB = F8 ? 1 : Elem<T>::kBytes; // bytes per weight element
+  constexpr int WCH = (F8 && !A8) ? 8 : 16;    // weight bytes per 16-byte LDS chunk
   const bool shared = (t.g == a.E);
   if (GATE_UP) {
     const bool up = lr >= 32;
@@ -141,17 +149,70 @@ __device__ __forceinline__ void big_tile_loads(const ExpertArgs &a, const BigTil
   }
 }
 
+// A8 gate-up epilogue: h = SwiGLU of the scaled accumulators, quantised with
+// the group's static scale hs; 128 E4M3 bytes per token row are staged in LDS
+// (16-byte chunks swizzled by row) and stored as whole chunks.
+__device__ __forceinline__ void big_epilogue_h8(const ExpertArgs &a, const BigTile &t,
+                                                const f32x4_t (&acc)[8][4], uint4 *lds, int tid,
+                                                float s0, float s1, float hs) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr_ = wave >> 2, wt_ = wave & 3, r16 = lane & 15, cg = lane >> 4;
+  constexpr int OC = BW / 2 / 16;   // 16-byte chunks per staged row (8)
+  char *stg = reinterpret_cast<char *>(lds);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wt_ * 64 + j * 16 + r16;
+    char *row = stg + r * OC * 16;
+    // fragment pairs as in the bf16 epilogue: gate frag gi, up frag gi + 2
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gi = (i >> 1) * 4 + (i & 1);
+      const int c = wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
+      const f32x4_t gv = acc[gi][j] * s0, uv = acc[gi + 2][j] * s1;
+      const uint32_t q = quant_e4m3x4(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
+                                      swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]), hs);
+      *reinterpret_cast<uint32_t *>(row + (((c >> 4) ^ (r & 7)) << 4) + (c & 15)) = q;
+    }
+  }
+  __syncthreads();
+  uint8_t *out = static_cast<uint8_t *>(a.out);
+#pragma unroll
+  for (int m = 0; m < 256 * OC / 512; ++m) {
+    const int q = tid + 512 * m;
+    const int r = q / OC, ch = q % OC;
+    const int c = t.col0 + ch * 16;
+    if (t.row0 + r < t.grp_end && c < t.Ig) {
+      const uint4 v = lds[r * OC + (ch ^ (r & 7))];
+      uint4 *dst = reinterpret_cast<uint4 *>(out + (size_t)(t.row0 + r) * a.ldh + c);
+      __builtin_nontemporal_store(v.x, &dst->x);
+      __builtin_nontemporal_store(v.y, &dst->y);
+      __builtin_nontemporal_store(v.z, &dst->z);
+      __builtin_nontemporal_store(v.w, &dst->w);
+    }
+  }
+}
+
 // Epilogue of a tile: lane holds D[weight row 16i + 4cg + q][token row 16j + r16]
 // of wavefront (wr_, wt_).  tid is the thread index.
-template <typename T, bool GATE_UP, bool F8>
+template <typename T, bool GATE_UP, bool F8, bool A8>
 __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile &t,
                                              const f32x4_t (&acc)[8][4], uint4 *lds, int tid) {
-  // FP8: scale of the gate (or down) matrix and of the up matrix
+  // FP8: scale of the gate (or down) matrix and of the up matrix (A8: times
+  // the activation scale of the GEMM's input)
   float s0 = 1.0f, s1 = 1.0f;
   if (F8) {
     const bool shared = (t.g == a.E);
     s0 = shared ? *a.ssc0 : a.sc0[t.g];
     if (GATE_UP) s1 = shared ? *a.ssc1 : a.sc1[t.g];
+  }
+  if (A8) {
+    const float as = GATE_UP ? *a.xs : a.hs[t.g];
+    s0 *= as;
+    s1 *= as;
+  }
+  if constexpr (A8 && GATE_UP) {
+    big_epilogue_h8(a, t, acc, lds, tid, s0, s1, a.hs[t.g]);
+    return;
   }
   const int lane = tid & 63, wave = tid >> 6;
   const int wr_ = wave >> 2, wt_ = wave & 3, r16 = lane & 15, cg = lane >> 4;
@@ -243,7 +304,34 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
 __device__ __forceinline__ uint4 weight_chunk(const uint4 &v) { return v; }
 __device__ __forceinline__ uint4 weight_chunk(const uint2 &q) { return e4m3x8_to_bf16(q); }
 
-template <typename T, bool GATE_UP, bool F8>
+// One 16x16x128 FP8 (E4M3 x E4M3) MFMA; each operand is two 16-byte chunks.
+__device__ __forceinline__ void mma_fp8(f32x4_t &acc, const uint4 &a0, const uint4 &a1,
+                                        const uint4 &b0, const uint4 &b1) {
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8_t bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+}
+
+// Order of one A8 stage per wavefront: the 8 B reads and the first A
+// fragment's 2 reads up front, then 8 groups of 4 MFMAs (one A fragment
+// against the 4 B fragments), each followed by the next A fragment's reads.
+// The global loads and LDS writes are left to the compiler: pinning them as
+// in the bf16 order leaves too few registers (the FP8 operands of a
+// fragment pair are held at once) and spills.
+__device__ __forceinline__ void stage_schedule_a8() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+template <typename T, bool GATE_UP, bool F8, bool A8>
 __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_col_tiles) {
   __shared__ uint4 lds[2 * ROWS * CH];   // 2 x 64 KB
 
@@ -257,13 +345,14 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
   const int xcd = blockIdx.x & 7, nb = gridDim.x >> 3;
   int r = blockIdx.x >> 3;
   BigTile cur;
-  while (r < per && !big_tile_at<T, GATE_UP>(a, n_tiles, n_col_tiles, per, xcd, r, cur)) r += nb;
+  while (r < per && !big_tile_at<T, GATE_UP, A8>(a, n_tiles, n_col_tiles, per, xcd, r, cur))
+    r += nb;
   if (r >= per) return;
 
   const int lr = tid >> 3, lc = tid & 7;
   const char *wb, *xb;
   uint32_t woff[4], xoff[4];
-  big_tile_loads<T, GATE_UP, F8>(a, cur, lr, lc, wb, xb, woff, xoff);
+  big_tile_loads<T, GATE_UP, F8, A8>(a, cur, lr, lc, wb, xb, woff, xoff);
 
   const int wr_ = wave >> 2, wt_ = wave & 3;
   const int r16 = lane & 15, cg = lane >> 4;
@@ -278,14 +367,14 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
   // iteration s - 2 and written to LDS at the end of iteration s - 1, so the
   // global latency is covered by two iterations of MFMA work.
   // Weight chunks: 16 bytes, or the 8 E4M3 code bytes of 8 weights (FP8).
-  typedef typename std::conditional<F8, uint2, uint4>::type wchunk_t;
+  typedef typename std::conditional<F8 && !A8, uint2, uint4>::type wchunk_t;
   wchunk_t aw0, aw1, aw2, aw3, bw0, bw1, bw2, bw3;
   uint4 ax0, ax1, ax2, ax3;   // set 0
   uint4 bx0, bx1, bx2, bx3;   // set 1
 #define HY3_GLOAD(S, kst)                                                              \
   {                                                                                    \
     const uint32_t kb_ = (uint32_t)(kst) * RB;                                         \
-    const uint32_t kw_ = F8 ? kb_ / 2 : kb_;   /* FP8 weight rows: half the bytes */   \
+    const uint32_t kw_ = (F8 && !A8) ? kb_ / 2 : kb_;   /* W8A16: half the bytes */  \
     S##w0 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[0]));                 \
     S##w1 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[1]));                 \
     S##w2 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[2]));                 \
@@ -304,7 +393,20 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     d_[(BW + 2 * 64) * CH] = S##x2; d_[(BW + 3 * 64) * CH] = S##x3;                    \
   }
 #define HY3_COMPUTE(buf)                                                               \
-  {                                                                                    \
+  if constexpr (A8) {                                                                  \
+    const uint4 *base_ = lds + (buf) * ROWS * CH;                                      \
+    uint4 b0_[4], b1_[4];                                                              \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                    \
+      b0_[j] = base_[rd_b + j * 16 * CH + sw0];                                        \
+      b1_[j] = base_[rd_b + j * 16 * CH + sw1];                                        \
+    }                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                    \
+      const uint4 a0_ = base_[rd_a + i * 16 * CH + sw0];                               \
+      const uint4 a1_ = base_[rd_a + i * 16 * CH + sw1];                               \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                    \
+          mma_fp8(acc[i][j], a0_, a1_, b0_[j], b1_[j]);                                \
+    }                                                                                  \
+  } else {                                                                             \
     const uint4 *base_ = lds + (buf) * ROWS * CH;                                      \
     _Pragma("unroll") for (int sub = 0; sub < 2; ++sub) {                              \
       const int swz = sub ? sw1 : sw0;                                                 \
@@ -326,7 +428,8 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     HY3_GLOAD(S, ((k) + 2 < cur.nk) ? (k) + 2 : 0);                                        \
     HY3_COMPUTE(B);                                                                    \
     HY3_LSTORE(SN, (B) ^ 1);                                                           \
-    if constexpr (sizeof(T) == 2) stage_schedule();                                    \
+    if constexpr (A8) stage_schedule_a8();                                             \
+    else if constexpr (sizeof(T) == 2) stage_schedule();                               \
     __syncthreads();                                                                   \
   }
 
@@ -354,7 +457,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
 
     BigTile nxt;
     int rn = r + nb;
-    while (rn < per && !big_tile_at<T, GATE_UP>(a, n_tiles, n_col_tiles, per, xcd, rn, nxt))
+    while (rn < per && !big_tile_at<T, GATE_UP, A8>(a, n_tiles, n_col_tiles, per, xcd, rn, nxt))
       rn += nb;
     const bool has_next = rn < per;
     // The address arithmetic below uses fresh copies of the thread index, so
@@ -363,14 +466,14 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     if (has_next) {   // the finished tile's load descriptors are free
       int tid_n = tid;
       asm volatile("" : "+v"(tid_n));
-      big_tile_loads<T, GATE_UP, F8>(a, nxt, tid_n >> 3, tid_n & 7, wb, xb, woff, xoff);
+      big_tile_loads<T, GATE_UP, F8, A8>(a, nxt, tid_n >> 3, tid_n & 7, wb, xb, woff, xoff);
       HY3_GLOAD(a, 0);
       HY3_GLOAD(b, (1 < nxt.nk) ? 1 : 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     int tid_e = tid;
     asm volatile("" : "+v"(tid_e));
-    big_epilogue<T, GATE_UP, F8>(a, cur, acc, lds, tid_e);
+    big_epilogue<T, GATE_UP, F8, A8>(a, cur, acc, lds, tid_e);
     __builtin_amdgcn_sched_barrier(0);
     if (!has_next) break;
     __syncthreads();   // the epilogue's LDS reads are done
@@ -386,7 +489,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
 
 }
 
-template <typename T, bool F8>
+template <typename T, bool F8, bool A8>
 hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   int nct;
   if (gate_up) {
@@ -409,23 +512,25 @@ hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   const long want = (logical + 7) / 8 * 8;
   const dim3 grid((unsigned)(want < cap ? want : cap));
   if (gate_up)
-    hipLaunchKernelGGL((expert_big_kernel<T, true, F8>), grid, dim3(512), 0, stream, a, nct);
+    hipLaunchKernelGGL((expert_big_kernel<T, true, F8, A8>), grid, dim3(512), 0, stream, a, nct);
   else
-    hipLaunchKernelGGL((expert_big_kernel<T, false, F8>), grid, dim3(512), 0, stream, a, nct);
+    hipLaunchKernelGGL((expert_big_kernel<T, false, F8, A8>), grid, dim3(512), 0, stream, a, nct);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_big_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_big_t<float, false>(a, true, stream)
-         : a.w_fp8       ? launch_big_t<bf16_t, true>(a, true, stream)
-                         : launch_big_t<bf16_t, false>(a, true, stream);
+  return dtype == DT_F32 ? launch_big_t<float, false, false>(a, true, stream)
+         : a.a8          ? launch_big_t<bf16_t, true, true>(a, true, stream)
+         : a.w_fp8       ? launch_big_t<bf16_t, true, false>(a, true, stream)
+                         : launch_big_t<bf16_t, false, false>(a, true, stream);
 }
 hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_big_t<float, false>(a, false, stream)
-         : a.w_fp8       ? launch_big_t<bf16_t, true>(a, false, stream)
-                         : launch_big_t<bf16_t, false>(a, false, stream);
+  return dtype == DT_F32 ? launch_big_t<float, false, false>(a, false, stream)
+         : a.a8          ? launch_big_t<bf16_t, true, true>(a, false, stream)
+         : a.w_fp8       ? launch_big_t<bf16_t, true, false>(a, false, stream)
+                         : launch_big_t<bf16_t, false, false>(a, false, stream);
 }
 
 }  // namespace hy3moe

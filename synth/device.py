@@ -26,7 +26,8 @@ def upload_weights(inp: MoEInputs, device) -> Dict[str, object]:
     import torch
     c = inp.cfg
     if c.w_format == "fp8_e4m3":
-        return _upload_fp8(inp, device)
+        d = _upload_fp8(inp, device)
+        return with_act_scales(inp, d, device) if c.act_format == "fp8_static" else d
     wg, wu, wd = inp.stacked_experts()
     d = {"w_router": torch.from_numpy(inp.w_router()).to(device),
          "w_gate": to_torch(wg, c.dtype, device), "w_up": to_torch(wu, c.dtype, device),
@@ -39,6 +40,16 @@ def upload_weights(inp: MoEInputs, device) -> Dict[str, object]:
     if sh is not None:
         d["ws_gate"], d["ws_up"], d["ws_down"] = (to_torch(a, c.dtype, device) for a in sh)
     return d
+
+
+def with_act_scales(inp: MoEInputs, weights: Dict[str, object], device) -> Dict[str, object]:
+    """The weights plus the static FP8 activation scales (x_scale [1], h_scale [E+1])."""
+    import torch
+    w = dict(weights)
+    a1, a2 = inp.act_scales()
+    w["x_scale"] = torch.tensor([a1], dtype=torch.float32).to(device)
+    w["h_scale"] = torch.from_numpy(a2).to(device)
+    return w
 
 
 def with_bias_of(inp: MoEInputs, weights: Dict[str, object], device) -> Dict[str, object]:

@@ -37,14 +37,15 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-from synth.device import to_torch, upload_weights, with_bias_of  # noqa: E402,F401
+from synth.device import (to_torch, upload_weights, with_act_scales,  # noqa: E402,F401
+                          with_bias_of)
 
 
 def config_of(inp: MoEInputs, **kw) -> sm.hy3moe_config:
     c = inp.cfg
     d = dict(T=c.T, H=c.H, E=c.E, K=c.K, I=c.I, I_shared=c.I_shared, dtype=c.dtype,
              route_mode=c.route_mode, scale=c.scale, renorm_eps=c.renorm_eps,
-             w_format=c.w_format)
+             w_format=c.w_format, act_format=c.act_format)
     d.update(kw)
     return sm.make_config(**d)
 
@@ -121,6 +122,14 @@ def shared_f64(inp: MoEInputs):
     if sh is None:
         return None
     return tuple(oracle.dequant_fp8(q, s) for q, s in zip(*sh))
+
+
+def a8_of(inp: MoEInputs):
+    """(a1, a2) static FP8 activation scales for the oracle, or None."""
+    if inp.cfg.act_format != "fp8_static":
+        return None
+    a1, a2 = inp.act_scales()
+    return float(a1), a2.astype(np.float64)
 
 
 def out_to_np(out: torch.Tensor) -> np.ndarray:

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "hy3moe.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(hy3moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(hy3moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 3
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 4
     for code in (0, -1, -2, -3, -4, -5):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -52,7 +52,7 @@ def test_abi_version_and_strerror(lib):
 def cfg_of(c, **kw):
     d = dict(T=c.T, H=c.H, E=c.E, K=c.K, I=c.I, I_shared=c.I_shared, dtype=c.dtype,
              route_mode=c.route_mode, scale=c.scale, renorm_eps=c.renorm_eps,
-             w_format=c.w_format)
+             w_format=c.w_format, act_format=c.act_format)
     d.update(kw)
     return sm.make_config(**d)
 
@@ -70,6 +70,10 @@ def test_workspace_layout_is_consistent(lib, cfg_id):
     assert (L.w_planes > 0) == planes
     if planes:
         names.append("w_planes")
+    assert (L.xq > 0) == (c.act_format == "fp8_static")
+    if L.xq:
+        names.append("xq")
+        assert L.total - L.xq >= c.T * c.H * 2
     offs = sorted(getattr(L, n) for n in names)
     assert all(o % 256 == 0 for o in offs)
     assert len(set(offs)) == len(offs)
@@ -88,6 +92,8 @@ def test_workspace_layout_is_consistent(lib, cfg_id):
     (dict(T=1 << 19), -2), (dict(H=65536, I=32768, I_shared=0), -2),
     # FP8 expert weights: bf16 activations and weight-streaming batches only
     (dict(w_format="fp8_e4m3", dtype="f32"), -2),
+    # static FP8 activations: with FP8 weights only
+    (dict(act_format="fp8_static"), -2),
 ])
 def test_invalid_configs_rejected(lib, bad, code):
     c = CONFIGS[1]
@@ -153,6 +159,50 @@ def test_weight_format_enum_is_checked(lib):
     assert sm.hy3moe_workspace_bytes(cfg, True) == 0
     L = b.hy3moe_ws_layout()
     assert lib.hy3moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == -1
+
+
+def test_activation_format_enum_is_checked(lib):
+    cfg = cfg_of(CONFIGS[7])
+    assert sm.hy3moe_workspace_bytes(cfg, True) > 0
+    cfg.act_format = 2
+    assert sm.hy3moe_workspace_bytes(cfg, True) == 0
+    L = b.hy3moe_ws_layout()
+    assert lib.hy3moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == -1
+
+
+def test_w8a8_path_choice(lib):
+    """W8A8 batches take the large-tile FP8-MFMA path only when H, I and
+    I_shared are multiples of 128 (its K stages hold 128 values)."""
+    big = sm.hy3moe_workspace_layout(cfg_of(CONFIGS[8]))
+    assert big.tile_rows == 256
+    for kw in (dict(H=4096 + 64), dict(I=1536 + 64), dict(I_shared=64)):
+        L = sm.hy3moe_workspace_layout(cfg_of(CONFIGS[8], **kw))
+        assert L.tile_rows == 128, kw
+        # ... while the same shapes with W8A16 stay on the large-tile path
+        L16 = sm.hy3moe_workspace_layout(cfg_of(CONFIGS[8], act_format="dtype", **kw))
+        assert L16.tile_rows == 256, kw
+
+
+def test_w8a8_needs_its_activation_scales(lib):
+    cfg = cfg_of(CONFIGS[7])
+    need = sm.hy3moe_workspace_bytes(cfg, True)
+    fw = lib.hy3moe_forward
+    no_h = b.hy3moe_weights(*([4096] * 13 + [None]))
+    no_x = b.hy3moe_weights(*([4096] * 12 + [None, 4096]))
+    mis = b.hy3moe_weights(*([4096] * 13 + [4098]))
+    for w, code in ((no_h, -1), (no_x, -1), (mis, -4)):
+        assert fw(ctypes.byref(cfg), 4096, ctypes.byref(w), 8192, None, None, 4096, need,
+                  None) == code
+
+
+def test_quantize_entry_validation(lib):
+    q = lib.hy3moe_quantize_e4m3
+    assert q(None, 1, 0, None, None, None) == 0          # n == 0: no-op
+    assert q(None, 1, -1, None, None, None) == -1
+    assert q(4096, 3, 8, 4096, 4096, None) == -1         # bad dtype
+    assert q(4096, 1, 8, None, 4096, None) == -1         # no scale
+    assert q(4104, 1, 8, 4096, 4096, None) == -4         # x not 16-byte aligned
+    assert q(4096, 0, 8, 4098, 4096, None) == -4         # scale not 4-byte aligned
 
 
 def test_fp8_weights_need_their_scales(lib):

@@ -15,9 +15,9 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (MARGIN, check_output, check_route, config_of, expert_cache, log,
+from gpu_util import (MARGIN, a8_of, check_output, check_route, config_of, expert_cache, log,
                       oracle_route, out_to_np, shared_f64, to_torch, upload_weights,
-                      with_bias_of)
+                      with_act_scales, with_bias_of)
 from synth import CONFIGS, ROUTER_SWEEP_M, MoEInputs
 
 pytestmark = pytest.mark.gpu
@@ -62,7 +62,8 @@ def sampled_check(inp, dev, weights, n_sample=256, seed=0, workload_shape=True):
     t_is_tie = np.isin(tokens, tie)
     ridx[t_is_tie] = gidx[tokens][t_is_tie]
     rw[t_is_tie] = gw[tokens][t_is_tie]
-    ref = oracle.forward_given_route(x64, ridx, rw, expert_cache(inp), c.E, shared_f64(inp))
+    ref = oracle.forward_given_route(x64, ridx, rw, expert_cache(inp), c.E, shared_f64(inp),
+                                     a8=a8_of(inp))
     got = out_to_np(out)[tokens]
     check_output(got, ref, c.dtype, c.name, workload_shape=workload_shape)
     counts = np.bincount(gidx.reshape(-1), minlength=c.E)
@@ -74,6 +75,7 @@ def sampled_check(inp, dev, weights, n_sample=256, seed=0, workload_shape=True):
 def decode_full_check(inp, dev, weights, workload_shape=True):
     c = inp.cfg
     log(f"case {c.name}")
+    weights = with_bias_of(inp, weights, dev)
     cfg = config_of(inp)
     x = to_torch(inp.x(), c.dtype, dev)
     out, idx, w = sm.forward(cfg, x, weights, return_route=True)
@@ -86,7 +88,7 @@ def decode_full_check(inp, dev, weights, workload_shape=True):
     tie = r.margin <= MARGIN
     ridx[tie], rw[tie] = gidx[tie], gw[tie]
     ref = oracle.forward_given_route(inp.x_f64(), ridx, rw, expert_cache(inp), c.E,
-                                     shared_f64(inp))
+                                     shared_f64(inp), a8=a8_of(inp))
     check_output(out_to_np(out), ref, c.dtype, c.name, workload_shape=workload_shape)
 
 
@@ -166,3 +168,20 @@ def test_hy3_prefill_T8192_skew_fp8_sampled(dev, hy3_fp8_weights):
     inp = MoEInputs(CONFIGS[6])
     log(f"case {inp.cfg.name}")
     sampled_check(inp, dev, hy3_fp8_weights, workload_shape=False)
+
+
+def test_hy3_decode_T16_w8a8_full(dev, hy3_fp8_weights):
+    """Hy3 decode with FP8 experts and static FP8 activations (W8A8), every
+    token.  h codes are decided from the GPU's float32 h, the oracle's from
+    its float64 h rounded to float32: where the two straddle a rounding
+    midpoint a code differs by one step, so the bound is the derived one."""
+    inp = MoEInputs(CONFIGS[7])
+    decode_full_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev),
+                      workload_shape=False)
+
+
+def test_hy3_prefill_T8192_skew_w8a8_sampled(dev, hy3_fp8_weights):
+    """The W8A8 prefill chunk: FP8 MFMAs on the large-tile path."""
+    inp = MoEInputs(CONFIGS[8])
+    log(f"case {inp.cfg.name}")
+    sampled_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev), workload_shape=False)

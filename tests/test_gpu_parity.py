@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (MARGIN, check_output, check_route, config_of, expert_cache, log,
+from gpu_util import (MARGIN, a8_of, check_output, check_route, config_of, expert_cache, log,
                       oracle_route, out_to_np, shared_f64, to_torch, upload_weights)
 from synth import CONFIGS, MoEInputs, random_small
 
@@ -38,7 +38,8 @@ def reference(inp, r, gidx, gw, tokens=None):
     w[tie] = gw[tie].astype(np.float64)
     if tokens is not None:
         x64, idx, w = x64[tokens], idx[tokens], w[tokens]
-    return oracle.forward_given_route(x64, idx, w, expert_cache(inp), c.E, shared_f64(inp))
+    return oracle.forward_given_route(x64, idx, w, expert_cache(inp), c.E, shared_f64(inp),
+                                      a8=a8_of(inp))
 
 
 def run_gpu(inp, dev, weights=None, workspace=None):
@@ -116,6 +117,25 @@ SMALL = {
     "fp8_big_T400_softmax": dict(seed=38, T=400, H=512, E=8, K=4, I=256, I_shared=128,
                                  dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
                                  bias_kind="none", w_format="fp8_e4m3"),
+    # Static FP8 activations (W8A8) on every path: weight streaming (1 and 4
+    # row fragments), tiled, large-tile FP8 MFMAs (with an H % 256 == 128
+    # column tail and softmax routing), and an H % 128 != 0 batch that the
+    # large-tile path hands to the tiled one
+    "w8a8_T16": dict(seed=40, T=16, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16",
+                     w_format="fp8_e4m3", act_format="fp8_static"),
+    "w8a8_T64_noshared": dict(seed=41, T=64, H=512, E=8, K=2, I=256, I_shared=0,
+                              dtype="bf16", w_format="fp8_e4m3", act_format="fp8_static"),
+    "w8a8_tiled_T300": dict(seed=42, T=300, H=512, E=24, K=4, I=256, I_shared=128,
+                            dtype="bf16", w_format="fp8_e4m3", act_format="fp8_static"),
+    "w8a8_big_T513_H384": dict(seed=43, T=513, H=384, E=4, K=2, I=256, I_shared=128,
+                               dtype="bf16", w_format="fp8_e4m3", act_format="fp8_static"),
+    "w8a8_big_T400_softmax": dict(seed=44, T=400, H=512, E=8, K=4, I=256, I_shared=128,
+                                  dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
+                                  bias_kind="none", w_format="fp8_e4m3",
+                                  act_format="fp8_static"),
+    "w8a8_T700_H320_to_tiled": dict(seed=45, T=700, H=320, E=4, K=3, I=192, I_shared=64,
+                                    dtype="bf16", w_format="fp8_e4m3",
+                                    act_format="fp8_static"),
 }
 
 
