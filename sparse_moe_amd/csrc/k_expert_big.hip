@@ -83,6 +83,17 @@ __device__ __forceinline__ void stage_schedule() {
   sched_group<1, 1, 1>(); sched_group<0, 1, 1>(); sched_group<1, 0, 1>(); sched_group<0, 0, 1>();
 }
 
+// A global-memory pointer that is the same in every lane of the wavefront,
+// moved to scalar registers (rebuilt as a global-address-space pointer, so
+// that loads through it stay global loads).
+__device__ __forceinline__ const char *wave_uniform(const char *p) {
+  typedef const __attribute__((address_space(1))) char gchar_t;
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char *)(gchar_t *)(((uint64_t)hi << 32) | lo);
+}
+
 // A tile of the list: its group, rows and output columns.
 struct BigTile {
   int g, row0, grp_end, Ig, col0, nk;
@@ -125,6 +136,9 @@ __device__ __forceinline__ void big_tile_loads(const ExpertArgs &a, const BigTil
     const bool up = lr >= 32;
     wb = shared ? static_cast<const char *>(up ? a.ws1 : a.ws0)
                 : static_cast<const char *>(up ? a.w1 : a.w0) + (size_t)t.g * a.I * a.H * WB;
+    // A wavefront stages 8 consecutive rows lr (lr = tid / 8), all gate or
+    // all up: the base is wave-uniform, held in scalar registers for A8.
+    if constexpr (A8) wb = wave_uniform(wb);
     xb = static_cast<const char *>(a.act);
   } else {
     wb = shared ? static_cast<const char *>(a.ws0)
@@ -316,19 +330,22 @@ __device__ __forceinline__ void mma_fp8(f32x4_t &acc, const uint4 &a0, const uin
 }
 
 // Order of one A8 stage per wavefront: the 8 B reads and the first A
-// fragment's 2 reads up front, then 8 groups of 4 MFMAs (one A fragment
-// against the 4 B fragments), each followed by the next A fragment's reads.
-// The global loads and LDS writes are left to the compiler: pinning them as
-// in the bf16 order leaves too few registers (the FP8 operands of a
-// fragment pair are held at once) and spills.
+// fragment's 2 reads up front, then 8 groups, each of: one piece of stage
+// k + 1 from registers to LDS, the same registers reloaded with that piece
+// of stage k + 2, 4 MFMAs (one A fragment against the 4 B fragments) and
+// the next A fragment's 2 reads.  One register set suffices and every load has
+// a whole iteration to land.  The next A fragment is read after the MFMAs
+// that use the current one, so its registers are reused; the reads land
+// while those MFMAs execute.
 __device__ __forceinline__ void stage_schedule_a8() {
   __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
 #pragma unroll
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 template <typename T, bool GATE_UP, bool F8, bool A8>
@@ -393,20 +410,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     d_[(BW + 2 * 64) * CH] = S##x2; d_[(BW + 3 * 64) * CH] = S##x3;                    \
   }
 #define HY3_COMPUTE(buf)                                                               \
-  if constexpr (A8) {                                                                  \
-    const uint4 *base_ = lds + (buf) * ROWS * CH;                                      \
-    uint4 b0_[4], b1_[4];                                                              \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                    \
-      b0_[j] = base_[rd_b + j * 16 * CH + sw0];                                        \
-      b1_[j] = base_[rd_b + j * 16 * CH + sw1];                                        \
-    }                                                                                  \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                    \
-      const uint4 a0_ = base_[rd_a + i * 16 * CH + sw0];                               \
-      const uint4 a1_ = base_[rd_a + i * 16 * CH + sw1];                               \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                    \
-          mma_fp8(acc[i][j], a0_, a1_, b0_[j], b1_[j]);                                \
-    }                                                                                  \
-  } else {                                                                             \
+  {                                                                                    \
     const uint4 *base_ = lds + (buf) * ROWS * CH;                                      \
     _Pragma("unroll") for (int sub = 0; sub < 2; ++sub) {                              \
       const int swz = sub ? sw1 : sw0;                                                 \
@@ -428,14 +432,67 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     HY3_GLOAD(S, ((k) + 2 < cur.nk) ? (k) + 2 : 0);                                        \
     HY3_COMPUTE(B);                                                                    \
     HY3_LSTORE(SN, (B) ^ 1);                                                           \
-    if constexpr (A8) stage_schedule_a8();                                             \
-    else if constexpr (sizeof(T) == 2) stage_schedule();                               \
+    if constexpr (sizeof(T) == 2) stage_schedule();                                    \
     __syncthreads();                                                                   \
   }
 
-  HY3_GLOAD(a, 0);
-  HY3_GLOAD(b, (1 < cur.nk) ? 1 : 0);
-  HY3_LSTORE(a, 0);
+  // A8: one register set st0..st7 of a stage (weight pieces 0-3, token
+  // pieces 4-7), refilled piece by piece as it is written to LDS (see
+  // stage_schedule_a8).  Named variables, not an array: an array indexed
+  // across the unrolled groups is left in scratch memory.
+  uint4 st0, st1, st2, st3, st4, st5, st6, st7;
+#define HY3_A8_LOAD(p, kst)                                                            \
+  st##p = *reinterpret_cast<const uint4 *>(((p) < 4 ? wb : xb) +                      \
+                                           ((uint32_t)(kst) * RB +                     \
+                                            ((p) < 4 ? woff[(p) & 3] : xoff[(p) & 3])));
+#define HY3_A8_STORE(p, buf)                                                           \
+  lds[(buf) * ROWS * CH + wr_l + ((p) < 4 ? (p) * 64 * CH : (BW + ((p) - 4) * 64) * CH)] = st##p;
+#define HY3_A8_LOAD_ALL(kst)                                                           \
+  HY3_A8_LOAD(0, kst) HY3_A8_LOAD(1, kst) HY3_A8_LOAD(2, kst) HY3_A8_LOAD(3, kst)       \
+  HY3_A8_LOAD(4, kst) HY3_A8_LOAD(5, kst) HY3_A8_LOAD(6, kst) HY3_A8_LOAD(7, kst)
+#define HY3_A8_STORE_ALL(buf)                                                          \
+  HY3_A8_STORE(0, buf) HY3_A8_STORE(1, buf) HY3_A8_STORE(2, buf) HY3_A8_STORE(3, buf)   \
+  HY3_A8_STORE(4, buf) HY3_A8_STORE(5, buf) HY3_A8_STORE(6, buf) HY3_A8_STORE(7, buf)
+// Group i of an iteration: piece i of stage k + 1 to LDS, piece i of stage
+// k + 2 into its registers, A fragment i against the 4 B fragments, then
+// the next A fragment's reads.
+#define HY3_A8_GROUP(i, B)                                                             \
+  HY3_A8_STORE(i, (B) ^ 1)                                                             \
+  HY3_A8_LOAD(i, kn_)                                                                  \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j)                                        \
+      mma_fp8(acc[i][j], a0_, a1_, b0_[j], b1_[j]);                                    \
+  if ((i) < 7) {                                                                       \
+    a0_ = base_[rd_a + ((i) + 1) * 16 * CH + sw0];                                     \
+    a1_ = base_[rd_a + ((i) + 1) * 16 * CH + sw1];                                     \
+  }
+// Iteration k: compute buffer B, write stage k + 1 to the other buffer and
+// load stage k + 2 (past the end: stage 0 again, written to a buffer that is
+// not read any more).
+#define HY3_A8_ITER(k, B)                                                              \
+  {                                                                                    \
+    const uint4 *base_ = lds + (B) * ROWS * CH;                                        \
+    const int kn_ = ((k) + 2 < cur.nk) ? (k) + 2 : 0;                                  \
+    uint4 b0_[4], b1_[4];                                                              \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                    \
+      b0_[j] = base_[rd_b + j * 16 * CH + sw0];                                        \
+      b1_[j] = base_[rd_b + j * 16 * CH + sw1];                                        \
+    }                                                                                  \
+    uint4 a0_ = base_[rd_a + sw0], a1_ = base_[rd_a + sw1];                            \
+    HY3_A8_GROUP(0, B) HY3_A8_GROUP(1, B) HY3_A8_GROUP(2, B) HY3_A8_GROUP(3, B)         \
+    HY3_A8_GROUP(4, B) HY3_A8_GROUP(5, B) HY3_A8_GROUP(6, B) HY3_A8_GROUP(7, B)         \
+    stage_schedule_a8();                                                               \
+    __syncthreads();                                                                   \
+  }
+
+  if constexpr (A8) {
+    HY3_A8_LOAD_ALL(0)
+    HY3_A8_STORE_ALL(0)
+    HY3_A8_LOAD_ALL((1 < cur.nk) ? 1 : 0)
+  } else {
+    HY3_GLOAD(a, 0);
+    HY3_GLOAD(b, (1 < cur.nk) ? 1 : 0);
+    HY3_LSTORE(a, 0);
+  }
   __syncthreads();
   f32x4_t acc[8][4];
   // Persistent over this workgroup's tiles.  Between two tiles the next
@@ -449,11 +506,19 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     __builtin_amdgcn_sched_barrier(0);
     const int nk = cur.nk;
     int k = 0;
-    for (; k + 2 <= nk; k += 2) {
-      HY3_ITER(k, a, 0, b);
-      HY3_ITER(k + 1, b, 1, a);
+    if constexpr (A8) {
+      for (; k + 2 <= nk; k += 2) {
+        HY3_A8_ITER(k, 0);
+        HY3_A8_ITER(k + 1, 1);
+      }
+      if (k < nk) HY3_A8_ITER(k, 0);
+    } else {
+      for (; k + 2 <= nk; k += 2) {
+        HY3_ITER(k, a, 0, b);
+        HY3_ITER(k + 1, b, 1, a);
+      }
+      if (k < nk) HY3_ITER(k, a, 0, b);
     }
-    if (k < nk) HY3_ITER(k, a, 0, b);
 
     BigTile nxt;
     int rn = r + nb;
@@ -467,8 +532,12 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
       int tid_n = tid;
       asm volatile("" : "+v"(tid_n));
       big_tile_loads<T, GATE_UP, F8, A8>(a, nxt, tid_n >> 3, tid_n & 7, wb, xb, woff, xoff);
-      HY3_GLOAD(a, 0);
-      HY3_GLOAD(b, (1 < nxt.nk) ? 1 : 0);
+      if constexpr (A8) {
+        HY3_A8_LOAD_ALL(0)
+      } else {
+        HY3_GLOAD(a, 0);
+        HY3_GLOAD(b, (1 < nxt.nk) ? 1 : 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     int tid_e = tid;
@@ -477,11 +546,22 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     __builtin_amdgcn_sched_barrier(0);
     if (!has_next) break;
     __syncthreads();   // the epilogue's LDS reads are done
-    HY3_LSTORE(a, 0);
+    if constexpr (A8) {
+      HY3_A8_STORE_ALL(0)
+      HY3_A8_LOAD_ALL((1 < nxt.nk) ? 1 : 0)
+    } else {
+      HY3_LSTORE(a, 0);
+    }
     __syncthreads();
     cur = nxt;
     r = rn;
   }
+#undef HY3_A8_ITER
+#undef HY3_A8_GROUP
+#undef HY3_A8_STORE_ALL
+#undef HY3_A8_LOAD_ALL
+#undef HY3_A8_STORE
+#undef HY3_A8_LOAD
 #undef HY3_ITER
 #undef HY3_COMPUTE
 #undef HY3_LSTORE
