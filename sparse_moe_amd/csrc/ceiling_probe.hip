@@ -1,12 +1,15 @@
 // Achievable-ceiling probes for the roofline (measurement helpers, not part
-// of the MoE layer): a dense bf16 MFMA microkernel with register operands
-// only, a 16-byte-per-lane device copy, and a 16-byte-per-lane streaming read
-// (the bound of the weight-streaming GEMMs).  Built into libhy3moe_probe.so.
+// of the MoE layer): dense bf16 and FP8 MFMA microkernels with register
+// operands only, a 16-byte-per-lane device copy, a 16-byte-per-lane streaming
+// read (the bound of the weight-streaming GEMMs), and one FP8 MFMA per
+// wavefront on given operands (its accumulation error, measured against
+// exact sums by the caller).  Built into libhy3moe_probe.so.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 
 namespace {
 
@@ -57,9 +60,64 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4 *__restrict__ src
   out[tid] = acc;
 }
 
+// The same with 16x16x128 E4M3 x E4M3 MFMAs (one per chain per iteration).
+__global__ __launch_bounds__(256) void mfma_fp8_peak_kernel(int iters, float *out) {
+  const int lane = threadIdx.x & 63;
+  i32x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = 0x38303830 + ((lane + i) & 7);
+    b[i] = 0x30383038 + ((lane * 3 + i) & 7);
+  }
+  f32x4_t acc[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[c], 0, 0, 0, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// Instance b (one wavefront): D = A B with C = 0, one 16x16x128 FP8 MFMA on
+// the lane operands a[b][lane] and b[b][lane] (32 bytes each).
+__global__ __launch_bounds__(64) void mfma_fp8_once_kernel(const i32x8_t *a, const i32x8_t *b,
+                                                          f32x4_t *d, int n) {
+  const int inst = blockIdx.x, lane = threadIdx.x;
+  if (inst >= n) return;
+  const size_t i = (size_t)inst * 64 + lane;
+  d[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[i], f32x4_t{0.f, 0.f, 0.f, 0.f},
+                                                          0, 0, 0, 0, 0, 0);
+}
+
 }  // namespace
 
 extern "C" {
+
+// FLOPs done = n_blocks * 4 waves * iters * 16 MFMAs * 2*16*16*128.
+// `out` needs n_blocks * 256 floats.  Returns a hipError_t code.
+int hy3moe_probe_mfma_fp8(int n_blocks, int iters, float *out, void *stream) {
+  if (n_blocks <= 0 || iters <= 0 || !out) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_fp8_peak_kernel, dim3(n_blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), iters, out);
+  return (int)hipGetLastError();
+}
+
+// n instances of one FP8 MFMA: a, b hold n x 64 lanes x 32 bytes (E4M3
+// codes), d receives n x 64 lanes x 4 floats (lane 16 c + r: rows 4 c + q,
+// column r).  Lane 16 g + r of a supplies row r and lane 16 g + r of b
+// column r, with the same 32 K positions.
+int hy3moe_probe_mfma_fp8_once(const void *a, const void *b, float *d, int n, void *stream) {
+  if (!a || !b || !d || n <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_fp8_once_kernel, dim3(n), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const i32x8_t *>(a), static_cast<const i32x8_t *>(b),
+                     reinterpret_cast<f32x4_t *>(d), n);
+  return (int)hipGetLastError();
+}
 
 // FLOPs done = n_blocks * 4 waves * iters * 16 MFMAs * 2*16*16*32.
 // `out` needs n_blocks * 256 floats.  Returns a hipError_t code.

@@ -109,6 +109,20 @@ __device__ __forceinline__ uint32_t quant_e4m3x4(float a, float b, float c, floa
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
+// The same with the quotient taken as v * r, r = 1 / s computed once (within
+// a float32 ulp of v / s): the GEMM epilogues quantise h this way, where h
+// itself carries the accumulation's float32 rounding.
+__device__ __forceinline__ uint32_t quant_e4m3x4_rcp(float a, float b, float c, float d,
+                                                     float r) {
+  const float lim = 448.0f;
+  a = fminf(fmaxf(a * r, -lim), lim);
+  b = fminf(fmaxf(b * r, -lim), lim);
+  c = fminf(fmaxf(c * r, -lim), lim);
+  d = fminf(fmaxf(d * r, -lim), lim);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
 // Four codes -> their values as 4 bf16 (exact): the bf16 form in which the
 // bf16-MFMA paths carry quantised activations.
 __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
@@ -116,9 +130,10 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
 }
 #undef HY3_E4M3_PAIR
 
-// SiLU(g) * u in fp32: g / (1 + e^-g) * u.
+// SiLU(g) * u in fp32: g / (1 + e^-g) * u, the quotient by the hardware
+// reciprocal (within an ulp; the result is rounded to bf16 or E4M3 after).
 __device__ __forceinline__ float swiglu(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) {

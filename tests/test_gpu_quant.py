@@ -70,3 +70,106 @@ def test_quantize_e4m3_empty_and_errors(dev):
     assert lib.hy3moe_quantize_e4m3(None, 1, 8, scale.data_ptr(), None, None) == -1
     assert lib.hy3moe_quantize_e4m3(None, 7, 0, None, None, None) == -1
     assert lib.hy3moe_quantize_e4m3(None, 1, -1, None, None, None) == -1
+
+
+def _grid_step(v: np.ndarray) -> np.ndarray:
+    """Spacing of the E4M3 grid at |v| (2^(e-3) in [2^e, 2^(e+1)), 2^-9 below 2^-6)."""
+    a = np.abs(v)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    return np.exp2(np.maximum(ex - 1, -6) - 3.0)
+
+
+@pytest.mark.parametrize("T, E, H, path_rows", [(400, 8, 512, 256), (300, 24, 512, 128),
+                                                (16, 16, 256, None)])
+def test_w8a8_codes_in_the_workspace(dev, T, E, H, path_rows):
+    """The quantised activations the forward leaves in its workspace: x codes
+    bit-exact against the oracle's quantiser; h codes equal to the oracle's
+    wherever the quotient h / a2 lies farther from a rounding midpoint than
+    the GPU's float32 h can be from the oracle's float64 h (an accumulation
+    error bound), and one grid step away at most elsewhere.  Large-tile
+    path: E4M3 bytes; the other paths: their bf16 values."""
+    from gpu_util import a8_of, config_of, expert_cache, shared_f64, to_torch, upload_weights
+    from synth import random_small
+    inp = random_small(50 + T, T=T, H=H, E=E, K=4, I=256, I_shared=128, dtype="bf16",
+                       w_format="fp8_e4m3", act_format="fp8_static")
+    c = inp.cfg
+    cfg = config_of(inp)
+    L = sm.hy3moe_workspace_layout(cfg)
+    if path_rows is not None:
+        assert L.tile_rows == path_rows
+    codes_path = L.tile_rows == 256
+    ws = sm.alloc_workspace(cfg, True, dev)
+    weights = upload_weights(inp, dev)
+    x = to_torch(inp.x(), c.dtype, dev)
+    sm.forward(cfg, x, weights, workspace=ws)
+    torch.cuda.synchronize()
+    wsh = ws.cpu().numpy()
+    a1, a2 = a8_of(inp)
+
+    def values(off, n):   # the stored activations as E4M3 values
+        if codes_path:
+            return oracle.fp8_e4m3_value(wsh[off:off + n])
+        bits = wsh[off:off + 2 * n].view(np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+
+    # x: bit-exact
+    x64 = inp.x_f64()
+    qx = oracle.quant_e4m3(x64, a1)
+    gx = values(L.xq, c.T * c.H).reshape(c.T, c.H)
+    np.testing.assert_array_equal(gx, oracle.fp8_e4m3_value(qx))
+
+    # h: per group, in expert-major row order
+    def i32(off, n):
+        return wsh[off:off + 4 * n].view(np.int32)
+    offsets = i32(L.offsets, c.E + 2)
+    R = c.T * c.K + c.T
+    sorted_token = i32(L.sorted_token, R)
+    ldh = max(c.I, c.I_shared)
+    xh = oracle.quant_dequant_e4m3(x64, a1)
+    experts = expert_cache(inp)
+    shared = shared_f64(inp)
+    n_all = n_near = 0
+    for g in range(c.E + 1):
+        r0, r1 = offsets[g], offsets[g + 1]
+        if r1 == r0:
+            continue
+        wg, wu, _ = experts(g) if g < c.E else shared
+        Ig = wg.shape[0]
+        a = xh[sorted_token[r0:r1]]
+        gg, uu = a @ wg.T, a @ wu.T
+        h64 = oracle.silu(gg) * uu
+        ref = oracle.fp8_e4m3_value(oracle.quant_e4m3(h64, a2[g]))
+        got = np.stack([values(L.h + (r * ldh) * (1 if codes_path else 2), Ig)
+                        for r in range(r0, r1)])
+        # how far the GPU's float32 h can be from h64: the GEMM's error, at
+        # most 1024 ulps (2^-23) of the sum of |products| on the FP8-MFMA
+        # path (measured in test_gpu_mfma_fp8.py; the bf16 MFMAs of the other
+        # paths are far closer), propagated through SiLU(g) u, plus a few
+        # ulps of h for the epilogue's own arithmetic
+        u32 = 2.0 ** -24
+        gemm = (1024 * 2.0 ** -23) if codes_path else 64 * u32
+        dg = gemm * (np.abs(a) @ np.abs(wg).T) + 4 * u32 * np.abs(gg)
+        du = gemm * (np.abs(a) @ np.abs(wu).T) + 4 * u32 * np.abs(uu)
+        sg = oracle.sigmoid(gg)
+        dsilu = np.abs(sg * (1 + gg * (1 - sg)))
+        dh = dsilu * np.abs(uu) * dg + np.abs(gg * sg) * du + 8 * u32 * np.abs(h64)
+        q = np.minimum(np.abs(np.float32(h64) / np.float32(a2[g])).astype(np.float64), 448.0)
+        step = _grid_step(q)
+        frac = q / step
+        near = np.abs(frac - np.floor(frac) - 0.5) * step <= dh / a2[g] + 4 * u32 * q
+        diff = got != ref
+        bad = np.argwhere(diff & ~near)
+        for i, j in bad[:4]:
+            log(f"  group {g} row {i} col {j}: g={gg[i, j]:.9g} u={uu[i, j]:.9g} "
+                f"h={h64[i, j]:.9g} q={q[i, j]:.9g} got={got[i, j]} ref={ref[i, j]} "
+                f"mid_dist={abs(frac[i, j] - np.floor(frac[i, j]) - 0.5) * step[i, j]:.3g} "
+                f"dh/a2={dh[i, j] / a2[g]:.3g} |g|sum={(np.abs(a) @ np.abs(wg).T)[i, j]:.4g} "
+                f"|u|sum={(np.abs(a) @ np.abs(wu).T)[i, j]:.4g}")
+        assert bad.size == 0, f"{bad.shape[0]} codes off beyond the bound in group {g}"
+        big_step = _grid_step(np.maximum(np.abs(got), np.abs(ref)))
+        assert (np.abs(got - ref) <= big_step * (1 + 1e-12)).all()
+        n_all += got.size
+        n_near += int(near.sum())
+    log(f"  T={T}: x codes exact ({c.T * c.H}); h codes {n_all}, "
+        f"{n_near} within the error bound of a midpoint")
+    assert n_near < (0.3 if codes_path else 0.03) * n_all
