@@ -305,8 +305,8 @@ def router_sweep(args, dev):
 
 
 def ceilings(dev):
-    """Achievable ceilings on this GPU: a dense bf16 MFMA microkernel (register
-    operands only, 16 independent chains per wavefront), a 16-byte-per-lane
+    """Achievable ceilings on this GPU: dense bf16 and FP8 MFMA microkernels
+    (register operands only, 16 independent chains per wavefront), a 16-byte-per-lane
     device copy of 4 GiB (read + write bytes counted) and a streaming read of
     the same 4 GiB."""
     import ctypes
@@ -332,6 +332,20 @@ def ceilings(dev):
         ms = e0.elapsed_time(e1)
         flops = blocks * 4 * iters * 16 * 2.0 * 16 * 16 * 32
         res[f"mfma_bf16_tflops_{blocks}blk"] = flops / ms / 1e9
+    L.hy3moe_probe_mfma_fp8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    for blocks in (2048, 4096):
+        iters = 2000
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        assert L.hy3moe_probe_mfma_fp8(blocks, 100, out.data_ptr(), s) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        assert L.hy3moe_probe_mfma_fp8(blocks, iters, out.data_ptr(), s) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        flops = blocks * 4 * iters * 16 * 2.0 * 16 * 16 * 128
+        res[f"mfma_fp8_tflops_{blocks}blk"] = flops / ms / 1e9
     n = 4 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -364,8 +378,10 @@ def ceilings(dev):
         res[f"read_GBs_{blocks}blk"] = gbs
         best = max(best, gbs)
     res["read_GBs_best"] = best
-    res["mfma_bf16_tflops_best"] = max(v for k, v in res.items() if k.startswith("mfma"))
-    res["peak_published"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_GBs": PEAK_HBM_GBS}
+    res["mfma_bf16_tflops_best"] = max(v for k, v in res.items() if k.startswith("mfma_bf16"))
+    res["mfma_fp8_tflops_best"] = max(v for k, v in res.items() if k.startswith("mfma_fp8"))
+    res["peak_published"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "fp8_tflops": PEAK_FP8_TFLOPS,
+                             "hbm_GBs": PEAK_HBM_GBS}
     return res
 
 
