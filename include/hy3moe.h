@@ -217,8 +217,9 @@ int hy3moe_forward(const hy3moe_config *cfg, const void *x, const hy3moe_weights
                    void *workspace, size_t ws_bytes, void *stream);
 
 /* Stages of hy3moe_forward, in launch order: router GEMM, score+select,
- * permutation (histogram, scan + tile list, scatter), gate-up + SwiGLU,
- * down, combine. */
+ * permutation (histogram, scan + tile list, scatter; with act_format
+ * FP8_STATIC preceded by the quantisation of x), gate-up + SwiGLU, down,
+ * combine. */
 #define HY3MOE_N_STAGES 6
 
 /* hy3moe_forward that also records HY3MOE_N_STAGES + 1 caller-created HIP

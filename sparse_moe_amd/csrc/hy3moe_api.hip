@@ -229,7 +229,18 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   if (rc) return rc;
   mark();
 
-  // 3. permutation
+  // 3. permutation (with static FP8 activations, preceded by the
+  // quantisation of x, which needs no routing: once for every gate-up GEMM,
+  // as code bytes for the large-tile path's FP8 MFMAs, else as their bf16
+  // values)
+  const int path = path_of(cfg);
+  const void *act = x;
+  if (a8) {
+    rc = check_launch(launch_quant_e4m3(x, cfg->dtype, (int64_t)T * H, w->x_scale, ws + L.xq,
+                                        path == PATH_BIG ? 0 : 1, s));
+    if (rc) return rc;
+    act = ws + L.xq;
+  }
   PermArgs pa;
   pa.idx = idx;
   pa.hist = reinterpret_cast<int32_t *>(ws + L.hist);
@@ -243,22 +254,12 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   pa.nchunks = L.n_chunks;
   pa.tile_rows = L.tile_rows;
   pa.max_tiles = L.max_tiles;
-  pa.sort_tiles = path_of(cfg) != PATH_SKINNY;
+  pa.sort_tiles = path != PATH_SKINNY;
   rc = check_launch(launch_permute(pa, s));
   if (rc) return rc;
   mark();
 
   // 4-5. grouped experts
-  const int path = path_of(cfg);
-  // Static FP8 activations: x quantised once for every gate-up GEMM, as code
-  // bytes for the large-tile path's FP8 MFMAs, else as their bf16 values.
-  const void *act = x;
-  if (a8) {
-    rc = check_launch(launch_quant_e4m3(x, cfg->dtype, (int64_t)T * H, w->x_scale, ws + L.xq,
-                                        path == PATH_BIG ? 0 : 1, s));
-    if (rc) return rc;
-    act = ws + L.xq;
-  }
   const int Imax = cfg->I > cfg->I_shared ? cfg->I : cfg->I_shared;
   ExpertArgs ea;
   ea.sorted_token = pa.sorted_token;
