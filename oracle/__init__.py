@@ -2,13 +2,15 @@
 imported by tests, the smoke check and the benchmark's CPU-baseline leg,
 never by the product path."""
 from .moe import (E4M3_MAX, ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, dense_masked,
-                  dequant_fp8, forward, forward_given_route, fp8_e4m3_value,
+                  dequant_fp8, dequant_mxfp4, e8m0_value, forward, forward_given_route,
+                  fp4_e2m1_value, fp8_e4m3_value,
                   layer_flops, quant_dequant_e4m3, quant_e4m3, route,
                   route_from_logits, router_logits, sigmoid, silu,
                   softmax_rows, swiglu_expert, topk_desc)
 
 __all__ = [
     "E4M3_MAX", "ROUTE_SIGMOID_BIAS", "ROUTE_SOFTMAX", "Route", "dense_masked", "dequant_fp8",
+    "dequant_mxfp4", "e8m0_value", "fp4_e2m1_value",
     "forward", "forward_given_route", "fp8_e4m3_value", "layer_flops", "quant_dequant_e4m3",
     "quant_e4m3", "route", "route_from_logits",
     "router_logits", "sigmoid", "silu", "softmax_rows", "swiglu_expert", "topk_desc",

@@ -50,6 +50,16 @@ E4M3 as above and one scale per expert matrix is the reading taken here.
 The oracle dequantises exactly (every E4M3 value times a float32 scale is
 exact in float64) and then runs the same float64 layer.
 
+MXFP4 expert weights (the CANN deployment article, section 8.2: routed
+experts W4A8 with W4 = MXFP4; section 五: MXFP4 weights derived from the
+MXFP8 conversion).  OCP microscaling: each block of 32 consecutive weights
+of a row (along the reduction axis) shares one E8M0 scale 2^(s-127), and
+each weight is an FP4 E2M1 code (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 with a
+sign); two codes per byte, the even element in the low nibble (the packing
+order is a reading: the pages do not give one).  Built weight-only
+(W4A16): activations stay bf16, and the oracle runs the float64 layer on
+the exactly dequantised weights.
+
 Static FP8 activations (W8A8; the CANN article, section 8.2 and the FP8
 path of section 六, where an FP8 Linear quantises its input with a static
 per-tensor input scale).  The expert input x is quantised with one float32
@@ -206,6 +216,47 @@ def fp8_e4m3_value(codes: np.ndarray) -> np.ndarray:
 def dequant_fp8(codes: np.ndarray, scale) -> np.ndarray:
     """scale * E4M3 value of every code, in float64 (one scale per matrix)."""
     return np.float64(np.float32(scale)) * fp8_e4m3_value(codes)
+
+
+def fp4_e2m1_value(nibbles: np.ndarray) -> np.ndarray:
+    """Value of OCP FP4 E2M1 codes (4-bit, given as integers 0..15), float64.
+
+    1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit; no infinities or
+    NaN.  Exponent field 0 is subnormal: (m/2) * 2^0; otherwise
+    (1 + m/2) * 2^(e-1).  Magnitudes: 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+    """
+    c = np.asarray(nibbles).astype(np.int64) & 15
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, m / 2.0, (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0))
+    return np.where(c >> 3, -mag, mag)
+
+
+def e8m0_value(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP E8M0 scale codes: 2^(c - 127), float64; 255 is NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c == 255, np.nan, np.exp2(c.astype(np.float64) - 127.0))
+
+
+MX_BLOCK = 32
+
+
+def dequant_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 matrix [rows, K] in float64 from packed E2M1 codes and E8M0 scales.
+
+    packed [rows, K/2] uint8 holds element 2j in the low nibble of byte j and
+    element 2j+1 in the high nibble; scales [rows, K/32] uint8 holds one
+    E8M0 scale per block of 32 consecutive elements of a row (along K).
+    value[r, k] = e8m0(scales[r, k // 32]) * e2m1(element k of row r).
+    """
+    p = np.asarray(packed, dtype=np.uint8)
+    rows, half = p.shape
+    nib = np.empty((rows, 2 * half), dtype=np.int64)
+    nib[:, 0::2] = p & 15
+    nib[:, 1::2] = p >> 4
+    sc = np.repeat(e8m0_value(scales), MX_BLOCK, axis=1)
+    assert sc.shape == nib.shape, (sc.shape, nib.shape)
+    return sc * fp4_e2m1_value(nib)
 
 
 E4M3_MAX = 448.0

@@ -43,6 +43,14 @@ the top binade (up to 448).  Each matrix gets its own float32 scale
 the spread of the bf16 weights.  Nothing here decodes the codes: that is
 the layer's own (de-quantisation) step.
 
+MXFP4 expert weights (``w_format == "mxfp4"``) are drawn as E2M1 codes
+(sign uniform; magnitude 0, 0.5, 1, 1.5, 2, 3, 4, 6 with probabilities
+.08, .17, .20, .17, .14, .12, .08, .04, standard deviation about 2.2),
+packed two per byte (even element in the low nibble), with one E8M0 scale
+per 32 consecutive weights of a row: 2^(round(log2(1 / (2.2 sqrt(fan_in))))
+- j), j uniform in {0, 1}, so scale times value has about the spread of the
+bf16 weights.
+
 Static FP8 activation scales (``act_format == "fp8_static"``, W8A8) stand
 in for calibrated ones: a1 = 4.5 / 448 for the layer input (x ~ N(0, 1):
 about 7 in a million values saturate) and a2[e] = (1 + U(0, 0.25)) * 12 / 448
@@ -60,6 +68,7 @@ import numpy as np
 T_X, T_WR, T_BIAS, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN = range(9)
 T_CODES, T_SCALES = 100, 200     # offsets of the FP8 code and scale streams
 T_ASCALES = 300                  # static FP8 activation scales
+T_FP4, T_MX = 400, 500           # MXFP4 code and E8M0 scale streams
 
 ROUTE_SIGMOID_BIAS = 0
 ROUTE_SOFTMAX = 1
@@ -111,7 +120,7 @@ class MoEConfig:
     scale: float               # router scaling factor applied to routed weights
     renorm_eps: float          # clamp of the renormalisation denominator
     bias_kind: str             # "uniform", "skew" or "none"
-    w_format: str = "dtype"    # expert weights: "dtype" (as `dtype`) or "fp8_e4m3"
+    w_format: str = "dtype"    # expert weights: "dtype" (as `dtype`), "fp8_e4m3" or "mxfp4"
     act_format: str = "dtype"  # expert activations: "dtype" or "fp8_static" (W8A8)
 
     def with_T(self, T: int) -> "MoEConfig":
@@ -163,6 +172,14 @@ CONFIGS: Dict[int, MoEConfig] = {
                  I=1536, I_shared=1536, dtype="bf16",
                  route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                  bias_kind="skew", w_format="fp8_e4m3", act_format="fp8_static"),
+    # Hy3 decode and prefill with MXFP4 experts (bf16 activations).
+    9: MoEConfig("hy3_decode_T16_mxfp4", 9, 9, T=16, H=4096, E=192, K=8, I=1536,
+                 I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                 scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform", w_format="mxfp4"),
+    10: MoEConfig("hy3_prefill_T8192_skew_mxfp4", 10, 9, T=8192, H=4096, E=192, K=8,
+                  I=1536, I_shared=1536, dtype="bf16",
+                  route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
+                  bias_kind="skew", w_format="mxfp4"),
 }
 
 ROUTER_SWEEP_M = (2, 64, 512, 4096)
@@ -191,6 +208,24 @@ def _fp8_codes(rng, shape) -> np.ndarray:
 
 def _fp8_scale(rng, fan_in: int) -> np.float32:
     return np.float32((1.0 + 0.25 * rng.random()) / (74.0 * np.sqrt(fan_in)))
+
+
+_FP4_P = np.array([.08, .17, .20, .17, .14, .12, .08, .04])
+
+
+def _fp4_packed(rng, rows: int, k: int) -> np.ndarray:
+    """[rows, k/2] bytes of E2M1 codes (even element in the low nibble)."""
+    n = rows * k
+    mag = rng.choice(8, size=n, p=_FP4_P).astype(np.uint8)
+    sign = rng.integers(0, 2, n, dtype=np.uint8) << 3
+    c = (mag | sign).reshape(rows, k // 2, 2)
+    return (c[:, :, 0] | (c[:, :, 1] << 4)).astype(np.uint8)
+
+
+def _mx_scales(rng, rows: int, k: int, fan_in: int) -> np.ndarray:
+    """[rows, k/32] E8M0 codes."""
+    base = 127 + int(np.rint(np.log2(1.0 / (2.2 * np.sqrt(fan_in)))))
+    return (base - rng.integers(0, 2, (rows, k // 32))).astype(np.uint8)
 
 
 def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
@@ -264,7 +299,7 @@ class MoEInputs:
         """(gate [I,H], up [I,H], down [H,I]) of routed expert ``e``, stored dtype."""
         c = self.cfg
         if c.w_format != "dtype":
-            raise ValueError("FP8 expert weights: use expert_fp8()")
+            raise ValueError("quantised expert weights: use expert_fp8() or expert_mxfp4()")
         mk = c.model_key
         g = _normal_f32(_rng(self.seed, mk, T_GATE, e), (c.I, c.H), 1.0 / np.sqrt(c.H))
         u = _normal_f32(_rng(self.seed, mk, T_UP, e), (c.I, c.H), 1.0 / np.sqrt(c.H))
@@ -276,7 +311,7 @@ class MoEInputs:
         if c.I_shared == 0:
             return None
         if c.w_format != "dtype":
-            raise ValueError("FP8 expert weights: use shared_fp8()")
+            raise ValueError("quantised expert weights: use shared_fp8() or shared_mxfp4()")
         k = ("shared",)
         if k not in self._cache:
             mk, Is = c.model_key, c.I_shared
@@ -345,6 +380,54 @@ class MoEInputs:
         with ThreadPoolExecutor(threads or _default_threads()) as ex:
             list(ex.map(job, range(c.E)))
         return wg, wu, wd, sc
+
+    # ---- MXFP4 expert weights (w_format == "mxfp4") ----
+    def expert_mxfp4(self, e: int):
+        """((gate, up, down) packed codes, (gate, up, down) E8M0 scales) of expert e."""
+        c = self.cfg
+        mk = c.model_key
+        shapes = ((c.I, c.H), (c.I, c.H), (c.H, c.I))
+        ids = (T_GATE, T_UP, T_DOWN)
+        codes = tuple(_fp4_packed(_rng(self.seed, mk, T_FP4 + t, e), *sh)
+                      for t, sh in zip(ids, shapes))
+        scales = tuple(_mx_scales(_rng(self.seed, mk, T_MX + t, e), sh[0], sh[1], sh[1])
+                       for t, sh in zip(ids, shapes))
+        return codes, scales
+
+    def shared_mxfp4(self):
+        c = self.cfg
+        if c.I_shared == 0:
+            return None
+        k = ("shared_mxfp4",)
+        if k not in self._cache:
+            mk, Is = c.model_key, c.I_shared
+            shapes = ((Is, c.H), (Is, c.H), (c.H, Is))
+            ids = (T_SGATE, T_SUP, T_SDOWN)
+            codes = tuple(_fp4_packed(_rng(self.seed, mk, T_FP4 + t), *sh)
+                          for t, sh in zip(ids, shapes))
+            scales = tuple(_mx_scales(_rng(self.seed, mk, T_MX + t), sh[0], sh[1], sh[1])
+                           for t, sh in zip(ids, shapes))
+            self._cache[k] = (codes, scales)
+        return self._cache[k]
+
+    def stacked_experts_mxfp4(self, threads: Optional[int] = None):
+        """Packed codes gate/up [E,I,H/2], down [E,H,I/2] and E8M0 scales
+        gate/up [E,I,H/32], down [E,H,I/32] (uint8)."""
+        c = self.cfg
+        wg = np.empty((c.E, c.I, c.H // 2), dtype=np.uint8)
+        wu = np.empty_like(wg)
+        wd = np.empty((c.E, c.H, c.I // 2), dtype=np.uint8)
+        sg = np.empty((c.E, c.I, c.H // 32), dtype=np.uint8)
+        su = np.empty_like(sg)
+        sd = np.empty((c.E, c.H, c.I // 32), dtype=np.uint8)
+
+        def job(e):
+            (g, u, d), (a, b2, dd) = self.expert_mxfp4(e)
+            wg[e], wu[e], wd[e], sg[e], su[e], sd[e] = g, u, d, a, b2, dd
+
+        with ThreadPoolExecutor(threads or _default_threads()) as ex:
+            list(ex.map(job, range(c.E)))
+        return wg, wu, wd, sg, su, sd
 
     def act_scales(self):
         """Static FP8 activation scales: (a1 float32, a2 float32 [E + 1])."""

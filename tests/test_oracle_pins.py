@@ -541,3 +541,66 @@ def test_w8a8_layer_is_within_the_quantisation_error_of_w8a16():
     got = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared, a8=a8)
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert 0.005 < rel < 0.08, rel
+
+
+# --------------------------------------------------------------------------
+# MXFP4 expert weights: E2M1 codes with E8M0 block scales
+# --------------------------------------------------------------------------
+# OCP Microscaling Formats v1.0, FP4 E2M1 table: codes 0..7 and their values
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_table():
+    v = oracle.fp4_e2m1_value(np.arange(16))
+    np.testing.assert_array_equal(v[:8], E2M1_TABLE)
+    np.testing.assert_array_equal(v[8:], [-x for x in E2M1_TABLE])
+    assert np.signbit(v[8])                        # code 8 is -0
+
+
+def test_e8m0_matches_torch_for_every_code():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    with np.errstate(invalid="ignore"):                   # code 255 is NaN
+        ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).float().numpy()
+    ref = ref.astype(np.float64)
+    got = oracle.e8m0_value(codes)
+    np.testing.assert_array_equal(got[:255], ref[:255])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert got[127] == 1.0 and got[128] == 2.0 and got[120] == 2.0 ** -7
+
+
+def test_mxfp4_dequant_packing_and_blocks():
+    """Even element in the low nibble; one scale per 32 consecutive elements."""
+    packed = np.zeros((2, 32), dtype=np.uint8)          # 2 rows, K = 64
+    packed[0, 0] = 0x7A                                  # el 0 = code 0xA (-1), el 1 = 7 (6)
+    packed[0, 15] = 0x30                                 # el 31 = code 3 (1.5)
+    packed[0, 16] = 0x05                                 # el 32 = code 5 (3)
+    packed[1, 31] = 0xF0                                 # el 63 = code 0xF (-6)
+    scales = np.array([[127, 129], [120, 121]], dtype=np.uint8)
+    d = oracle.dequant_mxfp4(packed, scales)
+    assert d.shape == (2, 64)
+    assert d[0, 0] == -1.0 and d[0, 1] == 6.0 and d[0, 31] == 1.5
+    assert d[0, 32] == 3.0 * 4.0                          # second block: scale 2^2
+    assert d[1, 63] == -6.0 * 2.0 ** -6
+    assert (d[0, 2:31] == 0).all() and (d[1, :63] == 0).all()
+
+
+def test_mxfp4_layer_equals_layer_on_dequantised_weights():
+    """An E8M0 scale code one higher on every block of a down matrix doubles
+    that expert's routed output exactly (the layer runs on scale * value)."""
+    inp = random_small(61, 6, 64, 4, 2, 32, 32, dtype="bf16", w_format="mxfp4")
+    c = inp.cfg
+    x = inp.x_f64()
+    deq = {}
+    for e in range(c.E):
+        codes, sc = inp.expert_mxfp4(e)
+        deq[e] = tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(codes, sc))
+    r = oracle.route(x, inp.w_router().astype(np.float64), c.K, 0,
+                     inp.bias().astype(np.float64), c.scale)
+    out = oracle.forward_given_route(x, r.idx, r.weight, lambda e: deq[e], c.E)
+    up1 = {}
+    for e in range(c.E):
+        codes, sc = inp.expert_mxfp4(e)
+        up1[e] = (deq[e][0], deq[e][1], oracle.dequant_mxfp4(codes[2], sc[2] + 1))
+    out2 = oracle.forward_given_route(x, r.idx, r.weight, lambda e: up1[e], c.E)
+    np.testing.assert_array_equal(out2, 2.0 * out)

@@ -109,3 +109,20 @@ def test_static_activation_scales():
     # one model: the decode and prefill W8A8 workloads share the scales
     np.testing.assert_array_equal(MoEInputs(CONFIGS[7]).act_scales()[1], a2)
     assert CONFIGS[7].act_format == CONFIGS[8].act_format == "fp8_static"
+
+
+def test_mxfp4_codes_and_scales():
+    inp = MoEInputs(CONFIGS[9].with_(H=256, I=128, I_shared=128, E=4))
+    (g, u, d), (sg, su, sd) = inp.expert_mxfp4(1)
+    assert g.shape == (128, 128) and d.shape == (256, 64) and g.dtype == np.uint8
+    assert sg.shape == (128, 8) and sd.shape == (256, 4)
+    import oracle
+    wg = oracle.dequant_mxfp4(g, sg)
+    # about the spread of the bf16 weights (std 1/sqrt(fan_in)), no NaN
+    assert 0.5 / np.sqrt(256) < wg.std() < 1.5 / np.sqrt(256)
+    assert np.isfinite(wg).all()
+    # deterministic, and the stacked form holds the same bytes
+    np.testing.assert_array_equal(inp.expert_mxfp4(1)[0][0], g)
+    st = inp.stacked_experts_mxfp4(threads=2)
+    np.testing.assert_array_equal(st[0][1], g)
+    np.testing.assert_array_equal(st[5][1], sd)
