@@ -562,7 +562,7 @@ def test_e8m0_matches_torch_for_every_code():
     codes = np.arange(256, dtype=np.uint8)
     with np.errstate(invalid="ignore"):                   # code 255 is NaN
         ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).float().numpy()
-    ref = ref.astype(np.float64)
+        ref = ref.astype(np.float64)
     got = oracle.e8m0_value(codes)
     np.testing.assert_array_equal(got[:255], ref[:255])
     assert np.isnan(got[255]) and np.isnan(ref[255])
