@@ -33,7 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4, "decode_fp8": 5, "prefill_fp8": 6,
-             "decode_w8a8": 7, "prefill_w8a8": 8}
+             "decode_w8a8": 7, "prefill_w8a8": 8, "decode_mxfp4": 9}
 ROUTER_WORKLOAD = 3            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
@@ -181,7 +181,8 @@ def main():
 
     # ---- algorithmic work ----
     eb = 2 if c.dtype == "bf16" else 4
-    web = 1 if c.w_format == "fp8_e4m3" else eb      # bytes per expert weight element
+    # bytes per expert weight element (MXFP4: half a byte + one scale byte per 32)
+    web = {"fp8_e4m3": 1, "mxfp4": 0.5 + 1 / 32}.get(c.w_format, eb)
     tile_rows = sm.hy3moe_workspace_layout(cfg).tile_rows
     # static FP8 activations: E4M3 bytes on the large-tile path (FP8 MFMAs),
     # their bf16 values on the others
@@ -203,10 +204,10 @@ def main():
     gu_s = stage_ms["gate_up"] / 1e3
     decode = args.workload.startswith("decode")
     if decode:
-        kind = "FP8 E4M3" if web == 1 else c.dtype
+        kind = {"fp8_e4m3": "FP8 E4M3", "mxfp4": "MXFP4"}.get(c.w_format, c.dtype)
         roof = {"kernel": "gate_up (weight-streaming grouped GEMM + SwiGLU)", "bound": "hbm",
                 "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "per_unit": f"{2 * I * H * web} B of {kind} gate+up weights per touched "
+                "per_unit": f"{2 * I * H * web:.0f} B of {kind} gate+up weights per touched "
                             f"expert x {groups} experts + x and h rows"}
     else:
         path = "256x256-tile" if tile_rows == 256 else "128x128-tile"
@@ -252,7 +253,7 @@ def main():
         "data": "synthetic (seeded, random-init weights of the layer's shapes)",
         "config": {"workload": c.name, "T": T, "H": H, "E": E, "K": K, "I": I, "I_shared": Is,
                    "route": "sigmoid+bias" if c.route_mode == 0 else "softmax",
-                   "expert_weights": "fp8_e4m3" if web == 1 else c.dtype,
+                   "expert_weights": c.w_format if c.w_format != "dtype" else c.dtype,
                    "expert_activations": ("fp8_e4m3_static" if c.act_format == "fp8_static"
                                           else c.dtype)},
         "roofline": roof, "cpu_baseline": cpu, "layer": layer,
@@ -407,7 +408,14 @@ def cpu_baseline(inp, args, gpu_idx):
     b64 = None if b is None else b.astype(np.float64)
     need = sorted(set(gpu_idx[tokens].reshape(-1).tolist()))
     t0 = time.time()
-    if c.w_format == "fp8_e4m3":      # the oracle's own dequantisation of the codes
+    if c.w_format == "mxfp4":         # the oracle's own dequantisation of the codes
+        def expert_f64(e):
+            codes, sc = inp.expert_mxfp4(e)
+            return tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(codes, sc))
+        shf = inp.shared_mxfp4()
+        sh = None if shf is None else tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(*shf))
+    elif c.w_format == "fp8_e4m3":
+        # the oracle's own dequantisation of the codes
         def expert_f64(e):
             codes, sc = inp.expert_fp8(e)
             return tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))

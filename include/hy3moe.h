@@ -86,6 +86,17 @@ extern "C" {
  * the tile paths, which decode each chunk on its way into LDS. */
 #define HY3MOE_WFMT_DTYPE    0
 #define HY3MOE_WFMT_FP8_E4M3 1
+/* MXFP4 (OCP microscaling; the CANN deployment article, section 8.2: routed
+ * experts W4 = MXFP4): each expert tensor holds FP4 E2M1 codes (sign, 2
+ * exponent bits with bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6),
+ * two per byte with the even element in the low nibble, rows of K/2 bytes;
+ * every block of 32 consecutive weights of a row (along K) has one E8M0
+ * scale 2^(s - 127) in the matching *_mx array.  Activations stay bfloat16
+ * (cfg.dtype HY3MOE_BF16, act_format DTYPE); H, I and I_shared must be
+ * multiples of 128.  The GEMMs decode the codes with their scale exactly to
+ * bfloat16.  Weight-streaming batches (T <= 64) only for now: larger T gives
+ * HY3MOE_ERR_UNSUPPORTED. */
+#define HY3MOE_WFMT_MXFP4    2
 
 /* Activations of the expert GEMMs.  DTYPE: x and h as cfg.dtype.
  * FP8_STATIC (W8A8; needs w_format FP8_E4M3): static per-tensor FP8
@@ -134,7 +145,13 @@ typedef struct hy3moe_config {
  *   x_scale [1]      fp32: static scale of the experts' input x
  *   h_scale [E + 1]  fp32: static scale of each routed expert's h, then the
  *                    shared expert's (entry E read only if I_shared > 0)
- * are required (4-byte aligned); ignored otherwise. */
+ * are required (4-byte aligned); ignored otherwise.  With w_format MXFP4 the
+ * six expert tensors hold packed E2M1 codes (gate/up [E, I, H/2], down
+ * [E, H, I/2], shared [I_shared, H/2] / [H, I_shared/2]) and
+ *   w_gate_mx, w_up_mx [E, I, H/32], w_down_mx [E, H, I/32]   E8M0 bytes
+ *   ws_gate_mx, ws_up_mx [I_shared, H/32], ws_down_mx [H, I_shared/32]
+ * are required (NULL only for the shared ones when I_shared == 0); the
+ * float scale pointers are then ignored. */
 typedef struct hy3moe_weights {
   const float *w_router;
   const float *expert_bias;
@@ -150,6 +167,12 @@ typedef struct hy3moe_weights {
   const float *ws_scale;
   const float *x_scale;
   const float *h_scale;
+  const uint8_t *w_gate_mx;
+  const uint8_t *w_up_mx;
+  const uint8_t *w_down_mx;
+  const uint8_t *ws_gate_mx;
+  const uint8_t *ws_up_mx;
+  const uint8_t *ws_down_mx;
 } hy3moe_weights;
 
 /* Byte offsets of the intermediate buffers inside a forward workspace (for

@@ -24,11 +24,12 @@ HY3MOE_ROUTER_FP32 = 0
 HY3MOE_ROUTER_SPLIT2_BF16 = 1
 HY3MOE_WFMT_DTYPE = 0
 HY3MOE_WFMT_FP8_E4M3 = 1
+HY3MOE_WFMT_MXFP4 = 2
 HY3MOE_AFMT_DTYPE = 0
 HY3MOE_AFMT_FP8_STATIC = 1
 
 HY3MOE_N_STAGES = 6
-ABI_VERSION = 4          # hy3moe_abi_version() of the library this binding matches
+ABI_VERSION = 5          # hy3moe_abi_version() of the library this binding matches
 STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 
 EXPORTED_SYMBOLS = (
@@ -51,7 +52,8 @@ class hy3moe_config(ctypes.Structure):
 
 WEIGHT_NAMES = ("w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up",
                 "ws_down", "w_gate_scale", "w_up_scale", "w_down_scale", "ws_scale",
-                "x_scale", "h_scale")
+                "x_scale", "h_scale", "w_gate_mx", "w_up_mx", "w_down_mx", "ws_gate_mx",
+                "ws_up_mx", "ws_down_mx")
 
 
 class hy3moe_weights(ctypes.Structure):
@@ -141,8 +143,9 @@ def make_config(T: int, H: int, E: int, K: int, I: int, I_shared: int, dtype: st
                          dtype=HY3MOE_BF16 if dtype == "bf16" else HY3MOE_F32,
                          route_mode=int(route_mode), router_prec=int(router_prec),
                          scale=float(scale), renorm_eps=float(renorm_eps),
-                         w_format=(HY3MOE_WFMT_FP8_E4M3 if w_format == "fp8_e4m3"
-                                   else HY3MOE_WFMT_DTYPE),
+                         w_format={"fp8_e4m3": HY3MOE_WFMT_FP8_E4M3,
+                                   "mxfp4": HY3MOE_WFMT_MXFP4}.get(w_format,
+                                                                   HY3MOE_WFMT_DTYPE),
                          act_format=(HY3MOE_AFMT_FP8_STATIC if act_format == "fp8_static"
                                      else HY3MOE_AFMT_DTYPE))
 

@@ -130,6 +130,21 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
 }
 #undef HY3_E4M3_PAIR
 
+// E8M0 scale code -> float 2^(c - 127) (c = 0: the float32 subnormal 2^-127;
+// c = 255, NaN in E8M0, is not expected).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  return c ? __uint_as_float(c << 23) : __uint_as_float(0x00400000u);
+}
+// 8 FP4 E2M1 codes (4 bytes, element 2j in the low nibble of byte j) times a
+// float scale -> 8 bf16 (exact for scales down to 2^-124).
+#define HY3_FP4_PAIR(w, sc, b) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((w), (sc), (b)))
+__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, float sc) {
+  return make_uint4(HY3_FP4_PAIR(w, sc, 0), HY3_FP4_PAIR(w, sc, 1), HY3_FP4_PAIR(w, sc, 2),
+                    HY3_FP4_PAIR(w, sc, 3));
+}
+#undef HY3_FP4_PAIR
+
 // SiLU(g) * u in fp32: g / (1 + e^-g) * u, the quotient by the hardware
 // reciprocal (within an ulp; the result is rounded to bf16 or E4M3 after).
 __device__ __forceinline__ float swiglu(float g, float u) {

@@ -39,10 +39,16 @@ int validate_cfg(const hy3moe_config *c) {
   if (c->T > (int64_t(1) << 24)) return HY3MOE_ERR_UNSUPPORTED;
   if (c->router_prec == HY3MOE_ROUTER_SPLIT2_BF16 && c->dtype != HY3MOE_BF16)
     return HY3MOE_ERR_UNSUPPORTED;
-  if (c->w_format != HY3MOE_WFMT_DTYPE && c->w_format != HY3MOE_WFMT_FP8_E4M3)
+  if (c->w_format != HY3MOE_WFMT_DTYPE && c->w_format != HY3MOE_WFMT_FP8_E4M3 &&
+      c->w_format != HY3MOE_WFMT_MXFP4)
     return HY3MOE_ERR_INVALID;
-  // FP8 expert weights need bf16 activations.
-  if (c->w_format == HY3MOE_WFMT_FP8_E4M3 && c->dtype != HY3MOE_BF16)
+  // FP8 and MXFP4 expert weights need bf16 activations.
+  if (c->w_format != HY3MOE_WFMT_DTYPE && c->dtype != HY3MOE_BF16)
+    return HY3MOE_ERR_UNSUPPORTED;
+  // MXFP4: 128 K values per 64-byte step of a weight row; weight-streaming
+  // batches only.
+  if (c->w_format == HY3MOE_WFMT_MXFP4 &&
+      (c->H % 128 || c->I % 128 || c->I_shared % 128 || c->T > SKINNY_MAX_T))
     return HY3MOE_ERR_UNSUPPORTED;
   if (c->act_format != HY3MOE_AFMT_DTYPE && c->act_format != HY3MOE_AFMT_FP8_STATIC)
     return HY3MOE_ERR_INVALID;
@@ -115,7 +121,7 @@ int check_launch(hipError_t e) { return e == hipSuccess ? HY3MOE_OK : HY3MOE_ERR
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 4; }
+int hy3moe_abi_version(void) { return 5; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {
@@ -193,6 +199,15 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
       return HY3MOE_ERR_INVALID;
     if (!al4(w->w_gate_scale) || !al4(w->w_up_scale) || !al4(w->w_down_scale) ||
         (has_shared && !al4(w->ws_scale)))
+      return HY3MOE_ERR_ALIGN;
+  }
+  const bool fp4 = cfg->w_format == HY3MOE_WFMT_MXFP4;
+  if (fp4) {
+    if (!w->w_gate_mx || !w->w_up_mx || !w->w_down_mx ||
+        (has_shared && (!w->ws_gate_mx || !w->ws_up_mx || !w->ws_down_mx)))
+      return HY3MOE_ERR_INVALID;
+    if (!al4(w->w_gate_mx) || !al4(w->w_up_mx) || !al4(w->w_down_mx) ||
+        (has_shared && (!al4(w->ws_gate_mx) || !al4(w->ws_up_mx) || !al4(w->ws_down_mx))))
       return HY3MOE_ERR_ALIGN;
   }
   const bool a8 = cfg->act_format == HY3MOE_AFMT_FP8_STATIC;
@@ -277,6 +292,11 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.a8 = a8 ? 1 : 0;
   ea.xs = a8 ? w->x_scale : nullptr;
   ea.hs = a8 ? w->h_scale : nullptr;
+  ea.w_fp4 = fp4 ? 1 : 0;
+  ea.mx0 = fp4 ? w->w_gate_mx : nullptr;
+  ea.mx1 = fp4 ? w->w_up_mx : nullptr;
+  ea.mxs0 = fp4 && has_shared ? w->ws_gate_mx : nullptr;
+  ea.mxs1 = fp4 && has_shared ? w->ws_up_mx : nullptr;
   rc = check_launch(launch_gate_up(ea, cfg->dtype, T, path, s));
   if (rc) return rc;
   mark();
@@ -286,6 +306,10 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.sc1 = nullptr;
   ea.ssc0 = fp8 && has_shared ? w->ws_scale + 2 : nullptr;
   ea.ssc1 = nullptr;
+  ea.mx0 = fp4 ? w->w_down_mx : nullptr;
+  ea.mx1 = nullptr;
+  ea.mxs0 = fp4 && has_shared ? w->ws_down_mx : nullptr;
+  ea.mxs1 = nullptr;
   rc = check_launch(launch_down(ea, cfg->dtype, T, path, s));
   if (rc) return rc;
   mark();

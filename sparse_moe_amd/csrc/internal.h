@@ -8,6 +8,8 @@
 namespace hy3moe {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
+// Storage of the expert weights inside the GEMM kernels.
+enum { WF_DTYPE = 0, WF_FP8 = 1, WF_MXFP4 = 2 };
 
 // Row-tile shapes of the expert GEMMs.
 constexpr int TILED_ROWS = 128;     // rows (token copies) per tile, large-T path
@@ -76,6 +78,11 @@ struct ExpertArgs {
   // and *ssc0 / *ssc1 for the shared expert (gate-up: gate, up; down: down).
   int w_fp8;
   const float *sc0, *sc1, *ssc0, *ssc1;
+  // MXFP4 expert weights (w_fp4 = 1): w0/w1/ws0/ws1 hold E2M1 codes, two per
+  // byte (rows of K/2 bytes), and mx0/mx1 (routed, [E][rows][K/32]) and
+  // mxs0/mxs1 (shared, [rows][K/32]) one E8M0 scale per 32 weights of a row.
+  int w_fp4;
+  const uint8_t *mx0, *mx1, *mxs0, *mxs1;
   // Static FP8 activations (a8 = 1, with w_fp8): act holds E4M3 codes on the
   // large-tile path and their exact bf16 values on the other two; *xs is the
   // scale of x and hs[g] that of group g's h (hs[E]: shared).  The gate-up

@@ -26,6 +26,13 @@
 // bytes of each token row; the two MFMAs of a step pair them up.  The scale
 // multiplies the float32 accumulators before SwiGLU / the store.  Half the
 // weight bytes per K value is the point: this path is bound by them.
+//
+// MXFP4 weights (E2M1 codes, two per byte, one E8M0 scale per 32 weights of
+// a row): a 64-byte step holds 128 K values.  Lane (r16, g) loads bytes
+// [16g, 16g + 16), K values 32g + [0, 32) -- exactly one scale block, whose
+// scale byte it also loads -- and decodes them, scale applied, to four bf16
+// fragments (v_cvt_scalef32_pk_bf16_fp4, exact); the token rows supply the
+// matching 64 bytes, and four MFMAs per weight fragment take a step.
 #include "common.cuh"
 #include "internal.h"
 
@@ -37,10 +44,18 @@ constexpr int UBASE = 8;          // 64-byte K steps per register set (one row f
 constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
 
 // 64-byte steps per register set: bf16 weights UBASE / MT; FP8 weights 6 / 3
-// / 1 for 1 / 2 / 4 row fragments (each step also holds two token chunks).
-template <int MT, bool F8>
+// / 1 for 1 / 2 / 4 row fragments (each step also holds two token chunks);
+// MXFP4 3 / 2 / 1 (four token chunks per step).
+template <int MT, int WF>
 constexpr int steps_per_set() {
-  return F8 ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1)) : UBASE / MT;
+  return WF == WF_FP8     ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1))
+         : WF == WF_MXFP4 ? (MT == 1 ? 3 : (MT == 2 ? 2 : 1))
+                          : UBASE / MT;
+}
+// 16-byte token chunks per 64-byte weight step.
+template <int WF>
+constexpr int token_chunks() {
+  return WF == WF_MXFP4 ? 4 : (WF == WF_FP8 ? 2 : 1);
 }
 
 // Where a unit's operands are (per lane) and what its epilogue needs.
@@ -48,6 +63,7 @@ template <int MT>
 struct UnitSrc {
   const char *w0p, *w1p;   // the two 16-row weight fragments (gate/up, or two down blocks)
   const char *xp[MT];      // token rows (gathered x for gate-up, h rows for down)
+  const uint8_t *s0p, *s1p;  // MXFP4: the lane's scale bytes of the two fragments
   int nsub;                // 64-byte K steps per row
   int nf;                  // fragments streamed (2; 1 for half of a down unit)
 };
@@ -61,11 +77,13 @@ struct UnitOut {
 // Unit u (tile u / n_col_blocks, column block u % n_col_blocks) of this
 // kernel; returns false if the column block lies past the group's width.
 // half = 1 or 2: only the first or the second 16-row fragment of a down unit.
-template <typename T, bool GATE_UP, int MT, bool F8>
+template <typename T, bool GATE_UP, int MT, int WF>
 __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_blocks, int lane,
                                         UnitSrc<MT> &src, UnitOut &o, int half = 0) {
+  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4;
   constexpr int EB = Elem<T>::kBytes;
-  constexpr int WB = F8 ? 1 : EB;           // bytes per weight element
+  // bytes per weight row of K elements (MXFP4: half a byte per element)
+  auto rowb = [](int K) { return F4 ? K / 2 : K * (F8 ? 1 : EB); };
   const int tile = u / n_col_blocks, cb = u - tile * n_col_blocks;
   const int g = a.tiles[2 * tile];
   o.row0 = a.tiles[2 * tile + 1];
@@ -73,7 +91,7 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
   const bool shared = (g == a.E);
   const int Ig = shared ? a.I_shared : a.I;
   o.col0 = cb * (GATE_UP ? 16 : 32) + (half == 2 ? 16 : 0);
-  o.nsub = (GATE_UP ? a.H : Ig) * WB / 64;
+  o.nsub = rowb(GATE_UP ? a.H : Ig) / 64;
   o.nf = half ? 1 : 2;
   if (o.col0 >= (GATE_UP ? Ig : a.H)) return false;
   src.nsub = o.nsub;
@@ -81,18 +99,31 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
   const int r16 = lane & 15, cg = lane >> 4;
   if (GATE_UP) {
     const char *gate = shared ? static_cast<const char *>(a.ws0)
-                              : static_cast<const char *>(a.w0) + (size_t)g * a.I * a.H * WB;
+                              : static_cast<const char *>(a.w0) + (size_t)g * a.I * rowb(a.H);
     const char *up = shared ? static_cast<const char *>(a.ws1)
-                            : static_cast<const char *>(a.w1) + (size_t)g * a.I * a.H * WB;
-    src.w0p = gate + (size_t)(o.col0 + r16) * a.H * WB + cg * 16;
-    src.w1p = up + (size_t)(o.col0 + r16) * a.H * WB + cg * 16;
+                            : static_cast<const char *>(a.w1) + (size_t)g * a.I * rowb(a.H);
+    src.w0p = gate + (size_t)(o.col0 + r16) * rowb(a.H) + cg * 16;
+    src.w1p = up + (size_t)(o.col0 + r16) * rowb(a.H) + cg * 16;
+    if (F4) {   // scale rows of H / 32 bytes; the lane's block is step * 4 + cg
+      const int sr = a.H / 32;
+      const uint8_t *sg = shared ? a.mxs0 : a.mx0 + (size_t)g * a.I * sr;
+      const uint8_t *su = shared ? a.mxs1 : a.mx1 + (size_t)g * a.I * sr;
+      src.s0p = sg + (size_t)(o.col0 + r16) * sr + cg;
+      src.s1p = su + (size_t)(o.col0 + r16) * sr + cg;
+    }
   } else {
     const char *dn = shared ? static_cast<const char *>(a.ws0)
-                            : static_cast<const char *>(a.w0) + (size_t)g * a.H * a.I * WB;
+                            : static_cast<const char *>(a.w0) + (size_t)g * a.H * rowb(a.I);
     const int n0 = (o.col0 + r16 < a.H) ? o.col0 + r16 : o.col0;
     const int n1 = (o.col0 + 16 + r16 < a.H) ? o.col0 + 16 + r16 : o.col0;
-    src.w0p = dn + (size_t)n0 * Ig * WB + cg * 16;
-    src.w1p = dn + (size_t)n1 * Ig * WB + cg * 16;
+    src.w0p = dn + (size_t)n0 * rowb(Ig) + cg * 16;
+    src.w1p = dn + (size_t)n1 * rowb(Ig) + cg * 16;
+    if (F4) {
+      const int sr = Ig / 32;
+      const uint8_t *sd = shared ? a.mxs0 : a.mx0 + (size_t)g * a.H * (a.I / 32);
+      src.s0p = sd + (size_t)n0 * sr + cg;
+      src.s1p = sd + (size_t)n1 * sr + cg;
+    }
   }
   if (F8) {
     o.sc0 = shared ? *a.ssc0 : a.sc0[g];
@@ -111,8 +142,9 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
     if (trow >= o.grp_end) trow = o.row0;
     const size_t arow = GATE_UP ? (size_t)a.sorted_token[trow] * a.H : (size_t)trow * a.ldh;
     // bf16 weights: chunk g of each 64-byte step; FP8: bytes [32g, 32g+32) of
-    // each 128-byte step of the token row (the K values of the lane's codes)
-    src.xp[m] = reinterpret_cast<const char *>(act + arow) + cg * (F8 ? 32 : 16);
+    // each 128-byte step of the token row; MXFP4: bytes [64g, 64g+64) of each
+    // 256-byte step (the K values of the lane's codes)
+    src.xp[m] = reinterpret_cast<const char *>(act + arow) + cg * 16 * token_chunks<WF>();
   }
   return true;
 }
@@ -122,7 +154,7 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
 // of them is split into its two 16-row fragments for twice as many
 // wavefronts, so the last round costs half a unit.  Returns the item index
 // (kmax when there is none) and fills src / o.
-template <typename T, bool GATE_UP, int MT, bool F8>
+template <typename T, bool GATE_UP, int MT, int WF>
 __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int nw, int n_units,
                                          int n_col_blocks, int lane, UnitSrc<MT> &src,
                                          UnitOut &o) {
@@ -133,10 +165,10 @@ __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int 
     if (k < full || !split) {
       const int u = w + k * nw;
       if (u >= n_units) return kmax;
-      if (unit_of<T, GATE_UP, MT, F8>(a, u, n_col_blocks, lane, src, o)) return k;
+      if (unit_of<T, GATE_UP, MT, WF>(a, u, n_col_blocks, lane, src, o)) return k;
     } else {
       if (w >= 2 * tail) return kmax;
-      if (unit_of<T, GATE_UP, MT, F8>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
+      if (unit_of<T, GATE_UP, MT, WF>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
                                       1 + (w & 1)))
         return k;
     }
@@ -144,9 +176,10 @@ __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int 
   return kmax;
 }
 
-template <typename T, bool GATE_UP, int MT, bool F8>
+template <typename T, bool GATE_UP, int MT, int WF>
 __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut &o,
                                               f32x4_t (&acc)[2][MT], int lane) {
+  constexpr bool F8 = WF == WF_FP8;
   const float s0 = F8 ? o.sc0 : 1.0f, s1 = F8 ? o.sc1 : 1.0f;
   const int r16 = lane & 15, cg = lane >> 4;
   // Lane holds D[col 4cg + q][token row 16m + r16].
@@ -177,11 +210,12 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
   }
 }
 
-template <typename T, bool GATE_UP, int MT, bool F8>
+template <typename T, bool GATE_UP, int MT, int WF>
 __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(ExpertArgs a,
                                                                           int n_col_blocks) {
-  constexpr int U = steps_per_set<MT, F8>();   // 64-byte K steps per row per register set
-  constexpr int XN = F8 ? 2 : 1;               // 16-byte token chunks per step
+  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4;
+  constexpr int U = steps_per_set<MT, WF>();   // 64-byte K steps per row per register set
+  constexpr int XN = token_chunks<WF>();       // 16-byte token chunks per step
   const int lane = threadIdx.x & 63;
   // The wavefront index is uniform; readfirstlane makes that visible to the
   // compiler, so every unit-dependent guard below is a scalar branch.  (An
@@ -195,7 +229,7 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   // units of one expert spread over all XCDs and HBM channels.
   UnitSrc<MT> src;    // item whose blocks are being loaded
   UnitOut om, ol;     // item being multiplied, item being loaded
-  int k_ld = next_item<T, GATE_UP, MT, F8>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
+  int k_ld = next_item<T, GATE_UP, MT, WF>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
   if (k_ld >= kmax) return;
   int k_mm = k_ld;
   om = ol;
@@ -209,34 +243,56 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
 
   uint4 aw0[U], aw1[U], ax[U][MT][XN];
   uint4 bw0[U], bw1[U], bx[U][MT][XN];
+  uint32_t as0[U], as1[U], bs0[U], bs1[U];   // MXFP4: the lane's block scale codes
   // Load the next block of the loading unit into set W0/W1/X, then move the
   // loading position on (to the next unit at the end of this one).  Steps past
   // nsub re-read the last step (in bounds) and are not used.
-#define HY3_LOAD(W0, W1, X)                                                            \
+#define HY3_LOAD(W0, W1, X, S0, S1)                                                    \
   {                                                                                    \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       const int st_ = s_ld + u < src.nsub ? s_ld + u : src.nsub - 1;                  \
       const int o_ = st_ * 64;                                                         \
       W0[u] = *reinterpret_cast<const uint4 *>(src.w0p + o_);                          \
       if (src.nf == 2) W1[u] = *reinterpret_cast<const uint4 *>(src.w1p + o_);         \
+      if constexpr (F4) {                                                              \
+        S0[u] = src.s0p[st_ * 4];                                                      \
+        if (src.nf == 2) S1[u] = src.s1p[st_ * 4];                                     \
+      }                                                                                \
       _Pragma("unroll") for (int m = 0; m < MT; ++m)                                   \
         _Pragma("unroll") for (int h = 0; h < XN; ++h)                                 \
           X[u][m][h] = *reinterpret_cast<const uint4 *>(src.xp[m] + st_ * 64 * XN + h * 16); \
     }                                                                                  \
     s_ld += U;                                                                         \
     if (s_ld >= src.nsub) {                                                            \
-      k_ld = next_item<T, GATE_UP, MT, F8>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
+      k_ld = next_item<T, GATE_UP, MT, WF>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src, ol);                             \
       s_ld = 0;                                                                        \
     }                                                                                  \
   }
   // Multiply one block of the multiplying unit; at its end, write the unit
   // and move on.  `more` turns false after the last unit.
-#define HY3_MMA(W0, W1, X)                                                             \
+#define HY3_MMA(W0, W1, X, S0, S1)                                                     \
   {                                                                                    \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       if (s_mm + u < om.nsub) {                                                        \
-        if constexpr (F8) {                                                            \
+        if constexpr (F4) {                                                            \
+          const float sc0_ = e8m0_to_f32(S0[u]);                                       \
+          const uint4 q0_ = W0[u];                                                     \
+          const uint4 f0_[4] = {fp4x8_to_bf16(q0_.x, sc0_), fp4x8_to_bf16(q0_.y, sc0_), \
+                                fp4x8_to_bf16(q0_.z, sc0_), fp4x8_to_bf16(q0_.w, sc0_)}; \
+          _Pragma("unroll") for (int m = 0; m < MT; ++m)                               \
+            _Pragma("unroll") for (int f = 0; f < 4; ++f)                              \
+              Mma<T>::step(acc[0][m], f0_[f], X[u][m][f]);                             \
+          if (om.nf == 2) {                                                            \
+            const float sc1_ = e8m0_to_f32(S1[u]);                                     \
+            const uint4 q1_ = W1[u];                                                   \
+            const uint4 f1_[4] = {fp4x8_to_bf16(q1_.x, sc1_), fp4x8_to_bf16(q1_.y, sc1_), \
+                                  fp4x8_to_bf16(q1_.z, sc1_), fp4x8_to_bf16(q1_.w, sc1_)}; \
+            _Pragma("unroll") for (int m = 0; m < MT; ++m)                             \
+              _Pragma("unroll") for (int f = 0; f < 4; ++f)                            \
+                Mma<T>::step(acc[1][m], f1_[f], X[u][m][f]);                           \
+          }                                                                            \
+        } else if constexpr (F8) {                                                     \
           uint4 l0_, h0_, l1_, h1_;                                                    \
           e4m3x16_to_bf16(W0[u], l0_, h0_);                                            \
           if (om.nf == 2) e4m3x16_to_bf16(W1[u], l1_, h1_);                            \
@@ -258,10 +314,10 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
     }                                                                                  \
     s_mm += U;                                                                         \
     if (s_mm >= om.nsub) {                                                             \
-      unit_epilogue<T, GATE_UP, MT, F8>(a, om, acc, lane);                             \
+      unit_epilogue<T, GATE_UP, MT, WF>(a, om, acc, lane);                             \
       _Pragma("unroll") for (int f = 0; f < 2; ++f)                                    \
         _Pragma("unroll") for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; \
-      k_mm = next_item<T, GATE_UP, MT, F8>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
+      k_mm = next_item<T, GATE_UP, MT, WF>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src_dummy, om);                       \
       s_mm = 0;                                                                        \
       more = k_mm < kmax;                                                              \
@@ -269,15 +325,15 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   }
   UnitSrc<MT> src_dummy;   // next_unit also fills operand pointers; the multiply side ignores them
   bool more = true;
-  HY3_LOAD(aw0, aw1, ax);
+  HY3_LOAD(aw0, aw1, ax, as0, as1);
   while (more) {
-    if (k_ld < kmax) HY3_LOAD(bw0, bw1, bx);
+    if (k_ld < kmax) HY3_LOAD(bw0, bw1, bx, bs0, bs1);
     __builtin_amdgcn_sched_barrier(0);   // keep the next block's loads ahead
-    HY3_MMA(aw0, aw1, ax);
+    HY3_MMA(aw0, aw1, ax, as0, as1);
     if (!more) break;
-    if (k_ld < kmax) HY3_LOAD(aw0, aw1, ax);
+    if (k_ld < kmax) HY3_LOAD(aw0, aw1, ax, as0, as1);
     __builtin_amdgcn_sched_barrier(0);
-    HY3_MMA(bw0, bw1, bx);
+    HY3_MMA(bw0, bw1, bx, bs0, bs1);
   }
 #undef HY3_MMA
 #undef HY3_LOAD
@@ -286,26 +342,26 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
 // Persistent grid: WAVES_PER_SIMD wavefronts per SIMD on the 256 CUs.
 constexpr int STREAM_BLOCKS = 256 * WAVES_PER_SIMD;
 
-template <typename T, int MT, bool F8>
+template <typename T, int MT, int WF>
 hipError_t launch_skinny_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int ncb = (Imax + 15) / 16;
-    hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, F8>), dim3(STREAM_BLOCKS), dim3(256),
+    hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF>), dim3(STREAM_BLOCKS), dim3(256),
                        0, stream, a, ncb);
   } else {
     const int ncb = (a.H + 31) / 32;
-    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, F8>), dim3(STREAM_BLOCKS), dim3(256),
+    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF>), dim3(STREAM_BLOCKS), dim3(256),
                        0, stream, a, ncb);
   }
   return hipGetLastError();
 }
 
-template <typename T, bool F8>
+template <typename T, int WF>
 hipError_t launch_skinny(const ExpertArgs &a, bool gate_up, int T_tokens, hipStream_t stream) {
-  if (T_tokens <= 16) return launch_skinny_t<T, 1, F8>(a, gate_up, stream);
-  if (T_tokens <= 32) return launch_skinny_t<T, 2, F8>(a, gate_up, stream);
-  return launch_skinny_t<T, 4, F8>(a, gate_up, stream);
+  if (T_tokens <= 16) return launch_skinny_t<T, 1, WF>(a, gate_up, stream);
+  if (T_tokens <= 32) return launch_skinny_t<T, 2, WF>(a, gate_up, stream);
+  return launch_skinny_t<T, 4, WF>(a, gate_up, stream);
 }
 
 }  // namespace
@@ -319,18 +375,20 @@ hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream);
 
 hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
   if (path == PATH_SKINNY)
-    return dtype == DT_F32 ? launch_skinny<float, false>(a, true, T, stream)
-           : a.w_fp8       ? launch_skinny<bf16_t, true>(a, true, T, stream)
-                           : launch_skinny<bf16_t, false>(a, true, T, stream);
+    return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, true, T, stream)
+           : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, true, T, stream)
+           : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, true, T, stream)
+                           : launch_skinny<bf16_t, WF_DTYPE>(a, true, T, stream);
   if (path == PATH_BIG) return launch_big_gate_up(a, dtype, stream);
   return launch_tiled_gate_up(a, dtype, stream);
 }
 
 hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
   if (path == PATH_SKINNY)
-    return dtype == DT_F32 ? launch_skinny<float, false>(a, false, T, stream)
-           : a.w_fp8       ? launch_skinny<bf16_t, true>(a, false, T, stream)
-                           : launch_skinny<bf16_t, false>(a, false, T, stream);
+    return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, false, T, stream)
+           : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, false, T, stream)
+           : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, false, T, stream)
+                           : launch_skinny<bf16_t, WF_DTYPE>(a, false, T, stream);
   if (path == PATH_BIG) return launch_big_down(a, dtype, stream);
   return launch_tiled_down(a, dtype, stream);
 }

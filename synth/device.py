@@ -25,6 +25,8 @@ def upload_weights(inp: MoEInputs, device) -> Dict[str, object]:
     """Router weight, expert bias (if any), stacked routed experts and the shared expert."""
     import torch
     c = inp.cfg
+    if c.w_format == "mxfp4":
+        return _upload_mxfp4(inp, device)
     if c.w_format == "fp8_e4m3":
         d = _upload_fp8(inp, device)
         return with_act_scales(inp, d, device) if c.act_format == "fp8_static" else d
@@ -59,6 +61,28 @@ def with_bias_of(inp: MoEInputs, weights: Dict[str, object], device) -> Dict[str
     b = inp.bias()
     w["expert_bias"] = None if b is None else torch.from_numpy(b).to(device)
     return w
+
+
+def _upload_mxfp4(inp: MoEInputs, device) -> Dict[str, object]:
+    """MXFP4 expert codes (packed uint8) with their E8M0 block scales (uint8)."""
+    import torch
+    wg, wu, wd, sg, su, sd = inp.stacked_experts_mxfp4()
+    d = {"w_router": torch.from_numpy(inp.w_router()).to(device)}
+    for k, a in (("w_gate", wg), ("w_up", wu), ("w_down", wd), ("w_gate_mx", sg),
+                 ("w_up_mx", su), ("w_down_mx", sd)):
+        d[k] = torch.from_numpy(a).to(device)
+    del wg, wu, wd, sg, su, sd
+    b = inp.bias()
+    if b is not None:
+        d["expert_bias"] = torch.from_numpy(b).to(device)
+    sh = inp.shared_mxfp4()
+    if sh is not None:
+        codes, scales = sh
+        for k, a in zip(("ws_gate", "ws_up", "ws_down"), codes):
+            d[k] = torch.from_numpy(a).to(device)
+        for k, a in zip(("ws_gate_mx", "ws_up_mx", "ws_down_mx"), scales):
+            d[k] = torch.from_numpy(a).to(device)
+    return d
 
 
 def _upload_fp8(inp: MoEInputs, device) -> Dict[str, object]:

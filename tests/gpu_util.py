@@ -102,10 +102,14 @@ def expert_cache(inp: MoEInputs):
     """expert(e) -> float64 (gate, up, down); FP8 weights dequantised by the oracle."""
     cache = {}
     fp8 = inp.cfg.w_format == "fp8_e4m3"
+    fp4 = inp.cfg.w_format == "mxfp4"
 
     def f(e):
         if e not in cache:
-            if fp8:
+            if fp4:
+                codes, sc = inp.expert_mxfp4(e)
+                cache[e] = tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(codes, sc))
+            elif fp8:
                 codes, sc = inp.expert_fp8(e)
                 cache[e] = tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))
             else:
@@ -116,6 +120,9 @@ def expert_cache(inp: MoEInputs):
 
 def shared_f64(inp: MoEInputs):
     """float64 (gate, up, down) of the shared expert, or None."""
+    if inp.cfg.w_format == "mxfp4":
+        sh = inp.shared_mxfp4()
+        return None if sh is None else tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(*sh))
     if inp.cfg.w_format != "fp8_e4m3":
         return inp.shared_f64()
     sh = inp.shared_fp8()

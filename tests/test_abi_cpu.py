@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 4
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 5
     for code in (0, -1, -2, -3, -4, -5):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -59,6 +59,8 @@ def cfg_of(c, **kw):
 
 @pytest.mark.parametrize("cfg_id", sorted(CONFIGS))
 def test_workspace_layout_is_consistent(lib, cfg_id):
+    if CONFIGS[cfg_id].w_format == "mxfp4" and CONFIGS[cfg_id].T > 64:
+        pytest.skip("MXFP4 weights: weight-streaming batches only so far")
     cfg = cfg_of(CONFIGS[cfg_id])
     L = sm.hy3moe_workspace_layout(cfg)
     assert L.total == sm.hy3moe_workspace_bytes(cfg, True) > 0
@@ -94,6 +96,10 @@ def test_workspace_layout_is_consistent(lib, cfg_id):
     (dict(w_format="fp8_e4m3", dtype="f32"), -2),
     # static FP8 activations: with FP8 weights only
     (dict(act_format="fp8_static"), -2),
+    # MXFP4 weights: bf16 activations, H, I, I_shared % 128, T <= 64, no W8A8
+    (dict(w_format="mxfp4", dtype="f32"), -2), (dict(w_format="mxfp4", H=4096 + 64), -2),
+    (dict(w_format="mxfp4", I=1536 + 64), -2), (dict(w_format="mxfp4", I_shared=64), -2),
+    (dict(w_format="mxfp4", T=65), -2), (dict(w_format="mxfp4", act_format="fp8_static"), -2),
 ])
 def test_invalid_configs_rejected(lib, bad, code):
     c = CONFIGS[1]
@@ -155,7 +161,7 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
 def test_weight_format_enum_is_checked(lib):
     cfg = cfg_of(CONFIGS[5])
     assert sm.hy3moe_workspace_bytes(cfg, True) > 0
-    cfg.w_format = 2
+    cfg.w_format = 3
     assert sm.hy3moe_workspace_bytes(cfg, True) == 0
     L = b.hy3moe_ws_layout()
     assert lib.hy3moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == -1
@@ -181,6 +187,29 @@ def test_w8a8_path_choice(lib):
         # ... while the same shapes with W8A16 stay on the large-tile path
         L16 = sm.hy3moe_workspace_layout(cfg_of(CONFIGS[8], act_format="dtype", **kw))
         assert L16.tile_rows == 256, kw
+
+
+def test_mxfp4_weights_need_their_block_scales(lib):
+    cfg = cfg_of(CONFIGS[9])
+    need = sm.hy3moe_workspace_bytes(cfg, True)
+    assert need > 0
+    fw = lib.hy3moe_forward
+    full = [4096] * 20
+    for missing in range(14, 20):                     # each of the six E8M0 arrays
+        w = list(full)
+        w[missing] = None
+        assert fw(ctypes.byref(cfg), 4096, ctypes.byref(b.hy3moe_weights(*w)), 8192, None,
+                  None, 4096, need, None) == -1, missing
+    w = list(full)
+    w[16] = 4098                                      # down scales not 4-byte aligned
+    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(b.hy3moe_weights(*w)), 8192, None, None,
+              4096, need, None) == -4
+    # without a shared expert its scale arrays may be NULL
+    cfg_ns = cfg_of(CONFIGS[9], I_shared=0)
+    w = full[:17] + [None, None, None]
+    rc = fw(ctypes.byref(cfg_ns), 4096, ctypes.byref(b.hy3moe_weights(*w)), 8192, None, None,
+            4096, sm.hy3moe_workspace_bytes(cfg_ns, True), None)
+    assert rc not in (-1, -4)
 
 
 def test_w8a8_needs_its_activation_scales(lib):

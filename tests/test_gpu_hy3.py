@@ -185,3 +185,16 @@ def test_hy3_prefill_T8192_skew_w8a8_sampled(dev, hy3_fp8_weights):
     inp = MoEInputs(CONFIGS[8])
     log(f"case {inp.cfg.name}")
     sampled_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev), workload_shape=False)
+
+
+def test_hy3_decode_T16_mxfp4_full(dev):
+    """Hy3 decode with MXFP4 experts (E2M1 codes, one E8M0 scale per 32
+    weights), every token; derived output bound as for the FP8 weights."""
+    inp = MoEInputs(CONFIGS[9])
+    log("generating and uploading MXFP4 Hy3 expert weights (192 x 10 MB)")
+    w = upload_weights(inp, dev)
+    torch.cuda.synchronize()
+    decode_full_check(inp, dev, w, workload_shape=False)
+    del w
+    gc.collect()
+    torch.cuda.empty_cache()

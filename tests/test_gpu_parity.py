@@ -136,6 +136,18 @@ SMALL = {
     "w8a8_T700_H320_to_tiled": dict(seed=45, T=700, H=320, E=4, K=3, I=192, I_shared=64,
                                     dtype="bf16", w_format="fp8_e4m3",
                                     act_format="fp8_static"),
+    # MXFP4 weights (E2M1 codes, E8M0 scale per 32) on the weight-streaming
+    # path: 1, 2 and 4 row fragments, softmax routing, no shared expert, a
+    # shared expert wider than the routed ones
+    "mxfp4_T1": dict(seed=70, T=1, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16",
+                     w_format="mxfp4"),
+    "mxfp4_T16": dict(seed=71, T=16, H=512, E=32, K=4, I=256, I_shared=128, dtype="bf16",
+                      w_format="mxfp4"),
+    "mxfp4_T20_noshared": dict(seed=72, T=20, H=256, E=8, K=2, I=128, I_shared=0,
+                               dtype="bf16", w_format="mxfp4"),
+    "mxfp4_T64_softmax": dict(seed=73, T=64, H=384, E=16, K=4, I=128, I_shared=256,
+                              dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
+                              bias_kind="none", w_format="mxfp4"),
 }
 
 
