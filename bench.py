@@ -33,7 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4, "decode_fp8": 5, "prefill_fp8": 6,
-             "decode_w8a8": 7, "prefill_w8a8": 8, "decode_mxfp4": 9}
+             "decode_w8a8": 7, "prefill_w8a8": 8, "decode_mxfp4": 9, "prefill_mxfp4": 10}
 ROUTER_WORKLOAD = 3            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published

@@ -94,8 +94,8 @@ extern "C" {
  * scale 2^(s - 127) in the matching *_mx array.  Activations stay bfloat16
  * (cfg.dtype HY3MOE_BF16, act_format DTYPE); H, I and I_shared must be
  * multiples of 128.  The GEMMs decode the codes with their scale exactly to
- * bfloat16.  Weight-streaming batches (T <= 64) only for now: larger T gives
- * HY3MOE_ERR_UNSUPPORTED. */
+ * bfloat16: in registers on the weight-streaming path (T <= 64), on the way
+ * into LDS on the tile paths. */
 #define HY3MOE_WFMT_MXFP4    2
 
 /* Activations of the expert GEMMs.  DTYPE: x and h as cfg.dtype.

@@ -45,10 +45,8 @@ int validate_cfg(const hy3moe_config *c) {
   // FP8 and MXFP4 expert weights need bf16 activations.
   if (c->w_format != HY3MOE_WFMT_DTYPE && c->dtype != HY3MOE_BF16)
     return HY3MOE_ERR_UNSUPPORTED;
-  // MXFP4: 128 K values per 64-byte step of a weight row; weight-streaming
-  // batches only.
-  if (c->w_format == HY3MOE_WFMT_MXFP4 &&
-      (c->H % 128 || c->I % 128 || c->I_shared % 128 || c->T > SKINNY_MAX_T))
+  // MXFP4: 128 K values per 64-byte step of a streamed weight row.
+  if (c->w_format == HY3MOE_WFMT_MXFP4 && (c->H % 128 || c->I % 128 || c->I_shared % 128))
     return HY3MOE_ERR_UNSUPPORTED;
   if (c->act_format != HY3MOE_AFMT_DTYPE && c->act_format != HY3MOE_AFMT_FP8_STATIC)
     return HY3MOE_ERR_INVALID;

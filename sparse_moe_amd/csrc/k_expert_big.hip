@@ -28,6 +28,10 @@
 //    finished tile's epilogue runs.
 // Group E is the shared expert (its own weights and width I_shared).
 //
+// MXFP4 weights (F4): a thread loads the 4 code bytes (8 E2M1 weights) of
+// its chunk and the E8M0 scale of the chunk's 32-weight block, and decodes
+// them with the scale exactly to 8 bf16 when it writes the chunk to LDS.
+//
 // FP8 E4M3 weights (F8): a thread loads the 8 code bytes of its weight chunk,
 // decodes them exactly to 8 bf16 when it writes the chunk to LDS, and the
 // per-matrix scale multiplies the accumulators in the epilogue.
@@ -124,25 +128,32 @@ __device__ __forceinline__ bool big_tile_at(const ExpertArgs &a, int n_tiles, in
 // block of 64 rows [64q, 64q+64) holds gate cols col0 + 32q + [0, 32) and then
 // the up cols of the same columns, so lr < 32 loads gate rows, lr >= 32 up rows.
 // Global addresses: a base pointer plus 32-bit offsets (every matrix < 4 GiB).
-template <typename T, bool GATE_UP, bool F8, bool A8>
+template <typename T, bool GATE_UP, int WF, bool A8>
 __device__ __forceinline__ void big_tile_loads(const ExpertArgs &a, const BigTile &t, int lr,
                                                int lc, const char *&wb, const char *&xb,
-                                               uint32_t *woff, uint32_t *xoff) {
+                                               uint32_t *woff, uint32_t *xoff,
+                                               const uint8_t *&sb) {
+  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4;
   constexpr int EB = A8 ? 1 : Elem<T>::kBytes; // bytes per token-row element
-  constexpr int WB = F8 ? 1 : Elem<T>::kBytes; // bytes per weight element
-  constexpr int WCH = (F8 && !A8) ? 8 : 16;    // weight bytes per 16-byte LDS chunk
+  // bytes of a weight row of K elements, and per 16-byte LDS chunk
+  auto rowb = [](int K) { return F4 ? (uint32_t)K / 2 : (uint32_t)K * (F8 ? 1 : Elem<T>::kBytes); };
+  constexpr int WCH = F4 ? 4 : ((F8 && !A8) ? 8 : 16);
   const bool shared = (t.g == a.E);
   if (GATE_UP) {
     const bool up = lr >= 32;
     wb = shared ? static_cast<const char *>(up ? a.ws1 : a.ws0)
-                : static_cast<const char *>(up ? a.w1 : a.w0) + (size_t)t.g * a.I * a.H * WB;
+                : static_cast<const char *>(up ? a.w1 : a.w0) + (size_t)t.g * a.I * rowb(a.H);
+    if (F4) sb = shared ? (up ? a.mxs1 : a.mxs0) : (up ? a.mx1 : a.mx0) + (size_t)t.g * a.I * (a.H / 32);
+    if constexpr (F4)
+      sb = reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<const char *>(sb)));
     // A wavefront stages 8 consecutive rows lr (lr = tid / 8), all gate or
     // all up: the base is wave-uniform, held in scalar registers for A8.
-    if constexpr (A8) wb = wave_uniform(wb);
+    if constexpr (A8 || F4) wb = wave_uniform(wb);
     xb = static_cast<const char *>(a.act);
   } else {
     wb = shared ? static_cast<const char *>(a.ws0)
-                : static_cast<const char *>(a.w0) + (size_t)t.g * a.H * a.I * WB;
+                : static_cast<const char *>(a.w0) + (size_t)t.g * a.H * rowb(a.I);
+    if (F4) sb = shared ? a.mxs0 : a.mx0 + (size_t)t.g * a.H * (a.I / 32);
     xb = static_cast<const char *>(a.act) + (size_t)t.row0 * a.ldh * EB;
   }
 #pragma unroll
@@ -151,10 +162,10 @@ __device__ __forceinline__ void big_tile_loads(const ExpertArgs &a, const BigTil
     if (GATE_UP) {
       int wrow = t.col0 + p * 32 + (lr & 31);
       if (wrow >= t.Ig) wrow = t.col0;         // column tail (Ig % 128 == 64)
-      woff[p] = (uint32_t)wrow * (uint32_t)(a.H * WB) + lc * WCH;
+      woff[p] = (uint32_t)wrow * rowb(a.H) + lc * WCH;
     } else {
       const int wrow = (t.col0 + r < a.H) ? t.col0 + r : t.col0;
-      woff[p] = (uint32_t)wrow * (uint32_t)(t.Ig * WB) + lc * WCH;
+      woff[p] = (uint32_t)wrow * rowb(t.Ig) + lc * WCH;
     }
     int trow = t.row0 + r;
     if (trow >= t.grp_end) trow = t.row0;      // ragged tail: reload a valid row
@@ -209,11 +220,12 @@ __device__ __forceinline__ void big_epilogue_h8(const ExpertArgs &a, const BigTi
 
 // Epilogue of a tile: lane holds D[weight row 16i + 4cg + q][token row 16j + r16]
 // of wavefront (wr_, wt_).  tid is the thread index.
-template <typename T, bool GATE_UP, bool F8, bool A8>
+template <typename T, bool GATE_UP, int WF, bool A8>
 __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile &t,
                                              const f32x4_t (&acc)[8][4], uint4 *lds, int tid) {
   // FP8: scale of the gate (or down) matrix and of the up matrix (A8: times
   // the activation scale of the GEMM's input)
+  constexpr bool F8 = WF == WF_FP8;
   float s0 = 1.0f, s1 = 1.0f;
   if (F8) {
     const bool shared = (t.g == a.E);
@@ -315,9 +327,13 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
   }
 }
 
-// LDS form of a staged weight chunk: as loaded, or decoded from E4M3 codes.
-__device__ __forceinline__ uint4 weight_chunk(const uint4 &v) { return v; }
-__device__ __forceinline__ uint4 weight_chunk(const uint2 &q) { return e4m3x8_to_bf16(q); }
+// LDS form of a staged weight chunk: as loaded, decoded from E4M3 codes, or
+// decoded from E2M1 codes with their block's E8M0 scale s (used by MXFP4 only).
+__device__ __forceinline__ uint4 weight_chunk(const uint4 &v, uint32_t) { return v; }
+__device__ __forceinline__ uint4 weight_chunk(const uint2 &q, uint32_t) { return e4m3x8_to_bf16(q); }
+__device__ __forceinline__ uint4 weight_chunk(uint32_t q, uint32_t s) {
+  return fp4x8_to_bf16(q, e8m0_to_f32(s));
+}
 
 // One 16x16x128 FP8 (E4M3 x E4M3) MFMA; each operand is two 16-byte chunks.
 __device__ __forceinline__ void mma_fp8(f32x4_t &acc, const uint4 &a0, const uint4 &a1,
@@ -349,8 +365,9 @@ __device__ __forceinline__ void stage_schedule_a8() {
   }
 }
 
-template <typename T, bool GATE_UP, bool F8, bool A8>
+template <typename T, bool GATE_UP, int WF, bool A8>
 __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_col_tiles) {
+  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4;
   __shared__ uint4 lds[2 * ROWS * CH];   // 2 x 64 KB
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -370,7 +387,8 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
   const int lr = tid >> 3, lc = tid & 7;
   const char *wb, *xb;
   uint32_t woff[4], xoff[4];
-  big_tile_loads<T, GATE_UP, F8, A8>(a, cur, lr, lc, wb, xb, woff, xoff);
+  const uint8_t *sb = nullptr;   // MXFP4: scale bytes of the weight rows
+  big_tile_loads<T, GATE_UP, WF, A8>(a, cur, lr, lc, wb, xb, woff, xoff, sb);
 
   const int wr_ = wave >> 2, wt_ = wave & 3;
   const int r16 = lane & 15, cg = lane >> 4;
@@ -385,14 +403,24 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
   // iteration s - 2 and written to LDS at the end of iteration s - 1, so the
   // global latency is covered by two iterations of MFMA work.
   // Weight chunks: 16 bytes, or the 8 E4M3 code bytes of 8 weights (FP8).
-  typedef typename std::conditional<F8 && !A8, uint2, uint4>::type wchunk_t;
+  // MXFP4: the 4 code bytes of 8 weights, and their block's scale code.
+  typedef typename std::conditional<
+      F4, uint32_t, typename std::conditional<F8 && !A8, uint2, uint4>::type>::type wchunk_t;
   wchunk_t aw0, aw1, aw2, aw3, bw0, bw1, bw2, bw3;
+  uint32_t as0 = 0, as1 = 0, as2 = 0, as3 = 0, bs0 = 0, bs1 = 0, bs2 = 0, bs3 = 0;
   uint4 ax0, ax1, ax2, ax3;   // set 0
   uint4 bx0, bx1, bx2, bx3;   // set 1
 #define HY3_GLOAD(S, kst)                                                              \
   {                                                                                    \
     const uint32_t kb_ = (uint32_t)(kst) * RB;                                         \
-    const uint32_t kw_ = (F8 && !A8) ? kb_ / 2 : kb_;   /* W8A16: half the bytes */  \
+    /* weight bytes: W8A16 half, MXFP4 a quarter of the bf16 stage */                 \
+    const uint32_t kw_ = F4 ? kb_ / 4 : ((F8 && !A8) ? kb_ / 2 : kb_);                 \
+    /* MXFP4: the scale of a chunk is byte woff / 16 of its row's scales (a row  */  \
+    /* of K/2 code bytes has K/32 scale bytes; chunk lc holds K lc*8 + [0, 8)) */      \
+    if constexpr (F4) {                                                                \
+      S##s0 = sb[(woff[0] >> 4) + kb_ / 64]; S##s1 = sb[(woff[1] >> 4) + kb_ / 64];    \
+      S##s2 = sb[(woff[2] >> 4) + kb_ / 64]; S##s3 = sb[(woff[3] >> 4) + kb_ / 64];    \
+    }                                                                                  \
     S##w0 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[0]));                 \
     S##w1 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[1]));                 \
     S##w2 = *reinterpret_cast<const wchunk_t *>(wb + (kw_ + woff[2]));                 \
@@ -405,8 +433,10 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
 #define HY3_LSTORE(S, buf)                                                             \
   {                                                                                    \
     uint4 *d_ = lds + (buf) * ROWS * CH + wr_l;                                        \
-    d_[0 * 64 * CH] = weight_chunk(S##w0); d_[1 * 64 * CH] = weight_chunk(S##w1);      \
-    d_[2 * 64 * CH] = weight_chunk(S##w2); d_[3 * 64 * CH] = weight_chunk(S##w3);      \
+    d_[0 * 64 * CH] = weight_chunk(S##w0, S##s0);                                      \
+    d_[1 * 64 * CH] = weight_chunk(S##w1, S##s1);                                      \
+    d_[2 * 64 * CH] = weight_chunk(S##w2, S##s2);                                      \
+    d_[3 * 64 * CH] = weight_chunk(S##w3, S##s3);                                      \
     d_[(BW + 0 * 64) * CH] = S##x0; d_[(BW + 1 * 64) * CH] = S##x1;                    \
     d_[(BW + 2 * 64) * CH] = S##x2; d_[(BW + 3 * 64) * CH] = S##x3;                    \
   }
@@ -532,7 +562,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     if (has_next) {   // the finished tile's load descriptors are free
       int tid_n = tid;
       asm volatile("" : "+v"(tid_n));
-      big_tile_loads<T, GATE_UP, F8, A8>(a, nxt, tid_n >> 3, tid_n & 7, wb, xb, woff, xoff);
+      big_tile_loads<T, GATE_UP, WF, A8>(a, nxt, tid_n >> 3, tid_n & 7, wb, xb, woff, xoff, sb);
       if constexpr (A8) {
         HY3_A8_LOAD_ALL(0)
       } else {
@@ -543,7 +573,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
     __builtin_amdgcn_sched_barrier(0);
     int tid_e = tid;
     asm volatile("" : "+v"(tid_e));
-    big_epilogue<T, GATE_UP, F8, A8>(a, cur, acc, lds, tid_e);
+    big_epilogue<T, GATE_UP, WF, A8>(a, cur, acc, lds, tid_e);
     __builtin_amdgcn_sched_barrier(0);
     if (!has_next) break;
     __syncthreads();   // the epilogue's LDS reads are done
@@ -570,7 +600,7 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
 
 }
 
-template <typename T, bool F8, bool A8>
+template <typename T, int WF, bool A8>
 hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   int nct;
   if (gate_up) {
@@ -593,25 +623,27 @@ hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   const long want = (logical + 7) / 8 * 8;
   const dim3 grid((unsigned)(want < cap ? want : cap));
   if (gate_up)
-    hipLaunchKernelGGL((expert_big_kernel<T, true, F8, A8>), grid, dim3(512), 0, stream, a, nct);
+    hipLaunchKernelGGL((expert_big_kernel<T, true, WF, A8>), grid, dim3(512), 0, stream, a, nct);
   else
-    hipLaunchKernelGGL((expert_big_kernel<T, false, F8, A8>), grid, dim3(512), 0, stream, a, nct);
+    hipLaunchKernelGGL((expert_big_kernel<T, false, WF, A8>), grid, dim3(512), 0, stream, a, nct);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_big_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_big_t<float, false, false>(a, true, stream)
-         : a.a8          ? launch_big_t<bf16_t, true, true>(a, true, stream)
-         : a.w_fp8       ? launch_big_t<bf16_t, true, false>(a, true, stream)
-                         : launch_big_t<bf16_t, false, false>(a, true, stream);
+  return dtype == DT_F32 ? launch_big_t<float, WF_DTYPE, false>(a, true, stream)
+         : a.a8          ? launch_big_t<bf16_t, WF_FP8, true>(a, true, stream)
+         : a.w_fp4       ? launch_big_t<bf16_t, WF_MXFP4, false>(a, true, stream)
+         : a.w_fp8       ? launch_big_t<bf16_t, WF_FP8, false>(a, true, stream)
+                         : launch_big_t<bf16_t, WF_DTYPE, false>(a, true, stream);
 }
 hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_big_t<float, false, false>(a, false, stream)
-         : a.a8          ? launch_big_t<bf16_t, true, true>(a, false, stream)
-         : a.w_fp8       ? launch_big_t<bf16_t, true, false>(a, false, stream)
-                         : launch_big_t<bf16_t, false, false>(a, false, stream);
+  return dtype == DT_F32 ? launch_big_t<float, WF_DTYPE, false>(a, false, stream)
+         : a.a8          ? launch_big_t<bf16_t, WF_FP8, true>(a, false, stream)
+         : a.w_fp4       ? launch_big_t<bf16_t, WF_MXFP4, false>(a, false, stream)
+         : a.w_fp8       ? launch_big_t<bf16_t, WF_FP8, false>(a, false, stream)
+                         : launch_big_t<bf16_t, WF_DTYPE, false>(a, false, stream);
 }
 
 }  // namespace hy3moe

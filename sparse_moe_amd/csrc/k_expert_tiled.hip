@@ -20,6 +20,10 @@
 // operand, so each lane ends with 4 consecutive output columns of one row.
 // Group E is the shared expert (its own weight pointers and width I_shared).
 //
+// MXFP4 weights (F4): each thread loads the 4 code bytes (8 E2M1 weights) of
+// its chunk and the E8M0 scale of the 32-weight block it lies in, and
+// decodes them with the scale exactly to 8 bf16 before the LDS write.
+//
 // FP8 E4M3 weights (F8): each thread loads the 8 code bytes of its chunk,
 // decodes them exactly to 8 bf16 before the LDS write, and the per-matrix
 // scale multiplies the accumulators in the epilogue; the rest is unchanged.
@@ -37,8 +41,9 @@ constexpr int CHUNKS = KB / 16;  // 8
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * CHUNKS + (chunk ^ (row & 7)); }
 
-template <typename T, bool GATE_UP, bool F8>
+template <typename T, bool GATE_UP, int WF>
 __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int n_col_tiles) {
+  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4;
   __shared__ uint4 lds[2][(BR + BT) * CHUNKS];   // 2 x 32 KB
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -55,8 +60,9 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
   const int Kdim = GATE_UP ? a.H : Ig;               // reduction length (elements)
   constexpr int EB = Elem<T>::kBytes;
   constexpr int EPC = Elem<T>::kPerChunk;
-  constexpr int WB = F8 ? 1 : EB;                    // bytes per weight element
-  constexpr int WCH = F8 ? 8 : 16;                   // weight bytes per 16-byte LDS chunk
+  constexpr int WCH = F4 ? 4 : (F8 ? 8 : 16);        // weight bytes per 16-byte LDS chunk
+  // bytes of a weight row of K elements
+  auto rowb = [](int K) { return F4 ? (size_t)K / 2 : (size_t)K * (F8 ? 1 : EB); };
 
   // Columns of this tile.
   const int col0 = ct * (GATE_UP ? TILED_GU_COLS : TILED_DN_COLS);
@@ -66,25 +72,30 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
   const int lrow = tid >> 3, lch = tid & 7;     // row 0..31 within a pass, chunk 0..7
   const char *wptr[4];
   const char *xptr[4];
+  const uint8_t *sptr[4];   // MXFP4: scale byte of the chunk's block at stage 0
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = p * 32 + lrow;   // LDS weight row 0..127
     const char *base;
-    size_t wrow;                   // element offset of the weight row
+    int wr;                        // weight row
+    const uint8_t *sbase = nullptr;
     if (GATE_UP) {
       const int half = r >> 6, rr = r & 63;
       const bool up = rr >= 32;
-      const int c = col0 + half * 32 + (rr & 31);
+      wr = col0 + half * 32 + (rr & 31);
       base = shared ? static_cast<const char *>(up ? a.ws1 : a.ws0)
-                    : static_cast<const char *>(up ? a.w1 : a.w0) + (size_t)g * a.I * a.H * WB;
-      wrow = (size_t)c * a.H;
+                    : static_cast<const char *>(up ? a.w1 : a.w0) + (size_t)g * a.I * rowb(a.H);
+      if (F4) sbase = shared ? (up ? a.mxs1 : a.mxs0)
+                             : (up ? a.mx1 : a.mx0) + (size_t)g * a.I * (a.H / 32);
     } else {
       base = shared ? static_cast<const char *>(a.ws0)
-                    : static_cast<const char *>(a.w0) + (size_t)g * a.H * a.I * WB;
-      const int n = (col0 + r < a.H) ? col0 + r : col0;   // column tail: reload a valid row
-      wrow = (size_t)n * Ig;
+                    : static_cast<const char *>(a.w0) + (size_t)g * a.H * rowb(a.I);
+      wr = (col0 + r < a.H) ? col0 + r : col0;   // column tail: reload a valid row
+      if (F4) sbase = shared ? a.mxs0 : a.mx0 + (size_t)g * a.H * (a.I / 32);
     }
-    wptr[p] = base + wrow * WB + lch * WCH;
+    wptr[p] = base + (size_t)wr * rowb(Kdim) + lch * WCH;
+    // the chunk's K values lch * 8 + [0, 8) lie in block lch / 4 of a stage
+    if (F4) sptr[p] = sbase + (size_t)wr * (Kdim / 32) + (lch >> 2);
 
     int trow = row0 + r;                       // expert-major row of this token slot
     if (trow >= grp_end) trow = row0;          // ragged tail: reload a valid row
@@ -97,18 +108,25 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
 
   uint4 wreg[4], xreg[4];
   uint2 wq[4];                     // FP8: the chunk's 8 code bytes
+  uint32_t wq4[4], ws4[4];         // MXFP4: the chunk's 4 code bytes and its scale code
   // kbyte: byte offset of the stage in a bf16 (or fp32) row; FP8 weight rows
   // advance by half of it.
 #define HY3_GLOAD(kbyte)                                                   \
   _Pragma("unroll") for (int p = 0; p < 4; ++p) {                          \
-    if constexpr (F8) wq[p] = *reinterpret_cast<const uint2 *>(wptr[p] + (kbyte) / 2); \
+    if constexpr (F4) {                                                    \
+      wq4[p] = *reinterpret_cast<const uint32_t *>(wptr[p] + (kbyte) / 4); \
+      ws4[p] = sptr[p][(kbyte) / 64];                                      \
+    } else if constexpr (F8)                                               \
+      wq[p] = *reinterpret_cast<const uint2 *>(wptr[p] + (kbyte) / 2);     \
     else wreg[p] = *reinterpret_cast<const uint4 *>(wptr[p] + (kbyte));    \
     xreg[p] = *reinterpret_cast<const uint4 *>(xptr[p] + (kbyte));         \
   }
 #define HY3_LSTORE(buf)                                                    \
   _Pragma("unroll") for (int p = 0; p < 4; ++p) {                          \
     const int r = p * 32 + lrow;                                           \
-    if constexpr (F8) lds[buf][swz(r, lch)] = e4m3x8_to_bf16(wq[p]);       \
+    if constexpr (F4)                                                      \
+      lds[buf][swz(r, lch)] = fp4x8_to_bf16(wq4[p], e8m0_to_f32(ws4[p]));  \
+    else if constexpr (F8) lds[buf][swz(r, lch)] = e4m3x8_to_bf16(wq[p]);  \
     else lds[buf][swz(r, lch)] = wreg[p];                                  \
     lds[buf][BR * CHUNKS + swz(r, lch)] = xreg[p];                         \
   }
@@ -201,30 +219,32 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
 
 }  // namespace
 
-template <typename T, bool F8>
+template <typename T, int WF>
 static hipError_t launch_tiled(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int nct = Imax / TILED_GU_COLS;
-    hipLaunchKernelGGL((expert_tiled_kernel<T, true, F8>), dim3(a.max_tiles * nct), dim3(256),
+    hipLaunchKernelGGL((expert_tiled_kernel<T, true, WF>), dim3(a.max_tiles * nct), dim3(256),
                        0, stream, a, nct);
   } else {
     const int nct = (a.H + TILED_DN_COLS - 1) / TILED_DN_COLS;
-    hipLaunchKernelGGL((expert_tiled_kernel<T, false, F8>), dim3(a.max_tiles * nct), dim3(256),
+    hipLaunchKernelGGL((expert_tiled_kernel<T, false, WF>), dim3(a.max_tiles * nct), dim3(256),
                        0, stream, a, nct);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_tiled_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_tiled<float, false>(a, true, stream)
-         : a.w_fp8       ? launch_tiled<bf16_t, true>(a, true, stream)
-                         : launch_tiled<bf16_t, false>(a, true, stream);
+  return dtype == DT_F32 ? launch_tiled<float, WF_DTYPE>(a, true, stream)
+         : a.w_fp4       ? launch_tiled<bf16_t, WF_MXFP4>(a, true, stream)
+         : a.w_fp8       ? launch_tiled<bf16_t, WF_FP8>(a, true, stream)
+                         : launch_tiled<bf16_t, WF_DTYPE>(a, true, stream);
 }
 hipError_t launch_tiled_down(const ExpertArgs &a, int dtype, hipStream_t stream) {
-  return dtype == DT_F32 ? launch_tiled<float, false>(a, false, stream)
-         : a.w_fp8       ? launch_tiled<bf16_t, true>(a, false, stream)
-                         : launch_tiled<bf16_t, false>(a, false, stream);
+  return dtype == DT_F32 ? launch_tiled<float, WF_DTYPE>(a, false, stream)
+         : a.w_fp4       ? launch_tiled<bf16_t, WF_MXFP4>(a, false, stream)
+         : a.w_fp8       ? launch_tiled<bf16_t, WF_FP8>(a, false, stream)
+                         : launch_tiled<bf16_t, WF_DTYPE>(a, false, stream);
 }
 
 }  // namespace hy3moe

@@ -187,14 +187,26 @@ def test_hy3_prefill_T8192_skew_w8a8_sampled(dev, hy3_fp8_weights):
     sampled_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev), workload_shape=False)
 
 
-def test_hy3_decode_T16_mxfp4_full(dev):
-    """Hy3 decode with MXFP4 experts (E2M1 codes, one E8M0 scale per 32
-    weights), every token; derived output bound as for the FP8 weights."""
+@pytest.fixture(scope="module")
+def hy3_mxfp4_weights(dev):
     inp = MoEInputs(CONFIGS[9])
     log("generating and uploading MXFP4 Hy3 expert weights (192 x 10 MB)")
     w = upload_weights(inp, dev)
     torch.cuda.synchronize()
-    decode_full_check(inp, dev, w, workload_shape=False)
+    yield w
     del w
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_hy3_decode_T16_mxfp4_full(dev, hy3_mxfp4_weights):
+    """Hy3 decode with MXFP4 experts (E2M1 codes, one E8M0 scale per 32
+    weights), every token; derived output bound as for the FP8 weights."""
+    decode_full_check(MoEInputs(CONFIGS[9]), dev, hy3_mxfp4_weights, workload_shape=False)
+
+
+def test_hy3_prefill_T8192_skew_mxfp4_sampled(dev, hy3_mxfp4_weights):
+    """The prefill chunk on the same MXFP4 experts (large-tile path)."""
+    inp = MoEInputs(CONFIGS[10])
+    log(f"case {inp.cfg.name}")
+    sampled_check(inp, dev, hy3_mxfp4_weights, workload_shape=False)

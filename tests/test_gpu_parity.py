@@ -148,6 +148,17 @@ SMALL = {
     "mxfp4_T64_softmax": dict(seed=73, T=64, H=384, E=16, K=4, I=128, I_shared=256,
                               dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
                               bias_kind="none", w_format="mxfp4"),
+    # ... and on the tiled and large-tile paths (ragged row tails; I % 256 ==
+    # 128 and H % 256 == 128 column tails)
+    "mxfp4_tiled_T300": dict(seed=74, T=300, H=512, E=24, K=4, I=256, I_shared=128,
+                             dtype="bf16", w_format="mxfp4"),
+    "mxfp4_tiled_T700_H384": dict(seed=75, T=700, H=384, E=12, K=3, I=384, I_shared=128,
+                                  dtype="bf16", w_format="mxfp4"),
+    "mxfp4_big_T513_H384": dict(seed=76, T=513, H=384, E=4, K=2, I=384, I_shared=128,
+                                dtype="bf16", w_format="mxfp4"),
+    "mxfp4_big_T400_softmax": dict(seed=77, T=400, H=512, E=8, K=4, I=256, I_shared=128,
+                                   dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
+                                   bias_kind="none", w_format="mxfp4"),
 }
 
 
