@@ -4,7 +4,8 @@ never by the product path."""
 from .moe import (E4M3_MAX, ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, dense_masked,
                   dequant_fp8, dequant_mxfp4, e8m0_value, forward, forward_given_route,
                   fp4_e2m1_value, fp8_e4m3_value,
-                  layer_flops, quant_dequant_e4m3, quant_e4m3, route,
+                  dequant_mxfp8, layer_flops, quant_dequant_e4m3, quant_dequant_mxfp8,
+                  quant_e4m3, quant_mxfp8, route,
                   route_from_logits, router_logits, sigmoid, silu,
                   softmax_rows, swiglu_expert, topk_desc)
 
@@ -12,6 +13,7 @@ __all__ = [
     "E4M3_MAX", "ROUTE_SIGMOID_BIAS", "ROUTE_SOFTMAX", "Route", "dense_masked", "dequant_fp8",
     "dequant_mxfp4", "e8m0_value", "fp4_e2m1_value",
     "forward", "forward_given_route", "fp8_e4m3_value", "layer_flops", "quant_dequant_e4m3",
-    "quant_e4m3", "route", "route_from_logits",
+    "quant_e4m3", "route", "route_from_logits", "dequant_mxfp8", "quant_dequant_mxfp8",
+    "quant_mxfp8",
     "router_logits", "sigmoid", "silu", "softmax_rows", "swiglu_expert", "topk_desc",
 ]

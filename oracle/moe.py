@@ -60,6 +60,14 @@ order is a reading: the pages do not give one).  Built weight-only
 (W4A16): activations stay bf16, and the oracle runs the float64 layer on
 the exactly dequantised weights.
 
+Dynamic MXFP8 activations (W4A8 with MXFP4 weights; the CANN article,
+section 8.2: W4A8, and section 六: the MXFP4 path produces dynamic MXFP8
+values).  Each block of 32 consecutive values of an activation row (x
+along H, h along I) shares an E8M0 scale set from the block's maximum as
+the OCP microscaling conversion does (floor(log2 amax) - 8), and the
+values are E4M3 codes of v / scale (saturating, nearest even), decided in
+float32 (h rounded from float64 to float32 first).
+
 Static FP8 activations (W8A8; the CANN article, section 8.2 and the FP8
 path of section 六, where an FP8 Linear quantises its input with a static
 per-tensor input scale).  The expert input x is quantised with one float32
@@ -297,6 +305,42 @@ def quant_dequant_e4m3(v: np.ndarray, scale) -> np.ndarray:
     return dequant_fp8(quant_e4m3(v, scale), scale)
 
 
+E4M3_EMAX = 8          # exponent of the largest E4M3 binade (448 = 1.75 * 2^8)
+
+
+def quant_mxfp8(v: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Dynamic MXFP8 (E4M3) quantisation of rows v [..., K] (K % 32 == 0).
+
+    OCP microscaling conversion, per block of 32 consecutive values of a row:
+    the shared exponent is floor(log2(max |v|)) - 8 (8: the largest E4M3
+    exponent), floored at -127 (and -127 for an all-zero block); the block's
+    scale is that power of two (E8M0 code = exponent + 127) and each element
+    is quant_e4m3(v, scale): v / scale (exact: a power of two), clamped to
+    +-448 (so magnitudes in (448, 512) * scale saturate) and rounded to the
+    nearest E4M3 value, ties to even.  v is rounded to float32 first (the
+    decision is taken in float32).  Returns (codes [..., K] uint8, scale
+    codes [..., K/32] uint8).
+    """
+    v32 = np.asarray(v, dtype=np.float32)
+    shp = v32.shape
+    blk = v32.reshape(shp[:-1] + (shp[-1] // MX_BLOCK, MX_BLOCK)).astype(np.float64)
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))         # amax = f 2^ex, f in [0.5, 1)
+    shared = np.where(amax > 0, np.maximum(ex.astype(np.int64) - 1 - E4M3_EMAX, -127), -127)
+    scale = np.exp2(shared.astype(np.float64))
+    codes = quant_e4m3(blk / scale[..., None], 1.0)           # exact division
+    return codes.reshape(shp), (shared + 127).astype(np.uint8)
+
+
+def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """e8m0(scale of the block) * E4M3 value, float64 (blocks of 32 along the last axis)."""
+    return np.repeat(e8m0_value(scales), MX_BLOCK, axis=-1) * fp8_e4m3_value(codes)
+
+
+def quant_dequant_mxfp8(v: np.ndarray) -> np.ndarray:
+    return dequant_mxfp8(*quant_mxfp8(v))
+
+
 # --------------------------------------------------------------------------
 # Experts
 # --------------------------------------------------------------------------
@@ -306,7 +350,8 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
-                  w_down: np.ndarray, a2: Optional[float] = None) -> np.ndarray:
+                  w_down: np.ndarray, a2: Optional[float] = None,
+                  amx: bool = False) -> np.ndarray:
     """One SwiGLU expert on rows ``a`` [n, H]:  down( silu(a W_gate^T) * (a W_up^T) ).
 
     Weights are in nn.Linear layout [out, in]: gate/up [I, H], down [H, I]
@@ -314,7 +359,9 @@ def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
 
     With ``a2`` (static FP8 activations, W8A8), the down projection's input
     h is first quantised to E4M3 with the static scale a2 and dequantised
-    (``quant_dequant_e4m3``), as an FP8 Linear quantises its input.
+    (``quant_dequant_e4m3``), as an FP8 Linear quantises its input.  With
+    ``amx`` (dynamic MXFP8 activations, W4A8) h is quantised per block of 32
+    along I instead (``quant_dequant_mxfp8``).
     """
     a = np.asarray(a, dtype=np.float64)
     g = a @ np.asarray(w_gate, dtype=np.float64).T
@@ -322,6 +369,8 @@ def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
     h = silu(g) * u
     if a2 is not None:
         h = quant_dequant_e4m3(h, a2)
+    if amx:
+        h = quant_dequant_mxfp8(h)
     return h @ np.asarray(w_down, dtype=np.float64).T
 
 
@@ -331,7 +380,8 @@ def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
 def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
                         experts: ExpertFn, E: int,
                         shared: Optional[Sequence[np.ndarray]] = None,
-                        a8: Optional[Tuple[float, Sequence[float]]] = None) -> np.ndarray:
+                        a8: Optional[Tuple[float, Sequence[float]]] = None,
+                        amx: bool = False) -> np.ndarray:
     """Routed experts + shared expert for a given route (the eager path).
 
     Follows the eager path of the HunyuanImage 3.0 MoE reading: every token
@@ -348,7 +398,10 @@ def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
     ``a8 = (a1, a2)`` selects static FP8 activations (W8A8): the expert input
     x is quantised once with the layer's scale a1 (``quant_dequant_e4m3``)
     and every expert's h with its own scale a2[e] (a2[E] for the shared
-    expert).  The router is not affected: it reads the unquantised x.
+    expert).  ``amx`` selects dynamic MXFP8 activations (W4A8): x and every
+    expert's h are quantised per block of 32 along the reduction axis
+    (``quant_dequant_mxfp8``).  The router is not affected: it reads the
+    unquantised x.
     """
     x = np.asarray(x, dtype=np.float64)
     idx = np.asarray(idx)
@@ -359,9 +412,11 @@ def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
     if a8 is not None:
         x = quant_dequant_e4m3(x, a8[0])
         a2 = [float(v) for v in a8[1]]
+    if amx:
+        x = quant_dequant_mxfp8(x)
     out_shared = np.zeros((T, H))
     if shared is not None:
-        out_shared = swiglu_expert(x, *shared, a2=a2[E])
+        out_shared = swiglu_expert(x, *shared, a2=a2[E], amx=amx)
     if T == 0 or K == 0:
         return out_shared
     flat_idx = idx.reshape(-1)
@@ -372,7 +427,7 @@ def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
         if not mask.any():
             continue
         wg, wu, wd = experts(e)
-        expert_out[mask] = swiglu_expert(x_rep[mask], wg, wu, wd, a2=a2[e])
+        expert_out[mask] = swiglu_expert(x_rep[mask], wg, wu, wd, a2=a2[e], amx=amx)
     routed = (expert_out.reshape(T, K, H) * weight[:, :, None]).sum(axis=1)
     return out_shared + routed
 
@@ -388,7 +443,8 @@ def forward(x, w_router, experts: ExpertFn, E: int, K: int,
 
 def dense_masked(x, idx, weight, experts: ExpertFn, E: int,
                  shared: Optional[Sequence[np.ndarray]] = None,
-                 a8: Optional[Tuple[float, Sequence[float]]] = None) -> np.ndarray:
+                 a8: Optional[Tuple[float, Sequence[float]]] = None,
+                 amx: bool = False) -> np.ndarray:
     """Brute force: evaluate every expert on every token and mask.
 
     out[t] = shared(x_t) + sum_e M[t, e] * f_e(x_t), where M is zero except
@@ -404,10 +460,13 @@ def dense_masked(x, idx, weight, experts: ExpertFn, E: int,
             M[t, idx[t, j]] += weight[t, j]
     if a8 is not None:
         x = quant_dequant_e4m3(x, a8[0])
+    if amx:
+        x = quant_dequant_mxfp8(x)
     sc = (lambda e: None) if a8 is None else (lambda e: float(a8[1][e]))
-    out = np.zeros((T, H)) if shared is None else swiglu_expert(x, *shared, a2=sc(E))
+    out = (np.zeros((T, H)) if shared is None
+           else swiglu_expert(x, *shared, a2=sc(E), amx=amx))
     for e in range(E):
-        out = out + M[:, e:e + 1] * swiglu_expert(x, *experts(e), a2=sc(e))
+        out = out + M[:, e:e + 1] * swiglu_expert(x, *experts(e), a2=sc(e), amx=amx)
     return out
 
 

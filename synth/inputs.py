@@ -121,7 +121,8 @@ class MoEConfig:
     renorm_eps: float          # clamp of the renormalisation denominator
     bias_kind: str             # "uniform", "skew" or "none"
     w_format: str = "dtype"    # expert weights: "dtype" (as `dtype`), "fp8_e4m3" or "mxfp4"
-    act_format: str = "dtype"  # expert activations: "dtype" or "fp8_static" (W8A8)
+    act_format: str = "dtype"  # expert activations: "dtype", "fp8_static" (W8A8) or
+                               # "mxfp8" (dynamic, with MXFP4 weights: W4A8)
 
     def with_T(self, T: int) -> "MoEConfig":
         return dataclasses.replace(self, T=int(T))
@@ -180,6 +181,15 @@ CONFIGS: Dict[int, MoEConfig] = {
                   I=1536, I_shared=1536, dtype="bf16",
                   route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                   bias_kind="skew", w_format="mxfp4"),
+    # The same MXFP4 experts with dynamic MXFP8 activations (W4A8).
+    11: MoEConfig("hy3_decode_T16_w4a8", 11, 9, T=16, H=4096, E=192, K=8, I=1536,
+                  I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform", w_format="mxfp4",
+                  act_format="mxfp8"),
+    12: MoEConfig("hy3_prefill_T8192_skew_w4a8", 12, 9, T=8192, H=4096, E=192, K=8,
+                  I=1536, I_shared=1536, dtype="bf16",
+                  route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
+                  bias_kind="skew", w_format="mxfp4", act_format="mxfp8"),
 }
 
 ROUTER_SWEEP_M = (2, 64, 512, 4096)

@@ -604,3 +604,126 @@ def test_mxfp4_layer_equals_layer_on_dequantised_weights():
         up1[e] = (deq[e][0], deq[e][1], oracle.dequant_mxfp4(codes[2], sc[2] + 1))
     out2 = oracle.forward_given_route(x, r.idx, r.weight, lambda e: up1[e], c.E)
     np.testing.assert_array_equal(out2, 2.0 * out)
+
+
+# --------------------------------------------------------------------------
+# Dynamic MXFP8 activations (W4A8)
+# --------------------------------------------------------------------------
+def _nearest_e4m3_brute(q: float) -> int:
+    """E4M3 code nearest to q (saturating at 448), ties to the even code, by
+    search over every finite code."""
+    best, bestd = None, None
+    for c in range(256):
+        if (c & 0x7F) == 0x7F:
+            continue
+        v = float(oracle.fp8_e4m3_value(np.array([c], dtype=np.uint8))[0])
+        if math.copysign(1.0, v) != math.copysign(1.0, q) and v != 0.0:
+            continue
+        d = abs(min(abs(q), 448.0) * math.copysign(1.0, q) - v)
+        if bestd is None or d < bestd or (d == bestd and (c & 1) == 0 and (best & 1) == 1):
+            best, bestd = c, d
+    if best is not None and float(oracle.fp8_e4m3_value(np.array([best], np.uint8))[0]) == 0.0:
+        best = 0x80 if math.copysign(1.0, q) < 0 else 0x00
+    return best
+
+
+def test_mxfp8_quant_against_brute_force():
+    """Per block: scale 2^(floor(log2 amax) - 8) from the float's exponent;
+    per element: the nearest E4M3 value of v / scale by exhaustive search."""
+    rng = np.random.default_rng(21)
+    rows = rng.standard_normal((3, 96)) * np.exp2(rng.integers(-20, 12, (3, 1)))
+    rows[1, 32:64] *= 1e-6                       # a block far smaller than its row
+    rows[2, 64:96] = 0.0                         # an all-zero block
+    v32 = rows.astype(np.float32)
+    codes, sc = oracle.quant_mxfp8(v32)
+    for r in range(3):
+        for b in range(3):
+            blk = [float(x) for x in v32[r, 32 * b:32 * b + 32]]
+            amax = max(abs(x) for x in blk)
+            if amax == 0:
+                assert sc[r, b] == 0 and (codes[r, 32 * b:32 * b + 32] & 0x7F == 0).all()
+                continue
+            e = math.frexp(amax)[1] - 1 - 8
+            assert sc[r, b] == e + 127
+            for k, x in enumerate(blk):
+                assert codes[r, 32 * b + k] == _nearest_e4m3_brute(x / 2.0 ** e), (r, b, k)
+
+
+def test_mxfp8_round_trip_and_saturation():
+    rng = np.random.default_rng(22)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    codes = rng.choice(finite, size=(4, 64))
+    codes[:, 0] = 0x78                           # 256: the largest element sets the scale
+    codes[:, 32] = 0xFD                          # -416
+    codes[:, 1:32] &= 0xBF                       # the rest below 256 in magnitude
+    codes[:, 33:64] &= 0xBF
+    s = rng.integers(100, 140, (4, 2)).astype(np.uint8)
+    v = oracle.dequant_mxfp8(codes, s)
+    c2, s2 = oracle.quant_mxfp8(v)
+    np.testing.assert_array_equal(s2, s)
+    np.testing.assert_array_equal(oracle.dequant_mxfp8(c2, s2), v)
+    # a block maximum in (448, 512) x scale saturates to 448 x scale
+    w = np.zeros((1, 32))
+    w[0, 0], w[0, 1] = 500.0, 100.0
+    c3, s3 = oracle.quant_mxfp8(w)
+    assert s3[0, 0] == 127 and oracle.dequant_mxfp8(c3, s3)[0, 0] == 448.0
+
+
+def _w4a8_small(seed, T=12, H=128, E=5, K=2, I=64, I_shared=64):
+    inp = random_small(seed, T, H, E, K, I, I_shared, dtype="bf16", w_format="mxfp4")
+    c = inp.cfg
+    experts = {}
+    for e in range(c.E):
+        codes, sc = inp.expert_mxfp4(e)
+        experts[e] = tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(codes, sc))
+    codes, sc = inp.shared_mxfp4()
+    shared = tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(codes, sc))
+    r = oracle.route(inp.x_f64(), inp.w_router().astype(np.float64), c.K, 0,
+                     inp.bias().astype(np.float64), c.scale)
+    return inp, experts, shared, r
+
+
+@pytest.mark.parametrize("seed", [5, 6])
+def test_w4a8_layer_eager_equals_dense_masked(seed):
+    inp, experts, shared, r = _w4a8_small(seed)
+    c = inp.cfg
+    x = inp.x_f64()
+    got = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared, amx=True)
+    ref = oracle.dense_masked(x, r.idx, r.weight, lambda e: experts[e], c.E, shared, amx=True)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_w4a8_layer_scalar_loops():
+    """One token at a time with element loops: x quantised per 32-block, each
+    picked expert's h quantised per 32-block, weighted sum."""
+    inp, experts, shared, r = _w4a8_small(7, T=2, H=64, E=4, K=2, I=64, I_shared=64)
+    c = inp.cfg
+    x = inp.x_f64()
+    got = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared,
+                                     amx=True)
+    for t in range(c.T):
+        xq = list(oracle.quant_dequant_mxfp8(x[t:t + 1])[0])
+        ref = [0.0] * c.H
+        picks = [(int(r.idx[t, j]), float(r.weight[t, j])) for j in range(c.K)] + [(c.E, 1.0)]
+        for e, w in picks:
+            wg, wu, wd = experts[e] if e < c.E else shared
+            h = []
+            for i in range(wg.shape[0]):
+                g = math.fsum(xq[k] * wg[i, k] for k in range(c.H))
+                u = math.fsum(xq[k] * wu[i, k] for k in range(c.H))
+                h.append(g / (1.0 + math.exp(-g)) * u)
+            hq = list(oracle.quant_dequant_mxfp8(np.array([h]))[0])
+            for n in range(c.H):
+                ref[n] += w * math.fsum(hq[i] * wd[n, i] for i in range(len(hq)))
+        np.testing.assert_allclose(got[t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_w4a8_layer_is_within_the_quantisation_error_of_w4a16():
+    inp, experts, shared, r = _w4a8_small(8, T=64, H=128, E=6, K=2, I=64, I_shared=64)
+    c = inp.cfg
+    x = inp.x_f64()
+    ref = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared)
+    got = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared,
+                                     amx=True)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 0.005 < rel < 0.08, rel
