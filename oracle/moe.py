@@ -66,7 +66,9 @@ values).  Each block of 32 consecutive values of an activation row (x
 along H, h along I) shares an E8M0 scale set from the block's maximum as
 the OCP microscaling conversion does (floor(log2 amax) - 8), and the
 values are E4M3 codes of v / scale (saturating, nearest even), decided in
-float32 (h rounded from float64 to float32 first).
+float32.  The dynamic quantisation is an operator on the layer's bfloat16
+activation tensors: x is bfloat16 already, and h is the SwiGLU output
+rounded to bfloat16 (round_bf16) before it is quantised.
 
 Static FP8 activations (W8A8; the CANN article, section 8.2 and the FP8
 path of section 六, where an FP8 Linear quantises its input with a static
@@ -341,6 +343,14 @@ def quant_dequant_mxfp8(v: np.ndarray) -> np.ndarray:
     return dequant_mxfp8(*quant_mxfp8(v))
 
 
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """v rounded to float32 and then to bfloat16 (8 significant bits, round
+    to nearest even), as float64."""
+    v64 = np.asarray(v, dtype=np.float32).astype(np.float64)
+    m, e = np.frexp(v64)                                    # v = m 2^e, |m| in [0.5, 1)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
 # --------------------------------------------------------------------------
 # Experts
 # --------------------------------------------------------------------------
@@ -360,8 +370,9 @@ def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
     With ``a2`` (static FP8 activations, W8A8), the down projection's input
     h is first quantised to E4M3 with the static scale a2 and dequantised
     (``quant_dequant_e4m3``), as an FP8 Linear quantises its input.  With
-    ``amx`` (dynamic MXFP8 activations, W4A8) h is quantised per block of 32
-    along I instead (``quant_dequant_mxfp8``).
+    ``amx`` (dynamic MXFP8 activations, W4A8) h, as the layer's bfloat16
+    activation tensor (``round_bf16``), is quantised per block of 32 along I
+    instead (``quant_dequant_mxfp8``).
     """
     a = np.asarray(a, dtype=np.float64)
     g = a @ np.asarray(w_gate, dtype=np.float64).T
@@ -370,7 +381,7 @@ def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
     if a2 is not None:
         h = quant_dequant_e4m3(h, a2)
     if amx:
-        h = quant_dequant_mxfp8(h)
+        h = quant_dequant_mxfp8(round_bf16(h))
     return h @ np.asarray(w_down, dtype=np.float64).T
 
 

@@ -693,9 +693,20 @@ def test_w4a8_layer_eager_equals_dense_masked(seed):
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
 
 
+def test_round_bf16_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(23)
+    v = (rng.standard_normal(100_000) * np.exp2(rng.uniform(-30, 30, 100_000))).astype(np.float32)
+    v[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0]   # ties
+    ref = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(oracle.round_bf16(v), ref)
+
+
 def test_w4a8_layer_scalar_loops():
     """One token at a time with element loops: x quantised per 32-block, each
-    picked expert's h quantised per 32-block, weighted sum."""
+    picked expert's h (rounded to bfloat16 by torch) quantised per 32-block,
+    weighted sum."""
+    torch = pytest.importorskip("torch")
     inp, experts, shared, r = _w4a8_small(7, T=2, H=64, E=4, K=2, I=64, I_shared=64)
     c = inp.cfg
     x = inp.x_f64()
@@ -712,7 +723,8 @@ def test_w4a8_layer_scalar_loops():
                 g = math.fsum(xq[k] * wg[i, k] for k in range(c.H))
                 u = math.fsum(xq[k] * wu[i, k] for k in range(c.H))
                 h.append(g / (1.0 + math.exp(-g)) * u)
-            hq = list(oracle.quant_dequant_mxfp8(np.array([h]))[0])
+            hb = torch.tensor(h, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+            hq = list(oracle.quant_dequant_mxfp8(hb[None, :])[0])
             for n in range(c.H):
                 ref[n] += w * math.fsum(hq[i] * wd[n, i] for i in range(len(hq)))
         np.testing.assert_allclose(got[t], ref, rtol=1e-12, atol=1e-13)
