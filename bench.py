@@ -33,7 +33,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4, "decode_fp8": 5, "prefill_fp8": 6,
-             "decode_w8a8": 7, "prefill_w8a8": 8, "decode_mxfp4": 9, "prefill_mxfp4": 10}
+             "decode_w8a8": 7, "prefill_w8a8": 8, "decode_mxfp4": 9, "prefill_mxfp4": 10,
+             "decode_w4a8": 11, "prefill_w4a8": 12}
 ROUTER_WORKLOAD = 3            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
@@ -188,6 +189,8 @@ def main():
     # their bf16 values on the others
     fp8_mma = c.act_format == "fp8_static" and tile_rows == 256
     ab = 1 if fp8_mma else eb                         # bytes per x / h element
+    if c.act_format == "mxfp8" and tile_rows < 128:   # codes + a scale byte per 32
+        ab = 1 + 1 / 32
     peak_mma = PEAK_FP8_TFLOPS if fp8_mma else PEAK_BF16_TFLOPS
     T, H, E, K, I, Is = c.T, c.H, c.E, c.K, c.I, c.I_shared
     R = T * K + (T if Is else 0)
@@ -254,8 +257,9 @@ def main():
         "config": {"workload": c.name, "T": T, "H": H, "E": E, "K": K, "I": I, "I_shared": Is,
                    "route": "sigmoid+bias" if c.route_mode == 0 else "softmax",
                    "expert_weights": c.w_format if c.w_format != "dtype" else c.dtype,
-                   "expert_activations": ("fp8_e4m3_static" if c.act_format == "fp8_static"
-                                          else c.dtype)},
+                   "expert_activations": {"fp8_static": "fp8_e4m3_static",
+                                          "mxfp8": "mxfp8_dynamic"}.get(c.act_format,
+                                                                        c.dtype)},
         "roofline": roof, "cpu_baseline": cpu, "layer": layer,
         "graph_ms_per_step": graph_ms,
     }
@@ -442,7 +446,8 @@ def cpu_baseline(inp, args, gpu_idx):
     while reps < 3 or (dt < args.cpu_seconds and reps < 10000):
         t1 = time.perf_counter()
         r = oracle.route(x64, wr, c.K, c.route_mode, b64, c.scale, c.renorm_eps)
-        oracle.forward_given_route(x64, r.idx, r.weight, ws.__getitem__, c.E, sh, a8=a8)
+        oracle.forward_given_route(x64, r.idx, r.weight, ws.__getitem__, c.E, sh, a8=a8,
+                                   amx=c.act_format == "mxfp8")
         dt += time.perf_counter() - t1
         reps += 1
     del ws

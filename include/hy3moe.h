@@ -111,6 +111,15 @@ extern "C" {
  * unquantised x. */
 #define HY3MOE_AFMT_DTYPE      0
 #define HY3MOE_AFMT_FP8_STATIC 1
+/* MXFP8 (W4A8 with w_format MXFP4; the CANN deployment article, section 8.2:
+ * routed experts W4A8; section 六: dynamic MXFP8 values): x and every
+ * group's h are quantised per block of 32 consecutive values of a row (along
+ * H and I) by the OCP microscaling rule: E8M0 scale 2^(floor(log2 amax) - 8)
+ * (floored at 2^-127), elements E4M3(v / scale), saturating, nearest even.
+ * The weight-streaming path multiplies MXFP4 weights by the MXFP8 codes with
+ * block-scaled FP4 x FP8 MFMAs; the tile paths multiply the same values in
+ * bf16. */
+#define HY3MOE_AFMT_MXFP8      2
 
 /* Shape and mode of one layer call. */
 typedef struct hy3moe_config {
@@ -150,8 +159,8 @@ typedef struct hy3moe_config {
  * [E, H, I/2], shared [I_shared, H/2] / [H, I_shared/2]) and
  *   w_gate_mx, w_up_mx [E, I, H/32], w_down_mx [E, H, I/32]   E8M0 bytes
  *   ws_gate_mx, ws_up_mx [I_shared, H/32], ws_down_mx [H, I_shared/32]
- * are required (NULL only for the shared ones when I_shared == 0); the
- * float scale pointers are then ignored. */
+ * are required (16-byte aligned; NULL only for the shared ones when
+ * I_shared == 0); the float scale pointers are then ignored. */
 typedef struct hy3moe_weights {
   const float *w_router;
   const float *expert_bias;
@@ -200,7 +209,13 @@ typedef struct hy3moe_ws_layout {
                             for bf16 batches of T >= 1024 (0 = not used)           */
   size_t xq;             /* act_format FP8_STATIC: quantised x [T][H], E4M3 bytes on
                             the large-tile path, else their bf16 values (0 = not
-                            used); h then holds h quantised the same way        */
+                            used); h then holds h quantised the same way.
+                            MXFP8: x as E4M3 bytes (weight-streaming path) or the
+                            bf16 values of the MXFP8 codes (tile paths)         */
+  size_t xs;             /* MXFP8: E8M0 scales of x [T][H/32] (0 = not used)   */
+  size_t hq;             /* MXFP8, weight-streaming path: E4M3 codes of h [R][I_max];
+                            the tile paths rewrite h in place with the bf16 values */
+  size_t hs;             /* MXFP8: E8M0 scales of h [R][I_max/32]              */
 } hy3moe_ws_layout;
 
 /* Workspace size in bytes for hy3moe_forward (for_forward != 0) or for

@@ -27,9 +27,10 @@ HY3MOE_WFMT_FP8_E4M3 = 1
 HY3MOE_WFMT_MXFP4 = 2
 HY3MOE_AFMT_DTYPE = 0
 HY3MOE_AFMT_FP8_STATIC = 1
+HY3MOE_AFMT_MXFP8 = 2
 
 HY3MOE_N_STAGES = 6
-ABI_VERSION = 5          # hy3moe_abi_version() of the library this binding matches
+ABI_VERSION = 6          # hy3moe_abi_version() of the library this binding matches
 STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 
 EXPORTED_SYMBOLS = (
@@ -69,7 +70,8 @@ class hy3moe_ws_layout(ctypes.Structure):
         ("hist", ctypes.c_size_t), ("n_chunks", ctypes.c_int32),
         ("tiles", ctypes.c_size_t), ("max_tiles", ctypes.c_int32),
         ("tile_rows", ctypes.c_int32), ("h", ctypes.c_size_t), ("y", ctypes.c_size_t),
-        ("w_planes", ctypes.c_size_t), ("xq", ctypes.c_size_t),
+        ("w_planes", ctypes.c_size_t), ("xq", ctypes.c_size_t), ("xs", ctypes.c_size_t),
+        ("hq", ctypes.c_size_t), ("hs", ctypes.c_size_t),
     ]
 
 
@@ -146,8 +148,9 @@ def make_config(T: int, H: int, E: int, K: int, I: int, I_shared: int, dtype: st
                          w_format={"fp8_e4m3": HY3MOE_WFMT_FP8_E4M3,
                                    "mxfp4": HY3MOE_WFMT_MXFP4}.get(w_format,
                                                                    HY3MOE_WFMT_DTYPE),
-                         act_format=(HY3MOE_AFMT_FP8_STATIC if act_format == "fp8_static"
-                                     else HY3MOE_AFMT_DTYPE))
+                         act_format={"fp8_static": HY3MOE_AFMT_FP8_STATIC,
+                                     "mxfp8": HY3MOE_AFMT_MXFP8}.get(act_format,
+                                                                     HY3MOE_AFMT_DTYPE))
 
 
 def hy3moe_workspace_bytes(cfg: hy3moe_config, for_forward: bool = True) -> int:

@@ -48,8 +48,12 @@ int validate_cfg(const hy3moe_config *c) {
   // MXFP4: 128 K values per 64-byte step of a streamed weight row.
   if (c->w_format == HY3MOE_WFMT_MXFP4 && (c->H % 128 || c->I % 128 || c->I_shared % 128))
     return HY3MOE_ERR_UNSUPPORTED;
-  if (c->act_format != HY3MOE_AFMT_DTYPE && c->act_format != HY3MOE_AFMT_FP8_STATIC)
+  if (c->act_format != HY3MOE_AFMT_DTYPE && c->act_format != HY3MOE_AFMT_FP8_STATIC &&
+      c->act_format != HY3MOE_AFMT_MXFP8)
     return HY3MOE_ERR_INVALID;
+  // Dynamic MXFP8 activations go with MXFP4 weights.
+  if (c->act_format == HY3MOE_AFMT_MXFP8 && c->w_format != HY3MOE_WFMT_MXFP4)
+    return HY3MOE_ERR_UNSUPPORTED;
   // Static FP8 activations go with FP8 weights.
   if (c->act_format == HY3MOE_AFMT_FP8_STATIC && c->w_format != HY3MOE_WFMT_FP8_E4M3)
     return HY3MOE_ERR_UNSUPPORTED;
@@ -104,8 +108,13 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
   const int eb = elt_bytes(c->dtype);
   L->h = off;           off += al((size_t)R * Imax * eb);
   L->y = off;           off += al((size_t)R * H * eb);
-  if (c->act_format == HY3MOE_AFMT_FP8_STATIC) {
+  if (c->act_format == HY3MOE_AFMT_FP8_STATIC || c->act_format == HY3MOE_AFMT_MXFP8) {
     L->xq = off;        off += al((size_t)T * H * 2);
+  }
+  if (c->act_format == HY3MOE_AFMT_MXFP8) {
+    L->xs = off;        off += al((size_t)T * H / 32);
+    L->hq = off;        off += al((size_t)R * Imax);
+    L->hs = off;        off += al((size_t)R * Imax / 32);
   }
   L->total = off;
 }
@@ -119,7 +128,7 @@ int check_launch(hipError_t e) { return e == hipSuccess ? HY3MOE_OK : HY3MOE_ERR
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 5; }
+int hy3moe_abi_version(void) { return 6; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {
@@ -204,8 +213,8 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
     if (!w->w_gate_mx || !w->w_up_mx || !w->w_down_mx ||
         (has_shared && (!w->ws_gate_mx || !w->ws_up_mx || !w->ws_down_mx)))
       return HY3MOE_ERR_INVALID;
-    if (!al4(w->w_gate_mx) || !al4(w->w_up_mx) || !al4(w->w_down_mx) ||
-        (has_shared && (!al4(w->ws_gate_mx) || !al4(w->ws_up_mx) || !al4(w->ws_down_mx))))
+    if (!al16(w->w_gate_mx) || !al16(w->w_up_mx) || !al16(w->w_down_mx) ||
+        (has_shared && (!al16(w->ws_gate_mx) || !al16(w->ws_up_mx) || !al16(w->ws_down_mx))))
       return HY3MOE_ERR_ALIGN;
   }
   const bool a8 = cfg->act_format == HY3MOE_AFMT_FP8_STATIC;
@@ -247,7 +256,15 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   // as code bytes for the large-tile path's FP8 MFMAs, else as their bf16
   // values)
   const int path = path_of(cfg);
+  const bool amx = cfg->act_format == HY3MOE_AFMT_MXFP8;
   const void *act = x;
+  if (amx) {   // codes and scales for the weight-streaming path, else bf16 values
+    rc = check_launch(launch_quant_mxfp8(x, (int64_t)T * H, ws + L.xq,
+                                         reinterpret_cast<uint8_t *>(ws + L.xs),
+                                         path == PATH_SKINNY ? 0 : 1, s));
+    if (rc) return rc;
+    act = ws + L.xq;
+  }
   if (a8) {
     rc = check_launch(launch_quant_e4m3(x, cfg->dtype, (int64_t)T * H, w->x_scale, ws + L.xq,
                                         path == PATH_BIG ? 0 : 1, s));
@@ -290,6 +307,8 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.a8 = a8 ? 1 : 0;
   ea.xs = a8 ? w->x_scale : nullptr;
   ea.hs = a8 ? w->h_scale : nullptr;
+  ea.amx = amx && path == PATH_SKINNY ? 1 : 0;
+  ea.act_sc = amx ? reinterpret_cast<const uint8_t *>(ws + L.xs) : nullptr;
   ea.w_fp4 = fp4 ? 1 : 0;
   ea.mx0 = fp4 ? w->w_gate_mx : nullptr;
   ea.mx1 = fp4 ? w->w_up_mx : nullptr;
@@ -299,6 +318,18 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   if (rc) return rc;
   mark();
   ea.act = ws + L.h; ea.w0 = w->w_down; ea.w1 = nullptr; ea.ws0 = w->ws_down; ea.ws1 = nullptr;
+  if (amx) {   // h, dynamic MXFP8 per 32 along I: codes + scales, or bf16 values in place
+    const int64_t nh = ((int64_t)T * K + (has_shared ? T : 0)) * Imax;
+    if (path == PATH_SKINNY) {
+      rc = check_launch(launch_quant_mxfp8(ws + L.h, nh, ws + L.hq,
+                                           reinterpret_cast<uint8_t *>(ws + L.hs), 0, s));
+      ea.act = ws + L.hq;
+      ea.act_sc = reinterpret_cast<const uint8_t *>(ws + L.hs);
+    } else {
+      rc = check_launch(launch_quant_mxfp8(ws + L.h, nh, ws + L.h, nullptr, 1, s));
+    }
+    if (rc) return rc;
+  }
   ea.out = ws + L.y;
   ea.sc0 = fp8 ? w->w_down_scale : nullptr;
   ea.sc1 = nullptr;

@@ -9,7 +9,9 @@ namespace hy3moe {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 // Storage of the expert weights inside the GEMM kernels.
-enum { WF_DTYPE = 0, WF_FP8 = 1, WF_MXFP4 = 2 };
+// WF_W4A8: MXFP4 weights with dynamic MXFP8 token rows (E4M3 codes and one
+// E8M0 scale per 32), multiplied by block-scaled FP4 x FP8 MFMAs.
+enum { WF_DTYPE = 0, WF_FP8 = 1, WF_MXFP4 = 2, WF_W4A8 = 3 };
 
 // Row-tile shapes of the expert GEMMs.
 constexpr int TILED_ROWS = 128;     // rows (token copies) per tile, large-T path
@@ -83,6 +85,12 @@ struct ExpertArgs {
   // mxs0/mxs1 (shared, [rows][K/32]) one E8M0 scale per 32 weights of a row.
   int w_fp4;
   const uint8_t *mx0, *mx1, *mxs0, *mxs1;
+  // Dynamic MXFP8 token rows (amx = 1, weight-streaming path): act holds
+  // E4M3 codes (rows of H or ldh bytes) and act_sc their E8M0 scales (rows
+  // of H / 32 or ldh / 32 bytes).  The tile paths read the exact bf16 values
+  // instead (amx = 0 there).
+  int amx;
+  const uint8_t *act_sc;
   // Static FP8 activations (a8 = 1, with w_fp8): act holds E4M3 codes on the
   // large-tile path and their exact bf16 values on the other two; *xs is the
   // scale of x and hs[g] that of group g's h (hs[E]: shared).  The gate-up
@@ -99,6 +107,13 @@ hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStrea
 // otherwise.
 hipError_t launch_quant_e4m3(const void *x, int dtype, int64_t n, const float *scale, void *q,
                              int carrier, hipStream_t stream);
+
+// Dynamic MXFP8 quantisation of n bf16 values (rows of a multiple of 32):
+// carrier = 0 writes E4M3 codes (q, n bytes) and one E8M0 scale per 32
+// (scales, n / 32 bytes); carrier = 1 writes the exact bf16 values (q, n
+// bf16; may be `in` itself).  n % 32 == 0, 16-byte aligned buffers.
+hipError_t launch_quant_mxfp8(const void *in, int64_t n, void *q, uint8_t *scales, int carrier,
+                              hipStream_t stream);
 
 // Combine ---------------------------------------------------------------------
 hipError_t launch_combine(const void *y, const int32_t *pos_of, const float *weight,

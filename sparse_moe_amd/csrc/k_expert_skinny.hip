@@ -33,6 +33,18 @@
 // scale byte it also loads -- and decodes them, scale applied, to four bf16
 // fragments (v_cvt_scalef32_pk_bf16_fp4, exact); the token rows supply the
 // matching 64 bytes, and four MFMAs per weight fragment take a step.
+//
+// W4A8 (MXFP4 weights, token rows as dynamic MXFP8: E4M3 codes with one E8M0
+// scale per 32): one block-scaled v_mfma_f32_16x16x128_f8f6f4 (FP4 A, FP8 B)
+// takes a step of a weight fragment -- no decode, and half the token bytes
+// of bf16.  Measured operand layout of that instruction with an FP4 A: lane
+// group g of A holds 32 FP4 values whose K positions (in B's byte order,
+// B lane group g' byte q = position 32g' + q) are two runs of 16:
+// 64 (g & 1) + 16 (g >> 1) + [0, 16) and that + 32; and the E8M0 scale in
+// lane group c, on either side, covers exactly A lane group c's 32
+// positions.  So A lane g takes weight block g of the step (16 contiguous
+// bytes, its own scale), and B lane g takes token bytes [16g, 16g + 16) and
+// [64 + 16g, 64 + 16g + 16) of the step with token block g's scale.
 #include "common.cuh"
 #include "internal.h"
 
@@ -50,12 +62,27 @@ template <int MT, int WF>
 constexpr int steps_per_set() {
   return WF == WF_FP8     ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1))
          : WF == WF_MXFP4 ? (MT == 1 ? 3 : (MT == 2 ? 2 : 1))
+         : WF == WF_W4A8  ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
                           : UBASE / MT;
 }
 // 16-byte token chunks per 64-byte weight step.
 template <int WF>
 constexpr int token_chunks() {
-  return WF == WF_MXFP4 ? 4 : (WF == WF_FP8 ? 2 : 1);
+  return WF == WF_MXFP4 ? 4 : ((WF == WF_FP8 || WF == WF_W4A8) ? 2 : 1);
+}
+
+// One block-scaled 16x16x128 MFMA: A = 32 FP4 E2M1 weights of the lane (16
+// bytes) with E8M0 scale sa, B = 32 FP8 E4M3 token values (two 16-byte
+// chunks) with E8M0 scale sb.
+__device__ __forceinline__ void mma_fp4_fp8(f32x4_t &acc, const uint4 &w, uint32_t sa,
+                                            const uint4 &x0, const uint4 &x1, uint32_t sb) {
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  const i32x8_t av = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+  const i32x8_t bv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  // formats: 4 = FP4 E2M1 (A), 0 = FP8 E4M3 (B); scale byte 0 of each operand
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 0, 0, (int)sa, 0,
+                                                         (int)sb);
 }
 
 // Where a unit's operands are (per lane) and what its epilogue needs.
@@ -64,6 +91,8 @@ struct UnitSrc {
   const char *w0p, *w1p;   // the two 16-row weight fragments (gate/up, or two down blocks)
   const char *xp[MT];      // token rows (gathered x for gate-up, h rows for down)
   const uint8_t *s0p, *s1p;  // MXFP4: the lane's scale bytes of the two fragments
+  const uint8_t *xsp[MT];    // W4A8: the lane's scale bytes of the token rows
+  bool vs;                   // W4A8: scale rows allow 16-byte loads of 4 steps
   int nsub;                // 64-byte K steps per row
   int nf;                  // fragments streamed (2; 1 for half of a down unit)
 };
@@ -80,7 +109,8 @@ struct UnitOut {
 template <typename T, bool GATE_UP, int MT, int WF>
 __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_blocks, int lane,
                                         UnitSrc<MT> &src, UnitOut &o, int half = 0) {
-  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4;
+  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4 || WF == WF_W4A8;
+  constexpr bool MXA = WF == WF_W4A8;
   constexpr int EB = Elem<T>::kBytes;
   // bytes per weight row of K elements (MXFP4: half a byte per element)
   auto rowb = [](int K) { return F4 ? K / 2 : K * (F8 ? 1 : EB); };
@@ -143,8 +173,17 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
     const size_t arow = GATE_UP ? (size_t)a.sorted_token[trow] * a.H : (size_t)trow * a.ldh;
     // bf16 weights: chunk g of each 64-byte step; FP8: bytes [32g, 32g+32) of
     // each 128-byte step of the token row; MXFP4: bytes [64g, 64g+64) of each
-    // 256-byte step (the K values of the lane's codes)
-    src.xp[m] = reinterpret_cast<const char *>(act + arow) + cg * 16 * token_chunks<WF>();
+    // 256-byte step (the K values of the lane's codes); W4A8: code bytes
+    // [32g, 32g+32) of each 128-byte step, and block scale step * 4 + g
+    if (MXA) {   // bytes [16g, 16g + 16) and [64 + 16g, ...) of each 128-byte step
+      src.xp[m] = static_cast<const char *>(a.act) + arow + cg * 16;
+      src.xsp[m] = a.act_sc + arow / 32 + cg;
+      // K % 512 == 0: weight scale rows of K/32 bytes are 16-byte multiples,
+      // and so are the token scale rows (x: K = H; h: rows of ldh / 32)
+      src.vs = (o.nsub & 3) == 0 && (GATE_UP || a.ldh % 512 == 0);
+    } else {
+      src.xp[m] = reinterpret_cast<const char *>(act + arow) + cg * 16 * token_chunks<WF>();
+    }
   }
   return true;
 }
@@ -213,7 +252,7 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
 template <typename T, bool GATE_UP, int MT, int WF>
 __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(ExpertArgs a,
                                                                           int n_col_blocks) {
-  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4;
+  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4, MXA = WF == WF_W4A8;
   constexpr int U = steps_per_set<MT, WF>();   // 64-byte K steps per row per register set
   constexpr int XN = token_chunks<WF>();       // 16-byte token chunks per step
   const int lane = threadIdx.x & 63;
@@ -244,23 +283,66 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   uint4 aw0[U], aw1[U], ax[U][MT][XN];
   uint4 bw0[U], bw1[U], bx[U][MT][XN];
   uint32_t as0[U], as1[U], bs0[U], bs1[U];   // MXFP4: the lane's block scale codes
+  uint32_t axs[U][MT], bxs[U][MT];           // W4A8: the token rows' block scale codes
   // Load the next block of the loading unit into set W0/W1/X, then move the
   // loading position on (to the next unit at the end of this one).  Steps past
   // nsub re-read the last step (in bounds) and are not used.
-#define HY3_LOAD(W0, W1, X, S0, S1)                                                    \
+  // W4A8, 4 steps per register set: the scales of steps st .. st + 3 (all four
+  // lane groups) are 16 contiguous bytes of a scale row when the unit's K is
+  // a multiple of 512 (then st % 4 == 0 and st + 3 < nsub, or st >= nsub;
+  // the rows are 16-byte aligned): one load per row instead of four byte
+  // loads per lane.
+  // The lane's byte of step st + v is byte g of word v, shifted to byte 0
+  // (the MFMA reads byte 0 of the scale register).  Otherwise byte loads.
+#define HY3_SCALES4(S0, S1, XS, u, st)                                                 \
+  {                                                                                    \
+    const int sh_ = 8 * (lane >> 4);                                                   \
+    if (src.vs) {                                                                      \
+      /* past the end: a valid group of 4 steps, not used */                          \
+      const int s4_ = (st) < src.nsub ? (st) : src.nsub - 4;                           \
+      const uint4 w0_ = *reinterpret_cast<const uint4 *>(src.s0p - (lane >> 4) + s4_ * 4); \
+      S0[(u) + 0] = w0_.x >> sh_; S0[(u) + 1] = w0_.y >> sh_;                          \
+      S0[(u) + 2] = w0_.z >> sh_; S0[(u) + 3] = w0_.w >> sh_;                          \
+      if (src.nf == 2) {                                                               \
+        const uint4 w1_ = *reinterpret_cast<const uint4 *>(src.s1p - (lane >> 4) + s4_ * 4); \
+        S1[(u) + 0] = w1_.x >> sh_; S1[(u) + 1] = w1_.y >> sh_;                        \
+        S1[(u) + 2] = w1_.z >> sh_; S1[(u) + 3] = w1_.w >> sh_;                        \
+      }                                                                                \
+      _Pragma("unroll") for (int m = 0; m < MT; ++m) {                                 \
+        const uint4 x_ = *reinterpret_cast<const uint4 *>(src.xsp[m] - (lane >> 4) + s4_ * 4); \
+        XS[(u) + 0][m] = x_.x >> sh_; XS[(u) + 1][m] = x_.y >> sh_;                    \
+        XS[(u) + 2][m] = x_.z >> sh_; XS[(u) + 3][m] = x_.w >> sh_;                    \
+      }                                                                                \
+    } else {                                                                           \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                  \
+        const int sv_ = (st) + v < src.nsub ? (st) + v : src.nsub - 1;                 \
+        S0[(u) + v] = src.s0p[sv_ * 4];                                                \
+        if (src.nf == 2) S1[(u) + v] = src.s1p[sv_ * 4];                               \
+        _Pragma("unroll") for (int m = 0; m < MT; ++m) XS[(u) + v][m] = src.xsp[m][sv_ * 4]; \
+      }                                                                                \
+    }                                                                                  \
+  }
+#define HY3_LOAD(W0, W1, X, S0, S1, XS)                                                \
   {                                                                                    \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       const int st_ = s_ld + u < src.nsub ? s_ld + u : src.nsub - 1;                  \
       const int o_ = st_ * 64;                                                         \
       W0[u] = *reinterpret_cast<const uint4 *>(src.w0p + o_);                          \
       if (src.nf == 2) W1[u] = *reinterpret_cast<const uint4 *>(src.w1p + o_);         \
-      if constexpr (F4) {                                                              \
+      if constexpr (F4 || (MXA && U % 4 != 0)) {                                       \
         S0[u] = src.s0p[st_ * 4];                                                      \
         if (src.nf == 2) S1[u] = src.s1p[st_ * 4];                                     \
       }                                                                                \
+      if constexpr (MXA && U % 4 != 0) {                                               \
+        _Pragma("unroll") for (int m = 0; m < MT; ++m) XS[u][m] = src.xsp[m][st_ * 4]; \
+      }                                                                                \
+      if constexpr (MXA && U % 4 == 0) {                                               \
+        if (u % 4 == 0) HY3_SCALES4(S0, S1, XS, u, s_ld + u);                          \
+      }                                                                                \
       _Pragma("unroll") for (int m = 0; m < MT; ++m)                                   \
         _Pragma("unroll") for (int h = 0; h < XN; ++h)                                 \
-          X[u][m][h] = *reinterpret_cast<const uint4 *>(src.xp[m] + st_ * 64 * XN + h * 16); \
+          X[u][m][h] = *reinterpret_cast<const uint4 *>(src.xp[m] + st_ * 64 * XN +      \
+                                                        h * (MXA ? 64 : 16));          \
     }                                                                                  \
     s_ld += U;                                                                         \
     if (s_ld >= src.nsub) {                                                            \
@@ -271,11 +353,17 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   }
   // Multiply one block of the multiplying unit; at its end, write the unit
   // and move on.  `more` turns false after the last unit.
-#define HY3_MMA(W0, W1, X, S0, S1)                                                     \
+#define HY3_MMA(W0, W1, X, S0, S1, XS)                                                 \
   {                                                                                    \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       if (s_mm + u < om.nsub) {                                                        \
-        if constexpr (F4) {                                                            \
+        if constexpr (MXA) {                                                           \
+          _Pragma("unroll") for (int m = 0; m < MT; ++m) {                             \
+            mma_fp4_fp8(acc[0][m], W0[u], S0[u], X[u][m][0], X[u][m][1], XS[u][m]);    \
+            if (om.nf == 2)                                                            \
+              mma_fp4_fp8(acc[1][m], W1[u], S1[u], X[u][m][0], X[u][m][1], XS[u][m]);  \
+          }                                                                            \
+        } else if constexpr (F4) {                                                     \
           const float sc0_ = e8m0_to_f32(S0[u]);                                       \
           const uint4 q0_ = W0[u];                                                     \
           const uint4 f0_[4] = {fp4x8_to_bf16(q0_.x, sc0_), fp4x8_to_bf16(q0_.y, sc0_), \
@@ -325,18 +413,19 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   }
   UnitSrc<MT> src_dummy;   // next_unit also fills operand pointers; the multiply side ignores them
   bool more = true;
-  HY3_LOAD(aw0, aw1, ax, as0, as1);
+  HY3_LOAD(aw0, aw1, ax, as0, as1, axs);
   while (more) {
-    if (k_ld < kmax) HY3_LOAD(bw0, bw1, bx, bs0, bs1);
+    if (k_ld < kmax) HY3_LOAD(bw0, bw1, bx, bs0, bs1, bxs);
     __builtin_amdgcn_sched_barrier(0);   // keep the next block's loads ahead
-    HY3_MMA(aw0, aw1, ax, as0, as1);
+    HY3_MMA(aw0, aw1, ax, as0, as1, axs);
     if (!more) break;
-    if (k_ld < kmax) HY3_LOAD(aw0, aw1, ax, as0, as1);
+    if (k_ld < kmax) HY3_LOAD(aw0, aw1, ax, as0, as1, axs);
     __builtin_amdgcn_sched_barrier(0);
-    HY3_MMA(bw0, bw1, bx, bs0, bs1);
+    HY3_MMA(bw0, bw1, bx, bs0, bs1, bxs);
   }
 #undef HY3_MMA
 #undef HY3_LOAD
+#undef HY3_SCALES4
 }
 
 // Persistent grid: WAVES_PER_SIMD wavefronts per SIMD on the 256 CUs.
@@ -376,6 +465,7 @@ hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
   if (path == PATH_SKINNY)
     return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, true, T, stream)
+           : a.amx         ? launch_skinny<bf16_t, WF_W4A8>(a, true, T, stream)
            : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, true, T, stream)
            : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, true, T, stream)
                            : launch_skinny<bf16_t, WF_DTYPE>(a, true, T, stream);
@@ -386,6 +476,7 @@ hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipSt
 hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
   if (path == PATH_SKINNY)
     return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, false, T, stream)
+           : a.amx         ? launch_skinny<bf16_t, WF_W4A8>(a, false, T, stream)
            : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, false, T, stream)
            : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, false, T, stream)
                            : launch_skinny<bf16_t, WF_DTYPE>(a, false, T, stream);

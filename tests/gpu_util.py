@@ -131,6 +131,11 @@ def shared_f64(inp: MoEInputs):
     return tuple(oracle.dequant_fp8(q, s) for q, s in zip(*sh))
 
 
+def amx_of(inp: MoEInputs) -> bool:
+    """True for dynamic MXFP8 activations (W4A8)."""
+    return inp.cfg.act_format == "mxfp8"
+
+
 def a8_of(inp: MoEInputs):
     """(a1, a2) static FP8 activation scales for the oracle, or None."""
     if inp.cfg.act_format != "fp8_static":

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 5
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 6
     for code in (0, -1, -2, -3, -4, -5):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -55,6 +55,10 @@ def cfg_of(c, **kw):
              w_format=c.w_format, act_format=c.act_format)
     d.update(kw)
     return sm.make_config(**d)
+
+
+def R_of(c):
+    return c.T * c.K + (c.T if c.I_shared else 0)
 
 
 @pytest.mark.parametrize("cfg_id", sorted(CONFIGS))
@@ -70,10 +74,16 @@ def test_workspace_layout_is_consistent(lib, cfg_id):
     assert (L.w_planes > 0) == planes
     if planes:
         names.append("w_planes")
-    assert (L.xq > 0) == (c.act_format == "fp8_static")
+    assert (L.xq > 0) == (c.act_format != "dtype")
     if L.xq:
         names.append("xq")
         assert L.total - L.xq >= c.T * c.H * 2
+    assert (L.hq > 0) == (L.xs > 0) == (L.hs > 0) == (c.act_format == "mxfp8")
+    if L.hq:
+        names += ["xs", "hq", "hs"]
+        assert L.hq - L.xs >= c.T * c.H // 32
+        assert L.hs - L.hq >= R_of(c) * max(c.I, c.I_shared)
+        assert L.total - L.hs >= R_of(c) * max(c.I, c.I_shared) // 32
     offs = sorted(getattr(L, n) for n in names)
     assert all(o % 256 == 0 for o in offs)
     assert len(set(offs)) == len(offs)
@@ -98,6 +108,8 @@ def test_workspace_layout_is_consistent(lib, cfg_id):
     (dict(w_format="mxfp4", dtype="f32"), -2), (dict(w_format="mxfp4", H=4096 + 64), -2),
     (dict(w_format="mxfp4", I=1536 + 64), -2), (dict(w_format="mxfp4", I_shared=64), -2),
     (dict(w_format="mxfp4", act_format="fp8_static"), -2),
+    # dynamic MXFP8 activations: with MXFP4 weights only
+    (dict(act_format="mxfp8"), -2), (dict(w_format="fp8_e4m3", act_format="mxfp8"), -2),
 ])
 def test_invalid_configs_rejected(lib, bad, code):
     c = CONFIGS[1]
@@ -168,7 +180,7 @@ def test_weight_format_enum_is_checked(lib):
 def test_activation_format_enum_is_checked(lib):
     cfg = cfg_of(CONFIGS[7])
     assert sm.hy3moe_workspace_bytes(cfg, True) > 0
-    cfg.act_format = 2
+    cfg.act_format = 3
     assert sm.hy3moe_workspace_bytes(cfg, True) == 0
     L = b.hy3moe_ws_layout()
     assert lib.hy3moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == -1
@@ -198,10 +210,11 @@ def test_mxfp4_weights_need_their_block_scales(lib):
         w[missing] = None
         assert fw(ctypes.byref(cfg), 4096, ctypes.byref(b.hy3moe_weights(*w)), 8192, None,
                   None, 4096, need, None) == -1, missing
-    w = list(full)
-    w[16] = 4098                                      # down scales not 4-byte aligned
-    assert fw(ctypes.byref(cfg), 4096, ctypes.byref(b.hy3moe_weights(*w)), 8192, None, None,
-              4096, need, None) == -4
+    for bad in (4098, 4100):                          # down scales not 16-byte aligned
+        w = list(full)
+        w[16] = bad
+        assert fw(ctypes.byref(cfg), 4096, ctypes.byref(b.hy3moe_weights(*w)), 8192, None,
+                  None, 4096, need, None) == -4
     # without a shared expert its scale arrays may be NULL
     cfg_ns = cfg_of(CONFIGS[9], I_shared=0)
     w = full[:17] + [None, None, None]

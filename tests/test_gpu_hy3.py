@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (MARGIN, a8_of, check_output, check_route, config_of, expert_cache, log,
+from gpu_util import (MARGIN, a8_of, amx_of, check_output, check_route, config_of, expert_cache, log,
                       oracle_route, out_to_np, shared_f64, to_torch, upload_weights,
                       with_act_scales, with_bias_of)
 from synth import CONFIGS, ROUTER_SWEEP_M, MoEInputs
@@ -63,7 +63,7 @@ def sampled_check(inp, dev, weights, n_sample=256, seed=0, workload_shape=True):
     ridx[t_is_tie] = gidx[tokens][t_is_tie]
     rw[t_is_tie] = gw[tokens][t_is_tie]
     ref = oracle.forward_given_route(x64, ridx, rw, expert_cache(inp), c.E, shared_f64(inp),
-                                     a8=a8_of(inp))
+                                     a8=a8_of(inp), amx=amx_of(inp))
     got = out_to_np(out)[tokens]
     check_output(got, ref, c.dtype, c.name, workload_shape=workload_shape)
     counts = np.bincount(gidx.reshape(-1), minlength=c.E)
@@ -88,7 +88,7 @@ def decode_full_check(inp, dev, weights, workload_shape=True):
     tie = r.margin <= MARGIN
     ridx[tie], rw[tie] = gidx[tie], gw[tie]
     ref = oracle.forward_given_route(inp.x_f64(), ridx, rw, expert_cache(inp), c.E,
-                                     shared_f64(inp), a8=a8_of(inp))
+                                     shared_f64(inp), a8=a8_of(inp), amx=amx_of(inp))
     check_output(out_to_np(out), ref, c.dtype, c.name, workload_shape=workload_shape)
 
 
@@ -208,5 +208,17 @@ def test_hy3_decode_T16_mxfp4_full(dev, hy3_mxfp4_weights):
 def test_hy3_prefill_T8192_skew_mxfp4_sampled(dev, hy3_mxfp4_weights):
     """The prefill chunk on the same MXFP4 experts (large-tile path)."""
     inp = MoEInputs(CONFIGS[10])
+    log(f"case {inp.cfg.name}")
+    sampled_check(inp, dev, hy3_mxfp4_weights, workload_shape=False)
+
+
+def test_hy3_decode_T16_w4a8_full(dev, hy3_mxfp4_weights):
+    """Hy3 decode, MXFP4 experts with dynamic MXFP8 activations (W4A8:
+    block-scaled FP4 x FP8 MFMAs), every token; derived output bound."""
+    decode_full_check(MoEInputs(CONFIGS[11]), dev, hy3_mxfp4_weights, workload_shape=False)
+
+
+def test_hy3_prefill_T8192_skew_w4a8_sampled(dev, hy3_mxfp4_weights):
+    inp = MoEInputs(CONFIGS[12])
     log(f"case {inp.cfg.name}")
     sampled_check(inp, dev, hy3_mxfp4_weights, workload_shape=False)

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (MARGIN, a8_of, check_output, check_route, config_of, expert_cache, log,
+from gpu_util import (MARGIN, a8_of, amx_of, check_output, check_route, config_of, expert_cache, log,
                       oracle_route, out_to_np, shared_f64, to_torch, upload_weights)
 from synth import CONFIGS, MoEInputs, random_small
 
@@ -39,7 +39,7 @@ def reference(inp, r, gidx, gw, tokens=None):
     if tokens is not None:
         x64, idx, w = x64[tokens], idx[tokens], w[tokens]
     return oracle.forward_given_route(x64, idx, w, expert_cache(inp), c.E, shared_f64(inp),
-                                      a8=a8_of(inp))
+                                      a8=a8_of(inp), amx=amx_of(inp))
 
 
 def run_gpu(inp, dev, weights=None, workspace=None):
@@ -159,6 +159,22 @@ SMALL = {
     "mxfp4_big_T400_softmax": dict(seed=77, T=400, H=512, E=8, K=4, I=256, I_shared=128,
                                    dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
                                    bias_kind="none", w_format="mxfp4"),
+    # W4A8: MXFP4 weights with dynamic MXFP8 activations; block-scaled FP4 x
+    # FP8 MFMAs on the weight-streaming path (1, 2 and 4 row fragments), the
+    # same values in bf16 on the tile paths
+    "w4a8_T1": dict(seed=80, T=1, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16",
+                    w_format="mxfp4", act_format="mxfp8"),
+    "w4a8_T16": dict(seed=81, T=16, H=512, E=32, K=4, I=256, I_shared=128, dtype="bf16",
+                     w_format="mxfp4", act_format="mxfp8"),
+    "w4a8_T20_noshared": dict(seed=82, T=20, H=256, E=8, K=2, I=128, I_shared=0,
+                              dtype="bf16", w_format="mxfp4", act_format="mxfp8"),
+    "w4a8_T64_softmax": dict(seed=83, T=64, H=384, E=16, K=4, I=128, I_shared=256,
+                             dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
+                             bias_kind="none", w_format="mxfp4", act_format="mxfp8"),
+    "w4a8_tiled_T300": dict(seed=84, T=300, H=512, E=24, K=4, I=256, I_shared=128,
+                            dtype="bf16", w_format="mxfp4", act_format="mxfp8"),
+    "w4a8_big_T513_H384": dict(seed=85, T=513, H=384, E=4, K=2, I=384, I_shared=128,
+                               dtype="bf16", w_format="mxfp4", act_format="mxfp8"),
 }
 
 

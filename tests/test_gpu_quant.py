@@ -173,3 +173,61 @@ def test_w8a8_codes_in_the_workspace(dev, T, E, H, path_rows):
     log(f"  T={T}: x codes exact ({c.T * c.H}); h codes {n_all}, "
         f"{n_near} within the error bound of a midpoint")
     assert n_near < (0.3 if codes_path else 0.03) * n_all
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_w4a8_codes_in_the_workspace(dev, T):
+    """Dynamic MXFP8 activations of a W4A8 forward on the weight-streaming
+    path: x codes and block scales bit-exact against the oracle; h values
+    (code x scale) equal to the oracle's except near a rounding midpoint or
+    a block-scale boundary, where they differ by at most one grid step."""
+    from gpu_util import config_of, expert_cache, shared_f64, to_torch, upload_weights
+    from synth import random_small
+    inp = random_small(90 + T, T=T, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16",
+                       w_format="mxfp4", act_format="mxfp8")
+    c = inp.cfg
+    cfg = config_of(inp)
+    L = sm.hy3moe_workspace_layout(cfg)
+    ws = sm.alloc_workspace(cfg, True, dev)
+    weights = upload_weights(inp, dev)
+    x = to_torch(inp.x(), c.dtype, dev)
+    sm.forward(cfg, x, weights, workspace=ws)
+    torch.cuda.synchronize()
+    wsh = ws.cpu().numpy()
+    x64 = inp.x_f64()
+    qx, sx = oracle.quant_mxfp8(x64)
+    np.testing.assert_array_equal(wsh[L.xs:L.xs + c.T * c.H // 32].reshape(c.T, -1), sx)
+    np.testing.assert_array_equal(wsh[L.xq:L.xq + c.T * c.H].reshape(c.T, c.H), qx)
+    offsets = wsh[L.offsets:L.offsets + 4 * (c.E + 2)].view(np.int32)
+    R = c.T * c.K + c.T
+    sorted_token = wsh[L.sorted_token:L.sorted_token + 4 * R].view(np.int32)
+    ldh = max(c.I, c.I_shared)
+    hq = wsh[L.hq:L.hq + R * ldh].reshape(R, ldh)
+    hs = wsh[L.hs:L.hs + R * ldh // 32].reshape(R, ldh // 32)
+    xh = oracle.dequant_mxfp8(qx, sx)
+    experts = expert_cache(inp)
+    shared = shared_f64(inp)
+    n_diff = n_all = 0
+    for g in range(c.E + 1):
+        r0, r1 = offsets[g], offsets[g + 1]
+        if r1 == r0:
+            continue
+        wg, wu, _ = experts(g) if g < c.E else shared
+        Ig = wg.shape[0]
+        a = xh[sorted_token[r0:r1]]
+        h64 = oracle.silu(a @ wg.T) * (a @ wu.T)
+        ref = oracle.quant_dequant_mxfp8(oracle.round_bf16(h64))
+        got = oracle.dequant_mxfp8(hq[r0:r1, :Ig], hs[r0:r1, :Ig // 32])
+        diff = got != ref
+        step = _grid_step(np.maximum(np.abs(got), np.abs(ref)) / np.repeat(
+            oracle.e8m0_value(hs[r0:r1, :Ig // 32]), 32, axis=1)) * np.repeat(
+            oracle.e8m0_value(hs[r0:r1, :Ig // 32]), 32, axis=1)
+        bad = np.abs(got - ref) > 2 * step * (1 + 1e-12)
+        if bad.any():
+            i, j = np.argwhere(bad)[0]
+            log(f"  group {g} row {i} col {j}: h={h64[i, j]:.9g} got={got[i, j]} ref={ref[i, j]}")
+        assert not bad.any()
+        n_diff += int(diff.sum())
+        n_all += got.size
+    log(f"  T={T}: x codes exact; h values {n_all}, {n_diff} one step off")
+    assert n_diff < 0.01 * n_all
