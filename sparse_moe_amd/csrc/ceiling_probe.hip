@@ -94,9 +94,35 @@ __global__ __launch_bounds__(64) void mfma_fp8_once_kernel(const i32x8_t *a, con
                                                           0, 0, 0, 0, 0, 0);
 }
 
+// Instance b: D = A B with C = 0, one block-scaled 16x16x128 MFMA with FP4
+// E2M1 A (16 bytes per lane) and FP8 E4M3 B (32 bytes per lane) and one E8M0
+// scale byte per lane on each side (byte 0 of sa[b][lane], sb[b][lane]).
+__global__ __launch_bounds__(64) void mfma_fp4fp8_once_kernel(const i32x8_t *a, const i32x8_t *b,
+                                                             const int *sa, const int *sb,
+                                                             f32x4_t *d, int n) {
+  const int inst = blockIdx.x, lane = threadIdx.x;
+  if (inst >= n) return;
+  const size_t i = (size_t)inst * 64 + lane;
+  d[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[i], f32x4_t{0.f, 0.f, 0.f, 0.f},
+                                                          4, 0, 0, sa[i], 0, sb[i]);
+}
+
 }  // namespace
 
 extern "C" {
+
+// n instances of one block-scaled FP4 x FP8 MFMA: a, b hold n x 64 lanes x
+// 32 bytes (A uses the first 16 bytes: 32 E2M1 codes, element 2j in the low
+// nibble of byte j), sa, sb n x 64 ints (E8M0 in byte 0), d n x 64 x 4 floats
+// (lane 16 c + r: rows 4 c + q, column r).
+int hy3moe_probe_mfma_fp4fp8_once(const void *a, const void *b, const int *sa, const int *sb,
+                                  float *d, int n, void *stream) {
+  if (!a || !b || !sa || !sb || !d || n <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_fp4fp8_once_kernel, dim3(n), dim3(64), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const i32x8_t *>(a),
+                     static_cast<const i32x8_t *>(b), sa, sb, reinterpret_cast<f32x4_t *>(d), n);
+  return (int)hipGetLastError();
+}
 
 // FLOPs done = n_blocks * 4 waves * iters * 16 MFMAs * 2*16*16*128.
 // `out` needs n_blocks * 256 floats.  Returns a hipError_t code.
