@@ -186,12 +186,16 @@ def main():
     web = {"fp8_e4m3": 1, "mxfp4": 0.5 + 1 / 32}.get(c.w_format, eb)
     tile_rows = sm.hy3moe_workspace_layout(cfg).tile_rows
     # static FP8 activations: E4M3 bytes on the large-tile path (FP8 MFMAs),
-    # their bf16 values on the others
-    fp8_mma = c.act_format == "fp8_static" and tile_rows == 256
+    # their bf16 values on the others; dynamic MXFP8: codes and a scale byte
+    # per 32 on the weight-streaming and large-tile paths (FP4 x FP8 MFMAs,
+    # which issue at the FP8 rate), bf16 values on the 128-row tiled path
+    fp8_mma = c.act_format in ("fp8_static", "mxfp8") and tile_rows == 256
     ab = 1 if fp8_mma else eb                         # bytes per x / h element
-    if c.act_format == "mxfp8" and tile_rows < 128:   # codes + a scale byte per 32
+    if c.act_format == "mxfp8" and tile_rows != 128:
         ab = 1 + 1 / 32
     peak_mma = PEAK_FP8_TFLOPS if fp8_mma else PEAK_BF16_TFLOPS
+    mma_dtype = ("mxfp4_x_mxfp8" if c.act_format == "mxfp8" else "fp8_e4m3") if fp8_mma \
+        else c.dtype
     T, H, E, K, I, Is = c.T, c.H, c.E, c.K, c.I, c.I_shared
     R = T * K + (T if Is else 0)
     groups = U + (1 if Is else 0)
@@ -215,7 +219,7 @@ def main():
     else:
         path = "256x256-tile" if tile_rows == 256 else "128x128-tile"
         if fp8_mma:
-            path += " FP8 MFMA"
+            path += " FP4 x FP8 MFMA" if c.act_format == "mxfp8" else " FP8 MFMA"
         roof = {"kernel": f"gate_up ({path} grouped GEMM + SwiGLU)", "bound": "mfma",
                 "achieved": gu_flops / gu_s / 1e12, "peak": peak_mma, "unit": "TFLOP/s",
                 "per_unit": f"{4 * H * I} FLOP per routed row x {T * K} rows + "
@@ -252,7 +256,7 @@ def main():
         "metric": METRIC, "value": T / layer_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3" if fp8_mma else c.dtype,
+        "dtype": mma_dtype,
         "data": "synthetic (seeded, random-init weights of the layer's shapes)",
         "config": {"workload": c.name, "T": T, "H": H, "E": E, "K": K, "I": I, "I_shared": Is,
                    "route": "sigmoid+bias" if c.route_mode == 0 else "softmax",

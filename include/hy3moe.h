@@ -116,9 +116,9 @@ extern "C" {
  * group's h are quantised per block of 32 consecutive values of a row (along
  * H and I) by the OCP microscaling rule: E8M0 scale 2^(floor(log2 amax) - 8)
  * (floored at 2^-127), elements E4M3(v / scale), saturating, nearest even.
- * The weight-streaming path multiplies MXFP4 weights by the MXFP8 codes with
- * block-scaled FP4 x FP8 MFMAs; the tile paths multiply the same values in
- * bf16. */
+ * The weight-streaming and large-tile paths multiply MXFP4 weights by the
+ * MXFP8 codes with block-scaled FP4 x FP8 MFMAs; the tiled path multiplies
+ * the same values in bf16. */
 #define HY3MOE_AFMT_MXFP8      2
 
 /* Shape and mode of one layer call. */
@@ -210,11 +210,12 @@ typedef struct hy3moe_ws_layout {
   size_t xq;             /* act_format FP8_STATIC: quantised x [T][H], E4M3 bytes on
                             the large-tile path, else their bf16 values (0 = not
                             used); h then holds h quantised the same way.
-                            MXFP8: x as E4M3 bytes (weight-streaming path) or the
-                            bf16 values of the MXFP8 codes (tile paths)         */
+                            MXFP8: x as E4M3 bytes (weight-streaming and large-tile
+                            paths) or the bf16 values of the codes (tiled path) */
   size_t xs;             /* MXFP8: E8M0 scales of x [T][H/32] (0 = not used)   */
-  size_t hq;             /* MXFP8, weight-streaming path: E4M3 codes of h [R][I_max];
-                            the tile paths rewrite h in place with the bf16 values */
+  size_t hq;             /* MXFP8: E4M3 codes of h [R][I_max] (weight-streaming and
+                            large-tile paths; the tiled path rewrites h in place
+                            with the bf16 values)                              */
   size_t hs;             /* MXFP8: E8M0 scales of h [R][I_max/32]              */
 } hy3moe_ws_layout;
 

@@ -145,6 +145,20 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, float sc) {
 }
 #undef HY3_FP4_PAIR
 
+// One block-scaled 16x16x128 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): A = 32 FP4 E2M1 weights of the lane (16
+// bytes) with E8M0 scale sa, B = 32 FP8 E4M3 token values (two 16-byte
+// chunks) with E8M0 scale sb.
+__device__ __forceinline__ void mma_fp4_fp8(f32x4_t &acc, const uint4 &w, uint32_t sa,
+                                            const uint4 &x0, const uint4 &x1, uint32_t sb) {
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  const i32x8_t av = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+  const i32x8_t bv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  // formats: 4 = FP4 E2M1 (A), 0 = FP8 E4M3 (B); scale byte 0 of each operand
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 0, 0, (int)sa, 0,
+                                                         (int)sb);
+}
+
 // SiLU(g) * u in fp32: g / (1 + e^-g) * u, the quotient by the hardware
 // reciprocal (within an ulp; the result is rounded to bf16 or E4M3 after).
 __device__ __forceinline__ float swiglu(float g, float u) {

@@ -258,10 +258,13 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   const int path = path_of(cfg);
   const bool amx = cfg->act_format == HY3MOE_AFMT_MXFP8;
   const void *act = x;
-  if (amx) {   // codes and scales for the weight-streaming path, else bf16 values
+  // MXFP8: codes and scales for the block-scaled MFMAs of the weight-streaming
+  // and large-tile paths, the bf16 values for the tiled path
+  const bool amx_codes = amx && path != PATH_TILED;
+  if (amx) {
     rc = check_launch(launch_quant_mxfp8(x, (int64_t)T * H, ws + L.xq,
                                          reinterpret_cast<uint8_t *>(ws + L.xs),
-                                         path == PATH_SKINNY ? 0 : 1, s));
+                                         amx_codes ? 0 : 1, s));
     if (rc) return rc;
     act = ws + L.xq;
   }
@@ -307,7 +310,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.a8 = a8 ? 1 : 0;
   ea.xs = a8 ? w->x_scale : nullptr;
   ea.hs = a8 ? w->h_scale : nullptr;
-  ea.amx = amx && path == PATH_SKINNY ? 1 : 0;
+  ea.amx = amx_codes ? 1 : 0;
   ea.act_sc = amx ? reinterpret_cast<const uint8_t *>(ws + L.xs) : nullptr;
   ea.w_fp4 = fp4 ? 1 : 0;
   ea.mx0 = fp4 ? w->w_gate_mx : nullptr;
@@ -320,7 +323,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.act = ws + L.h; ea.w0 = w->w_down; ea.w1 = nullptr; ea.ws0 = w->ws_down; ea.ws1 = nullptr;
   if (amx) {   // h, dynamic MXFP8 per 32 along I: codes + scales, or bf16 values in place
     const int64_t nh = ((int64_t)T * K + (has_shared ? T : 0)) * Imax;
-    if (path == PATH_SKINNY) {
+    if (amx_codes) {
       rc = check_launch(launch_quant_mxfp8(ws + L.h, nh, ws + L.hq,
                                            reinterpret_cast<uint8_t *>(ws + L.hs), 0, s));
       ea.act = ws + L.hq;

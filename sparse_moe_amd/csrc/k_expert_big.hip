@@ -600,6 +600,221 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
 
 }
 
+// W4A8 tiles (MXFP4 weights x dynamic MXFP8 tokens): block-scaled FP4 x FP8
+// MFMAs, 128 K values per stage.  Per stage and buffer the LDS holds the
+// 256 weight rows as 64-byte code rows (4 chunks, unswizzled: a wavefront's
+// A reads -- chunk g of 16 consecutive rows -- cover 1 KB contiguously),
+// the 256 token rows as 128-byte code rows (swizzled as in the A8 tiles),
+// and one dword of scales per row (blocks 0..3 of the stage).  With the
+// measured layout of the instruction, lane (g, r) takes chunk g of its
+// weight row and chunks g and 4 + g of its token row, with scale byte g of
+// each row.  Each thread stages 2 weight chunks, 4 token chunks and one
+// scale dword per stage, refilled piece by piece as in the A8 tiles.
+constexpr int W4_WCH = 4;                 // 16-byte chunks per staged weight row
+constexpr int W4_TOK = BW * W4_WCH;       // token region (uint4 units)
+constexpr int W4_SC = W4_TOK + BTK * CH;  // scale region: 512 dwords (weights, then tokens)
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(512, 1) void expert_big_w4a8_kernel(ExpertArgs a, int n_col_tiles) {
+  __shared__ uint4 lds[2 * ROWS * CH];   // 2 x 64 KB: buffers of 50 KB, and the epilogue's staging
+  static_assert(W4_SC + (BW + BTK) / 4 <= ROWS * CH, "W4A8 stage buffer");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_tiles = a.tiles[2 * a.max_tiles];
+  const int per = ((n_tiles + BAND - 1) / BAND * (BAND * n_col_tiles) + 7) >> 3;
+  const int xcd = blockIdx.x & 7, nb = gridDim.x >> 3;
+  int r = blockIdx.x >> 3;
+  BigTile cur;
+  while (r < per && !big_tile_at<bf16_t, GATE_UP, true>(a, n_tiles, n_col_tiles, per, xcd, r, cur))
+    r += nb;
+  if (r >= per) return;
+
+  // ---- load descriptors of a tile (recomputed per tile) ----
+  const char *wb, *xb;
+  const uint8_t *sp;               // this thread's scale row (weight row or token row)
+  uint32_t woff[2], xoff[4];
+  auto tile_loads = [&](const BigTile &t, int tq) {
+    const bool shared = (t.g == a.E);
+    const int K = GATE_UP ? a.H : t.Ig;
+    const int lrow = tq >> 2;      // weight rows lrow and lrow + 128, chunk tq & 3
+    if (GATE_UP) {
+      const bool up = (lrow & 63) >= 32;   // the same for both rows; uniform per wavefront
+      wb = shared ? static_cast<const char *>(up ? a.ws1 : a.ws0)
+                  : static_cast<const char *>(up ? a.w1 : a.w0) + (size_t)t.g * a.I * (a.H / 2);
+    } else {
+      wb = shared ? static_cast<const char *>(a.ws0)
+                  : static_cast<const char *>(a.w0) + (size_t)t.g * a.H * (a.I / 2);
+    }
+    wb = wave_uniform(wb);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int row = lrow + 128 * p;
+      int wrow;
+      if (GATE_UP) {
+        wrow = t.col0 + (row >> 6) * 32 + (row & 31);
+        if (wrow >= t.Ig) wrow = t.col0;
+      } else {
+        wrow = (t.col0 + row < a.H) ? t.col0 + row : t.col0;
+      }
+      woff[p] = (uint32_t)wrow * (uint32_t)(K / 2) + (tq & 3) * 16;
+    }
+    const int lr = tq >> 3, lc = tq & 7;
+    xb = static_cast<const char *>(a.act) + (GATE_UP ? 0 : (size_t)t.row0 * a.ldh);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      int trow = t.row0 + p * 64 + lr;
+      if (trow >= t.grp_end) trow = t.row0;
+      xoff[p] = GATE_UP ? (uint32_t)a.sorted_token[trow] * (uint32_t)a.H + lc * 16
+                        : (uint32_t)(trow - t.row0) * (uint32_t)a.ldh + lc * 16;
+    }
+    // scale dword: threads 0..255 the weight row tq, threads 256..511 token row tq - 256
+    if (tq < 256) {
+      const int row = tq;
+      int wrow;
+      const uint8_t *sb;
+      if (GATE_UP) {
+        const bool up = (row & 63) >= 32;
+        sb = shared ? (up ? a.mxs1 : a.mxs0) : (up ? a.mx1 : a.mx0) + (size_t)t.g * a.I * (a.H / 32);
+        wrow = t.col0 + (row >> 6) * 32 + (row & 31);
+        if (wrow >= t.Ig) wrow = t.col0;
+      } else {
+        sb = shared ? a.mxs0 : a.mx0 + (size_t)t.g * a.H * (a.I / 32);
+        wrow = (t.col0 + row < a.H) ? t.col0 + row : t.col0;
+      }
+      sp = sb + (size_t)wrow * (K / 32);
+    } else {
+      int trow = t.row0 + (tq - 256);
+      if (trow >= t.grp_end) trow = t.row0;
+      sp = a.act_sc + (GATE_UP ? (size_t)a.sorted_token[trow] * (a.H / 32)
+                               : (size_t)trow * (a.ldh / 32));
+    }
+  };
+  tile_loads(cur, tid);
+
+  const int wr_ = wave >> 2, wt_ = wave & 3;
+  const int r16 = lane & 15, cg = lane >> 4;
+  const int rd_a = (wr_ * 128 + r16) * W4_WCH + cg;                // + 16 i * W4_WCH per fragment
+  const int rd_b = W4_TOK + (wt_ * 64 + r16) * CH;                 // token rows, as in the A8 tiles
+  const int sw0 = cg ^ (r16 & 7), sw1 = (4 + cg) ^ (r16 & 7);
+  const int rs_a = (W4_SC * 16) + (wr_ * 128 + r16) * 4 + cg;      // scale bytes (byte offsets)
+  const int rs_b = (W4_SC * 16) + (BW + wt_ * 64 + r16) * 4 + cg;
+  const int lr = tid >> 3, lc = tid & 7;
+  const int wl0 = (tid >> 2) * W4_WCH + (tid & 3);                 // weight chunk slots
+  const int wl1 = ((tid >> 2) + 128) * W4_WCH + (tid & 3);
+  const int xl = W4_TOK + lr * CH + (lc ^ (lr & 7));               // token chunk slot, + 64 CH per piece
+
+  uint4 st0, st1, st2, st3, st4, st5;
+  uint32_t st6;
+#define HY3_W4_LOADW(p, kst)                                                           \
+  { st##p = *reinterpret_cast<const uint4 *>(wb + ((uint32_t)(kst) * 64 + woff[(p) & 1])); }
+#define HY3_W4_LOADX(p, kst)                                                           \
+  { st##p = *reinterpret_cast<const uint4 *>(xb + ((uint32_t)(kst) * 128 + xoff[((p) - 2) & 3])); }
+#define HY3_W4_LOADS(kst) { st6 = *reinterpret_cast<const uint32_t *>(sp + (kst) * 4); }
+#define HY3_W4_STORE(p, buf)                                                           \
+  {                                                                                    \
+    uint4 *b_ = lds + (buf) * ROWS * CH;                                               \
+    if ((p) == 0) b_[wl0] = st0;                                                       \
+    else if ((p) == 1) b_[wl1] = st1;                                                  \
+    else if ((p) < 6) b_[xl + ((p) - 2) * 64 * CH] = HY3_W4_PIECE(p);                   \
+    else reinterpret_cast<uint32_t *>(b_ + W4_SC)[tid] = st6;                          \
+  }
+#define HY3_W4_PIECE(p) ((p) == 2 ? st2 : (p) == 3 ? st3 : (p) == 4 ? st4 : st5)
+#define HY3_W4_LOAD_ALL(kst)                                                           \
+  { HY3_W4_LOADW(0, kst) HY3_W4_LOADW(1, kst) HY3_W4_LOADX(2, kst) HY3_W4_LOADX(3, kst) \
+    HY3_W4_LOADX(4, kst) HY3_W4_LOADX(5, kst) HY3_W4_LOADS(kst) }
+#define HY3_W4_STORE_ALL(buf)                                                          \
+  { HY3_W4_STORE(0, buf) HY3_W4_STORE(1, buf) HY3_W4_STORE(2, buf) HY3_W4_STORE(3, buf) \
+    HY3_W4_STORE(4, buf) HY3_W4_STORE(5, buf) HY3_W4_STORE(6, buf) }
+// Group i: staging piece i (i < 7) of stage k + 1 to LDS and the same piece
+// of stage k + 2 into its registers, weight fragment i against the 4 token
+// fragments, then the next weight fragment and its scale.
+#define HY3_W4_GROUP(i, B)                                                             \
+  if ((i) == 0) { HY3_W4_STORE(0, (B) ^ 1) HY3_W4_LOADW(0, kn_) }                      \
+  else if ((i) == 1) { HY3_W4_STORE(1, (B) ^ 1) HY3_W4_LOADW(1, kn_) }                 \
+  else if ((i) == 2) { HY3_W4_STORE(2, (B) ^ 1) HY3_W4_LOADX(2, kn_) }                 \
+  else if ((i) == 3) { HY3_W4_STORE(3, (B) ^ 1) HY3_W4_LOADX(3, kn_) }                 \
+  else if ((i) == 4) { HY3_W4_STORE(4, (B) ^ 1) HY3_W4_LOADX(4, kn_) }                 \
+  else if ((i) == 5) { HY3_W4_STORE(5, (B) ^ 1) HY3_W4_LOADX(5, kn_) }                 \
+  else if ((i) == 6) { HY3_W4_STORE(6, (B) ^ 1) HY3_W4_LOADS(kn_) }                    \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j)                                        \
+      mma_fp4_fp8(acc[i][j], a_, sa_, b0_[j], b1_[j], sb_[j]);                          \
+  if ((i) < 7) {                                                                       \
+    a_ = base_[rd_a + ((i) + 1) * 16 * W4_WCH];                                        \
+    sa_ = sbase_[rs_a + ((i) + 1) * 16 * 4];                                           \
+  }
+#define HY3_W4_ITER(k, B)                                                              \
+  {                                                                                    \
+    const uint4 *base_ = lds + (B) * ROWS * CH;                                        \
+    const uint8_t *sbase_ = reinterpret_cast<const uint8_t *>(base_);                  \
+    const int kn_ = ((k) + 2 < cur.nk) ? (k) + 2 : 0;                                  \
+    uint4 b0_[4], b1_[4];                                                              \
+    uint32_t sb_[4];                                                                   \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                    \
+      b0_[j] = base_[rd_b + j * 16 * CH + sw0];                                        \
+      b1_[j] = base_[rd_b + j * 16 * CH + sw1];                                        \
+      sb_[j] = sbase_[rs_b + j * 16 * 4];                                              \
+    }                                                                                  \
+    uint4 a_ = base_[rd_a];                                                            \
+    uint32_t sa_ = sbase_[rs_a];                                                       \
+    HY3_W4_GROUP(0, B) HY3_W4_GROUP(1, B) HY3_W4_GROUP(2, B) HY3_W4_GROUP(3, B)         \
+    HY3_W4_GROUP(4, B) HY3_W4_GROUP(5, B) HY3_W4_GROUP(6, B) HY3_W4_GROUP(7, B)         \
+    __syncthreads();                                                                   \
+  }
+
+  HY3_W4_LOAD_ALL(0)
+  HY3_W4_STORE_ALL(0)
+  HY3_W4_LOAD_ALL((1 < cur.nk) ? 1 : 0)
+  __syncthreads();
+  f32x4_t acc[8][4];
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_sched_barrier(0);
+    const int nk = cur.nk;
+    int k = 0;
+    for (; k + 2 <= nk; k += 2) {
+      HY3_W4_ITER(k, 0);
+      HY3_W4_ITER(k + 1, 1);
+    }
+    if (k < nk) HY3_W4_ITER(k, 0);
+
+    BigTile nxt;
+    int rn = r + nb;
+    while (rn < per && !big_tile_at<bf16_t, GATE_UP, true>(a, n_tiles, n_col_tiles, per, xcd, rn, nxt))
+      rn += nb;
+    const bool has_next = rn < per;
+    if (has_next) {
+      int tid_n = tid;
+      asm volatile("" : "+v"(tid_n));
+      tile_loads(nxt, tid_n);
+      HY3_W4_LOAD_ALL(0)
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int tid_e = tid;
+    asm volatile("" : "+v"(tid_e));
+    big_epilogue<bf16_t, GATE_UP, WF_W4A8, false>(a, cur, acc, lds, tid_e);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!has_next) break;
+    __syncthreads();
+    HY3_W4_STORE_ALL(0)
+    HY3_W4_LOAD_ALL((1 < nxt.nk) ? 1 : 0)
+    __syncthreads();
+    cur = nxt;
+    r = rn;
+  }
+#undef HY3_W4_ITER
+#undef HY3_W4_GROUP
+#undef HY3_W4_STORE_ALL
+#undef HY3_W4_LOAD_ALL
+#undef HY3_W4_PIECE
+#undef HY3_W4_STORE
+#undef HY3_W4_LOADS
+#undef HY3_W4_LOADX
+#undef HY3_W4_LOADW
+}
+
 template <typename T, int WF, bool A8>
 hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   int nct;
@@ -622,10 +837,17 @@ hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   const long cap = n_cu >= 8 ? n_cu / 8 * 8 : 8;
   const long want = (logical + 7) / 8 * 8;
   const dim3 grid((unsigned)(want < cap ? want : cap));
-  if (gate_up)
-    hipLaunchKernelGGL((expert_big_kernel<T, true, WF, A8>), grid, dim3(512), 0, stream, a, nct);
-  else
-    hipLaunchKernelGGL((expert_big_kernel<T, false, WF, A8>), grid, dim3(512), 0, stream, a, nct);
+  if constexpr (WF == WF_W4A8) {
+    if (gate_up)
+      hipLaunchKernelGGL((expert_big_w4a8_kernel<true>), grid, dim3(512), 0, stream, a, nct);
+    else
+      hipLaunchKernelGGL((expert_big_w4a8_kernel<false>), grid, dim3(512), 0, stream, a, nct);
+  } else {
+    if (gate_up)
+      hipLaunchKernelGGL((expert_big_kernel<T, true, WF, A8>), grid, dim3(512), 0, stream, a, nct);
+    else
+      hipLaunchKernelGGL((expert_big_kernel<T, false, WF, A8>), grid, dim3(512), 0, stream, a, nct);
+  }
   return hipGetLastError();
 }
 
@@ -633,6 +855,7 @@ hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
 
 hipError_t launch_big_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream) {
   return dtype == DT_F32 ? launch_big_t<float, WF_DTYPE, false>(a, true, stream)
+         : a.amx         ? launch_big_t<bf16_t, WF_W4A8, false>(a, true, stream)
          : a.a8          ? launch_big_t<bf16_t, WF_FP8, true>(a, true, stream)
          : a.w_fp4       ? launch_big_t<bf16_t, WF_MXFP4, false>(a, true, stream)
          : a.w_fp8       ? launch_big_t<bf16_t, WF_FP8, false>(a, true, stream)
@@ -640,6 +863,7 @@ hipError_t launch_big_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream
 }
 hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream) {
   return dtype == DT_F32 ? launch_big_t<float, WF_DTYPE, false>(a, false, stream)
+         : a.amx         ? launch_big_t<bf16_t, WF_W4A8, false>(a, false, stream)
          : a.a8          ? launch_big_t<bf16_t, WF_FP8, true>(a, false, stream)
          : a.w_fp4       ? launch_big_t<bf16_t, WF_MXFP4, false>(a, false, stream)
          : a.w_fp8       ? launch_big_t<bf16_t, WF_FP8, false>(a, false, stream)

@@ -71,20 +71,6 @@ constexpr int token_chunks() {
   return WF == WF_MXFP4 ? 4 : ((WF == WF_FP8 || WF == WF_W4A8) ? 2 : 1);
 }
 
-// One block-scaled 16x16x128 MFMA: A = 32 FP4 E2M1 weights of the lane (16
-// bytes) with E8M0 scale sa, B = 32 FP8 E4M3 token values (two 16-byte
-// chunks) with E8M0 scale sb.
-__device__ __forceinline__ void mma_fp4_fp8(f32x4_t &acc, const uint4 &w, uint32_t sa,
-                                            const uint4 &x0, const uint4 &x1, uint32_t sb) {
-  typedef int i32x8_t __attribute__((ext_vector_type(8)));
-  const i32x8_t av = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-  const i32x8_t bv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-  // formats: 4 = FP4 E2M1 (A), 0 = FP8 E4M3 (B); scale byte 0 of each operand
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 0, 0, (int)sa, 0,
-                                                         (int)sb);
-}
-
 // Where a unit's operands are (per lane) and what its epilogue needs.
 template <int MT>
 struct UnitSrc {
