@@ -116,9 +116,11 @@ extern "C" {
  * group's h are quantised per block of 32 consecutive values of a row (along
  * H and I) by the OCP microscaling rule: E8M0 scale 2^(floor(log2 amax) - 8)
  * (floored at 2^-127), elements E4M3(v / scale), saturating, nearest even.
- * The weight-streaming and large-tile paths multiply MXFP4 weights by the
- * MXFP8 codes with block-scaled FP4 x FP8 MFMAs; the tiled path multiplies
- * the same values in bf16. */
+ * h is the SwiGLU output rounded to bf16, then quantised.  The
+ * weight-streaming and large-tile paths multiply MXFP4 weights by the MXFP8
+ * codes with block-scaled FP4 x FP8 MFMAs (the large-tile gate-up GEMM
+ * quantises h in its epilogue); the tiled path multiplies the same values
+ * in bf16. */
 #define HY3MOE_AFMT_MXFP8      2
 
 /* Shape and mode of one layer call. */
@@ -257,8 +259,9 @@ int hy3moe_forward(const hy3moe_config *cfg, const void *x, const hy3moe_weights
 
 /* Stages of hy3moe_forward, in launch order: router GEMM, score+select,
  * permutation (histogram, scan + tile list, scatter; with act_format
- * FP8_STATIC preceded by the quantisation of x), gate-up + SwiGLU, down,
- * combine. */
+ * FP8_STATIC or MXFP8 preceded by the quantisation of x), gate-up + SwiGLU,
+ * down (with MXFP8 off the large-tile path preceded by the quantisation of
+ * h), combine. */
 #define HY3MOE_N_STAGES 6
 
 /* hy3moe_forward that also records HY3MOE_N_STAGES + 1 caller-created HIP

@@ -123,6 +123,26 @@ __device__ __forceinline__ uint32_t quant_e4m3x4_rcp(float a, float b, float c, 
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
+// Dynamic MXFP8 (OCP microscaling conversion) of a block of 32 consecutive
+// values held by four adjacent lanes, 8 each: the lanes exchange their
+// maxima, the block's shared exponent is floor(log2 amax) - 8 (8: E4M3's
+// largest exponent), floored at -127, i.e. the E8M0 code max(exponent field
+// - 8, 0); each value is multiplied by 2^-exponent (exact) and rounded to
+// E4M3 (saturating, nearest even).  Returns the lane's 8 codes and sets
+// `code` to the block's E8M0 code.  Every lane of the wavefront must call it.
+__device__ __forceinline__ uint2 mxfp8_quant8(const float (&v)[8], uint32_t &code) {
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  const uint32_t ef = (__float_as_uint(m) >> 23) & 0xFFu;
+  code = ef > 8u ? ef - 8u : 0u;
+  const float inv = __uint_as_float((254u - code) << 23);   // 2^-(code - 127)
+  return make_uint2(quant_e4m3x4_rcp(v[0], v[1], v[2], v[3], inv),
+                    quant_e4m3x4_rcp(v[4], v[5], v[6], v[7], inv));
+}
+
 // Four codes -> their values as 4 bf16 (exact): the bf16 form in which the
 // bf16-MFMA paths carry quantised activations.
 __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {

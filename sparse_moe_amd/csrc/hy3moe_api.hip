@@ -301,7 +301,10 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.E = E; ea.H = H; ea.I = cfg->I; ea.I_shared = cfg->I_shared; ea.ldh = Imax;
   ea.max_tiles = L.max_tiles;
   ea.act = act; ea.w0 = w->w_gate; ea.w1 = w->w_up; ea.ws0 = w->ws_gate; ea.ws1 = w->ws_up;
-  ea.out = ws + L.h;
+  // W4A8 on the large-tile path: the gate-up epilogue quantises h itself
+  const bool h_codes_fused = amx_codes && path == PATH_BIG;
+  ea.out = h_codes_fused ? ws + L.hq : ws + L.h;
+  ea.out_sc = h_codes_fused ? reinterpret_cast<uint8_t *>(ws + L.hs) : nullptr;
   ea.w_fp8 = fp8 ? 1 : 0;
   ea.sc0 = fp8 ? w->w_gate_scale : nullptr;
   ea.sc1 = fp8 ? w->w_up_scale : nullptr;
@@ -321,9 +324,13 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   if (rc) return rc;
   mark();
   ea.act = ws + L.h; ea.w0 = w->w_down; ea.w1 = nullptr; ea.ws0 = w->ws_down; ea.ws1 = nullptr;
+  ea.out_sc = nullptr;
   if (amx) {   // h, dynamic MXFP8 per 32 along I: codes + scales, or bf16 values in place
     const int64_t nh = ((int64_t)T * K + (has_shared ? T : 0)) * Imax;
-    if (amx_codes) {
+    if (h_codes_fused) {
+      ea.act = ws + L.hq;
+      ea.act_sc = reinterpret_cast<const uint8_t *>(ws + L.hs);
+    } else if (amx_codes) {
       rc = check_launch(launch_quant_mxfp8(ws + L.h, nh, ws + L.hq,
                                            reinterpret_cast<uint8_t *>(ws + L.hs), 0, s));
       ea.act = ws + L.hq;

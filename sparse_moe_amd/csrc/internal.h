@@ -85,12 +85,15 @@ struct ExpertArgs {
   // mxs0/mxs1 (shared, [rows][K/32]) one E8M0 scale per 32 weights of a row.
   int w_fp4;
   const uint8_t *mx0, *mx1, *mxs0, *mxs1;
-  // Dynamic MXFP8 token rows (amx = 1, weight-streaming path): act holds
-  // E4M3 codes (rows of H or ldh bytes) and act_sc their E8M0 scales (rows
-  // of H / 32 or ldh / 32 bytes).  The tile paths read the exact bf16 values
-  // instead (amx = 0 there).
+  // Dynamic MXFP8 token rows (amx = 1, weight-streaming and large-tile
+  // paths): act holds E4M3 codes (rows of H or ldh bytes) and act_sc their
+  // E8M0 scales (rows of H / 32 or ldh / 32 bytes).  The tiled path reads the
+  // exact bf16 values instead (amx = 0 there).  out_sc: when set, the
+  // large-tile gate-up GEMM quantises h itself and writes codes to out and
+  // their scales there (rows of ldh / 32 bytes).
   int amx;
   const uint8_t *act_sc;
+  uint8_t *out_sc;
   // Static FP8 activations (a8 = 1, with w_fp8): act holds E4M3 codes on the
   // large-tile path and their exact bf16 values on the other two; *xs is the
   // scale of x and hs[g] that of group g's h (hs[E]: shared).  The gate-up

@@ -284,6 +284,37 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
     __syncthreads();
     const int width = GATE_UP ? t.Ig : a.H;           // output columns of this matrix
     const size_t ldo = GATE_UP ? (size_t)a.ldh : (size_t)a.H;
+    if constexpr (WF == WF_W4A8 && GATE_UP) {
+      // W4A8: the staged bf16 h quantised to MXFP8 per 32 columns.  A row's
+      // 16 chunks go to 16 consecutive threads, so the 4 chunks of a block
+      // are in 4 adjacent lanes; out receives the codes (rows of ldh bytes)
+      // and out_sc the block scales.
+      uint8_t *hq = static_cast<uint8_t *>(a.out);
+#pragma unroll
+      for (int m = 0; m < 256 * OC / 512; ++m) {
+        const int q = tid + 512 * m;
+        const int r = q / OC, ch = q % OC;
+        const int c = t.col0 + ch * 8;
+        const uint4 u = lds[r * OC + (ch ^ (r & 7))];
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[2 * k] = __uint_as_float(w4[k] << 16);
+          v[2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+        }
+        uint32_t code;
+        const uint2 cq = mxfp8_quant8(v, code);   // all lanes: it exchanges maxima
+        if (t.row0 + r < t.grp_end && c < width) {
+          uint2 *dst = reinterpret_cast<uint2 *>(hq + (size_t)(t.row0 + r) * ldo + c);
+          __builtin_nontemporal_store(cq.x, &dst->x);
+          __builtin_nontemporal_store(cq.y, &dst->y);
+          if ((tid & 3) == 0)
+            a.out_sc[(size_t)(t.row0 + r) * (ldo / 32) + (c >> 5)] = (uint8_t)code;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int m = 0; m < 256 * OC / 512; ++m) {
       const int q = tid + 512 * m;

@@ -74,40 +74,31 @@ __global__ __launch_bounds__(64) void quant_tail_kernel(const T *x, int64_t begi
 
 // Dynamic MXFP8 quantisation (OCP microscaling conversion, blocks of 32
 // consecutive values along a row): four threads hold a block's 32 values
-// (8 each, 16 bytes of bf16), exchange their maxima, and take the shared
-// exponent floor(log2 amax) - 8 from the float's exponent field (floored at
-// -127: E8M0 code max(exp_field - 8, 0)); each value is then multiplied by
-// 2^-exponent (exact) and rounded to E4M3 (saturating, nearest even).
+// (8 each, 16 bytes of bf16) and quantise them together (mxfp8_quant8).
 // CARRIER: write the exact bf16 values (code value x 2^exponent) in place of
 // codes and scales.  Rows [n_rows, K], K % 32 == 0; in may alias q when
 // CARRIER (each thread rewrites only the 16 bytes it read).
 template <bool CARRIER>
 __global__ __launch_bounds__(256) void mxq_kernel(const bf16_t *in, int64_t n8, void *q,
                                                   uint8_t *scales) {
-  const int64_t stride = (int64_t)gridDim.x * 256;   // a multiple of 4: blocks stay together
+  // stride and n8 are multiples of 4, so the four lanes of a block (which
+  // exchange maxima) stay in or leave the loop together
+  const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
     float v[8];
     load8(in + 8 * i, v);
-    float m = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    const int ef = (int)((__float_as_uint(m) >> 23) & 0xFF);
-    const int code = ef > 8 ? ef - 8 : 0;              // E8M0: shared exponent + 127
-    const float inv = __uint_as_float((uint32_t)(254 - code) << 23);   // 2^-(code - 127)
-    const uint32_t c0 = quant_e4m3x4_rcp(v[0], v[1], v[2], v[3], inv);
-    const uint32_t c1 = quant_e4m3x4_rcp(v[4], v[5], v[6], v[7], inv);
+    uint32_t code;
+    const uint2 c = mxfp8_quant8(v, code);
     if (CARRIER) {
-      const float sc = e8m0_to_f32((uint32_t)code);
+      const float sc = e8m0_to_f32(code);
       const uint32_t w[4] = {
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, sc, false)),
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, sc, true)),
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, sc, false)),
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, sc, true))};
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true))};
       reinterpret_cast<uint4 *>(q)[i] = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
-      reinterpret_cast<uint2 *>(q)[i] = make_uint2(c0, c1);
+      reinterpret_cast<uint2 *>(q)[i] = c;
       if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)code;
     }
   }
