@@ -262,3 +262,79 @@ def test_w4a8_codes_in_the_workspace(dev, T, E):
     log(f"  T={T}: x codes exact; h values {n_all}, {n_diff} differ from the oracle's, "
         f"{n_scale} block scales one apart")
     assert n_diff < 0.01 * n_all
+
+
+def crafted_mx_rows(rng, H: int) -> np.ndarray:
+    """Rows of bf16-exact float32 values whose 32-value blocks hit every
+    decision of the MXFP8 quantiser: all-zero and negative-zero blocks;
+    blocks whose amax scales to exactly 448 with the other values on E4M3
+    codes or on the midpoints between neighbouring codes (ties to even);
+    amax mantissas up to 1 + 127/128 (scaled values in (448, 512)
+    saturate); block exponents from -100 to 100; bf16 subnormal blocks (E8M0
+    code 0); and random signed blocks spanning 2^20 in magnitude."""
+    vals = oracle.fp8_e4m3_value(np.arange(0x7F, dtype=np.uint8))   # 0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2
+    blocks = [np.zeros(32), -np.zeros(32)]
+    for m in (-100, -3, 0, 5, 100):
+        sc = 2.0 ** (m - 8)
+        for pool in (vals, mids):
+            for b0 in range(0, len(pool), 31):
+                part = pool[b0:b0 + 31]
+                blk = np.concatenate([[1.75 * 2.0 ** m], part * sc,
+                                      np.zeros(31 - len(part))])
+                sign = np.where(rng.random(32) < 0.5, -1.0, 1.0)
+                blocks.append(blk * sign)
+        for mant in (1.0, 1.5, 1.75, 1.78125, 1.8125, 1.875, 1.9921875):
+            blk = np.concatenate([[mant * 2.0 ** m], rng.choice(vals, 31) * sc])
+            blocks.append(blk)
+    for k in range(4):   # bf16 subnormals: multiples of 2^-133 below 2^-126
+        blocks.append(rng.integers(0, 128, 32) * 2.0 ** -133 * (-1) ** k)
+    for _ in range(16):   # rounded to bf16 below
+        mag = np.exp2(rng.uniform(-20, 0, 32) + rng.integers(-60, 60))
+        blocks.append(mag * np.where(rng.random(32) < 0.5, -1.0, 1.0))
+    flat = np.concatenate(blocks)
+    per_row = H // 32
+    n_rows = -(-len(blocks) // per_row)
+    flat = np.concatenate([flat, np.zeros(n_rows * H - flat.size)])
+    x = flat.reshape(n_rows, H).astype(np.float32)
+    # to bf16, nearest even (exact for all but the random blocks)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def test_mxfp8_quantiser_crafted_blocks(dev):
+    """The W4A8 forward's x quantisation on crafted blocks: codes and E8M0
+    scales bit-exact against the oracle's MXFP8 quantiser, in the layout the
+    weight-streaming kernels read, and the same from the large-tile path."""
+    from gpu_util import config_of, to_torch, upload_weights
+    from synth import random_small
+    rng = np.random.default_rng(7)
+    H = 256
+    x32 = crafted_mx_rows(rng, H)
+    qx, sx = oracle.quant_mxfp8(x32.astype(np.float64))
+    for T in (x32.shape[0], 400):
+        xx = np.resize(x32, (T, H))   # the large-tile case repeats the rows
+        inp = random_small(7, T=T, H=H, E=8, K=4, I=128, I_shared=128, dtype="bf16",
+                           w_format="mxfp4", act_format="mxfp8")
+        cfg = config_of(inp)
+        L = sm.hy3moe_workspace_layout(cfg)
+        assert L.tile_rows != 128
+        ws = sm.alloc_workspace(cfg, True, dev)
+        xb = (xx.view(np.uint32) >> 16).astype(np.uint16)   # bf16 bits
+        sm.forward(cfg, to_torch(xb, "bf16", dev), upload_weights(inp, dev), workspace=ws)
+        torch.cuda.synchronize()
+        wsh = ws.cpu().numpy()
+        got_s = wsh[L.xs:L.xs + T * H // 32].reshape(T, -1)
+        got_q = wsh[L.xq:L.xq + T * H].reshape(T, H)
+        ref_q, ref_s = np.resize(qx, (T, H)), np.resize(sx, (T, H // 32))
+        bad = np.argwhere(got_s != ref_s)
+        for i, b in bad[:4]:
+            log(f"  row {i} block {b}: scale got {got_s[i, b]} ref {ref_s[i, b]}")
+        np.testing.assert_array_equal(got_s, ref_s)
+        bad = np.argwhere(got_q != ref_q)
+        for i, j in bad[:4]:
+            log(f"  row {i} col {j}: x={xx[i, j]!r} code got {got_q[i, j]:#04x} "
+                f"ref {ref_q[i, j]:#04x} (scale code {ref_s[i, j // 32]})")
+        np.testing.assert_array_equal(got_q, ref_q)
+        log(f"  T={T}: {T * H // 32} blocks bit-exact (path rows {L.tile_rows})")
