@@ -32,10 +32,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-WORKLOADS = {"decode": 1, "prefill": 2, "softmax": 4, "decode_fp8": 5, "prefill_fp8": 6,
-             "decode_w8a8": 7, "prefill_w8a8": 8, "decode_mxfp4": 9, "prefill_mxfp4": 10,
-             "decode_w4a8": 11, "prefill_w4a8": 12}
-ROUTER_WORKLOAD = 3            # the router-only configuration (gate alone, M tokens)
+WORKLOADS = {"decode": "hy3_decode_T16", "prefill": "hy3_prefill_T8192_skew", "softmax": "hunyuanimage_softmax_T32768", "decode_fp8": "hy3_decode_T16_fp8", "prefill_fp8": "hy3_prefill_T8192_skew_fp8",
+             "decode_w8a8": "hy3_decode_T16_w8a8", "prefill_w8a8": "hy3_prefill_T8192_skew_w8a8", "decode_mxfp4": "hy3_decode_T16_mxfp4", "prefill_mxfp4": "hy3_prefill_T8192_skew_mxfp4",
+             "decode_w4a8": "hy3_decode_T16_w4a8", "prefill_w4a8": "hy3_prefill_T8192_skew_w4a8"}
+ROUTER_WORKLOAD = "hy3_router_only"            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published
@@ -92,7 +92,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
-              "(sharding is described in DESIGN.md).  Run with --gpus 1.", flush=True)
+              "(how the path would shard is described with the design).  Run with --gpus 1.", flush=True)
         sys.exit(2)
 
     import numpy as np

@@ -19,7 +19,7 @@ tensor (and any single expert of a stacked weight) can be regenerated on its
 own, in any order, on any number of threads.
 
 * ``key`` is a *model key* for weights (so that the decode and the prefill
-  workloads of the same model share one set of weights) and ``1000 + cfg_id``
+  workloads of the same model share one set of weights) and ``1000 + data_id``
   for per-workload data (activations and the expert bias).
 * tensor ids: 0 x, 1 router weight, 2 expert bias, 3 gate, 4 up, 5 down,
   6/7/8 shared gate/up/down.
@@ -107,7 +107,7 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
 @dataclasses.dataclass(frozen=True)
 class MoEConfig:
     name: str
-    cfg_id: int
+    data_id: int               # seed id of the workload's activations and expert bias
     model_key: int
     T: int
     H: int
@@ -135,58 +135,58 @@ class MoEConfig:
 # CANN deployment article section 一 lists router_scaling_factor=2.826).
 HY3_SCALE = 2.826
 
-CONFIGS: Dict[int, MoEConfig] = {
-    0: MoEConfig("tiny_fp32", 0, 0, T=8, H=256, E=16, K=4, I=128, I_shared=128,
+CONFIGS: Dict[str, MoEConfig] = {
+    "tiny_fp32": MoEConfig("tiny_fp32", 0, 0, T=8, H=256, E=16, K=4, I=128, I_shared=128,
                  dtype="f32", route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE,
                  renorm_eps=0.0, bias_kind="uniform"),
-    1: MoEConfig("hy3_decode_T16", 1, 1, T=16, H=4096, E=192, K=8, I=1536,
+    "hy3_decode_T16": MoEConfig("hy3_decode_T16", 1, 1, T=16, H=4096, E=192, K=8, I=1536,
                  I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform"),
-    2: MoEConfig("hy3_prefill_T8192_skew", 2, 1, T=8192, H=4096, E=192, K=8,
+    "hy3_prefill_T8192_skew": MoEConfig("hy3_prefill_T8192_skew", 2, 1, T=8192, H=4096, E=192, K=8,
                  I=1536, I_shared=1536, dtype="bf16",
                  route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                  bias_kind="skew"),
     # Router-only sweep: M in {2, 64, 512, 4096}; the expert weights are not used.
-    3: MoEConfig("hy3_router_only", 3, 1, T=4096, H=4096, E=192, K=8, I=1536,
+    "hy3_router_only": MoEConfig("hy3_router_only", 3, 1, T=4096, H=4096, E=192, K=8, I=1536,
                  I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform"),
-    4: MoEConfig("hunyuanimage_softmax_T32768", 4, 4, T=32768, H=4096, E=64,
+    "hunyuanimage_softmax_T32768": MoEConfig("hunyuanimage_softmax_T32768", 4, 4, T=32768, H=4096, E=64,
                  K=8, I=1536, I_shared=1536, dtype="bf16",
                  route_mode=ROUTE_SOFTMAX, scale=1.0, renorm_eps=1e-8,
                  bias_kind="none"),
     # Hy3 decode with FP8 E4M3 expert weights (one scale per matrix).
-    5: MoEConfig("hy3_decode_T16_fp8", 5, 5, T=16, H=4096, E=192, K=8, I=1536,
+    "hy3_decode_T16_fp8": MoEConfig("hy3_decode_T16_fp8", 5, 5, T=16, H=4096, E=192, K=8, I=1536,
                  I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform",
                  w_format="fp8_e4m3"),
     # Hy3 prefill chunk with the same FP8 experts and a skewed bias.
-    6: MoEConfig("hy3_prefill_T8192_skew_fp8", 6, 5, T=8192, H=4096, E=192, K=8,
+    "hy3_prefill_T8192_skew_fp8": MoEConfig("hy3_prefill_T8192_skew_fp8", 6, 5, T=8192, H=4096, E=192, K=8,
                  I=1536, I_shared=1536, dtype="bf16",
                  route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                  bias_kind="skew", w_format="fp8_e4m3"),
     # The same two shapes and FP8 experts with static FP8 activations (W8A8).
-    7: MoEConfig("hy3_decode_T16_w8a8", 7, 5, T=16, H=4096, E=192, K=8, I=1536,
+    "hy3_decode_T16_w8a8": MoEConfig("hy3_decode_T16_w8a8", 7, 5, T=16, H=4096, E=192, K=8, I=1536,
                  I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform",
                  w_format="fp8_e4m3", act_format="fp8_static"),
-    8: MoEConfig("hy3_prefill_T8192_skew_w8a8", 8, 5, T=8192, H=4096, E=192, K=8,
+    "hy3_prefill_T8192_skew_w8a8": MoEConfig("hy3_prefill_T8192_skew_w8a8", 8, 5, T=8192, H=4096, E=192, K=8,
                  I=1536, I_shared=1536, dtype="bf16",
                  route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                  bias_kind="skew", w_format="fp8_e4m3", act_format="fp8_static"),
     # Hy3 decode and prefill with MXFP4 experts (bf16 activations).
-    9: MoEConfig("hy3_decode_T16_mxfp4", 9, 9, T=16, H=4096, E=192, K=8, I=1536,
+    "hy3_decode_T16_mxfp4": MoEConfig("hy3_decode_T16_mxfp4", 9, 9, T=16, H=4096, E=192, K=8, I=1536,
                  I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform", w_format="mxfp4"),
-    10: MoEConfig("hy3_prefill_T8192_skew_mxfp4", 10, 9, T=8192, H=4096, E=192, K=8,
+    "hy3_prefill_T8192_skew_mxfp4": MoEConfig("hy3_prefill_T8192_skew_mxfp4", 10, 9, T=8192, H=4096, E=192, K=8,
                   I=1536, I_shared=1536, dtype="bf16",
                   route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                   bias_kind="skew", w_format="mxfp4"),
     # The same MXFP4 experts with dynamic MXFP8 activations (W4A8).
-    11: MoEConfig("hy3_decode_T16_w4a8", 11, 9, T=16, H=4096, E=192, K=8, I=1536,
+    "hy3_decode_T16_w4a8": MoEConfig("hy3_decode_T16_w4a8", 11, 9, T=16, H=4096, E=192, K=8, I=1536,
                   I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                   scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform", w_format="mxfp4",
                   act_format="mxfp8"),
-    12: MoEConfig("hy3_prefill_T8192_skew_w4a8", 12, 9, T=8192, H=4096, E=192, K=8,
+    "hy3_prefill_T8192_skew_w4a8": MoEConfig("hy3_prefill_T8192_skew_w4a8", 12, 9, T=8192, H=4096, E=192, K=8,
                   I=1536, I_shared=1536, dtype="bf16",
                   route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                   bias_kind="skew", w_format="mxfp4", act_format="mxfp8"),
@@ -271,7 +271,7 @@ class MoEInputs:
 
     # ---- data streams (per workload) ----
     def _data_key(self) -> int:
-        return 1000 + self.cfg.cfg_id
+        return 1000 + self.cfg.data_id
 
     def x(self) -> np.ndarray:
         k = ("x",)
@@ -458,8 +458,8 @@ class MoEInputs:
         return None if s is None else tuple(to_f64(a, self.cfg.dtype) for a in s)
 
 
-def make_inputs(cfg_id: int, seed: int = 0, T: Optional[int] = None) -> MoEInputs:
-    cfg = CONFIGS[cfg_id]
+def make_inputs(name: str, seed: int = 0, T: Optional[int] = None) -> MoEInputs:
+    cfg = CONFIGS[name]
     if T is not None:
         cfg = cfg.with_T(T)
     return MoEInputs(cfg, seed)

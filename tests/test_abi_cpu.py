@@ -61,15 +61,15 @@ def R_of(c):
     return c.T * c.K + (c.T if c.I_shared else 0)
 
 
-@pytest.mark.parametrize("cfg_id", sorted(CONFIGS))
-def test_workspace_layout_is_consistent(lib, cfg_id):
-    cfg = cfg_of(CONFIGS[cfg_id])
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_workspace_layout_is_consistent(lib, name):
+    cfg = cfg_of(CONFIGS[name])
     L = sm.hy3moe_workspace_layout(cfg)
     assert L.total == sm.hy3moe_workspace_bytes(cfg, True) > 0
     assert 0 < sm.hy3moe_workspace_bytes(cfg, False) <= L.total
     names = ["logits_part", "idx", "weight", "hist", "counts", "offsets", "sorted_token",
              "pos_of", "tiles", "h", "y"]
-    c = CONFIGS[cfg_id]
+    c = CONFIGS[name]
     planes = c.dtype == "bf16" and c.T >= 1024
     assert (L.w_planes > 0) == planes
     if planes:
@@ -112,7 +112,7 @@ def test_workspace_layout_is_consistent(lib, cfg_id):
     (dict(act_format="mxfp8"), -2), (dict(w_format="fp8_e4m3", act_format="mxfp8"), -2),
 ])
 def test_invalid_configs_rejected(lib, bad, code):
-    c = CONFIGS[1]
+    c = CONFIGS["hy3_decode_T16"]
     kw = dict(T=16, H=c.H, E=c.E, K=c.K, I=c.I, I_shared=c.I_shared, dtype="bf16",
               route_mode=0, scale=2.826)
     kw.update(bad)
@@ -127,7 +127,7 @@ def test_invalid_configs_rejected(lib, bad, code):
 
 
 def test_argument_errors_before_launch(lib):
-    cfg = cfg_of(CONFIGS[1])
+    cfg = cfg_of(CONFIGS["hy3_decode_T16"])
     need = sm.hy3moe_workspace_bytes(cfg, True)
     good = b.hy3moe_weights(*([4096] * 8))
     fw = lib.hy3moe_forward
@@ -154,7 +154,7 @@ def test_argument_errors_before_launch(lib):
 
 
 def test_zero_tokens_is_a_no_op(lib):
-    cfg = cfg_of(CONFIGS[1], T=0)
+    cfg = cfg_of(CONFIGS["hy3_decode_T16"], T=0)
     w = b.hy3moe_weights(*([4096] * 8))
     assert lib.hy3moe_forward(ctypes.byref(cfg), 4096, ctypes.byref(w), 8192, None, None,
                               4096, 0, None) == 0
@@ -169,7 +169,7 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
 
 
 def test_weight_format_enum_is_checked(lib):
-    cfg = cfg_of(CONFIGS[5])
+    cfg = cfg_of(CONFIGS["hy3_decode_T16_fp8"])
     assert sm.hy3moe_workspace_bytes(cfg, True) > 0
     cfg.w_format = 3
     assert sm.hy3moe_workspace_bytes(cfg, True) == 0
@@ -178,7 +178,7 @@ def test_weight_format_enum_is_checked(lib):
 
 
 def test_activation_format_enum_is_checked(lib):
-    cfg = cfg_of(CONFIGS[7])
+    cfg = cfg_of(CONFIGS["hy3_decode_T16_w8a8"])
     assert sm.hy3moe_workspace_bytes(cfg, True) > 0
     cfg.act_format = 3
     assert sm.hy3moe_workspace_bytes(cfg, True) == 0
@@ -189,18 +189,18 @@ def test_activation_format_enum_is_checked(lib):
 def test_w8a8_path_choice(lib):
     """W8A8 batches take the large-tile FP8-MFMA path only when H, I and
     I_shared are multiples of 128 (its K stages hold 128 values)."""
-    big = sm.hy3moe_workspace_layout(cfg_of(CONFIGS[8]))
+    big = sm.hy3moe_workspace_layout(cfg_of(CONFIGS["hy3_prefill_T8192_skew_w8a8"]))
     assert big.tile_rows == 256
     for kw in (dict(H=4096 + 64), dict(I=1536 + 64), dict(I_shared=64)):
-        L = sm.hy3moe_workspace_layout(cfg_of(CONFIGS[8], **kw))
+        L = sm.hy3moe_workspace_layout(cfg_of(CONFIGS["hy3_prefill_T8192_skew_w8a8"], **kw))
         assert L.tile_rows == 128, kw
         # ... while the same shapes with W8A16 stay on the large-tile path
-        L16 = sm.hy3moe_workspace_layout(cfg_of(CONFIGS[8], act_format="dtype", **kw))
+        L16 = sm.hy3moe_workspace_layout(cfg_of(CONFIGS["hy3_prefill_T8192_skew_w8a8"], act_format="dtype", **kw))
         assert L16.tile_rows == 256, kw
 
 
 def test_mxfp4_weights_need_their_block_scales(lib):
-    cfg = cfg_of(CONFIGS[9])
+    cfg = cfg_of(CONFIGS["hy3_decode_T16_mxfp4"])
     need = sm.hy3moe_workspace_bytes(cfg, True)
     assert need > 0
     fw = lib.hy3moe_forward
@@ -216,7 +216,7 @@ def test_mxfp4_weights_need_their_block_scales(lib):
         assert fw(ctypes.byref(cfg), 4096, ctypes.byref(b.hy3moe_weights(*w)), 8192, None,
                   None, 4096, need, None) == -4
     # without a shared expert its scale arrays may be NULL
-    cfg_ns = cfg_of(CONFIGS[9], I_shared=0)
+    cfg_ns = cfg_of(CONFIGS["hy3_decode_T16_mxfp4"], I_shared=0)
     w = full[:17] + [None, None, None]
     rc = fw(ctypes.byref(cfg_ns), 4096, ctypes.byref(b.hy3moe_weights(*w)), 8192, None, None,
             4096, sm.hy3moe_workspace_bytes(cfg_ns, True), None)
@@ -224,7 +224,7 @@ def test_mxfp4_weights_need_their_block_scales(lib):
 
 
 def test_w8a8_needs_its_activation_scales(lib):
-    cfg = cfg_of(CONFIGS[7])
+    cfg = cfg_of(CONFIGS["hy3_decode_T16_w8a8"])
     need = sm.hy3moe_workspace_bytes(cfg, True)
     fw = lib.hy3moe_forward
     no_h = b.hy3moe_weights(*([4096] * 13 + [None]))
@@ -246,7 +246,7 @@ def test_quantize_entry_validation(lib):
 
 
 def test_fp8_weights_need_their_scales(lib):
-    cfg = cfg_of(CONFIGS[5])
+    cfg = cfg_of(CONFIGS["hy3_decode_T16_fp8"])
     need = sm.hy3moe_workspace_bytes(cfg, True)
     fw = lib.hy3moe_forward
     ok = b.hy3moe_weights(*([4096] * 12))
@@ -260,7 +260,7 @@ def test_fp8_weights_need_their_scales(lib):
     assert fw(ctypes.byref(cfg), 4096, ctypes.byref(mis), 8192, None, None, 4096, need,
               None) == -4
     # the same weights without shared expert do not need the shared scales
-    cfg_ns = cfg_of(CONFIGS[5], I_shared=0)
+    cfg_ns = cfg_of(CONFIGS["hy3_decode_T16_fp8"], I_shared=0)
     need_ns = sm.hy3moe_workspace_bytes(cfg_ns, True)
     assert fw(ctypes.byref(cfg_ns), 4096, ctypes.byref(missing), 8192, None, None, 4096,
               need_ns - 1, None) == -3

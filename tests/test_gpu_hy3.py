@@ -32,7 +32,7 @@ def dev():
 
 @pytest.fixture(scope="module")
 def hy3_weights(dev):
-    inp = MoEInputs(CONFIGS[1])
+    inp = MoEInputs(CONFIGS["hy3_decode_T16"])
     log("generating and uploading Hy3 expert weights (192 x 37.7 MB)")
     w = upload_weights(inp, dev)
     torch.cuda.synchronize()
@@ -93,11 +93,11 @@ def decode_full_check(inp, dev, weights, workload_shape=True):
 
 
 def test_hy3_decode_T16_full(dev, hy3_weights):
-    decode_full_check(MoEInputs(CONFIGS[1]), dev, hy3_weights)
+    decode_full_check(MoEInputs(CONFIGS["hy3_decode_T16"]), dev, hy3_weights)
 
 
 def test_hy3_prefill_T8192_skew_sampled(dev, hy3_weights):
-    inp = MoEInputs(CONFIGS[2])
+    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew"])
     log(f"case {inp.cfg.name}")
     sampled_check(inp, dev, hy3_weights)
 
@@ -107,7 +107,7 @@ def test_router_sweep(dev, hy3_weights, M):
     """Logits of both router arithmetics against the float64 oracle, per token row:
     max|dL| / max|L| and ||dL|| / ||L||.  fp32-accurate: <= 1e-5 and the route
     matches; two-term split: <= 1e-3 (the stated bound for the split)."""
-    inp = MoEInputs(CONFIGS[3].with_T(M))
+    inp = MoEInputs(CONFIGS["hy3_router_only"].with_T(M))
     c = inp.cfg
     x = to_torch(inp.x(), c.dtype, dev)
     L64 = oracle.router_logits(inp.x_f64(), inp.w_router().astype(np.float64))
@@ -132,7 +132,7 @@ def test_router_sweep(dev, hy3_weights, M):
 def test_softmax_long_prefill_T32768_sampled(dev):
     gc.collect()
     torch.cuda.empty_cache()
-    inp = MoEInputs(CONFIGS[4])
+    inp = MoEInputs(CONFIGS["hunyuanimage_softmax_T32768"])
     log(f"case {inp.cfg.name}: uploading 64 experts")
     w = upload_weights(inp, dev)
     try:
@@ -144,7 +144,7 @@ def test_softmax_long_prefill_T32768_sampled(dev):
 
 @pytest.fixture(scope="module")
 def hy3_fp8_weights(dev):
-    inp = MoEInputs(CONFIGS[5])
+    inp = MoEInputs(CONFIGS["hy3_decode_T16_fp8"])
     log("generating and uploading FP8 Hy3 expert weights (192 x 18.9 MB)")
     w = upload_weights(inp, dev)
     torch.cuda.synchronize()
@@ -160,12 +160,12 @@ def test_hy3_decode_T16_fp8_full(dev, hy3_fp8_weights):
     Not one of the bf16 workloads the 2e-2 bound is stated for: the output
     bound is the derived one (max(2e-2, 2^-6 max|ref|), a bf16 ulp or two at
     the largest output); rel-L2 stays 5e-3."""
-    decode_full_check(MoEInputs(CONFIGS[5]), dev, hy3_fp8_weights, workload_shape=False)
+    decode_full_check(MoEInputs(CONFIGS["hy3_decode_T16_fp8"]), dev, hy3_fp8_weights, workload_shape=False)
 
 
 def test_hy3_prefill_T8192_skew_fp8_sampled(dev, hy3_fp8_weights):
     """The prefill chunk on the same FP8 experts (large-tile path)."""
-    inp = MoEInputs(CONFIGS[6])
+    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_fp8"])
     log(f"case {inp.cfg.name}")
     sampled_check(inp, dev, hy3_fp8_weights, workload_shape=False)
 
@@ -175,21 +175,21 @@ def test_hy3_decode_T16_w8a8_full(dev, hy3_fp8_weights):
     token.  h codes are decided from the GPU's float32 h, the oracle's from
     its float64 h rounded to float32: where the two straddle a rounding
     midpoint a code differs by one step, so the bound is the derived one."""
-    inp = MoEInputs(CONFIGS[7])
+    inp = MoEInputs(CONFIGS["hy3_decode_T16_w8a8"])
     decode_full_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev),
                       workload_shape=False)
 
 
 def test_hy3_prefill_T8192_skew_w8a8_sampled(dev, hy3_fp8_weights):
     """The W8A8 prefill chunk: FP8 MFMAs on the large-tile path."""
-    inp = MoEInputs(CONFIGS[8])
+    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_w8a8"])
     log(f"case {inp.cfg.name}")
     sampled_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev), workload_shape=False)
 
 
 @pytest.fixture(scope="module")
 def hy3_mxfp4_weights(dev):
-    inp = MoEInputs(CONFIGS[9])
+    inp = MoEInputs(CONFIGS["hy3_decode_T16_mxfp4"])
     log("generating and uploading MXFP4 Hy3 expert weights (192 x 10 MB)")
     w = upload_weights(inp, dev)
     torch.cuda.synchronize()
@@ -202,12 +202,12 @@ def hy3_mxfp4_weights(dev):
 def test_hy3_decode_T16_mxfp4_full(dev, hy3_mxfp4_weights):
     """Hy3 decode with MXFP4 experts (E2M1 codes, one E8M0 scale per 32
     weights), every token; derived output bound as for the FP8 weights."""
-    decode_full_check(MoEInputs(CONFIGS[9]), dev, hy3_mxfp4_weights, workload_shape=False)
+    decode_full_check(MoEInputs(CONFIGS["hy3_decode_T16_mxfp4"]), dev, hy3_mxfp4_weights, workload_shape=False)
 
 
 def test_hy3_prefill_T8192_skew_mxfp4_sampled(dev, hy3_mxfp4_weights):
     """The prefill chunk on the same MXFP4 experts (large-tile path)."""
-    inp = MoEInputs(CONFIGS[10])
+    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_mxfp4"])
     log(f"case {inp.cfg.name}")
     sampled_check(inp, dev, hy3_mxfp4_weights, workload_shape=False)
 
@@ -215,10 +215,10 @@ def test_hy3_prefill_T8192_skew_mxfp4_sampled(dev, hy3_mxfp4_weights):
 def test_hy3_decode_T16_w4a8_full(dev, hy3_mxfp4_weights):
     """Hy3 decode, MXFP4 experts with dynamic MXFP8 activations (W4A8:
     block-scaled FP4 x FP8 MFMAs), every token; derived output bound."""
-    decode_full_check(MoEInputs(CONFIGS[11]), dev, hy3_mxfp4_weights, workload_shape=False)
+    decode_full_check(MoEInputs(CONFIGS["hy3_decode_T16_w4a8"]), dev, hy3_mxfp4_weights, workload_shape=False)
 
 
 def test_hy3_prefill_T8192_skew_w4a8_sampled(dev, hy3_mxfp4_weights):
-    inp = MoEInputs(CONFIGS[12])
+    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_w4a8"])
     log(f"case {inp.cfg.name}")
     sampled_check(inp, dev, hy3_mxfp4_weights, workload_shape=False)

@@ -179,7 +179,7 @@ SMALL = {
 
 
 def test_cfg0_tiny_fp32(dev):
-    inp = MoEInputs(CONFIGS[0])
+    inp = MoEInputs(CONFIGS["tiny_fp32"])
     out, gidx, gw, r, info = full_check(inp, dev)
     # the route itself: sums of weights are the scale
     np.testing.assert_allclose(gw.sum(1), 2.826, rtol=0, atol=4 * np.spacing(np.float32(2.826)))

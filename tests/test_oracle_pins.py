@@ -169,7 +169,7 @@ def test_softmax_and_sigmoid_against_math():
 
 
 def test_logits_against_fsum():
-    inp = MoEInputs(CONFIGS[0])
+    inp = MoEInputs(CONFIGS["tiny_fp32"])
     x, w = inp.x_f64(), inp.w_router().astype(np.float64)
     L = oracle.router_logits(x, w)
     rng = np.random.default_rng(5)
@@ -223,7 +223,7 @@ def test_layer_matches_scalar_loops(seed):
 
 
 def _cfg0():
-    inp = MoEInputs(CONFIGS[0])
+    inp = MoEInputs(CONFIGS["tiny_fp32"])
     c = inp.cfg
     ex = [inp.expert_f64(e) for e in range(c.E)]
     return inp, c, inp.x_f64(), inp.w_router().astype(np.float64), \
@@ -385,7 +385,7 @@ def test_fp8_dequant_is_scale_times_value():
 def test_fp8_layer_equals_layer_on_dequantised_weights():
     """The FP8 layer is the float64 layer on scale * value weights: a scale of
     2^k on a down matrix scales that expert's routed output by exactly 2^k."""
-    inp = MoEInputs(CONFIGS[5].with_T(6).with_(H=64, E=4, K=2, I=32, I_shared=32))
+    inp = MoEInputs(CONFIGS["hy3_decode_T16_fp8"].with_T(6).with_(H=64, E=4, K=2, I=32, I_shared=32))
     c = inp.cfg
     x = inp.x_f64()
     wr = inp.w_router().astype(np.float64)

@@ -28,23 +28,23 @@ def test_ties_round_to_even():
 
 
 def test_determinism_and_independence():
-    a, b = make_inputs(0), make_inputs(0)
+    a, b = make_inputs("tiny_fp32"), make_inputs("tiny_fp32")
     np.testing.assert_array_equal(a.x(), b.x())
     np.testing.assert_array_equal(a.expert(3)[0], b.expert(3)[0])
     assert not np.array_equal(a.expert(3)[0], a.expert(4)[0])
-    assert not np.array_equal(make_inputs(0, seed=1).x(), a.x())
+    assert not np.array_equal(make_inputs("tiny_fp32", seed=1).x(), a.x())
 
 
 def test_decode_and_prefill_share_weights_not_data():
-    d = MoEInputs(CONFIGS[1].with_(T=4, H=64, I=32, I_shared=32))
-    p = MoEInputs(CONFIGS[2].with_(T=4, H=64, I=32, I_shared=32))
+    d = MoEInputs(CONFIGS["hy3_decode_T16"].with_(T=4, H=64, I=32, I_shared=32))
+    p = MoEInputs(CONFIGS["hy3_prefill_T8192_skew"].with_(T=4, H=64, I=32, I_shared=32))
     np.testing.assert_array_equal(d.w_router(), p.w_router())
     np.testing.assert_array_equal(d.expert(5)[2], p.expert(5)[2])
     assert not np.array_equal(d.x(), p.x())
 
 
 def test_distributions_cfg0():
-    inp = make_inputs(0)
+    inp = make_inputs("tiny_fp32")
     c = inp.cfg
     x = inp.x()
     assert x.dtype == np.float32 and x.shape == (c.T, c.H)
@@ -60,10 +60,10 @@ def test_distributions_cfg0():
 
 
 def test_skew_bias_and_softmax_have_expected_kinds():
-    p = MoEInputs(CONFIGS[2].with_(T=2, H=64, I=32, I_shared=32))
+    p = MoEInputs(CONFIGS["hy3_prefill_T8192_skew"].with_(T=2, H=64, I=32, I_shared=32))
     b = p.bias()
     assert abs(b.std() - 0.3) < 0.1
-    s = MoEInputs(CONFIGS[4].with_(T=2, H=64, I=32, I_shared=32))
+    s = MoEInputs(CONFIGS["hunyuanimage_softmax_T32768"].with_(T=2, H=64, I=32, I_shared=32))
     assert s.bias() is None and s.cfg.route_mode == 1
 
 
@@ -75,15 +75,15 @@ def test_bf16_storage_and_stack():
     np.testing.assert_array_equal(wg[2], inp.expert(2)[0])
 
 
-@pytest.mark.parametrize("cfg_id", sorted(CONFIGS))
-def test_config_shapes(cfg_id):
-    c = CONFIGS[cfg_id]
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_config_shapes(name):
+    c = CONFIGS[name]
     assert 1 <= c.K <= c.E and c.H % 8 == 0 and c.I % 8 == 0
 
 
 def test_fp8_codes_and_scales():
     from synth import CONFIGS, MoEInputs
-    inp = MoEInputs(CONFIGS[5].with_T(2).with_(H=256, E=3, I=128, I_shared=64))
+    inp = MoEInputs(CONFIGS["hy3_decode_T16_fp8"].with_T(2).with_(H=256, E=3, I=128, I_shared=64))
     (g, u, d), sc = inp.expert_fp8(1)
     assert g.dtype == np.uint8 and g.shape == (128, 256) and d.shape == (256, 128)
     for q in (g, u, d):
@@ -100,19 +100,19 @@ def test_fp8_codes_and_scales():
 
 
 def test_static_activation_scales():
-    inp = MoEInputs(CONFIGS[8])
+    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_w8a8"])
     a1, a2 = inp.act_scales()
     assert a1.dtype == np.float32 and a2.dtype == np.float32
     assert a2.shape == (inp.cfg.E + 1,)
     assert a1 == np.float32(4.5 / 448)
     assert (a2 >= np.float32(12 / 448)).all() and (a2 <= np.float32(1.25 * 12 / 448)).all()
     # one model: the decode and prefill W8A8 workloads share the scales
-    np.testing.assert_array_equal(MoEInputs(CONFIGS[7]).act_scales()[1], a2)
-    assert CONFIGS[7].act_format == CONFIGS[8].act_format == "fp8_static"
+    np.testing.assert_array_equal(MoEInputs(CONFIGS["hy3_decode_T16_w8a8"]).act_scales()[1], a2)
+    assert CONFIGS["hy3_decode_T16_w8a8"].act_format == CONFIGS["hy3_prefill_T8192_skew_w8a8"].act_format == "fp8_static"
 
 
 def test_mxfp4_codes_and_scales():
-    inp = MoEInputs(CONFIGS[9].with_(H=256, I=128, I_shared=128, E=4))
+    inp = MoEInputs(CONFIGS["hy3_decode_T16_mxfp4"].with_(H=256, I=128, I_shared=128, E=4))
     (g, u, d), (sg, su, sd) = inp.expert_mxfp4(1)
     assert g.shape == (128, 128) and d.shape == (256, 64) and g.dtype == np.uint8
     assert sg.shape == (128, 8) and sd.shape == (256, 4)
