@@ -207,8 +207,10 @@ typedef struct hy3moe_ws_layout {
   int32_t tile_rows;     /* rows per tile of the expert GEMMs for this T       */
   size_t h;              /* dtype [R][I_max]  SwiGLU activations, I_max = max(I, I_shared) */
   size_t y;              /* dtype [R][H]      expert outputs before the combine */
-  size_t w_planes;       /* bf16 [3][E][H] router weight split into bf16 terms, used
-                            for bf16 batches of T >= 1024 (0 = not used)           */
+  size_t w_planes;       /* router weight split into 3 bf16 terms (E padded to a
+                            multiple of 16), stored in the order the router GEMM
+                            reads its operand fragments; used for bf16 batches of
+                            T >= 1024 (0 = not used)                              */
   size_t xq;             /* act_format FP8_STATIC: quantised x [T][H], E4M3 bytes on
                             the large-tile path, else their bf16 values (0 = not
                             used); h then holds h quantised the same way.

@@ -79,12 +79,12 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
   const int E = c->E, K = c->K, H = c->H;
   const int64_t N = T * K;
   size_t off = 0;
-  L->n_ksplit = router_ksplit(T, H, E);
+  L->n_ksplit = router_ksplit(T, H, E, c->dtype);
   L->logits_part = off; off += al((size_t)L->n_ksplit * T * E * 8);
   L->idx = off;         off += al((size_t)N * 4);
   L->weight = off;      off += al((size_t)N * 4);
   if (router_use_planes(T, c->dtype)) {
-    L->w_planes = off;  off += al((size_t)3 * E * H * 2);
+    L->w_planes = off;  off += al((size_t)3 * ((E + 15) / 16 * 16) * H * 2);
   }
   if (!for_forward) { L->total = off; return; }
   L->n_chunks = (int32_t)((N + PERM_CHUNK - 1) / PERM_CHUNK);

@@ -38,7 +38,7 @@ inline int expert_path(int64_t T, int K, int E, bool big_ok = true) {
 // Router -------------------------------------------------------------------
 constexpr int ROUTER_PLANES_MIN_T = 1024;  // bf16 batches this large pre-split the weight
 bool router_use_planes(int64_t T, int dtype);
-int router_ksplit(int64_t T, int H, int E);
+int router_ksplit(int64_t T, int H, int E, int dtype);
 // planes: workspace for the bf16 weight planes [3][E][H], or null (split on the fly).
 hipError_t launch_router(const void *x, int dtype, int router_prec, const float *w_router,
                          uint16_t *planes, double *part, int T, int H, int E, int S,

@@ -329,14 +329,26 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float *__restrict
 
 // fp32 weight -> bf16 planes, 8 elements per thread.  PREC 0: hi, mid, lo
 // (exact three-term split); PREC 1: hi and bf16(256 (w - hi)).
+//
+// Fragment-major layout, so that each of the planes kernel's weight loads is
+// one contiguous 1 KB block per wavefront (8 whole cache lines, not 16
+// half lines of 16 rows): for expert block b (16 experts; E padded to a
+// multiple of 16, the padding rows repeating expert E-1), K step st (64
+// values), plane p and half `sub` (32 values), 64 lanes of 16 bytes, lane
+// 16 g + r holding W[16 b + r][64 st + 32 sub + 8 g + (0..7)], i.e. uint4
+// index (((b * (H/64) + st) * NP + p) * 2 + sub) * 64 + lane.
 template <int PREC>
 __global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ wr,
-                                                           uint16_t *__restrict__ planes,
-                                                           int64_t n) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (i >= n) return;
-  const float4 a = *reinterpret_cast<const float4 *>(wr + i);
-  const float4 b = *reinterpret_cast<const float4 *>(wr + i + 4);
+                                                           uint16_t *__restrict__ planes, int E,
+                                                           int H, int E_pad) {
+  constexpr int NP = (PREC == 0) ? 3 : 2;
+  const int cpr = H / 8;                                    // 8-value chunks per row
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)E_pad * cpr) return;
+  const int e = (int)(i / cpr), c = (int)(i - (int64_t)e * cpr);
+  const float *src = wr + (size_t)min(e, E - 1) * H + c * 8;
+  const float4 a = *reinterpret_cast<const float4 *>(src);
+  const float4 b = *reinterpret_cast<const float4 *>(src + 4);
   const float wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint16_t th[8], tm[8], tl[8];
 #pragma unroll
@@ -348,39 +360,64 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *__restri
       tm[j] = f32_to_bf16((wv[j] - bf16_to_f32(th[j])) * 256.0f);
     }
   }
-  *reinterpret_cast<uint4 *>(planes + i) =
-      make_uint4(pack2(th[0], th[1]), pack2(th[2], th[3]), pack2(th[4], th[5]), pack2(th[6], th[7]));
-  *reinterpret_cast<uint4 *>(planes + n + i) =
-      make_uint4(pack2(tm[0], tm[1]), pack2(tm[2], tm[3]), pack2(tm[4], tm[5]), pack2(tm[6], tm[7]));
+  // c * 8 = 64 st + 32 sub + 8 g
+  const int st = c >> 3, sub = (c >> 2) & 1, g = c & 3;
+  const size_t o = ((size_t)((e >> 4) * (H / 64) + st) * NP * 2 + sub) * 64 + g * 16 + (e & 15);
+  uint4 *out = reinterpret_cast<uint4 *>(planes);
+  out[o] = make_uint4(pack2(th[0], th[1]), pack2(th[2], th[3]), pack2(th[4], th[5]),
+                      pack2(th[6], th[7]));
+  out[o + 2 * 64] = make_uint4(pack2(tm[0], tm[1]), pack2(tm[2], tm[3]), pack2(tm[4], tm[5]),
+                               pack2(tm[6], tm[7]));
   if (PREC == 0)
-    *reinterpret_cast<uint4 *>(planes + 2 * n + i) =
-        make_uint4(pack2(tl[0], tl[1]), pack2(tl[2], tl[3]), pack2(tl[4], tl[5]), pack2(tl[6], tl[7]));
+    out[o + 4 * 64] = make_uint4(pack2(tl[0], tl[1]), pack2(tl[2], tl[3]), pack2(tl[4], tl[5]),
+                                 pack2(tl[6], tl[7]));
 }
 
-// Router GEMM on pre-split bf16 planes.  K steps of 64: the weight fragments
-// of step st+1 are loaded while step st computes (two register sets), the x
-// tile of step st+2 goes to registers and is written to the idle LDS buffer
-// at the end of step st+1.  Loads past the last step re-read it (in bounds,
-// unused) so that no load is conditional, and a scheduling barrier keeps them
-// at the top of the step.  The loop body is one fp64 fold period (4 steps),
-// so the fold needs no branch.  Token rows past T re-read row T-1 and are
-// not stored.
-template <int PREC>
-__global__ __launch_bounds__(256, 2) void router_planes_kernel(const uint16_t *__restrict__ x,
-                                                               const uint16_t *__restrict__ wp,
-                                                               double *__restrict__ part, int T,
-                                                               int H, int E, int kslice) {
+// Wavefronts (16 experts each) of a planes-kernel workgroup for E experts:
+// every expert of the layer in one workgroup where E <= 192, so that a
+// 64-token x tile is read once for all of them.
+inline int planes_waves(int E) { return E <= 64 ? 4 : E <= 128 ? 8 : 12; }
+
+// Router GEMM on pre-split bf16 planes.  A workgroup of NW wavefronts takes
+// 64 tokens x 16 NW experts over one K-slice.  K steps of 64: the weight
+// fragments of step st+1 are loaded while step st computes (two register
+// sets), the x tile of step st+2 goes to registers (wavefronts 0-3) and is
+// written to the idle LDS buffer at the end of step st+1.  Loads past the
+// last step re-read it (in bounds, unused) so that no load is conditional,
+// and a scheduling barrier keeps them at the top of the step.  The loop body
+// is one fp64 fold period (4 steps), so the fold needs no branch.  Token rows
+// past T re-read row T-1 and are not stored; experts past E re-read expert
+// E-1 and are not stored.
+//
+// XCD-aware order: the three weight planes (E x H x 6 bytes: 4.7 MB at Hy3
+// shape) exceed one XCD's L2, so the work items (slice, expert block, token
+// tile) are numbered slice-major and each XCD takes a contiguous run of
+// them (workgroup b runs on XCD b % 8): an XCD then reads only its slices'
+// share of the planes, which stays in its L2 while the x tiles stream past.
+template <int PREC, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void router_planes_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp, double *__restrict__ part,
+    int T, int H, int E, int kslice, int S) {
   constexpr int NP = (PREC == 0) ? 3 : 2;
   constexpr int XB = RT_TOK * 8;   // uint4 per LDS buffer
   constexpr int FOLD = RT_CHUNK / 64;
   __shared__ uint4 xs[2 * XB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * RT_TOK, e0 = blockIdx.y * RT_EXP, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_tt = (T + RT_TOK - 1) / RT_TOK, n_eb = (E + 16 * NW - 1) / (16 * NW);
+  const int n_items = n_tt * n_eb * S, per = (n_items + 7) / 8;
+  const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;   // the grid is padded to a multiple of 8 x per
+  const int combo = item / n_tt, tt = item - combo * n_tt;
+  const int s = combo / n_eb, eb = combo - s * n_eb;
+  const int t0 = tt * RT_TOK, e0 = eb * 16 * NW;
   const int kbeg = s * kslice;
+  const bool xload = wave < 4;     // wavefronts 0-3 stage the x tile
   const int r16 = lane & 15, g = lane >> 4;
-  const int e_row = min(e0 + wave * 16 + r16, E - 1);
-  const uint32_t pstride = (uint32_t)(E * H);   // elements per plane (< 2^24)
-  const uint16_t *wrow = wp + (size_t)e_row * H + kbeg + g * 8;
+  // the wavefront's expert block (blocks past the last repeat it: not stored)
+  const int blk = min((e0 >> 4) + wave, (E + 15) / 16 - 1);
+  const uint4 *wfrag = reinterpret_cast<const uint4 *>(wp) +
+                       (size_t)(blk * (H / 64) + kbeg / 64) * NP * 2 * 64 + lane;
   const int xrow = tid >> 3, xc = tid & 7;
   const uint16_t *xp0 = x + (size_t)min(t0 + xrow, T - 1) * H + kbeg + xc * 8;
   const uint16_t *xp1 = x + (size_t)min(t0 + xrow + 32, T - 1) * H + kbeg + xc * 8;
@@ -400,8 +437,7 @@ __global__ __launch_bounds__(256, 2) void router_planes_kernel(const uint16_t *_
   uint4 wA00, wA01, wA02, wA10, wA11, wA12, xA0, xA1;
   uint4 wB00, wB01, wB02, wB10, wB11, wB12, xB0, xB1;
 
-#define HY3_W(st, sub, p) \
-  (*reinterpret_cast<const uint4 *>(wrow + (p) * pstride + (uint32_t)((st) * 64 + (sub) * 32)))
+#define HY3_W(st, sub, p) (wfrag[(uint32_t)((((st) * NP + (p)) * 2 + (sub)) * 64)])
 #define HY3_LOADW(S, st)                                                               \
   {                                                                                    \
     const int st_ = (st);                                                              \
@@ -410,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void router_planes_kernel(const uint16_t *_
     if (NP == 3) { w##S##02 = HY3_W(st_, 0, 2); w##S##12 = HY3_W(st_, 1, 2); }         \
   }
 #define HY3_LOADX(S, st)                                                               \
-  {                                                                                    \
+  if (xload) {                                                                         \
     const int st_ = (st);                                                              \
     x##S##0 = *reinterpret_cast<const uint4 *>(xp0 + st_ * 64);                        \
     x##S##1 = *reinterpret_cast<const uint4 *>(xp1 + st_ * 64);                        \
@@ -430,8 +466,10 @@ __global__ __launch_bounds__(256, 2) void router_planes_kernel(const uint16_t *_
     __builtin_amdgcn_sched_barrier(0);                                                 \
     HY3_SUB(C, 0, buf);                                                                \
     HY3_SUB(C, 1, buf);                                                                \
-    xs[((buf) ^ 1) * XB + xw0] = x##N##0;                                              \
-    xs[((buf) ^ 1) * XB + xw1] = x##N##1;                                              \
+    if (xload) {                                                                       \
+      xs[((buf) ^ 1) * XB + xw0] = x##N##0;                                            \
+      xs[((buf) ^ 1) * XB + xw1] = x##N##1;                                            \
+    }                                                                                  \
     __syncthreads();                                                                   \
   }
 #define HY3_FOLD()                                                                     \
@@ -449,8 +487,10 @@ __global__ __launch_bounds__(256, 2) void router_planes_kernel(const uint16_t *_
   HY3_LOADW(A, 0);
   HY3_LOADX(A, 0);
   HY3_LOADX(B, min(1, n - 1));
-  xs[xw0] = xA0;
-  xs[xw1] = xA1;
+  if (xload) {
+    xs[xw0] = xA0;
+    xs[xw1] = xA1;
+  }
   __syncthreads();
   static_assert(FOLD == 4, "loop body is one fold period of 4 steps");
   int st = 0;
@@ -490,12 +530,18 @@ __global__ __launch_bounds__(256, 2) void router_planes_kernel(const uint16_t *_
 
 bool router_use_planes(int64_t T, int dtype) { return dtype == DT_BF16 && T >= ROUTER_PLANES_MIN_T; }
 
-int router_ksplit(int64_t T, int H, int E) {
-  // Enough workgroups to spread the weight read over the chip; each K-slice
-  // stays a multiple of 64 and at least 128 long.
-  const int64_t tiles = ((T + RT_TOK - 1) / RT_TOK) * ((E + RT_EXP - 1) / RT_EXP);
+int router_ksplit(int64_t T, int H, int E, int dtype) {
+  // Enough workgroups to spread the weight read over the chip (the planes
+  // kernel: about one workgroup of up to 12 wavefronts per CU; the others:
+  // 512 of 4 wavefronts); each K-slice stays a multiple of 64 and at least
+  // 128 long.
+  const bool planes = router_use_planes(T, dtype);
+  const int eb = planes ? 16 * planes_waves(E) : RT_EXP;
+  const int64_t tiles = ((T + RT_TOK - 1) / RT_TOK) * ((E + eb - 1) / eb);
+  const int64_t want = planes ? (planes_waves(E) == 4 ? 512 : 256) : 512;
   int S = 1;
-  while (S < MAX_KSPLIT && tiles * S < 512 && (H / (2 * S)) >= 128 && (H % (2 * S * 64)) == 0)
+  while (S < MAX_KSPLIT && tiles * S < want && (H / (2 * S)) >= 128 &&
+         (H % (2 * S * 64)) == 0)
     S *= 2;
   return S;
 }
@@ -506,18 +552,32 @@ hipError_t launch_router(const void *x, int dtype, int router_prec, const float 
   const int kslice = H / S;
   dim3 grid((T + RT_TOK - 1) / RT_TOK, (E + RT_EXP - 1) / RT_EXP, S);
   if (planes) {
-    const int64_t n = (int64_t)E * H;
-    const dim3 sgrid((unsigned)((n / 8 + 255) / 256));
+    const int E_pad = (E + 15) / 16 * 16;
+    const dim3 sgrid((unsigned)(((int64_t)E_pad * H / 8 + 255) / 256));
     const uint16_t *xb = static_cast<const uint16_t *>(x);
+    const int nw = planes_waves(E);
+    const int64_t items = (int64_t)((T + RT_TOK - 1) / RT_TOK) *
+                          ((E + 16 * nw - 1) / (16 * nw)) * S;
+    const dim3 pgrid((unsigned)((items + 7) / 8 * 8));   // 8 equal XCD runs
+    if (router_prec == 0)
+      hipLaunchKernelGGL(router_split_kernel<0>, sgrid, dim3(256), 0, stream, wr, planes, E, H,
+                         E_pad);
+    else
+      hipLaunchKernelGGL(router_split_kernel<1>, sgrid, dim3(256), 0, stream, wr, planes, E, H,
+                         E_pad);
+#define HY3_PLANES(P, NW)                                                              \
+  hipLaunchKernelGGL((router_planes_kernel<P, NW>), pgrid, dim3(64 * NW), 0, stream, xb, planes, \
+                     part, T, H, E, kslice, S)
     if (router_prec == 0) {
-      hipLaunchKernelGGL(router_split_kernel<0>, sgrid, dim3(256), 0, stream, wr, planes, n);
-      hipLaunchKernelGGL(router_planes_kernel<0>, grid, dim3(256), 0, stream, xb, planes, part,
-                         T, H, E, kslice);
+      if (nw == 4) HY3_PLANES(0, 4);
+      else if (nw == 8) HY3_PLANES(0, 8);
+      else HY3_PLANES(0, 12);
     } else {
-      hipLaunchKernelGGL(router_split_kernel<1>, sgrid, dim3(256), 0, stream, wr, planes, n);
-      hipLaunchKernelGGL(router_planes_kernel<1>, grid, dim3(256), 0, stream, xb, planes, part,
-                         T, H, E, kslice);
+      if (nw == 4) HY3_PLANES(1, 4);
+      else if (nw == 8) HY3_PLANES(1, 8);
+      else HY3_PLANES(1, 12);
     }
+#undef HY3_PLANES
     return hipGetLastError();
   }
   if (dtype == DT_F32) {
