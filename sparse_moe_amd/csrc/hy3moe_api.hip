@@ -300,6 +300,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.tiles = pa.tiles;
   ea.E = E; ea.H = H; ea.I = cfg->I; ea.I_shared = cfg->I_shared; ea.ldh = Imax;
   ea.max_tiles = L.max_tiles;
+  ea.n_rows = (int)((int64_t)T * K + (has_shared ? T : 0));
   ea.act = act; ea.w0 = w->w_gate; ea.w1 = w->w_up; ea.ws0 = w->ws_gate; ea.ws1 = w->ws_up;
   // W4A8 on the large-tile path: the gate-up epilogue quantises h itself
   const bool h_codes_fused = amx_codes && path == PATH_BIG;

@@ -75,6 +75,7 @@ struct ExpertArgs {
   const int32_t *offsets;
   const int32_t *tiles;   // (group, first row) pairs, then the tile count
   int E, H, I, I_shared, ldh, max_tiles;
+  int n_rows;             // rows of sorted_token (T K routed + T shared)
   // FP8 E4M3 expert weights (w_fp8 = 1): w0/w1/ws0/ws1 hold bytes and the
   // weight is scale * value, with scales sc0[g] / sc1[g] for routed group g
   // and *ssc0 / *ssc1 for the shared expert (gate-up: gate, up; down: down).

@@ -101,9 +101,11 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
   // bytes per weight row of K elements (MXFP4: half a byte per element)
   auto rowb = [](int K) { return F4 ? K / 2 : K * (F8 ? 1 : EB); };
   const int tile = u / n_col_blocks, cb = u - tile * n_col_blocks;
-  const int g = a.tiles[2 * tile];
-  o.row0 = a.tiles[2 * tile + 1];
-  o.grp_end = a.offsets[g + 1];
+  // uniform per wavefront (u is); readfirstlane keeps the values, read from
+  // LDS, in scalar registers, so the branches on them stay scalar
+  const int g = __builtin_amdgcn_readfirstlane(a.tiles[2 * tile]);
+  o.row0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * tile + 1]);
+  o.grp_end = __builtin_amdgcn_readfirstlane(a.offsets[g + 1]);
   const bool shared = (g == a.E);
   const int Ig = shared ? a.I_shared : a.I;
   o.col0 = cb * (GATE_UP ? 16 : 32) + (half == 2 ? 16 : 0);
@@ -235,10 +237,31 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
   }
 }
 
+// LDS bytes of the unit metadata a workgroup stages (see the kernel).
+inline size_t meta_lds_bytes(const ExpertArgs &a, bool gate_up) {
+  return 4 * ((size_t)2 * a.max_tiles + 1 + a.E + 2 + (gate_up ? a.n_rows : 0));
+}
+
 template <typename T, bool GATE_UP, int MT, int WF>
-__global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(ExpertArgs a,
+__global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(ExpertArgs a_in,
                                                                           int n_col_blocks) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4, MXA = WF == WF_W4A8;
+  // The unit metadata -- tile list, group offsets and (gate-up) the sorted
+  // token ids -- is staged in LDS once per workgroup, so that the set-up of a
+  // wavefront's next unit reads LDS instead of a chain of dependent global
+  // loads, which held back the unit's first weight loads at every change.
+  extern __shared__ int32_t meta[];
+  const int n_t = 2 * a_in.max_tiles + 1, n_o = a_in.E + 2;
+  for (int i = threadIdx.x; i < n_t; i += 256) meta[i] = a_in.tiles[i];
+  for (int i = threadIdx.x; i < n_o; i += 256) meta[n_t + i] = a_in.offsets[i];
+  if (GATE_UP)
+    for (int i = threadIdx.x; i < a_in.n_rows; i += 256)
+      meta[n_t + n_o + i] = a_in.sorted_token[i];
+  __syncthreads();
+  ExpertArgs a = a_in;
+  a.tiles = meta;
+  a.offsets = meta + n_t;
+  a.sorted_token = meta + n_t + n_o;
   constexpr int U = steps_per_set<MT, WF>();   // 64-byte K steps per row per register set
   constexpr int XN = token_chunks<WF>();       // 16-byte token chunks per step
   const int lane = threadIdx.x & 63;
@@ -247,7 +270,7 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   // MFMA is a whole-wavefront operation: it must never sit under a per-lane
   // EXEC mask that is expected to switch it off.)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_units = a.tiles[2 * a.max_tiles] * n_col_blocks;
+  const int n_units = __builtin_amdgcn_readfirstlane(a.tiles[2 * a.max_tiles]) * n_col_blocks;
   const int nw = gridDim.x * 4, w = blockIdx.x * 4 + wave;
   const int kmax = n_units / nw + 1;
   // Wavefront ids interleave the XCDs (block b runs on XCD b % 8), so the
@@ -423,11 +446,11 @@ hipError_t launch_skinny_t(const ExpertArgs &a, bool gate_up, hipStream_t stream
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int ncb = (Imax + 15) / 16;
     hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF>), dim3(STREAM_BLOCKS), dim3(256),
-                       0, stream, a, ncb);
+                       meta_lds_bytes(a, true), stream, a, ncb);
   } else {
     const int ncb = (a.H + 31) / 32;
     hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF>), dim3(STREAM_BLOCKS), dim3(256),
-                       0, stream, a, ncb);
+                       meta_lds_bytes(a, false), stream, a, ncb);
   }
   return hipGetLastError();
 }

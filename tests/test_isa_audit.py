@@ -41,7 +41,7 @@ def masked_mfmas(asm):
             kernel, depth = s.split(":")[0], 0
         elif s.startswith("s_endpgm"):
             depth = 0
-        elif s.startswith("s_or_saveexec"):
+        elif s.startswith(("s_or_saveexec", "s_andn2_saveexec")):
             pass        # the else half of an if/else region: same nesting level
         elif "saveexec" in s:
             depth += 1
