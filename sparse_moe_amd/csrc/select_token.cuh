@@ -12,8 +12,10 @@
 // the scores are evaluated in float64, so the selection is decided on
 // fp32-accurate logits with no further rounding.  Picks come out in
 // descending selection score; equal scores go to the lower expert index.
-// Each lane owns experts lane, lane+64, lane+128, lane+192 (E <= 256); the
-// arg-max of every round is a butterfly over the wavefront.
+// Each lane owns experts lane, lane+64, lane+128, lane+192 (E <= 256).  A
+// selection round takes the largest remaining score of the wavefront (DPP
+// moves within each row of 16 lanes, then the four row maxima) and the
+// lowest expert index holding it (one ballot per slot, lowest slot first).
 #pragma once
 
 #include "common.cuh"
@@ -25,6 +27,32 @@ __device__ __forceinline__ double wave_max_f64(double v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
   return v;
 }
+// max(v, v of lane CTRL(lane)) for a DPP lane pattern CTRL that stays in the row.
+template <int CTRL>
+__device__ __forceinline__ double dpp_max_f64(double v) {
+  const uint64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp((int)b, (int)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(b >> 32), (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return fmax(v, __longlong_as_double(((int64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)b, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((int64_t)hi << 32) | lo);
+}
+// Maximum over the wavefront, the same in every lane (exact: no rounding).
+// Row of 16: swap neighbours (quad_perm 1,0,3,2), pairs (2,3,0,1), then the
+// mirrored half row and the mirrored row; then the four rows' maxima.
+__device__ __forceinline__ double wave_max_f64_dpp(double v) {
+  v = dpp_max_f64<0xB1>(v);
+  v = dpp_max_f64<0x4E>(v);
+  v = dpp_max_f64<0x141>(v);
+  v = dpp_max_f64<0x140>(v);
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)),
+              fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -94,24 +122,32 @@ __device__ __forceinline__ void select_token(const double *__restrict__ part, in
   int my_pick = -1;
   double my_prob = 0.0, tot = 0.0;
   for (int j = 0; j < K; ++j) {
-    double bv = -INFINITY;
-    int be = 0x7fffffff;
+    double lv = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (live[q] && !taken[q]) lv = fmax(lv, sel[q]);
+    const double bv = wave_max_f64_dpp(lv);
+    // The winner: the lowest expert index lane + 64 q whose score is bv
+    // (slots in order, then the lowest lane).  Should no remaining score
+    // equal bv (only possible with NaN scores), the lowest remaining expert.
+    int owner = -1, slot = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (live[q] && !taken[q] && sel[q] > bv) { bv = sel[q]; be = lane + 64 * q; }
+      const uint64_t m = __ballot(live[q] && !taken[q] && sel[q] == bv);
+      if (owner < 0 && m) { owner = __builtin_ctzll(m); slot = q; }
     }
+    if (owner < 0) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+      for (int q = 0; q < 4; ++q) {
+        const uint64_t m = __ballot(live[q] && !taken[q]);
+        if (owner < 0 && m) { owner = __builtin_ctzll(m); slot = q; }
+      }
     }
-    // Every lane now agrees on the winner be.
-    const int owner = be & 63, slot = be >> 6;
+    const int be = owner + 64 * slot;
     double p = 0.0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) if (q == slot) p = prob[q];
-    p = __shfl(p, owner, 64);
+    p = readlane_f64(p, owner);   // owner is uniform
     if (lane == owner) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) if (q == slot) taken[q] = true;
