@@ -281,3 +281,30 @@ def test_route_entry_matches_forward_route(dev):
     np.testing.assert_array_equal(idx.cpu().numpy(), fidx)
     np.testing.assert_array_equal(wt.cpu().numpy(), fw)
     check_route(fidx, fw, oracle_route(inp))
+
+
+@pytest.mark.parametrize("route_mode", [0, 1])
+def test_route_indices_valid_with_nan_scores(dev, route_mode):
+    """Rows of x holding NaN give NaN logits.  The routing still returns K
+    distinct experts in [0, E) for every token (NaN scores never compare
+    equal, so the selection falls back to the lowest remaining experts),
+    and the rows without NaN match the oracle's routing.  hy3moe_route only:
+    no kernel here indexes memory with the picks."""
+    inp = random_small(26, T=70, H=256, E=24, K=6, I=128, I_shared=128, dtype="bf16",
+                       route_mode=route_mode)
+    w = upload_weights(inp, dev)
+    cfg = config_of(inp)
+    xb = np.array(inp.x(), copy=True)            # bf16 bits [T][H]
+    nan_rows = np.arange(0, 70, 7)
+    xb[nan_rows, 5] = 0x7FC0                      # bf16 quiet NaN
+    xb[nan_rows[::2], :] = 0x7FC0                 # some rows all NaN
+    idx, wt = sm.route(cfg, to_torch(xb, "bf16", dev), w["w_router"], w["expert_bias"])
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy().reshape(70, 6)
+    assert ((idx >= 0) & (idx < 24)).all()
+    assert all(len(set(r)) == 6 for r in idx)
+    r = oracle_route(inp)
+    ok = np.setdiff1d(np.arange(70), nan_rows)
+    ok = ok[r.margin[ok] > MARGIN]
+    assert ok.size > 40
+    np.testing.assert_array_equal(np.sort(idx[ok], 1), np.sort(r.idx[ok], 1))
