@@ -9,6 +9,7 @@ from .binding import (EXPORTED_SYMBOLS, HY3MOE_BF16, HY3MOE_F32,
                       hy3moe_workspace_bytes,
                       hy3moe_workspace_layout, hy3moe_ws_layout, load, make_config,
                       route, strerror)
+from .binding import ATTN_EXPORTED_SYMBOLS, ATTN_TILE, AttnPlan, attn_decode, attn_plan
 
 __all__ = [
     "EXPORTED_SYMBOLS", "HY3MOE_BF16", "HY3MOE_F32", "HY3MOE_N_STAGES", "STAGE_NAMES",
@@ -17,4 +18,5 @@ __all__ = [
     "Hy3MoEError", "alloc_workspace", "forward", "hy3moe_config", "hy3moe_forward",
     "hy3moe_quantize_e4m3", "hy3moe_route", "hy3moe_weights", "hy3moe_workspace_bytes", "hy3moe_workspace_layout",
     "hy3moe_ws_layout", "load", "make_config", "route", "strerror",
+    "ATTN_EXPORTED_SYMBOLS", "ATTN_TILE", "AttnPlan", "attn_decode", "attn_plan",
 ]

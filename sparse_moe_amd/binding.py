@@ -125,6 +125,20 @@ def load() -> ctypes.CDLL:
     L.hy3moe_quantize_e4m3.restype = ctypes.c_int
     L.hy3moe_quantize_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.hy3attn_max_tasks.restype = ctypes.c_int64
+    L.hy3attn_max_tasks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.hy3attn_workspace_bytes.restype = ctypes.c_size_t
+    L.hy3attn_workspace_bytes.argtypes = [ctypes.c_int64]
+    L.hy3attn_plan.restype = ctypes.c_int
+    L.hy3attn_plan.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
+    L.hy3attn_decode.restype = ctypes.c_int
+    L.hy3attn_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p, ctypes.c_void_p]
     if L.hy3moe_abi_version() != ABI_VERSION:
         raise RuntimeError("libhy3moe ABI version mismatch")
     _LIB = L
@@ -275,3 +289,70 @@ def forward(cfg: hy3moe_config, x, weights, workspace=None, return_route=False, 
         weight = torch.empty((int(cfg.T), int(cfg.K)), dtype=torch.float32, device=x.device)
     hy3moe_forward(cfg, x, weights, out, workspace, idx, weight, stream)
     return (out, idx, weight) if return_route else out
+
+
+# ---------------------------------------------------------------------------
+# Split-KV decode attention (include/hy3attn.h): argument marshalling only.
+# ---------------------------------------------------------------------------
+ATTN_EXPORTED_SYMBOLS = ("hy3attn_max_tasks", "hy3attn_workspace_bytes", "hy3attn_plan",
+                         "hy3attn_decode")
+ATTN_TILE = 256
+
+
+class AttnPlan:
+    """Task map from hy3attn_plan (host numpy arrays)."""
+
+    def __init__(self, tasks, worker_begin, row_begin, n_workers, tile):
+        self.tasks, self.worker_begin, self.row_begin = tasks, worker_begin, row_begin
+        self.n_workers, self.tile = n_workers, tile
+
+
+def attn_plan(kv_len, n_kv_heads: int, tile: int = ATTN_TILE, n_workers: int = 512) -> AttnPlan:
+    import numpy as np
+    L = load()
+    kv = np.ascontiguousarray(np.asarray(kv_len, dtype=np.int32))
+    B = int(kv.size)
+    cap = int(L.hy3attn_max_tasks(B, n_kv_heads, n_workers))
+    tasks = np.zeros((max(cap, 1), 4), dtype=np.int32)
+    wb = np.zeros(n_workers + 1, dtype=np.int32)
+    rb = np.zeros(B * n_kv_heads + 1, dtype=np.int32)
+    nt = ctypes.c_int64(0)
+    rc = L.hy3attn_plan(kv.ctypes.data if B else None, B, n_kv_heads, tile, n_workers,
+                        tasks.ctypes.data, cap, wb.ctypes.data, rb.ctypes.data,
+                        ctypes.byref(nt))
+    if rc != 0:
+        raise RuntimeError(f"hy3attn_plan failed ({rc})")
+    return AttnPlan(tasks[:nt.value].copy(), wb, rb, n_workers, tile)
+
+
+def attn_decode(q, k, v, kv_len, plan: AttnPlan, out=None, workspace=None):
+    """q [B][Hq][128], k, v [Hkv][sum L][128] bf16 torch tensors on one GPU;
+    returns out [B][Hq][128] bf16.  The plan's arrays are copied to the
+    device (the caller may build and copy them once per inference)."""
+    import numpy as np
+    import torch
+    L = load()
+    dev = q.device
+    B, Hq, _ = q.shape
+    Hkv = k.shape[0]
+    starts = np.zeros(B + 1, dtype=np.int32)
+    starts[1:] = np.cumsum(np.asarray(kv_len, dtype=np.int64))
+    kv_start = torch.from_numpy(starts).to(dev)
+    tasks = torch.from_numpy(plan.tasks.reshape(-1)).to(dev) if plan.tasks.size else \
+        torch.zeros(4, dtype=torch.int32, device=dev)
+    wb = torch.from_numpy(plan.worker_begin).to(dev)
+    rb = torch.from_numpy(plan.row_begin).to(dev)
+    n_tasks = int(plan.tasks.shape[0])
+    need = int(L.hy3attn_workspace_bytes(n_tasks))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = L.hy3attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_start.data_ptr(), B, Hkv,
+                          plan.tile, tasks.data_ptr(), n_tasks, wb.data_ptr(), plan.n_workers,
+                          rb.data_ptr(), workspace.data_ptr(), workspace.numel(), out.data_ptr(),
+                          stream)
+    if rc != 0:
+        raise RuntimeError(f"hy3attn_decode failed ({rc})")
+    return out

@@ -33,6 +33,7 @@ SOURCES = [
     "k_expert_big.hip",
     "k_combine.hip",
     "k_quant.hip",
+    "k_attention.hip",
 ]
 
 ARCH = "gfx950"

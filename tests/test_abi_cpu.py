@@ -4,6 +4,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import sparse_moe_amd as sm
@@ -265,3 +267,45 @@ def test_fp8_weights_need_their_scales(lib):
     assert fw(ctypes.byref(cfg_ns), 4096, ctypes.byref(missing), 8192, None, None, 4096,
               need_ns - 1, None) == -3
     del ok
+
+
+def attn_declared_functions():
+    text = open(os.path.join(ROOT, "include", "hy3attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hy3attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_attention_header_symbols_are_exported(lib):
+    fns = attn_declared_functions()
+    assert sorted(sm.ATTN_EXPORTED_SYMBOLS) == fns
+    for name in fns:
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value, name
+
+
+@pytest.mark.parametrize("kv_len, hkv, tile, workers", [
+    ([300, 700], 2, 256, 3), ([131072], 8, 256, 512), ([0, 1, 255, 256, 257, 5000], 8, 256, 7),
+    ([7] * 40, 8, 256, 512), ([100000, 3, 40000, 0, 9999], 8, 128, 300), ([], 8, 256, 4),
+    ([0, 0], 8, 256, 4)])
+def test_attention_plan_matches_the_oracle(lib, kv_len, hkv, tile, workers):
+    """The library's task map (host C++) equals the oracle's greedy fill."""
+    from oracle.attention import plan_split_kv
+    p = sm.attn_plan(kv_len, hkv, tile, workers)
+    ref = plan_split_kv(kv_len, hkv, tile, workers)
+    np.testing.assert_array_equal(p.tasks.reshape(-1, 4), ref.tasks)
+    np.testing.assert_array_equal(p.worker_begin, ref.worker_begin)
+    np.testing.assert_array_equal(p.row_begin, ref.row_begin)
+
+
+def test_attention_plan_rejects_bad_arguments(lib):
+    L = lib
+    nt = ctypes.c_int64(0)
+    buf = np.zeros(64, dtype=np.int32)
+    kv = np.array([5], dtype=np.int32)
+    assert L.hy3attn_plan(kv.ctypes.data, 1, 0, 256, 4, buf.ctypes.data, 8, buf.ctypes.data,
+                          buf.ctypes.data, ctypes.byref(nt)) == -1
+    kv_neg = np.array([-1], dtype=np.int32)
+    assert L.hy3attn_plan(kv_neg.ctypes.data, 1, 8, 256, 4, buf.ctypes.data, 8, buf.ctypes.data,
+                          buf.ctypes.data, ctypes.byref(nt)) == -1
+    big = np.array([100000], dtype=np.int32)
+    assert L.hy3attn_plan(big.ctypes.data, 1, 8, 256, 4, buf.ctypes.data, 2, buf.ctypes.data,
+                          buf.ctypes.data, ctypes.byref(nt)) == -2

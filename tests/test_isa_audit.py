@@ -21,7 +21,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not ava
 
 KERNEL_SOURCES = ["k_router.hip", "k_expert_skinny.hip", "k_expert_tiled.hip",
                   "k_expert_big.hip", "k_select.hip", "k_permute.hip", "k_combine.hip",
-                  "k_quant.hip"]
+                  "k_quant.hip", "k_attention.hip"]
 
 
 def assemble(src, tmp_path):
