@@ -68,12 +68,116 @@ def measured_traffic(workload, kernel):
     return d.get("bytes_per_launch")
 
 
+# Split-KV decode attention workloads (Hy3 GQA: 64 query / 8 KV heads,
+# head_dim 128): (description, cached lengths) from seeded generators.
+ATTN_WORKLOADS = {"attn_long": "one request, 131072 cached tokens",
+                  "attn_mixed": "32 requests, lengths log-uniform in [512, 65536]"}
+ATTN_WORKERS = 512
+
+
+def attention_bench(args, dev):
+    """Split + combine kernels of hy3attn_decode over the workload's batch:
+    W warm-up and K timed calls between synchronizations; per-kernel times
+    from HIP events recorded on the stream the kernels run on."""
+    import numpy as np
+    import torch
+    import sparse_moe_amd as sm
+    from synth.attention_inputs import attention_inputs, bits_to_f64, mixed_lengths
+    kv_len = [131072] if args.workload == "attn_long" else mixed_lengths(5, 32, 512, 65536)
+    hkv, d = 8, 128
+    qb, kb, vb = attention_inputs(11, kv_len, hkv)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = bf(qb), bf(kb), bf(vb)
+    plan = sm.attn_plan(kv_len, hkv, sm.ATTN_TILE, ATTN_WORKERS)
+    out = torch.empty_like(q)
+    L = sm.load()
+    n_tasks = int(plan.tasks.shape[0])
+    ws = torch.empty(int(L.hy3attn_workspace_bytes(n_tasks)) + 256, dtype=torch.uint8, device=dev)
+    starts = np.zeros(len(kv_len) + 1, dtype=np.int32)
+    starts[1:] = np.cumsum(kv_len)
+    kv_start = torch.from_numpy(starts).to(dev)
+    tasks = torch.from_numpy(plan.tasks.reshape(-1)).to(dev)
+    wb = torch.from_numpy(plan.worker_begin).to(dev)
+    rb = torch.from_numpy(plan.row_begin).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        rc = L.hy3attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_start.data_ptr(),
+                              len(kv_len), hkv, plan.tile, tasks.data_ptr(), n_tasks,
+                              wb.data_ptr(), plan.n_workers, rb.data_ptr(), ws.data_ptr(),
+                              ws.numel(), out.data_ptr(), stream.cuda_stream)
+        assert rc == 0, rc
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ev_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    tot = int(sum(kv_len))
+    kv_bytes = 2 * hkv * tot * d * 2                       # K and V, bf16
+    qo_bytes = 2 * len(kv_len) * 8 * hkv * d * 2            # q and out
+    alg = kv_bytes + qo_bytes
+    log(f"[bench] {args.workload}: {len(kv_len)} requests, {tot} tokens, {n_tasks} tasks; "
+        f"{ms:.4f} ms/call (events {ev_ms:.4f})")
+    if args.calib_copy_mib:   # a plain copy of known size for the counter runs
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle.attention import attention_decode
+        nb = min(len(kv_len), 4)
+        qf = bits_to_f64(qb[:nb])
+        nt = int(sum(kv_len[:nb]))
+        kf, vf = bits_to_f64(kb[:, :nt]), bits_to_f64(vb[:, :nt])
+        t1 = time.perf_counter()
+        attention_decode(qf, kf, vf, kv_len[:nb], 1.0 / np.sqrt(d))
+        dt = time.perf_counter() - t1
+        cpu = {"value": nt / dt, "unit": "KV tokens/s", "cores": torch.get_num_threads(),
+               "kind": "oracle",
+               "sample": f"first {nb} requests ({nt} cached tokens, 64 query heads), float64 numpy, once"}
+    return {
+        "metric": "Hy3 GQA split-KV decode attention: cached KV tokens/s (% HBM BW)",
+        "value": tot / (ms / 1e3), "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) q, K, V)",
+        "config": {"workload": args.workload, "requests": len(kv_len), "kv_tokens": tot,
+                   "q_heads": 64, "kv_heads": hkv, "head_dim": d, "tile": plan.tile,
+                   "workers": plan.n_workers, "tasks": n_tasks,
+                   "lengths": ATTN_WORKLOADS[args.workload]},
+        "roofline": {"kernel": "attn_split_kernel + attn_combine_kernel", "bound": "hbm",
+                     "achieved": alg / (ev_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": alg / (ev_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": measured_traffic(args.workload, "attn"),
+                     "per_unit": f"{2 * d * 2} B of K+V per cached token and KV head "
+                                 f"x {tot} tokens x {hkv} heads + q and out",
+                     "avg_launch_ms": ev_ms},
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(ATTN_WORKLOADS),
+                    default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens in the CPU oracle sample (default: 16 decode, 48 otherwise)")
@@ -109,6 +213,9 @@ def main():
     sm.load()
     if args.router_sweep:
         print(json.dumps(router_sweep(args, dev)), flush=True)
+        return
+    if args.workload in ATTN_WORKLOADS:
+        print(json.dumps(attention_bench(args, dev)), flush=True)
         return
     inp = MoEInputs(CONFIGS[WORKLOADS[args.workload]])
     c = inp.cfg

@@ -71,7 +71,7 @@ int hy3attn_plan(const int32_t *kv_len, int B, int n_kv_heads, int tile, int n_w
  *   workspace  hy3attn_workspace_bytes(n_tasks) bytes, 256-byte aligned
  *   out        bf16 [B][Hq][128]
  * The scale is 1/sqrt(128).  Two kernels: one workgroup per worker, then
- * one per (request, KV head) row for the combine.  Returns HY3ATTN_OK,
+ * one per (request, KV head, query head) for the combine.  Returns HY3ATTN_OK,
  * HY3ATTN_ERR_INVALID or HY3ATTN_ERR_HIP. */
 int hy3attn_decode(const void *q, const void *k, const void *v, const int32_t *kv_start, int B,
                    int n_kv_heads, int tile, const int32_t *tasks, int64_t n_tasks,

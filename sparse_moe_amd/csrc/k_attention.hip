@@ -5,7 +5,8 @@
 // workgroup per worker taking its tasks from the map, and a combine.
 //
 // HBM-bound: every cached key and value byte is read once.  A workgroup
-// (4 wavefronts) walks a task's tokens in chunks of 64; lane (row r, chunk c)
+// (4 wavefronts) walks a task's tokens in chunks of 32, the next chunk's
+// loads in flight while one is multiplied; lane (row r, chunk c)
 // of a wavefront holds head-dims 8c .. 8c+7 of token 4 i + r of its step i,
 // so one 16-byte load per lane covers 4 whole 256-byte key rows (1 KB
 // contiguous).  The 8 query heads' scores of a token are summed over the 16
@@ -29,8 +30,8 @@ namespace {
 
 constexpr int D = HY3ATTN_HEAD_DIM;   // 128
 constexpr int G = HY3ATTN_GROUP;      // 8 query heads per KV head
-constexpr int STEPS = 4;              // token steps per block (4 tokens per wavefront step)
-constexpr int CHUNK = 4 * 4 * STEPS;  // tokens per workgroup block: 4 waves x 4 rows x STEPS
+constexpr int STEPS = 2;              // token steps per chunk (4 tokens per wavefront step)
+constexpr int CHUNK = 4 * 4 * STEPS;  // tokens per workgroup chunk: 4 waves x 4 rows x STEPS
 
 struct Partial {
   float *o;    // [n_tasks][G][D] unnormalised output
@@ -116,20 +117,22 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(
     }
     const uint16_t *kh = k + (size_t)h * total * D + 8 * c;
     const uint16_t *vh = v + (size_t)h * total * D + 8 * c;
-    for (int cb = s; cb < e; cb += CHUNK) {
-      uint4 ku[STEPS], vu[STEPS];
-      bool ok[STEPS];
+    // Two register sets: the next chunk's keys and values are in flight while
+    // the current chunk is multiplied.  Tokens past e re-read token e - 1
+    // (in bounds) and are masked.
+    auto load = [&](uint4 (&ku)[STEPS], uint4 (&vu)[STEPS], int cb) {
 #pragma unroll
-      for (int i = 0; i < STEPS; ++i) {   // token of step i: wave 16 STEPS-block, 4 i + row
-        const int tok = cb + wave * 4 * STEPS + 4 * i + row;
-        ok[i] = tok < e;
-        const int tc = ok[i] ? tok : e - 1;               // in bounds; masked below
-        ku[i] = *reinterpret_cast<const uint4 *>(kh + (size_t)tc * D);
-        vu[i] = *reinterpret_cast<const uint4 *>(vh + (size_t)tc * D);
+      for (int i = 0; i < STEPS; ++i) {
+        const int tok = min(cb + wave * 4 * STEPS + 4 * i + row, e - 1);
+        ku[i] = *reinterpret_cast<const uint4 *>(kh + (size_t)tok * D);
+        vu[i] = *reinterpret_cast<const uint4 *>(vh + (size_t)tok * D);
       }
+    };
+    auto compute = [&](const uint4 (&ku)[STEPS], const uint4 (&vu)[STEPS], int cb) {
       float sc[STEPS][G];
 #pragma unroll
       for (int i = 0; i < STEPS; ++i) {
+        const bool ok = cb + wave * 4 * STEPS + 4 * i + row < e;
         float kf[8];
         bf16x8_to_f32(ku[i], kf);
 #pragma unroll
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc = fmaf(qv[g][j], kf[j], acc);
           acc = row16_sum(acc);
-          sc[i][g] = ok[i] ? acc : -INFINITY;
+          sc[i][g] = ok ? acc : -INFINITY;
         }
       }
 #pragma unroll
@@ -166,6 +169,15 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(
         }
         m[g] = mn;
       }
+    };
+    uint4 kA[STEPS], vA[STEPS], kB[STEPS], vB[STEPS];
+    load(kA, vA, s);
+    for (int cb = s; cb < e; cb += 2 * CHUNK) {
+      load(kB, vB, cb + CHUNK);
+      compute(kA, vA, cb);
+      if (cb + CHUNK >= e) break;
+      load(kA, vA, cb + 2 * CHUNK);
+      compute(kB, vB, cb + CHUNK);
     }
     // merge the 4 row streams of the wavefront (lanes c, 16 + c, 32 + c, 48 + c)
 #pragma unroll
@@ -215,28 +227,48 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(
   }
 }
 
-// One workgroup per (request, KV head) row: merge the row's splits.
+// One workgroup per (request, KV head) row and query head g: merge the row's
+// splits.  Thread (split lane sp of 8, dims 4 d4 .. 4 d4 + 3) takes splits
+// sp, sp + 8, ...; the maxima and the partial sums meet in LDS.
 __global__ __launch_bounds__(256) void attn_combine_kernel(const int32_t *__restrict__ row_begin,
                                                            Partial part, int Hkv,
                                                            uint16_t *__restrict__ out) {
-  const int r = blockIdx.x, b = r / Hkv, h = r - b * Hkv;
-  const int g = threadIdx.x >> 5, d4 = threadIdx.x & 31;
+  __shared__ float red[8][33][4];   // per split lane: 32 dim quads + the denominator
+  __shared__ float mx[8];
+  const int r = blockIdx.x / G, g = blockIdx.x - r * G, b = r / Hkv, h = r - b * Hkv;
+  const int sp = threadIdx.x >> 5, d4 = threadIdx.x & 31;
   const int t0 = row_begin[r], t1 = row_begin[r + 1];
   float M = -INFINITY;
-  for (int t = t0; t < t1; ++t) M = fmaxf(M, part.ml[(size_t)t * 2 * G + g]);
+  for (int t = t0 + sp; t < t1; t += 8) M = fmaxf(M, part.ml[(size_t)t * 2 * G + g]);
+  if (d4 == 0) mx[sp] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) M = fmaxf(M, mx[i]);
   float den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int t = t0; t < t1; ++t) {
+  for (int t = t0 + sp; t < t1; t += 8) {
     const float a = M == -INFINITY ? 0.f : exp2_or_zero(part.ml[(size_t)t * 2 * G + g] - M);
     den += part.ml[(size_t)t * 2 * G + G + g] * a;
     const float4 o = *reinterpret_cast<const float4 *>(part.o + ((size_t)t * G + g) * D + 4 * d4);
     num[0] += o.x * a; num[1] += o.y * a; num[2] += o.z * a; num[3] += o.w * a;
   }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[sp][d4][j] = num[j];
+  if (d4 == 0) red[sp][32][0] = den;
+  __syncthreads();
+  if (sp != 0) return;
+  float tot_den = 0.f, tot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {   // in split-lane order: the same sums every call
+    tot_den += red[i][32][0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tot[j] += red[i][d4][j];
+  }
   uint16_t res[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float x = den > 0.f ? num[j] / den : 0.f;   // no tokens: zeros
+    const float x = tot_den > 0.f ? tot[j] / tot_den : 0.f;   // no tokens: zeros
     uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);                   // round to nearest even
+    u += 0x7FFFu + ((u >> 16) & 1u);                           // round to nearest even
     res[j] = (uint16_t)(u >> 16);
   }
   uint16_t *dst = out + ((size_t)b * (G * Hkv) + G * h + g) * D + 4 * d4;
@@ -325,7 +357,7 @@ extern "C" int hy3attn_decode(const void *q, const void *k, const void *v, const
                        static_cast<const uint16_t *>(v), kv_start, B, n_kv_heads, tile, tasks,
                        worker_begin, part);
   if (hipGetLastError() != hipSuccess) return HY3ATTN_ERR_HIP;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)B * n_kv_heads)), dim3(256), 0,
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)B * n_kv_heads * G)), dim3(256), 0,
                      s, row_begin, part, n_kv_heads, static_cast<uint16_t *>(out));
   return hipGetLastError() == hipSuccess ? HY3ATTN_OK : HY3ATTN_ERR_HIP;
 }
