@@ -46,10 +46,17 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha():
+ATTN_SOURCES = ("k_attention.hip",)   # the split-KV attention path; the rest is the MoE layer's
+
+
+def kernel_sources_sha(kind: str = "moe"):
+    """Hash of the kernel sources a measurement depends on: the MoE layer's
+    (every source but the attention path's) or the attention path's."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_moe_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if (name in ATTN_SOURCES) != (kind == "attn"):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -63,7 +70,8 @@ def measured_traffic(workload, kernel):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("kernel_sources_sha") != kernel_sources_sha():
+    kind = "attn" if workload.startswith("attn") else "moe"
+    if d.get("kernel_sources_sha") != kernel_sources_sha(kind):
         return None
     return d.get("bytes_per_launch")
 
