@@ -70,6 +70,10 @@ int hy3attn_plan(const int32_t *kv_len, int B, int n_kv_heads, int tile, int n_w
  *              with the same tile and n_workers
  *   workspace  hy3attn_workspace_bytes(n_tasks) bytes, 256-byte aligned
  *   out        bf16 [B][Hq][128]
+ * q, k and v must be 16-byte aligned and out 8-byte aligned (else
+ * HY3ATTN_ERR_INVALID).  A task whose tiles lie past its request's length
+ * (a plan made for other lengths) contributes nothing; rows then hold the
+ * attention over the tokens their tasks do cover.
  * The scale is 1/sqrt(128).  Two kernels: one workgroup per worker, then
  * one per (request, KV head, query head) for the combine.  Returns HY3ATTN_OK,
  * HY3ATTN_ERR_INVALID or HY3ATTN_ERR_HIP. */

@@ -97,7 +97,17 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(
     const int t1 = __builtin_amdgcn_readfirstlane(tasks[4 * t + 3]);
     const int base = kv_start[b], L = kv_start[b + 1] - base;
     const int s = base + t0 * tile;                       // first token of the split
-    const int e = base + min(t1 * tile, L);               // end (> s: a task holds a token)
+    const int e = base + min(t1 * tile, L);               // end (> s for a plan of these lengths)
+    if (e <= s) {   // a plan made for other lengths: an empty split, no loads
+      const int g = tid >> 5, d4 = tid & 31;
+      *reinterpret_cast<float4 *>(part.o + ((size_t)t * G + g) * D + 4 * d4) =
+          make_float4(0.f, 0.f, 0.f, 0.f);
+      if (d4 == 0) {
+        part.ml[(size_t)t * 2 * G + g] = -INFINITY;
+        part.ml[(size_t)t * 2 * G + G + g] = 0.f;
+      }
+      continue;
+    }
     // the lane's 8 dims of the 8 query heads, in log2 units
     float qv[G][8];
 #pragma unroll
@@ -345,6 +355,10 @@ extern "C" int hy3attn_decode(const void *q, const void *k, const void *v, const
       (n_tasks > 0 && !workspace))
     return HY3ATTN_ERR_INVALID;
   if (ws_bytes < hy3attn_workspace_bytes(n_tasks) || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return HY3ATTN_ERR_INVALID;
+  // 16-byte vector loads of q, k and v rows, 8-byte stores of out
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+       reinterpret_cast<uintptr_t>(v)) & 15 || (reinterpret_cast<uintptr_t>(out) & 7))
     return HY3ATTN_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Partial part;

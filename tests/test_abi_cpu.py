@@ -309,3 +309,25 @@ def test_attention_plan_rejects_bad_arguments(lib):
     big = np.array([100000], dtype=np.int32)
     assert L.hy3attn_plan(big.ctypes.data, 1, 8, 256, 4, buf.ctypes.data, 2, buf.ctypes.data,
                           buf.ctypes.data, ctypes.byref(nt)) == -2
+
+
+def test_attention_decode_rejects_misaligned_or_missing_pointers(lib):
+    """Validation happens on the host before any launch (no GPU touched)."""
+    L = lib
+    ok = 1 << 20   # aligned stand-in addresses: rejected before use
+    args = dict(q=ok, k=ok, v=ok, kv=ok, B=1, hkv=8, tile=256, tasks=ok, nt=1, wb=ok, nw=4,
+                rb=ok, ws=ok, wsb=1 << 20, out=ok)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.hy3attn_decode(a["q"], a["k"], a["v"], a["kv"], a["B"], a["hkv"], a["tile"],
+                                a["tasks"], a["nt"], a["wb"], a["nw"], a["rb"], a["ws"], a["wsb"],
+                                a["out"], None)
+    assert call(q=ok + 8) == -1          # q not 16-byte aligned
+    assert call(k=ok + 4) == -1
+    assert call(out=ok + 2) == -1        # out not 8-byte aligned
+    assert call(ws=ok + 128) == -1       # workspace not 256-byte aligned
+    assert call(wsb=16) == -1            # workspace too small
+    assert call(q=None) == -1
+    assert call(hkv=0) == -1
+    assert call(B=0) == 0                # nothing to do

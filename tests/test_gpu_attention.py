@@ -84,3 +84,16 @@ def test_deterministic_bitwise(dev):
     a, _ = run(4, kv_len, 8, 256, 512, dev)
     b, _ = run(4, kv_len, 8, 256, 512, dev)
     np.testing.assert_array_equal(a, b)
+
+
+def test_plan_for_longer_lengths_covers_the_cached_tokens(dev):
+    """A plan made for lengths [1000, 500] run on caches of [300, 500]
+    tokens: tasks past request 0's 300 tokens are empty splits (no loads),
+    and the outputs are the attention over the cached tokens."""
+    kv_len = [300, 500]
+    qb, kb, vb = attention_inputs(6, kv_len, 8)
+    plan = sm.attn_plan([1000, 500], 8, 256, 9)
+    out = sm.attn_decode(bf16(qb, dev), bf16(kb, dev), bf16(vb, dev), kv_len, plan)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    check(got, (qb, kb, vb), kv_len, "plan for longer lengths")
