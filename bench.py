@@ -115,8 +115,9 @@ def attention_bench(args, dev):
     def call():
         rc = L.hy3attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_start.data_ptr(),
                               len(kv_len), hkv, plan.tile, tasks.data_ptr(), n_tasks,
-                              wb.data_ptr(), plan.n_workers, rb.data_ptr(), ws.data_ptr(),
-                              ws.numel(), out.data_ptr(), stream.cuda_stream)
+                              wb.data_ptr(), plan.n_workers, rb.data_ptr(),
+                              plan.row_begin.size - 1, ws.data_ptr(), ws.numel(),
+                              out.data_ptr(), stream.cuda_stream)
         assert rc == 0, rc
 
     for _ in range(args.warmup):

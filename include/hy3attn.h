@@ -68,19 +68,24 @@ int hy3attn_plan(const int32_t *kv_len, int B, int n_kv_heads, int tile, int n_w
  *   kv_start   int32 [B+1], kv_start[0] = 0, non-decreasing, total = kv_start[B]
  *   tasks, worker_begin, row_begin: the plan, copied to device memory, made
  *              with the same tile and n_workers
+ *   n_rows     rows of the plan (its row_begin holds n_rows + 1 entries); must
+ *              equal B * n_kv_heads, else HY3ATTN_ERR_INVALID
  *   workspace  hy3attn_workspace_bytes(n_tasks) bytes, 256-byte aligned
  *   out        bf16 [B][Hq][128]
  * q, k and v must be 16-byte aligned and out 8-byte aligned (else
  * HY3ATTN_ERR_INVALID).  A task whose tiles lie past its request's length
  * (a plan made for other lengths) contributes nothing; rows then hold the
- * attention over the tokens their tasks do cover.
+ * attention over the tokens their tasks do cover.  The kernels bound every
+ * plan entry before using it: task ranges are clamped to [0, n_tasks), and
+ * a task whose request or KV head lies outside [0, B) x [0, n_kv_heads), or
+ * whose tile range is empty or negative, is an empty split.
  * The scale is 1/sqrt(128).  Two kernels: one workgroup per worker, then
  * one per (request, KV head, query head) for the combine.  Returns HY3ATTN_OK,
  * HY3ATTN_ERR_INVALID or HY3ATTN_ERR_HIP. */
 int hy3attn_decode(const void *q, const void *k, const void *v, const int32_t *kv_start, int B,
                    int n_kv_heads, int tile, const int32_t *tasks, int64_t n_tasks,
                    const int32_t *worker_begin, int n_workers, const int32_t *row_begin,
-                   void *workspace, size_t ws_bytes, void *out, void *stream);
+                   int64_t n_rows, void *workspace, size_t ws_bytes, void *out, void *stream);
 
 #ifdef __cplusplus
 }

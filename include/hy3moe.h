@@ -103,7 +103,8 @@ extern "C" {
  * activations, the FP8 path of the CANN deployment article (section 六: an
  * FP8 Linear quantises its input with a static per-tensor input scale;
  * section 8.2: W8A8).  The experts' input x is quantised once with the
- * layer's scale x_scale and each group's h with its own scale h_scale[g]:
+ * layer's scale x_scale and each group's h (the SwiGLU output rounded to
+ * bf16, the layer's activation tensor) with its own scale h_scale[g]:
  * code = E4M3(v / scale), the quotient a correctly rounded float32 division,
  * clamped to +-448 (saturating), rounded to nearest even.  The GEMMs then
  * run on scale * value of both operands (FP8 MFMAs on the large-tile path,

@@ -75,10 +75,14 @@ path of section 六, where an FP8 Linear quantises its input with a static
 per-tensor input scale).  The expert input x is quantised with one float32
 scale a1 of the layer, and each expert's h (the down projection's input)
 with that expert's float32 scale a2[e] (a2[E]: shared expert): code =
-E4M3(v / a), saturating, round to nearest even, decided in float32 (h is
-rounded from float64 to float32 first); the GEMMs then run on scale times
-value.  Granularity, saturation, rounding and the precision of the decision
-are readings: the pages name only "static per-tensor".
+E4M3(v / a), saturating, round to nearest even, decided in float32; the
+GEMMs then run on scale times value.  What the FP8 Linear receives is the
+layer's activation tensor in the model's dtype: x is bfloat16 already, and
+h is the SwiGLU output rounded to bfloat16 (round_bf16) before it is
+quantised, exactly as for the dynamic MXFP8 quantiser below, so both
+activation quantisers see the same tensor.  Granularity, saturation,
+rounding and the precision of the decision are readings: the pages name
+only "static per-tensor".
 
 Parity pins: every public function is pinned by a test in
 ``tests/test_oracle_pins.py`` (hand-derived golden values, brute force over
@@ -181,19 +185,33 @@ def route_from_logits(logits: np.ndarray, K: int, mode: int = ROUTE_SIGMOID_BIAS
     else:
         raise ValueError("unknown route mode")
     idx = topk_desc(sel, K)
-    rows = np.arange(T)[:, None]
-    picked = prob[rows, idx]
-    tot = picked.sum(axis=1, keepdims=True)
-    if mode == ROUTE_SIGMOID_BIAS:
-        weight = scale * (picked / tot)
-    else:
-        weight = picked / np.maximum(tot, renorm_eps)
+    weight = combine_weights(prob, idx, mode, scale, renorm_eps)
     if K < E:
         ssorted = -np.sort(-sel, axis=1)
         margin = ssorted[:, K - 1] - ssorted[:, K]
     else:
         margin = np.full(T, np.inf)
     return Route(idx=idx, weight=weight, margin=margin, select_score=sel, prob=prob)
+
+
+def combine_weights(prob: np.ndarray, idx: np.ndarray, mode: int = ROUTE_SIGMOID_BIAS,
+                    scale: float = 2.826, renorm_eps: float = 1e-8) -> np.ndarray:
+    """Combine weights of the picks ``idx`` [T, K] from the unbiased scores.
+
+    Sigmoid mode (hy3 README, MoE routing row; HYV3Config route_norm and
+    router_scaling_factor): the picked sigmoid scores renormalised to sum 1,
+    times ``scale``.  Softmax mode (HunyuanImage 3.0 MoE reading, easy_topk):
+    the picked probabilities divided by their sum clamped below at
+    ``renorm_eps``.  The selection bias never enters: ``prob`` holds the
+    unbiased scores.
+    """
+    prob = np.asarray(prob, dtype=np.float64)
+    idx = np.asarray(idx, dtype=np.int64)
+    picked = np.take_along_axis(prob, idx, axis=1)
+    tot = picked.sum(axis=1, keepdims=True)
+    if mode == ROUTE_SIGMOID_BIAS:
+        return scale * (picked / tot)
+    return picked / np.maximum(tot, renorm_eps)
 
 
 def route(x, w_router, K: int, mode: int = ROUTE_SIGMOID_BIAS, bias=None,
@@ -368,18 +386,18 @@ def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
     (HunyuanImage 3.0 MoE reading, stacked gate/up and down weights).
 
     With ``a2`` (static FP8 activations, W8A8), the down projection's input
-    h is first quantised to E4M3 with the static scale a2 and dequantised
+    h, as the layer's bfloat16 activation tensor (``round_bf16``), is
+    quantised to E4M3 with the static scale a2 and dequantised
     (``quant_dequant_e4m3``), as an FP8 Linear quantises its input.  With
-    ``amx`` (dynamic MXFP8 activations, W4A8) h, as the layer's bfloat16
-    activation tensor (``round_bf16``), is quantised per block of 32 along I
-    instead (``quant_dequant_mxfp8``).
+    ``amx`` (dynamic MXFP8 activations, W4A8) the same bfloat16 h is
+    quantised per block of 32 along I instead (``quant_dequant_mxfp8``).
     """
     a = np.asarray(a, dtype=np.float64)
     g = a @ np.asarray(w_gate, dtype=np.float64).T
     u = a @ np.asarray(w_up, dtype=np.float64).T
     h = silu(g) * u
     if a2 is not None:
-        h = quant_dequant_e4m3(h, a2)
+        h = quant_dequant_e4m3(round_bf16(h), a2)
     if amx:
         h = quant_dequant_mxfp8(round_bf16(h))
     return h @ np.asarray(w_down, dtype=np.float64).T
@@ -441,6 +459,43 @@ def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
         expert_out[mask] = swiglu_expert(x_rep[mask], wg, wu, wd, a2=a2[e], amx=amx)
     routed = (expert_out.reshape(T, K, H) * weight[:, :, None]).sum(axis=1)
     return out_shared + routed
+
+
+def forward_by_expert(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
+                      experts: ExpertFn, E: int,
+                      shared: Optional[Sequence[np.ndarray]] = None,
+                      a8: Optional[Tuple[float, Sequence[float]]] = None,
+                      amx: bool = False) -> np.ndarray:
+    """The same sum as ``forward_given_route``, gathered expert by expert.
+
+    out[t] = shared(x_t) + sum_e sum_{j: idx[t, j] = e} weight[t, j] f_e(x_t).
+    Each routed expert is requested once, evaluated on the tokens routed to
+    it and its weighted rows added into the output, so no [T*K, H] copy of x
+    is built and only one expert's weights need to be held at a time: the
+    form used to check layers with tens of thousands of tokens.  Only the
+    order of the float64 additions differs from the eager path.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(idx)
+    weight = np.asarray(weight, dtype=np.float64)
+    T, H = x.shape
+    a2 = [None] * (E + 1)
+    if a8 is not None:
+        x = quant_dequant_e4m3(x, a8[0])
+        a2 = [float(v) for v in a8[1]]
+    if amx:
+        x = quant_dequant_mxfp8(x)
+    out = np.zeros((T, H))
+    if shared is not None:
+        out += swiglu_expert(x, *shared, a2=a2[E], amx=amx)
+    if T == 0 or idx.size == 0:
+        return out
+    for e in np.unique(idx):
+        tok, slot = np.nonzero(idx == e)
+        wg, wu, wd = experts(int(e))
+        y = swiglu_expert(x[tok], wg, wu, wd, a2=a2[int(e)], amx=amx)
+        np.add.at(out, tok, weight[tok, slot][:, None] * y)
+    return out
 
 
 def forward(x, w_router, experts: ExpertFn, E: int, K: int,

@@ -137,8 +137,8 @@ def load() -> ctypes.CDLL:
     L.hy3attn_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
-                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                 ctypes.c_void_p, ctypes.c_void_p]
+                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     if L.hy3moe_abi_version() != ABI_VERSION:
         raise RuntimeError("libhy3moe ABI version mismatch")
     _LIB = L
@@ -302,9 +302,10 @@ ATTN_TILE = 256
 class AttnPlan:
     """Task map from hy3attn_plan (host numpy arrays)."""
 
-    def __init__(self, tasks, worker_begin, row_begin, n_workers, tile):
+    def __init__(self, tasks, worker_begin, row_begin, n_workers, tile, B=None, n_kv_heads=None):
         self.tasks, self.worker_begin, self.row_begin = tasks, worker_begin, row_begin
         self.n_workers, self.tile = n_workers, tile
+        self.B, self.n_kv_heads = B, n_kv_heads
 
 
 def attn_plan(kv_len, n_kv_heads: int, tile: int = ATTN_TILE, n_workers: int = 512) -> AttnPlan:
@@ -322,7 +323,7 @@ def attn_plan(kv_len, n_kv_heads: int, tile: int = ATTN_TILE, n_workers: int = 5
                         ctypes.byref(nt))
     if rc != 0:
         raise RuntimeError(f"hy3attn_plan failed ({rc})")
-    return AttnPlan(tasks[:nt.value].copy(), wb, rb, n_workers, tile)
+    return AttnPlan(tasks[:nt.value].copy(), wb, rb, n_workers, tile, B, n_kv_heads)
 
 
 def attn_decode(q, k, v, kv_len, plan: AttnPlan, out=None, workspace=None):
@@ -335,6 +336,15 @@ def attn_decode(q, k, v, kv_len, plan: AttnPlan, out=None, workspace=None):
     dev = q.device
     B, Hq, _ = q.shape
     Hkv = k.shape[0]
+    if Hq != 8 * Hkv or q.shape[2] != 128 or k.shape != v.shape or k.shape[2] != 128:
+        raise ValueError("q must be [B][8*Hkv][128] and k, v [Hkv][tokens][128]")
+    if len(kv_len) != B or plan.row_begin.size != B * Hkv + 1:
+        raise ValueError("the plan was made for another batch or KV head count")
+    if plan.tasks.size and (int(plan.tasks[:, 0].max()) >= B or int(plan.tasks[:, 1].max()) >= Hkv
+                            or int(plan.tasks.min()) < 0):
+        raise ValueError("the plan holds tasks outside this batch")
+    if plan.worker_begin.size != plan.n_workers + 1:
+        raise ValueError("worker_begin must hold n_workers + 1 entries")
     starts = np.zeros(B + 1, dtype=np.int32)
     starts[1:] = np.cumsum(np.asarray(kv_len, dtype=np.int64))
     kv_start = torch.from_numpy(starts).to(dev)
@@ -351,8 +361,8 @@ def attn_decode(q, k, v, kv_len, plan: AttnPlan, out=None, workspace=None):
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = L.hy3attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_start.data_ptr(), B, Hkv,
                           plan.tile, tasks.data_ptr(), n_tasks, wb.data_ptr(), plan.n_workers,
-                          rb.data_ptr(), workspace.data_ptr(), workspace.numel(), out.data_ptr(),
-                          stream)
+                          rb.data_ptr(), plan.row_begin.size - 1, workspace.data_ptr(),
+                          workspace.numel(), out.data_ptr(), stream)
     if rc != 0:
         raise RuntimeError(f"hy3attn_decode failed ({rc})")
     return out

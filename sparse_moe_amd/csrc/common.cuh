@@ -109,9 +109,8 @@ __device__ __forceinline__ uint32_t quant_e4m3x4(float a, float b, float c, floa
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
-// The same with the quotient taken as v * r, r = 1 / s computed once (within
-// a float32 ulp of v / s): the GEMM epilogues quantise h this way, where h
-// itself carries the accumulation's float32 rounding.
+// The same with the quotient taken as v * r for a reciprocal r given by the
+// caller: exact when r is a power of two (the MXFP8 block scales below).
 __device__ __forceinline__ uint32_t quant_e4m3x4_rcp(float a, float b, float c, float d,
                                                      float r) {
   const float lim = 448.0f;
@@ -122,6 +121,19 @@ __device__ __forceinline__ uint32_t quant_e4m3x4_rcp(float a, float b, float c, 
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
+}
+// v rounded to bfloat16 (nearest even) and back: the value an activation
+// takes as the layer's bf16 tensor (finite inputs).
+__device__ __forceinline__ float round_bf16(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return __uint_as_float(u & 0xFFFF0000u);
+}
+// Static FP8 quantisation of the layer's bf16 h: E4M3 codes of round_bf16(v)
+// / s, four values (the SwiGLU outputs of a GEMM epilogue) at a time.
+__device__ __forceinline__ uint32_t quant_e4m3x4_bf16(float a, float b, float c, float d,
+                                                      float s) {
+  return quant_e4m3x4(round_bf16(a), round_bf16(b), round_bf16(c), round_bf16(d), s);
 }
 // Dynamic MXFP8 (OCP microscaling conversion) of a block of 32 consecutive
 // values held by four adjacent lanes, 8 each: the lanes exchange their

@@ -80,8 +80,8 @@ __device__ __forceinline__ void merge(float &m, float &l, float (&o)[8], float m
 __global__ __launch_bounds__(256, 2) void attn_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ kv_start, int B, int Hkv,
-    int tile, const int32_t *__restrict__ tasks, const int32_t *__restrict__ worker_begin,
-    Partial part) {
+    int tile, const int32_t *__restrict__ tasks, int n_tasks,
+    const int32_t *__restrict__ worker_begin, Partial part) {
   __shared__ float mls[4][2][G];       // per wavefront: m, l of the 8 heads
   __shared__ float os[4][G][D];        // per wavefront: unnormalised output
   const int tid = threadIdx.x, lane = tid & 63;
@@ -89,16 +89,22 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(
   const int row = lane >> 4, c = lane & 15;          // token row of a step, dim chunk
   const int total = kv_start[B];
   const float qscale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
-  const int t_end = worker_begin[blockIdx.x + 1];
-  for (int t = worker_begin[blockIdx.x]; t < t_end; ++t) {
+  // a worker's task range, clamped to the plan's tasks
+  const int t_beg = max(worker_begin[blockIdx.x], 0);
+  const int t_end = min(worker_begin[blockIdx.x + 1], n_tasks);
+  for (int t = t_beg; t < t_end; ++t) {
     const int b = __builtin_amdgcn_readfirstlane(tasks[4 * t]);
     const int h = __builtin_amdgcn_readfirstlane(tasks[4 * t + 1]);
     const int t0 = __builtin_amdgcn_readfirstlane(tasks[4 * t + 2]);
     const int t1 = __builtin_amdgcn_readfirstlane(tasks[4 * t + 3]);
-    const int base = kv_start[b], L = kv_start[b + 1] - base;
-    const int s = base + t0 * tile;                       // first token of the split
-    const int e = base + min(t1 * tile, L);               // end (> s for a plan of these lengths)
-    if (e <= s) {   // a plan made for other lengths: an empty split, no loads
+    // a task naming a request or KV head outside this call, or no tiles, is
+    // an empty split: kv_start is read only for a request of this call
+    const bool valid = b >= 0 && b < B && h >= 0 && h < Hkv && t0 >= 0 && t1 > t0;
+    const int base = valid ? kv_start[b] : 0, L = valid ? kv_start[b + 1] - base : 0;
+    const int64_t s64 = (int64_t)t0 * tile, e64 = min((int64_t)t1 * tile, (int64_t)L);
+    const int s = base + (int)min(s64, (int64_t)L);       // first token of the split
+    const int e = base + (int)e64;                        // end (> s for a plan of these lengths)
+    if (!valid || e <= s) {   // a plan made for other lengths: an empty split, no loads
       const int g = tid >> 5, d4 = tid & 31;
       *reinterpret_cast<float4 *>(part.o + ((size_t)t * G + g) * D + 4 * d4) =
           make_float4(0.f, 0.f, 0.f, 0.f);
@@ -241,13 +247,14 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(
 // splits.  Thread (split lane sp of 8, dims 4 d4 .. 4 d4 + 3) takes splits
 // sp, sp + 8, ...; the maxima and the partial sums meet in LDS.
 __global__ __launch_bounds__(256) void attn_combine_kernel(const int32_t *__restrict__ row_begin,
-                                                           Partial part, int Hkv,
+                                                           int n_tasks, Partial part, int Hkv,
                                                            uint16_t *__restrict__ out) {
   __shared__ float red[8][33][4];   // per split lane: 32 dim quads + the denominator
   __shared__ float mx[8];
   const int r = blockIdx.x / G, g = blockIdx.x - r * G, b = r / Hkv, h = r - b * Hkv;
   const int sp = threadIdx.x >> 5, d4 = threadIdx.x & 31;
-  const int t0 = row_begin[r], t1 = row_begin[r + 1];
+  // the row's task range, clamped to the plan's tasks
+  const int t0 = max(row_begin[r], 0), t1 = min(row_begin[r + 1], n_tasks);
   float M = -INFINITY;
   for (int t = t0 + sp; t < t1; t += 8) M = fmaxf(M, part.ml[(size_t)t * 2 * G + g]);
   if (d4 == 0) mx[sp] = M;
@@ -347,9 +354,13 @@ extern "C" int hy3attn_plan(const int32_t *kv_len, int B, int n_kv_heads, int ti
 extern "C" int hy3attn_decode(const void *q, const void *k, const void *v, const int32_t *kv_start,
                               int B, int n_kv_heads, int tile, const int32_t *tasks,
                               int64_t n_tasks, const int32_t *worker_begin, int n_workers,
-                              const int32_t *row_begin, void *workspace, size_t ws_bytes,
-                              void *out, void *stream) {
-  if (B < 0 || n_kv_heads < 1 || tile < 1 || n_workers < 1 || n_tasks < 0) return HY3ATTN_ERR_INVALID;
+                              const int32_t *row_begin, int64_t n_rows, void *workspace,
+                              size_t ws_bytes, void *out, void *stream) {
+  if (B < 0 || n_kv_heads < 1 || tile < 1 || n_workers < 1 || n_tasks < 0 ||
+      n_tasks > INT32_MAX)
+    return HY3ATTN_ERR_INVALID;
+  // the plan must have been made for this call's rows (request, KV head)
+  if (n_rows != (int64_t)B * n_kv_heads) return HY3ATTN_ERR_INVALID;
   if (B == 0) return HY3ATTN_OK;
   if (!q || !k || !v || !kv_start || !tasks || !worker_begin || !row_begin || !out ||
       (n_tasks > 0 && !workspace))
@@ -369,9 +380,9 @@ extern "C" int hy3attn_decode(const void *q, const void *k, const void *v, const
     hipLaunchKernelGGL(attn_split_kernel, dim3(n_workers), dim3(256), 0, s,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), kv_start, B, n_kv_heads, tile, tasks,
-                       worker_begin, part);
+                       (int)n_tasks, worker_begin, part);
   if (hipGetLastError() != hipSuccess) return HY3ATTN_ERR_HIP;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)B * n_kv_heads * G)), dim3(256), 0,
-                     s, row_begin, part, n_kv_heads, static_cast<uint16_t *>(out));
+                     s, row_begin, (int)n_tasks, part, n_kv_heads, static_cast<uint16_t *>(out));
   return hipGetLastError() == hipSuccess ? HY3ATTN_OK : HY3ATTN_ERR_HIP;
 }

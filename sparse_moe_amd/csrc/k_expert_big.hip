@@ -174,13 +174,13 @@ __device__ __forceinline__ void big_tile_loads(const ExpertArgs &a, const BigTil
   }
 }
 
-// A8 gate-up epilogue: h = SwiGLU of the scaled accumulators, quantised with
-// the group's static scale (rhs = its reciprocal); 128 E4M3 bytes per token
-// row are staged in LDS
+// A8 gate-up epilogue: h = SwiGLU of the scaled accumulators, rounded to
+// bf16 (the layer's activation tensor) and quantised with the group's static
+// scale hsc; 128 E4M3 bytes per token row are staged in LDS
 // (16-byte chunks swizzled by row) and stored as whole chunks.
 __device__ __forceinline__ void big_epilogue_h8(const ExpertArgs &a, const BigTile &t,
                                                 const f32x4_t (&acc)[8][4], uint4 *lds, int tid,
-                                                float s0, float s1, float rhs) {
+                                                float s0, float s1, float hsc) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wr_ = wave >> 2, wt_ = wave & 3, r16 = lane & 15, cg = lane >> 4;
   constexpr int OC = BW / 2 / 16;   // 16-byte chunks per staged row (8)
@@ -195,8 +195,8 @@ __device__ __forceinline__ void big_epilogue_h8(const ExpertArgs &a, const BigTi
       const int gi = (i >> 1) * 4 + (i & 1);
       const int c = wr_ * 64 + (i >> 1) * 32 + (i & 1) * 16 + 4 * cg;
       const f32x4_t gv = acc[gi][j] * s0, uv = acc[gi + 2][j] * s1;
-      const uint32_t q = quant_e4m3x4_rcp(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
-                                          swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]), rhs);
+      const uint32_t q = quant_e4m3x4_bf16(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
+                                           swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]), hsc);
       *reinterpret_cast<uint32_t *>(row + (((c >> 4) ^ (r & 7)) << 4) + (c & 15)) = q;
     }
   }
@@ -238,7 +238,7 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
     s1 *= as;
   }
   if constexpr (A8 && GATE_UP) {
-    big_epilogue_h8(a, t, acc, lds, tid, s0, s1, 1.0f / a.hs[t.g]);
+    big_epilogue_h8(a, t, acc, lds, tid, s0, s1, a.hs[t.g]);
     return;
   }
   const int lane = tid & 63, wave = tid >> 6;

@@ -86,7 +86,7 @@ struct UnitOut {
   int row0, grp_end, col0, nsub, nf;
   float sc0, sc1;          // FP8 weights: scales of fragment 0 / 1's matrix
                            // (times the input's activation scale with a8)
-  float hs;                // a8 gate-up: 1 / activation scale of the group's h
+  float hs;                // a8 gate-up: activation scale of the group's h
 };
 
 // Unit u (tile u / n_col_blocks, column block u % n_col_blocks) of this
@@ -150,7 +150,7 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
       const float as = GATE_UP ? *a.xs : a.hs[g];
       o.sc0 *= as;
       o.sc1 *= as;
-      o.hs = 1.0f / a.hs[g];
+      o.hs = a.hs[g];
     }
   }
   const T *act = static_cast<const T *>(a.act);
@@ -218,10 +218,10 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
     if (GATE_UP) {
       const f32x4_t gv = acc[0][m] * s0, uv = acc[1][m] * s1;
       T *dst = out + (size_t)trow * a.ldh + o.col0 + 4 * cg;
-      if (F8 && a.a8)   // h quantised with its static scale, stored as bf16 values
+      if (F8 && a.a8)   // bf16 h quantised with its static scale, stored as bf16 values
         *reinterpret_cast<uint2 *>(dst) = e4m3x4_to_bf16(
-            quant_e4m3x4_rcp(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]), swiglu(gv[2], uv[2]),
-                             swiglu(gv[3], uv[3]), o.hs));
+            quant_e4m3x4_bf16(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]), swiglu(gv[2], uv[2]),
+                              swiglu(gv[3], uv[3]), o.hs));
       else
         store4(dst, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]), swiglu(gv[2], uv[2]),
                swiglu(gv[3], uv[3]));

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
   // ---- epilogue: lane holds D[weight row 16i + 4cg + q][token row 16j + r16] ----
   T *out = static_cast<T *>(a.out);
   // FP8: scale of the gate (or down) matrix and of the up matrix
-  float s0 = 1.0f, s1 = 1.0f, hs = 1.0f;   // hs: 1 / activation scale of h (a8)
+  float s0 = 1.0f, s1 = 1.0f, hs = 1.0f;   // hs: activation scale of h (a8)
   if (F8) {
     s0 = shared ? *a.ssc0 : a.sc0[g];
     if (GATE_UP) s1 = shared ? *a.ssc1 : a.sc1[g];
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
       const float as = GATE_UP ? *a.xs : a.hs[g];
       s0 *= as;
       s1 *= as;
-      hs = 1.0f / a.hs[g];
+      hs = a.hs[g];
     }
   }
 #pragma unroll
@@ -197,10 +197,10 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
         // rows +32 are the matching up cols.
         const int c = col0 + wr_ * 32 + i * 16 + 4 * cg;
         const f32x4_t gv = acc[i][j] * s0, uv = acc[i + 2][j] * s1;
-        if (F8 && a.a8)   // h quantised with its static scale, stored as bf16 values
+        if (F8 && a.a8)   // bf16 h quantised with its static scale, stored as bf16 values
           *reinterpret_cast<uint2 *>(out + (size_t)trow * a.ldh + c) = e4m3x4_to_bf16(
-              quant_e4m3x4_rcp(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
-                               swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]), hs));
+              quant_e4m3x4_bf16(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
+                                swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]), hs));
         else
           store4(out + (size_t)trow * a.ldh + c, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]),
                  swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));

@@ -5,16 +5,24 @@ Comparison rules
 ----------------
 * Route indices: for every token whose oracle selection margin (K-th minus
   (K+1)-th selection score, float64) exceeds 1e-6, the set of picked experts
-  must equal the oracle's exactly, and the weight of each picked expert must
-  agree to 2e-6 relative.  Tokens at or below the margin have several correct
-  answers; their outputs are checked against the oracle run on the GPU's own
-  route (oracle.forward_given_route).
-* Outputs: bf16 activations/weights at the Hy3 / HunyuanImage workload shapes:
-  max-abs error <= 2e-2 and rel-L2 <= 5e-3 against the float64 oracle.  Other
-  synthetic shapes can have larger outputs, where one bf16 rounding of the
-  output alone exceeds 2e-2 (|out| >= 4 has a half-ulp of 1/64), so there the
-  absolute bound is max(2e-2, 2^-6 * max|ref|), two bf16 ulps at the largest
-  output; rel-L2 stays 5e-3.  fp32: max-abs <= 1e-4 and rel-L2 <= 1e-5.
+  must equal the oracle's exactly.  A token at or below the margin has
+  several correct answers; the GPU's picks must then be one of them: a
+  top-K of the float64 selection scores up to the margin (every picked score
+  at least every unpicked score minus 1e-6).
+* Weights: on every token, the GPU weight of each picked expert equals the
+  oracle's weight formula evaluated on the GPU's own picks, to 2e-6
+  relative, and the K weights sum to the scale (sigmoid mode) or 1 (softmax
+  mode) within K/2 float32 ulps of that sum.
+* Outputs: near-tie tokens are checked against the oracle run on the GPU's
+  picks with the oracle's weights for them (``route_for_reference``), never
+  the GPU's weights.  bf16 activations/weights at the Hy3 / HunyuanImage
+  workload shapes: max-abs error <= 2e-2 and rel-L2 <= 5e-3 against the
+  float64 oracle.  Other synthetic shapes can have larger outputs, where one
+  bf16 rounding of the output alone exceeds 2e-2 (|out| >= 4 has a half-ulp
+  of 1/64), so there each element must satisfy
+  |got - ref| <= 2e-2 + 2^-8 |ref| (the stated bound plus one bf16 output
+  rounding at that element's magnitude); rel-L2 stays 5e-3.
+  fp32: max-abs <= 1e-4 and rel-L2 <= 1e-5.
 """
 from __future__ import annotations
 
@@ -55,29 +63,72 @@ def oracle_route(inp: MoEInputs, x64: Optional[np.ndarray] = None) -> oracle.Rou
     if x64 is None:
         x64 = inp.x_f64()
     b = inp.bias()
-    return oracle.route(x64, inp.w_router().astype(np.float64), c.K, c.route_mode,
-                        None if b is None else b.astype(np.float64), c.scale, c.renorm_eps)
+    r = oracle.route(x64, inp.w_router().astype(np.float64), c.K, c.route_mode,
+                     None if b is None else b.astype(np.float64), c.scale, c.renorm_eps)
+    # the weight formula's parameters, for weights on the GPU's own picks
+    r.mode, r.scale, r.renorm_eps = c.route_mode, c.scale, c.renorm_eps
+    return r
+
+
+def oracle_weights_on(r: oracle.Route, picks: np.ndarray) -> np.ndarray:
+    """The oracle's combine weights (float64) for the given picks."""
+    return oracle.combine_weights(r.prob, picks.astype(np.int64), getattr(r, "mode", 0),
+                                  getattr(r, "scale", 2.826), getattr(r, "renorm_eps", 1e-8))
 
 
 def check_route(gpu_idx: np.ndarray, gpu_w: np.ndarray, r: oracle.Route,
                 wtol: float = 2e-6) -> dict:
+    T, E = r.select_score.shape
+    K = gpu_idx.shape[1] if gpu_idx.ndim == 2 else 0
     ok = r.margin > MARGIN
-    gs, os_ = np.sort(gpu_idx, 1), np.sort(r.idx, 1)
+    gi = gpu_idx.astype(np.int64)
+    assert ((gi >= 0) & (gi < E)).all(), "route index out of range"
+    gs, os_ = np.sort(gi, 1), np.sort(r.idx, 1)
+    # every token's picks are distinct
+    assert (np.diff(gs, axis=1) != 0).all(), "repeated expert in a token's picks"
     bad = np.nonzero(ok & (gs != os_).any(1))[0]
     assert bad.size == 0, f"route indices differ on {bad.size} tokens, first {bad[:5]}"
-    assert ((gpu_idx >= 0) & (gpu_idx < r.select_score.shape[1])).all()
-    # every token's picks are distinct
-    assert (np.diff(gs, axis=1) != 0).all()
-    # weights per picked expert (align by expert id)
-    go, oo = np.argsort(gpu_idx, 1), np.argsort(r.idx, 1)
-    gw = np.take_along_axis(gpu_w.astype(np.float64), go, 1)
-    ow = np.take_along_axis(r.weight, oo, 1)
-    rel = np.abs(gw[ok] - ow[ok]) / np.maximum(np.abs(ow[ok]), 1e-30)
+    # near-tie tokens: the picks are a top-K of the float64 selection scores
+    # up to the margin (a valid answer where several are correct)
+    sel = r.select_score
+    picked = np.take_along_axis(sel, gi, 1)
+    mask = np.ones((T, E), dtype=bool)
+    np.put_along_axis(mask, gi, False, 1)
+    unpicked_max = np.where(mask, sel, -np.inf).max(1) if K < E else np.full(T, -np.inf)
+    slack = picked.min(1) - unpicked_max if T else np.zeros(0)
+    assert (slack >= -MARGIN).all(), \
+        f"not a top-K on tokens {np.nonzero(slack < -MARGIN)[0][:5]} (slack {slack.min():.3e})"
+    # weights: the formula on the GPU's own picks, on every token
+    want = oracle_weights_on(r, gi)
+    rel = np.abs(gpu_w.astype(np.float64) - want) / np.maximum(np.abs(want), 1e-30)
     assert rel.size == 0 or rel.max() <= wtol, f"weights rel err {rel.max():.3e}"
+    # sums: the scale in sigmoid mode; 1 in softmax mode unless the clamp
+    # binds (picked mass below renorm_eps), where the formula's own sum holds
+    if getattr(r, "mode", 0) == 0:
+        target = np.full(T, getattr(r, "scale", 2.826))
+    else:
+        mass = np.take_along_axis(r.prob, gi, 1).sum(1)
+        target = np.where(mass >= r.renorm_eps, 1.0, want.sum(1))
+    sums = gpu_w.astype(np.float64).sum(1)
+    tol_sum = 0.5 * K * np.spacing(np.float32(target.max() if T else 1.0))
+    assert (np.abs(sums - target) <= tol_sum).all(), \
+        f"weight sums off by {np.abs(sums - target).max():.3e} (tol {tol_sum:.3e})"
     # GPU picks are in descending selection score (checked on the oracle's scores)
-    sc = np.take_along_axis(r.select_score, gpu_idx.astype(np.int64), 1)
-    assert (np.diff(sc, axis=1) <= 1e-6).all()
-    return {"near_ties": int((~ok).sum()), "weight_rel_err": float(rel.max()) if rel.size else 0.0}
+    assert (np.diff(picked, axis=1) <= MARGIN).all(), "picks not in descending score"
+    return {"near_ties": int((~ok).sum()), "weight_rel_err": float(rel.max()) if rel.size else 0.0,
+            "near_tie_min_slack": float(slack[~ok].min()) if (~ok).any() else None}
+
+
+def route_for_reference(r: oracle.Route, gpu_idx: np.ndarray):
+    """(idx, weight) to evaluate the oracle's layer on: the oracle's route
+    where the margin exceeds 1e-6; elsewhere the GPU's picks (a valid top-K,
+    by check_route) with the oracle's float64 weights for them."""
+    idx, w = r.idx.copy(), r.weight.copy()
+    tie = r.margin <= MARGIN
+    if tie.any():
+        idx[tie] = gpu_idx[tie]
+        w[tie] = oracle_weights_on(r, gpu_idx)[tie]
+    return idx, w
 
 
 def output_errors(got: np.ndarray, ref: np.ndarray) -> tuple:
@@ -87,15 +138,37 @@ def output_errors(got: np.ndarray, ref: np.ndarray) -> tuple:
 
 def check_output(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "",
                  workload_shape: bool = False) -> tuple:
-    """workload_shape=True: one of the named workloads, strict bf16 bound."""
+    """workload_shape=True: one of the named workloads, the stated bf16 bound.
+    Otherwise (bf16) each element is held to 2e-2 + 2^-8 |ref|."""
     mx, rel = output_errors(got, ref)
     tmax, trel = TOL[dtype]
-    if dtype == "bf16" and not workload_shape and ref.size:
-        tmax = max(tmax, 2.0 ** -6 * float(np.abs(ref).max()))
     top = float(np.abs(ref).max()) if ref.size else 0.0
+    if dtype == "bf16" and not workload_shape and ref.size:
+        excess = np.abs(got.astype(np.float64) - ref) - (tmax + 2.0 ** -8 * np.abs(ref))
+        worst = float(excess.max())
+        log(f"  {what} max_abs={mx:.3e} rel_l2={rel:.3e} (per element 2e-2 + 2^-8|ref|: "
+            f"worst margin {-worst:.3e}; rel tol {trel:g}; max|ref| {top:.3g})")
+        assert worst <= 0 and rel <= trel, f"{what}: max_abs {mx:.3e} rel_l2 {rel:.3e}"
+        return mx, rel
     log(f"  {what} max_abs={mx:.3e} rel_l2={rel:.3e} (tol {tmax:g}/{trel:g}; max|ref| {top:.3g})")
     assert mx <= tmax and rel <= trel, f"{what}: max_abs {mx:.3e} rel_l2 {rel:.3e}"
     return mx, rel
+
+
+def expert_fn(inp: MoEInputs):
+    """expert(e) -> float64 (gate, up, down), regenerated on every call (no
+    cache: the layer-sized checks request each expert once)."""
+    fmt = inp.cfg.w_format
+
+    def f(e):
+        if fmt == "mxfp4":
+            codes, sc = inp.expert_mxfp4(e)
+            return tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(codes, sc))
+        if fmt == "fp8_e4m3":
+            codes, sc = inp.expert_fp8(e)
+            return tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))
+        return inp.expert_f64(e)
+    return f
 
 
 def expert_cache(inp: MoEInputs):

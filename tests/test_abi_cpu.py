@@ -316,13 +316,13 @@ def test_attention_decode_rejects_misaligned_or_missing_pointers(lib):
     L = lib
     ok = 1 << 20   # aligned stand-in addresses: rejected before use
     args = dict(q=ok, k=ok, v=ok, kv=ok, B=1, hkv=8, tile=256, tasks=ok, nt=1, wb=ok, nw=4,
-                rb=ok, ws=ok, wsb=1 << 20, out=ok)
+                rb=ok, nrows=8, ws=ok, wsb=1 << 20, out=ok)
 
     def call(**kw):
         a = dict(args, **kw)
         return L.hy3attn_decode(a["q"], a["k"], a["v"], a["kv"], a["B"], a["hkv"], a["tile"],
-                                a["tasks"], a["nt"], a["wb"], a["nw"], a["rb"], a["ws"], a["wsb"],
-                                a["out"], None)
+                                a["tasks"], a["nt"], a["wb"], a["nw"], a["rb"], a["nrows"],
+                                a["ws"], a["wsb"], a["out"], None)
     assert call(q=ok + 8) == -1          # q not 16-byte aligned
     assert call(k=ok + 4) == -1
     assert call(out=ok + 2) == -1        # out not 8-byte aligned
@@ -330,4 +330,33 @@ def test_attention_decode_rejects_misaligned_or_missing_pointers(lib):
     assert call(wsb=16) == -1            # workspace too small
     assert call(q=None) == -1
     assert call(hkv=0) == -1
-    assert call(B=0) == 0                # nothing to do
+    assert call(B=0, nrows=0) == 0       # nothing to do
+    # a plan made for another batch or KV head count is rejected
+    assert call(nrows=7) == -1
+    assert call(nrows=16) == -1
+    assert call(B=2) == -1               # plan rows 8, call rows 16
+    assert call(hkv=4) == -1
+    assert call(nt=-1) == -1
+
+
+def test_attention_binding_rejects_a_plan_for_another_batch(lib):
+    """attn_decode checks the plan against the call's shapes on the host,
+    before anything is copied to a device (CPU tensors stand in here)."""
+    import torch
+    import sparse_moe_amd as sm
+    plan = sm.attn_plan([300, 500], 2, 256, 4)
+    q = torch.zeros((2, 16, 128), dtype=torch.bfloat16)
+    k = torch.zeros((2, 800, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):      # three requests, plan for two
+        sm.attn_decode(torch.zeros((3, 16, 128), dtype=torch.bfloat16), k, k, [300, 500, 1], plan)
+    with pytest.raises(ValueError):      # four KV heads, plan for two
+        sm.attn_decode(torch.zeros((2, 32, 128), dtype=torch.bfloat16),
+                       torch.zeros((4, 800, 128), dtype=torch.bfloat16),
+                       torch.zeros((4, 800, 128), dtype=torch.bfloat16), [300, 500], plan)
+    with pytest.raises(ValueError):      # query heads not 8 per KV head
+        sm.attn_decode(torch.zeros((2, 8, 128), dtype=torch.bfloat16), k, k, [300, 500], plan)
+    bad = sm.AttnPlan(plan.tasks.copy(), plan.worker_begin, plan.row_begin, plan.n_workers,
+                      plan.tile)
+    bad.tasks[0, 0] = 5                  # a task naming request 5
+    with pytest.raises(ValueError):
+        sm.attn_decode(q, k, k, [300, 500], bad)

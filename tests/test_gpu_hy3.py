@@ -3,11 +3,13 @@ times: Hy3 decode (T=16), Hy3 prefill with skewed bias (T=8192), the router
 sweep (M in {2, 64, 512, 4096}, fp32-accurate and two-term split), and the
 HunyuanImage-3.0 softmax long prefill (T=32768, E=64).
 
-Every route index is checked; outputs are checked on every token for decode
-and on a seeded sample of 256 tokens plus every near-tie token otherwise
-(each sampled row is computed by the oracle one by one from its route).
+Every route index and every output row is checked.  The oracle evaluates
+the layer expert by expert (``oracle.forward_by_expert``), regenerating one
+expert's weights at a time, so the largest workload (T=32768) needs no
+float64 copy of the whole weight set.
 """
 import gc
+import time
 
 import numpy as np
 import pytest
@@ -15,9 +17,9 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (MARGIN, a8_of, amx_of, check_output, check_route, config_of, expert_cache, log,
-                      oracle_route, out_to_np, shared_f64, to_torch, upload_weights,
-                      with_act_scales, with_bias_of)
+from gpu_util import (a8_of, amx_of, check_output, check_route, config_of, expert_fn, log,
+                      oracle_route, out_to_np, route_for_reference, shared_f64, to_torch,
+                      upload_weights, with_act_scales, with_bias_of)
 from synth import CONFIGS, ROUTER_SWEEP_M, MoEInputs
 
 pytestmark = pytest.mark.gpu
@@ -42,37 +44,9 @@ def hy3_weights(dev):
     torch.cuda.empty_cache()
 
 
-def sampled_check(inp, dev, weights, n_sample=256, seed=0, workload_shape=True):
-    c = inp.cfg
-    weights = with_bias_of(inp, weights, dev)
-    cfg = config_of(inp)
-    x = to_torch(inp.x(), c.dtype, dev)
-    out, idx, w = sm.forward(cfg, x, weights, return_route=True)
-    torch.cuda.synchronize()
-    gidx, gw = idx.cpu().numpy(), w.cpu().numpy()
-    log(f"  oracle route over all {c.T} tokens")
-    r = oracle_route(inp)
-    info = check_route(gidx, gw, r)
-    tie = np.nonzero(r.margin <= MARGIN)[0]
-    rng = np.random.default_rng(seed)
-    tokens = np.union1d(rng.choice(c.T, size=min(n_sample, c.T), replace=False), tie)
-    log(f"  near-tie tokens: {tie.size}; oracle outputs on {tokens.size} tokens")
-    x64 = inp.x_f64()[tokens]
-    ridx, rw = r.idx[tokens].copy(), r.weight[tokens].copy()
-    t_is_tie = np.isin(tokens, tie)
-    ridx[t_is_tie] = gidx[tokens][t_is_tie]
-    rw[t_is_tie] = gw[tokens][t_is_tie]
-    ref = oracle.forward_given_route(x64, ridx, rw, expert_cache(inp), c.E, shared_f64(inp),
-                                     a8=a8_of(inp), amx=amx_of(inp))
-    got = out_to_np(out)[tokens]
-    check_output(got, ref, c.dtype, c.name, workload_shape=workload_shape)
-    counts = np.bincount(gidx.reshape(-1), minlength=c.E)
-    log(f"  experts hit {int((counts > 0).sum())}/{c.E}, max load {counts.max()} "
-        f"(mean {counts.mean():.1f})")
-    return info
-
-
-def decode_full_check(inp, dev, weights, workload_shape=True):
+def layer_check(inp, dev, weights, workload_shape=True):
+    """Every route index and every output row of the layer against the
+    oracle (evaluated expert by expert, one expert's weights at a time)."""
     c = inp.cfg
     log(f"case {c.name}")
     weights = with_bias_of(inp, weights, dev)
@@ -81,25 +55,34 @@ def decode_full_check(inp, dev, weights, workload_shape=True):
     out, idx, w = sm.forward(cfg, x, weights, return_route=True)
     torch.cuda.synchronize()
     gidx, gw = idx.cpu().numpy(), w.cpu().numpy()
+    got = out_to_np(out)
+    del out, x
+    log(f"  oracle route over all {c.T} tokens")
     r = oracle_route(inp)
-    check_route(gidx, gw, r)
-    np.testing.assert_allclose(gw.sum(1), 2.826, rtol=0, atol=4 * np.spacing(np.float32(2.826)))
-    ridx, rw = r.idx.copy(), r.weight.copy()
-    tie = r.margin <= MARGIN
-    ridx[tie], rw[tie] = gidx[tie], gw[tie]
-    ref = oracle.forward_given_route(inp.x_f64(), ridx, rw, expert_cache(inp), c.E,
-                                     shared_f64(inp), a8=a8_of(inp), amx=amx_of(inp))
-    check_output(out_to_np(out), ref, c.dtype, c.name, workload_shape=workload_shape)
+    info = check_route(gidx, gw, r)
+    log(f"  near-tie tokens: {info['near_ties']} (min top-K slack {info['near_tie_min_slack']})")
+    ridx, rw = route_for_reference(r, gidx)
+    counts = np.bincount(gidx.reshape(-1), minlength=c.E)
+    log(f"  experts hit {int((counts > 0).sum())}/{c.E}, max load {counts.max()} "
+        f"(mean {counts.mean():.1f}); oracle outputs on all {c.T} tokens")
+    t0 = time.time()
+    ref = oracle.forward_by_expert(inp.x_f64(), ridx, rw, expert_fn(inp), c.E, shared_f64(inp),
+                                   a8=a8_of(inp), amx=amx_of(inp))
+    log(f"  oracle layer in {time.time() - t0:.1f}s")
+    check_output(got, ref, c.dtype, c.name, workload_shape=workload_shape)
+    return info
+
+
+def decode_full_check(inp, dev, weights, workload_shape=True):
+    layer_check(inp, dev, weights, workload_shape)
 
 
 def test_hy3_decode_T16_full(dev, hy3_weights):
     decode_full_check(MoEInputs(CONFIGS["hy3_decode_T16"]), dev, hy3_weights)
 
 
-def test_hy3_prefill_T8192_skew_sampled(dev, hy3_weights):
-    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew"])
-    log(f"case {inp.cfg.name}")
-    sampled_check(inp, dev, hy3_weights)
+def test_hy3_prefill_T8192_skew_full(dev, hy3_weights):
+    layer_check(MoEInputs(CONFIGS["hy3_prefill_T8192_skew"]), dev, hy3_weights)
 
 
 @pytest.mark.parametrize("M", ROUTER_SWEEP_M)
@@ -129,14 +112,14 @@ def test_router_sweep(dev, hy3_weights, M):
             check_route(idx.cpu().numpy(), w.cpu().numpy(), oracle_route(inp))
 
 
-def test_softmax_long_prefill_T32768_sampled(dev):
+def test_softmax_long_prefill_T32768_full(dev):
     gc.collect()
     torch.cuda.empty_cache()
     inp = MoEInputs(CONFIGS["hunyuanimage_softmax_T32768"])
     log(f"case {inp.cfg.name}: uploading 64 experts")
     w = upload_weights(inp, dev)
     try:
-        sampled_check(inp, dev, w)
+        layer_check(inp, dev, w)
     finally:
         del w
         torch.cuda.empty_cache()
@@ -157,17 +140,16 @@ def hy3_fp8_weights(dev):
 def test_hy3_decode_T16_fp8_full(dev, hy3_fp8_weights):
     """Hy3 decode with FP8 E4M3 experts (one scale per matrix), every token.
 
-    Not one of the bf16 workloads the 2e-2 bound is stated for: the output
-    bound is the derived one (max(2e-2, 2^-6 max|ref|), a bf16 ulp or two at
-    the largest output); rel-L2 stays 5e-3."""
+    Not one of the bf16 workloads the 2e-2 bound is stated for: each element
+    is held to 2e-2 + 2^-8 |ref| (the stated bound plus one bf16 output
+    rounding at its magnitude); rel-L2 stays 5e-3."""
     decode_full_check(MoEInputs(CONFIGS["hy3_decode_T16_fp8"]), dev, hy3_fp8_weights, workload_shape=False)
 
 
-def test_hy3_prefill_T8192_skew_fp8_sampled(dev, hy3_fp8_weights):
+def test_hy3_prefill_T8192_skew_fp8_full(dev, hy3_fp8_weights):
     """The prefill chunk on the same FP8 experts (large-tile path)."""
-    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_fp8"])
-    log(f"case {inp.cfg.name}")
-    sampled_check(inp, dev, hy3_fp8_weights, workload_shape=False)
+    layer_check(MoEInputs(CONFIGS["hy3_prefill_T8192_skew_fp8"]), dev, hy3_fp8_weights,
+                workload_shape=False)
 
 
 def test_hy3_decode_T16_w8a8_full(dev, hy3_fp8_weights):
@@ -180,11 +162,10 @@ def test_hy3_decode_T16_w8a8_full(dev, hy3_fp8_weights):
                       workload_shape=False)
 
 
-def test_hy3_prefill_T8192_skew_w8a8_sampled(dev, hy3_fp8_weights):
+def test_hy3_prefill_T8192_skew_w8a8_full(dev, hy3_fp8_weights):
     """The W8A8 prefill chunk: FP8 MFMAs on the large-tile path."""
     inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_w8a8"])
-    log(f"case {inp.cfg.name}")
-    sampled_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev), workload_shape=False)
+    layer_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev), workload_shape=False)
 
 
 @pytest.fixture(scope="module")
@@ -205,11 +186,10 @@ def test_hy3_decode_T16_mxfp4_full(dev, hy3_mxfp4_weights):
     decode_full_check(MoEInputs(CONFIGS["hy3_decode_T16_mxfp4"]), dev, hy3_mxfp4_weights, workload_shape=False)
 
 
-def test_hy3_prefill_T8192_skew_mxfp4_sampled(dev, hy3_mxfp4_weights):
+def test_hy3_prefill_T8192_skew_mxfp4_full(dev, hy3_mxfp4_weights):
     """The prefill chunk on the same MXFP4 experts (large-tile path)."""
-    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_mxfp4"])
-    log(f"case {inp.cfg.name}")
-    sampled_check(inp, dev, hy3_mxfp4_weights, workload_shape=False)
+    layer_check(MoEInputs(CONFIGS["hy3_prefill_T8192_skew_mxfp4"]), dev, hy3_mxfp4_weights,
+                workload_shape=False)
 
 
 def test_hy3_decode_T16_w4a8_full(dev, hy3_mxfp4_weights):
@@ -218,7 +198,6 @@ def test_hy3_decode_T16_w4a8_full(dev, hy3_mxfp4_weights):
     decode_full_check(MoEInputs(CONFIGS["hy3_decode_T16_w4a8"]), dev, hy3_mxfp4_weights, workload_shape=False)
 
 
-def test_hy3_prefill_T8192_skew_w4a8_sampled(dev, hy3_mxfp4_weights):
-    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_w4a8"])
-    log(f"case {inp.cfg.name}")
-    sampled_check(inp, dev, hy3_mxfp4_weights, workload_shape=False)
+def test_hy3_prefill_T8192_skew_w4a8_full(dev, hy3_mxfp4_weights):
+    layer_check(MoEInputs(CONFIGS["hy3_prefill_T8192_skew_w4a8"]), dev, hy3_mxfp4_weights,
+                workload_shape=False)

@@ -15,7 +15,8 @@ import torch
 import oracle
 import sparse_moe_amd as sm
 from gpu_util import (MARGIN, a8_of, amx_of, check_output, check_route, config_of, expert_cache, log,
-                      oracle_route, out_to_np, shared_f64, to_torch, upload_weights)
+                      oracle_route, out_to_np, route_for_reference, shared_f64, to_torch,
+                      upload_weights)
 from synth import CONFIGS, MoEInputs, random_small
 
 pytestmark = pytest.mark.gpu
@@ -29,13 +30,11 @@ def dev():
 
 
 def reference(inp, r, gidx, gw, tokens=None):
-    """Oracle output on the oracle's route, except near-tie tokens, which use the GPU's."""
+    """Oracle output on the oracle's route, except near-tie tokens, which use
+    the GPU's picks (a valid top-K) with the oracle's weights for them."""
     c = inp.cfg
     x64 = inp.x_f64()
-    idx, w = r.idx.copy(), r.weight.copy()
-    tie = r.margin <= MARGIN
-    idx[tie] = gidx[tie]
-    w[tie] = gw[tie].astype(np.float64)
+    idx, w = route_for_reference(r, gidx)
     if tokens is not None:
         x64, idx, w = x64[tokens], idx[tokens], w[tokens]
     return oracle.forward_given_route(x64, idx, w, expert_cache(inp), c.E, shared_f64(inp),
@@ -308,3 +307,41 @@ def test_route_indices_valid_with_nan_scores(dev, route_mode):
     ok = ok[r.margin[ok] > MARGIN]
     assert ok.size > 40
     np.testing.assert_array_equal(np.sort(idx[ok], 1), np.sort(r.idx[ok], 1))
+
+
+@pytest.mark.parametrize("route_mode", [0, 1])
+@pytest.mark.parametrize("T", [16, 300, 1100])
+def test_exact_ties_go_to_the_lower_expert_index(dev, T, route_mode):
+    """Experts e and e + 8 get identical router rows (and, in sigmoid mode,
+    identical biases), so their scores are equal on every token.  With K = 3
+    the top three are the best pair and one expert of the second-best pair:
+    every token has an exact tie at the K-th place.  The documented rule
+    (equal scores ordered by ascending expert index) fixes the answer: the
+    GPU's picks must equal the oracle's, order included.  T = 16, 300 and
+    1100 run the small, tiled and plane-split router kernels."""
+    kw = dict(route_mode=1, scale=1.0, renorm_eps=1e-8, bias_kind="none") if route_mode else {}
+    inp = random_small(27, T=T, H=256, E=16, K=3, I=64, I_shared=64, dtype="bf16", **kw)
+    wr = np.array(inp.w_router(), copy=True)
+    wr[8:] = wr[:8]
+    inp._cache[("wr",)] = wr
+    if route_mode == 0:
+        b = np.array(inp.bias(), copy=True)
+        b[8:] = b[:8]
+        inp._cache[("bias",)] = b
+    w = upload_weights(inp, dev)
+    cfg = config_of(inp)
+    idx, wt = sm.route(cfg, to_torch(inp.x(), "bf16", dev), w["w_router"], w.get("expert_bias"))
+    torch.cuda.synchronize()
+    gidx, gw = idx.cpu().numpy(), wt.cpu().numpy()
+    r = oracle_route(inp)
+    # pair-level separation: best pair, second pair and third pair apart by
+    # more than the margin, so the only ties are the constructed ones
+    ps = -np.sort(-r.select_score[:, :8], axis=1)
+    clear = (ps[:, 0] - ps[:, 1] > MARGIN) & (ps[:, 1] - ps[:, 2] > MARGIN)
+    assert clear.sum() >= 0.9 * T
+    np.testing.assert_array_equal(r.margin, 0.0)
+    np.testing.assert_array_equal(gidx[clear], r.idx[clear])
+    # the picks hold one full pair and the lower index of the next pair
+    assert ((gidx[clear][:, 1] - gidx[clear][:, 0]) == 8).all()
+    assert (gidx[clear][:, 2] < 8).all()
+    check_route(gidx, gw, r)

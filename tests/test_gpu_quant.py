@@ -100,11 +100,13 @@ def _h_error_bound(a, wg, wu, gemm):
                                                 (16, 16, 256, None)])
 def test_w8a8_codes_in_the_workspace(dev, T, E, H, path_rows):
     """The quantised activations the forward leaves in its workspace: x codes
-    bit-exact against the oracle's quantiser; h codes equal to the oracle's
-    wherever the quotient h / a2 lies farther from a rounding midpoint than
-    the GPU's float32 h can be from the oracle's float64 h (an accumulation
-    error bound), and one grid step away at most elsewhere.  Large-tile
-    path: E4M3 bytes; the other paths: their bf16 values."""
+    bit-exact against the oracle's quantiser.  h is quantised as the layer's
+    bf16 tensor, with a correctly rounded division by a2 on both sides, so
+    its code equals the oracle's wherever the GPU's float32 h (within an
+    accumulation error bound dh of the float64 h) rounds to the same bf16
+    value as the float64 h, i.e. no bf16 rounding boundary lies within dh
+    of h; elsewhere it is at most one E4M3 grid step away.  Large-tile path:
+    E4M3 bytes; the other paths: their bf16 values."""
     from gpu_util import a8_of, config_of, expert_cache, shared_f64, to_torch, upload_weights
     from synth import random_small
     inp = random_small(50 + T, T=T, H=H, E=E, K=4, I=256, I_shared=128, dtype="bf16",
@@ -154,30 +156,27 @@ def test_w8a8_codes_in_the_workspace(dev, T, E, H, path_rows):
         Ig = wg.shape[0]
         a = xh[sorted_token[r0:r1]]
         gg, uu = a @ wg.T, a @ wu.T
-        ref = oracle.fp8_e4m3_value(oracle.quant_e4m3(oracle.silu(gg) * uu, a2[g]))
         got = np.stack([values(L.h + (r * ldh) * (1 if codes_path else 2), Ig)
                         for r in range(r0, r1)])
         u32 = 2.0 ** -24
         h64, dh = _h_error_bound(a, wg, wu, (1024 * 2.0 ** -23) if codes_path else 64 * u32)
-        q = np.minimum(np.abs(np.float32(h64) / np.float32(a2[g])).astype(np.float64), 448.0)
-        step = _grid_step(q)
-        frac = q / step
-        near = np.abs(frac - np.floor(frac) - 0.5) * step <= dh / a2[g] + 4 * u32 * q
+        ref = oracle.fp8_e4m3_value(oracle.quant_e4m3(oracle.round_bf16(h64), a2[g]))
+        # the GPU's bf16 h is the oracle's unless a bf16 rounding boundary
+        # lies within dh of h (bf16 rounding is monotone)
+        near = oracle.round_bf16(h64 - dh) != oracle.round_bf16(h64 + dh)
         diff = got != ref
         bad = np.argwhere(diff & ~near)
         for i, j in bad[:4]:
             log(f"  group {g} row {i} col {j}: g={gg[i, j]:.9g} u={uu[i, j]:.9g} "
-                f"h={h64[i, j]:.9g} q={q[i, j]:.9g} got={got[i, j]} ref={ref[i, j]} "
-                f"mid_dist={abs(frac[i, j] - np.floor(frac[i, j]) - 0.5) * step[i, j]:.3g} "
-                f"dh/a2={dh[i, j] / a2[g]:.3g} |g|sum={(np.abs(a) @ np.abs(wg).T)[i, j]:.4g} "
-                f"|u|sum={(np.abs(a) @ np.abs(wu).T)[i, j]:.4g}")
+                f"h={h64[i, j]:.9g} bf16(h)={oracle.round_bf16(h64[i, j]):.9g} "
+                f"got={got[i, j]} ref={ref[i, j]} dh={dh[i, j]:.3g}")
         assert bad.size == 0, f"{bad.shape[0]} codes off beyond the bound in group {g}"
         big_step = _grid_step(np.maximum(np.abs(got), np.abs(ref)))
         assert (np.abs(got - ref) <= big_step * (1 + 1e-12)).all()
         n_all += got.size
         n_near += int(near.sum())
     log(f"  T={T}: x codes exact ({c.T * c.H}); h codes {n_all}, "
-        f"{n_near} within the error bound of a midpoint")
+        f"{n_near} within the error bound of a bf16 rounding boundary")
     assert n_near < (0.3 if codes_path else 0.03) * n_all
 
 

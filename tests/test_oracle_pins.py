@@ -505,8 +505,10 @@ def test_w8a8_layer_eager_equals_dense_masked(seed):
 
 def test_w8a8_layer_scalar_loops():
     """One token through a loop-only evaluation: quantise x with a1, run every
-    picked expert with element loops, quantise each h value with that
-    expert's a2, and sum with the route weights."""
+    picked expert with element loops, round each h value to bfloat16 (by
+    torch) and quantise it with that expert's a2, and sum with the route
+    weights."""
+    torch = pytest.importorskip("torch")
     inp, experts, shared, r, (a1, a2) = _w8a8_small(3, T=2, H=16, E=4, K=2, I=8, I_shared=8)
     c = inp.cfg
     x = inp.x_f64()
@@ -523,7 +525,8 @@ def test_w8a8_layer_scalar_loops():
                 g = math.fsum(xq[k] * wg[i, k] for k in range(c.H))
                 u = math.fsum(xq[k] * wu[i, k] for k in range(c.H))
                 h = g / (1.0 + math.exp(-g)) * u
-                hq.append(float(oracle.quant_dequant_e4m3(np.array([h]), a2[e])[0]))
+                hb = float(torch.tensor([h], dtype=torch.float32).to(torch.bfloat16).double())
+                hq.append(float(oracle.quant_dequant_e4m3(np.array([hb]), a2[e])[0]))
             for n in range(c.H):
                 ref[n] += w * math.fsum(hq[i] * wd[n, i] for i in range(len(hq)))
         np.testing.assert_allclose(got[t], ref, rtol=1e-12, atol=1e-13)
@@ -739,3 +742,57 @@ def test_w4a8_layer_is_within_the_quantisation_error_of_w4a16():
                                      amx=True)
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert 0.005 < rel < 0.08, rel
+
+
+# ------------------------------------------------- weights on given picks ----
+def test_combine_weights_closed_form():
+    """Weights of hand-chosen picks: sigmoid mode renormalises the picked
+    unbiased scores and scales them; softmax mode divides by the clamped sum."""
+    prob = np.array([[0.5, 0.25, 0.75, 0.125]])
+    w = oracle.combine_weights(prob, np.array([[2, 0]]), oracle.ROUTE_SIGMOID_BIAS, 2.826)
+    np.testing.assert_allclose(w, [[2.826 * 0.6, 2.826 * 0.4]], rtol=0, atol=1e-15)
+    w = oracle.combine_weights(prob, np.array([[1, 3]]), oracle.ROUTE_SOFTMAX, 1.0, 1e-8)
+    np.testing.assert_allclose(w, [[2 / 3, 1 / 3]], rtol=0, atol=1e-15)
+    # the clamp binds when the picked mass is below it
+    w = oracle.combine_weights(np.array([[1e-10, 3e-10]]), np.array([[0, 1]]),
+                               oracle.ROUTE_SOFTMAX, 1.0, 1e-8)
+    np.testing.assert_allclose(w, [[1e-2, 3e-2]], rtol=1e-12)
+
+
+# ------------------------------------- the expert-by-expert evaluation ----
+@pytest.mark.parametrize("seed, mode, fmt", [(0, 0, None), (1, 1, None), (2, 0, "a8"),
+                                              (3, 0, "amx"), (4, 0, "noshared")])
+def test_forward_by_expert_equals_dense_masked(seed, mode, fmt):
+    """The streamed form against brute-force dense evaluation of every expert
+    (the same sum, every expert on every token, masked)."""
+    kw = dict(route_mode=1, scale=1.0, renorm_eps=1e-8, bias_kind="none") if mode else {}
+    if fmt == "amx":
+        inp = random_small(200 + seed, T=11, H=64, E=6, K=3, I=32, I_shared=32, **kw)
+    else:
+        inp = random_small(200 + seed, T=13, H=8, E=7, K=3, I=5,
+                           I_shared=0 if fmt == "noshared" else 4, **kw)
+    c = inp.cfg
+    ex = [inp.expert_f64(e) for e in range(c.E)]
+    x = inp.x_f64()
+    b = inp.bias()
+    r = oracle.route(x, inp.w_router().astype(np.float64), c.K, mode,
+                     None if b is None else b.astype(np.float64), c.scale, c.renorm_eps)
+    sh = None if fmt == "noshared" else inp.shared_f64()
+    a8 = (0.01, np.linspace(0.002, 0.004, c.E + 1)) if fmt == "a8" else None
+    amx = fmt == "amx"
+    got = oracle.forward_by_expert(x, r.idx, r.weight, lambda e: ex[e], c.E, sh, a8=a8, amx=amx)
+    ref = oracle.dense_masked(x, r.idx, r.weight, lambda e: ex[e], c.E, sh, a8=a8, amx=amx)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    assert np.abs(ref).max() > 0.05
+
+
+def test_forward_by_expert_requests_each_expert_once():
+    inp = random_small(210, T=40, H=8, E=9, K=4, I=5, I_shared=4)
+    c = inp.cfg
+    ex = [inp.expert_f64(e) for e in range(c.E)]
+    r = oracle.route(inp.x_f64(), inp.w_router().astype(np.float64), c.K, 0,
+                     inp.bias().astype(np.float64), c.scale)
+    asked = []
+    oracle.forward_by_expert(inp.x_f64(), r.idx, r.weight,
+                             lambda e: asked.append(e) or ex[e], c.E, inp.shared_f64())
+    assert sorted(asked) == sorted(set(asked)) == sorted(set(r.idx.reshape(-1).tolist()))
