@@ -17,7 +17,10 @@ FP8 peak).
 Printed: one JSON line with tokens/s, the dominant kernel's roofline fraction
 (its per-launch duration measured live with HIP events on the library's
 stream, via hy3moe_forward_timed), the whole-layer fractions, and the CPU
-oracle timed on a bounded sample on this host.
+oracle timed on a bounded sample on this host.  The default run (decode)
+then times the prefill chunk on the same weights and adds it under
+"prefill" with its own roofline (bf16 MFMA) and stage times; the headline
+value stays the decode one.
 """
 from __future__ import annotations
 
@@ -199,6 +202,8 @@ def main():
     ap.add_argument("--router-sweep", action="store_true",
                     help="time the gate alone (hy3moe_route) at M = 2, 64, 512, 4096 tokens, "
                          "fp32-accurate and two-term split router, instead of the layer")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="default workload only: skip the prefill chunk timed after decode")
     ap.add_argument("--graph", action="store_true",
                     help="also time the layer as a captured HIP graph replayed K times")
     args = ap.parse_args()
@@ -213,7 +218,7 @@ def main():
 
     import sparse_moe_amd as sm
     from synth import CONFIGS, MoEInputs
-    from synth.device import to_torch, upload_weights
+    from synth.device import upload_weights, with_bias_of
 
     dev = torch.device("cuda:0")
     if args.ceilings:
@@ -227,12 +232,64 @@ def main():
         print(json.dumps(attention_bench(args, dev)), flush=True)
         return
     inp = MoEInputs(CONFIGS[WORKLOADS[args.workload]])
-    c = inp.cfg
     t0 = time.time()
     weights = upload_weights(inp, dev)
-    x = to_torch(inp.x(), c.dtype, dev)
     torch.cuda.synchronize()
-    log(f"[bench] {c.name}: inputs uploaded in {time.time() - t0:.1f}s")
+    log(f"[bench] {inp.cfg.name}: weights uploaded in {time.time() - t0:.1f}s")
+    m = layer_bench(inp, weights, args.workload, args, dev, graph=args.graph)
+    c = inp.cfg
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args, m["idx"])
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC, "value": c.T / (m["ms_per_step"] / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": m["mma_dtype"],
+        "data": "synthetic (seeded, random-init weights of the layer's shapes)",
+        "config": m["config"],
+        "roofline": m["roofline"], "cpu_baseline": cpu, "layer": m["layer"],
+        "graph_ms_per_step": m["graph_ms"],
+    }
+    # The default run also times the prefill chunk (T=8192, skewed bias) on the
+    # same Hy3 weights: the metric's bf16 MFMA half.  Its own roofline and
+    # stage times; the headline value stays the decode workload's.
+    if args.workload == "decode" and not args.no_prefill:
+        pinp = MoEInputs(CONFIGS[WORKLOADS["prefill"]])
+        assert pinp.cfg.model_key == c.model_key, "prefill must share the decode weights"
+        pw = with_bias_of(pinp, weights, dev)
+        pm = layer_bench(pinp, pw, "prefill", args, dev)
+        res["prefill"] = {"workload": pinp.cfg.name, "value": pinp.cfg.T / (pm["ms_per_step"] / 1e3),
+                          "unit": "tokens/s", "ms_per_step": pm["ms_per_step"],
+                          "steps": args.steps, "warmup": args.warmup, "dtype": pm["mma_dtype"],
+                          "config": pm["config"], "roofline": pm["roofline"],
+                          "layer": pm["layer"]}
+    print(json.dumps(res), flush=True)
+
+
+def layer_bench(inp, weights, key, args, dev, graph=False):
+    """Time hy3moe_forward on one workload: K steps between synchronisations
+    (wall clock), then K steps through hy3moe_forward_timed for per-stage HIP
+    event durations; returns the timings, the roofline of the gate-up kernel
+    and the whole-layer figures."""
+    import numpy as np
+    import torch
+
+    import sparse_moe_amd as sm
+    from synth.device import to_torch
+
+    c = inp.cfg
+    x = to_torch(inp.x(), c.dtype, dev)
     cfg = sm.make_config(c.T, c.H, c.E, c.K, c.I, c.I_shared, c.dtype, c.route_mode,
                          scale=c.scale, renorm_eps=c.renorm_eps, w_format=c.w_format,
                          act_format=c.act_format)
@@ -259,11 +316,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_per_step = wall * 1e3 / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+    log(f"[bench] {c.name}: timed {args.steps} steps: {ms_per_step:.4f} ms/step")
 
     # ---- optional: the same step captured once as a HIP graph, replayed ----
     graph_ms = None
-    if args.graph:
+    if graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -294,7 +351,7 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs]))
                 for i, name in enumerate(sm.STAGE_NAMES)}
-    log("[bench] stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+    log(f"[bench] {c.name} stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
 
     # ---- algorithmic work ----
     eb = 2 if c.dtype == "bf16" else 4
@@ -325,7 +382,7 @@ def main():
     layer_flops = 1.5 * gu_flops + 2.0 * T * H * E
     layer_s = ms_per_step / 1e3
     gu_s = stage_ms["gate_up"] / 1e3
-    decode = args.workload.startswith("decode")
+    decode = key.startswith("decode")
     if decode:
         kind = {"fp8_e4m3": "FP8 E4M3", "mxfp4": "MXFP4"}.get(c.w_format, c.dtype)
         roof = {"kernel": "gate_up (weight-streaming grouped GEMM + SwiGLU)", "bound": "hbm",
@@ -341,7 +398,7 @@ def main():
                 "per_unit": f"{4 * H * I} FLOP per routed row x {T * K} rows + "
                             f"{4 * H * Is} per shared row x {T}"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    tr = measured_traffic(args.workload, "gate_up")
+    tr = measured_traffic(key, "gate_up")
     roof["traffic"] = tr
     roof["avg_launch_ms"] = stage_ms["gate_up"]
 
@@ -356,34 +413,14 @@ def main():
                           else dn_flops / (stage_ms["down"] / 1e3) / 1e12),
     }
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args, idx.cpu().numpy())
-
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-
-    res = {
-        "metric": METRIC, "value": T / layer_s, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": mma_dtype,
-        "data": "synthetic (seeded, random-init weights of the layer's shapes)",
-        "config": {"workload": c.name, "T": T, "H": H, "E": E, "K": K, "I": I, "I_shared": Is,
-                   "route": "sigmoid+bias" if c.route_mode == 0 else "softmax",
-                   "expert_weights": c.w_format if c.w_format != "dtype" else c.dtype,
-                   "expert_activations": {"fp8_static": "fp8_e4m3_static",
-                                          "mxfp8": "mxfp8_dynamic"}.get(c.act_format,
-                                                                        c.dtype)},
-        "roofline": roof, "cpu_baseline": cpu, "layer": layer,
-        "graph_ms_per_step": graph_ms,
-    }
-    print(json.dumps(res), flush=True)
+    config = {"workload": c.name, "T": T, "H": H, "E": E, "K": K, "I": I, "I_shared": Is,
+              "route": "sigmoid+bias" if c.route_mode == 0 else "softmax",
+              "expert_weights": c.w_format if c.w_format != "dtype" else c.dtype,
+              "expert_activations": {"fp8_static": "fp8_e4m3_static",
+                                     "mxfp8": "mxfp8_dynamic"}.get(c.act_format, c.dtype)}
+    return {"ms_per_step": ms_per_step, "stage_ms": stage_ms, "roofline": roof, "layer": layer,
+            "config": config, "mma_dtype": mma_dtype, "graph_ms": graph_ms,
+            "idx": idx.cpu().numpy()}
 
 
 def router_sweep(args, dev):

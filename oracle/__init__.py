@@ -2,7 +2,7 @@
 imported by tests, the smoke check and the benchmark's CPU-baseline leg,
 never by the product path."""
 from .moe import (E4M3_MAX, ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, combine_weights,
-                  dense_masked, forward_by_expert,
+                  dense_masked, expert_h, forward_by_expert,
                   dequant_fp8, dequant_mxfp4, e8m0_value, forward, forward_given_route,
                   fp4_e2m1_value, fp8_e4m3_value,
                   dequant_mxfp8, layer_flops, quant_dequant_e4m3, quant_dequant_mxfp8,
@@ -12,7 +12,7 @@ from .moe import (E4M3_MAX, ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, combine_we
 
 __all__ = [
     "E4M3_MAX", "ROUTE_SIGMOID_BIAS", "ROUTE_SOFTMAX", "Route", "combine_weights",
-    "dense_masked", "dequant_fp8", "forward_by_expert",
+    "dense_masked", "dequant_fp8", "expert_h", "forward_by_expert",
     "dequant_mxfp4", "e8m0_value", "fp4_e2m1_value",
     "forward", "forward_given_route", "fp8_e4m3_value", "layer_flops", "quant_dequant_e4m3",
     "quant_e4m3", "route", "route_from_logits", "dequant_mxfp8", "quant_dequant_mxfp8",

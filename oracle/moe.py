@@ -377,30 +377,43 @@ def silu(z: np.ndarray) -> np.ndarray:
     return np.asarray(z, dtype=np.float64) * sigmoid(z)
 
 
+def expert_h(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+             a2: Optional[float] = None, amx: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """The SwiGLU activation of one expert on rows ``a`` [n, H].
+
+    Returns (h, h_in): h = silu(a W_gate^T) * (a W_up^T) in float64, and
+    h_in, what the down projection reads.  Without activation quantisation
+    h_in is h.  With ``a2`` (static FP8 activations, W8A8) h, as the layer's
+    bfloat16 activation tensor (``round_bf16``), is quantised to E4M3 with
+    the static scale a2 and dequantised (``quant_dequant_e4m3``), as an FP8
+    Linear quantises its input.  With ``amx`` (dynamic MXFP8 activations,
+    W4A8) the same bfloat16 h is quantised per block of 32 along I instead
+    (``quant_dequant_mxfp8``).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    g = a @ np.asarray(w_gate, dtype=np.float64).T
+    u = a @ np.asarray(w_up, dtype=np.float64).T
+    h = silu(g) * u
+    h_in = h
+    if a2 is not None:
+        h_in = quant_dequant_e4m3(round_bf16(h), a2)
+    if amx:
+        h_in = quant_dequant_mxfp8(round_bf16(h))
+    return h, h_in
+
+
 def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
                   w_down: np.ndarray, a2: Optional[float] = None,
                   amx: bool = False) -> np.ndarray:
     """One SwiGLU expert on rows ``a`` [n, H]:  down( silu(a W_gate^T) * (a W_up^T) ).
 
     Weights are in nn.Linear layout [out, in]: gate/up [I, H], down [H, I]
-    (HunyuanImage 3.0 MoE reading, stacked gate/up and down weights).
-
-    With ``a2`` (static FP8 activations, W8A8), the down projection's input
-    h, as the layer's bfloat16 activation tensor (``round_bf16``), is
-    quantised to E4M3 with the static scale a2 and dequantised
-    (``quant_dequant_e4m3``), as an FP8 Linear quantises its input.  With
-    ``amx`` (dynamic MXFP8 activations, W4A8) the same bfloat16 h is
-    quantised per block of 32 along I instead (``quant_dequant_mxfp8``).
+    (HunyuanImage 3.0 MoE reading, stacked gate/up and down weights).  The
+    down projection reads ``expert_h``'s h_in (quantised with ``a2`` or
+    ``amx``, see there).
     """
-    a = np.asarray(a, dtype=np.float64)
-    g = a @ np.asarray(w_gate, dtype=np.float64).T
-    u = a @ np.asarray(w_up, dtype=np.float64).T
-    h = silu(g) * u
-    if a2 is not None:
-        h = quant_dequant_e4m3(round_bf16(h), a2)
-    if amx:
-        h = quant_dequant_mxfp8(round_bf16(h))
-    return h @ np.asarray(w_down, dtype=np.float64).T
+    _, h_in = expert_h(a, w_gate, w_up, a2, amx)
+    return h_in @ np.asarray(w_down, dtype=np.float64).T
 
 
 # --------------------------------------------------------------------------
@@ -465,7 +478,7 @@ def forward_by_expert(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
                       experts: ExpertFn, E: int,
                       shared: Optional[Sequence[np.ndarray]] = None,
                       a8: Optional[Tuple[float, Sequence[float]]] = None,
-                      amx: bool = False) -> np.ndarray:
+                      amx: bool = False, h_hook=None) -> np.ndarray:
     """The same sum as ``forward_given_route``, gathered expert by expert.
 
     out[t] = shared(x_t) + sum_e sum_{j: idx[t, j] = e} weight[t, j] f_e(x_t).
@@ -474,6 +487,14 @@ def forward_by_expert(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
     is built and only one expert's weights need to be held at a time: the
     form used to check layers with tens of thousands of tokens.  Only the
     order of the float64 additions differs from the eager path.
+
+    ``h_hook(e, tok, a, w_gate, w_up, h, h_in) -> h_in`` (optional, e = E
+    for the shared expert, tok its tokens in ascending order, a their input
+    rows) sees each expert's activation before the down projection and
+    returns what the down projection reads: the tests use it where a
+    quantised activation code has two valid answers (a value within
+    rounding of a decision boundary), to continue with the one the GPU took
+    after checking it, as they do with the picks of near-tie tokens.
     """
     x = np.asarray(x, dtype=np.float64)
     idx = np.asarray(idx)
@@ -485,15 +506,22 @@ def forward_by_expert(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
         a2 = [float(v) for v in a8[1]]
     if amx:
         x = quant_dequant_mxfp8(x)
+
+    def expert_out(e, tok, wg, wu, wd):
+        a = x[tok]
+        h, h_in = expert_h(a, wg, wu, a2=a2[e], amx=amx)
+        if h_hook is not None:
+            h_in = h_hook(e, tok, a, wg, wu, h, h_in)
+        return h_in @ np.asarray(wd, dtype=np.float64).T
+
     out = np.zeros((T, H))
     if shared is not None:
-        out += swiglu_expert(x, *shared, a2=a2[E], amx=amx)
+        out += expert_out(E, np.arange(T), *shared)
     if T == 0 or idx.size == 0:
         return out
     for e in np.unique(idx):
         tok, slot = np.nonzero(idx == e)
-        wg, wu, wd = experts(int(e))
-        y = swiglu_expert(x[tok], wg, wu, wd, a2=a2[int(e)], amx=amx)
+        y = expert_out(int(e), tok, *experts(int(e)))
         np.add.at(out, tok, weight[tok, slot][:, None] * y)
     return out
 

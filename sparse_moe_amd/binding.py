@@ -30,7 +30,7 @@ HY3MOE_AFMT_FP8_STATIC = 1
 HY3MOE_AFMT_MXFP8 = 2
 
 HY3MOE_N_STAGES = 6
-ABI_VERSION = 6          # hy3moe_abi_version() of the library this binding matches
+ABI_VERSION = 7          # hy3moe_abi_version() of the library this binding matches
 STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 
 EXPORTED_SYMBOLS = (

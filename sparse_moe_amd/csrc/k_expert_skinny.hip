@@ -226,12 +226,14 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
         store4(dst, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]), swiglu(gv[2], uv[2]),
                swiglu(gv[3], uv[3]));
     } else {
+      // y stays float32 up to the combine's single rounding
+      float *y = static_cast<float *>(a.out);
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         const int n = o.col0 + f * 16 + 4 * cg;
         if (f >= o.nf || n >= a.H) continue;
         const f32x4_t v = acc[f][m] * (f ? s1 : s0);
-        store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
+        store4(y + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
       }
     }
   }

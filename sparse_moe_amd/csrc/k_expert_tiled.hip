@@ -206,12 +206,14 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
                  swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
       }
     } else {
+      // y stays float32 up to the combine's single rounding
+      float *y = static_cast<float *>(a.out);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = col0 + wr_ * 64 + i * 16 + 4 * cg;
         if (n >= a.H) continue;
         const f32x4_t v = acc[i][j] * s0;
-        store4(out + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
+        store4(y + (size_t)trow * a.H + n, v[0], v[1], v[2], v[3]);
       }
     }
   }

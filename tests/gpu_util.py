@@ -155,6 +155,116 @@ def check_output(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "",
     return mx, rel
 
 
+def h_error_bound(a, wg, wu, gemm):
+    """h = SiLU(a wg^T) (a wu^T) in float64, and how far the GPU's float32 h
+    can be from it: the GEMM's error, at most `gemm` times the sum of
+    |products| (1024 ulps (2^-23) for the FP8 and FP4 x FP8 MFMAs, measured
+    in test_gpu_mfma_fp8.py; the bf16 MFMAs are far closer), propagated
+    through SiLU(g) u, plus a few ulps of h for the epilogue's arithmetic."""
+    u32 = 2.0 ** -24
+    gg, uu = a @ wg.T, a @ wu.T
+    h64 = oracle.silu(gg) * uu
+    dg = gemm * (np.abs(a) @ np.abs(wg).T) + 4 * u32 * np.abs(gg)
+    du = gemm * (np.abs(a) @ np.abs(wu).T) + 4 * u32 * np.abs(uu)
+    sg = oracle.sigmoid(gg)
+    dsilu = np.abs(sg * (1 + gg * (1 - sg)))
+    dh = dsilu * np.abs(uu) * dg + np.abs(gg * sg) * du + 8 * u32 * np.abs(h64)
+    return h64, dh
+
+
+def grid_step(v):
+    """Spacing of the E4M3 grid at |v| (2^(e-3) in [2^e, 2^(e+1)), 2^-9 below 2^-6)."""
+    a = np.abs(v)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    return np.exp2(np.maximum(ex - 1, -6) - 3.0)
+
+
+class WorkspaceActivations:
+    """The quantised h a forward left in its workspace, as an ``h_hook`` for
+    ``oracle.forward_by_expert``.
+
+    For each group it reads the GPU's h rows (E4M3 codes, MXFP8 codes and
+    block scales, or the bf16 values of the codes, depending on the path),
+    checks them against the oracle's and returns what the oracle's down
+    projection continues with:
+
+    * the GPU's bf16 h is the oracle's round_bf16(h) wherever no bf16
+      rounding boundary lies within dh of the float64 h (dh: the GEMM and
+      epilogue error bound, ``h_error_bound``); there the GPU's quantised
+      value must equal the oracle's exactly (W8A8: per element; W4A8: per
+      block of 32, whose shared scale every element can move);
+    * elsewhere several codes are valid.  W8A8: the GPU's value must be the
+      oracle's quantisation of a bf16 value within [h - dh, h + dh].  W4A8: the block's values must lie within dh, one bf16
+      rounding and one grid step (or saturation) of the float64 h.  The GPU's
+      values are then taken, as the GPU's picks are for near-tie tokens.
+    """
+
+    def __init__(self, inp: MoEInputs, ws: torch.Tensor, L, codes_path: bool):
+        c = inp.cfg
+        self.E, self.K = c.E, c.K
+        self.a8, self.amx = a8_of(inp), amx_of(inp)
+        self.codes_path = codes_path
+        self.ldh = max(c.I, c.I_shared)
+        R = c.T * c.K + (c.T if c.I_shared else 0)
+        i32 = lambda off, n: ws[off:off + 4 * n].cpu().numpy().view(np.int32)
+        self.offsets = i32(L.offsets, c.E + 2)
+        self.sorted_token = i32(L.sorted_token, R)
+        assert codes_path or not self.amx, "W4A8 layer checks read MXFP8 codes"
+        if self.amx:
+            self.hq = ws[L.hq:L.hq + R * self.ldh].cpu().numpy().reshape(R, self.ldh)
+            self.hs = ws[L.hs:L.hs + R * self.ldh // 32].cpu().numpy().reshape(R, self.ldh // 32)
+        elif self.a8 and codes_path:
+            self.hq = ws[L.h:L.h + R * self.ldh].cpu().numpy().reshape(R, self.ldh)
+        else:       # the bf16 values of the codes
+            bits = ws[L.h:L.h + 2 * R * self.ldh].cpu().numpy().view(np.uint16)
+            self.hv = (bits.astype(np.uint32) << 16).view(np.float32).reshape(R, self.ldh)
+        # the FP8 and FP4 x FP8 MFMAs' accumulation error; bf16 MFMAs far closer
+        self.gemm = (1024 * 2.0 ** -23) if codes_path else 64 * 2.0 ** -24
+        self.n = self.n_amb = 0
+
+    def gpu_values(self, e, r0, r1, Ig):
+        """The GPU's h_in of group e: the MXFP8 values, or the static scale
+        times the E4M3 values (stored as codes or as their bf16 values)."""
+        if self.amx:
+            return oracle.dequant_mxfp8(self.hq[r0:r1, :Ig], self.hs[r0:r1, :Ig // 32])
+        v = (self.hv[r0:r1, :Ig].astype(np.float64) if hasattr(self, "hv")
+             else oracle.fp8_e4m3_value(self.hq[r0:r1, :Ig]))
+        return np.float64(np.float32(self.a8[1][e])) * v
+
+    def __call__(self, e, tok, a, wg, wu, h, h_in):
+        r0, r1 = self.offsets[e], self.offsets[e + 1]
+        assert r1 - r0 == len(tok) and (self.sorted_token[r0:r1] == tok).all(), \
+            f"group {e}: the GPU's rows are not the oracle's tokens"
+        Ig = wg.shape[0]
+        got = self.gpu_values(e, r0, r1, Ig)
+        _, dh = h_error_bound(a, wg, wu, self.gemm)
+        amb = oracle.round_bf16(h - dh) != oracle.round_bf16(h + dh)
+        if self.amx:
+            amb = np.repeat(amb.reshape(len(tok), -1, 32).any(axis=2), 32, axis=1)
+            # the GPU's block scales; a value may be a grid step off, or saturated
+            sc = np.repeat(oracle.e8m0_value(self.hs[r0:r1, :Ig // 32]), 32, axis=1)
+            step = grid_step(np.abs(got) / sc) * sc
+            sat = np.maximum(np.abs(h) + dh - 448.0 * sc, 0.0)
+            allowed = dh + 2.0 ** -8 * np.abs(h) + step + sat
+            ok_amb = np.abs(got - h) <= allowed * (1 + 1e-12)
+        else:
+            a2 = float(self.a8[1][e])
+            # quantisation is monotone: the valid values are the grid values
+            # between those of the interval's ends
+            lo = oracle.quant_dequant_e4m3(oracle.round_bf16(h - dh), a2)
+            hi = oracle.quant_dequant_e4m3(oracle.round_bf16(h + dh), a2)
+            ok_amb = (got >= lo) & (got <= hi)
+        bad = np.argwhere(np.where(amb, ~ok_amb, got != h_in))
+        if bad.size:
+            i, j = bad[0]
+            log(f"  group {e} row {i} col {j}: h={h[i, j]:.9g} dh={dh[i, j]:.3g} "
+                f"gpu={got[i, j]:.9g} oracle={h_in[i, j]:.9g} ambiguous={bool(amb[i, j])}")
+        assert bad.size == 0, f"group {e}: {bad.shape[0]} activation codes off"
+        self.n += h.size
+        self.n_amb += int(amb.sum())
+        return np.where(amb, got, h_in)
+
+
 def expert_fn(inp: MoEInputs):
     """expert(e) -> float64 (gate, up, down), regenerated on every call (no
     cache: the layer-sized checks request each expert once)."""

@@ -17,9 +17,9 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (a8_of, amx_of, check_output, check_route, config_of, expert_fn, log,
-                      oracle_route, out_to_np, route_for_reference, shared_f64, to_torch,
-                      upload_weights, with_act_scales, with_bias_of)
+from gpu_util import (WorkspaceActivations, a8_of, amx_of, check_output, check_route,
+                      config_of, expert_fn, log, oracle_route, out_to_np, route_for_reference,
+                      shared_f64, to_torch, upload_weights, with_act_scales, with_bias_of)
 from synth import CONFIGS, ROUTER_SWEEP_M, MoEInputs
 
 pytestmark = pytest.mark.gpu
@@ -52,11 +52,18 @@ def layer_check(inp, dev, weights, workload_shape=True):
     weights = with_bias_of(inp, weights, dev)
     cfg = config_of(inp)
     x = to_torch(inp.x(), c.dtype, dev)
-    out, idx, w = sm.forward(cfg, x, weights, return_route=True)
+    ws = sm.alloc_workspace(cfg, True, dev)
+    out, idx, w = sm.forward(cfg, x, weights, workspace=ws, return_route=True)
     torch.cuda.synchronize()
     gidx, gw = idx.cpu().numpy(), w.cpu().numpy()
     got = out_to_np(out)
-    del out, x
+    hook = None
+    if a8_of(inp) is not None or amx_of(inp):
+        # quantised activations: the GPU's h codes, checked, where two are valid
+        L = sm.hy3moe_workspace_layout(cfg)
+        codes = L.tile_rows == 256 if a8_of(inp) is not None else L.tile_rows != 128
+        hook = WorkspaceActivations(inp, ws, L, codes)
+    del out, x, ws
     log(f"  oracle route over all {c.T} tokens")
     r = oracle_route(inp)
     info = check_route(gidx, gw, r)
@@ -67,8 +74,11 @@ def layer_check(inp, dev, weights, workload_shape=True):
         f"(mean {counts.mean():.1f}); oracle outputs on all {c.T} tokens")
     t0 = time.time()
     ref = oracle.forward_by_expert(inp.x_f64(), ridx, rw, expert_fn(inp), c.E, shared_f64(inp),
-                                   a8=a8_of(inp), amx=amx_of(inp))
+                                   a8=a8_of(inp), amx=amx_of(inp), h_hook=hook)
     log(f"  oracle layer in {time.time() - t0:.1f}s")
+    if hook is not None:
+        log(f"  activation codes: {hook.n}, {hook.n_amb} within the error bound of a "
+            f"bf16 rounding boundary (GPU's taken after the check)")
     check_output(got, ref, c.dtype, c.name, workload_shape=workload_shape)
     return info
 

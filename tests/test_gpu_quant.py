@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import log
+from gpu_util import grid_step, h_error_bound, log
 
 pytestmark = pytest.mark.gpu
 
@@ -70,30 +70,6 @@ def test_quantize_e4m3_empty_and_errors(dev):
     assert lib.hy3moe_quantize_e4m3(None, 1, 8, scale.data_ptr(), None, None) == -1
     assert lib.hy3moe_quantize_e4m3(None, 7, 0, None, None, None) == -1
     assert lib.hy3moe_quantize_e4m3(None, 1, -1, None, None, None) == -1
-
-
-def _grid_step(v: np.ndarray) -> np.ndarray:
-    """Spacing of the E4M3 grid at |v| (2^(e-3) in [2^e, 2^(e+1)), 2^-9 below 2^-6)."""
-    a = np.abs(v)
-    _, ex = np.frexp(np.where(a > 0, a, 1.0))
-    return np.exp2(np.maximum(ex - 1, -6) - 3.0)
-
-
-def _h_error_bound(a, wg, wu, gemm):
-    """h = SiLU(a wg^T) (a wu^T) in float64, and how far the GPU's float32 h
-    can be from it: the GEMM's error, at most `gemm` times the sum of
-    |products| (1024 ulps (2^-23) for the FP8 and FP4 x FP8 MFMAs, measured
-    in test_gpu_mfma_fp8.py; the bf16 MFMAs are far closer), propagated
-    through SiLU(g) u, plus a few ulps of h for the epilogue's arithmetic."""
-    u32 = 2.0 ** -24
-    gg, uu = a @ wg.T, a @ wu.T
-    h64 = oracle.silu(gg) * uu
-    dg = gemm * (np.abs(a) @ np.abs(wg).T) + 4 * u32 * np.abs(gg)
-    du = gemm * (np.abs(a) @ np.abs(wu).T) + 4 * u32 * np.abs(uu)
-    sg = oracle.sigmoid(gg)
-    dsilu = np.abs(sg * (1 + gg * (1 - sg)))
-    dh = dsilu * np.abs(uu) * dg + np.abs(gg * sg) * du + 8 * u32 * np.abs(h64)
-    return h64, dh
 
 
 @pytest.mark.parametrize("T, E, H, path_rows", [(400, 8, 512, 256), (300, 24, 512, 128),
@@ -159,7 +135,7 @@ def test_w8a8_codes_in_the_workspace(dev, T, E, H, path_rows):
         got = np.stack([values(L.h + (r * ldh) * (1 if codes_path else 2), Ig)
                         for r in range(r0, r1)])
         u32 = 2.0 ** -24
-        h64, dh = _h_error_bound(a, wg, wu, (1024 * 2.0 ** -23) if codes_path else 64 * u32)
+        h64, dh = h_error_bound(a, wg, wu, (1024 * 2.0 ** -23) if codes_path else 64 * u32)
         ref = oracle.fp8_e4m3_value(oracle.quant_e4m3(oracle.round_bf16(h64), a2[g]))
         # the GPU's bf16 h is the oracle's unless a bf16 rounding boundary
         # lies within dh of h (bf16 rounding is monotone)
@@ -171,7 +147,7 @@ def test_w8a8_codes_in_the_workspace(dev, T, E, H, path_rows):
                 f"h={h64[i, j]:.9g} bf16(h)={oracle.round_bf16(h64[i, j]):.9g} "
                 f"got={got[i, j]} ref={ref[i, j]} dh={dh[i, j]:.3g}")
         assert bad.size == 0, f"{bad.shape[0]} codes off beyond the bound in group {g}"
-        big_step = _grid_step(np.maximum(np.abs(got), np.abs(ref)))
+        big_step = grid_step(np.maximum(np.abs(got), np.abs(ref)))
         assert (np.abs(got - ref) <= big_step * (1 + 1e-12)).all()
         n_all += got.size
         n_near += int(near.sum())
@@ -225,7 +201,7 @@ def test_w4a8_codes_in_the_workspace(dev, T, E):
         wg, wu, _ = experts(g) if g < c.E else shared
         Ig = wg.shape[0]
         a = xh[sorted_token[r0:r1]]
-        h64, dh = _h_error_bound(a, wg, wu, 1024 * 2.0 ** -23)
+        h64, dh = h_error_bound(a, wg, wu, 1024 * 2.0 ** -23)
         hb = oracle.round_bf16(h64)
         _, ref_sc = oracle.quant_mxfp8(hb)
         ref = oracle.quant_dequant_mxfp8(hb)
@@ -247,7 +223,7 @@ def test_w4a8_codes_in_the_workspace(dev, T, E):
         # values: |got - h| within the GEMM bound, bf16 rounding of h, and a
         # grid step of the stored code (rounding, or saturation at 448)
         sc = np.repeat(oracle.e8m0_value(got_sc), 32, axis=1)
-        step = _grid_step(np.abs(got) / sc) * sc
+        step = grid_step(np.abs(got) / sc) * sc
         sat = np.maximum(np.abs(h64) + dh - 448.0 * sc, 0.0)
         allowed = dh + 2.0 ** -8 * np.abs(h64) + step + sat
         bad = np.abs(got - h64) > allowed * (1 + 1e-12)
