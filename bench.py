@@ -539,6 +539,22 @@ def ceilings(dev):
         gbs = n * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
         res[f"read_GBs_{blocks}blk"] = gbs
         best = max(best, gbs)
+    L.hy3moe_probe_read_segments.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    for blocks in (512, 1024, 2048, 4096):
+        for depth in (8, 16):
+            out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+            assert L.hy3moe_probe_read_segments(src.data_ptr(), n, blocks, depth,
+                                                out.data_ptr(), s) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                L.hy3moe_probe_read_segments(src.data_ptr(), n, blocks, depth, out.data_ptr(), s)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = n * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+            res[f"read_seg_GBs_{blocks}blk_d{depth}"] = gbs
+            best = max(best, gbs)
     res["read_GBs_best"] = best
     res["mfma_bf16_tflops_best"] = max(v for k, v in res.items() if k.startswith("mfma_bf16"))
     res["mfma_fp8_tflops_best"] = max(v for k, v in res.items() if k.startswith("mfma_fp8"))

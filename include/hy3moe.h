@@ -207,8 +207,8 @@ typedef struct hy3moe_ws_layout {
   int32_t max_tiles;
   int32_t tile_rows;     /* rows per tile of the expert GEMMs for this T       */
   size_t h;              /* dtype [R][I_max]  SwiGLU activations, I_max = max(I, I_shared) */
-  size_t y;              /* float [R][H]      expert outputs before the combine (float32
-                            for every dtype: the combine rounds once, at the output) */
+  size_t y;              /* [R][H] expert outputs before the combine: IEEE fp16 for
+                            bf16 layers (11 significant bits), float32 for fp32 layers */
   size_t w_planes;       /* router weight split into 3 bf16 terms (E padded to a
                             multiple of 16), stored in the order the router GEMM
                             reads its operand fragments; used for bf16 batches of

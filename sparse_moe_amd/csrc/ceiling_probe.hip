@@ -1,7 +1,8 @@
 // Achievable-ceiling probes for the roofline (measurement helpers, not part
 // of the MoE layer): dense bf16 and FP8 MFMA microkernels with register
-// operands only, a 16-byte-per-lane device copy, a 16-byte-per-lane streaming
-// read (the bound of the weight-streaming GEMMs), and one FP8 MFMA per
+// operands only, a 16-byte-per-lane device copy, 16-byte-per-lane streaming
+// reads (grid-strided, and in contiguous per-workgroup segments with 8 or 16
+// loads in flight per lane: the bound of the weight-streaming GEMMs), and one FP8 MFMA per
 // wavefront on given operands (its accumulation error, measured against
 // exact sums by the caller).  Built into libhy3moe_probe.so.
 #include <hip/hip_runtime.h>
@@ -60,6 +61,32 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4 *__restrict__ src
   out[tid] = acc;
 }
 
+// Streaming read the way the weight-streaming GEMMs read weights: each
+// workgroup owns one contiguous segment of the buffer and its threads keep
+// DEPTH 16-byte non-temporal loads in flight, consecutive lanes on
+// consecutive 16 bytes (a wavefront load covers 1 KB), each round moving
+// DEPTH x 4 KB of the segment.  One word per thread is written so that the
+// loads stay.
+template <int DEPTH>
+__global__ __launch_bounds__(256) void read_segment_kernel(const uint4 *__restrict__ src,
+                                                           size_t n16, size_t seg16,
+                                                           uint32_t *__restrict__ out) {
+  const size_t beg = (size_t)blockIdx.x * seg16;
+  const size_t end = beg + seg16 < n16 ? beg + seg16 : n16;
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+  const u32x4_t *s4 = reinterpret_cast<const u32x4_t *>(src);
+  uint32_t acc = 0;
+  size_t i = beg + threadIdx.x;
+  for (; i + (DEPTH - 1) * 256 < end; i += DEPTH * 256) {
+    u32x4_t v[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) v[d] = __builtin_nontemporal_load(s4 + i + d * 256);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) acc ^= v[d][0] ^ v[d][3];
+  }
+  for (; i < end; i += 256) acc ^= src[i].y;
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
 // The same with 16x16x128 E4M3 x E4M3 MFMAs (one per chain per iteration).
 __global__ __launch_bounds__(256) void mfma_fp8_peak_kernel(int iters, float *out) {
   const int lane = threadIdx.x & 63;
@@ -168,6 +195,23 @@ int hy3moe_probe_read(const void *src, size_t bytes, int n_blocks, void *out, vo
   if (!src || !out || (bytes & 15) || n_blocks <= 0) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(read_kernel, dim3(n_blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4 *>(src), bytes / 16, static_cast<uint32_t *>(out));
+  return (int)hipGetLastError();
+}
+
+// Reads `bytes` (multiple of 16) from src as n_blocks contiguous segments,
+// depth (8 or 16) loads in flight per thread; out holds n_blocks x 256 words.
+int hy3moe_probe_read_segments(const void *src, size_t bytes, int n_blocks, int depth, void *out,
+                               void *stream) {
+  if (!src || !out || (bytes & 15) || n_blocks <= 0 || (depth != 8 && depth != 16))
+    return (int)hipErrorInvalidValue;
+  const size_t n16 = bytes / 16, seg16 = (n16 + n_blocks - 1) / n_blocks;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (depth == 8)
+    hipLaunchKernelGGL(read_segment_kernel<8>, dim3(n_blocks), dim3(256), 0, s,
+                       static_cast<const uint4 *>(src), n16, seg16, static_cast<uint32_t *>(out));
+  else
+    hipLaunchKernelGGL(read_segment_kernel<16>, dim3(n_blocks), dim3(256), 0, s,
+                       static_cast<const uint4 *>(src), n16, seg16, static_cast<uint32_t *>(out));
   return (int)hipGetLastError();
 }
 

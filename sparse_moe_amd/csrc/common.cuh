@@ -79,6 +79,31 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c, floa
   *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
 }
 
+// Expert outputs y (the down GEMMs' results before the combine): IEEE fp16
+// (11 significant bits, round to nearest even) for bf16 layers, float32 for
+// float32 layers.
+struct f16_t { uint16_t bits; };
+template <typename T> struct YElem { typedef f16_t type; };
+template <> struct YElem<float> { typedef float type; };
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ void store4(f16_t *p, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = pack_f16x2(a, b);
+  v.y = pack_f16x2(c, d);
+  *reinterpret_cast<uint2 *>(p) = v;
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
 // OCP FP8 E4M3 bytes -> bf16, exact (every E4M3 value is a bf16 value).  The
 // gfx950 scaled conversion with scale 1 decodes two bytes per instruction,
 // low bytes first.

@@ -107,7 +107,7 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
   const int Imax = c->I > c->I_shared ? c->I : c->I_shared;
   const int eb = elt_bytes(c->dtype);
   L->h = off;           off += al((size_t)R * Imax * eb);
-  L->y = off;           off += al((size_t)R * H * 4);   // float32: rounded once, by the combine
+  L->y = off;           off += al((size_t)R * H * eb);  // fp16 (bf16 layers) or float32
   if (c->act_format == HY3MOE_AFMT_FP8_STATIC || c->act_format == HY3MOE_AFMT_MXFP8) {
     L->xq = off;        off += al((size_t)T * H * 2);
   }
@@ -355,8 +355,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   mark();
 
   // 6. combine
-  rc = check_launch(launch_combine(reinterpret_cast<const float *>(ws + L.y), pa.pos_of, weight,
-                                   pa.offsets, T, K, H, E,
+  rc = check_launch(launch_combine(ws + L.y, pa.pos_of, weight, pa.offsets, T, K, H, E,
                                    has_shared ? 1 : 0, out, cfg->dtype, s));
   if (rc) return rc;
   mark();

@@ -70,7 +70,7 @@ struct ExpertArgs {
   const void *w1;         // gate-up: w_up [E][I][H]; down: unused
   const void *ws0;        // shared: gate [Is][H] / down [H][Is]
   const void *ws1;        // shared: up [Is][H]
-  void *out;              // gate-up: h [R][ldh]; down: y [R][H] float32
+  void *out;              // gate-up: h [R][ldh]; down: y [R][H] (fp16 for bf16 layers)
   const int32_t *sorted_token;
   const int32_t *offsets;
   const int32_t *tiles;   // (group, first row) pairs, then the tile count
@@ -120,7 +120,7 @@ hipError_t launch_quant_mxfp8(const void *in, int64_t n, void *q, uint8_t *scale
                               hipStream_t stream);
 
 // Combine ---------------------------------------------------------------------
-hipError_t launch_combine(const float *y, const int32_t *pos_of, const float *weight,
+hipError_t launch_combine(const void *y, const int32_t *pos_of, const float *weight,
                           const int32_t *offsets, int T, int K, int H, int E, int has_shared,
                           void *out, int dtype, hipStream_t stream);
 

@@ -7,9 +7,10 @@
 // [T, K, H], multiplied by the routing weights and summed over K, then the
 // shared branch added.)  Accumulation is fp32 in a fixed order (j = 0..K-1,
 // then the shared row) with one rounding to the output type, so results are
-// deterministic.  y is float32 (the expert GEMMs do not round it), so that
-// rounding is the only one after the down GEMM.  Each thread handles 8
-// output values (bf16) or 4 (float32).
+// deterministic.  y is fp16 for bf16 layers (11 significant bits: the bf16
+// rounding of every routed row's output before the weighted sum pushed the
+// Hy3 prefill layer past its error bound) and float32 for float32 layers.
+// Each thread handles 8 output values (bf16) or 4 (float32).
 #include "common.cuh"
 #include "internal.h"
 
@@ -17,14 +18,19 @@ namespace hy3moe {
 
 namespace {
 
-// 8 consecutive float32 values of a y row (two 16-byte loads).
-template <int V>
-__device__ __forceinline__ void load_y(const float *p, float *v) {
+// One 16-byte load of a y row: 8 fp16 values (bf16 layers) or 4 float32.
+__device__ __forceinline__ void load_y(const f16_t *p, float *v) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int i = 0; i < V; i += 4) {
-    const float4 u = *reinterpret_cast<const float4 *>(p + i);
-    v[i] = u.x; v[i + 1] = u.y; v[i + 2] = u.z; v[i + 3] = u.w;
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = f16_lo(w[i]);
+    v[2 * i + 1] = f16_hi(w[i]);
   }
+}
+__device__ __forceinline__ void load_y(const float *p, float *v) {
+  const float4 u = *reinterpret_cast<const float4 *>(p);
+  v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
 }
 
 template <typename T>
@@ -44,7 +50,7 @@ __device__ __forceinline__ void store_vec<float>(float *p, const float *v) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
+__global__ __launch_bounds__(256) void combine_kernel(const typename YElem<T>::type *__restrict__ y,
                                                       const int32_t *__restrict__ pos_of,
                                                       const float *__restrict__ weight,
                                                       const int32_t *__restrict__ offsets, int K,
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
       const int j = j0 + jj < K ? j0 + jj : K - 1;
       const int p = pos_of[(size_t)t * K + j];
       w[jj] = weight[(size_t)t * K + j];
-      load_y<V>(y + (size_t)p * H + n, v[jj]);
+      load_y(y + (size_t)p * H + n, v[jj]);
     }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   }
   if (has_shared) {
     float v[V];
-    load_y<V>(y + (size_t)(offsets[E] + t) * H + n, v);
+    load_y(y + (size_t)(offsets[E] + t) * H + n, v);
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] += v[i];
   }
@@ -86,18 +92,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float *y, const int32_t *pos_of, const float *weight,
+hipError_t launch_combine(const void *y, const int32_t *pos_of, const float *weight,
                           const int32_t *offsets, int T, int K, int H, int E, int has_shared,
                           void *out, int dtype, hipStream_t stream) {
   if (dtype == DT_F32) {
     dim3 grid(T, (H / 4 + 255) / 256);
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, stream,
-                       y, pos_of, weight, offsets, K, H, E, has_shared,
+                       static_cast<const float *>(y), pos_of, weight, offsets, K, H, E, has_shared,
                        static_cast<float *>(out));
   } else {
     dim3 grid(T, (H / 8 + 255) / 256);
     hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, stream,
-                       y, pos_of, weight, offsets, K, H, E, has_shared,
+                       static_cast<const f16_t *>(y), pos_of, weight, offsets, K, H, E, has_shared,
                        static_cast<bf16_t *>(out));
   }
   return hipGetLastError();

@@ -244,53 +244,6 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
   const int lane = tid & 63, wave = tid >> 6;
   const int wr_ = wave >> 2, wt_ = wave & 3, r16 = lane & 15, cg = lane >> 4;
   T *out = static_cast<T *>(a.out);
-  if constexpr (!GATE_UP && sizeof(T) == 2) {
-    // y stays float32 up to the combine's single rounding.  The tile (256
-    // token rows x 256 columns, 256 KB) goes through the 128 KB of LDS in two
-    // passes of 128 rows; in pass h every wavefront stages its accumulator
-    // rows j = 2h, 2h + 1 (so half its accumulators are free after the first
-    // pass): staged row rr = 32 wt_ + 16 (j - 2h) + r16 is token row
-    // 64 wt_ + 16 j + r16.  Float32 rows of 64 16-byte chunks, the chunk
-    // index XOR (row & 15) << 2; each wavefront then stores one whole 1 KB
-    // row per instruction.
-    float *y = static_cast<float *>(a.out);
-    char *stg = reinterpret_cast<char *>(lds);
-    constexpr int YC = BW / 4;   // 16-byte chunks per float32 row
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * half + jj;
-        const int r = wt_ * 32 + jj * 16 + r16;   // staged row
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int ch = (wr_ * 128 + i * 16 + 4 * cg) >> 2;
-          const f32x4_t v4 = acc[i][j] * s0;
-          *reinterpret_cast<float4 *>(stg + (size_t)(r * YC + (ch ^ ((r & 15) << 2))) * 16) =
-              make_float4(v4[0], v4[1], v4[2], v4[3]);
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < 128 * YC / 512; ++m) {
-        const int q = tid + 512 * m;
-        const int r = q / YC, ch = q % YC;
-        const int c = t.col0 + ch * 4;
-        const int grow = t.row0 + (r >> 5) * 64 + half * 32 + (r & 31);
-        if (grow < t.grp_end && c < a.H) {
-          const uint4 v = lds[r * YC + (ch ^ ((r & 15) << 2))];
-          uint4 *dst = reinterpret_cast<uint4 *>(y + (size_t)grow * a.H + c);
-          // written once, read by the combine: non-temporal
-          __builtin_nontemporal_store(v.x, &dst->x);
-          __builtin_nontemporal_store(v.y, &dst->y);
-          __builtin_nontemporal_store(v.z, &dst->z);
-          __builtin_nontemporal_store(v.w, &dst->w);
-        }
-      }
-      if (half == 0) __syncthreads();   // the first half's LDS reads are done
-    }
-    return;
-  }
   if constexpr (sizeof(T) == 2) {
     // Through LDS (free after the loop's last barrier): each lane writes its
     // 4-column pieces into bf16 token rows (16-byte chunks swizzled by row),
@@ -317,13 +270,14 @@ __device__ __forceinline__ void big_epilogue(const ExpertArgs &a, const BigTile 
           *reinterpret_cast<uint2 *>(row + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = v;
         }
       } else {
+        // y: fp16 (11 significant bits), rounded once more by the combine
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int c = wr_ * 128 + i * 16 + 4 * cg;
           const f32x4_t v4 = acc[i][j] * s0;
           uint2 v;
-          v.x = pack_bf16x2(v4[0], v4[1]);
-          v.y = pack_bf16x2(v4[2], v4[3]);
+          v.x = pack_f16x2(v4[0], v4[1]);
+          v.y = pack_f16x2(v4[2], v4[3]);
           *reinterpret_cast<uint2 *>(row + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2) = v;
         }
       }

@@ -226,8 +226,8 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
         store4(dst, swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]), swiglu(gv[2], uv[2]),
                swiglu(gv[3], uv[3]));
     } else {
-      // y stays float32 up to the combine's single rounding
-      float *y = static_cast<float *>(a.out);
+      // y: fp16 for bf16 layers (float32 for float32 layers)
+      typename YElem<T>::type *y = static_cast<typename YElem<T>::type *>(a.out);
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         const int n = o.col0 + f * 16 + 4 * cg;

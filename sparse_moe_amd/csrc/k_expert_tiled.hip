@@ -206,8 +206,8 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
                  swiglu(gv[2], uv[2]), swiglu(gv[3], uv[3]));
       }
     } else {
-      // y stays float32 up to the combine's single rounding
-      float *y = static_cast<float *>(a.out);
+      // y: fp16 for bf16 layers (float32 for float32 layers)
+      typename YElem<T>::type *y = static_cast<typename YElem<T>::type *>(a.out);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = col0 + wr_ * 64 + i * 16 + 4 * cg;

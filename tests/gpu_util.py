@@ -17,12 +17,14 @@ Comparison rules
   picks with the oracle's weights for them (``route_for_reference``), never
   the GPU's weights.  bf16 activations/weights at the Hy3 / HunyuanImage
   workload shapes: max-abs error <= 2e-2 and rel-L2 <= 5e-3 against the
-  float64 oracle.  Other synthetic shapes can have larger outputs, where one
-  bf16 rounding of the output alone exceeds 2e-2 (|out| >= 4 has a half-ulp
-  of 1/64), so there each element must satisfy
-  |got - ref| <= 2e-2 + 2^-8 |ref| (the stated bound plus one bf16 output
-  rounding at that element's magnitude); rel-L2 stays 5e-3.
-  fp32: max-abs <= 1e-4 and rel-L2 <= 1e-5.
+  float64 oracle.  Elsewhere (small synthetic shapes, quantised weights) the
+  bound is derived from the two roundings that remain in the bf16 path: h
+  rounded to bf16 and carried through the down projection, an error that
+  scales with the layer's output scale, and the output's own bf16 rounding,
+  at most 2^-8 |ref| at each element.  The 2e-2 is stated for the Hy3 layer,
+  whose float64 output has RMS 0.844 (Hy3 decode batch), so each element
+  must satisfy |got - ref| <= 2e-2 max(1, rms(ref) / 0.844) + 2^-8 |ref|;
+  rel-L2 stays 5e-3.  fp32: max-abs <= 1e-4 and rel-L2 <= 1e-5.
 """
 from __future__ import annotations
 
@@ -38,6 +40,7 @@ from synth import MoEInputs
 
 MARGIN = 1e-6
 TOL = {"bf16": (2e-2, 5e-3), "f32": (1e-4, 1e-5)}
+HY3_OUT_RMS = 0.844     # RMS of the Hy3 layer's float64 output (decode batch)
 
 
 def log(msg: str) -> None:
@@ -139,15 +142,19 @@ def output_errors(got: np.ndarray, ref: np.ndarray) -> tuple:
 def check_output(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "",
                  workload_shape: bool = False) -> tuple:
     """workload_shape=True: one of the named workloads, the stated bf16 bound.
-    Otherwise (bf16) each element is held to 2e-2 + 2^-8 |ref|."""
+    Otherwise (bf16) each element is held to 2e-2 max(1, rms(ref)/0.844) +
+    2^-8 |ref| (module docstring)."""
     mx, rel = output_errors(got, ref)
     tmax, trel = TOL[dtype]
     top = float(np.abs(ref).max()) if ref.size else 0.0
     if dtype == "bf16" and not workload_shape and ref.size:
-        excess = np.abs(got.astype(np.float64) - ref) - (tmax + 2.0 ** -8 * np.abs(ref))
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        absb = tmax * max(1.0, rms / HY3_OUT_RMS)
+        excess = np.abs(got.astype(np.float64) - ref) - (absb + 2.0 ** -8 * np.abs(ref))
         worst = float(excess.max())
-        log(f"  {what} max_abs={mx:.3e} rel_l2={rel:.3e} (per element 2e-2 + 2^-8|ref|: "
-            f"worst margin {-worst:.3e}; rel tol {trel:g}; max|ref| {top:.3g})")
+        log(f"  {what} max_abs={mx:.3e} rel_l2={rel:.3e} (per element {absb:.3g} + "
+            f"2^-8|ref|: worst margin {-worst:.3e}; rel tol {trel:g}; rms {rms:.3g}, "
+            f"max|ref| {top:.3g})")
         assert worst <= 0 and rel <= trel, f"{what}: max_abs {mx:.3e} rel_l2 {rel:.3e}"
         return mx, rel
     log(f"  {what} max_abs={mx:.3e} rel_l2={rel:.3e} (tol {tmax:g}/{trel:g}; max|ref| {top:.3g})")
@@ -188,13 +195,14 @@ class WorkspaceActivations:
     checks them against the oracle's and returns what the oracle's down
     projection continues with:
 
-    * the GPU's bf16 h is the oracle's round_bf16(h) wherever no bf16
-      rounding boundary lies within dh of the float64 h (dh: the GEMM and
-      epilogue error bound, ``h_error_bound``); there the GPU's quantised
-      value must equal the oracle's exactly (W8A8: per element; W4A8: per
-      block of 32, whose shared scale every element can move);
-    * elsewhere several codes are valid.  W8A8: the GPU's value must be the
-      oracle's quantisation of a bf16 value within [h - dh, h + dh].  W4A8: the block's values must lie within dh, one bf16
+    * the GPU's float32 h lies within dh of the float64 h (dh: the GEMM and
+      epilogue error bound, ``h_error_bound``).  W8A8: bf16 rounding and the
+      quantisation are monotone, so the GPU's code must lie between the
+      codes of h - dh and h + dh, and equal the oracle's where those agree.
+      W4A8: per block of 32 (whose shared scale every element can move), the
+      GPU's values must equal the oracle's where no element's bf16 value is
+      in doubt (no bf16 rounding boundary within dh of h);
+    * elsewhere several codes are valid.  W4A8: the block's values must lie within dh, one bf16
       rounding and one grid step (or saturation) of the float64 h.  The GPU's
       values are then taken, as the GPU's picks are for near-tie tokens.
     """
@@ -209,8 +217,7 @@ class WorkspaceActivations:
         i32 = lambda off, n: ws[off:off + 4 * n].cpu().numpy().view(np.int32)
         self.offsets = i32(L.offsets, c.E + 2)
         self.sorted_token = i32(L.sorted_token, R)
-        assert codes_path or not self.amx, "W4A8 layer checks read MXFP8 codes"
-        if self.amx:
+        if self.amx and codes_path:
             self.hq = ws[L.hq:L.hq + R * self.ldh].cpu().numpy().reshape(R, self.ldh)
             self.hs = ws[L.hs:L.hs + R * self.ldh // 32].cpu().numpy().reshape(R, self.ldh // 32)
         elif self.a8 and codes_path:
@@ -225,7 +232,9 @@ class WorkspaceActivations:
     def gpu_values(self, e, r0, r1, Ig):
         """The GPU's h_in of group e: the MXFP8 values, or the static scale
         times the E4M3 values (stored as codes or as their bf16 values)."""
-        if self.amx:
+        if self.amx:   # codes and block scales, or their values in bf16 (exact)
+            if hasattr(self, "hv"):
+                return self.hv[r0:r1, :Ig].astype(np.float64)
             return oracle.dequant_mxfp8(self.hq[r0:r1, :Ig], self.hs[r0:r1, :Ig // 32])
         v = (self.hv[r0:r1, :Ig].astype(np.float64) if hasattr(self, "hv")
              else oracle.fp8_e4m3_value(self.hq[r0:r1, :Ig]))
@@ -238,21 +247,27 @@ class WorkspaceActivations:
         Ig = wg.shape[0]
         got = self.gpu_values(e, r0, r1, Ig)
         _, dh = h_error_bound(a, wg, wu, self.gemm)
-        amb = oracle.round_bf16(h - dh) != oracle.round_bf16(h + dh)
         if self.amx:
+            amb = oracle.round_bf16(h - dh) != oracle.round_bf16(h + dh)
             amb = np.repeat(amb.reshape(len(tok), -1, 32).any(axis=2), 32, axis=1)
-            # the GPU's block scales; a value may be a grid step off, or saturated
-            sc = np.repeat(oracle.e8m0_value(self.hs[r0:r1, :Ig // 32]), 32, axis=1)
+            # the GPU's block scales (its largest code is in [256, 448]: the
+            # scale is 2^(floor(log2 max|value|) - 8)); a value may be a grid
+            # step off, or saturated
+            bmax = np.abs(got).reshape(len(tok), -1, 32).max(axis=2)
+            _, ex = np.frexp(np.where(bmax > 0, bmax, 1.0))
+            sc = np.repeat(np.where(bmax > 0, np.exp2(ex - 1.0 - 8.0), 2.0 ** -127), 32, axis=1)
             step = grid_step(np.abs(got) / sc) * sc
             sat = np.maximum(np.abs(h) + dh - 448.0 * sc, 0.0)
             allowed = dh + 2.0 ** -8 * np.abs(h) + step + sat
             ok_amb = np.abs(got - h) <= allowed * (1 + 1e-12)
         else:
             a2 = float(self.a8[1][e])
-            # quantisation is monotone: the valid values are the grid values
-            # between those of the interval's ends
+            # bf16 rounding and the quantisation are monotone: the valid
+            # values are the grid values between those of the interval's
+            # ends, and the code is ambiguous only where those differ
             lo = oracle.quant_dequant_e4m3(oracle.round_bf16(h - dh), a2)
             hi = oracle.quant_dequant_e4m3(oracle.round_bf16(h + dh), a2)
+            amb = lo != hi
             ok_amb = (got >= lo) & (got <= hi)
         bad = np.argwhere(np.where(amb, ~ok_amb, got != h_in))
         if bad.size:

@@ -91,7 +91,7 @@ def test_workspace_layout_is_consistent(lib, name):
     assert len(set(offs)) == len(offs)
     R = c.T * c.K + (c.T if c.I_shared else 0)
     eb = 2 if c.dtype == "bf16" else 4
-    assert L.total - L.y >= R * c.H * 4          # y is float32 for every dtype
+    assert L.total - L.y >= R * c.H * eb         # y: fp16 (bf16 layers) or float32
     assert L.y - L.h >= R * max(c.I, c.I_shared) * eb
     assert L.max_tiles >= (R + L.tile_rows - 1) // L.tile_rows
     assert L.tile_rows >= min(c.T, 16)
@@ -360,3 +360,4 @@ def test_attention_binding_rejects_a_plan_for_another_batch(lib):
     bad.tasks[0, 0] = 5                  # a task naming request 5
     with pytest.raises(ValueError):
         sm.attn_decode(q, k, k, [300, 500], bad)
+

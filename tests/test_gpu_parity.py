@@ -14,9 +14,9 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (MARGIN, a8_of, amx_of, check_output, check_route, config_of, expert_cache, log,
-                      oracle_route, out_to_np, route_for_reference, shared_f64, to_torch,
-                      upload_weights)
+from gpu_util import (MARGIN, WorkspaceActivations, a8_of, amx_of, check_output, check_route,
+                      config_of, expert_cache, log, oracle_route, out_to_np,
+                      route_for_reference, shared_f64, to_torch, upload_weights)
 from synth import CONFIGS, MoEInputs, random_small
 
 pytestmark = pytest.mark.gpu
@@ -56,10 +56,24 @@ def full_check(inp, dev, **kw):
     c = inp.cfg
     log(f"case {c.name}: T={c.T} H={c.H} E={c.E} K={c.K} I={c.I} Is={c.I_shared} "
         f"{c.dtype} mode={c.route_mode}")
+    quant_act = a8_of(inp) is not None or amx_of(inp)
+    if quant_act and kw.get("workspace") is None:
+        kw["workspace"] = sm.alloc_workspace(config_of(inp), True, dev)
     out, gidx, gw = run_gpu(inp, dev, **kw)
     r = oracle_route(inp)
     info = check_route(gidx, gw, r)
-    ref = reference(inp, r, gidx, gw)
+    if quant_act:
+        # activation codes with two valid answers: the GPU's, checked
+        L = sm.hy3moe_workspace_layout(config_of(inp))
+        codes = L.tile_rows == 256 if a8_of(inp) is not None else L.tile_rows != 128
+        hook = WorkspaceActivations(inp, kw["workspace"], L, codes)
+        ridx, rw = route_for_reference(r, gidx)
+        ref = oracle.forward_by_expert(inp.x_f64(), ridx, rw, expert_cache(inp), c.E,
+                                       shared_f64(inp), a8=a8_of(inp), amx=amx_of(inp),
+                                       h_hook=hook)
+        log(f"  activation codes {hook.n}, {hook.n_amb} at an ambiguous decision")
+    else:
+        ref = reference(inp, r, gidx, gw)
     check_output(out_to_np(out), ref, c.dtype, c.name)
     return out, gidx, gw, r, info
 
