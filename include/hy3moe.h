@@ -56,6 +56,8 @@ extern "C" {
 #define HY3MOE_ERR_WORKSPACE   -3  /* workspace smaller than hy3moe_workspace_bytes()   */
 #define HY3MOE_ERR_ALIGN       -4  /* a pointer is not 16-byte aligned                  */
 #define HY3MOE_ERR_HIP         -5  /* a kernel launch failed (hipGetLastError)          */
+#define HY3MOE_ERR_SCRATCH     -6  /* hy3moe_forward_static: the batch's workspace would
+                                      exceed HY3MOE_STATIC_SCRATCH_BYTES               */
 
 /* ---- enums ---- */
 #define HY3MOE_F32  0
@@ -279,6 +281,26 @@ int hy3moe_forward_timed(const hy3moe_config *cfg, const void *x, const hy3moe_w
                          void *out, int32_t *idx_out, float *weight_out,
                          void *workspace, size_t ws_bytes, void *stream,
                          void *const *stage_events);
+
+/* hy3moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Identical results to hy3moe_forward; the workspace is a static device
+ * array of HY3MOE_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on
+ * each GPU it runs on until the process ends (its address is looked up on
+ * the first call on a device), so the call itself allocates nothing.
+ *   x, w, out, idx_out, weight_out, stream: as hy3moe_forward.
+ * Batches whose forward workspace (hy3moe_workspace_bytes(cfg, 1)) exceeds
+ * the array return HY3MOE_ERR_SCRATCH before anything is launched (the Hy3
+ * layer fits up to about 350 tokens: decode batches).  Nothing in the array
+ * needs clearing between calls: every kernel writes what a later one reads.
+ * All calls on one GPU share its array: calls that overlap on a GPU (other
+ * streams, other threads) race and give undefined results; the caller must
+ * order them. */
+#define HY3MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int hy3moe_forward_static(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
+                          void *out, int32_t *idx_out, float *weight_out, void *stream);
+/* == HY3MOE_STATIC_SCRATCH_BYTES */
+size_t hy3moe_static_scratch_bytes(void);
 
 /* Static FP8 activation quantisation on its own: q[i] = E4M3(x[i] / *scale)
  * for i < n, as act_format FP8_STATIC quantises the experts' input (the CANN

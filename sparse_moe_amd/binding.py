@@ -36,8 +36,9 @@ STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 EXPORTED_SYMBOLS = (
     "hy3moe_abi_version", "hy3moe_strerror", "hy3moe_workspace_bytes",
     "hy3moe_workspace_layout", "hy3moe_route", "hy3moe_forward", "hy3moe_forward_timed",
-    "hy3moe_quantize_e4m3",
+    "hy3moe_quantize_e4m3", "hy3moe_forward_static", "hy3moe_static_scratch_bytes",
 )
+HY3MOE_ERR_SCRATCH = -6
 
 
 class hy3moe_config(ctypes.Structure):
@@ -122,6 +123,12 @@ def load() -> ctypes.CDLL:
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p,
                                        ctypes.POINTER(ctypes.c_void_p)]
+    L.hy3moe_forward_static.restype = ctypes.c_int
+    L.hy3moe_forward_static.argtypes = [ctypes.POINTER(hy3moe_config), ctypes.c_void_p,
+                                        ctypes.POINTER(hy3moe_weights), ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.hy3moe_static_scratch_bytes.restype = ctypes.c_size_t
+    L.hy3moe_static_scratch_bytes.argtypes = []
     L.hy3moe_quantize_e4m3.restype = ctypes.c_int
     L.hy3moe_quantize_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -245,6 +252,20 @@ def hy3moe_forward(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str, torch
                                workspace.numel(), _stream(stream))
     if rc != HY3MOE_OK:
         raise Hy3MoEError(rc, "hy3moe_forward")
+
+
+def hy3moe_forward_static(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str, torch.Tensor],
+                          out: torch.Tensor, idx_out: Optional[torch.Tensor] = None,
+                          weight_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """C ABI hy3moe_forward_static: hy3moe_forward with the library's static
+    per-GPU scratch instead of a caller workspace (allocates nothing)."""
+    ts = [weights.get(n) for n in WEIGHT_NAMES]
+    _check_dev(x, out, idx_out, weight_out, *ts)
+    w = hy3moe_weights(*[_ptr(t) for t in ts])
+    rc = load().hy3moe_forward_static(ctypes.byref(cfg), _ptr(x), ctypes.byref(w), _ptr(out),
+                                      _ptr(idx_out), _ptr(weight_out), _stream(stream))
+    if rc != HY3MOE_OK:
+        raise Hy3MoEError(rc, "hy3moe_forward_static")
 
 
 def hy3moe_forward_timed(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str, torch.Tensor],

@@ -7,6 +7,8 @@
 //   -> grouped gate-up + SwiGLU -> grouped down -> weighted combine.
 #include <string.h>
 
+#include <mutex>
+
 #include "hy3moe.h"
 #include "internal.h"
 
@@ -138,6 +140,9 @@ const char *hy3moe_strerror(int code) {
     case HY3MOE_ERR_WORKSPACE: return "workspace too small";
     case HY3MOE_ERR_ALIGN: return "pointer not aligned (16 bytes for tensors, 4 for idx/weight/bias)";
     case HY3MOE_ERR_HIP: return "HIP kernel launch failed";
+    case HY3MOE_ERR_SCRATCH:
+      return "batch needs more scratch than hy3moe_forward_static's static array holds "
+             "(use hy3moe_forward with a workspace)";
     default: return "unknown error code";
   }
 }
@@ -361,6 +366,59 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   mark();
   return HY3MOE_OK;
 }
+
+}  // extern "C"
+
+// Scratch of hy3moe_forward_static: one array per GPU, resident until the
+// process ends.  Its name is a host-side stand-in in host code; the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+static __device__ __align__(256) uint8_t scratch[HY3MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, or null
+
+// The current device's scratch address (looked up on its first use), or null
+// with *rc set.
+void *static_scratch(int *rc) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = HY3MOE_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *rc = HY3MOE_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int hy3moe_forward_static(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
+                          void *out, int32_t *idx_out, float *weight_out, void *stream) {
+  const int vrc = validate_cfg(cfg);
+  if (vrc != HY3MOE_OK) return vrc;
+  if (cfg->T == 0) return HY3MOE_OK;
+  hy3moe_ws_layout L;
+  compute_layout(cfg, 1, &L);
+  if (L.total > (size_t)HY3MOE_STATIC_SCRATCH_BYTES) return HY3MOE_ERR_SCRATCH;
+  int rc = HY3MOE_OK;
+  void *ws = static_scratch(&rc);
+  if (!ws) return rc;
+  return forward_impl(cfg, x, w, out, idx_out, weight_out, ws, HY3MOE_STATIC_SCRATCH_BYTES,
+                      stream, nullptr);
+}
+
+size_t hy3moe_static_scratch_bytes(void) { return HY3MOE_STATIC_SCRATCH_BYTES; }
 
 int hy3moe_quantize_e4m3(const void *x, int32_t dtype, int64_t n, const float *scale, uint8_t *q,
                          void *stream) {

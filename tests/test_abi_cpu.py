@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_strerror(lib):
     assert lib.hy3moe_abi_version() == b.ABI_VERSION == 7
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
 
@@ -361,3 +361,24 @@ def test_attention_binding_rejects_a_plan_for_another_batch(lib):
     with pytest.raises(ValueError):
         sm.attn_decode(q, k, k, [300, 500], bad)
 
+
+def test_static_forward_rejects_batches_beyond_its_scratch(lib):
+    """hy3moe_forward_static validates on the host before touching a device:
+    a batch whose workspace exceeds the static array is rejected, and so is a
+    bad configuration; T = 0 is a no-op."""
+    assert lib.hy3moe_static_scratch_bytes() == 64 << 20
+    w = sm.hy3moe_weights()
+    big = sm.make_config(4096, 4096, 192, 8, 1536, 1536, "bf16")
+    assert sm.hy3moe_workspace_bytes(big) > lib.hy3moe_static_scratch_bytes()
+    assert lib.hy3moe_forward_static(ctypes.byref(big), None, ctypes.byref(w), None, None, None,
+                                     None) == sm.HY3MOE_ERR_SCRATCH
+    bad = sm.make_config(16, 4096, 192, 8, 1536, 1536, "bf16")
+    bad.K = 0
+    assert lib.hy3moe_forward_static(ctypes.byref(bad), None, ctypes.byref(w), None, None, None,
+                                     None) == -1
+    empty = sm.make_config(0, 4096, 192, 8, 1536, 1536, "bf16")
+    assert lib.hy3moe_forward_static(ctypes.byref(empty), None, ctypes.byref(w), None, None, None,
+                                     None) == 0
+    # the Hy3 decode batch fits
+    dec = sm.make_config(16, 4096, 192, 8, 1536, 1536, "bf16")
+    assert sm.hy3moe_workspace_bytes(dec) <= lib.hy3moe_static_scratch_bytes()
