@@ -462,6 +462,23 @@ def router_sweep(args, dev):
             rows.append({"M": M, "router": name, "us_per_call": us,
                          "GB_s": nbytes / us / 1e3, "TFLOP_s": 2.0 * M * c.H * c.E / us / 1e6})
             log(f"[router] M={M:5d} {name:34s} {us:8.2f} us")
+            if sm.hy3moe_workspace_layout(cfg).w_planes:
+                # the same gate on the weight's offline split (hy3moe_router_split):
+                # no per-call split kernel, planes read as they are
+                planes = sm.router_split(wr, prec)
+                for _ in range(args.warmup):
+                    sm.hy3moe_route_planes(cfg, x, wr, planes, bias, idx, wgt, ws)
+                e0.record()
+                for _ in range(args.steps):
+                    sm.hy3moe_route_planes(cfg, x, wr, planes, bias, idx, wgt, ws)
+                e1.record()
+                torch.cuda.synchronize()
+                us2 = e0.elapsed_time(e1) * 1e3 / args.steps
+                pb = planes.numel() + M * c.H * 2
+                rows.append({"M": M, "router": name + ", offline planes", "us_per_call": us2,
+                             "GB_s": pb / us2 / 1e3,
+                             "TFLOP_s": 2.0 * M * c.H * c.E / us2 / 1e6})
+                log(f"[router] M={M:5d} {name + ', offline planes':34s} {us2:8.2f} us")
     return {"router_sweep": rows, "config": {"workload": c.name, "H": c.H, "E": c.E, "K": c.K},
             "steps": args.steps, "note": "gate only: router GEMM + score/select"}
 

@@ -187,6 +187,11 @@ typedef struct hy3moe_weights {
   const uint8_t *ws_gate_mx;
   const uint8_t *ws_up_mx;
   const uint8_t *ws_down_mx;
+  /* Optional: the router weight split offline by hy3moe_router_split with
+   * this layer's E, H and router_prec (NULL: split per call).  Used by bf16
+   * batches of 1024 tokens or more, which run the router GEMM on bf16 planes;
+   * smaller batches split w_router in registers and ignore it. */
+  const void *w_router_planes;
 } hy3moe_weights;
 
 /* Byte offsets of the intermediate buffers inside a forward workspace (for
@@ -247,6 +252,31 @@ int hy3moe_workspace_layout(const hy3moe_config *cfg, hy3moe_ws_layout *out);
 int hy3moe_route(const hy3moe_config *cfg, const void *x, const float *w_router,
                  const float *expert_bias, int32_t *idx, float *weight,
                  void *workspace, size_t ws_bytes, void *stream);
+
+/* The offline split of the router weight (Hy3 Preview inference case,
+ * section 2 "Router GEMM: dual BF16": the fp32 weight is split once, offline,
+ * into bf16 planes, so that no call re-splits it or writes and re-reads a
+ * split copy).  router_prec HY3MOE_ROUTER_FP32: the exact three-term split
+ * (hi, mid, lo, summing to the weight exactly); HY3MOE_ROUTER_SPLIT2_BF16:
+ * the page's two terms hi + lo/256.  The planes are stored in the order the
+ * router GEMM reads its operand fragments (an internal layout: pass them
+ * back unchanged as hy3moe_weights.w_router_planes or to
+ * hy3moe_route_planes, with the same E, H and router_prec).
+ *   w_router [E, H] fp32 device, 16-byte aligned; E 1..256, H % 64 == 0
+ *   planes   device out, hy3moe_router_planes_bytes(E, H, router_prec) bytes,
+ *            16-byte aligned
+ * Errors: HY3MOE_ERR_INVALID (bad E, H, router_prec, null pointer),
+ * HY3MOE_ERR_UNSUPPORTED (H % 64 or H > 65536), HY3MOE_ERR_WORKSPACE
+ * (planes_bytes too small), HY3MOE_ERR_ALIGN; launched on `stream`. */
+size_t hy3moe_router_planes_bytes(int32_t E, int32_t H, int32_t router_prec);
+int hy3moe_router_split(const float *w_router, int32_t E, int32_t H, int32_t router_prec,
+                        void *planes, size_t planes_bytes, void *stream);
+
+/* hy3moe_route with the router weight's offline split (w_router_planes from
+ * hy3moe_router_split, or NULL): identical results to hy3moe_route. */
+int hy3moe_route_planes(const hy3moe_config *cfg, const void *x, const float *w_router,
+                        const void *w_router_planes, const float *expert_bias, int32_t *idx,
+                        float *weight, void *workspace, size_t ws_bytes, void *stream);
 
 /* The whole layer: gate, token->expert permutation, grouped SwiGLU experts
  * (routed + shared), and the weighted top-K combine back to token order.

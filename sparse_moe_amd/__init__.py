@@ -3,6 +3,7 @@
 from .binding import (EXPORTED_SYMBOLS, HY3MOE_BF16, HY3MOE_F32,
                       HY3MOE_N_STAGES, HY3MOE_ROUTE_SIGMOID_BIAS, HY3MOE_ROUTE_SOFTMAX,
                       STAGE_NAMES, HY3MOE_ERR_SCRATCH, hy3moe_forward_static,
+                      hy3moe_route_planes, router_split,
                       hy3moe_forward_timed,
                       HY3MOE_ROUTER_FP32, HY3MOE_ROUTER_SPLIT2_BF16, Hy3MoEError,
                       alloc_workspace, forward, hy3moe_config, hy3moe_forward,
@@ -15,6 +16,7 @@ from .binding import ATTN_EXPORTED_SYMBOLS, ATTN_TILE, AttnPlan, attn_decode, at
 __all__ = [
     "EXPORTED_SYMBOLS", "HY3MOE_BF16", "HY3MOE_F32", "HY3MOE_N_STAGES", "STAGE_NAMES",
     "hy3moe_forward_timed", "HY3MOE_ERR_SCRATCH", "hy3moe_forward_static",
+    "hy3moe_route_planes", "router_split",
     "HY3MOE_ROUTE_SIGMOID_BIAS",
     "HY3MOE_ROUTE_SOFTMAX", "HY3MOE_ROUTER_FP32", "HY3MOE_ROUTER_SPLIT2_BF16",
     "Hy3MoEError", "alloc_workspace", "forward", "hy3moe_config", "hy3moe_forward",

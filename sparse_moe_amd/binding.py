@@ -30,13 +30,14 @@ HY3MOE_AFMT_FP8_STATIC = 1
 HY3MOE_AFMT_MXFP8 = 2
 
 HY3MOE_N_STAGES = 6
-ABI_VERSION = 7          # hy3moe_abi_version() of the library this binding matches
+ABI_VERSION = 8          # hy3moe_abi_version() of the library this binding matches
 STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 
 EXPORTED_SYMBOLS = (
     "hy3moe_abi_version", "hy3moe_strerror", "hy3moe_workspace_bytes",
     "hy3moe_workspace_layout", "hy3moe_route", "hy3moe_forward", "hy3moe_forward_timed",
     "hy3moe_quantize_e4m3", "hy3moe_forward_static", "hy3moe_static_scratch_bytes",
+    "hy3moe_router_planes_bytes", "hy3moe_router_split", "hy3moe_route_planes",
 )
 HY3MOE_ERR_SCRATCH = -6
 
@@ -55,7 +56,7 @@ class hy3moe_config(ctypes.Structure):
 WEIGHT_NAMES = ("w_router", "expert_bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up",
                 "ws_down", "w_gate_scale", "w_up_scale", "w_down_scale", "ws_scale",
                 "x_scale", "h_scale", "w_gate_mx", "w_up_mx", "w_down_mx", "ws_gate_mx",
-                "ws_up_mx", "ws_down_mx")
+                "ws_up_mx", "ws_down_mx", "w_router_planes")
 
 
 class hy3moe_weights(ctypes.Structure):
@@ -123,6 +124,17 @@ def load() -> ctypes.CDLL:
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p,
                                        ctypes.POINTER(ctypes.c_void_p)]
+    L.hy3moe_router_planes_bytes.restype = ctypes.c_size_t
+    L.hy3moe_router_planes_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    L.hy3moe_router_split.restype = ctypes.c_int
+    L.hy3moe_router_split.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]
+    L.hy3moe_route_planes.restype = ctypes.c_int
+    L.hy3moe_route_planes.argtypes = [ctypes.POINTER(hy3moe_config), ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]
     L.hy3moe_forward_static.restype = ctypes.c_int
     L.hy3moe_forward_static.argtypes = [ctypes.POINTER(hy3moe_config), ctypes.c_void_p,
                                         ctypes.POINTER(hy3moe_weights), ctypes.c_void_p,
@@ -254,6 +266,39 @@ def hy3moe_forward(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str, torch
         raise Hy3MoEError(rc, "hy3moe_forward")
 
 
+def router_split(w_router: torch.Tensor, router_prec: int = HY3MOE_ROUTER_FP32,
+                 stream=None) -> torch.Tensor:
+    """C ABI hy3moe_router_split: the offline bf16 split of the fp32 router
+    weight [E, H], returned as a uint8 device tensor of planes."""
+    _check_dev(w_router)
+    if w_router.dtype != torch.float32 or w_router.dim() != 2:
+        raise ValueError("w_router must be a float32 [E, H] tensor")
+    E, H = (int(v) for v in w_router.shape)
+    n = load().hy3moe_router_planes_bytes(E, H, router_prec)
+    if n == 0:
+        raise Hy3MoEError(-1, "hy3moe_router_planes_bytes")
+    planes = torch.empty(n, dtype=torch.uint8, device=w_router.device)
+    rc = load().hy3moe_router_split(_ptr(w_router), E, H, router_prec, _ptr(planes), n,
+                                    _stream(stream))
+    if rc != HY3MOE_OK:
+        raise Hy3MoEError(rc, "hy3moe_router_split")
+    return planes
+
+
+def hy3moe_route_planes(cfg: hy3moe_config, x: torch.Tensor, w_router: torch.Tensor,
+                        w_router_planes: Optional[torch.Tensor],
+                        expert_bias: Optional[torch.Tensor], idx: torch.Tensor,
+                        weight: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """C ABI hy3moe_route_planes (results in idx/weight)."""
+    _check_dev(x, w_router, w_router_planes, expert_bias, idx, weight, workspace)
+    rc = load().hy3moe_route_planes(ctypes.byref(cfg), _ptr(x), _ptr(w_router),
+                                    _ptr(w_router_planes), _ptr(expert_bias), _ptr(idx),
+                                    _ptr(weight), _ptr(workspace), workspace.numel(),
+                                    _stream(stream))
+    if rc != HY3MOE_OK:
+        raise Hy3MoEError(rc, "hy3moe_route_planes")
+
+
 def hy3moe_forward_static(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str, torch.Tensor],
                           out: torch.Tensor, idx_out: Optional[torch.Tensor] = None,
                           weight_out: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -290,13 +335,17 @@ def hy3moe_forward_timed(cfg: hy3moe_config, x: torch.Tensor, weights: Dict[str,
 
 # Convenience wrappers that allocate outputs (tests and benchmark).
 def route(cfg: hy3moe_config, x, w_router, expert_bias=None, workspace=None,
-          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+          stream=None, w_router_planes=None) -> Tuple[torch.Tensor, torch.Tensor]:
     T, K = int(cfg.T), int(cfg.K)
     idx = torch.empty((T, K), dtype=torch.int32, device=x.device)
     weight = torch.empty((T, K), dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(cfg, False, x.device)
-    hy3moe_route(cfg, x, w_router, expert_bias, idx, weight, workspace, stream)
+    if w_router_planes is None:
+        hy3moe_route(cfg, x, w_router, expert_bias, idx, weight, workspace, stream)
+    else:
+        hy3moe_route_planes(cfg, x, w_router, w_router_planes, expert_bias, idx, weight,
+                            workspace, stream)
     return idx, weight
 
 

@@ -130,7 +130,7 @@ int check_launch(hipError_t e) { return e == hipSuccess ? HY3MOE_OK : HY3MOE_ERR
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 7; }
+int hy3moe_abi_version(void) { return 8; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {
@@ -162,15 +162,41 @@ int hy3moe_workspace_layout(const hy3moe_config *cfg, hy3moe_ws_layout *out) {
   return HY3MOE_OK;
 }
 
+size_t hy3moe_router_planes_bytes(int32_t E, int32_t H, int32_t router_prec) {
+  if (E < 1 || E > 256 || H < 64 || H % 64 || H > 65536 ||
+      (router_prec != HY3MOE_ROUTER_FP32 && router_prec != HY3MOE_ROUTER_SPLIT2_BF16))
+    return 0;
+  return router_planes_bytes(E, H, router_prec);
+}
+
+int hy3moe_router_split(const float *w_router, int32_t E, int32_t H, int32_t router_prec,
+                        void *planes, size_t planes_bytes, void *stream) {
+  if (E < 1 || E > 256 || H < 1 || !w_router || !planes ||
+      (router_prec != HY3MOE_ROUTER_FP32 && router_prec != HY3MOE_ROUTER_SPLIT2_BF16))
+    return HY3MOE_ERR_INVALID;
+  if (H % 64 || H > 65536) return HY3MOE_ERR_UNSUPPORTED;
+  if (planes_bytes < router_planes_bytes(E, H, router_prec)) return HY3MOE_ERR_WORKSPACE;
+  if (!al16(w_router) || !al16(planes)) return HY3MOE_ERR_ALIGN;
+  return check_launch(launch_router_split(w_router, router_prec, static_cast<uint16_t *>(planes),
+                                          E, H, static_cast<hipStream_t>(stream)));
+}
+
 int hy3moe_route(const hy3moe_config *cfg, const void *x, const float *w_router,
                  const float *expert_bias, int32_t *idx, float *weight, void *workspace,
                  size_t ws_bytes, void *stream) {
+  return hy3moe_route_planes(cfg, x, w_router, nullptr, expert_bias, idx, weight, workspace,
+                             ws_bytes, stream);
+}
+
+int hy3moe_route_planes(const hy3moe_config *cfg, const void *x, const float *w_router,
+                        const void *w_router_planes, const float *expert_bias, int32_t *idx,
+                        float *weight, void *workspace, size_t ws_bytes, void *stream) {
   int rc = validate_cfg(cfg);
   if (rc != HY3MOE_OK) return rc;
   if (cfg->T == 0) return HY3MOE_OK;
   if (!x || !w_router || !idx || !weight || !workspace) return HY3MOE_ERR_INVALID;
   if (!al16(x) || !al16(w_router) || !al16(workspace) || !al4(idx) || !al4(weight) ||
-      (expert_bias && !al4(expert_bias)))
+      (expert_bias && !al4(expert_bias)) || (w_router_planes && !al16(w_router_planes)))
     return HY3MOE_ERR_ALIGN;
   hy3moe_ws_layout L;
   compute_layout(cfg, 0, &L);
@@ -180,8 +206,9 @@ int hy3moe_route(const hy3moe_config *cfg, const void *x, const float *w_router,
   const int T = (int)cfg->T;
   double *part = reinterpret_cast<double *>(ws + L.logits_part);
   uint16_t *planes = L.w_planes ? reinterpret_cast<uint16_t *>(ws + L.w_planes) : nullptr;
-  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w_router, planes, part, T, cfg->H,
-                                  cfg->E, L.n_ksplit, s));
+  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w_router, planes,
+                                  static_cast<const uint16_t *>(w_router_planes), part, T,
+                                  cfg->H, cfg->E, L.n_ksplit, s));
   if (rc) return rc;
   const float *bias = cfg->route_mode == HY3MOE_ROUTE_SIGMOID_BIAS ? expert_bias : nullptr;
   return check_launch(launch_select(part, L.n_ksplit, T, cfg->E, cfg->K, bias, cfg->route_mode,
@@ -201,7 +228,8 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   if (x == out) return HY3MOE_ERR_INVALID;
   if (!al16(x) || !al16(out) || !al16(workspace) || !al16(w->w_router) || !al16(w->w_gate) ||
       !al16(w->w_up) || !al16(w->w_down) || (w->expert_bias && !al4(w->expert_bias)) ||
-      (idx_out && !al4(idx_out)) || (weight_out && !al4(weight_out)))
+      (idx_out && !al4(idx_out)) || (weight_out && !al4(weight_out)) ||
+      (w->w_router_planes && !al16(w->w_router_planes)))
     return HY3MOE_ERR_ALIGN;
   if (has_shared && (!al16(w->ws_gate) || !al16(w->ws_up) || !al16(w->ws_down)))
     return HY3MOE_ERR_ALIGN;
@@ -246,8 +274,9 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   };
   mark();
   // 1-2. gate
-  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w->w_router, planes, part, T, H, E,
-                                  L.n_ksplit, s));
+  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w->w_router, planes,
+                                  static_cast<const uint16_t *>(w->w_router_planes), part, T, H,
+                                  E, L.n_ksplit, s));
   if (rc) return rc;
   mark();
   const float *bias = cfg->route_mode == HY3MOE_ROUTE_SIGMOID_BIAS ? w->expert_bias : nullptr;
@@ -306,6 +335,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   ea.E = E; ea.H = H; ea.I = cfg->I; ea.I_shared = cfg->I_shared; ea.ldh = Imax;
   ea.max_tiles = L.max_tiles;
   ea.n_rows = (int)((int64_t)T * K + (has_shared ? T : 0));
+  ea.n_tok = T;
   ea.act = act; ea.w0 = w->w_gate; ea.w1 = w->w_up; ea.ws0 = w->ws_gate; ea.ws1 = w->ws_up;
   // W4A8 on the large-tile path: the gate-up epilogue quantises h itself
   const bool h_codes_fused = amx_codes && path == PATH_BIG;

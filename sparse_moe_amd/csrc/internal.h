@@ -40,9 +40,17 @@ constexpr int ROUTER_PLANES_MIN_T = 1024;  // bf16 batches this large pre-split 
 bool router_use_planes(int64_t T, int dtype);
 int router_ksplit(int64_t T, int H, int E, int dtype);
 // planes: workspace for the bf16 weight planes [3][E][H], or null (split on the fly).
+// planes_in: the caller's planes from hy3moe_router_split (same E, H and
+// router_prec), used instead of splitting into `planes` when that path runs.
 hipError_t launch_router(const void *x, int dtype, int router_prec, const float *w_router,
-                         uint16_t *planes, double *part, int T, int H, int E, int S,
-                         hipStream_t stream);
+                         uint16_t *planes, const uint16_t *planes_in, double *part, int T, int H,
+                         int E, int S, hipStream_t stream);
+// Planes bytes for E experts of H values: NP bf16 planes (3 for the exact
+// split, 2 for the two-term one), E padded to a multiple of 16.
+size_t router_planes_bytes(int E, int H, int router_prec);
+// The split alone: fp32 w_router [E][H] -> planes (router_planes_bytes).
+hipError_t launch_router_split(const float *w_router, int router_prec, uint16_t *planes, int E,
+                               int H, hipStream_t stream);
 
 // Score + top-K select ------------------------------------------------------
 hipError_t launch_select(const double *part, int S, int T, int E, int K, const float *bias,
@@ -76,6 +84,7 @@ struct ExpertArgs {
   const int32_t *tiles;   // (group, first row) pairs, then the tile count
   int E, H, I, I_shared, ldh, max_tiles;
   int n_rows;             // rows of sorted_token (T K routed + T shared)
+  int n_tok;              // T (rows of x)
   // FP8 E4M3 expert weights (w_fp8 = 1): w0/w1/ws0/ws1 hold bytes and the
   // weight is scale * value, with scales sc0[g] / sc1[g] for routed group g
   // and *ssc0 / *ssc1 for the shared expert (gate-up: gate, up; down: down).

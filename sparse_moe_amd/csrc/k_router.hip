@@ -546,27 +546,43 @@ int router_ksplit(int64_t T, int H, int E, int dtype) {
   return S;
 }
 
+size_t router_planes_bytes(int E, int H, int router_prec) {
+  return (size_t)(router_prec == 0 ? 3 : 2) * ((E + 15) / 16 * 16) * H * 2;
+}
+
+hipError_t launch_router_split(const float *wr, int router_prec, uint16_t *planes, int E, int H,
+                               hipStream_t stream) {
+  const int E_pad = (E + 15) / 16 * 16;
+  const dim3 sgrid((unsigned)(((int64_t)E_pad * H / 8 + 255) / 256));
+  if (router_prec == 0)
+    hipLaunchKernelGGL(router_split_kernel<0>, sgrid, dim3(256), 0, stream, wr, planes, E, H,
+                       E_pad);
+  else
+    hipLaunchKernelGGL(router_split_kernel<1>, sgrid, dim3(256), 0, stream, wr, planes, E, H,
+                       E_pad);
+  return hipGetLastError();
+}
+
 hipError_t launch_router(const void *x, int dtype, int router_prec, const float *wr,
-                         uint16_t *planes, double *part, int T, int H, int E, int S,
-                         hipStream_t stream) {
+                         uint16_t *planes, const uint16_t *planes_in, double *part, int T, int H,
+                         int E, int S, hipStream_t stream) {
   const int kslice = H / S;
   dim3 grid((T + RT_TOK - 1) / RT_TOK, (E + RT_EXP - 1) / RT_EXP, S);
   if (planes) {
-    const int E_pad = (E + 15) / 16 * 16;
-    const dim3 sgrid((unsigned)(((int64_t)E_pad * H / 8 + 255) / 256));
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     const int nw = planes_waves(E);
     const int64_t items = (int64_t)((T + RT_TOK - 1) / RT_TOK) *
                           ((E + 16 * nw - 1) / (16 * nw)) * S;
     const dim3 pgrid((unsigned)((items + 7) / 8 * 8));   // 8 equal XCD runs
-    if (router_prec == 0)
-      hipLaunchKernelGGL(router_split_kernel<0>, sgrid, dim3(256), 0, stream, wr, planes, E, H,
-                         E_pad);
-    else
-      hipLaunchKernelGGL(router_split_kernel<1>, sgrid, dim3(256), 0, stream, wr, planes, E, H,
-                         E_pad);
+    // the caller's offline split, else split once into the workspace
+    const uint16_t *wp = planes_in;
+    if (!wp) {
+      const hipError_t e = launch_router_split(wr, router_prec, planes, E, H, stream);
+      if (e != hipSuccess) return e;
+      wp = planes;
+    }
 #define HY3_PLANES(P, NW)                                                              \
-  hipLaunchKernelGGL((router_planes_kernel<P, NW>), pgrid, dim3(64 * NW), 0, stream, xb, planes, \
+  hipLaunchKernelGGL((router_planes_kernel<P, NW>), pgrid, dim3(64 * NW), 0, stream, xb, wp, \
                      part, T, H, E, kslice, S)
     if (router_prec == 0) {
       if (nw == 4) HY3_PLANES(0, 4);

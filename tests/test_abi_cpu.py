@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 7
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 8
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -382,3 +382,23 @@ def test_static_forward_rejects_batches_beyond_its_scratch(lib):
     # the Hy3 decode batch fits
     dec = sm.make_config(16, 4096, 192, 8, 1536, 1536, "bf16")
     assert sm.hy3moe_workspace_bytes(dec) <= lib.hy3moe_static_scratch_bytes()
+
+
+def test_router_split_validates_on_the_host(lib):
+    """hy3moe_router_split and hy3moe_router_planes_bytes reject bad shapes,
+    precisions, sizes and alignment before launching anything."""
+    assert lib.hy3moe_router_planes_bytes(192, 4096, 0) == 3 * 192 * 4096 * 2
+    assert lib.hy3moe_router_planes_bytes(192, 4096, 1) == 2 * 192 * 4096 * 2
+    assert lib.hy3moe_router_planes_bytes(10, 256, 0) == 3 * 16 * 256 * 2   # E padded to 16
+    assert lib.hy3moe_router_planes_bytes(0, 4096, 0) == 0
+    assert lib.hy3moe_router_planes_bytes(192, 4000, 0) == 0
+    assert lib.hy3moe_router_planes_bytes(192, 4096, 7) == 0
+    ok = 1 << 20
+    n = 3 * 192 * 4096 * 2
+    assert lib.hy3moe_router_split(ok, 192, 4096, 0, ok, n - 1, None) == -3
+    assert lib.hy3moe_router_split(ok, 192, 4096, 0, None, n, None) == -1
+    assert lib.hy3moe_router_split(ok, 192, 4096, 5, ok, n, None) == -1
+    assert lib.hy3moe_router_split(ok, 0, 4096, 0, ok, n, None) == -1
+    assert lib.hy3moe_router_split(ok, 192, 4000, 0, ok, n, None) == -2
+    assert lib.hy3moe_router_split(ok + 8, 192, 4096, 0, ok, n, None) == -4
+    assert lib.hy3moe_router_split(ok, 192, 4096, 0, ok + 4, n, None) == -4
