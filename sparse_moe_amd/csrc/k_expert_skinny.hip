@@ -76,6 +76,7 @@ template <int MT>
 struct UnitSrc {
   const char *w0p, *w1p;   // the two 16-row weight fragments (gate/up, or two down blocks)
   const char *xp[MT];      // token rows (gathered x for gate-up, h rows for down)
+  uint32_t xlo[MT];        // XL: byte offsets of the lane's token chunks in the LDS copy of x
   const uint8_t *s0p, *s1p;  // MXFP4: the lane's scale bytes of the two fragments
   const uint8_t *xsp[MT];    // W4A8: the lane's scale bytes of the token rows
   bool vs;                   // W4A8: scale rows allow 16-byte loads of 4 steps
@@ -89,10 +90,18 @@ struct UnitOut {
   float hs;                // a8 gate-up: activation scale of the group's h
 };
 
+// XL (gate-up at T <= 16): the workgroup copies every token row of x into
+// LDS once, and the token operand of each step is read from there, so the
+// global loads carry only weights (the load path, not HBM, bounded the FP8
+// and MXFP4 weights, whose token chunks per weight byte are 2x and 4x
+// bf16's).  Rows of the copy are padded by 16 bytes, which spreads the 16
+// gathered rows of a wavefront read over the banks.
+__host__ __device__ constexpr int x_lds_stride(int row_bytes) { return row_bytes + 16; }
+
 // Unit u (tile u / n_col_blocks, column block u % n_col_blocks) of this
 // kernel; returns false if the column block lies past the group's width.
 // half = 1 or 2: only the first or the second 16-row fragment of a down unit.
-template <typename T, bool GATE_UP, int MT, int WF>
+template <typename T, bool GATE_UP, int MT, int WF, bool XL>
 __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_blocks, int lane,
                                         UnitSrc<MT> &src, UnitOut &o, int half = 0) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4 || WF == WF_W4A8;
@@ -163,6 +172,9 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
     // each 128-byte step of the token row; MXFP4: bytes [64g, 64g+64) of each
     // 256-byte step (the K values of the lane's codes); W4A8: code bytes
     // [32g, 32g+32) of each 128-byte step, and block scale step * 4 + g
+    if (XL)   // the token's row of the LDS copy, the lane's chunk of a step
+      src.xlo[m] = (uint32_t)a.sorted_token[trow] * (uint32_t)x_lds_stride(a.H * (MXA ? 1 : EB)) +
+                   cg * 16 * (MXA ? 1 : token_chunks<WF>());
     if (MXA) {   // bytes [16g, 16g + 16) and [64 + 16g, ...) of each 128-byte step
       src.xp[m] = static_cast<const char *>(a.act) + arow + cg * 16;
       src.xsp[m] = a.act_sc + arow / 32 + cg;
@@ -181,7 +193,7 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
 // of them is split into its two 16-row fragments for twice as many
 // wavefronts, so the last round costs half a unit.  Returns the item index
 // (kmax when there is none) and fills src / o.
-template <typename T, bool GATE_UP, int MT, int WF>
+template <typename T, bool GATE_UP, int MT, int WF, bool XL>
 __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int nw, int n_units,
                                          int n_col_blocks, int lane, UnitSrc<MT> &src,
                                          UnitOut &o) {
@@ -192,10 +204,10 @@ __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int 
     if (k < full || !split) {
       const int u = w + k * nw;
       if (u >= n_units) return kmax;
-      if (unit_of<T, GATE_UP, MT, WF>(a, u, n_col_blocks, lane, src, o)) return k;
+      if (unit_of<T, GATE_UP, MT, WF, XL>(a, u, n_col_blocks, lane, src, o)) return k;
     } else {
       if (w >= 2 * tail) return kmax;
-      if (unit_of<T, GATE_UP, MT, WF>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
+      if (unit_of<T, GATE_UP, MT, WF, XL>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
                                       1 + (w & 1)))
         return k;
     }
@@ -244,21 +256,40 @@ inline size_t meta_lds_bytes(const ExpertArgs &a, bool gate_up) {
   return 4 * ((size_t)2 * a.max_tiles + 1 + a.E + 2 + (gate_up ? a.n_rows : 0));
 }
 
-template <typename T, bool GATE_UP, int MT, int WF>
-__global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(ExpertArgs a_in,
-                                                                          int n_col_blocks) {
+// Threads per workgroup: 256 (two workgroups per CU), or 512 with the LDS
+// copy of x (one per CU holding it), two wavefronts per SIMD either way.
+template <bool XL> constexpr int stream_threads() { return XL ? 512 : 256; }
+
+template <typename T, bool GATE_UP, int MT, int WF, bool XL>
+__global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_stream_kernel(
+    ExpertArgs a_in, int n_col_blocks) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4, MXA = WF == WF_W4A8;
+  constexpr int NT = stream_threads<XL>(), WPB = NT / 64;
   // The unit metadata -- tile list, group offsets and (gate-up) the sorted
   // token ids -- is staged in LDS once per workgroup, so that the set-up of a
   // wavefront's next unit reads LDS instead of a chain of dependent global
   // loads, which held back the unit's first weight loads at every change.
   extern __shared__ int32_t meta[];
   const int n_t = 2 * a_in.max_tiles + 1, n_o = a_in.E + 2;
-  for (int i = threadIdx.x; i < n_t; i += 256) meta[i] = a_in.tiles[i];
-  for (int i = threadIdx.x; i < n_o; i += 256) meta[n_t + i] = a_in.offsets[i];
+  for (int i = threadIdx.x; i < n_t; i += NT) meta[i] = a_in.tiles[i];
+  for (int i = threadIdx.x; i < n_o; i += NT) meta[n_t + i] = a_in.offsets[i];
   if (GATE_UP)
-    for (int i = threadIdx.x; i < a_in.n_rows; i += 256)
+    for (int i = threadIdx.x; i < a_in.n_rows; i += NT)
       meta[n_t + n_o + i] = a_in.sorted_token[i];
+  // XL: every token row of x, 16-byte chunks, after the metadata (16-byte aligned)
+  const int meta_n = (n_t + n_o + (GATE_UP ? a_in.n_rows : 0) + 3) & ~3;
+  const char *xl = reinterpret_cast<const char *>(meta + meta_n);
+  if constexpr (XL) {
+    const int rb = a_in.H * (MXA ? 1 : Elem<T>::kBytes), cpr = rb / 16;
+    const int rs = x_lds_stride(rb);
+    char *dst = reinterpret_cast<char *>(meta + meta_n);
+    const char *src_x = static_cast<const char *>(a_in.act);
+    for (int i = threadIdx.x; i < a_in.n_tok * cpr; i += NT) {
+      const int t = i / cpr, c = i - t * cpr;
+      *reinterpret_cast<uint4 *>(dst + t * rs + c * 16) =
+          *reinterpret_cast<const uint4 *>(src_x + (size_t)t * rb + c * 16);
+    }
+  }
   __syncthreads();
   ExpertArgs a = a_in;
   a.tiles = meta;
@@ -273,13 +304,13 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
   // EXEC mask that is expected to switch it off.)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = __builtin_amdgcn_readfirstlane(a.tiles[2 * a.max_tiles]) * n_col_blocks;
-  const int nw = gridDim.x * 4, w = blockIdx.x * 4 + wave;
+  const int nw = gridDim.x * WPB, w = blockIdx.x * WPB + wave;
   const int kmax = n_units / nw + 1;
   // Wavefront ids interleave the XCDs (block b runs on XCD b % 8), so the
   // units of one expert spread over all XCDs and HBM channels.
   UnitSrc<MT> src;    // item whose blocks are being loaded
   UnitOut om, ol;     // item being multiplied, item being loaded
-  int k_ld = next_item<T, GATE_UP, MT, WF>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
+  int k_ld = next_item<T, GATE_UP, MT, WF, XL>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
   if (k_ld >= kmax) return;
   int k_mm = k_ld;
   om = ol;
@@ -352,12 +383,15 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
       }                                                                                \
       _Pragma("unroll") for (int m = 0; m < MT; ++m)                                   \
         _Pragma("unroll") for (int h = 0; h < XN; ++h)                                 \
-          X[u][m][h] = *reinterpret_cast<const uint4 *>(src.xp[m] + st_ * 64 * XN +      \
-                                                        h * (MXA ? 64 : 16));          \
+          X[u][m][h] = XL ? *reinterpret_cast<const uint4 *>(xl + src.xlo[m] +          \
+                                                             st_ * 64 * XN +           \
+                                                             h * (MXA ? 64 : 16))      \
+                          : *reinterpret_cast<const uint4 *>(src.xp[m] + st_ * 64 * XN + \
+                                                             h * (MXA ? 64 : 16));     \
     }                                                                                  \
     s_ld += U;                                                                         \
     if (s_ld >= src.nsub) {                                                            \
-      k_ld = next_item<T, GATE_UP, MT, WF>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
+      k_ld = next_item<T, GATE_UP, MT, WF, XL>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src, ol);                             \
       s_ld = 0;                                                                        \
     }                                                                                  \
@@ -416,7 +450,7 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
       unit_epilogue<T, GATE_UP, MT, WF>(a, om, acc, lane);                             \
       _Pragma("unroll") for (int f = 0; f < 2; ++f)                                    \
         _Pragma("unroll") for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; \
-      k_mm = next_item<T, GATE_UP, MT, WF>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
+      k_mm = next_item<T, GATE_UP, MT, WF, XL>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src_dummy, om);                       \
       s_mm = 0;                                                                        \
       more = k_mm < kmax;                                                              \
@@ -441,18 +475,36 @@ __global__ __launch_bounds__(256, WAVES_PER_SIMD) void expert_stream_kernel(Expe
 
 // Persistent grid: WAVES_PER_SIMD wavefronts per SIMD on the 256 CUs.
 constexpr int STREAM_BLOCKS = 256 * WAVES_PER_SIMD;
+constexpr size_t STREAM_XL_LDS_MAX = 150 * 1024;   // metadata + x copy of one workgroup
+
+// LDS bytes of the x copy (rows padded), or 0 when the gate-up GEMM of this
+// batch does not stage x: one 16-row fragment (T <= 16) and the copy fits.
+template <typename T, int MT, int WF>
+size_t x_lds_bytes(const ExpertArgs &a) {
+  if (MT != 1) return 0;
+  const int rb = a.H * (WF == WF_W4A8 ? 1 : Elem<T>::kBytes);
+  const size_t meta = (meta_lds_bytes(a, true) + 15) / 16 * 16;
+  const size_t x = (size_t)a.n_tok * x_lds_stride(rb);
+  return meta + x <= STREAM_XL_LDS_MAX ? x : 0;
+}
 
 template <typename T, int MT, int WF>
 hipError_t launch_skinny_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int ncb = (Imax + 15) / 16;
-    hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF>), dim3(STREAM_BLOCKS), dim3(256),
-                       meta_lds_bytes(a, true), stream, a, ncb);
+    const size_t xb = x_lds_bytes<T, MT, WF>(a);
+    if (xb)   // one 512-thread workgroup per CU, x in LDS
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, true>), dim3(STREAM_BLOCKS / 2),
+                         dim3(512), (meta_lds_bytes(a, true) + 15) / 16 * 16 + xb, stream, a,
+                         ncb);
+    else
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, false>), dim3(STREAM_BLOCKS),
+                         dim3(256), meta_lds_bytes(a, true), stream, a, ncb);
   } else {
     const int ncb = (a.H + 31) / 32;
-    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF>), dim3(STREAM_BLOCKS), dim3(256),
-                       meta_lds_bytes(a, false), stream, a, ncb);
+    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF, false>), dim3(STREAM_BLOCKS),
+                       dim3(256), meta_lds_bytes(a, false), stream, a, ncb);
   }
   return hipGetLastError();
 }
