@@ -12,7 +12,9 @@ Default workload: Hy3 decode, T=16 tokens, H=4096, 192 routed experts
 `--workload decode_fp8` / `prefill_fp8` are the decode and prefill shapes with
 FP8 E4M3 expert weights, `decode_w8a8` / `prefill_w8a8` the same with static
 FP8 activations as well (FP8 MFMAs on the large-tile path, priced against the
-FP8 peak).
+FP8 peak); `_mxfp4` / `_w4a8` use MXFP4 experts (with dynamic MXFP8
+activations for W4A8), and `_mixed` runs the routed experts at W4A8 and the
+shared expert at W8A8 in one call.
 
 Printed: one JSON line with tokens/s, the dominant kernel's roofline fraction
 (its per-launch duration measured live with HIP events on the library's
@@ -37,7 +39,8 @@ if ROOT not in sys.path:
 
 WORKLOADS = {"decode": "hy3_decode_T16", "prefill": "hy3_prefill_T8192_skew", "softmax": "hunyuanimage_softmax_T32768", "decode_fp8": "hy3_decode_T16_fp8", "prefill_fp8": "hy3_prefill_T8192_skew_fp8",
              "decode_w8a8": "hy3_decode_T16_w8a8", "prefill_w8a8": "hy3_prefill_T8192_skew_w8a8", "decode_mxfp4": "hy3_decode_T16_mxfp4", "prefill_mxfp4": "hy3_prefill_T8192_skew_mxfp4",
-             "decode_w4a8": "hy3_decode_T16_w4a8", "prefill_w4a8": "hy3_prefill_T8192_skew_w4a8"}
+             "decode_w4a8": "hy3_decode_T16_w4a8", "prefill_w4a8": "hy3_prefill_T8192_skew_w4a8",
+             "decode_mixed": "hy3_decode_T16_mixed", "prefill_mixed": "hy3_prefill_T8192_skew_mixed"}
 ROUTER_WORKLOAD = "hy3_router_only"            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
@@ -292,12 +295,19 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
     x = to_torch(inp.x(), c.dtype, dev)
     cfg = sm.make_config(c.T, c.H, c.E, c.K, c.I, c.I_shared, c.dtype, c.route_mode,
                          scale=c.scale, renorm_eps=c.renorm_eps, w_format=c.w_format,
-                         act_format=c.act_format)
+                         act_format=c.act_format, shared_w_format=c.shared_w_format,
+                         shared_act_format=c.shared_act_format)
     ws = sm.alloc_workspace(cfg, True, dev)
     out = torch.empty_like(x)
     idx = torch.empty((c.T, c.K), dtype=torch.int32, device=dev)
     wgt = torch.empty((c.T, c.K), dtype=torch.float32, device=dev)
 
+    # The router weight's offline split (Hy3 Preview inference case, section
+    # 2: prepared once, like the weights): batches that run the router GEMM
+    # on bf16 planes read them instead of splitting per call.
+    if sm.hy3moe_workspace_layout(cfg).w_planes:
+        weights = dict(weights, w_router_planes=sm.router_split(weights["w_router"],
+                                                                cfg.router_prec))
     # Route of this batch (outside the timed region) for the byte/FLOP counts.
     sm.hy3moe_forward(cfg, x, weights, out, ws, idx, wgt)
     torch.cuda.synchronize()
@@ -355,27 +365,41 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
 
     # ---- algorithmic work ----
     eb = 2 if c.dtype == "bf16" else 4
-    # bytes per expert weight element (MXFP4: half a byte + one scale byte per 32)
-    web = {"fp8_e4m3": 1, "mxfp4": 0.5 + 1 / 32}.get(c.w_format, eb)
     tile_rows = sm.hy3moe_workspace_layout(cfg).tile_rows
-    # static FP8 activations: E4M3 bytes on the large-tile path (FP8 MFMAs),
-    # their bf16 values on the others; dynamic MXFP8: codes and a scale byte
-    # per 32 on the weight-streaming and large-tile paths (FP4 x FP8 MFMAs,
-    # which issue at the FP8 rate), bf16 values on the 128-row tiled path
-    fp8_mma = c.act_format in ("fp8_static", "mxfp8") and tile_rows == 256
-    ab = 1 if fp8_mma else eb                         # bytes per x / h element
-    if c.act_format == "mxfp8" and tile_rows != 128:
-        ab = 1 + 1 / 32
-    peak_mma = PEAK_FP8_TFLOPS if fp8_mma else PEAK_BF16_TFLOPS
-    mma_dtype = ("mxfp4_x_mxfp8" if c.act_format == "mxfp8" else "fp8_e4m3") if fp8_mma \
-        else c.dtype
+
+    def branch(wf, af):
+        """(bytes per weight element, bytes per x / h element, FP8-rate MFMAs)
+        of one branch.  MXFP4 weights: half a byte + one scale byte per 32.
+        Static FP8 activations: E4M3 bytes on the large-tile path (FP8 MFMAs),
+        their bf16 values on the others; dynamic MXFP8: codes and a scale byte
+        per 32 on the weight-streaming and large-tile paths (FP4 x FP8 MFMAs,
+        which issue at the FP8 rate), bf16 values on the 128-row tiled path."""
+        web = {"fp8_e4m3": 1, "mxfp4": 0.5 + 1 / 32}.get(wf, eb)
+        f8 = af in ("fp8_static", "mxfp8") and tile_rows == 256
+        ab = 1 if f8 else eb
+        if af == "mxfp8" and tile_rows != 128:
+            ab = 1 + 1 / 32
+        mma = ("mxfp4_x_mxfp8" if af == "mxfp8" else "fp8_e4m3") if f8 else c.dtype
+        return web, ab, f8, mma
+
     T, H, E, K, I, Is = c.T, c.H, c.E, c.K, c.I, c.I_shared
+    web, ab, fp8_mma, mma_dtype = branch(c.w_format, c.act_format)
+    mixed = bool(Is) and (c.sw_format, c.sa_format) != (c.w_format, c.act_format)
+    web_s, ab_s, f8_s, mma_s = branch(c.sw_format, c.sa_format) if Is else (0, 0, fp8_mma,
+                                                                             mma_dtype)
+    if mixed and mma_s != mma_dtype:
+        mma_dtype += "+" + mma_s
+    fp8_mma = fp8_mma and f8_s                 # priced at the FP8 peak only if both are
+    peak_mma = PEAK_FP8_TFLOPS if fp8_mma else PEAK_BF16_TFLOPS
     R = T * K + (T if Is else 0)
     groups = U + (1 if Is else 0)
-    gu_weight_bytes = U * 2 * I * H * web + (2 * Is * H * web if Is else 0)
-    dn_weight_bytes = U * H * I * web + (H * Is * web if Is else 0)
-    gu_bytes = gu_weight_bytes + T * H * ab + R * I * ab
-    dn_bytes = dn_weight_bytes + R * I * ab + R * H * eb
+    gu_weight_bytes = U * 2 * I * H * web + 2 * Is * H * web_s
+    dn_weight_bytes = U * H * I * web + H * Is * web_s
+    # each branch reads x in its own activation format
+    x_bytes = T * H * ab + (T * H * ab_s if mixed else 0)
+    h_bytes = T * K * I * ab + T * Is * ab_s
+    gu_bytes = gu_weight_bytes + x_bytes + h_bytes
+    dn_bytes = dn_weight_bytes + h_bytes + R * H * eb
     layer_bytes = gu_weight_bytes + dn_weight_bytes + E * H * 4 + 2 * T * H * eb
     gu_flops = 4.0 * H * (T * K * I + (T * Is if Is else 0))
     dn_flops = 2.0 * H * (T * K * I + (T * Is if Is else 0))
@@ -383,16 +407,24 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
     layer_s = ms_per_step / 1e3
     gu_s = stage_ms["gate_up"] / 1e3
     decode = key.startswith("decode")
+    names = {"fp8_e4m3": "FP8 E4M3", "mxfp4": "MXFP4"}
     if decode:
-        kind = {"fp8_e4m3": "FP8 E4M3", "mxfp4": "MXFP4"}.get(c.w_format, c.dtype)
+        kind = names.get(c.w_format, c.dtype)
+        per_unit = (f"{2 * I * H * web:.0f} B of {kind} gate+up weights per touched "
+                    f"expert x {U} routed experts")
+        if Is:
+            per_unit += (f" + {2 * Is * H * web_s:.0f} B of "
+                         f"{names.get(c.sw_format, c.dtype)} shared gate+up weights")
         roof = {"kernel": "gate_up (weight-streaming grouped GEMM + SwiGLU)", "bound": "hbm",
                 "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "per_unit": f"{2 * I * H * web:.0f} B of {kind} gate+up weights per touched "
-                            f"expert x {groups} experts + x and h rows"}
+                "per_unit": per_unit + " + x and h rows"}
     else:
         path = "256x256-tile" if tile_rows == 256 else "128x128-tile"
         if fp8_mma:
             path += " FP4 x FP8 MFMA" if c.act_format == "mxfp8" else " FP8 MFMA"
+            if mixed and mma_s != branch(c.w_format, c.act_format)[3]:
+                path += " (shared expert: FP8 MFMA)" if c.sa_format == "fp8_static" \
+                    else " (shared expert: FP4 x FP8 MFMA)"
         roof = {"kernel": f"gate_up ({path} grouped GEMM + SwiGLU)", "bound": "mfma",
                 "achieved": gu_flops / gu_s / 1e12, "peak": peak_mma, "unit": "TFLOP/s",
                 "per_unit": f"{4 * H * I} FLOP per routed row x {T * K} rows + "
@@ -418,6 +450,11 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
               "expert_weights": c.w_format if c.w_format != "dtype" else c.dtype,
               "expert_activations": {"fp8_static": "fp8_e4m3_static",
                                      "mxfp8": "mxfp8_dynamic"}.get(c.act_format, c.dtype)}
+    if mixed:
+        config["shared_expert_weights"] = c.sw_format if c.sw_format != "dtype" else c.dtype
+        config["shared_expert_activations"] = {"fp8_static": "fp8_e4m3_static",
+                                               "mxfp8": "mxfp8_dynamic"}.get(c.sa_format,
+                                                                             c.dtype)
     return {"ms_per_step": ms_per_step, "stage_ms": stage_ms, "roofline": roof, "layer": layer,
             "config": config, "mma_dtype": mma_dtype, "graph_ms": graph_ms,
             "idx": idx.cpu().numpy()}
@@ -602,26 +639,31 @@ def cpu_baseline(inp, args, gpu_idx):
     b64 = None if b is None else b.astype(np.float64)
     need = sorted(set(gpu_idx[tokens].reshape(-1).tolist()))
     t0 = time.time()
-    if c.w_format == "mxfp4":         # the oracle's own dequantisation of the codes
-        def expert_f64(e):
-            codes, sc = inp.expert_mxfp4(e)
+    # the oracle's own dequantisation of the codes, each branch in its format
+    def dequant(fmt, get_codes, plain):
+        if fmt == "mxfp4":
+            codes, sc = get_codes("mxfp4")
             return tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(codes, sc))
-        shf = inp.shared_mxfp4()
-        sh = None if shf is None else tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(*shf))
-    elif c.w_format == "fp8_e4m3":
-        # the oracle's own dequantisation of the codes
-        def expert_f64(e):
-            codes, sc = inp.expert_fp8(e)
+        if fmt == "fp8_e4m3":
+            codes, sc = get_codes("fp8")
             return tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))
-        shf = inp.shared_fp8()
-        sh = None if shf is None else tuple(oracle.dequant_fp8(q, s) for q, s in zip(*shf))
-    else:
-        expert_f64 = inp.expert_f64
-        sh = inp.shared_f64()
-    a8 = None
-    if c.act_format == "fp8_static":
+        return plain()
+
+    def expert_f64(e):
+        return dequant(c.w_format, lambda k: getattr(inp, f"expert_{k}")(e),
+                       lambda: inp.expert_f64(e))
+
+    sh = None
+    if c.I_shared:
+        sh = dequant(c.sw_format, lambda k: getattr(inp, f"shared_{k}")(), inp.shared_f64)
+
+    def a8_of(fmt):
+        if fmt != "fp8_static":
+            return None
         a1, a2 = inp.act_scales()
-        a8 = (float(a1), a2.astype(np.float64))
+        return float(a1), a2.astype(np.float64)
+    act = dict(a8=a8_of(c.act_format), amx=c.act_format == "mxfp8",
+               shared_a8=a8_of(c.sa_format), shared_amx=c.sa_format == "mxfp8")
     with ThreadPoolExecutor(8) as ex:
         ws = dict(zip(need, ex.map(expert_f64, need)))
     log(f"[bench] oracle sample: {n} tokens, {len(need)} experts in float64 "
@@ -636,8 +678,7 @@ def cpu_baseline(inp, args, gpu_idx):
     while reps < 3 or (dt < args.cpu_seconds and reps < 10000):
         t1 = time.perf_counter()
         r = oracle.route(x64, wr, c.K, c.route_mode, b64, c.scale, c.renorm_eps)
-        oracle.forward_given_route(x64, r.idx, r.weight, ws.__getitem__, c.E, sh, a8=a8,
-                                   amx=c.act_format == "mxfp8")
+        oracle.forward_given_route(x64, r.idx, r.weight, ws.__getitem__, c.E, sh, **act)
         dt += time.perf_counter() - t1
         reps += 1
     del ws

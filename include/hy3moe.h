@@ -126,6 +126,10 @@ extern "C" {
  * in bf16. */
 #define HY3MOE_AFMT_MXFP8      2
 
+/* hy3moe_config.shared_w_format / shared_act_format: the shared expert uses
+ * the routed experts' formats. */
+#define HY3MOE_FMT_AS_ROUTED  -1
+
 /* Shape and mode of one layer call. */
 typedef struct hy3moe_config {
   int64_t T;          /* tokens (rows of x)                                   */
@@ -141,6 +145,17 @@ typedef struct hy3moe_config {
   float   renorm_eps; /* softmax mode: clamp of the top-K sum (1e-8); sigmoid mode: unused */
   int32_t w_format;   /* HY3MOE_WFMT_*: storage of the expert weights            */
   int32_t act_format; /* HY3MOE_AFMT_*: activations of the expert GEMMs          */
+  /* Formats of the shared expert, or HY3MOE_FMT_AS_ROUTED (-1) for the routed
+   * ones.  The CANN deployment article (section 8.2) runs the routed experts
+   * at W4A8 (w_format MXFP4, act_format MXFP8) and the shared expert at W8A8
+   * (shared_w_format FP8_E4M3, shared_act_format FP8_STATIC).  Formats of its
+   * own follow the same rules as the routed ones (checked against I_shared)
+   * and read the shared tensors in those formats: ws_scale for FP8 weights,
+   * the ws_*_mx scales for MXFP4, x_scale and h_scale[E] for static FP8
+   * activations.  The expert GEMMs then run as two launches each (routed
+   * groups, then the shared group), sharing the permutation and the combine. */
+  int32_t shared_w_format;
+  int32_t shared_act_format;
 } hy3moe_config;
 
 /* Weights.  Layouts follow nn.Linear [out, in] (K-contiguous rows), stacked
@@ -210,7 +225,9 @@ typedef struct hy3moe_ws_layout {
   size_t pos_of;         /* int32 [T][K]  expert-major row of (token, pick)     */
   size_t hist;           /* int32 [n_chunks][E] per-chunk expert counts / prefixes */
   int32_t n_chunks;      /* (token, pick) chunks of the permutation             */
-  size_t tiles;          /* int32 [2*max_tiles] (group, first row) per row tile, then n_tiles */
+  size_t tiles;          /* int32 [2*max_tiles+2] (group, first row) per row tile, then the
+                            tile count and the routed tile count (the shared expert's
+                            tiles come last when it has formats of its own) */
   int32_t max_tiles;
   int32_t tile_rows;     /* rows per tile of the expert GEMMs for this T       */
   size_t h;              /* dtype [R][I_max]  SwiGLU activations, I_max = max(I, I_shared) */
@@ -230,6 +247,9 @@ typedef struct hy3moe_ws_layout {
                             large-tile paths; the tiled path rewrites h in place
                             with the bf16 values)                              */
   size_t hs;             /* MXFP8: E8M0 scales of h [R][I_max/32]              */
+  size_t xq_shared;      /* the shared expert's quantised x when its activation
+                            format differs from the routed one (as xq; 0 = not used) */
+  size_t xs_shared;      /* its MXFP8 scales (0 = not used)                       */
 } hy3moe_ws_layout;
 
 /* Workspace size in bytes for hy3moe_forward (for_forward != 0) or for

@@ -1,7 +1,7 @@
 """CPU oracle of the MoE FFN layer (float64).  TEST INFRASTRUCTURE ONLY:
 imported by tests, the smoke check and the benchmark's CPU-baseline leg,
 never by the product path."""
-from .moe import (E4M3_MAX, ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, combine_weights,
+from .moe import (AS_ROUTED, E4M3_MAX, ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, combine_weights,
                   dense_masked, expert_h, forward_by_expert,
                   dequant_fp8, dequant_mxfp4, e8m0_value, forward, forward_given_route,
                   fp4_e2m1_value, fp8_e4m3_value,
@@ -11,7 +11,7 @@ from .moe import (E4M3_MAX, ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX, Route, combine_we
                   softmax_rows, swiglu_expert, topk_desc)
 
 __all__ = [
-    "E4M3_MAX", "ROUTE_SIGMOID_BIAS", "ROUTE_SOFTMAX", "Route", "combine_weights",
+    "AS_ROUTED", "E4M3_MAX", "ROUTE_SIGMOID_BIAS", "ROUTE_SOFTMAX", "Route", "combine_weights",
     "dense_masked", "dequant_fp8", "expert_h", "forward_by_expert",
     "dequant_mxfp4", "e8m0_value", "fp4_e2m1_value",
     "forward", "forward_given_route", "fp8_e4m3_value", "layer_flops", "quant_dequant_e4m3",

@@ -419,11 +419,50 @@ def swiglu_expert(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
 # --------------------------------------------------------------------------
 # Whole layer
 # --------------------------------------------------------------------------
+# The shared expert's activation format when it is the routed experts' one.
+AS_ROUTED = "as_routed"
+
+
+def _branch_inputs(x: np.ndarray, E: int, a8, amx: bool, shared_a8, shared_amx):
+    """Expert inputs and h formats of the two branches of the layer.
+
+    Returns ((x_r, a2_r, amx_r), (x_s, a2_s, amx_s)): the routed experts'
+    input rows, their static h scales (a2_r[e], None without static FP8
+    activations) and MXFP8 flag, then the same for the shared expert.  A
+    branch quantises x once with its own activation format: static FP8 with
+    the layer's scale a1 (``quant_dequant_e4m3``), or dynamic MXFP8 per 32
+    along H (``quant_dequant_mxfp8``).  The shared expert takes the routed
+    formats unless ``shared_a8`` / ``shared_amx`` say otherwise (the CANN
+    deployment article, section 8.2, runs the routed experts at W4A8 and the
+    shared expert at W8A8); its static h scale is a2[E].
+    """
+    if isinstance(shared_a8, str):
+        shared_a8 = a8
+    if isinstance(shared_amx, str):
+        shared_amx = amx
+
+    def quant_x(f8, mx):
+        v = x
+        if f8 is not None:
+            v = quant_dequant_e4m3(v, f8[0])
+        if mx:
+            v = quant_dequant_mxfp8(v)
+        return v
+
+    x_r = quant_x(a8, amx)
+    a2_r = [None] * E if a8 is None else [float(a8[1][e]) for e in range(E)]
+    same = (shared_a8 is a8) and (bool(shared_amx) == bool(amx))
+    x_s = x_r if same else quant_x(shared_a8, shared_amx)
+    a2_s = None if shared_a8 is None else float(shared_a8[1][E])
+    return (x_r, a2_r, bool(amx)), (x_s, a2_s, bool(shared_amx))
+
+
 def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
                         experts: ExpertFn, E: int,
                         shared: Optional[Sequence[np.ndarray]] = None,
                         a8: Optional[Tuple[float, Sequence[float]]] = None,
-                        amx: bool = False) -> np.ndarray:
+                        amx: bool = False, shared_a8=AS_ROUTED,
+                        shared_amx=AS_ROUTED) -> np.ndarray:
     """Routed experts + shared expert for a given route (the eager path).
 
     Follows the eager path of the HunyuanImage 3.0 MoE reading: every token
@@ -443,33 +482,30 @@ def forward_given_route(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
     expert).  ``amx`` selects dynamic MXFP8 activations (W4A8): x and every
     expert's h are quantised per block of 32 along the reduction axis
     (``quant_dequant_mxfp8``).  The router is not affected: it reads the
-    unquantised x.
+    unquantised x.  ``shared_a8`` / ``shared_amx`` give the shared expert
+    formats of its own (``_branch_inputs``).
     """
     x = np.asarray(x, dtype=np.float64)
     idx = np.asarray(idx)
     weight = np.asarray(weight, dtype=np.float64)
     T, H = x.shape
     K = idx.shape[1] if idx.ndim == 2 else 0
-    a2 = [None] * (E + 1)
-    if a8 is not None:
-        x = quant_dequant_e4m3(x, a8[0])
-        a2 = [float(v) for v in a8[1]]
-    if amx:
-        x = quant_dequant_mxfp8(x)
+    (x_r, a2_r, amx_r), (x_s, a2_s, amx_s) = _branch_inputs(x, E, a8, amx, shared_a8,
+                                                             shared_amx)
     out_shared = np.zeros((T, H))
     if shared is not None:
-        out_shared = swiglu_expert(x, *shared, a2=a2[E], amx=amx)
+        out_shared = swiglu_expert(x_s, *shared, a2=a2_s, amx=amx_s)
     if T == 0 or K == 0:
         return out_shared
     flat_idx = idx.reshape(-1)
-    x_rep = np.repeat(x, K, axis=0)                 # [T*K, H], copy j of token t at t*K+j
+    x_rep = np.repeat(x_r, K, axis=0)               # [T*K, H], copy j of token t at t*K+j
     expert_out = np.zeros_like(x_rep)
     for e in range(E):
         mask = flat_idx == e
         if not mask.any():
             continue
         wg, wu, wd = experts(e)
-        expert_out[mask] = swiglu_expert(x_rep[mask], wg, wu, wd, a2=a2[e], amx=amx)
+        expert_out[mask] = swiglu_expert(x_rep[mask], wg, wu, wd, a2=a2_r[e], amx=amx_r)
     routed = (expert_out.reshape(T, K, H) * weight[:, :, None]).sum(axis=1)
     return out_shared + routed
 
@@ -478,7 +514,8 @@ def forward_by_expert(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
                       experts: ExpertFn, E: int,
                       shared: Optional[Sequence[np.ndarray]] = None,
                       a8: Optional[Tuple[float, Sequence[float]]] = None,
-                      amx: bool = False, h_hook=None) -> np.ndarray:
+                      amx: bool = False, h_hook=None, shared_a8=AS_ROUTED,
+                      shared_amx=AS_ROUTED) -> np.ndarray:
     """The same sum as ``forward_given_route``, gathered expert by expert.
 
     out[t] = shared(x_t) + sum_e sum_{j: idx[t, j] = e} weight[t, j] f_e(x_t).
@@ -500,16 +537,12 @@ def forward_by_expert(x: np.ndarray, idx: np.ndarray, weight: np.ndarray,
     idx = np.asarray(idx)
     weight = np.asarray(weight, dtype=np.float64)
     T, H = x.shape
-    a2 = [None] * (E + 1)
-    if a8 is not None:
-        x = quant_dequant_e4m3(x, a8[0])
-        a2 = [float(v) for v in a8[1]]
-    if amx:
-        x = quant_dequant_mxfp8(x)
+    (x_r, a2_r, amx_r), (x_s, a2_s, amx_s) = _branch_inputs(x, E, a8, amx, shared_a8,
+                                                             shared_amx)
 
     def expert_out(e, tok, wg, wu, wd):
-        a = x[tok]
-        h, h_in = expert_h(a, wg, wu, a2=a2[e], amx=amx)
+        a, a2, mx = (x_s[tok], a2_s, amx_s) if e == E else (x_r[tok], a2_r[e], amx_r)
+        h, h_in = expert_h(a, wg, wu, a2=a2, amx=mx)
         if h_hook is not None:
             h_in = h_hook(e, tok, a, wg, wu, h, h_in)
         return h_in @ np.asarray(wd, dtype=np.float64).T
@@ -538,12 +571,13 @@ def forward(x, w_router, experts: ExpertFn, E: int, K: int,
 def dense_masked(x, idx, weight, experts: ExpertFn, E: int,
                  shared: Optional[Sequence[np.ndarray]] = None,
                  a8: Optional[Tuple[float, Sequence[float]]] = None,
-                 amx: bool = False) -> np.ndarray:
+                 amx: bool = False, shared_a8=AS_ROUTED,
+                 shared_amx=AS_ROUTED) -> np.ndarray:
     """Brute force: evaluate every expert on every token and mask.
 
     out[t] = shared(x_t) + sum_e M[t, e] * f_e(x_t), where M is zero except
     M[t, idx[t, j]] = weight[t, j].  Used on tiny inputs only, as a check of
-    the sparse dispatch above (``a8`` as there).
+    the sparse dispatch above (activation formats as there).
     """
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
@@ -552,15 +586,12 @@ def dense_masked(x, idx, weight, experts: ExpertFn, E: int,
     for t in range(T):
         for j in range(idx.shape[1]):
             M[t, idx[t, j]] += weight[t, j]
-    if a8 is not None:
-        x = quant_dequant_e4m3(x, a8[0])
-    if amx:
-        x = quant_dequant_mxfp8(x)
-    sc = (lambda e: None) if a8 is None else (lambda e: float(a8[1][e]))
+    (x_r, a2_r, amx_r), (x_s, a2_s, amx_s) = _branch_inputs(x, E, a8, amx, shared_a8,
+                                                             shared_amx)
     out = (np.zeros((T, H)) if shared is None
-           else swiglu_expert(x, *shared, a2=sc(E), amx=amx))
+           else swiglu_expert(x_s, *shared, a2=a2_s, amx=amx_s))
     for e in range(E):
-        out = out + M[:, e:e + 1] * swiglu_expert(x, *experts(e), a2=sc(e), amx=amx)
+        out = out + M[:, e:e + 1] * swiglu_expert(x_r, *experts(e), a2=a2_r[e], amx=amx_r)
     return out
 
 

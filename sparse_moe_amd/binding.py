@@ -28,9 +28,10 @@ HY3MOE_WFMT_MXFP4 = 2
 HY3MOE_AFMT_DTYPE = 0
 HY3MOE_AFMT_FP8_STATIC = 1
 HY3MOE_AFMT_MXFP8 = 2
+HY3MOE_FMT_AS_ROUTED = -1
 
 HY3MOE_N_STAGES = 6
-ABI_VERSION = 8          # hy3moe_abi_version() of the library this binding matches
+ABI_VERSION = 9          # hy3moe_abi_version() of the library this binding matches
 STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 
 EXPORTED_SYMBOLS = (
@@ -49,7 +50,8 @@ class hy3moe_config(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("route_mode", ctypes.c_int32),
         ("router_prec", ctypes.c_int32), ("scale", ctypes.c_float),
         ("renorm_eps", ctypes.c_float), ("w_format", ctypes.c_int32),
-        ("act_format", ctypes.c_int32),
+        ("act_format", ctypes.c_int32), ("shared_w_format", ctypes.c_int32),
+        ("shared_act_format", ctypes.c_int32),
     ]
 
 
@@ -74,6 +76,7 @@ class hy3moe_ws_layout(ctypes.Structure):
         ("tile_rows", ctypes.c_int32), ("h", ctypes.c_size_t), ("y", ctypes.c_size_t),
         ("w_planes", ctypes.c_size_t), ("xq", ctypes.c_size_t), ("xs", ctypes.c_size_t),
         ("hq", ctypes.c_size_t), ("hs", ctypes.c_size_t),
+        ("xq_shared", ctypes.c_size_t), ("xs_shared", ctypes.c_size_t),
     ]
 
 
@@ -168,22 +171,28 @@ def strerror(code: int) -> str:
     return load().hy3moe_strerror(int(code)).decode()
 
 
+_WFMT = {"dtype": HY3MOE_WFMT_DTYPE, "fp8_e4m3": HY3MOE_WFMT_FP8_E4M3, "mxfp4": HY3MOE_WFMT_MXFP4}
+_AFMT = {"dtype": HY3MOE_AFMT_DTYPE, "fp8_static": HY3MOE_AFMT_FP8_STATIC,
+         "mxfp8": HY3MOE_AFMT_MXFP8}
+
+
 def make_config(T: int, H: int, E: int, K: int, I: int, I_shared: int, dtype: str = "bf16",
                 route_mode: int = HY3MOE_ROUTE_SIGMOID_BIAS,
                 router_prec: int = HY3MOE_ROUTER_FP32, scale: float = 2.826,
                 renorm_eps: float = 1e-8, w_format: str = "dtype",
-                act_format: str = "dtype") -> hy3moe_config:
+                act_format: str = "dtype", shared_w_format: Optional[str] = None,
+                shared_act_format: Optional[str] = None) -> hy3moe_config:
+    """shared_w_format / shared_act_format: None for the routed formats."""
     return hy3moe_config(T=int(T), H=int(H), E=int(E), K=int(K), I=int(I),
                          I_shared=int(I_shared),
                          dtype=HY3MOE_BF16 if dtype == "bf16" else HY3MOE_F32,
                          route_mode=int(route_mode), router_prec=int(router_prec),
                          scale=float(scale), renorm_eps=float(renorm_eps),
-                         w_format={"fp8_e4m3": HY3MOE_WFMT_FP8_E4M3,
-                                   "mxfp4": HY3MOE_WFMT_MXFP4}.get(w_format,
-                                                                   HY3MOE_WFMT_DTYPE),
-                         act_format={"fp8_static": HY3MOE_AFMT_FP8_STATIC,
-                                     "mxfp8": HY3MOE_AFMT_MXFP8}.get(act_format,
-                                                                     HY3MOE_AFMT_DTYPE))
+                         w_format=_WFMT[w_format], act_format=_AFMT[act_format],
+                         shared_w_format=(HY3MOE_FMT_AS_ROUTED if shared_w_format is None
+                                          else _WFMT[shared_w_format]),
+                         shared_act_format=(HY3MOE_FMT_AS_ROUTED if shared_act_format is None
+                                            else _AFMT[shared_act_format]))
 
 
 def hy3moe_workspace_bytes(cfg: hy3moe_config, for_forward: bool = True) -> int:

@@ -26,6 +26,37 @@ size_t al(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 int elt_bytes(int dtype) { return dtype == HY3MOE_F32 ? 4 : 2; }
 
+// Formats of one branch of the layer: the routed experts, or the shared
+// expert (its own formats when shared_w_format / shared_act_format are set).
+struct BranchFmt {
+  int w, act;
+  bool operator!=(const BranchFmt &o) const { return w != o.w || act != o.act; }
+};
+BranchFmt routed_fmt(const hy3moe_config *c) { return {c->w_format, c->act_format}; }
+BranchFmt shared_fmt(const hy3moe_config *c) {
+  return {c->shared_w_format == HY3MOE_FMT_AS_ROUTED ? c->w_format : c->shared_w_format,
+          c->shared_act_format == HY3MOE_FMT_AS_ROUTED ? c->act_format : c->shared_act_format};
+}
+// Does the shared expert run in formats of its own (separate GEMM launches)?
+bool mixed(const hy3moe_config *c) { return c->I_shared > 0 && shared_fmt(c) != routed_fmt(c); }
+
+// The format rules of one branch whose expert intermediate size is Ib.
+int validate_fmt(const hy3moe_config *c, BranchFmt f, int Ib) {
+  if (f.w != HY3MOE_WFMT_DTYPE && f.w != HY3MOE_WFMT_FP8_E4M3 && f.w != HY3MOE_WFMT_MXFP4)
+    return HY3MOE_ERR_INVALID;
+  if (f.act != HY3MOE_AFMT_DTYPE && f.act != HY3MOE_AFMT_FP8_STATIC && f.act != HY3MOE_AFMT_MXFP8)
+    return HY3MOE_ERR_INVALID;
+  // FP8 and MXFP4 expert weights need bf16 activations.
+  if (f.w != HY3MOE_WFMT_DTYPE && c->dtype != HY3MOE_BF16) return HY3MOE_ERR_UNSUPPORTED;
+  // MXFP4: 128 K values per 64-byte step of a streamed weight row.
+  if (f.w == HY3MOE_WFMT_MXFP4 && (c->H % 128 || Ib % 128)) return HY3MOE_ERR_UNSUPPORTED;
+  // Dynamic MXFP8 activations go with MXFP4 weights, static FP8 with FP8.
+  if (f.act == HY3MOE_AFMT_MXFP8 && f.w != HY3MOE_WFMT_MXFP4) return HY3MOE_ERR_UNSUPPORTED;
+  if (f.act == HY3MOE_AFMT_FP8_STATIC && f.w != HY3MOE_WFMT_FP8_E4M3)
+    return HY3MOE_ERR_UNSUPPORTED;
+  return HY3MOE_OK;
+}
+
 int validate_cfg(const hy3moe_config *c) {
   if (!c) return HY3MOE_ERR_INVALID;
   if (c->T < 0 || c->E < 1 || c->E > 256 || c->K < 1 || c->K > c->E || c->K > 64)
@@ -41,24 +72,14 @@ int validate_cfg(const hy3moe_config *c) {
   if (c->T > (int64_t(1) << 24)) return HY3MOE_ERR_UNSUPPORTED;
   if (c->router_prec == HY3MOE_ROUTER_SPLIT2_BF16 && c->dtype != HY3MOE_BF16)
     return HY3MOE_ERR_UNSUPPORTED;
-  if (c->w_format != HY3MOE_WFMT_DTYPE && c->w_format != HY3MOE_WFMT_FP8_E4M3 &&
-      c->w_format != HY3MOE_WFMT_MXFP4)
+  if ((c->shared_w_format < HY3MOE_FMT_AS_ROUTED) || (c->shared_act_format < HY3MOE_FMT_AS_ROUTED))
     return HY3MOE_ERR_INVALID;
-  // FP8 and MXFP4 expert weights need bf16 activations.
-  if (c->w_format != HY3MOE_WFMT_DTYPE && c->dtype != HY3MOE_BF16)
-    return HY3MOE_ERR_UNSUPPORTED;
-  // MXFP4: 128 K values per 64-byte step of a streamed weight row.
-  if (c->w_format == HY3MOE_WFMT_MXFP4 && (c->H % 128 || c->I % 128 || c->I_shared % 128))
-    return HY3MOE_ERR_UNSUPPORTED;
-  if (c->act_format != HY3MOE_AFMT_DTYPE && c->act_format != HY3MOE_AFMT_FP8_STATIC &&
-      c->act_format != HY3MOE_AFMT_MXFP8)
-    return HY3MOE_ERR_INVALID;
-  // Dynamic MXFP8 activations go with MXFP4 weights.
-  if (c->act_format == HY3MOE_AFMT_MXFP8 && c->w_format != HY3MOE_WFMT_MXFP4)
-    return HY3MOE_ERR_UNSUPPORTED;
-  // Static FP8 activations go with FP8 weights.
-  if (c->act_format == HY3MOE_AFMT_FP8_STATIC && c->w_format != HY3MOE_WFMT_FP8_E4M3)
-    return HY3MOE_ERR_UNSUPPORTED;
+  int rc = validate_fmt(c, routed_fmt(c), c->I);
+  if (rc != HY3MOE_OK) return rc;
+  if (c->I_shared > 0) {
+    rc = validate_fmt(c, shared_fmt(c), c->I_shared);
+    if (rc != HY3MOE_OK) return rc;
+  }
   // The expert GEMMs address x and every expert matrix with 32-bit offsets.
   const uint64_t eb = c->dtype == HY3MOE_F32 ? 4 : 2, lim = uint64_t(1) << 32;
   const uint64_t Imax = c->I > c->I_shared ? c->I : c->I_shared;
@@ -68,11 +89,13 @@ int validate_cfg(const hy3moe_config *c) {
 }
 
 // GEMM path of a layer call: static FP8 activations run the large-tile
-// path's FP8 MFMAs, whose 128-value K stages need H, I, I_shared % 128 == 0.
+// path's FP8 MFMAs, whose 128-value K stages need H and the branch's
+// intermediate size % 128 == 0.
 int path_of(const hy3moe_config *c) {
-  const bool big_ok = c->act_format != HY3MOE_AFMT_FP8_STATIC ||
-                      (c->H % 128 == 0 && c->I % 128 == 0 && c->I_shared % 128 == 0);
-  return expert_path(c->T, c->K, c->E, big_ok);
+  const bool r_ok = c->act_format != HY3MOE_AFMT_FP8_STATIC || (c->H % 128 == 0 && c->I % 128 == 0);
+  const bool s_ok = c->I_shared == 0 || shared_fmt(c).act != HY3MOE_AFMT_FP8_STATIC ||
+                    (c->H % 128 == 0 && c->I_shared % 128 == 0);
+  return expert_path(c->T, c->K, c->E, r_ok && s_ok);
 }
 
 void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L) {
@@ -105,16 +128,28 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
     L->tile_rows = path == PATH_BIG ? BIG_ROWS : TILED_ROWS;
     L->max_tiles = (int32_t)((R + L->tile_rows - 1) / L->tile_rows + E + 1);
   }
-  L->tiles = off;       off += al((size_t)(2 * L->max_tiles + 1) * 4);
+  L->tiles = off;       off += al((size_t)(2 * L->max_tiles + 2) * 4);
   const int Imax = c->I > c->I_shared ? c->I : c->I_shared;
   const int eb = elt_bytes(c->dtype);
   L->h = off;           off += al((size_t)R * Imax * eb);
   L->y = off;           off += al((size_t)R * H * eb);  // fp16 (bf16 layers) or float32
-  if (c->act_format == HY3MOE_AFMT_FP8_STATIC || c->act_format == HY3MOE_AFMT_MXFP8) {
+  // quantised x of the routed branch (xq, xs) and, with formats of its own,
+  // of the shared branch (xq_shared, xs_shared); MXFP8 codes of h (hq, hs)
+  const BranchFmt rf = routed_fmt(c), sf = shared_fmt(c);
+  const bool mix = mixed(c);
+  if (rf.act != HY3MOE_AFMT_DTYPE || (!mix && sf.act != HY3MOE_AFMT_DTYPE)) {
     L->xq = off;        off += al((size_t)T * H * 2);
   }
-  if (c->act_format == HY3MOE_AFMT_MXFP8) {
+  if (rf.act == HY3MOE_AFMT_MXFP8) {
     L->xs = off;        off += al((size_t)T * H / 32);
+  }
+  if (mix && sf.act != HY3MOE_AFMT_DTYPE) {
+    L->xq_shared = off; off += al((size_t)T * H * 2);
+    if (sf.act == HY3MOE_AFMT_MXFP8) {
+      L->xs_shared = off; off += al((size_t)T * H / 32);
+    }
+  }
+  if (rf.act == HY3MOE_AFMT_MXFP8 || (c->I_shared > 0 && sf.act == HY3MOE_AFMT_MXFP8)) {
     L->hq = off;        off += al((size_t)R * Imax);
     L->hs = off;        off += al((size_t)R * Imax / 32);
   }
@@ -130,7 +165,7 @@ int check_launch(hipError_t e) { return e == hipSuccess ? HY3MOE_OK : HY3MOE_ERR
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 8; }
+int hy3moe_abi_version(void) { return 9; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {
@@ -215,6 +250,56 @@ int hy3moe_route_planes(const hy3moe_config *cfg, const void *x, const float *w_
                                     cfg->scale, cfg->renorm_eps, idx, weight, s));
 }
 
+// Pointer and alignment checks of one branch's weights (routed: the stacked
+// tensors; shared: the shared expert's).
+static int check_branch_weights(const hy3moe_weights *w, BranchFmt f, bool shared) {
+  if (f.w == HY3MOE_WFMT_FP8_E4M3) {
+    if (shared) {
+      if (!w->ws_scale) return HY3MOE_ERR_INVALID;
+      if (!al4(w->ws_scale)) return HY3MOE_ERR_ALIGN;
+    } else {
+      if (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale) return HY3MOE_ERR_INVALID;
+      if (!al4(w->w_gate_scale) || !al4(w->w_up_scale) || !al4(w->w_down_scale))
+        return HY3MOE_ERR_ALIGN;
+    }
+  }
+  if (f.w == HY3MOE_WFMT_MXFP4) {
+    const uint8_t *g = shared ? w->ws_gate_mx : w->w_gate_mx, *u = shared ? w->ws_up_mx : w->w_up_mx,
+                  *d = shared ? w->ws_down_mx : w->w_down_mx;
+    if (!g || !u || !d) return HY3MOE_ERR_INVALID;
+    if (!al16(g) || !al16(u) || !al16(d)) return HY3MOE_ERR_ALIGN;
+  }
+  if (f.act == HY3MOE_AFMT_FP8_STATIC) {
+    if (!w->x_scale || !w->h_scale) return HY3MOE_ERR_INVALID;
+    if (!al4(w->x_scale) || !al4(w->h_scale)) return HY3MOE_ERR_ALIGN;
+  }
+  return HY3MOE_OK;
+}
+
+// The format-dependent fields of one branch's expert GEMM (gate-up or down).
+static void set_branch_weights(ExpertArgs &ea, const hy3moe_weights *w, BranchFmt f,
+                               bool gate_up, bool has_shared) {
+  const bool fp8 = f.w == HY3MOE_WFMT_FP8_E4M3, fp4 = f.w == HY3MOE_WFMT_MXFP4;
+  const bool a8 = f.act == HY3MOE_AFMT_FP8_STATIC;
+  ea.w0 = gate_up ? w->w_gate : w->w_down;
+  ea.w1 = gate_up ? w->w_up : nullptr;
+  ea.ws0 = gate_up ? w->ws_gate : w->ws_down;
+  ea.ws1 = gate_up ? w->ws_up : nullptr;
+  ea.w_fp8 = fp8 ? 1 : 0;
+  ea.sc0 = fp8 ? (gate_up ? w->w_gate_scale : w->w_down_scale) : nullptr;
+  ea.sc1 = fp8 && gate_up ? w->w_up_scale : nullptr;
+  ea.ssc0 = fp8 && has_shared ? w->ws_scale + (gate_up ? 0 : 2) : nullptr;
+  ea.ssc1 = fp8 && has_shared && gate_up ? w->ws_scale + 1 : nullptr;
+  ea.a8 = a8 ? 1 : 0;
+  ea.xs = a8 ? w->x_scale : nullptr;
+  ea.hs = a8 ? w->h_scale : nullptr;
+  ea.w_fp4 = fp4 ? 1 : 0;
+  ea.mx0 = fp4 ? (gate_up ? w->w_gate_mx : w->w_down_mx) : nullptr;
+  ea.mx1 = fp4 && gate_up ? w->w_up_mx : nullptr;
+  ea.mxs0 = fp4 && has_shared ? (gate_up ? w->ws_gate_mx : w->ws_down_mx) : nullptr;
+  ea.mxs1 = fp4 && has_shared && gate_up ? w->ws_up_mx : nullptr;
+}
+
 static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
                         void *out, int32_t *idx_out, float *weight_out, void *workspace,
                         size_t ws_bytes, void *stream, void *const *events) {
@@ -233,28 +318,11 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
     return HY3MOE_ERR_ALIGN;
   if (has_shared && (!al16(w->ws_gate) || !al16(w->ws_up) || !al16(w->ws_down)))
     return HY3MOE_ERR_ALIGN;
-  const bool fp8 = cfg->w_format == HY3MOE_WFMT_FP8_E4M3;
-  if (fp8) {
-    if (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale || (has_shared && !w->ws_scale))
-      return HY3MOE_ERR_INVALID;
-    if (!al4(w->w_gate_scale) || !al4(w->w_up_scale) || !al4(w->w_down_scale) ||
-        (has_shared && !al4(w->ws_scale)))
-      return HY3MOE_ERR_ALIGN;
-  }
-  const bool fp4 = cfg->w_format == HY3MOE_WFMT_MXFP4;
-  if (fp4) {
-    if (!w->w_gate_mx || !w->w_up_mx || !w->w_down_mx ||
-        (has_shared && (!w->ws_gate_mx || !w->ws_up_mx || !w->ws_down_mx)))
-      return HY3MOE_ERR_INVALID;
-    if (!al16(w->w_gate_mx) || !al16(w->w_up_mx) || !al16(w->w_down_mx) ||
-        (has_shared && (!al16(w->ws_gate_mx) || !al16(w->ws_up_mx) || !al16(w->ws_down_mx))))
-      return HY3MOE_ERR_ALIGN;
-  }
-  const bool a8 = cfg->act_format == HY3MOE_AFMT_FP8_STATIC;
-  if (a8) {
-    if (!w->x_scale || !w->h_scale) return HY3MOE_ERR_INVALID;
-    if (!al4(w->x_scale) || !al4(w->h_scale)) return HY3MOE_ERR_ALIGN;
-  }
+  const BranchFmt rf = routed_fmt(cfg), sf = shared_fmt(cfg);
+  const bool mix = mixed(cfg);
+  rc = check_branch_weights(w, rf, false);
+  if (rc == HY3MOE_OK && has_shared) rc = check_branch_weights(w, sf, true);
+  if (rc != HY3MOE_OK) return rc;
   hy3moe_ws_layout L;
   compute_layout(cfg, 1, &L);
   if (ws_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
@@ -285,28 +353,46 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   if (rc) return rc;
   mark();
 
-  // 3. permutation (with static FP8 activations, preceded by the
-  // quantisation of x, which needs no routing: once for every gate-up GEMM,
-  // as code bytes for the large-tile path's FP8 MFMAs, else as their bf16
-  // values)
+  // 3. quantisation of x (needs no routing) for each branch that quantises
+  // its activations, then the permutation.  A branch is the routed experts
+  // (group selection GRP_ROUTED), or the shared expert when it has formats
+  // of its own (GRP_SHARED); otherwise one launch covers both (GRP_ALL).
   const int path = path_of(cfg);
-  const bool amx = cfg->act_format == HY3MOE_AFMT_MXFP8;
-  const void *act = x;
-  // MXFP8: codes and scales for the block-scaled MFMAs of the weight-streaming
-  // and large-tile paths, the bf16 values for the tiled path
-  const bool amx_codes = amx && path != PATH_TILED;
-  if (amx) {
-    rc = check_launch(launch_quant_mxfp8(x, (int64_t)T * H, ws + L.xq,
-                                         reinterpret_cast<uint8_t *>(ws + L.xs),
-                                         amx_codes ? 0 : 1, s));
+  const int Imax = cfg->I > cfg->I_shared ? cfg->I : cfg->I_shared;
+  const int64_t N = (int64_t)T * K;
+  const int64_t R = N + (has_shared ? T : 0);
+  struct Branch {
+    BranchFmt f;
+    int grp_sel;
+    int64_t r0, r1;            // its rows of h and y
+    const void *act;           // its x: as given, or quantised
+    const uint8_t *act_sc;     // MXFP8 scales of its x
+    char *xq;                  // where its quantised x goes
+    uint8_t *xs;
+  };
+  Branch br[2];
+  int nbr = 0;
+  br[nbr++] = {rf, mix ? GRP_ROUTED : GRP_ALL, 0, mix ? N : R, x, nullptr, ws + L.xq,
+               reinterpret_cast<uint8_t *>(ws + L.xs)};
+  if (mix)
+    br[nbr++] = {sf, GRP_SHARED, N, R, x, nullptr, ws + L.xq_shared,
+                 reinterpret_cast<uint8_t *>(ws + L.xs_shared)};
+  for (int b = 0; b < nbr; ++b) {
+    Branch &B = br[b];
+    if (B.f.act == HY3MOE_AFMT_MXFP8) {
+      // codes and scales for the block-scaled MFMAs of the weight-streaming
+      // and large-tile paths, the bf16 values for the tiled path
+      rc = check_launch(launch_quant_mxfp8(x, (int64_t)T * H, B.xq, B.xs,
+                                           path != PATH_TILED ? 0 : 1, s));
+      B.act = B.xq;
+      B.act_sc = B.xs;
+    } else if (B.f.act == HY3MOE_AFMT_FP8_STATIC) {
+      // code bytes for the large-tile path's FP8 MFMAs, else their bf16 values
+      rc = check_launch(launch_quant_e4m3(x, cfg->dtype, (int64_t)T * H, w->x_scale, B.xq,
+                                          path == PATH_BIG ? 0 : 1, s));
+      B.act = B.xq;
+    }
     if (rc) return rc;
-    act = ws + L.xq;
-  }
-  if (a8) {
-    rc = check_launch(launch_quant_e4m3(x, cfg->dtype, (int64_t)T * H, w->x_scale, ws + L.xq,
-                                        path == PATH_BIG ? 0 : 1, s));
-    if (rc) return rc;
-    act = ws + L.xq;
   }
   PermArgs pa;
   pa.idx = idx;
@@ -322,71 +408,77 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   pa.tile_rows = L.tile_rows;
   pa.max_tiles = L.max_tiles;
   pa.sort_tiles = path != PATH_SKINNY;
+  pa.shared_last = mix ? 1 : 0;
   rc = check_launch(launch_permute(pa, s));
   if (rc) return rc;
   mark();
 
   // 4-5. grouped experts
-  const int Imax = cfg->I > cfg->I_shared ? cfg->I : cfg->I_shared;
   ExpertArgs ea;
   ea.sorted_token = pa.sorted_token;
   ea.offsets = pa.offsets;
   ea.tiles = pa.tiles;
   ea.E = E; ea.H = H; ea.I = cfg->I; ea.I_shared = cfg->I_shared; ea.ldh = Imax;
   ea.max_tiles = L.max_tiles;
-  ea.n_rows = (int)((int64_t)T * K + (has_shared ? T : 0));
+  ea.n_rows = (int)R;
   ea.n_tok = T;
-  ea.act = act; ea.w0 = w->w_gate; ea.w1 = w->w_up; ea.ws0 = w->ws_gate; ea.ws1 = w->ws_up;
-  // W4A8 on the large-tile path: the gate-up epilogue quantises h itself
-  const bool h_codes_fused = amx_codes && path == PATH_BIG;
-  ea.out = h_codes_fused ? ws + L.hq : ws + L.h;
-  ea.out_sc = h_codes_fused ? reinterpret_cast<uint8_t *>(ws + L.hs) : nullptr;
-  ea.w_fp8 = fp8 ? 1 : 0;
-  ea.sc0 = fp8 ? w->w_gate_scale : nullptr;
-  ea.sc1 = fp8 ? w->w_up_scale : nullptr;
-  ea.ssc0 = fp8 && has_shared ? w->ws_scale : nullptr;
-  ea.ssc1 = fp8 && has_shared ? w->ws_scale + 1 : nullptr;
-  ea.a8 = a8 ? 1 : 0;
-  ea.xs = a8 ? w->x_scale : nullptr;
-  ea.hs = a8 ? w->h_scale : nullptr;
-  ea.amx = amx_codes ? 1 : 0;
-  ea.act_sc = amx ? reinterpret_cast<const uint8_t *>(ws + L.xs) : nullptr;
-  ea.w_fp4 = fp4 ? 1 : 0;
-  ea.mx0 = fp4 ? w->w_gate_mx : nullptr;
-  ea.mx1 = fp4 ? w->w_up_mx : nullptr;
-  ea.mxs0 = fp4 && has_shared ? w->ws_gate_mx : nullptr;
-  ea.mxs1 = fp4 && has_shared ? w->ws_up_mx : nullptr;
-  rc = check_launch(launch_gate_up(ea, cfg->dtype, T, path, s));
-  if (rc) return rc;
-  mark();
-  ea.act = ws + L.h; ea.w0 = w->w_down; ea.w1 = nullptr; ea.ws0 = w->ws_down; ea.ws1 = nullptr;
-  ea.out_sc = nullptr;
-  if (amx) {   // h, dynamic MXFP8 per 32 along I: codes + scales, or bf16 values in place
-    const int64_t nh = ((int64_t)T * K + (has_shared ? T : 0)) * Imax;
-    if (h_codes_fused) {
-      ea.act = ws + L.hq;
-      ea.act_sc = reinterpret_cast<const uint8_t *>(ws + L.hs);
-    } else if (amx_codes) {
-      rc = check_launch(launch_quant_mxfp8(ws + L.h, nh, ws + L.hq,
-                                           reinterpret_cast<uint8_t *>(ws + L.hs), 0, s));
-      ea.act = ws + L.hq;
-      ea.act_sc = reinterpret_cast<const uint8_t *>(ws + L.hs);
-    } else {
-      rc = check_launch(launch_quant_mxfp8(ws + L.h, nh, ws + L.h, nullptr, 1, s));
-    }
+  // per branch: MXFP8 codes for the block-scaled MFMAs (not the tiled path),
+  // and on the large-tile path h quantised by the gate-up epilogue itself.
+  // h of every branch shares one buffer by rows; a branch that stores
+  // 1-byte codes there (static FP8 on the large-tile path: row r at byte
+  // r * ldh) is shifted by r0 * ldh bytes, past the 2-byte rows of the
+  // rows before it.
+  bool amx_codes[2], h_fused[2];
+  char *hbase[2];
+  for (int b = 0; b < nbr; ++b) {
+    const Branch &B = br[b];
+    const bool amx = B.f.act == HY3MOE_AFMT_MXFP8;
+    amx_codes[b] = amx && path != PATH_TILED;
+    h_fused[b] = amx_codes[b] && path == PATH_BIG;
+    hbase[b] = ws + L.h +
+               (B.f.act == HY3MOE_AFMT_FP8_STATIC && path == PATH_BIG ? B.r0 * Imax : 0);
+    set_branch_weights(ea, w, B.f, true, has_shared);
+    ea.grp_sel = B.grp_sel;
+    ea.act = B.act;
+    ea.amx = amx_codes[b] ? 1 : 0;
+    ea.act_sc = amx ? B.act_sc : nullptr;
+    ea.out = h_fused[b] ? ws + L.hq : hbase[b];
+    ea.out_sc = h_fused[b] ? reinterpret_cast<uint8_t *>(ws + L.hs) : nullptr;
+    rc = check_launch(launch_gate_up(ea, cfg->dtype, T, path, s));
     if (rc) return rc;
   }
-  ea.out = ws + L.y;
-  ea.sc0 = fp8 ? w->w_down_scale : nullptr;
-  ea.sc1 = nullptr;
-  ea.ssc0 = fp8 && has_shared ? w->ws_scale + 2 : nullptr;
-  ea.ssc1 = nullptr;
-  ea.mx0 = fp4 ? w->w_down_mx : nullptr;
-  ea.mx1 = nullptr;
-  ea.mxs0 = fp4 && has_shared ? w->ws_down_mx : nullptr;
-  ea.mxs1 = nullptr;
-  rc = check_launch(launch_down(ea, cfg->dtype, T, path, s));
-  if (rc) return rc;
+  mark();
+  for (int b = 0; b < nbr; ++b) {
+    const Branch &B = br[b];
+    set_branch_weights(ea, w, B.f, false, has_shared);
+    ea.grp_sel = B.grp_sel;
+    ea.act = hbase[b];
+    ea.amx = amx_codes[b] ? 1 : 0;
+    ea.act_sc = nullptr;
+    ea.out_sc = nullptr;
+    if (B.f.act == HY3MOE_AFMT_MXFP8) {
+      // h, dynamic MXFP8 per 32 along I over the branch's rows: codes and
+      // scales, or the bf16 values in place
+      const int64_t h0 = B.r0 * Imax, nh = (B.r1 - B.r0) * Imax;
+      if (h_fused[b]) {
+        ea.act = ws + L.hq;
+        ea.act_sc = reinterpret_cast<const uint8_t *>(ws + L.hs);
+      } else if (amx_codes[b]) {
+        rc = check_launch(launch_quant_mxfp8(ws + L.h + h0 * 2, nh, ws + L.hq + h0,
+                                             reinterpret_cast<uint8_t *>(ws + L.hs) + h0 / 32, 0,
+                                             s));
+        ea.act = ws + L.hq;
+        ea.act_sc = reinterpret_cast<const uint8_t *>(ws + L.hs);
+      } else {
+        rc = check_launch(launch_quant_mxfp8(ws + L.h + h0 * 2, nh, ws + L.h + h0 * 2, nullptr,
+                                             1, s));
+      }
+      if (rc) return rc;
+    }
+    ea.out = ws + L.y;
+    rc = check_launch(launch_down(ea, cfg->dtype, T, path, s));
+    if (rc) return rc;
+  }
   mark();
 
   // 6. combine

@@ -25,6 +25,8 @@ constexpr int MAX_KSPLIT = 16;      // router K-slices (partial logit sets)
 constexpr int BIG_ROWS = 256;       // rows per tile of the large-tile path
 constexpr int BIG_MIN_AVG_ROWS = 192;  // mean routed rows per expert that selects it
 
+enum { GRP_ALL = 0, GRP_ROUTED = 1, GRP_SHARED = 2 };
+
 // Which expert-GEMM path runs for a batch (the tile list is built for it).
 enum { PATH_SKINNY = 0, PATH_TILED = 1, PATH_BIG = 2 };
 // big_ok = false keeps batches off the large-tile path (static FP8
@@ -65,9 +67,10 @@ struct PermArgs {
   int32_t *offsets;       // [E+2]
   int32_t *sorted_token;  // [R]
   int32_t *pos_of;        // [T*K]
-  int32_t *tiles;         // [2*max_tiles + 1]
+  int32_t *tiles;         // [2*max_tiles + 2]: pairs, tile count, routed tile count
   int T, K, E, T_shared, nchunks, tile_rows, max_tiles;
   int sort_tiles;         // tile list largest groups first (else group order)
+  int shared_last;        // the shared expert's tiles after every routed tile
 };
 hipError_t launch_permute(const PermArgs &a, hipStream_t stream);
 
@@ -81,10 +84,15 @@ struct ExpertArgs {
   void *out;              // gate-up: h [R][ldh]; down: y [R][H] (fp16 for bf16 layers)
   const int32_t *sorted_token;
   const int32_t *offsets;
-  const int32_t *tiles;   // (group, first row) pairs, then the tile count
+  const int32_t *tiles;   // (group, first row) pairs, then the tile count and the
+                          // routed tile count
   int E, H, I, I_shared, ldh, max_tiles;
   int n_rows;             // rows of sorted_token (T K routed + T shared)
   int n_tok;              // T (rows of x)
+  // Groups this launch computes: GRP_ALL, GRP_ROUTED (the tiles before the
+  // routed tile count) or GRP_SHARED (the tiles after it); the last two need
+  // a tile list made with shared_last.
+  int grp_sel;
   // FP8 E4M3 expert weights (w_fp8 = 1): w0/w1/ws0/ws1 hold bytes and the
   // weight is scale * value, with scales sc0[g] / sc1[g] for routed group g
   // and *ssc0 / *ssc1 for the shared expert (gate-up: gate, up; down: down).
@@ -111,6 +119,15 @@ struct ExpertArgs {
   int a8;
   const float *xs, *hs;
 };
+// The slice of the tile list a launch walks (ExpertArgs::grp_sel): first
+// tile index and tile count.
+__device__ __forceinline__ void tile_slice(const ExpertArgs &a, const int32_t *tiles, int &base,
+                                           int &n) {
+  const int total = tiles[2 * a.max_tiles], routed = tiles[2 * a.max_tiles + 1];
+  base = a.grp_sel == GRP_SHARED ? routed : 0;
+  n = a.grp_sel == GRP_ROUTED ? routed : (a.grp_sel == GRP_SHARED ? total - routed : total);
+}
+
 hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);
 hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);
 

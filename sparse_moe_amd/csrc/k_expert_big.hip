@@ -407,7 +407,9 @@ __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_
   // on XCD b % 8); each XCD takes a contiguous run of `per` logical tiles
   // (`per` from the device-side tile count, so every XCD gets an equal share of
   // real tiles), and its workgroups walk that run with a stride of their count.
-  const int n_tiles = a.tiles[2 * a.max_tiles];
+  int tbase, n_tiles;   // this launch's slice of the tile list (grp_sel)
+  tile_slice(a, a.tiles, tbase, n_tiles);
+  a.tiles += 2 * tbase;
   const int per = ((n_tiles + BAND - 1) / BAND * (BAND * n_col_tiles) + 7) >> 3;
   const int xcd = blockIdx.x & 7, nb = gridDim.x >> 3;
   int r = blockIdx.x >> 3;
@@ -652,7 +654,9 @@ __global__ __launch_bounds__(512, 1) void expert_big_w4a8_kernel(ExpertArgs a, i
   static_assert(W4_SC + (BW + BTK) / 4 <= ROWS * CH, "W4A8 stage buffer");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_tiles = a.tiles[2 * a.max_tiles];
+  int tbase, n_tiles;   // this launch's slice of the tile list (grp_sel)
+  tile_slice(a, a.tiles, tbase, n_tiles);
+  a.tiles += 2 * tbase;
   const int per = ((n_tiles + BAND - 1) / BAND * (BAND * n_col_tiles) + 7) >> 3;
   const int xcd = blockIdx.x & 7, nb = gridDim.x >> 3;
   int r = blockIdx.x >> 3;

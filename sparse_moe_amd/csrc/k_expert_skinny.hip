@@ -253,7 +253,7 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
 
 // LDS bytes of the unit metadata a workgroup stages (see the kernel).
 inline size_t meta_lds_bytes(const ExpertArgs &a, bool gate_up) {
-  return 4 * ((size_t)2 * a.max_tiles + 1 + a.E + 2 + (gate_up ? a.n_rows : 0));
+  return 4 * ((size_t)2 * a.max_tiles + 2 + a.E + 2 + (gate_up ? a.n_rows : 0));
 }
 
 // Threads per workgroup: 256 (two workgroups per CU), or 512 with the LDS
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   // wavefront's next unit reads LDS instead of a chain of dependent global
   // loads, which held back the unit's first weight loads at every change.
   extern __shared__ int32_t meta[];
-  const int n_t = 2 * a_in.max_tiles + 1, n_o = a_in.E + 2;
+  const int n_t = 2 * a_in.max_tiles + 2, n_o = a_in.E + 2;
   for (int i = threadIdx.x; i < n_t; i += NT) meta[i] = a_in.tiles[i];
   for (int i = threadIdx.x; i < n_o; i += NT) meta[n_t + i] = a_in.offsets[i];
   if (GATE_UP)
@@ -292,7 +292,9 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   }
   __syncthreads();
   ExpertArgs a = a_in;
-  a.tiles = meta;
+  int tbase, n_tiles;   // this launch's slice of the tile list (grp_sel)
+  tile_slice(a_in, meta, tbase, n_tiles);
+  a.tiles = meta + 2 * tbase;
   a.offsets = meta + n_t;
   a.sorted_token = meta + n_t + n_o;
   constexpr int U = steps_per_set<MT, WF>();   // 64-byte K steps per row per register set
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   // MFMA is a whole-wavefront operation: it must never sit under a per-lane
   // EXEC mask that is expected to switch it off.)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_units = __builtin_amdgcn_readfirstlane(a.tiles[2 * a.max_tiles]) * n_col_blocks;
+  const int n_units = __builtin_amdgcn_readfirstlane(n_tiles) * n_col_blocks;
   const int nw = gridDim.x * WPB, w = blockIdx.x * WPB + wave;
   const int kmax = n_units / nw + 1;
   // Wavefront ids interleave the XCDs (block b runs on XCD b % 8), so the

@@ -47,7 +47,9 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
   __shared__ uint4 lds[2][(BR + BT) * CHUNKS];   // 2 x 32 KB
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_tiles = a.tiles[2 * a.max_tiles];
+  int tbase, n_tiles;   // this launch's slice of the tile list (grp_sel)
+  tile_slice(a, a.tiles, tbase, n_tiles);
+  a.tiles += 2 * tbase;
   const int tile = blockIdx.x / n_col_tiles;
   const int ct = blockIdx.x % n_col_tiles;
   if (tile >= n_tiles) return;

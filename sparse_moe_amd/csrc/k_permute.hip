@@ -118,10 +118,13 @@ __device__ void block_exclusive_scan(int *v, int n, int *total) {
 
 // From per-group row counts cnt[0..E] (LDS, group E = shared expert) write
 // counts, offsets and the row-tile list (largest groups first when
-// sort_tiles, else in group order) and leave the row offsets in
-// off[0..E+1] (LDS).  Called by all 256 threads of one block.
+// sort_tiles, else in group order; with shared_last the shared expert's
+// tiles come after every routed tile, whatever its size) and leave the row
+// offsets in off[0..E+1] (LDS).  The list ends with the tile count and the
+// count of routed tiles (the tiles before the shared expert's when
+// shared_last).  Called by all 256 threads of one block.
 __device__ void scan_groups(int *cnt, int *off, int E, int tile_rows, int max_tiles,
-                            int sort_tiles, int32_t *__restrict__ counts,
+                            int sort_tiles, int shared_last, int32_t *__restrict__ counts,
                             int32_t *__restrict__ offsets, int32_t *__restrict__ tiles) {
   __shared__ __attribute__((aligned(16))) int ntile[MAXG + 3];   // padded to whole int4s
   __shared__ int order[MAXG], tstart[MAXG + 1];
@@ -135,12 +138,22 @@ __device__ void scan_groups(int *cnt, int *off, int E, int tile_rows, int max_ti
   for (int g = tid; g < (G + 3) / 4 * 4; g += 256)
     ntile[g] = g < G ? (cnt[g] + tile_rows - 1) / tile_rows : -1;   // -1: never counted
   __syncthreads();
+  // shared_last: the shared expert takes no part in the ranking (-1) and is
+  // placed last; its count is restored below
+  const int shared_tiles = ntile[E];
+  __syncthreads();
+  if (shared_last && sort_tiles && tid == 0) ntile[E] = -1;
+  __syncthreads();
   // Rank of group g: groups with more tiles, or as many and a lower index.
   // Four counts per LDS read, several reads in flight.
   const int4 *nt4 = reinterpret_cast<const int4 *>(ntile);
   if (!sort_tiles) {
     for (int g = tid; g < G; g += 256) order[g] = g;
   } else for (int g = tid; g < G; g += 256) {
+    if (shared_last && g == E) {
+      order[E] = E;
+      continue;
+    }
     const int mine = ntile[g];
     int r = 0;
 #pragma unroll 8
@@ -154,6 +167,8 @@ __device__ void scan_groups(int *cnt, int *off, int E, int tile_rows, int max_ti
     }
     order[r] = g;
   }
+  __syncthreads();
+  if (tid == 0) ntile[E] = shared_tiles;
   __syncthreads();
   for (int r = tid; r < G; r += 256) tstart[r] = ntile[order[r]];
   __syncthreads();
@@ -172,13 +187,17 @@ __device__ void scan_groups(int *cnt, int *off, int E, int tile_rows, int max_ti
       tiles[2 * ts + 1] = off[g] + i * tile_rows;
     }
   }
-  if (tid == 0) tiles[2 * max_tiles] = min(total_tiles, max_tiles);
+  if (tid == 0) {
+    tiles[2 * max_tiles] = min(total_tiles, max_tiles);
+    tiles[2 * max_tiles + 1] = min(shared_last ? total_tiles - shared_tiles : total_tiles, max_tiles);
+  }
   __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t *__restrict__ hist, int nchunks,
                                                         int E, int T_shared, int tile_rows,
                                                         int max_tiles, int sort_tiles,
+                                                        int shared_last,
                                                         int32_t *__restrict__ counts,
                                                         int32_t *__restrict__ offsets,
                                                         int32_t *__restrict__ tiles) {
@@ -204,7 +223,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t *__restrict__ hi
   }
   if (tid == 0) cnt[E] = T_shared;
   __syncthreads();
-  scan_groups(cnt, off, E, tile_rows, max_tiles, sort_tiles, counts, offsets, tiles);
+  scan_groups(cnt, off, E, tile_rows, max_tiles, sort_tiles, shared_last, counts, offsets, tiles);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
@@ -229,7 +248,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
 __global__ __launch_bounds__(256) void perm_small_kernel(const int32_t *__restrict__ idx, int N,
                                                          int K, int E, int nchunks, int T_shared,
                                                          int tile_rows, int max_tiles,
-                                                         int sort_tiles,
+                                                         int sort_tiles, int shared_last,
                                                          int32_t *__restrict__ counts,
                                                          int32_t *__restrict__ offsets,
                                                          int32_t *__restrict__ tiles,
@@ -255,7 +274,7 @@ __global__ __launch_bounds__(256) void perm_small_kernel(const int32_t *__restri
   }
   if (tid == 0) tot[E] = T_shared;
   __syncthreads();
-  scan_groups(tot, off, E, tile_rows, max_tiles, sort_tiles, counts, offsets, tiles);
+  scan_groups(tot, off, E, tile_rows, max_tiles, sort_tiles, shared_last, counts, offsets, tiles);
   for (int e = lane; e < E; e += 64) cnt[wave][e] += off[e];
   __syncthreads();
   if (wave < nchunks) scatter_chunk(idx_s, N, K, wave, lane, cnt[wave], sorted_token, pos_of);
@@ -268,7 +287,8 @@ hipError_t launch_permute(const PermArgs &a, hipStream_t stream) {
   const int N = a.T * a.K;
   if (a.nchunks <= 4) {
     hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(256), 0, stream, a.idx, N, a.K, a.E,
-                       a.nchunks, a.T_shared, a.tile_rows, a.max_tiles, a.sort_tiles, a.counts,
+                       a.nchunks, a.T_shared, a.tile_rows, a.max_tiles, a.sort_tiles,
+                       a.shared_last, a.counts,
                        a.offsets,
                        a.tiles, a.sorted_token, a.pos_of);
     return hipGetLastError();
@@ -277,7 +297,8 @@ hipError_t launch_permute(const PermArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL(perm_hist_kernel, dim3(blocks), dim3(256), 0, stream, a.idx, N, a.E,
                      a.nchunks, a.hist);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, stream, a.hist, a.nchunks, a.E,
-                     a.T_shared, a.tile_rows, a.max_tiles, a.sort_tiles, a.counts, a.offsets,
+                     a.T_shared, a.tile_rows, a.max_tiles, a.sort_tiles, a.shared_last, a.counts,
+                     a.offsets,
                      a.tiles);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(blocks), dim3(256), 0, stream, a.idx, N, a.K,
                      a.E, a.nchunks, a.hist, a.offsets, a.T_shared, a.sorted_token, a.pos_of);

@@ -22,25 +22,28 @@ def to_torch(a: np.ndarray, dtype: str, device):
 
 
 def upload_weights(inp: MoEInputs, device) -> Dict[str, object]:
-    """Router weight, expert bias (if any), stacked routed experts and the shared expert."""
+    """Router weight, expert bias (if any), the stacked routed experts and the
+    shared expert, each branch in its own weight format, plus the static FP8
+    activation scales when a branch uses them."""
     import torch
     c = inp.cfg
+    d = {"w_router": torch.from_numpy(inp.w_router()).to(device)}
     if c.w_format == "mxfp4":
-        return _upload_mxfp4(inp, device)
-    if c.w_format == "fp8_e4m3":
-        d = _upload_fp8(inp, device)
-        return with_act_scales(inp, d, device) if c.act_format == "fp8_static" else d
-    wg, wu, wd = inp.stacked_experts()
-    d = {"w_router": torch.from_numpy(inp.w_router()).to(device),
-         "w_gate": to_torch(wg, c.dtype, device), "w_up": to_torch(wu, c.dtype, device),
-         "w_down": to_torch(wd, c.dtype, device)}
-    del wg, wu, wd
+        d.update(_routed_mxfp4(inp, device))
+    elif c.w_format == "fp8_e4m3":
+        d.update(_routed_fp8(inp, device))
+    else:
+        wg, wu, wd = inp.stacked_experts()
+        d.update({"w_gate": to_torch(wg, c.dtype, device), "w_up": to_torch(wu, c.dtype, device),
+                  "w_down": to_torch(wd, c.dtype, device)})
+        del wg, wu, wd
     b = inp.bias()
     if b is not None:
         d["expert_bias"] = torch.from_numpy(b).to(device)
-    sh = inp.shared()
-    if sh is not None:
-        d["ws_gate"], d["ws_up"], d["ws_down"] = (to_torch(a, c.dtype, device) for a in sh)
+    if c.I_shared:
+        d.update(_shared(inp, device))
+    if "fp8_static" in (c.act_format, c.sa_format if c.I_shared else c.act_format):
+        d = with_act_scales(inp, d, device)
     return d
 
 
@@ -63,46 +66,44 @@ def with_bias_of(inp: MoEInputs, weights: Dict[str, object], device) -> Dict[str
     return w
 
 
-def _upload_mxfp4(inp: MoEInputs, device) -> Dict[str, object]:
-    """MXFP4 expert codes (packed uint8) with their E8M0 block scales (uint8)."""
+def _routed_mxfp4(inp: MoEInputs, device) -> Dict[str, object]:
+    """MXFP4 routed experts: packed E2M1 codes (uint8) and E8M0 block scales (uint8)."""
     import torch
     wg, wu, wd, sg, su, sd = inp.stacked_experts_mxfp4()
-    d = {"w_router": torch.from_numpy(inp.w_router()).to(device)}
+    d = {}
     for k, a in (("w_gate", wg), ("w_up", wu), ("w_down", wd), ("w_gate_mx", sg),
                  ("w_up_mx", su), ("w_down_mx", sd)):
         d[k] = torch.from_numpy(a).to(device)
-    del wg, wu, wd, sg, su, sd
-    b = inp.bias()
-    if b is not None:
-        d["expert_bias"] = torch.from_numpy(b).to(device)
-    sh = inp.shared_mxfp4()
-    if sh is not None:
-        codes, scales = sh
+    return d
+
+
+def _routed_fp8(inp: MoEInputs, device) -> Dict[str, object]:
+    """FP8 E4M3 routed experts (uint8 codes) with their float32 scales."""
+    import torch
+    wg, wu, wd, sc = inp.stacked_experts_fp8()
+    return {"w_gate": torch.from_numpy(wg).to(device), "w_up": torch.from_numpy(wu).to(device),
+            "w_down": torch.from_numpy(wd).to(device),
+            "w_gate_scale": torch.from_numpy(np.ascontiguousarray(sc[0])).to(device),
+            "w_up_scale": torch.from_numpy(np.ascontiguousarray(sc[1])).to(device),
+            "w_down_scale": torch.from_numpy(np.ascontiguousarray(sc[2])).to(device)}
+
+
+def _shared(inp: MoEInputs, device) -> Dict[str, object]:
+    """The shared expert in its weight format."""
+    import torch
+    c = inp.cfg
+    d = {}
+    if c.sw_format == "mxfp4":
+        codes, scales = inp.shared_mxfp4()
         for k, a in zip(("ws_gate", "ws_up", "ws_down"), codes):
             d[k] = torch.from_numpy(a).to(device)
         for k, a in zip(("ws_gate_mx", "ws_up_mx", "ws_down_mx"), scales):
             d[k] = torch.from_numpy(a).to(device)
-    return d
-
-
-def _upload_fp8(inp: MoEInputs, device) -> Dict[str, object]:
-    """FP8 E4M3 expert codes (uint8) with their float32 scales."""
-    import torch
-    c = inp.cfg
-    wg, wu, wd, sc = inp.stacked_experts_fp8()
-    d = {"w_router": torch.from_numpy(inp.w_router()).to(device),
-         "w_gate": torch.from_numpy(wg).to(device), "w_up": torch.from_numpy(wu).to(device),
-         "w_down": torch.from_numpy(wd).to(device),
-         "w_gate_scale": torch.from_numpy(np.ascontiguousarray(sc[0])).to(device),
-         "w_up_scale": torch.from_numpy(np.ascontiguousarray(sc[1])).to(device),
-         "w_down_scale": torch.from_numpy(np.ascontiguousarray(sc[2])).to(device)}
-    del wg, wu, wd
-    b = inp.bias()
-    if b is not None:
-        d["expert_bias"] = torch.from_numpy(b).to(device)
-    sh = inp.shared_fp8()
-    if sh is not None:
-        codes, scales = sh
+    elif c.sw_format == "fp8_e4m3":
+        codes, scales = inp.shared_fp8()
         d["ws_gate"], d["ws_up"], d["ws_down"] = (torch.from_numpy(q).to(device) for q in codes)
         d["ws_scale"] = torch.from_numpy(np.array(scales, dtype=np.float32)).to(device)
+    else:
+        d["ws_gate"], d["ws_up"], d["ws_down"] = (to_torch(a, c.dtype, device)
+                                                  for a in inp.shared())
     return d

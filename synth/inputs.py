@@ -51,6 +51,10 @@ per 32 consecutive weights of a row: 2^(round(log2(1 / (2.2 sqrt(fan_in))))
 - j), j uniform in {0, 1}, so scale times value has about the spread of the
 bf16 weights.
 
+The shared expert may take formats of its own (``shared_w_format``,
+``shared_act_format``); its tensors are then drawn in those formats, from
+the same streams as above.
+
 Static FP8 activation scales (``act_format == "fp8_static"``, W8A8) stand
 in for calibrated ones: a1 = 4.5 / 448 for the layer input (x ~ N(0, 1):
 about 7 in a million values saturate) and a2[e] = (1 + U(0, 0.25)) * 12 / 448
@@ -123,6 +127,18 @@ class MoEConfig:
     w_format: str = "dtype"    # expert weights: "dtype" (as `dtype`), "fp8_e4m3" or "mxfp4"
     act_format: str = "dtype"  # expert activations: "dtype", "fp8_static" (W8A8) or
                                # "mxfp8" (dynamic, with MXFP4 weights: W4A8)
+    shared_w_format: Optional[str] = None    # the shared expert's, None: as the routed ones
+    shared_act_format: Optional[str] = None
+
+    @property
+    def sw_format(self) -> str:
+        """Weight format of the shared expert."""
+        return self.w_format if self.shared_w_format is None else self.shared_w_format
+
+    @property
+    def sa_format(self) -> str:
+        """Activation format of the shared expert."""
+        return self.act_format if self.shared_act_format is None else self.shared_act_format
 
     def with_T(self, T: int) -> "MoEConfig":
         return dataclasses.replace(self, T=int(T))
@@ -190,6 +206,19 @@ CONFIGS: Dict[str, MoEConfig] = {
                   I=1536, I_shared=1536, dtype="bf16",
                   route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                   bias_kind="skew", w_format="mxfp4", act_format="mxfp8"),
+    # Mixed precision in one layer: the routed experts at W4A8 (the MXFP4
+    # experts above, MXFP8 activations) and the shared expert at W8A8 (FP8
+    # E4M3 weights, static FP8 activations).
+    "hy3_decode_T16_mixed": MoEConfig("hy3_decode_T16_mixed", 13, 9, T=16, H=4096, E=192, K=8,
+                  I=1536, I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform", w_format="mxfp4",
+                  act_format="mxfp8", shared_w_format="fp8_e4m3",
+                  shared_act_format="fp8_static"),
+    "hy3_prefill_T8192_skew_mixed": MoEConfig("hy3_prefill_T8192_skew_mixed", 14, 9, T=8192,
+                  H=4096, E=192, K=8, I=1536, I_shared=1536, dtype="bf16",
+                  route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
+                  bias_kind="skew", w_format="mxfp4", act_format="mxfp8",
+                  shared_w_format="fp8_e4m3", shared_act_format="fp8_static"),
 }
 
 ROUTER_SWEEP_M = (2, 64, 512, 4096)
@@ -320,7 +349,7 @@ class MoEInputs:
         c = self.cfg
         if c.I_shared == 0:
             return None
-        if c.w_format != "dtype":
+        if c.sw_format != "dtype":
             raise ValueError("quantised expert weights: use shared_fp8() or shared_mxfp4()")
         k = ("shared",)
         if k not in self._cache:
@@ -469,10 +498,12 @@ def random_small(seed: int, T: int, H: int, E: int, K: int, I: int, I_shared: in
                  dtype: str = "f32", route_mode: int = ROUTE_SIGMOID_BIAS,
                  scale: float = HY3_SCALE, renorm_eps: float = 0.0,
                  bias_kind: str = "uniform", w_format: str = "dtype",
-                 act_format: str = "dtype") -> MoEInputs:
+                 act_format: str = "dtype", shared_w_format: Optional[str] = None,
+                 shared_act_format: Optional[str] = None) -> MoEInputs:
     """A small ad-hoc workload with the same distributions (for property tests)."""
     cfg = MoEConfig(f"small_{seed}", 900 + (seed % 97), 900 + seed, T=T, H=H, E=E, K=K,
                     I=I, I_shared=I_shared, dtype=dtype, route_mode=route_mode,
                     scale=scale, renorm_eps=renorm_eps, bias_kind=bias_kind,
-                    w_format=w_format, act_format=act_format)
+                    w_format=w_format, act_format=act_format,
+                    shared_w_format=shared_w_format, shared_act_format=shared_act_format)
     return MoEInputs(cfg, seed)

@@ -56,7 +56,8 @@ def config_of(inp: MoEInputs, **kw) -> sm.hy3moe_config:
     c = inp.cfg
     d = dict(T=c.T, H=c.H, E=c.E, K=c.K, I=c.I, I_shared=c.I_shared, dtype=c.dtype,
              route_mode=c.route_mode, scale=c.scale, renorm_eps=c.renorm_eps,
-             w_format=c.w_format, act_format=c.act_format)
+             w_format=c.w_format, act_format=c.act_format,
+             shared_w_format=c.shared_w_format, shared_act_format=c.shared_act_format)
     d.update(kw)
     return sm.make_config(**d)
 
@@ -207,47 +208,80 @@ class WorkspaceActivations:
       values are then taken, as the GPU's picks are for near-tie tokens.
     """
 
-    def __init__(self, inp: MoEInputs, ws: torch.Tensor, L, codes_path: bool):
+    def __init__(self, inp: MoEInputs, ws: torch.Tensor, L, codes_path=None):
+        """codes_path: None for where the forward's GEMM path leaves h, or
+        (routed, shared) booleans that say so (checks of fake workspaces)."""
         c = inp.cfg
         self.E, self.K = c.E, c.K
-        self.a8, self.amx = a8_of(inp), amx_of(inp)
-        self.codes_path = codes_path
         self.ldh = max(c.I, c.I_shared)
         R = c.T * c.K + (c.T if c.I_shared else 0)
+        self.N = c.T * c.K
         i32 = lambda off, n: ws[off:off + 4 * n].cpu().numpy().view(np.int32)
         self.offsets = i32(L.offsets, c.E + 2)
         self.sorted_token = i32(L.sorted_token, R)
-        if self.amx and codes_path:
-            self.hq = ws[L.hq:L.hq + R * self.ldh].cpu().numpy().reshape(R, self.ldh)
-            self.hs = ws[L.hs:L.hs + R * self.ldh // 32].cpu().numpy().reshape(R, self.ldh // 32)
-        elif self.a8 and codes_path:
-            self.hq = ws[L.h:L.h + R * self.ldh].cpu().numpy().reshape(R, self.ldh)
-        else:       # the bf16 values of the codes
-            bits = ws[L.h:L.h + 2 * R * self.ldh].cpu().numpy().view(np.uint16)
-            self.hv = (bits.astype(np.uint32) << 16).view(np.float32).reshape(R, self.ldh)
-        # the FP8 and FP4 x FP8 MFMAs' accumulation error; bf16 MFMAs far closer
-        self.gemm = (1024 * 2.0 ** -23) if codes_path else 64 * 2.0 ** -24
+        # per branch (routed, shared): format, and where the forward left h.
+        # MXFP8: codes and block scales in hq / hs on the weight-streaming
+        # and large-tile paths; static FP8: codes in h (row r at byte r *
+        # ldh, past the earlier rows' 2-byte h when the shared expert has
+        # formats of its own) on the large-tile path.  Elsewhere h holds the
+        # bf16 values of the codes.
+        mixed = c.I_shared > 0 and (c.sw_format, c.sa_format) != (c.w_format, c.act_format)
+        self.fmt = {}
+        for i, (br, act) in enumerate((("routed", c.act_format), ("shared", c.sa_format))):
+            a8 = _a8(inp, act)
+            codes = L.tile_rows == 256 if a8 is not None else L.tile_rows != 128
+            if codes_path is not None:
+                codes = bool(codes_path[i])
+            self.fmt[br] = (a8, act == "mxfp8", codes)
+        self.R = R
+        self.ws, self.L = ws, L
+        self.h8_base = {"routed": 0, "shared": self.N * self.ldh if mixed else 0}
+        self._arr = {}
         self.n = self.n_amb = 0
 
-    def gpu_values(self, e, r0, r1, Ig):
+    def _get(self, key):
+        if key not in self._arr:
+            ws, L, R, ldh = self.ws, self.L, self.R, self.ldh
+            if key == "hq":
+                a = ws[L.hq:L.hq + R * ldh].cpu().numpy().reshape(R, ldh)
+            elif key == "hs":
+                a = ws[L.hs:L.hs + R * ldh // 32].cpu().numpy().reshape(R, ldh // 32)
+            elif key == "hv":
+                bits = ws[L.h:L.h + 2 * R * ldh].cpu().numpy().view(np.uint16)
+                a = (bits.astype(np.uint32) << 16).view(np.float32).reshape(R, ldh)
+            else:        # ("h8", byte offset of row 0)
+                o = L.h + key[1]
+                a = ws[o:o + R * ldh].cpu().numpy().reshape(R, ldh)
+            self._arr[key] = a
+        return self._arr[key]
+
+    def gpu_values(self, br, e, r0, r1, Ig):
         """The GPU's h_in of group e: the MXFP8 values, or the static scale
         times the E4M3 values (stored as codes or as their bf16 values)."""
-        if self.amx:   # codes and block scales, or their values in bf16 (exact)
-            if hasattr(self, "hv"):
-                return self.hv[r0:r1, :Ig].astype(np.float64)
-            return oracle.dequant_mxfp8(self.hq[r0:r1, :Ig], self.hs[r0:r1, :Ig // 32])
-        v = (self.hv[r0:r1, :Ig].astype(np.float64) if hasattr(self, "hv")
-             else oracle.fp8_e4m3_value(self.hq[r0:r1, :Ig]))
-        return np.float64(np.float32(self.a8[1][e])) * v
+        a8, amx, codes = self.fmt[br]
+        if amx:        # codes and block scales, or their values in bf16 (exact)
+            if not codes:
+                return self._get("hv")[r0:r1, :Ig].astype(np.float64)
+            return oracle.dequant_mxfp8(self._get("hq")[r0:r1, :Ig],
+                                        self._get("hs")[r0:r1, :Ig // 32])
+        v = (oracle.fp8_e4m3_value(self._get(("h8", self.h8_base[br]))[r0:r1, :Ig]) if codes
+             else self._get("hv")[r0:r1, :Ig].astype(np.float64))
+        return np.float64(np.float32(a8[1][e])) * v
 
     def __call__(self, e, tok, a, wg, wu, h, h_in):
         r0, r1 = self.offsets[e], self.offsets[e + 1]
         assert r1 - r0 == len(tok) and (self.sorted_token[r0:r1] == tok).all(), \
             f"group {e}: the GPU's rows are not the oracle's tokens"
+        br = "shared" if e == self.E else "routed"
+        a8, amx, codes = self.fmt[br]
+        if a8 is None and not amx:
+            return h_in          # this branch keeps its activations unquantised
         Ig = wg.shape[0]
-        got = self.gpu_values(e, r0, r1, Ig)
-        _, dh = h_error_bound(a, wg, wu, self.gemm)
-        if self.amx:
+        got = self.gpu_values(br, e, r0, r1, Ig)
+        # the FP8 and FP4 x FP8 MFMAs' accumulation error; bf16 MFMAs far closer
+        gemm = (1024 * 2.0 ** -23) if codes else 64 * 2.0 ** -24
+        _, dh = h_error_bound(a, wg, wu, gemm)
+        if amx:
             amb = oracle.round_bf16(h - dh) != oracle.round_bf16(h + dh)
             amb = np.repeat(amb.reshape(len(tok), -1, 32).any(axis=2), 32, axis=1)
             # the GPU's block scales (its largest code is in [256, 448]: the
@@ -261,7 +295,7 @@ class WorkspaceActivations:
             allowed = dh + 2.0 ** -8 * np.abs(h) + step + sat
             ok_amb = np.abs(got - h) <= allowed * (1 + 1e-12)
         else:
-            a2 = float(self.a8[1][e])
+            a2 = float(a8[1][e])
             # bf16 rounding and the quantisation are monotone: the valid
             # values are the grid values between those of the interval's
             # ends, and the code is ambiguous only where those differ
@@ -317,29 +351,45 @@ def expert_cache(inp: MoEInputs):
 
 
 def shared_f64(inp: MoEInputs):
-    """float64 (gate, up, down) of the shared expert, or None."""
-    if inp.cfg.w_format == "mxfp4":
-        sh = inp.shared_mxfp4()
-        return None if sh is None else tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(*sh))
-    if inp.cfg.w_format != "fp8_e4m3":
-        return inp.shared_f64()
-    sh = inp.shared_fp8()
-    if sh is None:
+    """float64 (gate, up, down) of the shared expert (in its own weight format), or None."""
+    fmt = inp.cfg.sw_format
+    if inp.cfg.I_shared == 0:
         return None
-    return tuple(oracle.dequant_fp8(q, s) for q, s in zip(*sh))
+    if fmt == "mxfp4":
+        return tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(*inp.shared_mxfp4()))
+    if fmt == "fp8_e4m3":
+        return tuple(oracle.dequant_fp8(q, s) for q, s in zip(*inp.shared_fp8()))
+    return inp.shared_f64()
+
+
+def _a8(inp: MoEInputs, fmt: str):
+    if fmt != "fp8_static":
+        return None
+    a1, a2 = inp.act_scales()
+    return float(a1), a2.astype(np.float64)
 
 
 def amx_of(inp: MoEInputs) -> bool:
-    """True for dynamic MXFP8 activations (W4A8)."""
+    """True for dynamic MXFP8 activations (W4A8) of the routed experts."""
     return inp.cfg.act_format == "mxfp8"
 
 
 def a8_of(inp: MoEInputs):
-    """(a1, a2) static FP8 activation scales for the oracle, or None."""
-    if inp.cfg.act_format != "fp8_static":
-        return None
-    a1, a2 = inp.act_scales()
-    return float(a1), a2.astype(np.float64)
+    """(a1, a2) static FP8 activation scales of the routed experts for the oracle, or None."""
+    return _a8(inp, inp.cfg.act_format)
+
+
+def quant_act(inp: MoEInputs) -> bool:
+    """Does either branch quantise its activations?"""
+    c = inp.cfg
+    return c.act_format != "dtype" or (c.I_shared > 0 and c.sa_format != "dtype")
+
+
+def act_kw(inp: MoEInputs) -> dict:
+    """The oracle's activation-format arguments of this workload (both branches)."""
+    c = inp.cfg
+    return dict(a8=a8_of(inp), amx=amx_of(inp), shared_a8=_a8(inp, c.sa_format),
+                shared_amx=c.sa_format == "mxfp8")
 
 
 def out_to_np(out: torch.Tensor) -> np.ndarray:

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 8
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 9
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -54,7 +54,8 @@ def test_abi_version_and_strerror(lib):
 def cfg_of(c, **kw):
     d = dict(T=c.T, H=c.H, E=c.E, K=c.K, I=c.I, I_shared=c.I_shared, dtype=c.dtype,
              route_mode=c.route_mode, scale=c.scale, renorm_eps=c.renorm_eps,
-             w_format=c.w_format, act_format=c.act_format)
+             w_format=c.w_format, act_format=c.act_format,
+             shared_w_format=c.shared_w_format, shared_act_format=c.shared_act_format)
     d.update(kw)
     return sm.make_config(**d)
 
@@ -76,13 +77,23 @@ def test_workspace_layout_is_consistent(lib, name):
     assert (L.w_planes > 0) == planes
     if planes:
         names.append("w_planes")
+    mixed = (c.sw_format, c.sa_format) != (c.w_format, c.act_format)
     assert (L.xq > 0) == (c.act_format != "dtype")
     if L.xq:
         names.append("xq")
         assert L.total - L.xq >= c.T * c.H * 2
-    assert (L.hq > 0) == (L.xs > 0) == (L.hs > 0) == (c.act_format == "mxfp8")
+    assert (L.xs > 0) == (c.act_format == "mxfp8")
+    assert (L.xq_shared > 0) == (mixed and c.sa_format != "dtype")
+    assert (L.xs_shared > 0) == (mixed and c.sa_format == "mxfp8")
+    for n in ("xq_shared", "xs_shared"):
+        if getattr(L, n):
+            names.append(n)
+    assert L.total - max(L.xq_shared, L.xs_shared) >= (c.T * c.H // 32 if L.xs_shared else 0)
+    assert (L.hq > 0) == (L.hs > 0) == ("mxfp8" in (c.act_format, c.sa_format))
+    if L.xs:
+        names.append("xs")
     if L.hq:
-        names += ["xs", "hq", "hs"]
+        names += ["hq", "hs"]
         assert L.hq - L.xs >= c.T * c.H // 32
         assert L.hs - L.hq >= R_of(c) * max(c.I, c.I_shared)
         assert L.total - L.hs >= R_of(c) * max(c.I, c.I_shared) // 32
@@ -402,3 +413,60 @@ def test_router_split_validates_on_the_host(lib):
     assert lib.hy3moe_router_split(ok, 192, 4000, 0, ok, n, None) == -2
     assert lib.hy3moe_router_split(ok + 8, 192, 4096, 0, ok, n, None) == -4
     assert lib.hy3moe_router_split(ok, 192, 4096, 0, ok + 4, n, None) == -4
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(shared_w_format=3), -1), (dict(shared_act_format=3), -1),
+    (dict(shared_w_format=-2), -1),
+    # a branch's formats follow the same rules: MXFP8 activations need MXFP4
+    # weights, static FP8 needs FP8 weights, MXFP4 needs I_shared % 128 == 0
+    (dict(shared_act_format="mxfp8"), -2),
+    (dict(shared_w_format="mxfp4", shared_act_format="fp8_static"), -2),
+    (dict(shared_w_format="mxfp4", I_shared=1536 + 64), -2),
+    (dict(w_format="dtype", act_format="dtype", shared_w_format=None,
+          shared_act_format="fp8_static"), -2),
+])
+def test_shared_formats_are_validated(lib, bad, code):
+    raw = {k: v for k, v in bad.items() if isinstance(v, int) and k.startswith("shared_")}
+    cfg = cfg_of(CONFIGS["hy3_decode_T16_mixed"],
+                 **{k: v for k, v in bad.items() if k not in raw})
+    for k, v in raw.items():         # enum values the binding has no name for
+        setattr(cfg, k, v)
+    assert sm.hy3moe_workspace_bytes(cfg, True) == 0
+    L = b.hy3moe_ws_layout()
+    assert lib.hy3moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == code
+
+
+def test_shared_formats_ignored_without_a_shared_expert(lib):
+    cfg = cfg_of(CONFIGS["hy3_decode_T16_mixed"], I_shared=0, shared_act_format="mxfp8")
+    L = sm.hy3moe_workspace_layout(cfg)
+    assert L.xq_shared == L.xs_shared == 0 and L.total > 0
+
+
+def test_mixed_layer_needs_each_branch_weights(lib):
+    """Routed W4A8 + shared W8A8: the routed E8M0 scales, the shared FP8
+    scales and the static activation scales are required; the shared E8M0
+    scales and the routed FP8 scales are not."""
+    cfg = cfg_of(CONFIGS["hy3_decode_T16_mixed"])
+    need = sm.hy3moe_workspace_bytes(cfg, True)
+    fw = lib.hy3moe_forward
+    names = b.WEIGHT_NAMES
+    full = {n: 4096 for n in names}
+    full["expert_bias"] = 4096
+    for n in ("w_router_planes", "w_gate_scale", "w_up_scale", "w_down_scale", "ws_gate_mx",
+              "ws_up_mx", "ws_down_mx"):
+        full[n] = None
+
+    def call(d):
+        w = b.hy3moe_weights(*[d[n] for n in names])
+        return fw(ctypes.byref(cfg), 4096, ctypes.byref(w), 8192, None, None, 4096, need - 1,
+                  None)
+
+    assert call(full) == -3                     # every check passed, then the workspace size
+    for n in ("ws_scale", "x_scale", "h_scale", "w_gate_mx", "w_up_mx", "w_down_mx"):
+        d = dict(full)
+        d[n] = None
+        assert call(d) == -1, n
+    d = dict(full)
+    d["ws_scale"] = 4098
+    assert call(d) == -4

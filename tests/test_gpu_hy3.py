@@ -17,8 +17,8 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (WorkspaceActivations, a8_of, amx_of, check_output, check_route,
-                      config_of, expert_fn, log, oracle_route, out_to_np, route_for_reference,
+from gpu_util import (WorkspaceActivations, act_kw, check_output, check_route, config_of,
+                      expert_fn, log, oracle_route, out_to_np, quant_act, route_for_reference,
                       shared_f64, to_torch, upload_weights, with_act_scales, with_bias_of)
 from synth import CONFIGS, ROUTER_SWEEP_M, MoEInputs
 
@@ -58,11 +58,9 @@ def layer_check(inp, dev, weights, workload_shape=True):
     gidx, gw = idx.cpu().numpy(), w.cpu().numpy()
     got = out_to_np(out)
     hook = None
-    if a8_of(inp) is not None or amx_of(inp):
+    if quant_act(inp):
         # quantised activations: the GPU's h codes, checked, where two are valid
-        L = sm.hy3moe_workspace_layout(cfg)
-        codes = L.tile_rows == 256 if a8_of(inp) is not None else L.tile_rows != 128
-        hook = WorkspaceActivations(inp, ws, L, codes)
+        hook = WorkspaceActivations(inp, ws, sm.hy3moe_workspace_layout(cfg))
     del out, x, ws
     log(f"  oracle route over all {c.T} tokens")
     r = oracle_route(inp)
@@ -74,7 +72,7 @@ def layer_check(inp, dev, weights, workload_shape=True):
         f"(mean {counts.mean():.1f}); oracle outputs on all {c.T} tokens")
     t0 = time.time()
     ref = oracle.forward_by_expert(inp.x_f64(), ridx, rw, expert_fn(inp), c.E, shared_f64(inp),
-                                   a8=a8_of(inp), amx=amx_of(inp), h_hook=hook)
+                                   **act_kw(inp), h_hook=hook)
     log(f"  oracle layer in {time.time() - t0:.1f}s")
     if hook is not None:
         log(f"  activation codes: {hook.n}, {hook.n_amb} within the error bound of a "
@@ -212,3 +210,27 @@ def test_hy3_decode_T16_w4a8_full(dev, hy3_mxfp4_weights):
 def test_hy3_prefill_T8192_skew_w4a8_full(dev, hy3_mxfp4_weights):
     layer_check(MoEInputs(CONFIGS["hy3_prefill_T8192_skew_w4a8"]), dev, hy3_mxfp4_weights,
                 workload_shape=False)
+
+
+def test_hy3_decode_T16_mixed_full(dev, hy3_mxfp4_weights):
+    """Routed experts at W4A8 and the shared expert at W8A8 in one call (the
+    CANN deployment article's section 8.2 split), every token: the MXFP4
+    routed experts of the W4A8 workloads, a FP8 shared expert with static
+    activation scales; derived output bound."""
+    inp = MoEInputs(CONFIGS["hy3_decode_T16_mixed"])
+    decode_full_check(inp, dev, mixed_weights(inp, hy3_mxfp4_weights, dev), workload_shape=False)
+
+
+def test_hy3_prefill_T8192_skew_mixed_full(dev, hy3_mxfp4_weights):
+    inp = MoEInputs(CONFIGS["hy3_prefill_T8192_skew_mixed"])
+    layer_check(inp, dev, mixed_weights(inp, hy3_mxfp4_weights, dev), workload_shape=False)
+
+
+def mixed_weights(inp, routed, dev):
+    """The routed MXFP4 weights with this workload's FP8 shared expert and
+    static activation scales."""
+    codes, scales = inp.shared_fp8()
+    w = {k: v for k, v in routed.items() if not k.startswith("ws_")}
+    w["ws_gate"], w["ws_up"], w["ws_down"] = (torch.from_numpy(q).to(dev) for q in codes)
+    w["ws_scale"] = torch.from_numpy(np.array(scales, dtype=np.float32)).to(dev)
+    return with_act_scales(inp, w, dev)

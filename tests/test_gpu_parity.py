@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import sparse_moe_amd as sm
-from gpu_util import (MARGIN, WorkspaceActivations, a8_of, amx_of, check_output, check_route,
-                      config_of, expert_cache, log, oracle_route, out_to_np,
+from gpu_util import (MARGIN, WorkspaceActivations, act_kw, check_output, check_route,
+                      config_of, expert_cache, log, oracle_route, out_to_np, quant_act,
                       route_for_reference, shared_f64, to_torch, upload_weights)
 from synth import CONFIGS, MoEInputs, random_small
 
@@ -38,7 +38,7 @@ def reference(inp, r, gidx, gw, tokens=None):
     if tokens is not None:
         x64, idx, w = x64[tokens], idx[tokens], w[tokens]
     return oracle.forward_given_route(x64, idx, w, expert_cache(inp), c.E, shared_f64(inp),
-                                      a8=a8_of(inp), amx=amx_of(inp))
+                                      **act_kw(inp))
 
 
 def run_gpu(inp, dev, weights=None, workspace=None):
@@ -56,21 +56,19 @@ def full_check(inp, dev, **kw):
     c = inp.cfg
     log(f"case {c.name}: T={c.T} H={c.H} E={c.E} K={c.K} I={c.I} Is={c.I_shared} "
         f"{c.dtype} mode={c.route_mode}")
-    quant_act = a8_of(inp) is not None or amx_of(inp)
-    if quant_act and kw.get("workspace") is None:
+    quantised = quant_act(inp)
+    if quantised and kw.get("workspace") is None:
         kw["workspace"] = sm.alloc_workspace(config_of(inp), True, dev)
     out, gidx, gw = run_gpu(inp, dev, **kw)
     r = oracle_route(inp)
     info = check_route(gidx, gw, r)
-    if quant_act:
+    if quantised:
         # activation codes with two valid answers: the GPU's, checked
         L = sm.hy3moe_workspace_layout(config_of(inp))
-        codes = L.tile_rows == 256 if a8_of(inp) is not None else L.tile_rows != 128
-        hook = WorkspaceActivations(inp, kw["workspace"], L, codes)
+        hook = WorkspaceActivations(inp, kw["workspace"], L)
         ridx, rw = route_for_reference(r, gidx)
         ref = oracle.forward_by_expert(inp.x_f64(), ridx, rw, expert_cache(inp), c.E,
-                                       shared_f64(inp), a8=a8_of(inp), amx=amx_of(inp),
-                                       h_hook=hook)
+                                       shared_f64(inp), **act_kw(inp), h_hook=hook)
         log(f"  activation codes {hook.n}, {hook.n_amb} at an ambiguous decision")
     else:
         ref = reference(inp, r, gidx, gw)
@@ -188,6 +186,41 @@ SMALL = {
                             dtype="bf16", w_format="mxfp4", act_format="mxfp8"),
     "w4a8_big_T513_H384": dict(seed=85, T=513, H=384, E=4, K=2, I=384, I_shared=128,
                                dtype="bf16", w_format="mxfp4", act_format="mxfp8"),
+    # The shared expert in formats of its own (separate launches over the
+    # shared tiles, which the permutation places last): routed W4A8 with a
+    # W8A8 shared expert on each path (a shared expert wider than the routed
+    # ones; ragged tails), routed bf16 with an MXFP4 shared expert, routed
+    # FP8 weights with a bf16 shared expert, and W8A8 routed experts with a
+    # W4A8 shared one
+    "mixed_T1": dict(seed=90, T=1, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16",
+                     w_format="mxfp4", act_format="mxfp8", shared_w_format="fp8_e4m3",
+                     shared_act_format="fp8_static"),
+    "mixed_T16": dict(seed=91, T=16, H=512, E=32, K=4, I=256, I_shared=384, dtype="bf16",
+                      w_format="mxfp4", act_format="mxfp8", shared_w_format="fp8_e4m3",
+                      shared_act_format="fp8_static"),
+    "mixed_tiled_T300": dict(seed=92, T=300, H=512, E=24, K=4, I=256, I_shared=128,
+                             dtype="bf16", w_format="mxfp4", act_format="mxfp8",
+                             shared_w_format="fp8_e4m3", shared_act_format="fp8_static"),
+    "mixed_big_T513_H384": dict(seed=93, T=513, H=384, E=4, K=2, I=384, I_shared=256,
+                                dtype="bf16", w_format="mxfp4", act_format="mxfp8",
+                                shared_w_format="fp8_e4m3", shared_act_format="fp8_static"),
+    "mixed_big_T400_softmax": dict(seed=94, T=400, H=512, E=8, K=4, I=256, I_shared=128,
+                                   dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
+                                   bias_kind="none", w_format="mxfp4", act_format="mxfp8",
+                                   shared_w_format="fp8_e4m3", shared_act_format="fp8_static"),
+    "mixed_bf16_shared_mxfp4_T40": dict(seed=95, T=40, H=256, E=16, K=4, I=128, I_shared=256,
+                                        dtype="bf16", shared_w_format="mxfp4"),
+    "mixed_fp8_shared_bf16_big_T400": dict(seed=96, T=400, H=512, E=8, K=4, I=256,
+                                           I_shared=128, dtype="bf16", w_format="fp8_e4m3",
+                                           shared_w_format="dtype"),
+    "mixed_w8a8_shared_w4a8_T300": dict(seed=97, T=300, H=512, E=24, K=4, I=256, I_shared=128,
+                                        dtype="bf16", w_format="fp8_e4m3",
+                                        act_format="fp8_static", shared_w_format="mxfp4",
+                                        shared_act_format="mxfp8"),
+    "mixed_w8a8_shared_w4a8_big_T513": dict(seed=98, T=513, H=384, E=4, K=2, I=256,
+                                            I_shared=384, dtype="bf16", w_format="fp8_e4m3",
+                                            act_format="fp8_static", shared_w_format="mxfp4",
+                                            shared_act_format="mxfp8"),
 }
 
 

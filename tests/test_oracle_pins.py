@@ -744,6 +744,80 @@ def test_w4a8_layer_is_within_the_quantisation_error_of_w4a16():
     assert 0.005 < rel < 0.08, rel
 
 
+# ------------------------------- per-branch formats (routed W4A8, shared W8A8) ----
+def _mixed_small(seed, T=12, H=128, E=5, K=2, I=64, I_shared=64):
+    inp = random_small(seed, T, H, E, K, I, I_shared, dtype="bf16", w_format="mxfp4",
+                       act_format="mxfp8", shared_w_format="fp8_e4m3",
+                       shared_act_format="fp8_static")
+    c = inp.cfg
+    experts = {}
+    for e in range(c.E):
+        codes, sc = inp.expert_mxfp4(e)
+        experts[e] = tuple(oracle.dequant_mxfp4(q, s) for q, s in zip(codes, sc))
+    codes, sc = inp.shared_fp8()
+    shared = tuple(oracle.dequant_fp8(q, s) for q, s in zip(codes, sc))
+    a1, a2 = inp.act_scales()
+    r = oracle.route(inp.x_f64(), inp.w_router().astype(np.float64), c.K, 0,
+                     inp.bias().astype(np.float64), c.scale)
+    return inp, experts, shared, r, (float(a1), a2.astype(np.float64))
+
+
+def test_mixed_layer_scalar_loops():
+    """One token at a time with element loops: the routed experts read x
+    quantised per 32-block and quantise their h (rounded to bfloat16 by
+    torch) per 32-block; the shared expert reads x quantised with a1 and
+    quantises its h with a2[E]."""
+    torch = pytest.importorskip("torch")
+    inp, experts, shared, r, (a1, a2) = _mixed_small(9, T=2, H=64, E=4, K=2, I=64,
+                                                     I_shared=64)
+    c = inp.cfg
+    x = inp.x_f64()
+    got = oracle.forward_given_route(x, r.idx, r.weight, lambda e: experts[e], c.E, shared,
+                                     amx=True, shared_a8=(a1, a2), shared_amx=False)
+    for t in range(c.T):
+        x_mx = list(oracle.quant_dequant_mxfp8(x[t:t + 1])[0])
+        x_8 = [float(oracle.quant_dequant_e4m3(np.array([x[t, k]]), a1)[0]) for k in range(c.H)]
+        ref = [0.0] * c.H
+        picks = [(int(r.idx[t, j]), float(r.weight[t, j])) for j in range(c.K)] + [(c.E, 1.0)]
+        for e, w in picks:
+            wg, wu, wd = experts[e] if e < c.E else shared
+            xq = x_8 if e == c.E else x_mx
+            h = []
+            for i in range(wg.shape[0]):
+                g = math.fsum(xq[k] * wg[i, k] for k in range(c.H))
+                u = math.fsum(xq[k] * wu[i, k] for k in range(c.H))
+                h.append(g / (1.0 + math.exp(-g)) * u)
+            hb = torch.tensor(h, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+            if e == c.E:
+                hq = [float(oracle.quant_dequant_e4m3(np.array([v]), a2[e])[0]) for v in hb]
+            else:
+                hq = list(oracle.quant_dequant_mxfp8(hb[None, :])[0])
+            for n in range(c.H):
+                ref[n] += w * math.fsum(hq[i] * wd[n, i] for i in range(len(hq)))
+        np.testing.assert_allclose(got[t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_mixed_layer_is_the_sum_of_its_branches():
+    """The routed part in the routed formats plus the shared expert alone in
+    its own (no routed picks); and the shared formats given as the routed
+    ones reproduce the single-format layer."""
+    inp, experts, shared, r, a8 = _mixed_small(10, T=20)
+    c = inp.cfg
+    x = inp.x_f64()
+    ex = lambda e: experts[e]
+    got = oracle.forward_given_route(x, r.idx, r.weight, ex, c.E, shared, amx=True,
+                                     shared_a8=a8, shared_amx=False)
+    routed = oracle.forward_given_route(x, r.idx, r.weight, ex, c.E, None, amx=True)
+    alone = oracle.forward_given_route(x, r.idx[:, :0], r.weight[:, :0], ex, c.E, shared, a8=a8)
+    np.testing.assert_allclose(got, routed + alone, rtol=1e-12, atol=1e-12)
+    # the branches differ: quantising the shared expert as the routed ones moves the output
+    as_routed = oracle.forward_given_route(x, r.idx, r.weight, ex, c.E, shared, amx=True)
+    assert np.abs(as_routed - got).max() > 1e-3
+    same = oracle.forward_given_route(x, r.idx, r.weight, ex, c.E, shared, amx=True,
+                                      shared_a8=None, shared_amx=True)
+    np.testing.assert_array_equal(same, as_routed)
+
+
 # ------------------------------------------------- weights on given picks ----
 def test_combine_weights_closed_form():
     """Weights of hand-chosen picks: sigmoid mode renormalises the picked
@@ -761,12 +835,13 @@ def test_combine_weights_closed_form():
 
 # ------------------------------------- the expert-by-expert evaluation ----
 @pytest.mark.parametrize("seed, mode, fmt", [(0, 0, None), (1, 1, None), (2, 0, "a8"),
-                                              (3, 0, "amx"), (4, 0, "noshared")])
+                                              (3, 0, "amx"), (4, 0, "noshared"),
+                                              (5, 0, "mixed")])
 def test_forward_by_expert_equals_dense_masked(seed, mode, fmt):
     """The streamed form against brute-force dense evaluation of every expert
     (the same sum, every expert on every token, masked)."""
     kw = dict(route_mode=1, scale=1.0, renorm_eps=1e-8, bias_kind="none") if mode else {}
-    if fmt == "amx":
+    if fmt in ("amx", "mixed"):
         inp = random_small(200 + seed, T=11, H=64, E=6, K=3, I=32, I_shared=32, **kw)
     else:
         inp = random_small(200 + seed, T=13, H=8, E=7, K=3, I=5,
@@ -779,9 +854,16 @@ def test_forward_by_expert_equals_dense_masked(seed, mode, fmt):
                      None if b is None else b.astype(np.float64), c.scale, c.renorm_eps)
     sh = None if fmt == "noshared" else inp.shared_f64()
     a8 = (0.01, np.linspace(0.002, 0.004, c.E + 1)) if fmt == "a8" else None
-    amx = fmt == "amx"
-    got = oracle.forward_by_expert(x, r.idx, r.weight, lambda e: ex[e], c.E, sh, a8=a8, amx=amx)
-    ref = oracle.dense_masked(x, r.idx, r.weight, lambda e: ex[e], c.E, sh, a8=a8, amx=amx)
+    amx = fmt in ("amx", "mixed")
+    # mixed: routed MXFP8, the shared expert static FP8
+    fk = dict(shared_a8=(0.01, np.linspace(0.002, 0.004, c.E + 1)),
+              shared_amx=False) if fmt == "mixed" else {}
+    got = oracle.forward_by_expert(x, r.idx, r.weight, lambda e: ex[e], c.E, sh, a8=a8, amx=amx,
+                                   **fk)
+    ref = oracle.dense_masked(x, r.idx, r.weight, lambda e: ex[e], c.E, sh, a8=a8, amx=amx, **fk)
+    eager = oracle.forward_given_route(x, r.idx, r.weight, lambda e: ex[e], c.E, sh, a8=a8,
+                                       amx=amx, **fk)
+    np.testing.assert_allclose(eager, ref, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
     assert np.abs(ref).max() > 0.05
 
