@@ -391,33 +391,35 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
         mma_dtype += "+" + mma_s
     fp8_mma = fp8_mma and f8_s                 # priced at the FP8 peak only if both are
     peak_mma = PEAK_FP8_TFLOPS if fp8_mma else PEAK_BF16_TFLOPS
-    R = T * K + (T if Is else 0)
-    groups = U + (1 if Is else 0)
-    gu_weight_bytes = U * 2 * I * H * web + 2 * Is * H * web_s
-    dn_weight_bytes = U * H * I * web + H * Is * web_s
-    # each branch reads x in its own activation format
-    x_bytes = T * H * ab + (T * H * ab_s if mixed else 0)
-    h_bytes = T * K * I * ab + T * Is * ab_s
-    gu_bytes = gu_weight_bytes + x_bytes + h_bytes
-    dn_bytes = dn_weight_bytes + h_bytes + R * H * eb
-    layer_bytes = gu_weight_bytes + dn_weight_bytes + E * H * 4 + 2 * T * H * eb
-    gu_flops = 4.0 * H * (T * K * I + (T * Is if Is else 0))
-    dn_flops = 2.0 * H * (T * K * I + (T * Is if Is else 0))
-    layer_flops = 1.5 * gu_flops + 2.0 * T * H * E
+    # When hy3moe_forward runs the shared expert's GEMMs on its side stream
+    # (large-tile path, or formats of its own: shared_meta in the layout),
+    # the gate-up and down stages on the caller's stream (and their kernels'
+    # launches) are the routed experts' GEMMs alone; otherwise the shared
+    # expert is one more group of those launches.
+    side = bool(Is) and sm.hy3moe_workspace_layout(cfg).shared_meta > 0
+    Ish = 0 if side else Is
+    gu_bytes = (U * 2 * I * H * web + 2 * Ish * H * web_s + T * H * ab + T * K * I * ab
+                + T * Ish * ab_s)
+    dn_bytes = (U * H * I * web + H * Ish * web_s + T * K * I * ab + T * Ish * ab_s
+                + (T * K + (T if Ish else 0)) * H * eb)
+    gu_flops = 4.0 * H * (T * K * I + T * Ish)
+    dn_flops = 2.0 * H * (T * K * I + T * Ish)
+    shared_note = (" (the shared expert runs on the side stream)" if side else
+                   f" + {2 * Is * H * web_s:.0f} B of the shared expert's" if Is else "")
+    # the whole layer: every weight read once, x in, out written
+    layer_bytes = (U * 3 * I * H * web + 3 * Is * H * web_s + E * H * 4 + 2 * T * H * eb)
+    layer_flops = 6.0 * H * (T * K * I + T * Is) + 2.0 * T * H * E
     layer_s = ms_per_step / 1e3
     gu_s = stage_ms["gate_up"] / 1e3
     decode = key.startswith("decode")
     names = {"fp8_e4m3": "FP8 E4M3", "mxfp4": "MXFP4"}
     if decode:
         kind = names.get(c.w_format, c.dtype)
-        per_unit = (f"{2 * I * H * web:.0f} B of {kind} gate+up weights per touched "
-                    f"expert x {U} routed experts")
-        if Is:
-            per_unit += (f" + {2 * Is * H * web_s:.0f} B of "
-                         f"{names.get(c.sw_format, c.dtype)} shared gate+up weights")
-        roof = {"kernel": "gate_up (weight-streaming grouped GEMM + SwiGLU)", "bound": "hbm",
-                "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "per_unit": per_unit + " + x and h rows"}
+        roof = {"kernel": "gate_up (weight-streaming grouped GEMM + SwiGLU)",
+                "bound": "hbm", "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "per_unit": f"{2 * I * H * web:.0f} B of {kind} gate+up weights per touched "
+                            f"routed expert x {U} experts{shared_note} + x and h rows"}
     else:
         path = "256x256-tile" if tile_rows == 256 else "128x128-tile"
         if fp8_mma:
@@ -425,10 +427,12 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
             if mixed and mma_s != branch(c.w_format, c.act_format)[3]:
                 path += " (shared expert: FP8 MFMA)" if c.sa_format == "fp8_static" \
                     else " (shared expert: FP4 x FP8 MFMA)"
-        roof = {"kernel": f"gate_up ({path} grouped GEMM + SwiGLU)", "bound": "mfma",
-                "achieved": gu_flops / gu_s / 1e12, "peak": peak_mma, "unit": "TFLOP/s",
-                "per_unit": f"{4 * H * I} FLOP per routed row x {T * K} rows + "
-                            f"{4 * H * Is} per shared row x {T}"}
+        roof = {"kernel": f"gate_up ({path} grouped GEMM + SwiGLU)",
+                "bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": peak_mma,
+                "unit": "TFLOP/s",
+                "per_unit": f"{4 * H * I} FLOP per routed row x {T * K} rows"
+                            + (" (the shared expert runs on the side stream)" if side else
+                               f" + {4 * H * Is} per shared row x {T}" if Is else "")}
     roof["frac"] = roof["achieved"] / roof["peak"]
     tr = measured_traffic(key, "gate_up")
     roof["traffic"] = tr

@@ -250,6 +250,10 @@ typedef struct hy3moe_ws_layout {
   size_t xq_shared;      /* the shared expert's quantised x when its activation
                             format differs from the routed one (as xq; 0 = not used) */
   size_t xs_shared;      /* its MXFP8 scales (0 = not used)                       */
+  size_t shared_meta;    /* int32: the shared expert's own tile list [2*max_tiles+2],
+                            offsets [E+2] and row map [R] for its launches on the
+                            side stream (0: the shared expert, if any, runs in
+                            the routed experts' launches on the caller's stream) */
 } hy3moe_ws_layout;
 
 /* Workspace size in bytes for hy3moe_forward (for_forward != 0) or for
@@ -308,16 +312,33 @@ int hy3moe_route_planes(const hy3moe_config *cfg, const void *x, const float *w_
  * (section 3: routing/index preprocessing with a contiguous row range per
  * expert, gate-up GEMM reading x through the route index, down GEMM written
  * compactly per expert, top-K weighted aggregation at the end) and the
- * shared/routed sum of the HunyuanImage 3.0 MoE reading ("Shared MLP"). */
+ * shared/routed sum of the HunyuanImage 3.0 MoE reading ("Shared MLP").
+ * The shared expert depends on x only, so when it has GEMM launches of its
+ * own (formats of its own, or the large-tile path of prefill batches:
+ * hy3moe_ws_layout.shared_meta != 0) they run on a side stream that the
+ * library creates on its first such call on each device (default
+ * priority), beside the routing chain on `stream`: forked from
+ * `stream` by an event after x is quantised and joined back into it by
+ * another before the combine (the CANN deployment article, section 8.5, and
+ * the hy3 README's performance notes run shared and routed experts on two
+ * streams).  Everything the call enqueues is ordered before work later
+ * enqueued on `stream`; under HIP graph capture of `stream` the fork and
+ * join become graph edges.  A call made while `stream` is being captured
+ * before the side stream exists keeps the shared expert on `stream`.
+ * Results are identical either way.  Calls from several host threads on one
+ * device enqueue their fork and join under a lock and share the side
+ * stream. */
 int hy3moe_forward(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
                    void *out, int32_t *idx_out, float *weight_out,
                    void *workspace, size_t ws_bytes, void *stream);
 
-/* Stages of hy3moe_forward, in launch order: router GEMM, score+select,
- * permutation (histogram, scan + tile list, scatter; with act_format
- * FP8_STATIC or MXFP8 preceded by the quantisation of x), gate-up + SwiGLU,
- * down (with MXFP8 off the large-tile path preceded by the quantisation of
- * h), combine. */
+/* Stages of hy3moe_forward on `stream`, in launch order: router GEMM (with
+ * act_format FP8_STATIC or MXFP8 preceded by the quantisation of x),
+ * score+select, permutation (histogram, scan + tile list, scatter),
+ * gate-up + SwiGLU, down (with MXFP8 off the large-tile path preceded by
+ * the quantisation of h), combine (preceded by the join of the side
+ * stream).  When the shared expert runs on the side stream (shared_meta !=
+ * 0) the gate-up and down stages are the routed experts' GEMMs alone. */
 #define HY3MOE_N_STAGES 6
 
 /* hy3moe_forward that also records HY3MOE_N_STAGES + 1 caller-created HIP
@@ -334,7 +355,8 @@ int hy3moe_forward_timed(const hy3moe_config *cfg, const void *x, const hy3moe_w
 
 /* hy3moe_forward for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
- * Identical results to hy3moe_forward; the workspace is a static device
+ * Identical results to hy3moe_forward, with every kernel on `stream` (no
+ * side stream); the workspace is a static device
  * array of HY3MOE_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on
  * each GPU it runs on until the process ends (its address is looked up on
  * the first call on a device), so the call itself allocates nothing.

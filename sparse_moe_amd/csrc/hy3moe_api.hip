@@ -153,6 +153,16 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
     L->hq = off;        off += al((size_t)R * Imax);
     L->hs = off;        off += al((size_t)R * Imax / 32);
   }
+  // the shared expert's own tile list, offsets and row map, for launches
+  // beside the routing chain: when it has launches of its own anyway
+  // (formats of its own) and on the large-tile path.  A weight-streaming
+  // launch of one group has too little parallelism to gain from it and
+  // holds CUs the routing kernels need; there the shared expert stays a
+  // group of the routed experts' launches.
+  if (c->I_shared > 0 && (mix || path == PATH_BIG)) {
+    L->shared_meta = off;
+    off += al((size_t)(2 * L->max_tiles + 2 + E + 2 + R) * 4);
+  }
   L->total = off;
 }
 
@@ -161,11 +171,47 @@ bool al4(const void *p) { return ((uintptr_t)p & 3) == 0; }
 
 int check_launch(hipError_t e) { return e == hipSuccess ? HY3MOE_OK : HY3MOE_ERR_HIP; }
 
+// The side stream of each device: the shared expert's branch runs on it,
+// forked from and joined back into the caller's stream by two events.
+// Created on the first hy3moe_forward on the device (not while the caller's
+// stream is being captured: such a call stays on the caller's stream);
+// default priority.  The lock is held while a call enqueues its fork and
+// join, so calls from several host threads do not interleave them.
+constexpr int kMaxSideDevices = 64;
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  int state = 0;   // 0 not created, 1 ready, -1 creation failed
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxSideDevices];
+
+// The current device's side stream with *lock holding g_side_mu, or null
+// (then the shared expert runs on the caller's stream).
+SideStream *side_stream(hipStream_t caller, std::unique_lock<std::mutex> *lock) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  std::unique_lock<std::mutex> lk(g_side_mu);
+  SideStream &sd = g_side[dev];
+  if (sd.state == 0) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+      return nullptr;
+    const bool ok = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess &&
+                    hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) == hipSuccess &&
+                    hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) == hipSuccess;
+    sd.state = ok ? 1 : -1;
+  }
+  if (sd.state != 1) return nullptr;
+  *lock = std::move(lk);
+  return &sd;
+}
+
 }  // namespace
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 9; }
+int hy3moe_abi_version(void) { return 10; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {
@@ -302,7 +348,7 @@ static void set_branch_weights(ExpertArgs &ea, const hy3moe_weights *w, BranchFm
 
 static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
                         void *out, int32_t *idx_out, float *weight_out, void *workspace,
-                        size_t ws_bytes, void *stream, void *const *events) {
+                        size_t ws_bytes, void *stream, void *const *events, bool overlap) {
   int rc = validate_cfg(cfg);
   if (rc != HY3MOE_OK) return rc;
   if (cfg->T == 0) return HY3MOE_OK;
@@ -335,153 +381,231 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(ws + L.idx);
   float *weight = weight_out ? weight_out : reinterpret_cast<float *>(ws + L.weight);
 
+  // The shared expert needs x only, not the route: with a side stream it
+  // runs there, beside the routing chain (the CANN deployment article,
+  // section 8.5, and the hy3 README's performance notes put the shared and
+  // routed experts on two streams).
+  std::unique_lock<std::mutex> side_lock;
+  SideStream *side = (overlap && L.shared_meta) ? side_stream(s, &side_lock) : nullptr;
+
   int stage = 0;
   auto mark = [&]() {
     if (events) hipEventRecord(static_cast<hipEvent_t>(events[stage]), s);
     ++stage;
   };
-  mark();
-  // 1-2. gate
-  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w->w_router, planes,
-                                  static_cast<const uint16_t *>(w->w_router_planes), part, T, H,
-                                  E, L.n_ksplit, s));
-  if (rc) return rc;
-  mark();
-  const float *bias = cfg->route_mode == HY3MOE_ROUTE_SIGMOID_BIAS ? w->expert_bias : nullptr;
-  rc = check_launch(launch_select(part, L.n_ksplit, T, E, K, bias, cfg->route_mode, cfg->scale,
-                                  cfg->renorm_eps, idx, weight, s));
-  if (rc) return rc;
-  mark();
 
-  // 3. quantisation of x (needs no routing) for each branch that quantises
-  // its activations, then the permutation.  A branch is the routed experts
-  // (group selection GRP_ROUTED), or the shared expert when it has formats
-  // of its own (GRP_SHARED); otherwise one launch covers both (GRP_ALL).
+  // A branch is the routed experts (group selection GRP_ROUTED), or the
+  // shared expert (GRP_SHARED) when it runs on the side stream or has
+  // formats of its own; otherwise one launch per GEMM covers both (GRP_ALL).
   const int path = path_of(cfg);
   const int Imax = cfg->I > cfg->I_shared ? cfg->I : cfg->I_shared;
   const int64_t N = (int64_t)T * K;
   const int64_t R = N + (has_shared ? T : 0);
+  const bool split = has_shared && (mix || side);
   struct Branch {
     BranchFmt f;
     int grp_sel;
     int64_t r0, r1;            // its rows of h and y
+    hipStream_t st;            // the stream it runs on
     const void *act;           // its x: as given, or quantised
     const uint8_t *act_sc;     // MXFP8 scales of its x
     char *xq;                  // where its quantised x goes
     uint8_t *xs;
+    int32_t *tiles, *offsets, *sorted_token;   // its tile list and row maps
   };
+  int32_t *meta = L.shared_meta ? reinterpret_cast<int32_t *>(ws + L.shared_meta) : nullptr;
   Branch br[2];
-  int nbr = 0;
-  br[nbr++] = {rf, mix ? GRP_ROUTED : GRP_ALL, 0, mix ? N : R, x, nullptr, ws + L.xq,
-               reinterpret_cast<uint8_t *>(ws + L.xs)};
-  if (mix)
-    br[nbr++] = {sf, GRP_SHARED, N, R, x, nullptr, ws + L.xq_shared,
-                 reinterpret_cast<uint8_t *>(ws + L.xs_shared)};
-  for (int b = 0; b < nbr; ++b) {
-    Branch &B = br[b];
+  const int nbr = split ? 2 : 1;
+  br[0] = {rf, split ? GRP_ROUTED : GRP_ALL, 0, split ? N : R, s, x, nullptr, ws + L.xq,
+           reinterpret_cast<uint8_t *>(ws + L.xs), reinterpret_cast<int32_t *>(ws + L.tiles),
+           reinterpret_cast<int32_t *>(ws + L.offsets),
+           reinterpret_cast<int32_t *>(ws + L.sorted_token)};
+  if (split) {
+    br[1] = {sf, GRP_SHARED, N, R, side ? side->s : s, x, nullptr,
+             mix ? ws + L.xq_shared : ws + L.xq,
+             reinterpret_cast<uint8_t *>(mix ? ws + L.xs_shared : ws + L.xs), br[0].tiles,
+             br[0].offsets, br[0].sorted_token};
+    if (side) {   // its own metadata, written on the side stream
+      br[1].tiles = meta;
+      br[1].offsets = meta + 2 * L.max_tiles + 2;
+      br[1].sorted_token = br[1].offsets + E + 2;
+    }
+  }
+
+  // Quantisation of x for a branch that quantises its activations: MXFP8
+  // codes and scales for the block-scaled MFMAs of the weight-streaming and
+  // large-tile paths (bf16 values for the tiled path); static FP8 code bytes
+  // for the large-tile path's FP8 MFMAs, else their bf16 values.
+  auto quantise_x = [&](Branch &B) -> int {
+    int e = HY3MOE_OK;
     if (B.f.act == HY3MOE_AFMT_MXFP8) {
-      // codes and scales for the block-scaled MFMAs of the weight-streaming
-      // and large-tile paths, the bf16 values for the tiled path
-      rc = check_launch(launch_quant_mxfp8(x, (int64_t)T * H, B.xq, B.xs,
-                                           path != PATH_TILED ? 0 : 1, s));
-      B.act = B.xq;
+      e = check_launch(launch_quant_mxfp8(x, (int64_t)T * H, B.xq, B.xs,
+                                          path != PATH_TILED ? 0 : 1, B.st));
       B.act_sc = B.xs;
     } else if (B.f.act == HY3MOE_AFMT_FP8_STATIC) {
-      // code bytes for the large-tile path's FP8 MFMAs, else their bf16 values
-      rc = check_launch(launch_quant_e4m3(x, cfg->dtype, (int64_t)T * H, w->x_scale, B.xq,
-                                          path == PATH_BIG ? 0 : 1, s));
-      B.act = B.xq;
+      e = check_launch(launch_quant_e4m3(x, cfg->dtype, (int64_t)T * H, w->x_scale, B.xq,
+                                         path == PATH_BIG ? 0 : 1, B.st));
     }
+    if (B.f.act != HY3MOE_AFMT_DTYPE) B.act = B.xq;
+    return e;
+  };
+
+  // The expert GEMMs of one branch.  h of every branch shares one buffer by
+  // rows; a branch that stores 1-byte codes there (static FP8 on the
+  // large-tile path: row r at byte r * ldh) is shifted by r0 * ldh bytes,
+  // past the 2-byte rows before it, when the formats differ.  On the
+  // large-tile path MXFP8 h is quantised by the gate-up epilogue itself.
+  ExpertArgs base;
+  base.E = E; base.H = H; base.I = cfg->I; base.I_shared = cfg->I_shared; base.ldh = Imax;
+  base.max_tiles = L.max_tiles;
+  base.n_rows = (int)R;
+  base.n_tok = T;
+  auto branch_args = [&](const Branch &B, bool gate_up) {
+    ExpertArgs ea = base;
+    ea.sorted_token = B.sorted_token;
+    ea.offsets = B.offsets;
+    ea.tiles = B.tiles;
+    set_branch_weights(ea, w, B.f, gate_up, has_shared);
+    ea.grp_sel = B.grp_sel;
+    return ea;
+  };
+  auto h_base = [&](const Branch &B) {
+    return ws + L.h + (B.f.act == HY3MOE_AFMT_FP8_STATIC && path == PATH_BIG && mix
+                           ? B.r0 * Imax : 0);
+  };
+  auto gate_up = [&](const Branch &B) -> int {
+    const bool amx = B.f.act == HY3MOE_AFMT_MXFP8;
+    const bool amx_codes = amx && path != PATH_TILED, fused = amx_codes && path == PATH_BIG;
+    ExpertArgs ea = branch_args(B, true);
+    ea.act = B.act;
+    ea.amx = amx_codes ? 1 : 0;
+    ea.act_sc = amx ? B.act_sc : nullptr;
+    ea.out = fused ? ws + L.hq : h_base(B);
+    ea.out_sc = fused ? reinterpret_cast<uint8_t *>(ws + L.hs) : nullptr;
+    return check_launch(launch_gate_up(ea, cfg->dtype, T, path, B.st));
+  };
+  auto down = [&](const Branch &B) -> int {
+    const bool amx = B.f.act == HY3MOE_AFMT_MXFP8;
+    const bool amx_codes = amx && path != PATH_TILED, fused = amx_codes && path == PATH_BIG;
+    ExpertArgs ea = branch_args(B, false);
+    ea.act = h_base(B);
+    ea.amx = amx_codes ? 1 : 0;
+    ea.act_sc = nullptr;
+    ea.out_sc = nullptr;
+    if (amx) {
+      // h, dynamic MXFP8 per 32 along I over the branch's rows: codes and
+      // scales, or the bf16 values in place
+      const int64_t h0 = B.r0 * Imax, nh = (B.r1 - B.r0) * Imax;
+      int e = HY3MOE_OK;
+      if (!fused && amx_codes)
+        e = check_launch(launch_quant_mxfp8(ws + L.h + h0 * 2, nh, ws + L.hq + h0,
+                                            reinterpret_cast<uint8_t *>(ws + L.hs) + h0 / 32, 0,
+                                            B.st));
+      else if (!fused)
+        e = check_launch(launch_quant_mxfp8(ws + L.h + h0 * 2, nh, ws + L.h + h0 * 2, nullptr,
+                                            1, B.st));
+      if (e) return e;
+      if (amx_codes) {
+        ea.act = ws + L.hq;
+        ea.act_sc = reinterpret_cast<const uint8_t *>(ws + L.hs);
+      }
+    }
+    ea.out = ws + L.y;
+    return check_launch(launch_down(ea, cfg->dtype, T, path, B.st));
+  };
+
+  mark();
+  // 0. x quantised once for the routed experts (and for the shared expert
+  // when it shares their format), before the fork
+  rc = quantise_x(br[0]);
+  if (rc) return rc;
+  if (split && !mix) {
+    br[1].act = br[0].act;
+    br[1].act_sc = br[0].act_sc;
+  }
+  bool joined = true;
+  if (side) {
+    // fork: the shared expert's metadata, x quantisation (formats of its
+    // own) and GEMMs on the side stream; the caller's stream waits for the
+    // join before the combine (or before returning an error)
+    hipStream_t ss = side->s;
+    rc = check_launch(hipEventRecord(side->fork, s));
+    if (!rc) rc = check_launch(hipStreamWaitEvent(ss, side->fork, 0));
     if (rc) return rc;
+    joined = false;
+    rc = check_launch(launch_shared_meta(br[1].tiles, br[1].offsets, br[1].sorted_token, T,
+                                         (int)N, E, L.tile_rows, L.max_tiles, ss));
+    if (!rc && mix) rc = quantise_x(br[1]);
+    if (!rc) rc = gate_up(br[1]);
+    if (!rc) rc = down(br[1]);
+    const int jr = check_launch(hipEventRecord(side->join, ss));
+    if (!rc) rc = jr;
+  }
+  auto join = [&]() -> int {
+    if (joined) return HY3MOE_OK;
+    joined = true;
+    return check_launch(hipStreamWaitEvent(s, side->join, 0));
+  };
+  auto fail = [&](int e) {
+    join();
+    return e;
+  };
+  if (rc) return fail(rc);
+
+  // 1-2. gate
+  rc = check_launch(launch_router(x, cfg->dtype, cfg->router_prec, w->w_router, planes,
+                                  static_cast<const uint16_t *>(w->w_router_planes), part, T, H,
+                                  E, L.n_ksplit, s));
+  if (rc) return fail(rc);
+  mark();
+  const float *bias = cfg->route_mode == HY3MOE_ROUTE_SIGMOID_BIAS ? w->expert_bias : nullptr;
+  rc = check_launch(launch_select(part, L.n_ksplit, T, E, K, bias, cfg->route_mode, cfg->scale,
+                                  cfg->renorm_eps, idx, weight, s));
+  if (rc) return fail(rc);
+  mark();
+
+  // 3. the shared expert's x in formats of its own when it stays on this
+  // stream, then the permutation (the shared expert's tiles last when it
+  // has launches of its own)
+  if (split && !side && mix) {
+    rc = quantise_x(br[1]);
+    if (rc) return fail(rc);
   }
   PermArgs pa;
   pa.idx = idx;
   pa.hist = reinterpret_cast<int32_t *>(ws + L.hist);
   pa.counts = reinterpret_cast<int32_t *>(ws + L.counts);
-  pa.offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
-  pa.sorted_token = reinterpret_cast<int32_t *>(ws + L.sorted_token);
+  pa.offsets = br[0].offsets;
+  pa.sorted_token = br[0].sorted_token;
   pa.pos_of = reinterpret_cast<int32_t *>(ws + L.pos_of);
-  pa.tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
+  pa.tiles = br[0].tiles;
   pa.T = T; pa.K = K; pa.E = E;
   pa.T_shared = has_shared ? T : 0;
   pa.nchunks = L.n_chunks;
   pa.tile_rows = L.tile_rows;
   pa.max_tiles = L.max_tiles;
   pa.sort_tiles = path != PATH_SKINNY;
-  pa.shared_last = mix ? 1 : 0;
+  pa.shared_last = split ? 1 : 0;
   rc = check_launch(launch_permute(pa, s));
+  if (rc) return fail(rc);
+  mark();
+
+  // 4-5. grouped experts of the branches on this stream
+  const int nb_here = side ? 1 : nbr;
+  for (int b = 0; b < nb_here; ++b) {
+    rc = gate_up(br[b]);
+    if (rc) return fail(rc);
+  }
+  mark();
+  for (int b = 0; b < nb_here; ++b) {
+    rc = down(br[b]);
+    if (rc) return fail(rc);
+  }
+  mark();
+
+  // 6. combine, after the join
+  rc = join();
   if (rc) return rc;
-  mark();
-
-  // 4-5. grouped experts
-  ExpertArgs ea;
-  ea.sorted_token = pa.sorted_token;
-  ea.offsets = pa.offsets;
-  ea.tiles = pa.tiles;
-  ea.E = E; ea.H = H; ea.I = cfg->I; ea.I_shared = cfg->I_shared; ea.ldh = Imax;
-  ea.max_tiles = L.max_tiles;
-  ea.n_rows = (int)R;
-  ea.n_tok = T;
-  // per branch: MXFP8 codes for the block-scaled MFMAs (not the tiled path),
-  // and on the large-tile path h quantised by the gate-up epilogue itself.
-  // h of every branch shares one buffer by rows; a branch that stores
-  // 1-byte codes there (static FP8 on the large-tile path: row r at byte
-  // r * ldh) is shifted by r0 * ldh bytes, past the 2-byte rows of the
-  // rows before it.
-  bool amx_codes[2], h_fused[2];
-  char *hbase[2];
-  for (int b = 0; b < nbr; ++b) {
-    const Branch &B = br[b];
-    const bool amx = B.f.act == HY3MOE_AFMT_MXFP8;
-    amx_codes[b] = amx && path != PATH_TILED;
-    h_fused[b] = amx_codes[b] && path == PATH_BIG;
-    hbase[b] = ws + L.h +
-               (B.f.act == HY3MOE_AFMT_FP8_STATIC && path == PATH_BIG ? B.r0 * Imax : 0);
-    set_branch_weights(ea, w, B.f, true, has_shared);
-    ea.grp_sel = B.grp_sel;
-    ea.act = B.act;
-    ea.amx = amx_codes[b] ? 1 : 0;
-    ea.act_sc = amx ? B.act_sc : nullptr;
-    ea.out = h_fused[b] ? ws + L.hq : hbase[b];
-    ea.out_sc = h_fused[b] ? reinterpret_cast<uint8_t *>(ws + L.hs) : nullptr;
-    rc = check_launch(launch_gate_up(ea, cfg->dtype, T, path, s));
-    if (rc) return rc;
-  }
-  mark();
-  for (int b = 0; b < nbr; ++b) {
-    const Branch &B = br[b];
-    set_branch_weights(ea, w, B.f, false, has_shared);
-    ea.grp_sel = B.grp_sel;
-    ea.act = hbase[b];
-    ea.amx = amx_codes[b] ? 1 : 0;
-    ea.act_sc = nullptr;
-    ea.out_sc = nullptr;
-    if (B.f.act == HY3MOE_AFMT_MXFP8) {
-      // h, dynamic MXFP8 per 32 along I over the branch's rows: codes and
-      // scales, or the bf16 values in place
-      const int64_t h0 = B.r0 * Imax, nh = (B.r1 - B.r0) * Imax;
-      if (h_fused[b]) {
-        ea.act = ws + L.hq;
-        ea.act_sc = reinterpret_cast<const uint8_t *>(ws + L.hs);
-      } else if (amx_codes[b]) {
-        rc = check_launch(launch_quant_mxfp8(ws + L.h + h0 * 2, nh, ws + L.hq + h0,
-                                             reinterpret_cast<uint8_t *>(ws + L.hs) + h0 / 32, 0,
-                                             s));
-        ea.act = ws + L.hq;
-        ea.act_sc = reinterpret_cast<const uint8_t *>(ws + L.hs);
-      } else {
-        rc = check_launch(launch_quant_mxfp8(ws + L.h + h0 * 2, nh, ws + L.h + h0 * 2, nullptr,
-                                             1, s));
-      }
-      if (rc) return rc;
-    }
-    ea.out = ws + L.y;
-    rc = check_launch(launch_down(ea, cfg->dtype, T, path, s));
-    if (rc) return rc;
-  }
-  mark();
-
-  // 6. combine
   rc = check_launch(launch_combine(ws + L.y, pa.pos_of, weight, pa.offsets, T, K, H, E,
                                    has_shared ? 1 : 0, out, cfg->dtype, s));
   if (rc) return rc;
@@ -536,8 +660,9 @@ int hy3moe_forward_static(const hy3moe_config *cfg, const void *x, const hy3moe_
   int rc = HY3MOE_OK;
   void *ws = static_scratch(&rc);
   if (!ws) return rc;
+  // the shared expert stays on the caller's stream: no side stream is created
   return forward_impl(cfg, x, w, out, idx_out, weight_out, ws, HY3MOE_STATIC_SCRATCH_BYTES,
-                      stream, nullptr);
+                      stream, nullptr, false);
 }
 
 size_t hy3moe_static_scratch_bytes(void) { return HY3MOE_STATIC_SCRATCH_BYTES; }
@@ -555,7 +680,8 @@ int hy3moe_quantize_e4m3(const void *x, int32_t dtype, int64_t n, const float *s
 int hy3moe_forward(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w, void *out,
                    int32_t *idx_out, float *weight_out, void *workspace, size_t ws_bytes,
                    void *stream) {
-  return forward_impl(cfg, x, w, out, idx_out, weight_out, workspace, ws_bytes, stream, nullptr);
+  return forward_impl(cfg, x, w, out, idx_out, weight_out, workspace, ws_bytes, stream, nullptr,
+                      true);
 }
 
 int hy3moe_forward_timed(const hy3moe_config *cfg, const void *x, const hy3moe_weights *w,
@@ -565,7 +691,7 @@ int hy3moe_forward_timed(const hy3moe_config *cfg, const void *x, const hy3moe_w
   for (int i = 0; i <= HY3MOE_N_STAGES; ++i)
     if (!stage_events[i]) return HY3MOE_ERR_INVALID;
   return forward_impl(cfg, x, w, out, idx_out, weight_out, workspace, ws_bytes, stream,
-                      stage_events);
+                      stage_events, true);
 }
 
 }  // extern "C"

@@ -73,6 +73,13 @@ struct PermArgs {
   int shared_last;        // the shared expert's tiles after every routed tile
 };
 hipError_t launch_permute(const PermArgs &a, hipStream_t stream);
+// Metadata of the shared expert's own launches, which need no routing: a
+// tile list [2*max_tiles + 2] holding only its tiles (group E, rows N + i
+// tile_rows, then the tile count and a routed tile count of 0), offsets
+// [E+2] (every routed group empty at row N, the shared rows [N, N + T)) and
+// the identity map sorted_token[N + t] = t of a [N + T] row map.
+hipError_t launch_shared_meta(int32_t *tiles, int32_t *offsets, int32_t *sorted_token, int T,
+                              int N, int E, int tile_rows, int max_tiles, hipStream_t stream);
 
 // Expert GEMMs ----------------------------------------------------------------
 struct ExpertArgs {
@@ -91,7 +98,8 @@ struct ExpertArgs {
   int n_tok;              // T (rows of x)
   // Groups this launch computes: GRP_ALL, GRP_ROUTED (the tiles before the
   // routed tile count) or GRP_SHARED (the tiles after it); the last two need
-  // a tile list made with shared_last.
+  // a tile list made with shared_last, or the shared expert's own list
+  // (launch_shared_meta).
   int grp_sel;
   // FP8 E4M3 expert weights (w_fp8 = 1): w0/w1/ws0/ws1 hold bytes and the
   // weight is scale * value, with scales sc0[g] / sc1[g] for routed group g

@@ -397,7 +397,9 @@ __device__ __forceinline__ void stage_schedule_a8() {
   }
 }
 
-template <typename T, bool GATE_UP, int WF, bool A8>
+// BRANCH names the instantiation only (0: routed experts or every group, 1:
+// the shared expert's own launches), so that profiles list them apart.
+template <typename T, bool GATE_UP, int WF, bool A8, int BRANCH>
 __global__ __launch_bounds__(512, 1) void expert_big_kernel(ExpertArgs a, int n_col_tiles) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4;
   __shared__ uint4 lds[2 * ROWS * CH];   // 2 x 64 KB
@@ -648,7 +650,7 @@ constexpr int W4_WCH = 4;                 // 16-byte chunks per staged weight ro
 constexpr int W4_TOK = BW * W4_WCH;       // token region (uint4 units)
 constexpr int W4_SC = W4_TOK + BTK * CH;  // scale region: 512 dwords (weights, then tokens)
 
-template <bool GATE_UP>
+template <bool GATE_UP, int BRANCH>
 __global__ __launch_bounds__(512, 1) void expert_big_w4a8_kernel(ExpertArgs a, int n_col_tiles) {
   __shared__ uint4 lds[2 * ROWS * CH];   // 2 x 64 KB: buffers of 50 KB, and the epilogue's staging
   static_assert(W4_SC + (BW + BTK) / 4 <= ROWS * CH, "W4A8 stage buffer");
@@ -851,8 +853,8 @@ __global__ __launch_bounds__(512, 1) void expert_big_w4a8_kernel(ExpertArgs a, i
 #undef HY3_W4_LOADW
 }
 
-template <typename T, int WF, bool A8>
-hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+template <typename T, int WF, bool A8, int BRANCH>
+hipError_t launch_big_b(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   int nct;
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
@@ -875,16 +877,22 @@ hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   const dim3 grid((unsigned)(want < cap ? want : cap));
   if constexpr (WF == WF_W4A8) {
     if (gate_up)
-      hipLaunchKernelGGL((expert_big_w4a8_kernel<true>), grid, dim3(512), 0, stream, a, nct);
+      hipLaunchKernelGGL((expert_big_w4a8_kernel<true, BRANCH>), grid, dim3(512), 0, stream, a, nct);
     else
-      hipLaunchKernelGGL((expert_big_w4a8_kernel<false>), grid, dim3(512), 0, stream, a, nct);
+      hipLaunchKernelGGL((expert_big_w4a8_kernel<false, BRANCH>), grid, dim3(512), 0, stream, a, nct);
   } else {
     if (gate_up)
-      hipLaunchKernelGGL((expert_big_kernel<T, true, WF, A8>), grid, dim3(512), 0, stream, a, nct);
+      hipLaunchKernelGGL((expert_big_kernel<T, true, WF, A8, BRANCH>), grid, dim3(512), 0, stream, a, nct);
     else
-      hipLaunchKernelGGL((expert_big_kernel<T, false, WF, A8>), grid, dim3(512), 0, stream, a, nct);
+      hipLaunchKernelGGL((expert_big_kernel<T, false, WF, A8, BRANCH>), grid, dim3(512), 0, stream, a, nct);
   }
   return hipGetLastError();
+}
+
+template <typename T, int WF, bool A8>
+hipError_t launch_big_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+  return a.grp_sel == GRP_SHARED ? launch_big_b<T, WF, A8, 1>(a, gate_up, stream)
+                                 : launch_big_b<T, WF, A8, 0>(a, gate_up, stream);
 }
 
 }  // namespace

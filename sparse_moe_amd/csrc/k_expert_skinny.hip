@@ -260,7 +260,10 @@ inline size_t meta_lds_bytes(const ExpertArgs &a, bool gate_up) {
 // copy of x (one per CU holding it), two wavefronts per SIMD either way.
 template <bool XL> constexpr int stream_threads() { return XL ? 512 : 256; }
 
-template <typename T, bool GATE_UP, int MT, int WF, bool XL>
+// BRANCH names the instantiation only: 0 for the routed experts (or every
+// group), 1 for the shared expert's own launches, which profiles then list
+// apart.
+template <typename T, bool GATE_UP, int MT, int WF, bool XL, int BRANCH>
 __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_stream_kernel(
     ExpertArgs a_in, int n_col_blocks) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4, MXA = WF == WF_W4A8;
@@ -490,25 +493,31 @@ size_t x_lds_bytes(const ExpertArgs &a) {
   return meta + x <= STREAM_XL_LDS_MAX ? x : 0;
 }
 
-template <typename T, int MT, int WF>
-hipError_t launch_skinny_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+template <typename T, int MT, int WF, int BRANCH>
+hipError_t launch_skinny_b(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int ncb = (Imax + 15) / 16;
     const size_t xb = x_lds_bytes<T, MT, WF>(a);
     if (xb)   // one 512-thread workgroup per CU, x in LDS
-      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, true>), dim3(STREAM_BLOCKS / 2),
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, true, BRANCH>), dim3(STREAM_BLOCKS / 2),
                          dim3(512), (meta_lds_bytes(a, true) + 15) / 16 * 16 + xb, stream, a,
                          ncb);
     else
-      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, false>), dim3(STREAM_BLOCKS),
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, false, BRANCH>), dim3(STREAM_BLOCKS),
                          dim3(256), meta_lds_bytes(a, true), stream, a, ncb);
   } else {
     const int ncb = (a.H + 31) / 32;
-    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF, false>), dim3(STREAM_BLOCKS),
+    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF, false, BRANCH>), dim3(STREAM_BLOCKS),
                        dim3(256), meta_lds_bytes(a, false), stream, a, ncb);
   }
   return hipGetLastError();
+}
+
+template <typename T, int MT, int WF>
+hipError_t launch_skinny_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+  return a.grp_sel == GRP_SHARED ? launch_skinny_b<T, MT, WF, 1>(a, gate_up, stream)
+                                 : launch_skinny_b<T, MT, WF, 0>(a, gate_up, stream);
 }
 
 template <typename T, int WF>

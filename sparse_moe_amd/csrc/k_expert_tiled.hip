@@ -41,7 +41,9 @@ constexpr int CHUNKS = KB / 16;  // 8
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * CHUNKS + (chunk ^ (row & 7)); }
 
-template <typename T, bool GATE_UP, int WF>
+// BRANCH names the instantiation only (0: routed experts or every group, 1:
+// the shared expert's own launches).
+template <typename T, bool GATE_UP, int WF, int BRANCH>
 __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int n_col_tiles) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4;
   __shared__ uint4 lds[2][(BR + BT) * CHUNKS];   // 2 x 32 KB
@@ -223,19 +225,25 @@ __global__ __launch_bounds__(256, 2) void expert_tiled_kernel(ExpertArgs a, int 
 
 }  // namespace
 
-template <typename T, int WF>
-static hipError_t launch_tiled(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+template <typename T, int WF, int BRANCH>
+static hipError_t launch_tiled_b(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int nct = Imax / TILED_GU_COLS;
-    hipLaunchKernelGGL((expert_tiled_kernel<T, true, WF>), dim3(a.max_tiles * nct), dim3(256),
+    hipLaunchKernelGGL((expert_tiled_kernel<T, true, WF, BRANCH>), dim3(a.max_tiles * nct), dim3(256),
                        0, stream, a, nct);
   } else {
     const int nct = (a.H + TILED_DN_COLS - 1) / TILED_DN_COLS;
-    hipLaunchKernelGGL((expert_tiled_kernel<T, false, WF>), dim3(a.max_tiles * nct), dim3(256),
+    hipLaunchKernelGGL((expert_tiled_kernel<T, false, WF, BRANCH>), dim3(a.max_tiles * nct), dim3(256),
                        0, stream, a, nct);
   }
   return hipGetLastError();
+}
+
+template <typename T, int WF>
+static hipError_t launch_tiled(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+  return a.grp_sel == GRP_SHARED ? launch_tiled_b<T, WF, 1>(a, gate_up, stream)
+                                 : launch_tiled_b<T, WF, 0>(a, gate_up, stream);
 }
 
 hipError_t launch_tiled_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream) {

@@ -305,4 +305,34 @@ hipError_t launch_permute(const PermArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+namespace {
+__global__ __launch_bounds__(256) void shared_meta_kernel(int32_t *__restrict__ tiles,
+                                                          int32_t *__restrict__ offsets,
+                                                          int32_t *__restrict__ sorted_token,
+                                                          int T, int N, int E, int tile_rows,
+                                                          int max_tiles) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int n_sh = (T + tile_rows - 1) / tile_rows;
+  if (i < n_sh) {
+    tiles[2 * i] = E;
+    tiles[2 * i + 1] = N + i * tile_rows;
+  }
+  if (i == 0) {
+    tiles[2 * max_tiles] = n_sh;
+    tiles[2 * max_tiles + 1] = 0;
+  }
+  if (i <= E) offsets[i] = N;
+  if (i == E + 1) offsets[i] = N + T;
+  if (i < T) sorted_token[N + i] = i;
+}
+}  // namespace
+
+hipError_t launch_shared_meta(int32_t *tiles, int32_t *offsets, int32_t *sorted_token, int T,
+                              int N, int E, int tile_rows, int max_tiles, hipStream_t stream) {
+  const int n = T > E + 2 ? T : E + 2;
+  hipLaunchKernelGGL(shared_meta_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, tiles,
+                     offsets, sorted_token, T, N, E, tile_rows, max_tiles);
+  return hipGetLastError();
+}
+
 }  // namespace hy3moe

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 9
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 10
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -90,6 +90,10 @@ def test_workspace_layout_is_consistent(lib, name):
             names.append(n)
     assert L.total - max(L.xq_shared, L.xs_shared) >= (c.T * c.H // 32 if L.xs_shared else 0)
     assert (L.hq > 0) == (L.hs > 0) == ("mxfp8" in (c.act_format, c.sa_format))
+    assert (L.shared_meta > 0) == (c.I_shared > 0 and (mixed or L.tile_rows == 256))
+    if L.shared_meta:
+        names.append("shared_meta")
+        assert L.total - L.shared_meta >= 4 * (2 * L.max_tiles + 2 + c.E + 2 + R_of(c))
     if L.xs:
         names.append("xs")
     if L.hq:

@@ -280,22 +280,71 @@ def test_permutation_is_exact_and_stable(dev, T):
     np.testing.assert_array_equal(pos_of[order], np.arange(N))
     np.testing.assert_array_equal(sorted_token[:N], order // c.K)
     np.testing.assert_array_equal(sorted_token[N:], np.arange(c.T))
-    # tiles cover every row exactly once; largest groups first on the tile-grid
-    # paths, group order on the weight-streaming path
-    tiles = arr(L.tiles, 2 * L.max_tiles + 1)
-    nt = tiles[-1]
+    # tiles cover every row exactly once.  When the shared expert runs on
+    # the side stream (the large-tile path) its tiles come last, after the
+    # routed tile count; the groups before are ranked largest first on the
+    # tile-grid paths and kept in group order on the weight-streaming path
+    tiles = arr(L.tiles, 2 * L.max_tiles + 2)
+    nt, n_routed = tiles[-2], tiles[-1]
     pairs = tiles[:2 * nt].reshape(-1, 2)
     covered = np.zeros(N + c.T, dtype=int)
     for g, r0 in pairs:
         covered[r0:min(r0 + L.tile_rows, offsets[g + 1])] += 1
     assert (covered == 1).all()
-    if T <= 64:
-        assert (np.diff(pairs[:, 0]) >= 0).all()
+    side = L.shared_meta > 0
+    assert side == (L.tile_rows == 256)
+    G = c.E if side else c.E + 1
+    if side:
+        assert (pairs[:n_routed, 0] < c.E).all() and (pairs[n_routed:, 0] == c.E).all()
     else:
-        per_group = np.array([np.sum(pairs[:, 0] == g) for g in range(c.E + 1)])
-        firsts = [np.argmax(pairs[:, 0] == g) for g in range(c.E + 1) if per_group[g]]
-        assert all(per_group[pairs[i, 0]] >= per_group[pairs[j, 0]]
+        assert n_routed == nt
+    ranked = pairs[:n_routed]
+    if T <= 64:
+        assert (np.diff(ranked[:, 0]) >= 0).all()
+    else:
+        per_group = np.array([np.sum(ranked[:, 0] == g) for g in range(G)])
+        firsts = [np.argmax(ranked[:, 0] == g) for g in range(G) if per_group[g]]
+        assert all(per_group[ranked[i, 0]] >= per_group[ranked[j, 0]]
                    for i, j in zip(sorted(firsts)[:-1], sorted(firsts)[1:]))
+    if not side:
+        return
+    # the side stream's own metadata: the shared tiles, empty routed groups
+    # at row N, and the identity row map of the shared rows
+    nm = 2 * L.max_tiles + 2
+    meta = arr(L.shared_meta, nm + c.E + 2 + N + c.T)
+    n_sh = -(-c.T // L.tile_rows)
+    assert meta[nm - 2] == n_sh and meta[nm - 1] == 0
+    np.testing.assert_array_equal(meta[:2 * n_sh].reshape(-1, 2),
+                                  [[c.E, N + i * L.tile_rows] for i in range(n_sh)])
+    np.testing.assert_array_equal(meta[nm:nm + c.E + 2], [N] * (c.E + 1) + [N + c.T])
+    np.testing.assert_array_equal(meta[nm + c.E + 2 + N:], np.arange(c.T))
+
+
+@pytest.mark.parametrize("name", ["skinny_T16", "tiled_T300_ragged", "big_T513_tails",
+                                  "w8a8_big_T400_softmax", "w4a8_T16", "mixed_big_T513_H384",
+                                  "mixed_tiled_T300", "skinny_T64_f32"])
+def test_side_stream_matches_the_serial_chain(dev, name):
+    """hy3moe_forward runs the shared expert on its side stream beside the
+    routing chain on the large-tile path and with formats of its own;
+    hy3moe_forward_static keeps every kernel on the caller's stream.  Same
+    kernels on the same rows: the outputs and routes agree bit for bit, on
+    every GEMM path."""
+    inp = random_small(**SMALL[name])
+    c = inp.cfg
+    cfg = config_of(inp)
+    assert sm.hy3moe_workspace_bytes(cfg, True) <= sm.load().hy3moe_static_scratch_bytes()
+    w = upload_weights(inp, dev)
+    x = to_torch(inp.x(), c.dtype, dev)
+    log(f"side stream vs serial: {name}")
+    out, idx, wt = sm.forward(cfg, x, w, return_route=True)
+    ref = torch.empty_like(x)
+    ridx = torch.empty_like(idx)
+    rwt = torch.empty_like(wt)
+    sm.hy3moe_forward_static(cfg, x, w, ref, ridx, rwt)
+    torch.cuda.synchronize()
+    bits = torch.int16 if c.dtype == "bf16" else torch.int32
+    assert torch.equal(out.view(bits), ref.view(bits))
+    assert torch.equal(idx, ridx) and torch.equal(wt.view(torch.int32), rwt.view(torch.int32))
 
 
 def test_deterministic_bitwise(dev):

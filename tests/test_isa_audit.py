@@ -66,10 +66,11 @@ def test_large_tile_bf16_kernels_do_not_spill(tmp_path):
     pairs = re.findall(r"\.name:\s+(\S+)\s+\.private_segment_fixed_size:\s+(\d+)", asm)
     bf16 = [(n, int(v)) for n, v in pairs if "expert_big_kernelINS_6bf16_t" in n]
     # gate-up and down with bf16, FP8 and MXFP4 weights, and FP8 weights with
-    # FP8 activations (template <T, GATE_UP, weight format, A8>)
-    assert len(bf16) == 8
-    tight = [(n, v) for n, v in bf16 if re.search(r"Li[01]ELb0EEEv", n)]
-    assert len(tight) == 4
+    # FP8 activations, each for the routed and the shared expert's launches
+    # (template <T, GATE_UP, weight format, A8, BRANCH>)
+    assert len(bf16) == 16
+    tight = [(n, v) for n, v in bf16 if re.search(r"Li[01]ELb0ELi[01]EEEv", n)]
+    assert len(tight) == 8
     assert all(v == 0 for _, v in tight), tight
     # the MXFP4 and FP8-MFMA variants keep a few registers of tile bookkeeping
     # in scratch (outside the K loop)
