@@ -365,7 +365,7 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
 
     # ---- algorithmic work ----
     eb = 2 if c.dtype == "bf16" else 4
-    tile_rows = sm.hy3moe_workspace_layout(cfg).tile_rows
+    gemm_path = sm.hy3moe_workspace_layout(cfg).gemm_path
 
     def branch(wf, af):
         """(bytes per weight element, bytes per x / h element, FP8-rate MFMAs)
@@ -375,9 +375,9 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
         per 32 on the weight-streaming and large-tile paths (FP4 x FP8 MFMAs,
         which issue at the FP8 rate), bf16 values on the 128-row tiled path."""
         web = {"fp8_e4m3": 1, "mxfp4": 0.5 + 1 / 32}.get(wf, eb)
-        f8 = af in ("fp8_static", "mxfp8") and tile_rows == 256
+        f8 = af in ("fp8_static", "mxfp8") and gemm_path == 2
         ab = 1 if f8 else eb
-        if af == "mxfp8" and tile_rows != 128:
+        if af == "mxfp8" and gemm_path != 1:
             ab = 1 + 1 / 32
         mma = ("mxfp4_x_mxfp8" if af == "mxfp8" else "fp8_e4m3") if f8 else c.dtype
         return web, ab, f8, mma
@@ -421,7 +421,7 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
                 "per_unit": f"{2 * I * H * web:.0f} B of {kind} gate+up weights per touched "
                             f"routed expert x {U} experts{shared_note} + x and h rows"}
     else:
-        path = "256x256-tile" if tile_rows == 256 else "128x128-tile"
+        path = "128x128-tile" if gemm_path == 1 else "256x256-tile"
         if fp8_mma:
             path += " FP4 x FP8 MFMA" if c.act_format == "mxfp8" else " FP8 MFMA"
             if mixed and mma_s != branch(c.w_format, c.act_format)[3]:

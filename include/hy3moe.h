@@ -254,6 +254,8 @@ typedef struct hy3moe_ws_layout {
                             offsets [E+2] and row map [R] for its launches on the
                             side stream (0: the shared expert, if any, runs in
                             the routed experts' launches on the caller's stream) */
+  int32_t gemm_path;     /* expert GEMMs: 0 weight streaming (T <= 64), 1 tiles of
+                            128 rows, 2 tiles of 256 rows                      */
 } hy3moe_ws_layout;
 
 /* Workspace size in bytes for hy3moe_forward (for_forward != 0) or for

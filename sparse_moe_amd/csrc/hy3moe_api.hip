@@ -121,6 +121,7 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
   L->sorted_token = off; off += al((size_t)R * 4);
   L->pos_of = off;      off += al((size_t)N * 4);
   const int path = path_of(c);
+  L->gemm_path = path;
   if (path == PATH_SKINNY) {
     L->tile_rows = skinny_tile_rows((int)T);
     L->max_tiles = E + 1;
@@ -211,7 +212,7 @@ SideStream *side_stream(hipStream_t caller, std::unique_lock<std::mutex> *lock) 
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 10; }
+int hy3moe_abi_version(void) { return 11; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {

@@ -229,7 +229,7 @@ class WorkspaceActivations:
         self.fmt = {}
         for i, (br, act) in enumerate((("routed", c.act_format), ("shared", c.sa_format))):
             a8 = _a8(inp, act)
-            codes = L.tile_rows == 256 if a8 is not None else L.tile_rows != 128
+            codes = L.gemm_path == 2 if a8 is not None else L.gemm_path != 1
             if codes_path is not None:
                 codes = bool(codes_path[i])
             self.fmt[br] = (a8, act == "mxfp8", codes)

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 10
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 11
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -90,7 +90,7 @@ def test_workspace_layout_is_consistent(lib, name):
             names.append(n)
     assert L.total - max(L.xq_shared, L.xs_shared) >= (c.T * c.H // 32 if L.xs_shared else 0)
     assert (L.hq > 0) == (L.hs > 0) == ("mxfp8" in (c.act_format, c.sa_format))
-    assert (L.shared_meta > 0) == (c.I_shared > 0 and (mixed or L.tile_rows == 256))
+    assert (L.shared_meta > 0) == (c.I_shared > 0 and (mixed or L.gemm_path == 2))
     if L.shared_meta:
         names.append("shared_meta")
         assert L.total - L.shared_meta >= 4 * (2 * L.max_tiles + 2 + c.E + 2 + R_of(c))
@@ -110,6 +110,8 @@ def test_workspace_layout_is_consistent(lib, name):
     assert L.y - L.h >= R * max(c.I, c.I_shared) * eb
     assert L.max_tiles >= (R + L.tile_rows - 1) // L.tile_rows
     assert L.tile_rows >= min(c.T, 16)
+    want = {0: L.tile_rows, 1: 128, 2: 256}[L.gemm_path]
+    assert L.tile_rows == want and (L.gemm_path == 0) == (c.T <= 64)
 
 
 @pytest.mark.parametrize("bad, code", [
@@ -207,13 +209,14 @@ def test_w8a8_path_choice(lib):
     """W8A8 batches take the large-tile FP8-MFMA path only when H, I and
     I_shared are multiples of 128 (its K stages hold 128 values)."""
     big = sm.hy3moe_workspace_layout(cfg_of(CONFIGS["hy3_prefill_T8192_skew_w8a8"]))
-    assert big.tile_rows == 256
+    assert big.gemm_path == 2 and big.tile_rows == 256
     for kw in (dict(H=4096 + 64), dict(I=1536 + 64), dict(I_shared=64)):
         L = sm.hy3moe_workspace_layout(cfg_of(CONFIGS["hy3_prefill_T8192_skew_w8a8"], **kw))
-        assert L.tile_rows == 128, kw
+        assert L.gemm_path == 1 and L.tile_rows == 128, kw
         # ... while the same shapes with W8A16 stay on the large-tile path
-        L16 = sm.hy3moe_workspace_layout(cfg_of(CONFIGS["hy3_prefill_T8192_skew_w8a8"], act_format="dtype", **kw))
-        assert L16.tile_rows == 256, kw
+        L16 = sm.hy3moe_workspace_layout(cfg_of(CONFIGS["hy3_prefill_T8192_skew_w8a8"],
+                                                act_format="dtype", **kw))
+        assert L16.gemm_path == 2 and L16.tile_rows == 256, kw
 
 
 def test_mxfp4_weights_need_their_block_scales(lib):

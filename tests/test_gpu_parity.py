@@ -292,7 +292,7 @@ def test_permutation_is_exact_and_stable(dev, T):
         covered[r0:min(r0 + L.tile_rows, offsets[g + 1])] += 1
     assert (covered == 1).all()
     side = L.shared_meta > 0
-    assert side == (L.tile_rows == 256)
+    assert side == (L.gemm_path == 2)
     G = c.E if side else c.E + 1
     if side:
         assert (pairs[:n_routed, 0] < c.E).all() and (pairs[n_routed:, 0] == c.E).all()

@@ -91,7 +91,7 @@ def test_w8a8_codes_in_the_workspace(dev, T, E, H, path_rows):
     L = sm.hy3moe_workspace_layout(cfg)
     if path_rows is not None:
         assert L.tile_rows == path_rows
-    codes_path = L.tile_rows == 256
+    codes_path = L.gemm_path == 2
     ws = sm.alloc_workspace(cfg, True, dev)
     weights = upload_weights(inp, dev)
     x = to_torch(inp.x(), c.dtype, dev)
