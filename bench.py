@@ -175,7 +175,7 @@ def attention_bench(args, dev):
                    "q_heads": 64, "kv_heads": hkv, "head_dim": d, "tile": plan.tile,
                    "workers": plan.n_workers, "tasks": n_tasks,
                    "lengths": ATTN_WORKLOADS[args.workload]},
-        "roofline": {"kernel": "attn_split_kernel + attn_combine_kernel", "bound": "hbm",
+        "roofline": {"kernel": "attn_split_mfma_kernel + attn_combine_kernel", "bound": "hbm",
                      "achieved": alg / (ev_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": alg / (ev_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": measured_traffic(args.workload, "attn"),

@@ -5,18 +5,13 @@
 // workgroup per worker taking its tasks from the map, and a combine.
 //
 // HBM-bound: every cached key and value byte is read once.  A workgroup
-// (4 wavefronts) walks a task's tokens in chunks of 32, the next chunk's
-// loads in flight while one is multiplied; lane (row r, chunk c)
-// of a wavefront holds head-dims 8c .. 8c+7 of token 4 i + r of its step i,
-// so one 16-byte load per lane covers 4 whole 256-byte key rows (1 KB
-// contiguous).  The 8 query heads' scores of a token are summed over the 16
-// lanes of its row with DPP moves (the sum lands in all 16 lanes), and each
-// row keeps its own online softmax (running maximum m, sum l and the
-// unnormalised output of its 8 dims for the 8 heads) over the tokens it
-// sees.  At the end of a task the 16 row streams of the workgroup are merged
-// (lane shuffles inside a wavefront, then LDS) and written as one split.
-// Scores are kept in log2 units (q is pre-multiplied by log2(e)/sqrt(128)),
-// so the softmax uses exp2.
+// (4 wavefronts) walks a task's tokens in steps of 128, each wavefront a
+// 32-token block, the next block's loads in flight while one is multiplied.
+// The 8 query heads' scores and the P V product run on MFMA (see
+// attn_split_mfma_kernel); the softmax keeps one running maximum per head
+// and wavefront.  At the end of a task the 4 wavefronts' streams are merged
+// in LDS and written as one split.  Scores are kept in log2 units (scaled by
+// log2(e)/sqrt(128) after the dot product), so the softmax uses exp2.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -28,82 +23,140 @@ namespace hy3attn {
 
 namespace {
 
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
 constexpr int D = HY3ATTN_HEAD_DIM;   // 128
 constexpr int G = HY3ATTN_GROUP;      // 8 query heads per KV head
-constexpr int STEPS = 2;              // token steps per chunk (4 tokens per wavefront step)
-constexpr int CHUNK = 4 * 4 * STEPS;  // tokens per workgroup chunk: 4 waves x 4 rows x STEPS
-
 struct Partial {
   float *o;    // [n_tasks][G][D] unnormalised output
   float *ml;   // [n_tasks][2][G]: running maximum (log2 units), sum
 };
 
-__device__ __forceinline__ void bf16x8_to_f32(const uint4 u, float *f) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+__device__ __forceinline__ float exp2_or_zero(float x) { return x == -INFINITY ? 0.f : exp2f(x); }
+
+// The split kernel.  Per wavefront, 32-token blocks of a task
+// (the workgroup's 4 wavefronts take consecutive blocks of each 128-token
+// step):
+//  * scores: S^T[token][head] = K Q^T with MFMA 16x16x32 (bf16 in, float32
+//    out), K the A operand loaded straight from memory (lane (m, g) takes
+//    dims 32s + 8g .. +8 of token m of a 16-token tile: 16 rows x 64 bytes per
+//    instruction, every row whole over the 4 K steps), Q^T the B operand held
+//    for the task (columns 8..15 zero: 8 query heads per KV head).  Lane (n, g)
+//    then holds the scores of head n for tokens 4g .. 4g+3 of each tile.
+//  * softmax: one running maximum per head, common to the wavefront (the
+//    block maximum crosses the 4 lane groups of a head with two shuffles);
+//    each lane keeps a partial sum.
+//  * P V: O[head][dim] += P[head][token] V[token][dim], again MFMA
+//    16x16x32.  The contraction runs over the block's 32 tokens in the order
+//    that puts lane (n, g)'s own 8 probabilities in its A operand (slot j:
+//    token 4g + j of tile 0 for j < 4, token 4g + j - 4 of tile 1 after), so
+//    P needs no data movement; the B operand gathers the same tokens' values
+//    of one dimension from the wavefront's V tile in LDS (32 rows x 256
+//    bytes, written by the wavefront itself).  P goes in as bf16 hi + lo
+//    (two MFMAs on the same V operand), so it keeps ~16 significant bits and
+//    the float32 partial sum l matches it.
+// The unnormalised output, maximum and sum per task go to the same partials
+// the combine kernel reads.
+__device__ __forceinline__ f32x4 mma_bf16(const uint4 &a, const uint4 &b, f32x4 c) {
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// The softmax and P V of one 32-token block, given its score tiles s0, s1
+// (S^T of tokens tb + [0, 16) and tb + [16, 32)) and the block's V rows in
+// this wavefront's LDS tile vs.
+__device__ __forceinline__ void block_softmax_pv(const f32x4 &s0, const f32x4 &s1, int tb, int e,
+                                                 float qscale, float &m, float &l, f32x4 (&o)[8],
+                                                 const uint16_t *vs, int g4, int n16) {
+  float sv[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  for (int j = 0; j < 8; ++j) {
+    const int tok = tb + 16 * (j >> 2) + 4 * g4 + (j & 3);
+    const float x = (j < 4 ? s0 : s1)[j & 3];
+    sv[j] = tok < e ? x * qscale : -INFINITY;
+  }
+  float mb = sv[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mb = fmaxf(mb, sv[j]);
+  mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+  mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+  const float mn = fmaxf(m, mb);
+  const float a = mn == -INFINITY ? 1.f : exp2_or_zero(m - mn);
+  uint32_t ph[4], pl[4];
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const float p0 = mn == -INFINITY ? 0.f : exp2_or_zero(sv[j] - mn);
+    const float p1 = mn == -INFINITY ? 0.f : exp2_or_zero(sv[j + 1] - mn);
+    ps += p0 + p1;
+    const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
+    const float r0 = p0 - __uint_as_float(h0 << 16), r1 = p1 - __uint_as_float(h1 << 16);
+    ph[j >> 1] = h0 | (h1 << 16);
+    pl[j >> 1] = bf16_rne(r0) | (bf16_rne(r1) << 16);
+  }
+  l = l * a + ps;
+  m = mn;
+  // the O rows of this lane are heads 4 g4 + r: their rescale factors
+  float ar[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ar[r] = __shfl(a, 4 * g4 + r, 64);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    o[i][0] *= ar[0]; o[i][1] *= ar[1]; o[i][2] *= ar[2]; o[i][3] *= ar[3];
+  }
+  const uint4 pa_hi = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+  const uint4 pa_lo = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+  // B operand of dim block i: the tokens of slots j (rows 4 g4 + j, then
+  // 16 + 4 g4 + j - 4) at dim 16 i + n16
+  const uint16_t *c0 = vs + (4 * g4) * D + n16, *c1 = vs + (16 + 4 * g4) * D + n16;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 bv = make_uint4(
+        (uint32_t)c0[0 * D + 16 * i] | ((uint32_t)c0[1 * D + 16 * i] << 16),
+        (uint32_t)c0[2 * D + 16 * i] | ((uint32_t)c0[3 * D + 16 * i] << 16),
+        (uint32_t)c1[0 * D + 16 * i] | ((uint32_t)c1[1 * D + 16 * i] << 16),
+        (uint32_t)c1[2 * D + 16 * i] | ((uint32_t)c1[3 * D + 16 * i] << 16));
+    o[i] = mma_bf16(pa_hi, bv, o[i]);
+    o[i] = mma_bf16(pa_lo, bv, o[i]);
   }
 }
 
-// x + x of lane CTRL(lane), for a DPP pattern inside a row of 16 lanes.
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float x) {
-  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF,
-                                            0xF, false);
-  return x + __int_as_float(y);
-}
-// Sum over the 16 lanes of a row, in all of them: neighbours, pairs, the
-// mirrored half row, the mirrored row.
-__device__ __forceinline__ float row16_sum(float x) {
-  x = dpp_add<0xB1>(x);
-  x = dpp_add<0x4E>(x);
-  x = dpp_add<0x141>(x);
-  return dpp_add<0x140>(x);
-}
-
-__device__ __forceinline__ float exp2_or_zero(float x) { return x == -INFINITY ? 0.f : exp2f(x); }
-
-// Merge stream (m2, l2, o2) into (m, l, o) for one head.
-__device__ __forceinline__ void merge(float &m, float &l, float (&o)[8], float m2, float l2,
-                                      const float (&o2)[8]) {
-  const float M = fmaxf(m, m2);
-  const float a = M == -INFINITY ? 0.f : exp2_or_zero(m - M);
-  const float b = M == -INFINITY ? 0.f : exp2_or_zero(m2 - M);
-  l = l * a + l2 * b;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = o[i] * a + o2[i] * b;
-  m = M;
-}
-
-__global__ __launch_bounds__(256, 2) void attn_split_kernel(
+__global__ __launch_bounds__(256, 2) void attn_split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ kv_start, int B, int Hkv,
     int tile, const int32_t *__restrict__ tasks, int n_tasks,
     const int32_t *__restrict__ worker_begin, Partial part) {
-  __shared__ float mls[4][2][G];       // per wavefront: m, l of the 8 heads
-  __shared__ float os[4][G][D];        // per wavefront: unnormalised output
+  constexpr int BLK = 32;                  // tokens per wavefront block
+  constexpr int STEP = 4 * BLK;            // tokens per workgroup step
+  __shared__ uint4 vtile[4][BLK * D / 8];  // per wavefront: [32 tokens][128 dims] bf16
+  __shared__ float mls[4][2][G];
+  __shared__ float os[4][G][D];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row = lane >> 4, c = lane & 15;          // token row of a step, dim chunk
+  const int n16 = lane & 15, g4 = lane >> 4;
   const int total = kv_start[B];
   const float qscale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
-  // a worker's task range, clamped to the plan's tasks
   const int t_beg = max(worker_begin[blockIdx.x], 0);
   const int t_end = min(worker_begin[blockIdx.x + 1], n_tasks);
+  uint4 *vw = vtile[wave];
+  const uint16_t *vs = reinterpret_cast<const uint16_t *>(vtile[wave]);
   for (int t = t_beg; t < t_end; ++t) {
     const int b = __builtin_amdgcn_readfirstlane(tasks[4 * t]);
     const int h = __builtin_amdgcn_readfirstlane(tasks[4 * t + 1]);
     const int t0 = __builtin_amdgcn_readfirstlane(tasks[4 * t + 2]);
     const int t1 = __builtin_amdgcn_readfirstlane(tasks[4 * t + 3]);
-    // a task naming a request or KV head outside this call, or no tiles, is
-    // an empty split: kv_start is read only for a request of this call
     const bool valid = b >= 0 && b < B && h >= 0 && h < Hkv && t0 >= 0 && t1 > t0;
     const int base = valid ? kv_start[b] : 0, L = valid ? kv_start[b + 1] - base : 0;
     const int64_t s64 = (int64_t)t0 * tile, e64 = min((int64_t)t1 * tile, (int64_t)L);
-    const int s = base + (int)min(s64, (int64_t)L);       // first token of the split
-    const int e = base + (int)e64;                        // end (> s for a plan of these lengths)
+    const int s = base + (int)min(s64, (int64_t)L);
+    const int e = base + (int)e64;
     if (!valid || e <= s) {   // a plan made for other lengths: an empty split, no loads
       const int g = tid >> 5, d4 = tid & 31;
       *reinterpret_cast<float4 *>(part.o + ((size_t)t * G + g) * D + 4 * d4) =
@@ -114,109 +167,80 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(
       }
       continue;
     }
-    // the lane's 8 dims of the 8 query heads, in log2 units
-    float qv[G][8];
+    // Q^T operand: lane (head n16, K group g4), dims 32 st + 8 g4 .. +8
+    uint4 qb[4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint4 u = *reinterpret_cast<const uint4 *>(q + ((size_t)b * (G * Hkv) + G * h + g) * D + 8 * c);
-      bf16x8_to_f32(u, qv[g]);
+    for (int st = 0; st < 4; ++st)
+      qb[st] = n16 < G ? *reinterpret_cast<const uint4 *>(
+                             q + ((size_t)b * (G * Hkv) + G * h + n16) * D + 32 * st + 8 * g4)
+                       : make_uint4(0u, 0u, 0u, 0u);
+    float m = -INFINITY, l = 0.f;    // head n16: common maximum, this lane's partial sum
+    f32x4 o[8];                      // O[head 4 g4 + r][dim 16 i + n16]
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qv[g][i] *= qscale;
+    for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the KV head's rows: a uniform base plus 32-bit element offsets (the
+    // caller's K and V hold fewer than 2^31 elements per KV head)
+    const uint16_t *kh = k + (size_t)h * total * D;
+    const uint16_t *vh = v + (size_t)h * total * D;
+    // A block's loads: K operands of its 2 tiles x 4 K steps (lane (m, g):
+    // token m of the tile, dims 32 st + 8 g), V rows (lane (row g, chunk n):
+    // dims 8 n .. +8 of token 4 i + g); tokens past e re-read token e - 1 (in
+    // bounds) and are masked.  Two sets of named registers: the next block's
+    // loads are in flight while one is multiplied.
+#define ATT_K(S, tt, st, tok) S##k##tt##st = *reinterpret_cast<const uint4 *>(kh + ((tok) * D + 32 * st + 8 * g4));
+#define ATT_V(S, i)                                                                    \
+  S##v##i = *reinterpret_cast<const uint4 *>(                                          \
+      vh + ((uint32_t)min(tb_ + 4 * i + g4, e - 1) * D + 8 * n16));
+#define ATT_W(S, i) vw[(4 * i + g4) * 16 + n16] = S##v##i;
+#define ATT_LOAD(S, cb)                                                                \
+  {                                                                                    \
+    const int tb_ = (cb) + BLK * wave;                                                 \
+    const uint32_t ta_ = (uint32_t)min(tb_ + n16, e - 1);                              \
+    const uint32_t tc_ = (uint32_t)min(tb_ + 16 + n16, e - 1);                         \
+    ATT_K(S, 0, 0, ta_) ATT_K(S, 0, 1, ta_) ATT_K(S, 0, 2, ta_) ATT_K(S, 0, 3, ta_)    \
+    ATT_K(S, 1, 0, tc_) ATT_K(S, 1, 1, tc_) ATT_K(S, 1, 2, tc_) ATT_K(S, 1, 3, tc_)    \
+    ATT_V(S, 0) ATT_V(S, 1) ATT_V(S, 2) ATT_V(S, 3)                                    \
+    ATT_V(S, 4) ATT_V(S, 5) ATT_V(S, 6) ATT_V(S, 7)                                    \
+  }
+#define ATT_COMPUTE(S, cb)                                                             \
+  {                                                                                    \
+    const int tb_ = (cb) + BLK * wave;                                                 \
+    f32x4 s0_ = f32x4{0.f, 0.f, 0.f, 0.f}, s1_ = f32x4{0.f, 0.f, 0.f, 0.f};           \
+    s0_ = mma_bf16(S##k00, qb[0], s0_); s0_ = mma_bf16(S##k01, qb[1], s0_);            \
+    s0_ = mma_bf16(S##k02, qb[2], s0_); s0_ = mma_bf16(S##k03, qb[3], s0_);            \
+    s1_ = mma_bf16(S##k10, qb[0], s1_); s1_ = mma_bf16(S##k11, qb[1], s1_);            \
+    s1_ = mma_bf16(S##k12, qb[2], s1_); s1_ = mma_bf16(S##k13, qb[3], s1_);            \
+    ATT_W(S, 0) ATT_W(S, 1) ATT_W(S, 2) ATT_W(S, 3)                                    \
+    ATT_W(S, 4) ATT_W(S, 5) ATT_W(S, 6) ATT_W(S, 7)                                    \
+    block_softmax_pv(s0_, s1_, tb_, e, qscale, m, l, o, vs, g4, n16);                  \
+  }
+    uint4 ak00, ak01, ak02, ak03, ak10, ak11, ak12, ak13, av0, av1, av2, av3, av4, av5, av6, av7;
+    uint4 bk00, bk01, bk02, bk03, bk10, bk11, bk12, bk13, bv0, bv1, bv2, bv3, bv4, bv5, bv6, bv7;
+    ATT_LOAD(a, s)
+    for (int cb = s; cb < e; cb += 2 * STEP) {
+      ATT_LOAD(b, cb + STEP)
+      ATT_COMPUTE(a, cb)
+      if (cb + STEP >= e) break;
+      ATT_LOAD(a, cb + 2 * STEP)
+      ATT_COMPUTE(b, cb + STEP)
     }
-    float m[G], l[G], o[G][8];
+#undef ATT_COMPUTE
+#undef ATT_LOAD
+#undef ATT_W
+#undef ATT_V
+#undef ATT_K
+    // the wavefront's sum of head n16 over its 4 lane groups
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (g4 < 2) {   // heads 0..7 of O
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m[g] = -INFINITY;
-      l[g] = 0.f;
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[g][i] = 0.f;
+        for (int r = 0; r < 4; ++r) os[wave][4 * g4 + r][16 * i + n16] = o[i][r];
     }
-    const uint16_t *kh = k + (size_t)h * total * D + 8 * c;
-    const uint16_t *vh = v + (size_t)h * total * D + 8 * c;
-    // Two register sets: the next chunk's keys and values are in flight while
-    // the current chunk is multiplied.  Tokens past e re-read token e - 1
-    // (in bounds) and are masked.
-    auto load = [&](uint4 (&ku)[STEPS], uint4 (&vu)[STEPS], int cb) {
-#pragma unroll
-      for (int i = 0; i < STEPS; ++i) {
-        const int tok = min(cb + wave * 4 * STEPS + 4 * i + row, e - 1);
-        ku[i] = *reinterpret_cast<const uint4 *>(kh + (size_t)tok * D);
-        vu[i] = *reinterpret_cast<const uint4 *>(vh + (size_t)tok * D);
-      }
-    };
-    auto compute = [&](const uint4 (&ku)[STEPS], const uint4 (&vu)[STEPS], int cb) {
-      float sc[STEPS][G];
-#pragma unroll
-      for (int i = 0; i < STEPS; ++i) {
-        const bool ok = cb + wave * 4 * STEPS + 4 * i + row < e;
-        float kf[8];
-        bf16x8_to_f32(ku[i], kf);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float acc = 0.f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc = fmaf(qv[g][j], kf[j], acc);
-          acc = row16_sum(acc);
-          sc[i][g] = ok ? acc : -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float mb = sc[0][g];
-#pragma unroll
-        for (int i = 1; i < STEPS; ++i) mb = fmaxf(mb, sc[i][g]);
-        const float mn = fmaxf(m[g], mb);
-        const float a = mn == -INFINITY ? 1.f : exp2_or_zero(m[g] - mn);
-        float p[STEPS], ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < STEPS; ++i) {
-          p[i] = mn == -INFINITY ? 0.f : exp2_or_zero(sc[i][g] - mn);
-          ps += p[i];
-        }
-        l[g] = l[g] * a + ps;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] *= a;
-#pragma unroll
-        for (int i = 0; i < STEPS; ++i) {
-          float vf[8];
-          bf16x8_to_f32(vu[i], vf);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o[g][j] = fmaf(p[i], vf[j], o[g][j]);
-        }
-        m[g] = mn;
-      }
-    };
-    uint4 kA[STEPS], vA[STEPS], kB[STEPS], vB[STEPS];
-    load(kA, vA, s);
-    for (int cb = s; cb < e; cb += 2 * CHUNK) {
-      load(kB, vB, cb + CHUNK);
-      compute(kA, vA, cb);
-      if (cb + CHUNK >= e) break;
-      load(kA, vA, cb + 2 * CHUNK);
-      compute(kB, vB, cb + CHUNK);
-    }
-    // merge the 4 row streams of the wavefront (lanes c, 16 + c, 32 + c, 48 + c)
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float m2 = __shfl_xor(m[g], off, 64), l2 = __shfl_xor(l[g], off, 64);
-        float o2[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o2[j] = __shfl_xor(o[g][j], off, 64);
-        merge(m[g], l[g], o[g], m2, l2, o2);
-      }
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) os[wave][g][8 * c + j] = o[g][j];
-        if (c == 0) {
-          mls[wave][0][g] = m[g];
-          mls[wave][1][g] = l[g];
-        }
-      }
+    if (lane < G) {
+      mls[wave][0][lane] = m;
+      mls[wave][1][lane] = l;
     }
     __syncthreads();
     {   // thread (head g, dims 4 d4 .. 4 d4 + 3): merge the 4 wavefronts
@@ -377,7 +401,7 @@ extern "C" int hy3attn_decode(const void *q, const void *k, const void *v, const
   part.o = static_cast<float *>(workspace);
   part.ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
   if (n_tasks > 0)
-    hipLaunchKernelGGL(attn_split_kernel, dim3(n_workers), dim3(256), 0, s,
+    hipLaunchKernelGGL(attn_split_mfma_kernel, dim3(n_workers), dim3(256), 0, s,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), kv_start, B, n_kv_heads, tile, tasks,
                        (int)n_tasks, worker_begin, part);
