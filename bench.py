@@ -365,17 +365,20 @@ def layer_bench(inp, weights, key, args, dev, graph=False):
 
     # ---- algorithmic work ----
     eb = 2 if c.dtype == "bf16" else 4
-    gemm_path = sm.hy3moe_workspace_layout(cfg).gemm_path
+    lay = sm.hy3moe_workspace_layout(cfg)
+    gemm_path, a8_codes = lay.gemm_path, bool(lay.a8_codes)
 
     def branch(wf, af):
         """(bytes per weight element, bytes per x / h element, FP8-rate MFMAs)
         of one branch.  MXFP4 weights: half a byte + one scale byte per 32.
-        Static FP8 activations: E4M3 bytes on the large-tile path (FP8 MFMAs),
-        their bf16 values on the others; dynamic MXFP8: codes and a scale byte
-        per 32 on the weight-streaming and large-tile paths (FP4 x FP8 MFMAs,
-        which issue at the FP8 rate), bf16 values on the 128-row tiled path."""
+        Static FP8 activations: E4M3 bytes where the layout reports code rows
+        (a8_codes: FP8 MFMAs), their bf16 values elsewhere; dynamic MXFP8:
+        codes and a scale byte per 32 on the weight-streaming and large-tile
+        paths (FP4 x FP8 MFMAs, which issue at the FP8 rate), bf16 values on
+        the 128-row tiled path."""
         web = {"fp8_e4m3": 1, "mxfp4": 0.5 + 1 / 32}.get(wf, eb)
-        f8 = af in ("fp8_static", "mxfp8") and gemm_path == 2
+        f8 = ((af == "fp8_static" and a8_codes) or
+              (af == "mxfp8" and gemm_path == 2))
         ab = 1 if f8 else eb
         if af == "mxfp8" and gemm_path != 1:
             ab = 1 + 1 / 32

@@ -256,6 +256,10 @@ typedef struct hy3moe_ws_layout {
                             the routed experts' launches on the caller's stream) */
   int32_t gemm_path;     /* expert GEMMs: 0 weight streaming (T <= 64), 1 tiles of
                             128 rows, 2 tiles of 256 rows                      */
+  int32_t a8_codes;      /* static FP8 activations (x and h) are stored as E4M3
+                            codes for FP8 MFMAs (large tiles; weight streaming
+                            when H, I and I_shared are multiples of 128), else
+                            as the bf16 values of the codes                    */
 } hy3moe_ws_layout;
 
 /* Workspace size in bytes for hy3moe_forward (for_forward != 0) or for

@@ -31,7 +31,7 @@ HY3MOE_AFMT_MXFP8 = 2
 HY3MOE_FMT_AS_ROUTED = -1
 
 HY3MOE_N_STAGES = 6
-ABI_VERSION = 11          # hy3moe_abi_version() of the library this binding matches
+ABI_VERSION = 12          # hy3moe_abi_version() of the library this binding matches
 STAGE_NAMES = ("router", "select", "permute", "gate_up", "down", "combine")
 
 EXPORTED_SYMBOLS = (
@@ -78,6 +78,7 @@ class hy3moe_ws_layout(ctypes.Structure):
         ("hq", ctypes.c_size_t), ("hs", ctypes.c_size_t),
         ("xq_shared", ctypes.c_size_t), ("xs_shared", ctypes.c_size_t),
         ("shared_meta", ctypes.c_size_t), ("gemm_path", ctypes.c_int32),
+        ("a8_codes", ctypes.c_int32),
     ]
 
 

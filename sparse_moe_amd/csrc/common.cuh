@@ -205,6 +205,19 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, float sc) {
 // One block-scaled 16x16x128 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): A = 32 FP4 E2M1 weights of the lane (16
 // bytes) with E8M0 scale sa, B = 32 FP8 E4M3 token values (two 16-byte
 // chunks) with E8M0 scale sb.
+// One 16x16x128 FP8 (E4M3 x E4M3) MFMA; each operand is two 16-byte chunks.
+// A and B lane group g's 32 bytes pair up byte for byte (both operands are
+// 8-bit), so any K order that both sides share gives the same sum.
+__device__ __forceinline__ void mma_fp8(f32x4_t &acc, const uint4 &a0, const uint4 &a1,
+                                        const uint4 &b0, const uint4 &b1) {
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8_t bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+}
+
 __device__ __forceinline__ void mma_fp4_fp8(f32x4_t &acc, const uint4 &w, uint32_t sa,
                                             const uint4 &x0, const uint4 &x1, uint32_t sb) {
   typedef int i32x8_t __attribute__((ext_vector_type(8)));

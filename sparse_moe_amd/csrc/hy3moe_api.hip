@@ -122,6 +122,11 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
   L->pos_of = off;      off += al((size_t)N * 4);
   const int path = path_of(c);
   L->gemm_path = path;
+  // static FP8 activations as E4M3 codes for FP8 MFMAs: the large-tile path,
+  // and weight streaming when every K (H, I, I_shared) is a multiple of 128
+  L->a8_codes = path == PATH_BIG ||
+                (path == PATH_SKINNY && c->H % 128 == 0 && c->I % 128 == 0 &&
+                 c->I_shared % 128 == 0);
   if (path == PATH_SKINNY) {
     L->tile_rows = skinny_tile_rows((int)T);
     L->max_tiles = E + 1;
@@ -212,7 +217,7 @@ SideStream *side_stream(hipStream_t caller, std::unique_lock<std::mutex> *lock) 
 
 extern "C" {
 
-int hy3moe_abi_version(void) { return 11; }
+int hy3moe_abi_version(void) { return 12; }
 
 const char *hy3moe_strerror(int code) {
   switch (code) {
@@ -445,7 +450,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
       B.act_sc = B.xs;
     } else if (B.f.act == HY3MOE_AFMT_FP8_STATIC) {
       e = check_launch(launch_quant_e4m3(x, cfg->dtype, (int64_t)T * H, w->x_scale, B.xq,
-                                         path == PATH_BIG ? 0 : 1, B.st));
+                                         L.a8_codes ? 0 : 1, B.st));
     }
     if (B.f.act != HY3MOE_AFMT_DTYPE) B.act = B.xq;
     return e;
@@ -461,6 +466,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   base.max_tiles = L.max_tiles;
   base.n_rows = (int)R;
   base.n_tok = T;
+  base.a8_codes = L.a8_codes;
   auto branch_args = [&](const Branch &B, bool gate_up) {
     ExpertArgs ea = base;
     ea.sorted_token = B.sorted_token;
@@ -471,7 +477,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
     return ea;
   };
   auto h_base = [&](const Branch &B) {
-    return ws + L.h + (B.f.act == HY3MOE_AFMT_FP8_STATIC && path == PATH_BIG && mix
+    return ws + L.h + (B.f.act == HY3MOE_AFMT_FP8_STATIC && L.a8_codes && mix
                            ? B.r0 * Imax : 0);
   };
   auto gate_up = [&](const Branch &B) -> int {

@@ -11,7 +11,10 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 // Storage of the expert weights inside the GEMM kernels.
 // WF_W4A8: MXFP4 weights with dynamic MXFP8 token rows (E4M3 codes and one
 // E8M0 scale per 32), multiplied by block-scaled FP4 x FP8 MFMAs.
-enum { WF_DTYPE = 0, WF_FP8 = 1, WF_MXFP4 = 2, WF_W4A8 = 3 };
+// WF_W8A8: FP8 weights with static FP8 token rows as E4M3 codes, multiplied
+// by FP8 x FP8 MFMAs (the weight-streaming path; the large-tile path has its
+// own A8 kernels).
+enum { WF_DTYPE = 0, WF_FP8 = 1, WF_MXFP4 = 2, WF_W4A8 = 3, WF_W8A8 = 4 };
 
 // Row-tile shapes of the expert GEMMs.
 constexpr int TILED_ROWS = 128;     // rows (token copies) per tile, large-T path
@@ -126,6 +129,10 @@ struct ExpertArgs {
   // GEMMs store h quantised with hs[g] in the same form.
   int a8;
   const float *xs, *hs;
+  // With a8: the token rows are E4M3 codes (FP8 MFMAs: the large-tile path,
+  // and the weight-streaming path when H, I and I_shared are multiples of
+  // 128), else the bf16 values of the codes (bf16 MFMAs).
+  int a8_codes;
 };
 // The slice of the tile list a launch walks (ExpertArgs::grp_sel): first
 // tile index and tile count.

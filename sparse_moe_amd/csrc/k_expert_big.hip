@@ -367,17 +367,6 @@ __device__ __forceinline__ uint4 weight_chunk(uint32_t q, uint32_t s) {
   return fp4x8_to_bf16(q, e8m0_to_f32(s));
 }
 
-// One 16x16x128 FP8 (E4M3 x E4M3) MFMA; each operand is two 16-byte chunks.
-__device__ __forceinline__ void mma_fp8(f32x4_t &acc, const uint4 &a0, const uint4 &a1,
-                                        const uint4 &b0, const uint4 &b1) {
-  typedef int i32x8_t __attribute__((ext_vector_type(8)));
-  const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-  const i32x8_t bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
-}
-
 // Order of one A8 stage per wavefront: the 8 B reads and the first A
 // fragment's 2 reads up front, then 8 groups, each of: one piece of stage
 // k + 1 from registers to LDS, the same registers reloaded with that piece

@@ -45,6 +45,15 @@
 // positions.  So A lane g takes weight block g of the step (16 contiguous
 // bytes, its own scale), and B lane g takes token bytes [16g, 16g + 16) and
 // [64 + 16g, 64 + 16g + 16) of the step with token block g's scale.
+//
+// W8A8 (FP8 weights, static FP8 token rows as E4M3 codes; H, I and I_shared
+// multiples of 128): two consecutive 64-byte steps of a weight fragment are
+// one v_mfma_f32_16x16x128_f8f6f4 (FP8 x FP8).  Lane (r16, g) supplies bytes
+// [16g, 16g + 16) of each of the two steps on both sides (weights and token
+// codes), so A and B pair up byte for byte; the weight scale times the
+// activation scale multiplies the accumulators.  Half the token bytes of the
+// bf16 values, a quarter of the MFMAs, no decode.  The gate-up epilogue
+// stores h as E4M3 codes for the down GEMM.
 #include "common.cuh"
 #include "internal.h"
 
@@ -57,10 +66,12 @@ constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
 
 // 64-byte steps per register set: bf16 weights UBASE / MT; FP8 weights 6 / 3
 // / 1 for 1 / 2 / 4 row fragments (each step also holds two token chunks);
-// MXFP4 3 / 2 / 1 (four token chunks per step).
+// W8A8 8 / 4 / 2 (one chunk of codes per step; even, as two steps make one
+// MFMA); MXFP4 3 / 2 / 1 (four token chunks per step).
 template <int MT, int WF>
 constexpr int steps_per_set() {
-  return WF == WF_FP8     ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1))
+  return WF == WF_W8A8    ? (MT == 1 ? 8 : (MT == 2 ? 4 : 2))   // even: pairs of steps
+         : WF == WF_FP8   ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1))
          : WF == WF_MXFP4 ? (MT == 1 ? 3 : (MT == 2 ? 2 : 1))
          : WF == WF_W4A8  ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
                           : UBASE / MT;
@@ -70,6 +81,9 @@ template <int WF>
 constexpr int token_chunks() {
   return WF == WF_MXFP4 ? 4 : ((WF == WF_FP8 || WF == WF_W4A8) ? 2 : 1);
 }
+// Token rows of E4M3 codes (one byte per K value).
+template <int WF>
+constexpr bool token_codes() { return WF == WF_W4A8 || WF == WF_W8A8; }
 
 // Where a unit's operands are (per lane) and what its epilogue needs.
 template <int MT>
@@ -104,8 +118,8 @@ __host__ __device__ constexpr int x_lds_stride(int row_bytes) { return row_bytes
 template <typename T, bool GATE_UP, int MT, int WF, bool XL>
 __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_blocks, int lane,
                                         UnitSrc<MT> &src, UnitOut &o, int half = 0) {
-  constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4 || WF == WF_W4A8;
-  constexpr bool MXA = WF == WF_W4A8;
+  constexpr bool F8 = WF == WF_FP8 || WF == WF_W8A8, F4 = WF == WF_MXFP4 || WF == WF_W4A8;
+  constexpr bool MXA = WF == WF_W4A8, CODES = token_codes<WF>();
   constexpr int EB = Elem<T>::kBytes;
   // bytes per weight row of K elements (MXFP4: half a byte per element)
   auto rowb = [](int K) { return F4 ? K / 2 : K * (F8 ? 1 : EB); };
@@ -152,6 +166,10 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
       src.s1p = sd + (size_t)n1 * sr + cg;
     }
   }
+  if (o.nf == 1) {   // one fragment: the second's loads re-read the first (cache hits), so
+    src.w1p = src.w0p;   // that the load sequence, and with it the compiler's waits on
+    src.s1p = src.s0p;   // the in-order load counter, does not depend on nf
+  }
   if (F8) {
     o.sc0 = shared ? *a.ssc0 : a.sc0[g];
     o.sc1 = GATE_UP ? (shared ? *a.ssc1 : a.sc1[g]) : o.sc0;
@@ -173,9 +191,11 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
     // 256-byte step (the K values of the lane's codes); W4A8: code bytes
     // [32g, 32g+32) of each 128-byte step, and block scale step * 4 + g
     if (XL)   // the token's row of the LDS copy, the lane's chunk of a step
-      src.xlo[m] = (uint32_t)a.sorted_token[trow] * (uint32_t)x_lds_stride(a.H * (MXA ? 1 : EB)) +
+      src.xlo[m] = (uint32_t)a.sorted_token[trow] * (uint32_t)x_lds_stride(a.H * (CODES ? 1 : EB)) +
                    cg * 16 * (MXA ? 1 : token_chunks<WF>());
-    if (MXA) {   // bytes [16g, 16g + 16) and [64 + 16g, ...) of each 128-byte step
+    if (WF == WF_W8A8) {   // code bytes [16g, 16g + 16) of each 64-byte step
+      src.xp[m] = static_cast<const char *>(a.act) + arow + cg * 16;
+    } else if (MXA) {   // bytes [16g, 16g + 16) and [64 + 16g, ...) of each 128-byte step
       src.xp[m] = static_cast<const char *>(a.act) + arow + cg * 16;
       src.xsp[m] = a.act_sc + arow / 32 + cg;
       // K % 512 == 0: weight scale rows of K/32 bytes are 16-byte multiples,
@@ -218,7 +238,7 @@ __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int 
 template <typename T, bool GATE_UP, int MT, int WF>
 __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut &o,
                                               f32x4_t (&acc)[2][MT], int lane) {
-  constexpr bool F8 = WF == WF_FP8;
+  constexpr bool F8 = WF == WF_FP8 || WF == WF_W8A8;
   const float s0 = F8 ? o.sc0 : 1.0f, s1 = F8 ? o.sc1 : 1.0f;
   const int r16 = lane & 15, cg = lane >> 4;
   // Lane holds D[col 4cg + q][token row 16m + r16].
@@ -230,7 +250,12 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
     if (GATE_UP) {
       const f32x4_t gv = acc[0][m] * s0, uv = acc[1][m] * s1;
       T *dst = out + (size_t)trow * a.ldh + o.col0 + 4 * cg;
-      if (F8 && a.a8)   // bf16 h quantised with its static scale, stored as bf16 values
+      if (WF == WF_W8A8)   // bf16 h quantised with its static scale: 4 code bytes
+        *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(a.out) + (size_t)trow * a.ldh +
+                                      o.col0 + 4 * cg) =
+            quant_e4m3x4_bf16(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]), swiglu(gv[2], uv[2]),
+                              swiglu(gv[3], uv[3]), o.hs);
+      else if (F8 && a.a8)   // bf16 h quantised with its static scale, stored as bf16 values
         *reinterpret_cast<uint2 *>(dst) = e4m3x4_to_bf16(
             quant_e4m3x4_bf16(swiglu(gv[0], uv[0]), swiglu(gv[1], uv[1]), swiglu(gv[2], uv[2]),
                               swiglu(gv[3], uv[3]), o.hs));
@@ -251,9 +276,14 @@ __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut
   }
 }
 
+// Floats of the per-group scales a workgroup stages (FP8 weights; reserved
+// for every format).
+__host__ __device__ constexpr int scale_lds_floats(int E) { return 3 * (E + 1) + 1; }
+
 // LDS bytes of the unit metadata a workgroup stages (see the kernel).
 inline size_t meta_lds_bytes(const ExpertArgs &a, bool gate_up) {
-  return 4 * ((size_t)2 * a.max_tiles + 2 + a.E + 2 + (gate_up ? a.n_rows : 0));
+  return 4 * ((size_t)2 * a.max_tiles + 2 + a.E + 2 + (gate_up ? a.n_rows : 0) +
+              scale_lds_floats(a.E));
 }
 
 // Threads per workgroup: 256 (two workgroups per CU), or 512 with the LDS
@@ -267,30 +297,86 @@ template <typename T, bool GATE_UP, int MT, int WF, bool XL, int BRANCH>
 __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_stream_kernel(
     ExpertArgs a_in, int n_col_blocks) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4, MXA = WF == WF_W4A8;
+  constexpr bool A8C = WF == WF_W8A8, CODES = token_codes<WF>();
   constexpr int NT = stream_threads<XL>(), WPB = NT / 64;
   // The unit metadata -- tile list, group offsets and (gate-up) the sorted
   // token ids -- is staged in LDS once per workgroup, so that the set-up of a
   // wavefront's next unit reads LDS instead of a chain of dependent global
   // loads, which held back the unit's first weight loads at every change.
+  // Each thread issues its loads of a round together and then writes them
+  // (one memory round trip per round, not one per word or chunk).
   extern __shared__ int32_t meta[];
   const int n_t = 2 * a_in.max_tiles + 2, n_o = a_in.E + 2;
-  for (int i = threadIdx.x; i < n_t; i += NT) meta[i] = a_in.tiles[i];
-  for (int i = threadIdx.x; i < n_o; i += NT) meta[n_t + i] = a_in.offsets[i];
-  if (GATE_UP)
-    for (int i = threadIdx.x; i < a_in.n_rows; i += NT)
-      meta[n_t + n_o + i] = a_in.sorted_token[i];
-  // XL: every token row of x, 16-byte chunks, after the metadata (16-byte aligned)
-  const int meta_n = (n_t + n_o + (GATE_UP ? a_in.n_rows : 0) + 3) & ~3;
+  const int n_m = n_t + n_o + (GATE_UP ? a_in.n_rows : 0);
+  constexpr int MB = 4;   // words per thread per round
+  for (int base = 0; base < n_m; base += NT * MB) {
+    // past the end a thread copies the last word again (no branch: a branch
+    // per word would have its load sunk into it)
+    int32_t v[MB];
+    int at[MB];
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int i = min(base + j * NT + (int)threadIdx.x, n_m - 1);
+      // word i of the concatenation: select the array's (shifted) base, then index
+      const int32_t *p = i < n_t ? a_in.tiles
+                         : i < n_t + n_o ? a_in.offsets - n_t
+                                         : a_in.sorted_token - (n_t + n_o);
+      v[j] = p[i];
+      at[j] = i;
+    }
+#pragma unroll
+    for (int j = 0; j < MB; ++j) meta[at[j]] = v[j];
+  }
+  // FP8 weights: the scales of every group of this launch (weights, and with
+  // a8 the activations) follow, so that a unit's set-up issues no global
+  // load: the wavefront would wait there for all of its streaming loads, as
+  // the wait counter is in order.  Layout: sc0[E+1] (group E: the shared
+  // expert), sc1[E+1], hs[E+1], xs.
+  constexpr bool FSC = F8 || A8C;
+  const int n_sc = scale_lds_floats(a_in.E);
+  float *scl = reinterpret_cast<float *>(meta + n_m);
+  if constexpr (FSC) {
+    const int E = a_in.E;
+    const bool routed = a_in.grp_sel != GRP_SHARED;
+    const bool shared = a_in.grp_sel != GRP_ROUTED && a_in.I_shared > 0;
+    for (int i = threadIdx.x; i <= E; i += NT) {
+      float s0 = 0.f, s1 = 0.f, h = 0.f;
+      if (i < E ? routed : shared) {   // pointers of groups outside the launch may be null
+        s0 = i < E ? a_in.sc0[i] : *a_in.ssc0;
+        if (GATE_UP) s1 = i < E ? a_in.sc1[i] : *a_in.ssc1;
+        if (a_in.a8) h = a_in.hs[i];
+      }
+      scl[i] = s0;
+      scl[E + 1 + i] = s1;
+      scl[2 * (E + 1) + i] = h;
+    }
+    if (threadIdx.x == 0) scl[3 * (E + 1)] = a_in.a8 ? *a_in.xs : 0.f;
+  }
+  // XL: every token row of x, 16-byte chunks, after the metadata (16-byte
+  // aligned), XB chunks per thread per round
+  const int meta_n = (n_m + n_sc + 3) & ~3;
   const char *xl = reinterpret_cast<const char *>(meta + meta_n);
   if constexpr (XL) {
-    const int rb = a_in.H * (MXA ? 1 : Elem<T>::kBytes), cpr = rb / 16;
+    const int rb = a_in.H * (CODES ? 1 : Elem<T>::kBytes), cpr = rb / 16;
     const int rs = x_lds_stride(rb);
+    const int n_x = a_in.n_tok * cpr;
     char *dst = reinterpret_cast<char *>(meta + meta_n);
     const char *src_x = static_cast<const char *>(a_in.act);
-    for (int i = threadIdx.x; i < a_in.n_tok * cpr; i += NT) {
-      const int t = i / cpr, c = i - t * cpr;
-      *reinterpret_cast<uint4 *>(dst + t * rs + c * 16) =
-          *reinterpret_cast<const uint4 *>(src_x + (size_t)t * rb + c * 16);
+    constexpr int XB = 8;
+    for (int base = 0; base < n_x; base += NT * XB) {
+      // Past the end a thread copies the last chunk again (the same bytes to
+      // the same place): no branch, so the loads are not sunk into one each.
+      uint4 v[XB];
+      int at[XB];
+#pragma unroll
+      for (int j = 0; j < XB; ++j) {
+        const int i = min(base + j * NT + (int)threadIdx.x, n_x - 1);
+        const int t = i / cpr, c = i - t * cpr;
+        v[j] = *reinterpret_cast<const uint4 *>(src_x + (size_t)t * rb + c * 16);
+        at[j] = t * rs + c * 16;
+      }
+#pragma unroll
+      for (int j = 0; j < XB; ++j) *reinterpret_cast<uint4 *>(dst + at[j]) = v[j];
     }
   }
   __syncthreads();
@@ -300,6 +386,14 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   a.tiles = meta + 2 * tbase;
   a.offsets = meta + n_t;
   a.sorted_token = meta + n_t + n_o;
+  if constexpr (FSC) {
+    a.sc0 = scl;
+    a.sc1 = scl + (a_in.E + 1);
+    a.ssc0 = scl + a_in.E;
+    a.ssc1 = scl + (a_in.E + 1) + a_in.E;
+    a.hs = scl + 2 * (a_in.E + 1);
+    a.xs = scl + 3 * (a_in.E + 1);
+  }
   constexpr int U = steps_per_set<MT, WF>();   // 64-byte K steps per row per register set
   constexpr int XN = token_chunks<WF>();       // 16-byte token chunks per step
   const int lane = threadIdx.x & 63;
@@ -350,7 +444,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
       const uint4 w0_ = *reinterpret_cast<const uint4 *>(src.s0p - (lane >> 4) + s4_ * 4); \
       S0[(u) + 0] = w0_.x >> sh_; S0[(u) + 1] = w0_.y >> sh_;                          \
       S0[(u) + 2] = w0_.z >> sh_; S0[(u) + 3] = w0_.w >> sh_;                          \
-      if (src.nf == 2) {                                                               \
+      {                                                                                \
         const uint4 w1_ = *reinterpret_cast<const uint4 *>(src.s1p - (lane >> 4) + s4_ * 4); \
         S1[(u) + 0] = w1_.x >> sh_; S1[(u) + 1] = w1_.y >> sh_;                        \
         S1[(u) + 2] = w1_.z >> sh_; S1[(u) + 3] = w1_.w >> sh_;                        \
@@ -364,7 +458,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
       _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                  \
         const int sv_ = (st) + v < src.nsub ? (st) + v : src.nsub - 1;                 \
         S0[(u) + v] = src.s0p[sv_ * 4];                                                \
-        if (src.nf == 2) S1[(u) + v] = src.s1p[sv_ * 4];                               \
+        S1[(u) + v] = src.s1p[sv_ * 4];                                                \
         _Pragma("unroll") for (int m = 0; m < MT; ++m) XS[(u) + v][m] = src.xsp[m][sv_ * 4]; \
       }                                                                                \
     }                                                                                  \
@@ -375,10 +469,10 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
       const int st_ = s_ld + u < src.nsub ? s_ld + u : src.nsub - 1;                  \
       const int o_ = st_ * 64;                                                         \
       W0[u] = *reinterpret_cast<const uint4 *>(src.w0p + o_);                          \
-      if (src.nf == 2) W1[u] = *reinterpret_cast<const uint4 *>(src.w1p + o_);         \
+      W1[u] = *reinterpret_cast<const uint4 *>(src.w1p + o_);                          \
       if constexpr (F4 || (MXA && U % 4 != 0)) {                                       \
         S0[u] = src.s0p[st_ * 4];                                                      \
-        if (src.nf == 2) S1[u] = src.s1p[st_ * 4];                                     \
+        S1[u] = src.s1p[st_ * 4];                                                      \
       }                                                                                \
       if constexpr (MXA && U % 4 != 0) {                                               \
         _Pragma("unroll") for (int m = 0; m < MT; ++m) XS[u][m] = src.xsp[m][st_ * 4]; \
@@ -407,7 +501,16 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   {                                                                                    \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       if (s_mm + u < om.nsub) {                                                        \
-        if constexpr (MXA) {                                                           \
+        if constexpr (A8C) {                                                           \
+          /* steps u and u + 1 (nsub and U are even) form one 128-K MFMA */           \
+          if ((u & 1) == 0) {                                                          \
+            _Pragma("unroll") for (int m = 0; m < MT; ++m) {                           \
+              mma_fp8(acc[0][m], W0[u], W0[u + 1], X[u][m][0], X[u + 1][m][0]);       \
+              if (om.nf == 2)                                                          \
+                mma_fp8(acc[1][m], W1[u], W1[u + 1], X[u][m][0], X[u + 1][m][0]);     \
+            }                                                                          \
+          }                                                                            \
+        } else if constexpr (MXA) {                                                    \
           _Pragma("unroll") for (int m = 0; m < MT; ++m) {                             \
             mma_fp4_fp8(acc[0][m], W0[u], S0[u], X[u][m][0], X[u][m][1], XS[u][m]);    \
             if (om.nf == 2)                                                            \
@@ -487,7 +590,7 @@ constexpr size_t STREAM_XL_LDS_MAX = 150 * 1024;   // metadata + x copy of one w
 template <typename T, int MT, int WF>
 size_t x_lds_bytes(const ExpertArgs &a) {
   if (MT != 1) return 0;
-  const int rb = a.H * (WF == WF_W4A8 ? 1 : Elem<T>::kBytes);
+  const int rb = a.H * (token_codes<WF>() ? 1 : Elem<T>::kBytes);
   const size_t meta = (meta_lds_bytes(a, true) + 15) / 16 * 16;
   const size_t x = (size_t)a.n_tok * x_lds_stride(rb);
   return meta + x <= STREAM_XL_LDS_MAX ? x : 0;
@@ -541,6 +644,7 @@ hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipSt
     return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, true, T, stream)
            : a.amx         ? launch_skinny<bf16_t, WF_W4A8>(a, true, T, stream)
            : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, true, T, stream)
+           : a.w_fp8 && a.a8 && a.a8_codes ? launch_skinny<bf16_t, WF_W8A8>(a, true, T, stream)
            : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, true, T, stream)
                            : launch_skinny<bf16_t, WF_DTYPE>(a, true, T, stream);
   if (path == PATH_BIG) return launch_big_gate_up(a, dtype, stream);
@@ -552,6 +656,7 @@ hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStrea
     return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, false, T, stream)
            : a.amx         ? launch_skinny<bf16_t, WF_W4A8>(a, false, T, stream)
            : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, false, T, stream)
+           : a.w_fp8 && a.a8 && a.a8_codes ? launch_skinny<bf16_t, WF_W8A8>(a, false, T, stream)
            : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, false, T, stream)
                            : launch_skinny<bf16_t, WF_DTYPE>(a, false, T, stream);
   if (path == PATH_BIG) return launch_big_down(a, dtype, stream);

@@ -223,13 +223,13 @@ class WorkspaceActivations:
         # MXFP8: codes and block scales in hq / hs on the weight-streaming
         # and large-tile paths; static FP8: codes in h (row r at byte r *
         # ldh, past the earlier rows' 2-byte h when the shared expert has
-        # formats of its own) on the large-tile path.  Elsewhere h holds the
-        # bf16 values of the codes.
+        # formats of its own) where the layout says the token rows are codes
+        # (a8_codes).  Elsewhere h holds the bf16 values of the codes.
         mixed = c.I_shared > 0 and (c.sw_format, c.sa_format) != (c.w_format, c.act_format)
         self.fmt = {}
         for i, (br, act) in enumerate((("routed", c.act_format), ("shared", c.sa_format))):
             a8 = _a8(inp, act)
-            codes = L.gemm_path == 2 if a8 is not None else L.gemm_path != 1
+            codes = bool(L.a8_codes) if a8 is not None else L.gemm_path != 1
             if codes_path is not None:
                 codes = bool(codes_path[i])
             self.fmt[br] = (a8, act == "mxfp8", codes)

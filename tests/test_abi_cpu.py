@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 11
+    assert lib.hy3moe_abi_version() == b.ABI_VERSION == 12
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert sm.strerror(code) and sm.strerror(code) != "unknown error code"
     assert sm.strerror(7) == "unknown error code"
@@ -112,6 +112,10 @@ def test_workspace_layout_is_consistent(lib, name):
     assert L.tile_rows >= min(c.T, 16)
     want = {0: L.tile_rows, 1: 128, 2: 256}[L.gemm_path]
     assert L.tile_rows == want and (L.gemm_path == 0) == (c.T <= 64)
+    # token rows as E4M3 codes: the large-tile path, and the weight-streaming
+    # path when every K of its FP8 MFMAs is a multiple of 128
+    k128 = c.H % 128 == 0 and c.I % 128 == 0 and c.I_shared % 128 == 0
+    assert bool(L.a8_codes) == (L.gemm_path == 2 or (L.gemm_path == 0 and k128))
 
 
 @pytest.mark.parametrize("bad, code", [

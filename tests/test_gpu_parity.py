@@ -136,6 +136,12 @@ SMALL = {
                      w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_T64_noshared": dict(seed=41, T=64, H=512, E=8, K=2, I=256, I_shared=0,
                               dtype="bf16", w_format="fp8_e4m3", act_format="fp8_static"),
+    # weight-streaming W8A8 with two 16-row fragments (FP8 x FP8 MFMAs), and
+    # with a K that is not a multiple of 128 (bf16 values of the codes)
+    "w8a8_T32_codes": dict(seed=43, T=32, H=384, E=12, K=4, I=256, I_shared=128, dtype="bf16",
+                           w_format="fp8_e4m3", act_format="fp8_static"),
+    "w8a8_T16_values": dict(seed=44, T=16, H=320, E=10, K=4, I=192, I_shared=64, dtype="bf16",
+                            w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_tiled_T300": dict(seed=42, T=300, H=512, E=24, K=4, I=256, I_shared=128,
                             dtype="bf16", w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_big_T513_H384": dict(seed=43, T=513, H=384, E=4, K=2, I=256, I_shared=128,

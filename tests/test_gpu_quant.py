@@ -80,8 +80,10 @@ def test_w8a8_codes_in_the_workspace(dev, T, E, H, path_rows):
     bf16 tensor, with a correctly rounded division by a2 on both sides, and
     the GPU's float32 h lies within an accumulation error bound dh of the
     float64 h: its code must lie between the codes of h - dh and h + dh
-    (both steps are monotone), and equal the oracle's where those agree.  Large-tile path:
-    E4M3 bytes; the other paths: their bf16 values."""
+    (both steps are monotone), and equal the oracle's where those agree.  Where the
+    layout reports code rows (a8_codes: the large-tile path, and the
+    weight-streaming path when H, I and I_shared are multiples of 128): E4M3
+    bytes; otherwise their bf16 values."""
     from gpu_util import a8_of, config_of, expert_cache, shared_f64, to_torch, upload_weights
     from synth import random_small
     inp = random_small(50 + T, T=T, H=H, E=E, K=4, I=256, I_shared=128, dtype="bf16",
@@ -91,7 +93,7 @@ def test_w8a8_codes_in_the_workspace(dev, T, E, H, path_rows):
     L = sm.hy3moe_workspace_layout(cfg)
     if path_rows is not None:
         assert L.tile_rows == path_rows
-    codes_path = L.gemm_path == 2
+    codes_path = bool(L.a8_codes)
     ws = sm.alloc_workspace(cfg, True, dev)
     weights = upload_weights(inp, dev)
     x = to_torch(inp.x(), c.dtype, dev)
