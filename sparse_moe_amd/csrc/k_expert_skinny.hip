@@ -54,6 +54,8 @@
 // activation scale multiplies the accumulators.  Half the token bytes of the
 // bf16 values, a quarter of the MFMAs, no decode.  The gate-up epilogue
 // stores h as E4M3 codes for the down GEMM.
+#include <type_traits>
+
 #include "common.cuh"
 #include "internal.h"
 
@@ -67,10 +69,12 @@ constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
 // 64-byte steps per register set: bf16 weights UBASE / MT; FP8 weights 6 / 3
 // / 1 for 1 / 2 / 4 row fragments (each step also holds two token chunks);
 // W8A8 8 / 4 / 2 (one chunk of codes per step; even, as two steps make one
-// MFMA); MXFP4 3 / 2 / 1 (four token chunks per step).
-template <int MT, int WF>
+// MFMA); MXFP4 3 / 2 / 1 (four token chunks per step).  With the four-row
+// weight loads (TR, one fragment) a multiple of four: FP8 takes 4.
+template <int MT, int WF, bool TR = false>
 constexpr int steps_per_set() {
-  return WF == WF_W8A8    ? (MT == 1 ? 8 : (MT == 2 ? 4 : 2))   // even: pairs of steps
+  return TR && WF == WF_FP8 ? 4
+         : WF == WF_W8A8  ? (MT == 1 ? 8 : (MT == 2 ? 4 : 2))   // even: pairs of steps
          : WF == WF_FP8   ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1))
          : WF == WF_MXFP4 ? (MT == 1 ? 3 : (MT == 2 ? 2 : 1))
          : WF == WF_W4A8  ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
@@ -96,6 +100,7 @@ struct UnitSrc {
   bool vs;                   // W4A8: scale rows allow 16-byte loads of 4 steps
   int nsub;                // 64-byte K steps per row
   int nf;                  // fragments streamed (2; 1 for half of a down unit)
+  int rowb;                // TR: bytes per weight row (the stride of the four-row loads)
 };
 struct UnitOut {
   int row0, grp_end, col0, nsub, nf;
@@ -112,10 +117,50 @@ struct UnitOut {
 // gathered rows of a wavefront read over the banks.
 __host__ __device__ constexpr int x_lds_stride(int row_bytes) { return row_bytes + 16; }
 
+// TR (one 16-row fragment, every K row a multiple of 256 bytes): a weight
+// load covers four rows x 256 contiguous bytes instead of sixteen rows x 64
+// bytes, with a non-temporal hint; a streaming read in that form ran ~10 %
+// faster than the MFMA-shaped one at the rows of 1.5-4 KB of these GEMMs.
+// Load j of a group of four 64-byte steps holds row 4 j + l / 16, bytes
+// [16 (l % 16), +16) of the group's 256; the wavefront's 4 KB LDS buffer
+// turns the group into the MFMA layout (step s: row l % 16, bytes [64 s +
+// 16 (l / 16), +16)).  Chunk c of row r sits in slot 16 r + (c ^ r), so that
+// neither pass has bank conflicts.  LDS operations of one wavefront complete
+// in order; the wavefront-scope fences keep the compiler from reordering
+// them across the passes.
+constexpr int TR_WAVE_BYTES = 4096;
+
+__device__ __forceinline__ uint4 load_nt16(const char *p) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int U>
+__device__ __forceinline__ void transpose_groups(uint4 (&W)[U], uint4 *lb, int lane) {
+  static_assert(U % 4 == 0, "groups of four steps");
+#pragma unroll
+  for (int q = 0; q < U / 4; ++q) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + (lane >> 4), c = lane & 15;
+      lb[16 * r + (c ^ r)] = W[4 * q + j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int r = lane & 15, c = 4 * st + (lane >> 4);
+      W[4 * q + st] = lb[16 * r + (c ^ r)];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // Unit u (tile u / n_col_blocks, column block u % n_col_blocks) of this
 // kernel; returns false if the column block lies past the group's width.
 // half = 1 or 2: only the first or the second 16-row fragment of a down unit.
-template <typename T, bool GATE_UP, int MT, int WF, bool XL>
+template <typename T, bool GATE_UP, int MT, int WF, bool XL, bool TR>
 __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_blocks, int lane,
                                         UnitSrc<MT> &src, UnitOut &o, int half = 0) {
   constexpr bool F8 = WF == WF_FP8 || WF == WF_W8A8, F4 = WF == WF_MXFP4 || WF == WF_W4A8;
@@ -143,8 +188,11 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
                               : static_cast<const char *>(a.w0) + (size_t)g * a.I * rowb(a.H);
     const char *up = shared ? static_cast<const char *>(a.ws1)
                             : static_cast<const char *>(a.w1) + (size_t)g * a.I * rowb(a.H);
-    src.w0p = gate + (size_t)(o.col0 + r16) * rowb(a.H) + cg * 16;
-    src.w1p = up + (size_t)(o.col0 + r16) * rowb(a.H) + cg * 16;
+    // TR: lane (l / 16) of a four-row load, bytes [16 (l % 16), +16) of its 256
+    const int lr = TR ? (lane >> 4) : r16, lc = TR ? (lane & 15) : cg;
+    src.w0p = gate + (size_t)(o.col0 + lr) * rowb(a.H) + lc * 16;
+    src.w1p = up + (size_t)(o.col0 + lr) * rowb(a.H) + lc * 16;
+    src.rowb = rowb(a.H);
     if (F4) {   // scale rows of H / 32 bytes; the lane's block is step * 4 + cg
       const int sr = a.H / 32;
       const uint8_t *sg = shared ? a.mxs0 : a.mx0 + (size_t)g * a.I * sr;
@@ -157,8 +205,14 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
                             : static_cast<const char *>(a.w0) + (size_t)g * a.H * rowb(a.I);
     const int n0 = (o.col0 + r16 < a.H) ? o.col0 + r16 : o.col0;
     const int n1 = (o.col0 + 16 + r16 < a.H) ? o.col0 + 16 + r16 : o.col0;
-    src.w0p = dn + (size_t)n0 * rowb(Ig) + cg * 16;
-    src.w1p = dn + (size_t)n1 * rowb(Ig) + cg * 16;
+    if (TR) {   // H % 64 == 0: the fragments' rows all exist
+      src.w0p = dn + (size_t)(o.col0 + (lane >> 4)) * rowb(Ig) + (lane & 15) * 16;
+      src.w1p = src.w0p + (size_t)16 * rowb(Ig);
+    } else {
+      src.w0p = dn + (size_t)n0 * rowb(Ig) + cg * 16;
+      src.w1p = dn + (size_t)n1 * rowb(Ig) + cg * 16;
+    }
+    src.rowb = rowb(Ig);
     if (F4) {
       const int sr = Ig / 32;
       const uint8_t *sd = shared ? a.mxs0 : a.mx0 + (size_t)g * a.H * (a.I / 32);
@@ -213,7 +267,7 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
 // of them is split into its two 16-row fragments for twice as many
 // wavefronts, so the last round costs half a unit.  Returns the item index
 // (kmax when there is none) and fills src / o.
-template <typename T, bool GATE_UP, int MT, int WF, bool XL>
+template <typename T, bool GATE_UP, int MT, int WF, bool XL, bool TR>
 __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int nw, int n_units,
                                          int n_col_blocks, int lane, UnitSrc<MT> &src,
                                          UnitOut &o) {
@@ -224,10 +278,10 @@ __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int 
     if (k < full || !split) {
       const int u = w + k * nw;
       if (u >= n_units) return kmax;
-      if (unit_of<T, GATE_UP, MT, WF, XL>(a, u, n_col_blocks, lane, src, o)) return k;
+      if (unit_of<T, GATE_UP, MT, WF, XL, TR>(a, u, n_col_blocks, lane, src, o)) return k;
     } else {
       if (w >= 2 * tail) return kmax;
-      if (unit_of<T, GATE_UP, MT, WF, XL>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
+      if (unit_of<T, GATE_UP, MT, WF, XL, TR>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
                                       1 + (w & 1)))
         return k;
     }
@@ -293,7 +347,7 @@ template <bool XL> constexpr int stream_threads() { return XL ? 512 : 256; }
 // BRANCH names the instantiation only: 0 for the routed experts (or every
 // group), 1 for the shared expert's own launches, which profiles then list
 // apart.
-template <typename T, bool GATE_UP, int MT, int WF, bool XL, int BRANCH>
+template <typename T, bool GATE_UP, int MT, int WF, bool XL, bool TR, int BRANCH>
 __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_stream_kernel(
     ExpertArgs a_in, int n_col_blocks) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4, MXA = WF == WF_W4A8;
@@ -379,6 +433,11 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
       for (int j = 0; j < XB; ++j) *reinterpret_cast<uint4 *>(dst + at[j]) = v[j];
     }
   }
+  // TR: each wavefront's 4 KB transposition buffer after the x copy
+  const int x_bytes = XL ? a_in.n_tok * x_lds_stride(a_in.H * (CODES ? 1 : Elem<T>::kBytes)) : 0;
+  uint4 *lb = reinterpret_cast<uint4 *>(reinterpret_cast<char *>(meta + meta_n) + x_bytes +
+                                        (threadIdx.x >> 6) * TR_WAVE_BYTES);
+  (void)lb;
   __syncthreads();
   ExpertArgs a = a_in;
   int tbase, n_tiles;   // this launch's slice of the tile list (grp_sel)
@@ -394,7 +453,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
     a.hs = scl + 2 * (a_in.E + 1);
     a.xs = scl + 3 * (a_in.E + 1);
   }
-  constexpr int U = steps_per_set<MT, WF>();   // 64-byte K steps per row per register set
+  constexpr int U = steps_per_set<MT, WF, TR>();   // 64-byte K steps per row per register set
   constexpr int XN = token_chunks<WF>();       // 16-byte token chunks per step
   const int lane = threadIdx.x & 63;
   // The wavefront index is uniform; readfirstlane makes that visible to the
@@ -409,7 +468,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   // units of one expert spread over all XCDs and HBM channels.
   UnitSrc<MT> src;    // item whose blocks are being loaded
   UnitOut om, ol;     // item being multiplied, item being loaded
-  int k_ld = next_item<T, GATE_UP, MT, WF, XL>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
+  int k_ld = next_item<T, GATE_UP, MT, WF, XL, TR>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
   if (k_ld >= kmax) return;
   int k_mm = k_ld;
   om = ol;
@@ -467,9 +526,16 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   {                                                                                    \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       const int st_ = s_ld + u < src.nsub ? s_ld + u : src.nsub - 1;                  \
-      const int o_ = st_ * 64;                                                         \
-      W0[u] = *reinterpret_cast<const uint4 *>(src.w0p + o_);                          \
-      W1[u] = *reinterpret_cast<const uint4 *>(src.w1p + o_);                          \
+      if constexpr (TR) {   /* load j of the group at step 4 q: rows 4 j .. 4 j + 3 */ \
+        const int g_ = s_ld + (u & ~3) < src.nsub ? s_ld + (u & ~3) : src.nsub - 4;     \
+        const size_t o_ = (size_t)g_ * 64 + (size_t)(4 * (u & 3)) * src.rowb;           \
+        W0[u] = load_nt16(src.w0p + o_);                                               \
+        W1[u] = load_nt16(src.w1p + o_);                                               \
+      } else {                                                                         \
+        const int o_ = st_ * 64;                                                       \
+        W0[u] = *reinterpret_cast<const uint4 *>(src.w0p + o_);                        \
+        W1[u] = *reinterpret_cast<const uint4 *>(src.w1p + o_);                        \
+      }                                                                                \
       if constexpr (F4 || (MXA && U % 4 != 0)) {                                       \
         S0[u] = src.s0p[st_ * 4];                                                      \
         S1[u] = src.s1p[st_ * 4];                                                      \
@@ -490,7 +556,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
     }                                                                                  \
     s_ld += U;                                                                         \
     if (s_ld >= src.nsub) {                                                            \
-      k_ld = next_item<T, GATE_UP, MT, WF, XL>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
+      k_ld = next_item<T, GATE_UP, MT, WF, XL, TR>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src, ol);                             \
       s_ld = 0;                                                                        \
     }                                                                                  \
@@ -499,6 +565,10 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   // and move on.  `more` turns false after the last unit.
 #define HY3_MMA(W0, W1, X, S0, S1, XS)                                                 \
   {                                                                                    \
+    if constexpr (TR) {                                                                \
+      transpose_groups<U>(W0, lb, lane);                                               \
+      transpose_groups<U>(W1, lb, lane);                                               \
+    }                                                                                  \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       if (s_mm + u < om.nsub) {                                                        \
         if constexpr (A8C) {                                                           \
@@ -558,7 +628,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
       unit_epilogue<T, GATE_UP, MT, WF>(a, om, acc, lane);                             \
       _Pragma("unroll") for (int f = 0; f < 2; ++f)                                    \
         _Pragma("unroll") for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; \
-      k_mm = next_item<T, GATE_UP, MT, WF, XL>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
+      k_mm = next_item<T, GATE_UP, MT, WF, XL, TR>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src_dummy, om);                       \
       s_mm = 0;                                                                        \
       more = k_mm < kmax;                                                              \
@@ -596,25 +666,64 @@ size_t x_lds_bytes(const ExpertArgs &a) {
   return meta + x <= STREAM_XL_LDS_MAX ? x : 0;
 }
 
-template <typename T, int MT, int WF, int BRANCH>
-hipError_t launch_skinny_b(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+// Bytes per weight row of K elements.
+template <typename T, int WF>
+constexpr int weight_row_bytes(int K) {
+  return (WF == WF_MXFP4 || WF == WF_W4A8) ? K / 2
+         : (WF == WF_FP8 || WF == WF_W8A8) ? K
+                                           : K * Elem<T>::kBytes;
+}
+
+// Formats with a TR instantiation (one fragment, steps per set a multiple
+// of four); the launch takes it when every weight row of the launch is a
+// multiple of 256 bytes.
+template <typename T, int MT, int WF>
+constexpr bool tr_format() {
+  return MT == 1 && steps_per_set<MT, WF, true>() % 4 == 0 && !std::is_same<T, float>::value;
+  // (MXFP4 weights with bf16 tokens: three steps per set, as four spill)
+}
+template <typename T, int WF>
+bool tr_rows(const ExpertArgs &a, bool gate_up) {
+  auto ok = [](int K) { return weight_row_bytes<T, WF>(K) % 256 == 0; };
+  if (gate_up) return ok(a.H);
+  return (a.grp_sel == GRP_SHARED || ok(a.I)) &&
+         (a.grp_sel == GRP_ROUTED || a.I_shared == 0 || ok(a.I_shared));
+}
+
+template <typename T, int MT, int WF, bool TR, int BRANCH>
+hipError_t launch_skinny_tr(const ExpertArgs &a, bool gate_up, size_t xb, hipStream_t stream) {
+  const size_t meta = (meta_lds_bytes(a, gate_up) + 15) / 16 * 16;
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int ncb = (Imax + 15) / 16;
-    const size_t xb = x_lds_bytes<T, MT, WF>(a);
     if (xb)   // one 512-thread workgroup per CU, x in LDS
-      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, true, BRANCH>), dim3(STREAM_BLOCKS / 2),
-                         dim3(512), (meta_lds_bytes(a, true) + 15) / 16 * 16 + xb, stream, a,
-                         ncb);
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, true, TR, BRANCH>),
+                         dim3(STREAM_BLOCKS / 2), dim3(512),
+                         meta + xb + (TR ? 8 * TR_WAVE_BYTES : 0), stream, a, ncb);
     else
-      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, false, BRANCH>), dim3(STREAM_BLOCKS),
-                         dim3(256), meta_lds_bytes(a, true), stream, a, ncb);
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, false, TR, BRANCH>),
+                         dim3(STREAM_BLOCKS), dim3(256), meta + (TR ? 4 * TR_WAVE_BYTES : 0),
+                         stream, a, ncb);
   } else {
     const int ncb = (a.H + 31) / 32;
-    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF, false, BRANCH>), dim3(STREAM_BLOCKS),
-                       dim3(256), meta_lds_bytes(a, false), stream, a, ncb);
+    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF, false, TR, BRANCH>),
+                       dim3(STREAM_BLOCKS), dim3(256), meta + (TR ? 4 * TR_WAVE_BYTES : 0),
+                       stream, a, ncb);
   }
   return hipGetLastError();
+}
+
+template <typename T, int MT, int WF, int BRANCH>
+hipError_t launch_skinny_b(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+  const size_t xb = gate_up ? x_lds_bytes<T, MT, WF>(a) : 0;
+  if constexpr (tr_format<T, MT, WF>()) {
+    // TR unless the x copy leaves no room for the 8 wavefronts' buffers
+    const size_t meta = (meta_lds_bytes(a, gate_up) + 15) / 16 * 16;
+    const bool room = !xb || meta + xb + 8 * TR_WAVE_BYTES <= STREAM_XL_LDS_MAX;
+    if (room && tr_rows<T, WF>(a, gate_up))
+      return launch_skinny_tr<T, MT, WF, true, BRANCH>(a, gate_up, xb, stream);
+  }
+  return launch_skinny_tr<T, MT, WF, false, BRANCH>(a, gate_up, xb, stream);
 }
 
 template <typename T, int MT, int WF>

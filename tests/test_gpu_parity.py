@@ -142,6 +142,10 @@ SMALL = {
                            w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_T16_values": dict(seed=44, T=16, H=320, E=10, K=4, I=192, I_shared=64, dtype="bf16",
                             w_format="fp8_e4m3", act_format="fp8_static"),
+    # one fragment with every weight row a multiple of 256 bytes: the
+    # four-row weight loads (W8A8, W4A8 and bf16)
+    "w8a8_T8_rows256": dict(seed=45, T=8, H=512, E=8, K=2, I=256, I_shared=256, dtype="bf16",
+                            w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_tiled_T300": dict(seed=42, T=300, H=512, E=24, K=4, I=256, I_shared=128,
                             dtype="bf16", w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_big_T513_H384": dict(seed=43, T=513, H=384, E=4, K=2, I=256, I_shared=128,
@@ -183,6 +187,8 @@ SMALL = {
                     w_format="mxfp4", act_format="mxfp8"),
     "w4a8_T16": dict(seed=81, T=16, H=512, E=32, K=4, I=256, I_shared=128, dtype="bf16",
                      w_format="mxfp4", act_format="mxfp8"),
+    "w4a8_T12_rows256": dict(seed=84, T=12, H=512, E=8, K=3, I=512, I_shared=512, dtype="bf16",
+                             w_format="mxfp4", act_format="mxfp8"),
     "w4a8_T20_noshared": dict(seed=82, T=20, H=256, E=8, K=2, I=128, I_shared=0,
                               dtype="bf16", w_format="mxfp4", act_format="mxfp8"),
     "w4a8_T64_softmax": dict(seed=83, T=64, H=384, E=16, K=4, I=128, I_shared=256,
