@@ -530,8 +530,9 @@ def router_sweep(args, dev):
 def ceilings(dev):
     """Achievable ceilings on this GPU: dense bf16 and FP8 MFMA microkernels
     (register operands only, 16 independent chains per wavefront), a 16-byte-per-lane
-    device copy of 4 GiB (read + write bytes counted) and a streaming read of
-    the same 4 GiB."""
+    device copy of 4 GiB (read + write bytes counted), a streaming read of
+    the same 4 GiB, and the weight-streaming GEMMs' reads with the MFMAs
+    removed."""
     import ctypes
 
     import torch
@@ -617,6 +618,29 @@ def ceilings(dev):
             res[f"read_seg_GBs_{blocks}blk_d{depth}"] = gbs
             best = max(best, gbs)
     res["read_GBs_best"] = best
+    # the weight-streaming GEMMs' reads with the MFMAs removed, at the weight
+    # row lengths of the Hy3 decode GEMMs (bf16 gate-up 8 KB, FP8 gate-up
+    # 4 KB, bf16 down 3 KB, FP8 down 1.5 KB): 16 rows x 64 B per load (the
+    # MFMA operand layout) and 4 rows x 256 B with the non-temporal hint (the
+    # four-row loads the kernels transpose through LDS)
+    L.hy3moe_probe_read_fragments.argtypes = [
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+    blocks = 512
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    for rowbytes in (8192, 4096, 3072, 1536):
+        for rows, nt, tag in ((16, 0, "rows16"), (4, 1, "rows4_nt")):
+            rb = ctypes.c_size_t(0)
+            args = (src.data_ptr(), n, rowbytes, rows, nt, blocks, out.data_ptr(),
+                    ctypes.byref(rb), s)
+            assert L.hy3moe_probe_read_fragments(*args) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                L.hy3moe_probe_read_fragments(*args)
+            e1.record()
+            torch.cuda.synchronize()
+            res[f"read_frag_GBs_{rowbytes}B_{tag}"] = rb.value * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
     res["mfma_bf16_tflops_best"] = max(v for k, v in res.items() if k.startswith("mfma_bf16"))
     res["mfma_fp8_tflops_best"] = max(v for k, v in res.items() if k.startswith("mfma_fp8"))
     res["peak_published"] = {"bf16_tflops": PEAK_BF16_TFLOPS, "fp8_tflops": PEAK_FP8_TFLOPS,

@@ -2,7 +2,8 @@
 // of the MoE layer): dense bf16 and FP8 MFMA microkernels with register
 // operands only, a 16-byte-per-lane device copy, 16-byte-per-lane streaming
 // reads (grid-strided, and in contiguous per-workgroup segments with 8 or 16
-// loads in flight per lane: the bound of the weight-streaming GEMMs), and one FP8 MFMA per
+// loads in flight per lane), the weight-streaming GEMMs' fragment reads with
+// the MFMAs removed (16 rows x 64 B or 4 rows x 256 B per load), and one FP8 MFMA per
 // wavefront on given operands (its accumulation error, measured against
 // exact sums by the caller).  Built into libhy3moe_probe.so.
 #include <hip/hip_runtime.h>
@@ -87,6 +88,71 @@ __global__ __launch_bounds__(256) void read_segment_kernel(const uint4 *__restri
   for (; i < end; i += 256) acc ^= src[i].y;
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
+// The weight-streaming GEMMs' read with the MFMAs removed: a unit is two
+// fragments of 16 rows x rowbytes (the second half a buffer away, like the
+// gate and up matrices), units striped over the wavefronts, each fragment
+// read in sets of 8 loads (16 rows x 512 B) with two sets in flight.  A load
+// covers R rows x 1024 / R contiguous bytes: R = 16 is the MFMA operand
+// layout (64 B per row per load), R = 4 the four-row loads that the kernels
+// transpose through LDS; NT adds the non-temporal hint.  One word per thread
+// is written so that the loads stay.
+template <int R, bool NT>
+__global__ __launch_bounds__(256, 2) void read_fragments_kernel(const char *__restrict__ w,
+                                                                size_t half, int rowbytes,
+                                                                int n_units,
+                                                                uint32_t *__restrict__ out) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+  constexpr int U = 8, LPR = 64 / R, W = 1024 / R, NRG = 16 / R;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = gridDim.x * 4, wid = blockIdx.x * 4 + wave;
+  const int spu = rowbytes / 512;   // sets per unit
+  const int my_units = wid < n_units ? (n_units - wid + nw - 1) / nw : 0;
+  const int total_sets = my_units * spu;
+  uint32_t acc = 0;
+  // set -> (unit, 512-byte column), load j -> (row group, column group);
+  // every address lies inside its unit's 16 x rowbytes fragment
+  auto addr = [&](int set, int j) -> const u32x4_t * {
+    const int k = set / spu, sc = set - k * spu;
+    const size_t f = (size_t)(wid + k * nw) * 16 * rowbytes;
+    const int row = (j % NRG) * R + lane / LPR;
+    const size_t byte = (size_t)sc * 512 + (j / NRG) * W + (lane % LPR) * 16;
+    return reinterpret_cast<const u32x4_t *>(w + f + (size_t)row * rowbytes + byte);
+  };
+  auto ld = [&](const u32x4_t *p) { return NT ? __builtin_nontemporal_load(p) : *p; };
+  auto second = [&](const u32x4_t *p) {
+    return reinterpret_cast<const u32x4_t *>(reinterpret_cast<const char *>(p) + half);
+  };
+  u32x4_t a0[U], a1[U], b0[U], b1[U];
+  if (total_sets > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) { a0[u] = ld(addr(0, u)); a1[u] = ld(second(addr(0, u))); }
+  }
+  for (int set = 0; set < total_sets; set += 2) {
+    if (set + 1 < total_sets) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        b0[u] = ld(addr(set + 1, u));
+        b1[u] = ld(second(addr(set + 1, u)));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      acc ^= a0[u][0] ^ a0[u][1] ^ a0[u][2] ^ a0[u][3] ^ a1[u][0] ^ a1[u][1] ^ a1[u][2] ^ a1[u][3];
+    if (set + 1 >= total_sets) break;
+    if (set + 2 < total_sets) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a0[u] = ld(addr(set + 2, u));
+        a1[u] = ld(second(addr(set + 2, u)));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      acc ^= b0[u][0] ^ b0[u][1] ^ b0[u][2] ^ b0[u][3] ^ b1[u][0] ^ b1[u][1] ^ b1[u][2] ^ b1[u][3];
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 // The same with 16x16x128 E4M3 x E4M3 MFMAs (one per chain per iteration).
 __global__ __launch_bounds__(256) void mfma_fp8_peak_kernel(int iters, float *out) {
   const int lane = threadIdx.x & 63;
@@ -195,6 +261,36 @@ int hy3moe_probe_read(const void *src, size_t bytes, int n_blocks, void *out, vo
   if (!src || !out || (bytes & 15) || n_blocks <= 0) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(read_kernel, dim3(n_blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4 *>(src), bytes / 16, static_cast<uint32_t *>(out));
+  return (int)hipGetLastError();
+}
+
+// Reads the units of 2 x 16 rows x rowbytes that fit in `bytes` in the
+// weight-streaming GEMMs' pattern (read_fragments_kernel): rows_per_load 16
+// or 4, nontemporal 0 or 1, rowbytes a positive multiple of 512; returns
+// the bytes read through *read_bytes.  out holds n_blocks x 256 words.
+int hy3moe_probe_read_fragments(const void *src, size_t bytes, int rowbytes, int rows_per_load,
+                                int nontemporal, int n_blocks, void *out, size_t *read_bytes,
+                                void *stream) {
+  if (!src || !out || !read_bytes || n_blocks <= 0 || rowbytes <= 0 || rowbytes % 512 ||
+      (rows_per_load != 16 && rows_per_load != 4))
+    return (int)hipErrorInvalidValue;
+  const size_t half = bytes / 2;
+  const size_t units = half / ((size_t)16 * rowbytes);
+  if (units == 0 || units > (size_t)1 << 30) return (int)hipErrorInvalidValue;
+  *read_bytes = 2 * units * 16 * (size_t)rowbytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char *w = static_cast<const char *>(src);
+  uint32_t *o = static_cast<uint32_t *>(out);
+  const int n = (int)units;
+#define HY3_RF(R_, NT_)                                                                \
+  hipLaunchKernelGGL((read_fragments_kernel<R_, NT_>), dim3(n_blocks), dim3(256), 0, s, w, half, \
+                     rowbytes, n, o)
+  if (rows_per_load == 16) {
+    if (nontemporal) HY3_RF(16, true); else HY3_RF(16, false);
+  } else {
+    if (nontemporal) HY3_RF(4, true); else HY3_RF(4, false);
+  }
+#undef HY3_RF
   return (int)hipGetLastError();
 }
 
