@@ -53,15 +53,17 @@ def log(msg):
 
 
 ATTN_SOURCES = ("k_attention.hip",)   # the split-KV attention path; the rest is the MoE layer's
+PROBE_SOURCES = ("ceiling_probe.hip",)  # measurement probes: part of neither path
 
 
 def kernel_sources_sha(kind: str = "moe"):
     """Hash of the kernel sources a measurement depends on: the MoE layer's
-    (every source but the attention path's) or the attention path's."""
+    (every source but the attention path's and the ceiling probes') or the
+    attention path's."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_moe_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if (name in ATTN_SOURCES) != (kind == "attn"):
+        if name in PROBE_SOURCES or (name in ATTN_SOURCES) != (kind == "attn"):
             continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
