@@ -117,10 +117,11 @@ struct UnitOut {
 // gathered rows of a wavefront read over the banks.
 __host__ __device__ constexpr int x_lds_stride(int row_bytes) { return row_bytes + 16; }
 
-// TR (one 16-row fragment, every K row a multiple of 256 bytes): a weight
-// load covers four rows x 256 contiguous bytes instead of sixteen rows x 64
-// bytes, with a non-temporal hint; a streaming read in that form ran ~10 %
-// faster than the MFMA-shaped one at the rows of 1.5-4 KB of these GEMMs.
+// TR (one 16-row fragment, or two for bf16 and W8A8; every K row a multiple
+// of 256 bytes): a weight load covers four rows x 256 contiguous bytes
+// instead of sixteen rows x 64 bytes, with a non-temporal hint; a streaming
+// read in that form ran ~10 % faster than the MFMA-shaped one at the rows of
+// 1.5-4 KB of these GEMMs.
 // Load j of a group of four 64-byte steps holds row 4 j + l / 16, bytes
 // [16 (l % 16), +16) of the group's 256; the wavefront's 4 KB LDS buffer
 // turns the group into the MFMA layout (step s: row l % 16, bytes [64 s +
@@ -371,11 +372,11 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
       const int i = min(base + j * NT + (int)threadIdx.x, n_m - 1);
-      // word i of the concatenation: select the array's (shifted) base, then index
-      const int32_t *p = i < n_t ? a_in.tiles
-                         : i < n_t + n_o ? a_in.offsets - n_t
-                                         : a_in.sorted_token - (n_t + n_o);
-      v[j] = p[i];
+      // word i of the concatenation: select the array and its first word
+      const bool in_t = i < n_t, in_o = i < n_t + n_o;
+      const int32_t *arr = in_t ? a_in.tiles : (in_o ? a_in.offsets : a_in.sorted_token);
+      const int first = in_t ? 0 : (in_o ? n_t : n_t + n_o);
+      v[j] = arr[i - first];
       at[j] = i;
     }
 #pragma unroll
@@ -674,13 +675,16 @@ constexpr int weight_row_bytes(int K) {
                                            : K * Elem<T>::kBytes;
 }
 
-// Formats with a TR instantiation (one fragment, steps per set a multiple
-// of four); the launch takes it when every weight row of the launch is a
-// multiple of 256 bytes.
+// Formats with a TR instantiation (steps per set a multiple of four); the
+// launch takes it when every weight row of the launch is a multiple of 256
+// bytes.
 template <typename T, int MT, int WF>
 constexpr bool tr_format() {
-  return MT == 1 && steps_per_set<MT, WF, true>() % 4 == 0 && !std::is_same<T, float>::value;
-  // (MXFP4 weights with bf16 tokens: three steps per set, as four spill)
+  // One fragment: every format but MXFP4 weights with bf16 tokens (three
+  // steps per set, as four spill); two fragments: bf16 and W8A8 (four steps
+  // per set already; the others spill at four).
+  return !std::is_same<T, float>::value && steps_per_set<MT, WF, true>() % 4 == 0 &&
+         (MT == 1 ? WF != WF_MXFP4 : (MT == 2 && (WF == WF_DTYPE || WF == WF_W8A8)));
 }
 template <typename T, int WF>
 bool tr_rows(const ExpertArgs &a, bool gate_up) {

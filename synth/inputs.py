@@ -206,6 +206,15 @@ CONFIGS: Dict[str, MoEConfig] = {
                   I=1536, I_shared=1536, dtype="bf16",
                   route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                   bias_kind="skew", w_format="mxfp4", act_format="mxfp8"),
+    # Hy3 decode with 32 tokens (two 16-row token fragments per unit), on the
+    # bf16 and on the FP8 weights, the latter with static FP8 activations.
+    "hy3_decode_T32": MoEConfig("hy3_decode_T32", 15, 1, T=32, H=4096, E=192, K=8, I=1536,
+                 I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                 scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform"),
+    "hy3_decode_T32_w8a8": MoEConfig("hy3_decode_T32_w8a8", 16, 5, T=32, H=4096, E=192, K=8,
+                 I=1536, I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                 scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform",
+                 w_format="fp8_e4m3", act_format="fp8_static"),
     # Mixed precision in one layer: the routed experts at W4A8 (the MXFP4
     # experts above, MXFP8 activations) and the shared expert at W8A8 (FP8
     # E4M3 weights, static FP8 activations).

@@ -93,6 +93,13 @@ def test_hy3_prefill_T8192_skew_full(dev, hy3_weights):
     layer_check(MoEInputs(CONFIGS["hy3_prefill_T8192_skew"]), dev, hy3_weights)
 
 
+def test_hy3_decode_T32_full(dev, hy3_weights):
+    """32 tokens on the Hy3 weights: two 16-row token fragments per work unit
+    (the four-row weight loads at two fragments), every token, the stated
+    bf16 bound (the decode workload's shapes and dtypes at another T)."""
+    decode_full_check(MoEInputs(CONFIGS["hy3_decode_T32"]), dev, hy3_weights)
+
+
 @pytest.mark.parametrize("M", ROUTER_SWEEP_M)
 def test_router_sweep(dev, hy3_weights, M):
     """Logits of both router arithmetics against the float64 oracle, per token row:
@@ -167,6 +174,13 @@ def test_hy3_decode_T16_w8a8_full(dev, hy3_fp8_weights):
     are valid and the check continues with the GPU's (WorkspaceActivations);
     derived output bound."""
     inp = MoEInputs(CONFIGS["hy3_decode_T16_w8a8"])
+    decode_full_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev),
+                      workload_shape=False)
+
+
+def test_hy3_decode_T32_w8a8_full(dev, hy3_fp8_weights):
+    """W8A8 decode with 32 tokens (FP8 MFMAs at two token fragments)."""
+    inp = MoEInputs(CONFIGS["hy3_decode_T32_w8a8"])
     decode_full_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev),
                       workload_shape=False)
 

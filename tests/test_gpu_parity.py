@@ -78,6 +78,8 @@ def full_check(inp, dev, **kw):
 
 SMALL = {
     "skinny_T1": dict(seed=1, T=1, H=512, E=32, K=8, I=256, I_shared=256, dtype="bf16"),
+    "skinny_T32_rows256": dict(seed=7, T=32, H=256, E=12, K=4, I=128, I_shared=128,
+                               dtype="bf16"),
     "skinny_T16": dict(seed=2, T=16, H=512, E=32, K=8, I=256, I_shared=256, dtype="bf16"),
     "skinny_T20": dict(seed=3, T=20, H=512, E=24, K=6, I=192, I_shared=128, dtype="bf16"),
     "skinny_T40": dict(seed=4, T=40, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16"),
@@ -146,6 +148,8 @@ SMALL = {
     # four-row weight loads (W8A8, W4A8 and bf16)
     "w8a8_T8_rows256": dict(seed=45, T=8, H=512, E=8, K=2, I=256, I_shared=256, dtype="bf16",
                             w_format="fp8_e4m3", act_format="fp8_static"),
+    "w8a8_T24_rows256": dict(seed=46, T=24, H=512, E=8, K=2, I=256, I_shared=256, dtype="bf16",
+                             w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_tiled_T300": dict(seed=42, T=300, H=512, E=24, K=4, I=256, I_shared=128,
                             dtype="bf16", w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_big_T513_H384": dict(seed=43, T=513, H=384, E=4, K=2, I=256, I_shared=128,
