@@ -19,8 +19,12 @@ namespace hy3moe {
 namespace {
 
 // One 16-byte load of a y row: 8 fp16 values (bf16 layers) or 4 float32.
+// The fp16 rows are read once, with the non-temporal hint (Hy3 prefill
+// combine 0.133 -> 0.122 ms).
 __device__ __forceinline__ void load_y(const f16_t *p, float *v) {
-  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  const uint4 u = make_uint4(q[0], q[1], q[2], q[3]);
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
