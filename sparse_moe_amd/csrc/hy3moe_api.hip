@@ -442,6 +442,24 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   // codes and scales for the block-scaled MFMAs of the weight-streaming and
   // large-tile paths (bf16 values for the tiled path); static FP8 code bytes
   // for the large-tile path's FP8 MFMAs, else their bf16 values.
+  // The quantisation quantise_x launches, as the select launch can host it.
+  auto hosted_quant = [&](const Branch &B) {
+    HostedQuant h;
+    if (B.f.act == HY3MOE_AFMT_MXFP8) {
+      h.mode = QH_MXFP8;
+      h.carrier = path != PATH_TILED ? 0 : 1;
+      h.scales = B.xs;
+    } else if (B.f.act == HY3MOE_AFMT_FP8_STATIC) {
+      h.mode = QH_E4M3;
+      h.carrier = L.a8_codes ? 0 : 1;
+      h.scale = w->x_scale;
+    }
+    h.x = x;
+    h.dtype = cfg->dtype;
+    h.n = (int64_t)T * H;
+    h.q = B.xq;
+    return h;
+  };
   auto quantise_x = [&](Branch &B) -> int {
     int e = HY3MOE_OK;
     if (B.f.act == HY3MOE_AFMT_MXFP8) {
@@ -523,9 +541,18 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
 
   mark();
   // 0. x quantised once for the routed experts (and for the shared expert
-  // when it shares their format), before the fork
-  rc = quantise_x(br[0]);
-  if (rc) return rc;
+  // when it shares their format), before the fork.  A weight-streaming
+  // batch with one branch has the select launch host it instead (one launch
+  // fewer on the decode chain).
+  HostedQuant hq;
+  if (path == PATH_SKINNY && !split && br[0].f.act != HY3MOE_AFMT_DTYPE) {
+    hq = hosted_quant(br[0]);
+    br[0].act = br[0].xq;
+    if (br[0].f.act == HY3MOE_AFMT_MXFP8) br[0].act_sc = br[0].xs;
+  } else {
+    rc = quantise_x(br[0]);
+    if (rc) return rc;
+  }
   if (split && !mix) {
     br[1].act = br[0].act;
     br[1].act_sc = br[0].act_sc;
@@ -567,7 +594,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
   mark();
   const float *bias = cfg->route_mode == HY3MOE_ROUTE_SIGMOID_BIAS ? w->expert_bias : nullptr;
   rc = check_launch(launch_select(part, L.n_ksplit, T, E, K, bias, cfg->route_mode, cfg->scale,
-                                  cfg->renorm_eps, idx, weight, s));
+                                  cfg->renorm_eps, idx, weight, s, hq));
   if (rc) return fail(rc);
   mark();
 

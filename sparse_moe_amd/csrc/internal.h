@@ -58,9 +58,25 @@ hipError_t launch_router_split(const float *w_router, int router_prec, uint16_t 
                                int H, hipStream_t stream);
 
 // Score + top-K select ------------------------------------------------------
+// An activation quantisation the select launch may host in workgroups of
+// its own (it needs neither the route nor the select): mode QH_NONE, QH_E4M3
+// (static FP8 of n elements of x, n % 8 == 0; carrier 1 writes the codes'
+// bf16 values) or QH_MXFP8 (dynamic MXFP8 of n bf16 values in rows of a
+// multiple of 32; codes and scales, or carrier 1 the bf16 values).
+enum { QH_NONE = 0, QH_E4M3 = 1, QH_MXFP8 = 2 };
+struct HostedQuant {
+  int mode = QH_NONE;
+  const void *x = nullptr;
+  int dtype = DT_BF16;
+  int64_t n = 0;
+  const float *scale = nullptr;
+  void *q = nullptr;
+  uint8_t *scales = nullptr;
+  int carrier = 0;
+};
 hipError_t launch_select(const double *part, int S, int T, int E, int K, const float *bias,
                          int route_mode, float scale, float renorm_eps, int32_t *idx,
-                         float *weight, hipStream_t stream);
+                         float *weight, hipStream_t stream, const HostedQuant &hq = HostedQuant());
 
 // Permutation ---------------------------------------------------------------
 struct PermArgs {

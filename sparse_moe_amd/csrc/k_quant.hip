@@ -9,30 +9,11 @@
 // elements per step with 16-byte loads.
 #include "common.cuh"
 #include "internal.h"
+#include "quant_dev.cuh"
 
 namespace hy3moe {
 
 namespace {
-
-template <typename T>
-__device__ __forceinline__ void load8(const T *p, float *v);
-template <>
-__device__ __forceinline__ void load8<bf16_t>(const bf16_t *p, float *v) {
-  const uint4 u = *reinterpret_cast<const uint4 *>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float *p, float *v) {
-  const float4 a = reinterpret_cast<const float4 *>(p)[0];
-  const float4 b = reinterpret_cast<const float4 *>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
 
 __device__ __forceinline__ float load1(const bf16_t *p) {
   return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(p) << 16);
@@ -45,18 +26,8 @@ __global__ __launch_bounds__(256) void quant_vec_kernel(const T *x, int64_t n8,
                                                         const float *scale, void *q) {
   const float s = *scale;
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
-    float v[8];
-    load8(x + 8 * i, v);
-    const uint32_t c0 = quant_e4m3x4(v[0], v[1], v[2], v[3], s);
-    const uint32_t c1 = quant_e4m3x4(v[4], v[5], v[6], v[7], s);
-    if (CARRIER) {
-      const uint2 lo = e4m3x4_to_bf16(c0), hi = e4m3x4_to_bf16(c1);
-      reinterpret_cast<uint4 *>(q)[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    } else {
-      reinterpret_cast<uint2 *>(q)[i] = make_uint2(c0, c1);
-    }
-  }
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride)
+    quant_e4m3_8<T, CARRIER>(x, i, s, q);
 }
 
 // Elements [begin, n): one per thread (the tail of the vector kernel).
@@ -72,36 +43,16 @@ __global__ __launch_bounds__(64) void quant_tail_kernel(const T *x, int64_t begi
     reinterpret_cast<uint8_t *>(q)[i] = (uint8_t)(c & 0xFFu);
 }
 
-// Dynamic MXFP8 quantisation (OCP microscaling conversion, blocks of 32
-// consecutive values along a row): four threads hold a block's 32 values
-// (8 each, 16 bytes of bf16) and quantise them together (mxfp8_quant8).
-// CARRIER: write the exact bf16 values (code value x 2^exponent) in place of
-// codes and scales.  Rows [n_rows, K], K % 32 == 0; in may alias q when
-// CARRIER (each thread rewrites only the 16 bytes it read).
+// Dynamic MXFP8 quantisation of rows of a multiple of 32 values (see
+// quant_dev.cuh).
 template <bool CARRIER>
 __global__ __launch_bounds__(256) void mxq_kernel(const bf16_t *in, int64_t n8, void *q,
                                                   uint8_t *scales) {
   // stride and n8 are multiples of 4, so the four lanes of a block (which
   // exchange maxima) stay in or leave the loop together
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
-    float v[8];
-    load8(in + 8 * i, v);
-    uint32_t code;
-    const uint2 c = mxfp8_quant8(v, code);
-    if (CARRIER) {
-      const float sc = e8m0_to_f32(code);
-      const uint32_t w[4] = {
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false)),
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true)),
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false)),
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true))};
-      reinterpret_cast<uint4 *>(q)[i] = make_uint4(w[0], w[1], w[2], w[3]);
-    } else {
-      reinterpret_cast<uint2 *>(q)[i] = c;
-      if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)code;
-    }
-  }
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride)
+    quant_mxfp8_8<CARRIER>(in, i, q, scales);
 }
 
 template <typename T, bool CARRIER>
