@@ -41,7 +41,8 @@ WORKLOADS = {"decode": "hy3_decode_T16", "prefill": "hy3_prefill_T8192_skew", "s
              "decode_w8a8": "hy3_decode_T16_w8a8", "prefill_w8a8": "hy3_prefill_T8192_skew_w8a8", "decode_mxfp4": "hy3_decode_T16_mxfp4", "prefill_mxfp4": "hy3_prefill_T8192_skew_mxfp4",
              "decode_w4a8": "hy3_decode_T16_w4a8", "prefill_w4a8": "hy3_prefill_T8192_skew_w4a8",
              "decode_mixed": "hy3_decode_T16_mixed", "prefill_mixed": "hy3_prefill_T8192_skew_mixed",
-             "decode_T32": "hy3_decode_T32", "decode_T32_w8a8": "hy3_decode_T32_w8a8"}
+             "decode_T32": "hy3_decode_T32", "decode_T32_w8a8": "hy3_decode_T32_w8a8",
+             "decode_T64": "hy3_decode_T64"}
 ROUTER_WORKLOAD = "hy3_router_only"            # the router-only configuration (gate alone, M tokens)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published

@@ -71,9 +71,9 @@ constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
 // W8A8 8 / 4 / 2 (one chunk of codes per step; even, as two steps make one
 // MFMA); MXFP4 3 / 2 / 1 (four token chunks per step).  With the four-row
 // weight loads (TR, one fragment) a multiple of four: FP8 takes 4.
-template <int MT, int WF, bool TR = false>
+template <int MT, int WF, int TRG = 0>
 constexpr int steps_per_set() {
-  return TR && WF == WF_FP8 ? 4
+  return TRG == 4 && WF == WF_FP8 ? 4
          : WF == WF_W8A8  ? (MT == 1 ? 8 : (MT == 2 ? 4 : 2))   // even: pairs of steps
          : WF == WF_FP8   ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1))
          : WF == WF_MXFP4 ? (MT == 1 ? 3 : (MT == 2 ? 2 : 1))
@@ -117,19 +117,20 @@ struct UnitOut {
 // gathered rows of a wavefront read over the banks.
 __host__ __device__ constexpr int x_lds_stride(int row_bytes) { return row_bytes + 16; }
 
-// TR (one 16-row fragment, or two for bf16 and W8A8; every K row a multiple
-// of 256 bytes): a weight load covers four rows x 256 contiguous bytes
+// TR (grouped weight loads; every K row of the launch a multiple of the
+// group's 64 TRG bytes): a weight load covers 16 / TRG rows x 64 TRG
+// contiguous bytes (TRG = 4: four rows x 256 B; TRG = 2: eight rows x 128 B)
 // instead of sixteen rows x 64 bytes, with a non-temporal hint; a streaming
-// read in that form ran ~10 % faster than the MFMA-shaped one at the rows of
-// 1.5-4 KB of these GEMMs.
-// Load j of a group of four 64-byte steps holds row 4 j + l / 16, bytes
-// [16 (l % 16), +16) of the group's 256; the wavefront's 4 KB LDS buffer
-// turns the group into the MFMA layout (step s: row l % 16, bytes [64 s +
-// 16 (l / 16), +16)).  Chunk c of row r sits in slot 16 r + (c ^ r), so that
-// neither pass has bank conflicts.  LDS operations of one wavefront complete
-// in order; the wavefront-scope fences keep the compiler from reordering
-// them across the passes.
-constexpr int TR_WAVE_BYTES = 4096;
+// read in those forms ran ~10 % faster than the MFMA-shaped one at the rows
+// of 1.5-4 KB of these GEMMs.  Load j of a group of TRG 64-byte steps holds
+// row (16 / TRG) j + l / (4 TRG), bytes [16 (l % 4 TRG), +16) of the group's
+// 64 TRG; the wavefront's LDS buffer (1 KB x TRG) turns the group into the
+// MFMA layout (step s: row l % 16, bytes [64 s + 16 (l / 16), +16)).  Chunk
+// c of row r sits in slot 4 TRG r + (c ^ (r % 4 TRG)), so the passes are
+// free of bank conflicts (TRG = 4) or two-way (TRG = 2).  LDS operations of
+// one wavefront complete in order; the wavefront-scope fences keep the
+// compiler from reordering them across the passes.
+__host__ __device__ constexpr int tr_wave_bytes(int trg) { return 1024 * trg; }
 
 __device__ __forceinline__ uint4 load_nt16(const char *p) {
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -137,22 +138,25 @@ __device__ __forceinline__ uint4 load_nt16(const char *p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-template <int U>
+template <int U, int TRG>
 __device__ __forceinline__ void transpose_groups(uint4 (&W)[U], uint4 *lb, int lane) {
-  static_assert(U % 4 == 0, "groups of four steps");
+  static_assert(TRG == 2 || TRG == 4, "groups of two or four steps");
+  static_assert(U % TRG == 0, "whole groups per register set");
+  constexpr int CPR = 4 * TRG;      // 16-byte chunks per row of a group
+  constexpr int RPL = 16 / TRG;     // rows per load
 #pragma unroll
-  for (int q = 0; q < U / 4; ++q) {
+  for (int q = 0; q < U / TRG; ++q) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * j + (lane >> 4), c = lane & 15;
-      lb[16 * r + (c ^ r)] = W[4 * q + j];
+    for (int j = 0; j < TRG; ++j) {
+      const int r = RPL * j + lane / CPR, c = lane % CPR;
+      lb[CPR * r + (c ^ (r % CPR))] = W[TRG * q + j];
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < TRG; ++st) {
       const int r = lane & 15, c = 4 * st + (lane >> 4);
-      W[4 * q + st] = lb[16 * r + (c ^ r)];
+      W[TRG * q + st] = lb[CPR * r + (c ^ (r % CPR))];
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
@@ -161,7 +165,7 @@ __device__ __forceinline__ void transpose_groups(uint4 (&W)[U], uint4 *lb, int l
 // Unit u (tile u / n_col_blocks, column block u % n_col_blocks) of this
 // kernel; returns false if the column block lies past the group's width.
 // half = 1 or 2: only the first or the second 16-row fragment of a down unit.
-template <typename T, bool GATE_UP, int MT, int WF, bool XL, bool TR>
+template <typename T, bool GATE_UP, int MT, int WF, bool XL, int TRG>
 __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_blocks, int lane,
                                         UnitSrc<MT> &src, UnitOut &o, int half = 0) {
   constexpr bool F8 = WF == WF_FP8 || WF == WF_W8A8, F4 = WF == WF_MXFP4 || WF == WF_W4A8;
@@ -189,8 +193,9 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
                               : static_cast<const char *>(a.w0) + (size_t)g * a.I * rowb(a.H);
     const char *up = shared ? static_cast<const char *>(a.ws1)
                             : static_cast<const char *>(a.w1) + (size_t)g * a.I * rowb(a.H);
-    // TR: lane (l / 16) of a four-row load, bytes [16 (l % 16), +16) of its 256
-    const int lr = TR ? (lane >> 4) : r16, lc = TR ? (lane & 15) : cg;
+    // TR: row l / (4 TRG) of a grouped load, bytes [16 (l % 4 TRG), +16) of
+    // the row's 64 TRG
+    const int lr = TRG ? lane / (4 * TRG) : r16, lc = TRG ? lane % (4 * TRG) : cg;
     src.w0p = gate + (size_t)(o.col0 + lr) * rowb(a.H) + lc * 16;
     src.w1p = up + (size_t)(o.col0 + lr) * rowb(a.H) + lc * 16;
     src.rowb = rowb(a.H);
@@ -206,8 +211,8 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
                             : static_cast<const char *>(a.w0) + (size_t)g * a.H * rowb(a.I);
     const int n0 = (o.col0 + r16 < a.H) ? o.col0 + r16 : o.col0;
     const int n1 = (o.col0 + 16 + r16 < a.H) ? o.col0 + 16 + r16 : o.col0;
-    if (TR) {   // H % 64 == 0: the fragments' rows all exist
-      src.w0p = dn + (size_t)(o.col0 + (lane >> 4)) * rowb(Ig) + (lane & 15) * 16;
+    if (TRG) {   // H % 64 == 0: the fragments' rows all exist
+      src.w0p = dn + (size_t)(o.col0 + lane / (4 * TRG)) * rowb(Ig) + lane % (4 * TRG) * 16;
       src.w1p = src.w0p + (size_t)16 * rowb(Ig);
     } else {
       src.w0p = dn + (size_t)n0 * rowb(Ig) + cg * 16;
@@ -268,7 +273,7 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
 // of them is split into its two 16-row fragments for twice as many
 // wavefronts, so the last round costs half a unit.  Returns the item index
 // (kmax when there is none) and fills src / o.
-template <typename T, bool GATE_UP, int MT, int WF, bool XL, bool TR>
+template <typename T, bool GATE_UP, int MT, int WF, bool XL, int TRG>
 __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int nw, int n_units,
                                          int n_col_blocks, int lane, UnitSrc<MT> &src,
                                          UnitOut &o) {
@@ -279,10 +284,10 @@ __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int 
     if (k < full || !split) {
       const int u = w + k * nw;
       if (u >= n_units) return kmax;
-      if (unit_of<T, GATE_UP, MT, WF, XL, TR>(a, u, n_col_blocks, lane, src, o)) return k;
+      if (unit_of<T, GATE_UP, MT, WF, XL, TRG>(a, u, n_col_blocks, lane, src, o)) return k;
     } else {
       if (w >= 2 * tail) return kmax;
-      if (unit_of<T, GATE_UP, MT, WF, XL, TR>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
+      if (unit_of<T, GATE_UP, MT, WF, XL, TRG>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
                                       1 + (w & 1)))
         return k;
     }
@@ -348,11 +353,12 @@ template <bool XL> constexpr int stream_threads() { return XL ? 512 : 256; }
 // BRANCH names the instantiation only: 0 for the routed experts (or every
 // group), 1 for the shared expert's own launches, which profiles then list
 // apart.
-template <typename T, bool GATE_UP, int MT, int WF, bool XL, bool TR, int BRANCH>
+template <typename T, bool GATE_UP, int MT, int WF, bool XL, int TRG, int BRANCH>
 __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_stream_kernel(
     ExpertArgs a_in, int n_col_blocks) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4, MXA = WF == WF_W4A8;
   constexpr bool A8C = WF == WF_W8A8, CODES = token_codes<WF>();
+  constexpr bool TR = TRG > 0;
   constexpr int NT = stream_threads<XL>(), WPB = NT / 64;
   // The unit metadata -- tile list, group offsets and (gate-up) the sorted
   // token ids -- is staged in LDS once per workgroup, so that the set-up of a
@@ -434,10 +440,10 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
       for (int j = 0; j < XB; ++j) *reinterpret_cast<uint4 *>(dst + at[j]) = v[j];
     }
   }
-  // TR: each wavefront's 4 KB transposition buffer after the x copy
+  // TR: each wavefront's transposition buffer after the x copy
   const int x_bytes = XL ? a_in.n_tok * x_lds_stride(a_in.H * (CODES ? 1 : Elem<T>::kBytes)) : 0;
   uint4 *lb = reinterpret_cast<uint4 *>(reinterpret_cast<char *>(meta + meta_n) + x_bytes +
-                                        (threadIdx.x >> 6) * TR_WAVE_BYTES);
+                                        (threadIdx.x >> 6) * tr_wave_bytes(TRG));
   (void)lb;
   __syncthreads();
   ExpertArgs a = a_in;
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
     a.hs = scl + 2 * (a_in.E + 1);
     a.xs = scl + 3 * (a_in.E + 1);
   }
-  constexpr int U = steps_per_set<MT, WF, TR>();   // 64-byte K steps per row per register set
+  constexpr int U = steps_per_set<MT, WF, TRG>();   // 64-byte K steps per row per register set
   constexpr int XN = token_chunks<WF>();       // 16-byte token chunks per step
   const int lane = threadIdx.x & 63;
   // The wavefront index is uniform; readfirstlane makes that visible to the
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   // units of one expert spread over all XCDs and HBM channels.
   UnitSrc<MT> src;    // item whose blocks are being loaded
   UnitOut om, ol;     // item being multiplied, item being loaded
-  int k_ld = next_item<T, GATE_UP, MT, WF, XL, TR>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
+  int k_ld = next_item<T, GATE_UP, MT, WF, XL, TRG>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
   if (k_ld >= kmax) return;
   int k_mm = k_ld;
   om = ol;
@@ -527,9 +533,10 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   {                                                                                    \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       const int st_ = s_ld + u < src.nsub ? s_ld + u : src.nsub - 1;                  \
-      if constexpr (TR) {   /* load j of the group at step 4 q: rows 4 j .. 4 j + 3 */ \
-        const int g_ = s_ld + (u & ~3) < src.nsub ? s_ld + (u & ~3) : src.nsub - 4;     \
-        const size_t o_ = (size_t)g_ * 64 + (size_t)(4 * (u & 3)) * src.rowb;           \
+      if constexpr (TR) {   /* load j of a group: rows (16 / TRG) j .. */             \
+        const int g_ = s_ld + (u & ~(TRG - 1)) < src.nsub ? s_ld + (u & ~(TRG - 1))   \
+                                                          : src.nsub - TRG;             \
+        const size_t o_ = (size_t)g_ * 64 + (size_t)(16 / TRG * (u & (TRG - 1))) * src.rowb; \
         W0[u] = load_nt16(src.w0p + o_);                                               \
         W1[u] = load_nt16(src.w1p + o_);                                               \
       } else {                                                                         \
@@ -557,7 +564,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
     }                                                                                  \
     s_ld += U;                                                                         \
     if (s_ld >= src.nsub) {                                                            \
-      k_ld = next_item<T, GATE_UP, MT, WF, XL, TR>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
+      k_ld = next_item<T, GATE_UP, MT, WF, XL, TRG>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src, ol);                             \
       s_ld = 0;                                                                        \
     }                                                                                  \
@@ -567,8 +574,8 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
 #define HY3_MMA(W0, W1, X, S0, S1, XS)                                                 \
   {                                                                                    \
     if constexpr (TR) {                                                                \
-      transpose_groups<U>(W0, lb, lane);                                               \
-      transpose_groups<U>(W1, lb, lane);                                               \
+      transpose_groups<U, TRG>(W0, lb, lane);                                          \
+      transpose_groups<U, TRG>(W1, lb, lane);                                          \
     }                                                                                  \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                    \
       if (s_mm + u < om.nsub) {                                                        \
@@ -629,7 +636,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
       unit_epilogue<T, GATE_UP, MT, WF>(a, om, acc, lane);                             \
       _Pragma("unroll") for (int f = 0; f < 2; ++f)                                    \
         _Pragma("unroll") for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; \
-      k_mm = next_item<T, GATE_UP, MT, WF, XL, TR>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
+      k_mm = next_item<T, GATE_UP, MT, WF, XL, TRG>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src_dummy, om);                       \
       s_mm = 0;                                                                        \
       more = k_mm < kmax;                                                              \
@@ -654,7 +661,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
 
 // Persistent grid: WAVES_PER_SIMD wavefronts per SIMD on the 256 CUs.
 constexpr int STREAM_BLOCKS = 256 * WAVES_PER_SIMD;
-constexpr size_t STREAM_XL_LDS_MAX = 150 * 1024;   // metadata + x copy of one workgroup
+constexpr size_t STREAM_XL_LDS_MAX = 160 * 1024;   // LDS of one workgroup (one per CU)
 
 // LDS bytes of the x copy (rows padded), or 0 when the gate-up GEMM of this
 // batch does not stage x: one 16-row fragment (T <= 16) and the copy fits.
@@ -675,44 +682,46 @@ constexpr int weight_row_bytes(int K) {
                                            : K * Elem<T>::kBytes;
 }
 
-// Formats with a TR instantiation (steps per set a multiple of four); the
-// launch takes it when every weight row of the launch is a multiple of 256
-// bytes.
+// Group size of the grouped weight loads for a format and token fragment
+// count (0: none): four 64-byte steps where the register sets hold whole
+// groups of four without spilling, else two.  MXFP4 weights with bf16
+// tokens take three steps per set (four spill); FP8 takes four at one
+// fragment, and neither FP8 nor W4A8 has an even count at four fragments.
 template <typename T, int MT, int WF>
-constexpr bool tr_format() {
-  // One fragment: every format but MXFP4 weights with bf16 tokens (three
-  // steps per set, as four spill); two fragments: bf16 and W8A8 (four steps
-  // per set already; the others spill at four).
-  return !std::is_same<T, float>::value && steps_per_set<MT, WF, true>() % 4 == 0 &&
-         (MT == 1 ? WF != WF_MXFP4 : (MT == 2 && (WF == WF_DTYPE || WF == WF_W8A8)));
+constexpr int tr_group() {
+  if (std::is_same<T, float>::value || WF == WF_MXFP4) return 0;
+  if (MT == 1) return 4;
+  if (MT == 2) return (WF == WF_DTYPE || WF == WF_W8A8) ? 4 : (WF == WF_W4A8 ? 2 : 0);
+  return (WF == WF_DTYPE || WF == WF_W8A8) ? 2 : 0;
 }
+// Every weight row of the launch a multiple of a group's 64 trg bytes.
 template <typename T, int WF>
-bool tr_rows(const ExpertArgs &a, bool gate_up) {
-  auto ok = [](int K) { return weight_row_bytes<T, WF>(K) % 256 == 0; };
+bool tr_rows(const ExpertArgs &a, bool gate_up, int trg) {
+  auto ok = [trg](int K) { return weight_row_bytes<T, WF>(K) % (64 * trg) == 0; };
   if (gate_up) return ok(a.H);
   return (a.grp_sel == GRP_SHARED || ok(a.I)) &&
          (a.grp_sel == GRP_ROUTED || a.I_shared == 0 || ok(a.I_shared));
 }
 
-template <typename T, int MT, int WF, bool TR, int BRANCH>
+template <typename T, int MT, int WF, int TRG, int BRANCH>
 hipError_t launch_skinny_tr(const ExpertArgs &a, bool gate_up, size_t xb, hipStream_t stream) {
   const size_t meta = (meta_lds_bytes(a, gate_up) + 15) / 16 * 16;
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int ncb = (Imax + 15) / 16;
     if (xb)   // one 512-thread workgroup per CU, x in LDS
-      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, true, TR, BRANCH>),
-                         dim3(STREAM_BLOCKS / 2), dim3(512),
-                         meta + xb + (TR ? 8 * TR_WAVE_BYTES : 0), stream, a, ncb);
-    else
-      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, false, TR, BRANCH>),
-                         dim3(STREAM_BLOCKS), dim3(256), meta + (TR ? 4 * TR_WAVE_BYTES : 0),
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, true, TRG, BRANCH>),
+                         dim3(STREAM_BLOCKS / 2), dim3(512), meta + xb + 8 * tr_wave_bytes(TRG),
                          stream, a, ncb);
+    else
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, false, TRG, BRANCH>),
+                         dim3(STREAM_BLOCKS), dim3(256), meta + 4 * tr_wave_bytes(TRG), stream, a,
+                         ncb);
   } else {
     const int ncb = (a.H + 31) / 32;
-    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF, false, TR, BRANCH>),
-                       dim3(STREAM_BLOCKS), dim3(256), meta + (TR ? 4 * TR_WAVE_BYTES : 0),
-                       stream, a, ncb);
+    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF, false, TRG, BRANCH>),
+                       dim3(STREAM_BLOCKS), dim3(256), meta + 4 * tr_wave_bytes(TRG), stream, a,
+                       ncb);
   }
   return hipGetLastError();
 }
@@ -720,16 +729,27 @@ hipError_t launch_skinny_tr(const ExpertArgs &a, bool gate_up, size_t xb, hipStr
 template <typename T, int MT, int WF, int BRANCH>
 hipError_t launch_skinny_b(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
   const size_t xb = gate_up ? x_lds_bytes<T, MT, WF>(a) : 0;
-  if constexpr (tr_format<T, MT, WF>()) {
-    // TR, with the LDS copy of x when it leaves room for the 8 wavefronts'
-    // buffers (else the tokens come from global memory: measured faster
-    // than the copy without TR for bf16 x at H = 4096)
+  constexpr int G = tr_group<T, MT, WF>();
+  if constexpr (G > 0) {
+    // The grouped loads with the LDS copy of x when it leaves room for the
+    // 8 wavefronts' buffers; for one fragment, groups of two steps (half the
+    // buffer) when only those leave room; else the grouped loads with the
+    // tokens from global memory (measured faster than the copy without them
+    // for bf16 x at H = 4096).
     const size_t meta = (meta_lds_bytes(a, gate_up) + 15) / 16 * 16;
-    const bool room = !xb || meta + xb + 8 * TR_WAVE_BYTES <= STREAM_XL_LDS_MAX;
-    if (tr_rows<T, WF>(a, gate_up))
-      return launch_skinny_tr<T, MT, WF, true, BRANCH>(a, gate_up, room ? xb : 0, stream);
+    auto room = [&](int trg) {
+      return !xb || meta + xb + 8 * (size_t)tr_wave_bytes(trg) <= STREAM_XL_LDS_MAX;
+    };
+    if (tr_rows<T, WF>(a, gate_up, G) && room(G))
+      return launch_skinny_tr<T, MT, WF, G, BRANCH>(a, gate_up, xb, stream);
+    if constexpr (G == 4 && MT == 1) {
+      if (xb && tr_rows<T, WF>(a, gate_up, 2) && room(2))
+        return launch_skinny_tr<T, MT, WF, 2, BRANCH>(a, gate_up, xb, stream);
+    }
+    if (tr_rows<T, WF>(a, gate_up, G))
+      return launch_skinny_tr<T, MT, WF, G, BRANCH>(a, gate_up, 0, stream);
   }
-  return launch_skinny_tr<T, MT, WF, false, BRANCH>(a, gate_up, xb, stream);
+  return launch_skinny_tr<T, MT, WF, 0, BRANCH>(a, gate_up, xb, stream);
 }
 
 template <typename T, int MT, int WF>

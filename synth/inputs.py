@@ -215,6 +215,10 @@ CONFIGS: Dict[str, MoEConfig] = {
                  I=1536, I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform",
                  w_format="fp8_e4m3", act_format="fp8_static"),
+    # ... and with 64 tokens (four token fragments per unit), bf16.
+    "hy3_decode_T64": MoEConfig("hy3_decode_T64", 17, 1, T=64, H=4096, E=192, K=8, I=1536,
+                 I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
+                 scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform"),
     # Mixed precision in one layer: the routed experts at W4A8 (the MXFP4
     # experts above, MXFP8 activations) and the shared expert at W8A8 (FP8
     # E4M3 weights, static FP8 activations).

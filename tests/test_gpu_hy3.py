@@ -178,6 +178,12 @@ def test_hy3_decode_T16_w8a8_full(dev, hy3_fp8_weights):
                       workload_shape=False)
 
 
+def test_hy3_decode_T64_full(dev, hy3_weights):
+    """64 tokens on the Hy3 weights: four token fragments per work unit (the
+    two-step grouped weight loads), every token, the stated bf16 bound."""
+    decode_full_check(MoEInputs(CONFIGS["hy3_decode_T64"]), dev, hy3_weights)
+
+
 def test_hy3_decode_T32_w8a8_full(dev, hy3_fp8_weights):
     """W8A8 decode with 32 tokens (FP8 MFMAs at two token fragments)."""
     inp = MoEInputs(CONFIGS["hy3_decode_T32_w8a8"])

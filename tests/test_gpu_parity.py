@@ -193,6 +193,8 @@ SMALL = {
                      w_format="mxfp4", act_format="mxfp8"),
     "w4a8_T12_rows256": dict(seed=84, T=12, H=512, E=8, K=3, I=512, I_shared=512, dtype="bf16",
                              w_format="mxfp4", act_format="mxfp8"),
+    "w4a8_T24_rows128": dict(seed=85, T=24, H=512, E=8, K=2, I=256, I_shared=256, dtype="bf16",
+                             w_format="mxfp4", act_format="mxfp8"),
     "w4a8_T20_noshared": dict(seed=82, T=20, H=256, E=8, K=2, I=128, I_shared=0,
                               dtype="bf16", w_format="mxfp4", act_format="mxfp8"),
     "w4a8_T64_softmax": dict(seed=83, T=64, H=384, E=16, K=4, I=128, I_shared=256,
