@@ -69,11 +69,13 @@ constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
 // 64-byte steps per register set: bf16 weights UBASE / MT; FP8 weights 6 / 3
 // / 1 for 1 / 2 / 4 row fragments (each step also holds two token chunks);
 // W8A8 8 / 4 / 2 (one chunk of codes per step; even, as two steps make one
-// MFMA); MXFP4 3 / 2 / 1 (four token chunks per step).  With the four-row
-// weight loads (TR, one fragment) a multiple of four: FP8 takes 4.
+// MFMA); MXFP4 3 / 2 / 1 (four token chunks per step).  With the grouped
+// weight loads (TRG steps per group) a multiple of the group: FP8 takes 4
+// in groups of four, MXFP4 2 in groups of two.
 template <int MT, int WF, int TRG = 0>
 constexpr int steps_per_set() {
   return TRG == 4 && WF == WF_FP8 ? 4
+         : TRG == 2 && WF == WF_MXFP4 ? 2
          : WF == WF_W8A8  ? (MT == 1 ? 8 : (MT == 2 ? 4 : 2))   // even: pairs of steps
          : WF == WF_FP8   ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1))
          : WF == WF_MXFP4 ? (MT == 1 ? 3 : (MT == 2 ? 2 : 1))
@@ -684,12 +686,15 @@ constexpr int weight_row_bytes(int K) {
 
 // Group size of the grouped weight loads for a format and token fragment
 // count (0: none): four 64-byte steps where the register sets hold whole
-// groups of four without spilling, else two.  MXFP4 weights with bf16
-// tokens take three steps per set (four spill); FP8 takes four at one
-// fragment, and neither FP8 nor W4A8 has an even count at four fragments.
+// groups of four without spilling, else two.  FP8 takes four steps per set
+// at one fragment; MXFP4 weights with bf16 tokens take one group of two (at
+// four they spill; the grouped loads with two steps per set beat the
+// MFMA-shaped ones with three: Hy3 decode 0.254 -> 0.202 ms); at four
+// fragments neither FP8, W4A8 nor MXFP4 has an even count.
 template <typename T, int MT, int WF>
 constexpr int tr_group() {
-  if (std::is_same<T, float>::value || WF == WF_MXFP4) return 0;
+  if (std::is_same<T, float>::value) return 0;
+  if (WF == WF_MXFP4) return MT <= 2 ? 2 : 0;
   if (MT == 1) return 4;
   if (MT == 2) return (WF == WF_DTYPE || WF == WF_W8A8) ? 4 : (WF == WF_W4A8 ? 2 : 0);
   return (WF == WF_DTYPE || WF == WF_W8A8) ? 2 : 0;
