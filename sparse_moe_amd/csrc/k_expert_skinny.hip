@@ -4,8 +4,10 @@
 // grouped GEMM has very low arithmetic intensity and is bound by the bytes
 // of expert weights read from HBM (Hy3 Preview inference case, section on
 // decode parallelism: small-batch MoE grouped GEMM is memory-bound).  This
-// path reads every touched weight byte exactly once, straight from global
-// memory into MFMA operand registers (no LDS round trip).
+// path reads every touched weight byte exactly once, from global memory
+// into registers: in the MFMA operand layout itself, or (the grouped loads,
+// TR below) in wider row pieces that a per-wavefront LDS buffer turns into
+// that layout.
 //
 // Work unit = one wavefront's share of one group (routed expert or the shared
 // expert, all of its <= 16*MT rows): 16 gate + 16 up weight rows (gate-up) or
@@ -102,7 +104,7 @@ struct UnitSrc {
   bool vs;                   // W4A8: scale rows allow 16-byte loads of 4 steps
   int nsub;                // 64-byte K steps per row
   int nf;                  // fragments streamed (2; 1 for half of a down unit)
-  int rowb;                // TR: bytes per weight row (the stride of the four-row loads)
+  int rowb;                // TR: bytes per weight row (the stride of the grouped loads)
 };
 struct UnitOut {
   int row0, grp_end, col0, nsub, nf;
