@@ -73,17 +73,26 @@ constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
 // W8A8 8 / 4 / 2 (one chunk of codes per step; even, as two steps make one
 // MFMA); MXFP4 3 / 2 / 1 (four token chunks per step).  With the grouped
 // weight loads (TRG steps per group) a multiple of the group: FP8 takes 4
-// in groups of four, MXFP4 2 in groups of two.
-template <int MT, int WF, int TRG = 0>
+// in groups of four, MXFP4 2 in groups of two, or 4 when its token chunks
+// are read at multiply time (XD, below).
+template <int MT, int WF, int TRG = 0, bool XD = false>
 constexpr int steps_per_set() {
   return TRG == 4 && WF == WF_FP8 ? 4
-         : TRG == 2 && WF == WF_MXFP4 ? 2
+         : TRG == 2 && WF == WF_MXFP4 ? (XD ? 4 : 2)
          : WF == WF_W8A8  ? (MT == 1 ? 8 : (MT == 2 ? 4 : 2))   // even: pairs of steps
          : WF == WF_FP8   ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1))
          : WF == WF_MXFP4 ? (MT == 1 ? 3 : (MT == 2 ? 2 : 1))
          : WF == WF_W4A8  ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
                           : UBASE / MT;
 }
+// XD: the token chunks of a step are read from the LDS copy of x when the
+// step is multiplied, not with its weights one register set ahead.  For
+// MXFP4 weights with bf16 tokens (four chunks per step) that frees the
+// registers for a second group of grouped loads per set (Hy3 decode
+// gate-up 116 -> 109 us); for the other formats, whose steps hold one or
+// two chunks, it measured the same or slower.
+template <bool XL, int MT, int WF>
+constexpr bool tokens_at_multiply() { return XL && MT == 1 && WF == WF_MXFP4; }
 // 16-byte token chunks per 64-byte weight step.
 template <int WF>
 constexpr int token_chunks() {
@@ -111,6 +120,7 @@ struct UnitOut {
   float sc0, sc1;          // FP8 weights: scales of fragment 0 / 1's matrix
                            // (times the input's activation scale with a8)
   float hs;                // a8 gate-up: activation scale of the group's h
+  uint32_t xlo;            // XD: byte offset of the lane's token chunks in the LDS copy of x
 };
 
 // XL (gate-up at T <= 16): the workgroup copies every token row of x into
@@ -255,7 +265,7 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
     // 256-byte step (the K values of the lane's codes); W4A8: code bytes
     // [32g, 32g+32) of each 128-byte step, and block scale step * 4 + g
     if (XL)   // the token's row of the LDS copy, the lane's chunk of a step
-      src.xlo[m] = (uint32_t)a.sorted_token[trow] * (uint32_t)x_lds_stride(a.H * (CODES ? 1 : EB)) +
+      o.xlo = src.xlo[m] = (uint32_t)a.sorted_token[trow] * (uint32_t)x_lds_stride(a.H * (CODES ? 1 : EB)) +
                    cg * 16 * (MXA ? 1 : token_chunks<WF>());
     if (WF == WF_W8A8) {   // code bytes [16g, 16g + 16) of each 64-byte step
       src.xp[m] = static_cast<const char *>(a.act) + arow + cg * 16;
@@ -464,7 +474,8 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
     a.hs = scl + 2 * (a_in.E + 1);
     a.xs = scl + 3 * (a_in.E + 1);
   }
-  constexpr int U = steps_per_set<MT, WF, TRG>();   // 64-byte K steps per row per register set
+  constexpr bool XD = tokens_at_multiply<XL, MT, WF>();
+  constexpr int U = steps_per_set<MT, WF, TRG, XD>();   // 64-byte K steps per row per register set
   constexpr int XN = token_chunks<WF>();       // 16-byte token chunks per step
   const int lane = threadIdx.x & 63;
   // The wavefront index is uniform; readfirstlane makes that visible to the
@@ -558,6 +569,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
       if constexpr (MXA && U % 4 == 0) {                                               \
         if (u % 4 == 0) HY3_SCALES4(S0, S1, XS, u, s_ld + u);                          \
       }                                                                                \
+      if constexpr (!XD)                                                               \
       _Pragma("unroll") for (int m = 0; m < MT; ++m)                                   \
         _Pragma("unroll") for (int h = 0; h < XN; ++h)                                 \
           X[u][m][h] = XL ? *reinterpret_cast<const uint4 *>(xl + src.xlo[m] +          \
@@ -577,6 +589,14 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   // and move on.  `more` turns false after the last unit.
 #define HY3_MMA(W0, W1, X, S0, S1, XS)                                                 \
   {                                                                                    \
+    if constexpr (XD) {   /* this block's token chunks (one fragment), from LDS */    \
+      _Pragma("unroll") for (int u = 0; u < U; ++u) {                                  \
+        const int sx_ = s_mm + u < om.nsub ? s_mm + u : om.nsub - 1;                   \
+        _Pragma("unroll") for (int h = 0; h < XN; ++h)                                 \
+          X[u][0][h] = *reinterpret_cast<const uint4 *>(xl + om.xlo + sx_ * 64 * XN +  \
+                                                        h * (MXA ? 64 : 16));           \
+      }                                                                                \
+    }                                                                                  \
     if constexpr (TR) {                                                                \
       transpose_groups<U, TRG>(W0, lb, lane);                                          \
       transpose_groups<U, TRG>(W1, lb, lane);                                          \
@@ -689,10 +709,11 @@ constexpr int weight_row_bytes(int K) {
 // Group size of the grouped weight loads for a format and token fragment
 // count (0: none): four 64-byte steps where the register sets hold whole
 // groups of four without spilling, else two.  FP8 takes four steps per set
-// at one fragment; MXFP4 weights with bf16 tokens take one group of two (at
+// at one fragment; MXFP4 weights with bf16 tokens take groups of two (at
 // four they spill; the grouped loads with two steps per set beat the
-// MFMA-shaped ones with three: Hy3 decode 0.254 -> 0.202 ms); at four
-// fragments neither FP8, W4A8 nor MXFP4 has an even count.
+// MFMA-shaped ones with three: Hy3 decode 0.254 -> 0.202 ms), two groups
+// per set when the tokens are read at multiply time; at four fragments
+// neither FP8, W4A8 nor MXFP4 has an even count.
 template <typename T, int MT, int WF>
 constexpr int tr_group() {
   if (std::is_same<T, float>::value) return 0;

@@ -168,6 +168,13 @@ SMALL = {
                      w_format="mxfp4"),
     "mxfp4_T16": dict(seed=71, T=16, H=512, E=32, K=4, I=256, I_shared=128, dtype="bf16",
                       w_format="mxfp4"),
+    # one fragment with x in LDS: rows of 192 bytes (no grouped loads, three
+    # steps per set) and of 384 bytes (two groups of two per set, a partial
+    # last set)
+    "mxfp4_T8_H384": dict(seed=78, T=8, H=384, E=8, K=2, I=128, I_shared=128, dtype="bf16",
+                          w_format="mxfp4"),
+    "mxfp4_T12_H768": dict(seed=79, T=12, H=768, E=12, K=3, I=256, I_shared=128,
+                           dtype="bf16", w_format="mxfp4"),
     "mxfp4_T20_noshared": dict(seed=72, T=20, H=256, E=8, K=2, I=128, I_shared=0,
                                dtype="bf16", w_format="mxfp4"),
     "mxfp4_T64_softmax": dict(seed=73, T=64, H=384, E=16, K=4, I=128, I_shared=256,
