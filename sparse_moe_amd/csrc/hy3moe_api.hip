@@ -12,10 +12,6 @@
 #include "hy3moe.h"
 #include "internal.h"
 
-namespace hy3moe {
-int skinny_tile_rows(int T);
-}
-
 using namespace hy3moe;
 
 namespace {
@@ -128,12 +124,11 @@ void compute_layout(const hy3moe_config *c, int for_forward, hy3moe_ws_layout *L
                 (path == PATH_SKINNY && c->H % 128 == 0 && c->I % 128 == 0 &&
                  c->I_shared % 128 == 0);
   if (path == PATH_SKINNY) {
-    L->tile_rows = skinny_tile_rows((int)T);
-    L->max_tiles = E + 1;
+    L->tile_rows = SKINNY_ROWS;
   } else {
     L->tile_rows = path == PATH_BIG ? BIG_ROWS : TILED_ROWS;
-    L->max_tiles = (int32_t)((R + L->tile_rows - 1) / L->tile_rows + E + 1);
   }
+  L->max_tiles = (int32_t)((R + L->tile_rows - 1) / L->tile_rows + E + 1);
   L->tiles = off;       off += al((size_t)(2 * L->max_tiles + 2) * 4);
   const int Imax = c->I > c->I_shared ? c->I : c->I_shared;
   const int eb = elt_bytes(c->dtype);
@@ -507,7 +502,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
     ea.act_sc = amx ? B.act_sc : nullptr;
     ea.out = fused ? ws + L.hq : h_base(B);
     ea.out_sc = fused ? reinterpret_cast<uint8_t *>(ws + L.hs) : nullptr;
-    return check_launch(launch_gate_up(ea, cfg->dtype, T, path, B.st));
+    return check_launch(launch_gate_up(ea, cfg->dtype, path, B.st));
   };
   auto down = [&](const Branch &B) -> int {
     const bool amx = B.f.act == HY3MOE_AFMT_MXFP8;
@@ -536,7 +531,7 @@ static int forward_impl(const hy3moe_config *cfg, const void *x, const hy3moe_we
       }
     }
     ea.out = ws + L.y;
-    return check_launch(launch_down(ea, cfg->dtype, T, path, B.st));
+    return check_launch(launch_down(ea, cfg->dtype, path, B.st));
   };
 
   mark();

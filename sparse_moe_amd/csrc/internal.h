@@ -21,6 +21,7 @@ constexpr int TILED_ROWS = 128;     // rows (token copies) per tile, large-T pat
 constexpr int TILED_GU_COLS = 64;   // h columns per gate-up tile (64 gate + 64 up rows)
 constexpr int TILED_DN_COLS = 128;  // y columns per down tile
 constexpr int SKINNY_MAX_T = 64;    // at or below this T the weight-streaming path runs
+constexpr int SKINNY_ROWS = 16;     // rows per tile of the weight-streaming path
 constexpr int SKINNY_GU_COLS = 64;  // h columns per skinny gate-up workgroup
 constexpr int SKINNY_DN_COLS = 128; // y columns per skinny down workgroup
 constexpr int PERM_CHUNK = 1024;    // (token, pick) entries per wavefront in the permutation
@@ -159,8 +160,8 @@ __device__ __forceinline__ void tile_slice(const ExpertArgs &a, const int32_t *t
   n = a.grp_sel == GRP_ROUTED ? routed : (a.grp_sel == GRP_SHARED ? total - routed : total);
 }
 
-hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);
-hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream);
+hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int path, hipStream_t stream);
+hipError_t launch_down(const ExpertArgs &a, int dtype, int path, hipStream_t stream);
 
 // Static FP8 activation quantisation: q[i] = E4M3(x[i] / *scale) for n
 // elements of x (dtype); carrier = 0 stores the code bytes, 1 their values as

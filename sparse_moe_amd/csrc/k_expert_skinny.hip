@@ -9,15 +9,17 @@
 // TR below) in wider row pieces that a per-wavefront LDS buffer turns into
 // that layout.
 //
-// Work unit = one wavefront's share of one group (routed expert or the shared
-// expert, all of its <= 16*MT rows): 16 gate + 16 up weight rows (gate-up) or
-// 32 output rows of W_down (down), over the whole K.  The grid is persistent:
+// Work unit = one wavefront's share of one 16-row tile of a group (routed
+// expert or the shared expert; a group of more rows has several tiles): 16
+// gate + 16 up weight rows (gate-up) or 32 output rows of W_down (down), over
+// the whole K.  The grid is persistent:
 // a fixed number of wavefronts strides over the units counted on the device,
 // so no partially filled round of waves is left at the end.  Inside a unit,
 // K is streamed in blocks of U 64-byte steps per row with two register sets,
 // so one block of loads is in flight while the previous one feeds the MFMAs
-// (8 steps = 24 loads per lane per block for one row fragment; fewer steps
-// with more row fragments to stay within two wavefronts' registers per SIMD).
+// (for bf16, 8 steps = 24 loads per lane per block; fewer for the formats
+// whose steps need more registers, to stay within two wavefronts' registers
+// per SIMD).
 // The token rows (gathered through sorted_token for gate-up, contiguous h rows
 // for down; padded by reloading a valid row) are the other MFMA operand.
 //
@@ -65,25 +67,27 @@ namespace hy3moe {
 
 namespace {
 
-constexpr int UBASE = 8;          // 64-byte K steps per register set (one row fragment)
+constexpr int UBASE = 8;          // 64-byte K steps per register set (bf16 weights)
 constexpr int WAVES_PER_SIMD = 2; // persistent grid occupancy
+// Token rows of a unit: one 16-row MFMA fragment (the tiles of this path hold
+// 16 rows).
+constexpr int MT = 1;
 
-// 64-byte steps per register set: bf16 weights UBASE / MT; FP8 weights 6 / 3
-// / 1 for 1 / 2 / 4 row fragments (each step also holds two token chunks);
-// W8A8 8 / 4 / 2 (one chunk of codes per step; even, as two steps make one
-// MFMA); MXFP4 3 / 2 / 1 (four token chunks per step).  With the grouped
-// weight loads (TRG steps per group) a multiple of the group: FP8 takes 4
-// in groups of four, MXFP4 2 in groups of two, or 4 when its token chunks
-// are read at multiply time (XD, below).
-template <int MT, int WF, int TRG = 0, bool XD = false>
+// 64-byte steps per register set: bf16 weights UBASE; FP8 weights 6 (each
+// step also holds two token chunks); W8A8 8 (one chunk of codes per step;
+// even, as two steps make one MFMA); MXFP4 3 (four token chunks per step);
+// W4A8 4.  With the grouped weight loads (TRG steps per group) a multiple of
+// the group: FP8 takes 4 in groups of four, MXFP4 2 in groups of two, or 4
+// when its token chunks are read at multiply time (XD, below).
+template <int WF, int TRG = 0, bool XD = false>
 constexpr int steps_per_set() {
   return TRG == 4 && WF == WF_FP8 ? 4
          : TRG == 2 && WF == WF_MXFP4 ? (XD ? 4 : 2)
-         : WF == WF_W8A8  ? (MT == 1 ? 8 : (MT == 2 ? 4 : 2))   // even: pairs of steps
-         : WF == WF_FP8   ? (MT == 1 ? 6 : (MT == 2 ? 3 : 1))
-         : WF == WF_MXFP4 ? (MT == 1 ? 3 : (MT == 2 ? 2 : 1))
-         : WF == WF_W4A8  ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
-                          : UBASE / MT;
+         : WF == WF_W8A8  ? 8   // even: pairs of steps
+         : WF == WF_FP8   ? 6
+         : WF == WF_MXFP4 ? 3
+         : WF == WF_W4A8  ? 4
+                          : UBASE;
 }
 // XD: the token chunks of a step are read from the LDS copy of x when the
 // step is multiplied, not with its weights one register set ahead.  For
@@ -91,8 +95,8 @@ constexpr int steps_per_set() {
 // registers for a second group of grouped loads per set (Hy3 decode
 // gate-up 116 -> 109 us); for the other formats, whose steps hold one or
 // two chunks, it measured the same or slower.
-template <bool XL, int MT, int WF>
-constexpr bool tokens_at_multiply() { return XL && MT == 1 && WF == WF_MXFP4; }
+template <bool XL, int WF>
+constexpr bool tokens_at_multiply() { return XL && WF == WF_MXFP4; }
 // 16-byte token chunks per 64-byte weight step.
 template <int WF>
 constexpr int token_chunks() {
@@ -103,7 +107,6 @@ template <int WF>
 constexpr bool token_codes() { return WF == WF_W4A8 || WF == WF_W8A8; }
 
 // Where a unit's operands are (per lane) and what its epilogue needs.
-template <int MT>
 struct UnitSrc {
   const char *w0p, *w1p;   // the two 16-row weight fragments (gate/up, or two down blocks)
   const char *xp[MT];      // token rows (gathered x for gate-up, h rows for down)
@@ -123,8 +126,10 @@ struct UnitOut {
   uint32_t xlo;            // XD: byte offset of the lane's token chunks in the LDS copy of x
 };
 
-// XL (gate-up at T <= 16): the workgroup copies every token row of x into
-// LDS once, and the token operand of each step is read from there, so the
+// XL (gate-up, where the copy and the wavefronts' buffers fit: T <= 16 for
+// bf16 x at H = 4096, about 32 for E4M3 codes): the workgroup copies every
+// token row of x into LDS once, and the token operand of each step is read
+// from there, so the
 // global loads carry only weights (the load path, not HBM, bounded the FP8
 // and MXFP4 weights, whose token chunks per weight byte are 2x and 4x
 // bf16's).  Rows of the copy are padded by 16 bytes, which spreads the 16
@@ -179,9 +184,9 @@ __device__ __forceinline__ void transpose_groups(uint4 (&W)[U], uint4 *lb, int l
 // Unit u (tile u / n_col_blocks, column block u % n_col_blocks) of this
 // kernel; returns false if the column block lies past the group's width.
 // half = 1 or 2: only the first or the second 16-row fragment of a down unit.
-template <typename T, bool GATE_UP, int MT, int WF, bool XL, int TRG>
+template <typename T, bool GATE_UP, int WF, bool XL, int TRG>
 __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_blocks, int lane,
-                                        UnitSrc<MT> &src, UnitOut &o, int half = 0) {
+                                        UnitSrc &src, UnitOut &o, int half = 0) {
   constexpr bool F8 = WF == WF_FP8 || WF == WF_W8A8, F4 = WF == WF_MXFP4 || WF == WF_W4A8;
   constexpr bool MXA = WF == WF_W4A8, CODES = token_codes<WF>();
   constexpr int EB = Elem<T>::kBytes;
@@ -287,9 +292,9 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
 // of them is split into its two 16-row fragments for twice as many
 // wavefronts, so the last round costs half a unit.  Returns the item index
 // (kmax when there is none) and fills src / o.
-template <typename T, bool GATE_UP, int MT, int WF, bool XL, int TRG>
+template <typename T, bool GATE_UP, int WF, bool XL, int TRG>
 __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int nw, int n_units,
-                                         int n_col_blocks, int lane, UnitSrc<MT> &src,
+                                         int n_col_blocks, int lane, UnitSrc &src,
                                          UnitOut &o) {
   const int full = n_units / nw, tail = n_units - full * nw;
   const bool split = !GATE_UP && 2 * tail <= nw;
@@ -298,10 +303,10 @@ __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int 
     if (k < full || !split) {
       const int u = w + k * nw;
       if (u >= n_units) return kmax;
-      if (unit_of<T, GATE_UP, MT, WF, XL, TRG>(a, u, n_col_blocks, lane, src, o)) return k;
+      if (unit_of<T, GATE_UP, WF, XL, TRG>(a, u, n_col_blocks, lane, src, o)) return k;
     } else {
       if (w >= 2 * tail) return kmax;
-      if (unit_of<T, GATE_UP, MT, WF, XL, TRG>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
+      if (unit_of<T, GATE_UP, WF, XL, TRG>(a, full * nw + (w >> 1), n_col_blocks, lane, src, o,
                                       1 + (w & 1)))
         return k;
     }
@@ -309,7 +314,7 @@ __device__ __forceinline__ int next_item(const ExpertArgs &a, int k, int w, int 
   return kmax;
 }
 
-template <typename T, bool GATE_UP, int MT, int WF>
+template <typename T, bool GATE_UP, int WF>
 __device__ __forceinline__ void unit_epilogue(const ExpertArgs &a, const UnitOut &o,
                                               f32x4_t (&acc)[2][MT], int lane) {
   constexpr bool F8 = WF == WF_FP8 || WF == WF_W8A8;
@@ -367,7 +372,7 @@ template <bool XL> constexpr int stream_threads() { return XL ? 512 : 256; }
 // BRANCH names the instantiation only: 0 for the routed experts (or every
 // group), 1 for the shared expert's own launches, which profiles then list
 // apart.
-template <typename T, bool GATE_UP, int MT, int WF, bool XL, int TRG, int BRANCH>
+template <typename T, bool GATE_UP, int WF, bool XL, int TRG, int BRANCH>
 __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_stream_kernel(
     ExpertArgs a_in, int n_col_blocks) {
   constexpr bool F8 = WF == WF_FP8, F4 = WF == WF_MXFP4, MXA = WF == WF_W4A8;
@@ -474,8 +479,8 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
     a.hs = scl + 2 * (a_in.E + 1);
     a.xs = scl + 3 * (a_in.E + 1);
   }
-  constexpr bool XD = tokens_at_multiply<XL, MT, WF>();
-  constexpr int U = steps_per_set<MT, WF, TRG, XD>();   // 64-byte K steps per row per register set
+  constexpr bool XD = tokens_at_multiply<XL, WF>();
+  constexpr int U = steps_per_set<WF, TRG, XD>();   // 64-byte K steps per row per register set
   constexpr int XN = token_chunks<WF>();       // 16-byte token chunks per step
   const int lane = threadIdx.x & 63;
   // The wavefront index is uniform; readfirstlane makes that visible to the
@@ -488,9 +493,9 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   const int kmax = n_units / nw + 1;
   // Wavefront ids interleave the XCDs (block b runs on XCD b % 8), so the
   // units of one expert spread over all XCDs and HBM channels.
-  UnitSrc<MT> src;    // item whose blocks are being loaded
+  UnitSrc src;    // item whose blocks are being loaded
   UnitOut om, ol;     // item being multiplied, item being loaded
-  int k_ld = next_item<T, GATE_UP, MT, WF, XL, TRG>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
+  int k_ld = next_item<T, GATE_UP, WF, XL, TRG>(a, 0, w, nw, n_units, n_col_blocks, lane, src, ol);
   if (k_ld >= kmax) return;
   int k_mm = k_ld;
   om = ol;
@@ -580,7 +585,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
     }                                                                                  \
     s_ld += U;                                                                         \
     if (s_ld >= src.nsub) {                                                            \
-      k_ld = next_item<T, GATE_UP, MT, WF, XL, TRG>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
+      k_ld = next_item<T, GATE_UP, WF, XL, TRG>(a, k_ld + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src, ol);                             \
       s_ld = 0;                                                                        \
     }                                                                                  \
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   // and move on.  `more` turns false after the last unit.
 #define HY3_MMA(W0, W1, X, S0, S1, XS)                                                 \
   {                                                                                    \
-    if constexpr (XD) {   /* this block's token chunks (one fragment), from LDS */    \
+    if constexpr (XD) {   /* this block's token chunks, from LDS */                 \
       _Pragma("unroll") for (int u = 0; u < U; ++u) {                                  \
         const int sx_ = s_mm + u < om.nsub ? s_mm + u : om.nsub - 1;                   \
         _Pragma("unroll") for (int h = 0; h < XN; ++h)                                 \
@@ -657,16 +662,16 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
     }                                                                                  \
     s_mm += U;                                                                         \
     if (s_mm >= om.nsub) {                                                             \
-      unit_epilogue<T, GATE_UP, MT, WF>(a, om, acc, lane);                             \
+      unit_epilogue<T, GATE_UP, WF>(a, om, acc, lane);                             \
       _Pragma("unroll") for (int f = 0; f < 2; ++f)                                    \
         _Pragma("unroll") for (int m = 0; m < MT; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; \
-      k_mm = next_item<T, GATE_UP, MT, WF, XL, TRG>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
+      k_mm = next_item<T, GATE_UP, WF, XL, TRG>(a, k_mm + 1, w, nw, n_units, n_col_blocks,   \
                                            lane, src_dummy, om);                       \
       s_mm = 0;                                                                        \
       more = k_mm < kmax;                                                              \
     }                                                                                  \
   }
-  UnitSrc<MT> src_dummy;   // next_unit also fills operand pointers; the multiply side ignores them
+  UnitSrc src_dummy;   // next_unit also fills operand pointers; the multiply side ignores them
   bool more = true;
   HY3_LOAD(aw0, aw1, ax, as0, as1, axs);
   while (more) {
@@ -688,10 +693,9 @@ constexpr int STREAM_BLOCKS = 256 * WAVES_PER_SIMD;
 constexpr size_t STREAM_XL_LDS_MAX = 160 * 1024;   // LDS of one workgroup (one per CU)
 
 // LDS bytes of the x copy (rows padded), or 0 when the gate-up GEMM of this
-// batch does not stage x: one 16-row fragment (T <= 16) and the copy fits.
-template <typename T, int MT, int WF>
+// batch does not stage x (the copy and the unit metadata do not fit).
+template <typename T, int WF>
 size_t x_lds_bytes(const ExpertArgs &a) {
-  if (MT != 1) return 0;
   const int rb = a.H * (token_codes<WF>() ? 1 : Elem<T>::kBytes);
   const size_t meta = (meta_lds_bytes(a, true) + 15) / 16 * 16;
   const size_t x = (size_t)a.n_tok * x_lds_stride(rb);
@@ -706,21 +710,16 @@ constexpr int weight_row_bytes(int K) {
                                            : K * Elem<T>::kBytes;
 }
 
-// Group size of the grouped weight loads for a format and token fragment
-// count (0: none): four 64-byte steps where the register sets hold whole
-// groups of four without spilling, else two.  FP8 takes four steps per set
-// at one fragment; MXFP4 weights with bf16 tokens take groups of two (at
-// four they spill; the grouped loads with two steps per set beat the
-// MFMA-shaped ones with three: Hy3 decode 0.254 -> 0.202 ms), two groups
-// per set when the tokens are read at multiply time; at four fragments
-// neither FP8, W4A8 nor MXFP4 has an even count.
-template <typename T, int MT, int WF>
+// Group size of the grouped weight loads for a format (0: none): four
+// 64-byte steps where the register sets hold whole groups of four without
+// spilling, else two.  FP8 takes four steps per set; MXFP4 weights with bf16
+// tokens take groups of two (at four they spill; the grouped loads with two
+// steps per set beat the MFMA-shaped ones with three: Hy3 decode 0.254 ->
+// 0.202 ms), two groups per set when the tokens are read at multiply time.
+template <typename T, int WF>
 constexpr int tr_group() {
   if (std::is_same<T, float>::value) return 0;
-  if (WF == WF_MXFP4) return MT <= 2 ? 2 : 0;
-  if (MT == 1) return 4;
-  if (MT == 2) return (WF == WF_DTYPE || WF == WF_W8A8) ? 4 : (WF == WF_W4A8 ? 2 : 0);
-  return (WF == WF_DTYPE || WF == WF_W8A8) ? 2 : 0;
+  return WF == WF_MXFP4 ? 2 : 4;
 }
 // Every weight row of the launch a multiple of a group's 64 trg bytes.
 template <typename T, int WF>
@@ -731,37 +730,37 @@ bool tr_rows(const ExpertArgs &a, bool gate_up, int trg) {
          (a.grp_sel == GRP_ROUTED || a.I_shared == 0 || ok(a.I_shared));
 }
 
-template <typename T, int MT, int WF, int TRG, int BRANCH>
+template <typename T, int WF, int TRG, int BRANCH>
 hipError_t launch_skinny_tr(const ExpertArgs &a, bool gate_up, size_t xb, hipStream_t stream) {
   const size_t meta = (meta_lds_bytes(a, gate_up) + 15) / 16 * 16;
   if (gate_up) {
     const int Imax = a.I > a.I_shared ? a.I : a.I_shared;
     const int ncb = (Imax + 15) / 16;
     if (xb)   // one 512-thread workgroup per CU, x in LDS
-      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, true, TRG, BRANCH>),
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, WF, true, TRG, BRANCH>),
                          dim3(STREAM_BLOCKS / 2), dim3(512), meta + xb + 8 * tr_wave_bytes(TRG),
                          stream, a, ncb);
     else
-      hipLaunchKernelGGL((expert_stream_kernel<T, true, MT, WF, false, TRG, BRANCH>),
+      hipLaunchKernelGGL((expert_stream_kernel<T, true, WF, false, TRG, BRANCH>),
                          dim3(STREAM_BLOCKS), dim3(256), meta + 4 * tr_wave_bytes(TRG), stream, a,
                          ncb);
   } else {
     const int ncb = (a.H + 31) / 32;
-    hipLaunchKernelGGL((expert_stream_kernel<T, false, MT, WF, false, TRG, BRANCH>),
+    hipLaunchKernelGGL((expert_stream_kernel<T, false, WF, false, TRG, BRANCH>),
                        dim3(STREAM_BLOCKS), dim3(256), meta + 4 * tr_wave_bytes(TRG), stream, a,
                        ncb);
   }
   return hipGetLastError();
 }
 
-template <typename T, int MT, int WF, int BRANCH>
+template <typename T, int WF, int BRANCH>
 hipError_t launch_skinny_b(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
-  const size_t xb = gate_up ? x_lds_bytes<T, MT, WF>(a) : 0;
-  constexpr int G = tr_group<T, MT, WF>();
+  const size_t xb = gate_up ? x_lds_bytes<T, WF>(a) : 0;
+  constexpr int G = tr_group<T, WF>();
   if constexpr (G > 0) {
     // The grouped loads with the LDS copy of x when it leaves room for the
-    // 8 wavefronts' buffers; for one fragment, groups of two steps (half the
-    // buffer) when only those leave room; else the grouped loads with the
+    // 8 wavefronts' buffers; groups of two steps (half the buffer) when only
+    // those leave room; else the grouped loads with the
     // tokens from global memory (measured faster than the copy without them
     // for bf16 x at H = 4096).
     const size_t meta = (meta_lds_bytes(a, gate_up) + 15) / 16 * 16;
@@ -769,59 +768,59 @@ hipError_t launch_skinny_b(const ExpertArgs &a, bool gate_up, hipStream_t stream
       return !xb || meta + xb + 8 * (size_t)tr_wave_bytes(trg) <= STREAM_XL_LDS_MAX;
     };
     if (tr_rows<T, WF>(a, gate_up, G) && room(G))
-      return launch_skinny_tr<T, MT, WF, G, BRANCH>(a, gate_up, xb, stream);
-    if constexpr (G == 4 && MT == 1) {
+      return launch_skinny_tr<T, WF, G, BRANCH>(a, gate_up, xb, stream);
+    if constexpr (G == 4) {
       if (xb && tr_rows<T, WF>(a, gate_up, 2) && room(2))
-        return launch_skinny_tr<T, MT, WF, 2, BRANCH>(a, gate_up, xb, stream);
+        return launch_skinny_tr<T, WF, 2, BRANCH>(a, gate_up, xb, stream);
     }
     if (tr_rows<T, WF>(a, gate_up, G))
-      return launch_skinny_tr<T, MT, WF, G, BRANCH>(a, gate_up, 0, stream);
+      return launch_skinny_tr<T, WF, G, BRANCH>(a, gate_up, 0, stream);
   }
-  return launch_skinny_tr<T, MT, WF, 0, BRANCH>(a, gate_up, xb, stream);
+  return launch_skinny_tr<T, WF, 0, BRANCH>(a, gate_up, xb, stream);
 }
 
-template <typename T, int MT, int WF>
-hipError_t launch_skinny_t(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
-  return a.grp_sel == GRP_SHARED ? launch_skinny_b<T, MT, WF, 1>(a, gate_up, stream)
-                                 : launch_skinny_b<T, MT, WF, 0>(a, gate_up, stream);
-}
-
+// Every batch of this path runs units of one 16-row token fragment: the
+// tile list holds tiles of SKINNY_ROWS rows, and a group of more rows has
+// several, each of which streams the group's weights again (their units of
+// one column block run in the same round of the persistent grid, so the
+// repeated rows are mostly cache hits).  Tiles of 32 and 64 rows with two
+// and four fragments per unit, which read the weights once, were slower:
+// their register sets held fewer steps and their padding fragments cost
+// full token loads for routed experts of a few rows (Hy3 decode T=64
+// 0.915 -> 0.805 ms, T=32 0.661 -> 0.652 ms).
 template <typename T, int WF>
-hipError_t launch_skinny(const ExpertArgs &a, bool gate_up, int T_tokens, hipStream_t stream) {
-  if (T_tokens <= 16) return launch_skinny_t<T, 1, WF>(a, gate_up, stream);
-  if (T_tokens <= 32) return launch_skinny_t<T, 2, WF>(a, gate_up, stream);
-  return launch_skinny_t<T, 4, WF>(a, gate_up, stream);
+hipError_t launch_skinny(const ExpertArgs &a, bool gate_up, hipStream_t stream) {
+  return a.grp_sel == GRP_SHARED ? launch_skinny_b<T, WF, 1>(a, gate_up, stream)
+                                 : launch_skinny_b<T, WF, 0>(a, gate_up, stream);
 }
 
 }  // namespace
-
-int skinny_tile_rows(int T) { return T <= 16 ? 16 : (T <= 32 ? 32 : 64); }
 
 hipError_t launch_tiled_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_tiled_down(const ExpertArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_big_gate_up(const ExpertArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_big_down(const ExpertArgs &a, int dtype, hipStream_t stream);
 
-hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
+hipError_t launch_gate_up(const ExpertArgs &a, int dtype, int path, hipStream_t stream) {
   if (path == PATH_SKINNY)
-    return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, true, T, stream)
-           : a.amx         ? launch_skinny<bf16_t, WF_W4A8>(a, true, T, stream)
-           : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, true, T, stream)
-           : a.w_fp8 && a.a8 && a.a8_codes ? launch_skinny<bf16_t, WF_W8A8>(a, true, T, stream)
-           : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, true, T, stream)
-                           : launch_skinny<bf16_t, WF_DTYPE>(a, true, T, stream);
+    return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, true, stream)
+           : a.amx         ? launch_skinny<bf16_t, WF_W4A8>(a, true, stream)
+           : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, true, stream)
+           : a.w_fp8 && a.a8 && a.a8_codes ? launch_skinny<bf16_t, WF_W8A8>(a, true, stream)
+           : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, true, stream)
+                           : launch_skinny<bf16_t, WF_DTYPE>(a, true, stream);
   if (path == PATH_BIG) return launch_big_gate_up(a, dtype, stream);
   return launch_tiled_gate_up(a, dtype, stream);
 }
 
-hipError_t launch_down(const ExpertArgs &a, int dtype, int T, int path, hipStream_t stream) {
+hipError_t launch_down(const ExpertArgs &a, int dtype, int path, hipStream_t stream) {
   if (path == PATH_SKINNY)
-    return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, false, T, stream)
-           : a.amx         ? launch_skinny<bf16_t, WF_W4A8>(a, false, T, stream)
-           : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, false, T, stream)
-           : a.w_fp8 && a.a8 && a.a8_codes ? launch_skinny<bf16_t, WF_W8A8>(a, false, T, stream)
-           : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, false, T, stream)
-                           : launch_skinny<bf16_t, WF_DTYPE>(a, false, T, stream);
+    return dtype == DT_F32 ? launch_skinny<float, WF_DTYPE>(a, false, stream)
+           : a.amx         ? launch_skinny<bf16_t, WF_W4A8>(a, false, stream)
+           : a.w_fp4       ? launch_skinny<bf16_t, WF_MXFP4>(a, false, stream)
+           : a.w_fp8 && a.a8 && a.a8_codes ? launch_skinny<bf16_t, WF_W8A8>(a, false, stream)
+           : a.w_fp8       ? launch_skinny<bf16_t, WF_FP8>(a, false, stream)
+                           : launch_skinny<bf16_t, WF_DTYPE>(a, false, stream);
   if (path == PATH_BIG) return launch_big_down(a, dtype, stream);
   return launch_tiled_down(a, dtype, stream);
 }

@@ -206,7 +206,7 @@ CONFIGS: Dict[str, MoEConfig] = {
                   I=1536, I_shared=1536, dtype="bf16",
                   route_mode=ROUTE_SIGMOID_BIAS, scale=HY3_SCALE, renorm_eps=0.0,
                   bias_kind="skew", w_format="mxfp4", act_format="mxfp8"),
-    # Hy3 decode with 32 tokens (two 16-row token fragments per unit), on the
+    # Hy3 decode with 32 tokens (the shared expert in two 16-row tiles), on the
     # bf16 and on the FP8 weights, the latter with static FP8 activations.
     "hy3_decode_T32": MoEConfig("hy3_decode_T32", 15, 1, T=32, H=4096, E=192, K=8, I=1536,
                  I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
@@ -215,7 +215,7 @@ CONFIGS: Dict[str, MoEConfig] = {
                  I=1536, I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform",
                  w_format="fp8_e4m3", act_format="fp8_static"),
-    # ... and with 64 tokens (four token fragments per unit), bf16.
+    # ... and with 64 tokens (the shared expert in four 16-row tiles), bf16.
     "hy3_decode_T64": MoEConfig("hy3_decode_T64", 17, 1, T=64, H=4096, E=192, K=8, I=1536,
                  I_shared=1536, dtype="bf16", route_mode=ROUTE_SIGMOID_BIAS,
                  scale=HY3_SCALE, renorm_eps=0.0, bias_kind="uniform"),

@@ -94,9 +94,9 @@ def test_hy3_prefill_T8192_skew_full(dev, hy3_weights):
 
 
 def test_hy3_decode_T32_full(dev, hy3_weights):
-    """32 tokens on the Hy3 weights: two 16-row token fragments per work unit
-    (the four-row weight loads at two fragments), every token, the stated
-    bf16 bound (the decode workload's shapes and dtypes at another T)."""
+    """32 tokens on the Hy3 weights (the shared expert in two 16-row tiles),
+    every token, the stated bf16 bound (the decode workload's shapes and
+    dtypes at another T)."""
     decode_full_check(MoEInputs(CONFIGS["hy3_decode_T32"]), dev, hy3_weights)
 
 
@@ -179,13 +179,13 @@ def test_hy3_decode_T16_w8a8_full(dev, hy3_fp8_weights):
 
 
 def test_hy3_decode_T64_full(dev, hy3_weights):
-    """64 tokens on the Hy3 weights: four token fragments per work unit (the
-    two-step grouped weight loads), every token, the stated bf16 bound."""
+    """64 tokens on the Hy3 weights (the shared expert in four 16-row tiles),
+    every token, the stated bf16 bound."""
     decode_full_check(MoEInputs(CONFIGS["hy3_decode_T64"]), dev, hy3_weights)
 
 
 def test_hy3_decode_T32_w8a8_full(dev, hy3_fp8_weights):
-    """W8A8 decode with 32 tokens (FP8 MFMAs at two token fragments)."""
+    """W8A8 decode with 32 tokens (FP8 MFMAs, the E4M3 codes of x in LDS)."""
     inp = MoEInputs(CONFIGS["hy3_decode_T32_w8a8"])
     decode_full_check(inp, dev, with_act_scales(inp, hy3_fp8_weights, dev),
                       workload_shape=False)

@@ -1,7 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
 
 Small and medium cases run the oracle on every token; they span the
-weight-streaming path (T <= 64; 1, 2 and 4 row fragments) and the tiled path
+weight-streaming path (T <= 64; groups of one and of several 16-row
+tiles) and the tiled path
 (several row tiles per expert with ragged tails), fp32 and bf16, both routing
 modes, with/without the shared expert, K = E, E = 256, forced routing and the
 empty batch.  The full-size workloads check every route index and a seeded
@@ -106,7 +107,7 @@ SMALL = {
     "big_T300_f32": dict(seed=19, T=300, H=256, E=2, K=2, I=128, I_shared=192, dtype="f32"),
     "big_softmax_T600": dict(seed=20, T=600, H=256, E=8, K=3, I=128, I_shared=128, dtype="bf16",
                              route_mode=1, scale=1.0, renorm_eps=1e-8, bias_kind="none"),
-    # FP8 E4M3 expert weights (weight-streaming path; 1, 2 and 4 row fragments;
+    # FP8 E4M3 expert weights (weight-streaming path at 1 to 64 tokens;
     # ragged K blocks; no shared expert; softmax routing)
     "fp8_T1": dict(seed=30, T=1, H=512, E=32, K=8, I=256, I_shared=256, dtype="bf16",
                    w_format="fp8_e4m3"),
@@ -130,21 +131,21 @@ SMALL = {
     "fp8_big_T400_softmax": dict(seed=38, T=400, H=512, E=8, K=4, I=256, I_shared=128,
                                  dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
                                  bias_kind="none", w_format="fp8_e4m3"),
-    # Static FP8 activations (W8A8) on every path: weight streaming (1 and 4
-    # row fragments), tiled, large-tile FP8 MFMAs (with an H % 256 == 128
+    # Static FP8 activations (W8A8) on every path: weight streaming (16 and 64
+    # tokens), tiled, large-tile FP8 MFMAs (with an H % 256 == 128
     # column tail and softmax routing), and an H % 128 != 0 batch that the
     # large-tile path hands to the tiled one
     "w8a8_T16": dict(seed=40, T=16, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16",
                      w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_T64_noshared": dict(seed=41, T=64, H=512, E=8, K=2, I=256, I_shared=0,
                               dtype="bf16", w_format="fp8_e4m3", act_format="fp8_static"),
-    # weight-streaming W8A8 with two 16-row fragments (FP8 x FP8 MFMAs), and
+    # weight-streaming W8A8 at 32 tokens (FP8 x FP8 MFMAs), and
     # with a K that is not a multiple of 128 (bf16 values of the codes)
     "w8a8_T32_codes": dict(seed=43, T=32, H=384, E=12, K=4, I=256, I_shared=128, dtype="bf16",
                            w_format="fp8_e4m3", act_format="fp8_static"),
     "w8a8_T16_values": dict(seed=44, T=16, H=320, E=10, K=4, I=192, I_shared=64, dtype="bf16",
                             w_format="fp8_e4m3", act_format="fp8_static"),
-    # one fragment with every weight row a multiple of 256 bytes: the
+    # every weight row a multiple of 256 bytes: the
     # four-row weight loads (W8A8, W4A8 and bf16)
     "w8a8_T8_rows256": dict(seed=45, T=8, H=512, E=8, K=2, I=256, I_shared=256, dtype="bf16",
                             w_format="fp8_e4m3", act_format="fp8_static"),
@@ -162,13 +163,13 @@ SMALL = {
                                     dtype="bf16", w_format="fp8_e4m3",
                                     act_format="fp8_static"),
     # MXFP4 weights (E2M1 codes, E8M0 scale per 32) on the weight-streaming
-    # path: 1, 2 and 4 row fragments, softmax routing, no shared expert, a
+    # path: 1 to 64 tokens, softmax routing, no shared expert, a
     # shared expert wider than the routed ones
     "mxfp4_T1": dict(seed=70, T=1, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16",
                      w_format="mxfp4"),
     "mxfp4_T16": dict(seed=71, T=16, H=512, E=32, K=4, I=256, I_shared=128, dtype="bf16",
                       w_format="mxfp4"),
-    # one fragment with x in LDS: rows of 192 bytes (no grouped loads, three
+    # x in LDS: rows of 192 bytes (no grouped loads, three
     # steps per set) and of 384 bytes (two groups of two per set, a partial
     # last set)
     "mxfp4_T8_H384": dict(seed=78, T=8, H=384, E=8, K=2, I=128, I_shared=128, dtype="bf16",
@@ -192,7 +193,7 @@ SMALL = {
                                    dtype="bf16", route_mode=1, scale=1.0, renorm_eps=1e-8,
                                    bias_kind="none", w_format="mxfp4"),
     # W4A8: MXFP4 weights with dynamic MXFP8 activations; block-scaled FP4 x
-    # FP8 MFMAs on the weight-streaming path (1, 2 and 4 row fragments), the
+    # FP8 MFMAs on the weight-streaming path (1 to 64 tokens), the
     # same values in bf16 on the tile paths
     "w4a8_T1": dict(seed=80, T=1, H=256, E=16, K=4, I=128, I_shared=128, dtype="bf16",
                     w_format="mxfp4", act_format="mxfp8"),
