@@ -113,7 +113,7 @@ struct UnitSrc {
   uint32_t xlo[MT];        // XL: byte offsets of the lane's token chunks in the LDS copy of x
   const uint8_t *s0p, *s1p;  // MXFP4: the lane's scale bytes of the two fragments
   const uint8_t *xsp[MT];    // W4A8: the lane's scale bytes of the token rows
-  bool vs;                   // W4A8: scale rows allow 16-byte loads of 4 steps
+  bool vs;                   // MXFP4, W4A8: scale rows allow 16-byte loads of 4 steps
   int nsub;                // 64-byte K steps per row
   int nf;                  // fragments streamed (2; 1 for half of a down unit)
   int rowb;                // TR: bytes per weight row (the stride of the grouped loads)
@@ -280,6 +280,9 @@ __device__ __forceinline__ bool unit_of(const ExpertArgs &a, int u, int n_col_bl
       // K % 512 == 0: weight scale rows of K/32 bytes are 16-byte multiples,
       // and so are the token scale rows (x: K = H; h: rows of ldh / 32)
       src.vs = (o.nsub & 3) == 0 && (GATE_UP || a.ldh % 512 == 0);
+    } else if (WF == WF_MXFP4) {
+      src.xp[m] = reinterpret_cast<const char *>(act + arow) + cg * 16 * token_chunks<WF>();
+      src.vs = (o.nsub & 3) == 0;   // the weight scale rows (K / 32 bytes), as for W4A8
     } else {
       src.xp[m] = reinterpret_cast<const char *>(act + arow) + cg * 16 * token_chunks<WF>();
     }
@@ -482,6 +485,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   constexpr bool XD = tokens_at_multiply<XL, WF>();
   constexpr int U = steps_per_set<WF, TRG, XD>();   // 64-byte K steps per row per register set
   constexpr int XN = token_chunks<WF>();       // 16-byte token chunks per step
+  constexpr bool SC4 = (F4 || MXA) && U % 4 == 0;   // block scales of 4 steps per load
   const int lane = threadIdx.x & 63;
   // The wavefront index is uniform; readfirstlane makes that visible to the
   // compiler, so every unit-dependent guard below is a scalar branch.  (An
@@ -514,28 +518,30 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
   // Load the next block of the loading unit into set W0/W1/X, then move the
   // loading position on (to the next unit at the end of this one).  Steps past
   // nsub re-read the last step (in bounds) and are not used.
-  // W4A8, 4 steps per register set: the scales of steps st .. st + 3 (all four
-  // lane groups) are 16 contiguous bytes of a scale row when the unit's K is
-  // a multiple of 512 (then st % 4 == 0 and st + 3 < nsub, or st >= nsub;
-  // the rows are 16-byte aligned): one load per row instead of four byte
-  // loads per lane.
-  // The lane's byte of step st + v is byte g of word v, shifted to byte 0
-  // (the MFMA reads byte 0 of the scale register).  Otherwise byte loads.
+  // MXFP4 and W4A8 weights, 4 steps per register set: the scales of steps
+  // st .. st + 3 (all four lane groups) are 16 contiguous bytes of a scale
+  // row when the unit's K is a multiple of 512 (then st % 4 == 0 and st + 3 <
+  // nsub, or st >= nsub; the rows are 16-byte aligned): one load per row
+  // instead of four byte loads per lane (MXFP4 Hy3 decode gate-up 109 -> 90
+  // us).  The lane's byte of step st + v is byte g of word v, shifted to byte
+  // 0 (the MFMA reads byte 0 of the scale register; the MXFP4 decode takes
+  // the byte alone).  Otherwise byte loads.
 #define HY3_SCALES4(S0, S1, XS, u, st)                                                 \
   {                                                                                    \
     const int sh_ = 8 * (lane >> 4);                                                   \
+    constexpr uint32_t sm_ = MXA ? 0xFFFFFFFFu : 0xFFu;                                \
     if (src.vs) {                                                                      \
       /* past the end: a valid group of 4 steps, not used */                          \
       const int s4_ = (st) < src.nsub ? (st) : src.nsub - 4;                           \
       const uint4 w0_ = *reinterpret_cast<const uint4 *>(src.s0p - (lane >> 4) + s4_ * 4); \
-      S0[(u) + 0] = w0_.x >> sh_; S0[(u) + 1] = w0_.y >> sh_;                          \
-      S0[(u) + 2] = w0_.z >> sh_; S0[(u) + 3] = w0_.w >> sh_;                          \
+      S0[(u) + 0] = (w0_.x >> sh_) & sm_; S0[(u) + 1] = (w0_.y >> sh_) & sm_;          \
+      S0[(u) + 2] = (w0_.z >> sh_) & sm_; S0[(u) + 3] = (w0_.w >> sh_) & sm_;          \
       {                                                                                \
         const uint4 w1_ = *reinterpret_cast<const uint4 *>(src.s1p - (lane >> 4) + s4_ * 4); \
-        S1[(u) + 0] = w1_.x >> sh_; S1[(u) + 1] = w1_.y >> sh_;                        \
-        S1[(u) + 2] = w1_.z >> sh_; S1[(u) + 3] = w1_.w >> sh_;                        \
+        S1[(u) + 0] = (w1_.x >> sh_) & sm_; S1[(u) + 1] = (w1_.y >> sh_) & sm_;        \
+        S1[(u) + 2] = (w1_.z >> sh_) & sm_; S1[(u) + 3] = (w1_.w >> sh_) & sm_;        \
       }                                                                                \
-      _Pragma("unroll") for (int m = 0; m < MT; ++m) {                                 \
+      if constexpr (MXA) _Pragma("unroll") for (int m = 0; m < MT; ++m) {              \
         const uint4 x_ = *reinterpret_cast<const uint4 *>(src.xsp[m] - (lane >> 4) + s4_ * 4); \
         XS[(u) + 0][m] = x_.x >> sh_; XS[(u) + 1][m] = x_.y >> sh_;                    \
         XS[(u) + 2][m] = x_.z >> sh_; XS[(u) + 3][m] = x_.w >> sh_;                    \
@@ -545,7 +551,7 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
         const int sv_ = (st) + v < src.nsub ? (st) + v : src.nsub - 1;                 \
         S0[(u) + v] = src.s0p[sv_ * 4];                                                \
         S1[(u) + v] = src.s1p[sv_ * 4];                                                \
-        _Pragma("unroll") for (int m = 0; m < MT; ++m) XS[(u) + v][m] = src.xsp[m][sv_ * 4]; \
+        if constexpr (MXA) _Pragma("unroll") for (int m = 0; m < MT; ++m) XS[(u) + v][m] = src.xsp[m][sv_ * 4]; \
       }                                                                                \
     }                                                                                  \
   }
@@ -564,14 +570,14 @@ __global__ __launch_bounds__(stream_threads<XL>(), WAVES_PER_SIMD) void expert_s
         W0[u] = *reinterpret_cast<const uint4 *>(src.w0p + o_);                        \
         W1[u] = *reinterpret_cast<const uint4 *>(src.w1p + o_);                        \
       }                                                                                \
-      if constexpr (F4 || (MXA && U % 4 != 0)) {                                       \
+      if constexpr ((F4 || MXA) && !SC4) {                                             \
         S0[u] = src.s0p[st_ * 4];                                                      \
         S1[u] = src.s1p[st_ * 4];                                                      \
       }                                                                                \
-      if constexpr (MXA && U % 4 != 0) {                                               \
+      if constexpr (MXA && !SC4) {                                                     \
         _Pragma("unroll") for (int m = 0; m < MT; ++m) XS[u][m] = src.xsp[m][st_ * 4]; \
       }                                                                                \
-      if constexpr (MXA && U % 4 == 0) {                                               \
+      if constexpr (SC4) {                                                             \
         if (u % 4 == 0) HY3_SCALES4(S0, S1, XS, u, s_ld + u);                          \
       }                                                                                \
       if constexpr (!XD)                                                               \
