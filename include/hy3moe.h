@@ -237,8 +237,8 @@ typedef struct hy3moe_ws_layout {
                             multiple of 16), stored in the order the router GEMM
                             reads its operand fragments; used for bf16 batches of
                             T >= 1024 (0 = not used)                              */
-  size_t xq;             /* act_format FP8_STATIC: quantised x [T][H], E4M3 bytes on
-                            the large-tile path, else their bf16 values (0 = not
+  size_t xq;             /* act_format FP8_STATIC: quantised x [T][H], E4M3 bytes
+                            when a8_codes is set, else their bf16 values (0 = not
                             used); h then holds h quantised the same way.
                             MXFP8: x as E4M3 bytes (weight-streaming and large-tile
                             paths) or the bf16 values of the codes (tiled path) */
@@ -254,8 +254,8 @@ typedef struct hy3moe_ws_layout {
                             offsets [E+2] and row map [R] for its launches on the
                             side stream (0: the shared expert, if any, runs in
                             the routed experts' launches on the caller's stream) */
-  int32_t gemm_path;     /* expert GEMMs: 0 weight streaming (T <= 64), 1 tiles of
-                            128 rows, 2 tiles of 256 rows                      */
+  int32_t gemm_path;     /* expert GEMMs: 0 weight streaming (T <= 64, tiles of 16
+                            rows), 1 tiles of 128 rows, 2 tiles of 256 rows    */
   int32_t a8_codes;      /* static FP8 activations (x and h) are stored as E4M3
                             codes for FP8 MFMAs (large tiles; weight streaming
                             when H, I and I_shared are multiples of 128), else
